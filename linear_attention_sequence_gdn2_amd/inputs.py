@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs for the GDN-2 operator (shared by tests, bench and smoke).
+
+This module holds only random-number generation and the input recipe; none of
+the operator's arithmetic lives here.  Both the HIP path and the fp64 oracle
+are fed from the same host tensors it returns.
+
+Recipe (shapes from the Gated DeltaNet-2 pages: 16 heads with 128-dim keys and
+values, iplexlaw.co.kr blog section "Experimental comparison"; 64-token chunks,
+section "Token path and parallel training"; 2K x 8 and 16K x 1 training shapes,
+section "Ablations and training throughput", Figure 2):
+
+* q, k ~ N(0, 1) per channel, then L2-normalised per (batch, token, head) in fp32
+  (the pages normalise q and k before the operator), then optionally rounded to
+  bf16 (round-to-nearest-even).  v ~ N(0, 1), same rounding.
+* log_alpha: ``"softplus"``  -> -softplus(N(0,1)) * 0.1   (tiny fp32 workload)
+             ``"logsigmoid"`` -> log(sigmoid(N(3,1)))      (decay ~0.9-0.99)
+* gates ``"channel"``: b = sigmoid(N(0,1)) per key channel, w = sigmoid(N(0,1))
+  per value channel.  ``"kda"``: one beta = sigmoid(N(0,1)) per (b,t,h),
+  broadcast to b and w.  ``"gdn"``: as ``"kda"`` and log_alpha drawn once per
+  (b,t,h) and broadcast over key channels.
+* S0 ~ N(0, s0_std) (zeros when s0_std == 0), dO ~ N(0, 1), dS_final ~ N(0, 0.01).
+
+The second argument of every N(mu, sigma) is a standard deviation.  Draw order
+is fixed: q, k, v, log_alpha, b, w, S0, dO, dS_final.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, asdict
+
+import torch
+import torch.nn.functional as F
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    seed: int
+    qkv_dtype: str = "bf16"          # "bf16" or "f32"
+    decay: str = "logsigmoid"        # "softplus" or "logsigmoid"
+    gates: str = "channel"           # "channel", "kda" or "gdn"
+    s0_std: float = 0.0
+    grads: bool = False              # also draw dO and dS_final
+    extra: dict = field(default_factory=dict)
+
+    def as_dict(self):
+        return asdict(self)
+
+
+# The five workloads of the operator, named by what they are.
+WORKLOADS = {
+    "tiny_f32_B1H2T128d32": Workload("tiny_f32_B1H2T128d32", 1, 128, 2, 32, 32, 1001,
+                                     qkv_dtype="f32", decay="softplus"),
+    "fwd_bf16_B8H16T2048d128": Workload("fwd_bf16_B8H16T2048d128", 8, 2048, 16, 128, 128, 1002),
+    "long_bf16_B1H16T16384d128": Workload("long_bf16_B1H16T16384d128", 1, 16384, 16, 128, 128, 1003,
+                                          s0_std=0.02),
+    "kda_bf16_B4H16T4096d128": Workload("kda_bf16_B4H16T4096d128", 4, 4096, 16, 128, 128, 1004,
+                                        gates="kda"),
+    "gdn_bf16_B4H16T4096d128": Workload("gdn_bf16_B4H16T4096d128", 4, 4096, 16, 128, 128, 1004,
+                                        gates="gdn"),
+    "fwdbwd_bf16_B4H16T4096d128": Workload("fwdbwd_bf16_B4H16T4096d128", 4, 4096, 16, 128, 128, 1005,
+                                           s0_std=0.02, grads=True),
+}
+
+
+def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", gates="channel",
+                s0_std=0.0, grads=False):
+    """Return a dict of CPU tensors.
+
+    ``q``, ``k``, ``v`` have dtype bf16 (or fp32 when ``qkv_dtype == "f32"``);
+    ``q32``, ``k32``, ``v32`` are the same values widened exactly to fp32.
+    Gates, decay, states and upstream gradients are fp32.
+    """
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    shp_k = (B, T, H, dk)
+    shp_v = (B, T, H, dv)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+    q = randn(*shp_k)
+    q = q / q.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    k = randn(*shp_k)
+    k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    v = randn(*shp_v)
+
+    if gates == "gdn":
+        la = F.logsigmoid(randn(B, T, H, 1) + 3.0).expand(shp_k).contiguous()
+    elif decay == "softplus":
+        la = -F.softplus(randn(*shp_k)) * 0.1
+    elif decay == "logsigmoid":
+        la = F.logsigmoid(randn(*shp_k) + 3.0)
+    else:
+        raise ValueError(decay)
+
+    if gates == "channel":
+        b = torch.sigmoid(randn(*shp_k))
+        w = torch.sigmoid(randn(*shp_v))
+    elif gates in ("kda", "gdn"):
+        beta = torch.sigmoid(randn(B, T, H, 1))
+        b = beta.expand(shp_k).contiguous()
+        w = beta.expand(shp_v).contiguous()
+    else:
+        raise ValueError(gates)
+
+    if s0_std > 0:
+        S0 = randn(B, H, dk, dv) * s0_std
+    else:
+        S0 = None
+
+    out = {}
+    if qkv_dtype == "bf16":
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            tb = t.to(torch.bfloat16)
+            out[name] = tb
+            out[name + "32"] = tb.float()
+    elif qkv_dtype == "f32":
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            out[name] = t
+            out[name + "32"] = t
+    else:
+        raise ValueError(qkv_dtype)
+    out.update(log_alpha=la.contiguous(), b=b.contiguous(), w=w.contiguous(), S0=S0)
+
+    if grads:
+        out["dO"] = randn(*shp_v)
+        out["dS_final"] = randn(B, H, dk, dv) * 0.01
+    return out
+
+
+def make_workload(wl: Workload, **override):
+    kw = dict(B=wl.B, T=wl.T, H=wl.H, dk=wl.dk, dv=wl.dv, seed=wl.seed, qkv_dtype=wl.qkv_dtype,
+              decay=wl.decay, gates=wl.gates, s0_std=wl.s0_std, grads=wl.grads)
+    kw.update(override)
+    return make_inputs(**kw)

@@ -1,0 +1,121 @@
+"""fp64 CPU oracle for the Gated DeltaNet-2 operator -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``gdn2_oracle.c`` (plain C,
+double precision, token by token) through ctypes and shares no code with the
+HIP library in ``linear_attention_sequence_gdn2_amd``.
+
+The rule it follows (iplexlaw.co.kr blog on Gated DeltaNet-2, section
+"Independent control on two axes"; the paper abstract in the OpenAlex record of
+arXiv:2605.22791 states the same gate roles): e = b*k on key channels,
+z = w*v on value channels, decay S by diag(exp(log_alpha)) first, read
+r = S^T e, write S += k (z - r)^T, and the query reads the updated state.
+
+Pins (see tests/test_oracle_pins.py): KDA and Gated DeltaNet reductions,
+read-after-write, brute-force transition products, causal linear attention,
+pure decay, finite-difference gradients.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn2_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn2_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, baseline x86-64, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.gdn2_oracle_fwd.argtypes = [I, I, I, I, I] + [P] * 9 + [I]
+        lib.gdn2_oracle_fwd.restype = I
+        lib.gdn2_oracle_bwd.argtypes = [I, I, I, I, I] + [P] * 16 + [I]
+        lib.gdn2_oracle_bwd.restype = I
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(q, k, v, log_alpha, b, w, S0=None, nthreads=None):
+    """Token-by-token forward.  Token tensors are [B,T,H,D]; S0 is [B,H,dk,dv] or None.
+
+    Returns (o [B,T,H,dv], S_final [B,H,dk,dv]) as float64 numpy arrays.
+    """
+    q, k, v, la, bb, ww, s0 = (_f64(t) for t in (q, k, v, log_alpha, b, w, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and la.shape == q.shape and bb.shape == q.shape
+    assert v.shape == (B, T, H, dv) and ww.shape == v.shape
+    if s0 is not None:
+        assert s0.shape == (B, H, dk, dv)
+    o = np.empty((B, T, H, dv), np.float64)
+    sf = np.empty((B, H, dk, dv), np.float64)
+    rc = _load().gdn2_oracle_fwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bb),
+                                 _ptr(ww), _ptr(s0), _ptr(o), _ptr(sf),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("gdn2_oracle_fwd failed (%d)" % rc)
+    return o, sf
+
+
+def bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, nthreads=None):
+    """Reverse-mode gradients of sum(dO*o) + sum(dS_final*S_final).
+
+    Returns a dict with dq, dk, dv, dlog_alpha, db, dw (input shapes) and dS0.
+    """
+    q, k, v, la, bb, ww, s0, do, dsf = (_f64(t) for t in (q, k, v, log_alpha, b, w, S0, dO, dS_final))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert do.shape == (B, T, H, dv)
+    out = {
+        "dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(v),
+        "dlog_alpha": np.empty_like(la), "db": np.empty_like(bb), "dw": np.empty_like(ww),
+        "dS0": np.empty((B, H, dk, dv), np.float64),
+    }
+    rc = _load().gdn2_oracle_bwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bb),
+                                 _ptr(ww), _ptr(s0), _ptr(do), _ptr(dsf),
+                                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["dlog_alpha"]), _ptr(out["db"]), _ptr(out["dw"]),
+                                 _ptr(out["dS0"]), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("gdn2_oracle_bwd failed (%d)" % rc)
+    return out
