@@ -1,0 +1,114 @@
+/*
+ * gdn2.h -- C ABI of libgdn2.so, the MI355X (gfx950) Gated DeltaNet-2 chunkwise operator.
+ *
+ * The operator (iplexlaw.co.kr blog on Gated DeltaNet-2, section "Independent
+ * control on two axes"; the paper abstract, OpenAlex record of arXiv:2605.22791):
+ * per (batch, head) a state S of dk x dv values (key axis = rows) is carried
+ * through the tokens.  For token t
+ *
+ *     e = b_t * k_t              erase gate on the key channels
+ *     z = w_t * v_t              write gate on the value channels
+ *     Sbar = diag(exp(log_alpha_t)) S        channel-wise decay on the key axis
+ *     S = Sbar + k_t (z - Sbar^T e)^T        read through e, write along k
+ *     o_t = S^T q_t                          the query reads the updated state
+ *
+ * The library evaluates this rule in the chunkwise WY form with 64-token
+ * chunks (same blog, section "Token path and parallel training": cumulative
+ * channel decay absorbed into asymmetric erase factors, a triangular solve and
+ * dense matrix products per chunk, fp32 decay, state and solve).  The backward
+ * pass is the gate-aware adjoint (gradients flow through the gated e and z).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *   row-major and 16-byte aligned.  The library allocates nothing, frees
+ *   nothing and keeps no global mutable state; calls on different streams may
+ *   run concurrently.
+ * - Token tensors are [B, T, H, D]: q, k, log_alpha, b and the key-side
+ *   gradients use D = dk; v, w, o and the value-side gradients use D = dv.
+ *   States are [B, H, dk, dv] fp32 (key channel = row).
+ * - q, k, v have dtype shape->qkv_dtype (fp32 or bf16).  log_alpha, b, w, S0,
+ *   dO, dS_final and every output are fp32.
+ * - log_alpha is the natural log of the per-channel decay (alpha = exp).  b and
+ *   w are gate VALUES (after any sigmoid), not logits, and are not clamped.
+ *   Gradients are taken with respect to exactly these inputs.  q is not scaled.
+ * - Any T >= 1 is accepted; a ragged tail chunk is padded internally with
+ *   identity tokens (k = 0, log_alpha = 0) that leave the state unchanged.
+ * - Supported sizes: B, H >= 1, T >= 1, chunk == 64, dk and dv in {32, 64, 128},
+ *   B*T*H*max(dk,dv) < 2^31.
+ * - Numerical range: within one 64-token chunk the cumulative log-decay of a
+ *   key channel must stay above -80 (the factorised decay exp(-G) is formed in
+ *   fp32).  Outside that range results are undefined (non-finite values).
+ * - Execution is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  Results are valid once the stream has reached the call.
+ * - Errors: arguments are checked on the host before any launch; on failure
+ *   nothing is launched and nothing is written.  GDN2_ERR_HIP reports a launch
+ *   failure (hipGetLastError after the launch).  No C++ exception crosses the ABI.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN2_OK = 0,
+    GDN2_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, misaligned pointer */
+    GDN2_ERR_UNSUPPORTED = 2,   /* valid request outside the supported sizes/dtypes */
+    GDN2_ERR_WORKSPACE = 3,     /* workspace smaller than *_workspace_size() or NULL */
+    GDN2_ERR_HIP = 4            /* the HIP runtime reported an error at launch */
+} gdn2_status;
+
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
+
+typedef struct {
+    int B, T, H;      /* batch, tokens, heads */
+    int dk, dv;       /* key and value head dimensions */
+    int chunk;        /* must be 64 */
+    int qkv_dtype;    /* a gdn2_dtype: dtype of q, k and v */
+} gdn2_shape;
+
+/* Bytes of device workspace gdn2_chunk_fwd needs (0 for every supported shape);
+ * (size_t)-1 if the shape is invalid. */
+size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);
+
+/* Forward pass: o [B,T,H,dv] and the final state S_final [B,H,dk,dv].
+ * S0 == NULL means a zero start state; S_final == NULL means it is not wanted.
+ * workspace may be NULL when gdn2_chunk_fwd_workspace_size() is 0. */
+int gdn2_chunk_fwd(const gdn2_shape *shape,
+                   const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *b, const float *w,
+                   const float *S0,
+                   float *o, float *S_final,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace gdn2_chunk_bwd needs: two fp32 states per chunk per
+ * (batch, head), i.e. 2 * B*H*ceil(T/64)*dk*dv*4 bytes; (size_t)-1 if invalid. */
+size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape);
+
+/* Gate-aware backward pass of loss = sum(dO * o) + sum(dS_final * S_final):
+ * writes dq, dk, dlog_alpha, db [B,T,H,dk], dv, dw [B,T,H,dv] and, unless
+ * dS0 == NULL, dS0 [B,H,dk,dv].  S0 == NULL and dS_final == NULL mean zeros.
+ * The forward state is recomputed from the inputs; nothing from a previous
+ * gdn2_chunk_fwd call is needed.  The workspace (see above) is overwritten. */
+int gdn2_chunk_bwd(const gdn2_shape *shape,
+                   const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *b, const float *w,
+                   const float *S0,
+                   const float *dO, const float *dS_final,
+                   float *dq, float *dk, float *dv,
+                   float *dlog_alpha, float *db, float *dw,
+                   float *dS0,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable description of a gdn2_status value. */
+const char *gdn2_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

@@ -1,0 +1,147 @@
+"""ctypes binding of libgdn2.so (the C ABI in include/gdn2.h).
+
+Argument marshalling only: checks dtypes, devices and contiguity, allocates
+the outputs and the workspace with torch on the inputs' device, and passes raw
+device pointers plus the current HIP stream.  Every step of the operator runs
+in the HIP kernels of libgdn2.so; there is no fallback.  If the library has
+not been built, or the tensors are not on a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+
+GDN2_F32 = 0
+GDN2_BF16 = 1
+STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3: "GDN2_ERR_WORKSPACE",
+          4: "GDN2_ERR_HIP"}
+EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
+           "gdn2_chunk_bwd_workspace_size", "gdn2_strerror"]
+
+
+class Gdn2Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("chunk", ctypes.c_int), ("qkv_dtype", ctypes.c_int)]
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Load libgdn2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn2.so is not built (%s); run python -m "
+                               "linear_attention_sequence_gdn2_amd.build" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        SP = ctypes.POINTER(Gdn2Shape)
+        lib.gdn2_chunk_fwd.argtypes = [SP] + [P] * 9 + [P, ctypes.c_size_t, P]
+        lib.gdn2_chunk_fwd.restype = ctypes.c_int
+        lib.gdn2_chunk_bwd.argtypes = [SP] + [P] * 16 + [P, ctypes.c_size_t, P]
+        lib.gdn2_chunk_bwd.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_workspace_size.argtypes = [SP]
+        lib.gdn2_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+        lib.gdn2_chunk_bwd_workspace_size.argtypes = [SP]
+        lib.gdn2_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.gdn2_strerror.argtypes = [ctypes.c_int]
+        lib.gdn2_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(code):
+    if code != 0:
+        raise Gdn2Error(code, load().gdn2_strerror(code).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_shape(B, T, H, dk, dv, qkv_dtype):
+    return Gdn2Shape(B, T, H, dk, dv, 64, GDN2_BF16 if qkv_dtype == torch.bfloat16 else GDN2_F32)
+
+
+def _validate(q, k, v, log_alpha, b, w, extra=()):
+    if not q.is_cuda:
+        raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % q.device)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    for name, t, shp, dt in (("k", k, (B, T, H, dk), q.dtype), ("v", v, (B, T, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                             ("b", b, (B, T, H, dk), torch.float32), ("w", w, (B, T, H, dv), torch.float32)):
+        if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device:
+            raise ValueError("gdn2: %s has shape %s dtype %s device %s, expected %s %s %s"
+                             % (name, tuple(t.shape), t.dtype, t.device, shp, dt, q.device))
+    for t in (q, k, v, log_alpha, b, w) + tuple(x for x in extra if x is not None):
+        if not t.is_contiguous():
+            raise ValueError("gdn2: tensors must be contiguous")
+    return B, T, H, dk, dv
+
+
+def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
+    """o [B,T,H,dv] fp32 and S_final [B,H,dk,dv] fp32 (None if not wanted)."""
+    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0,))
+    if S0 is not None and (tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("gdn2: S0 must be float32 [B,H,dk,dv]")
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    ws_bytes = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(shape))
+    if ws_bytes == ctypes.c_size_t(-1).value:
+        raise Gdn2Error(2, "unsupported shape")
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check(lib.gdn2_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                              _ptr(w), _ptr(S0), _ptr(o), _ptr(sf), _ptr(ws), ws_bytes, _stream(q.device)))
+    return o, sf
+
+
+def bwd_workspace_bytes(B, T, H, dk, dv, qkv_dtype):
+    shape = make_shape(B, T, H, dk, dv, qkv_dtype)
+    return load().gdn2_chunk_bwd_workspace_size(ctypes.byref(shape))
+
+
+def bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, want_dS0=True, workspace=None):
+    """Gradients of sum(dO*o) + sum(dS_final*S_final): dict of fp32 tensors
+    dq, dk, dv, dlog_alpha, db, dw (input shapes) and dS0 (or None)."""
+    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0, dO, dS_final))
+    if tuple(dO.shape) != (B, T, H, dv) or dO.dtype != torch.float32:
+        raise ValueError("gdn2: dO must be float32 [B,T,H,dv]")
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
+            raise ValueError("gdn2: %s must be float32 [B,H,dk,dv]" % name)
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    dev = q.device
+    out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
+    out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    out["dw"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    out["dS0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    ws_bytes = lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(shape))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(lib.gdn2_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                              _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                              _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]), _ptr(out["dw"]),
+                              _ptr(out["dS0"]), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out

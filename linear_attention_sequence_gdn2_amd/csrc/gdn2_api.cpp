@@ -1,0 +1,128 @@
+// gdn2_api.cpp -- the C ABI of libgdn2.so: argument checks, workspace sizing and
+// kernel dispatch.  No allocation, no global mutable state, no exceptions.
+#include <stdint.h>
+#include <stddef.h>
+
+#include "gdn2.h"
+#include "gdn2_kernels.h"
+
+namespace {
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const gdn2_shape *s) {
+    if (!s) return GDN2_ERR_INVALID_ARG;
+    if (s->B < 1 || s->T < 1 || s->H < 1 || s->dk < 1 || s->dv < 1) return GDN2_ERR_INVALID_ARG;
+    if (s->chunk != 64) return GDN2_ERR_UNSUPPORTED;
+    if (!dim_ok(s->dk) || !dim_ok(s->dv)) return GDN2_ERR_UNSUPPORTED;
+    if (s->qkv_dtype != GDN2_F32 && s->qkv_dtype != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    const int dmax = s->dk > s->dv ? s->dk : s->dv;
+    const unsigned long long n = (unsigned long long)s->B * s->T * s->H * dmax;
+    if (n >= (1ull << 31)) return GDN2_ERR_UNSUPPORTED;
+    // grid size (workgroups) must fit in 32 bits; chunk-state workspace indexing uses size_t
+    if ((unsigned long long)s->B * s->H * s->dv / 16 >= (1ull << 31)) return GDN2_ERR_UNSUPPORTED;
+    return GDN2_OK;
+}
+
+int nchunks(const gdn2_shape *s) { return (s->T + 63) / 64; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn2_strerror(int status) {
+    switch (status) {
+        case GDN2_OK: return "success";
+        case GDN2_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or misaligned pointer)";
+        case GDN2_ERR_UNSUPPORTED: return "unsupported shape or dtype (chunk must be 64, dk/dv in {32,64,128})";
+        case GDN2_ERR_WORKSPACE: return "workspace missing or smaller than the required size";
+        case GDN2_ERR_HIP: return "HIP runtime error at kernel launch";
+        default: return "unknown gdn2 status";
+    }
+}
+
+size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return (size_t)-1;
+    return 0;
+}
+
+int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *b, const float *w, const float *S0, float *o,
+                   float *S_final, void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
+
+    gdn2::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_alpha; a.bg = b; a.wg = w;
+    a.S0 = S0; a.o = o; a.S_final = S_final; a.states = nullptr;
+    a.B = shape->B; a.T = shape->T; a.H = shape->H; a.dv = shape->dv;
+    const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
+    a.nvt = shape->dv / vt;
+    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, false,
+                                          reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return (size_t)-1;
+    return 2 * (size_t)shape->B * shape->H * nchunks(shape) * (size_t)shape->dk * shape->dv * sizeof(float);
+}
+
+int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *b, const float *w, const float *S0,
+                   const float *dO, const float *dS_final, float *dq, float *dk, float *dv,
+                   float *dlog_alpha, float *db, float *dw, float *dS0, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv || !dlog_alpha || !db || !dw)
+        return GDN2_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_alpha, db, dw, dS0, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
+    const size_t need = gdn2_chunk_bwd_workspace_size(shape);
+    if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+
+    const size_t half = need / 2 / sizeof(float);
+    float *states = reinterpret_cast<float *>(workspace);
+    float *dstates = states + half;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const bool bf16 = shape->qkv_dtype == GDN2_BF16;
+
+    // 1) forward state sweep: start state of every chunk
+    gdn2::FwdArgs f{};
+    f.q = q; f.k = k; f.v = v;
+    f.la = log_alpha; f.bg = b; f.wg = w;
+    f.S0 = S0; f.o = nullptr; f.S_final = nullptr; f.states = states;
+    f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv;
+    const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
+    f.nvt = shape->dv / vt;
+    hipError_t e = gdn2::launch_fwd(f, shape->dk, vt, bf16, true, hs);
+    if (e != hipSuccess) return GDN2_ERR_HIP;
+
+    gdn2::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_alpha; a.bg = b; a.wg = w;
+    a.dO = dO; a.dS_final = dS_final;
+    a.states = states; a.dstates = dstates;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw; a.dS0 = dS0;
+    a.B = shape->B; a.T = shape->T; a.H = shape->H; a.DV = shape->dv;
+    a.nvt = f.nvt;
+    // 2) reverse sweep over chunks: gradient w.r.t. every chunk's end state, and dS0
+    e = gdn2::launch_bwd_reverse(a, shape->dk, vt, bf16, hs);
+    if (e != hipSuccess) return GDN2_ERR_HIP;
+    // 3) chunk-parallel gradients of all token inputs
+    e = gdn2::launch_bwd_chunk(a, shape->dk, bf16, hs);
+    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// gdn2_device.h -- gfx950 building blocks shared by the GDN-2 kernels.
+//
+// MFMA operand layouts used throughout (wave of 64 lanes, lane l, r = l % 16,
+// g = l / 16), checked on gfx950:
+//   v_mfma_f32_16x16x32_bf16   A: lane holds A[r][8g + i], i < 8
+//                              B: lane holds B[8g + i][r]
+//                              D: lane holds D[4g + i][r], i < 4
+//   v_mfma_f32_16x16x16_bf16   A: A[r][4g + i], B: B[4g + i][r], D: D[4g + i][r]
+// Only the sum over the contraction index matters, so any consistent
+// permutation of it between A and B is allowed; the kernels use that to feed a
+// D fragment of a transposed product straight back in as an A operand.
+//
+// Precision: products whose error reaches the output directly use a split
+// ("hi + lo") bf16 representation of each fp32 operand, x = hi + lo with
+// hi = bf16(x), lo = bf16(x - hi), and three MFMAs (lo*hi + hi*lo + hi*hi),
+// which carries about 16 significant bits; accumulation is fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kChunk = 64;
+constexpr int kThreads = 256;
+
+struct Split8 {
+    bf16x8 hi, lo;
+};
+struct Split4 {
+    bf16x4 hi, lo;
+};
+
+__device__ __forceinline__ f32x4 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// split-bf16 product: about 16 significant bits per operand
+__device__ __forceinline__ f32x4 mfma32x3(const Split8 &a, const Split8 &b, f32x4 c) {
+    c = mfma32(a.lo, b.hi, c);
+    c = mfma32(a.hi, b.lo, c);
+    return mfma32(a.hi, b.hi, c);
+}
+
+__device__ __forceinline__ f32x4 mfma16x3(const Split4 &a, const Split4 &b, f32x4 c) {
+    c = mfma16(a.lo, b.hi, c);
+    c = mfma16(a.hi, b.lo, c);
+    return mfma16(a.hi, b.hi, c);
+}
+
+__device__ __forceinline__ void split1(float x, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+__device__ __forceinline__ Split8 split8(const float *x) {
+    Split8 s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __bf16 h, l;
+        split1(x[i], h, l);
+        s.hi[i] = h;
+        s.lo[i] = l;
+    }
+    return s;
+}
+
+__device__ __forceinline__ Split4 split4(const f32x4 &x) {
+    Split4 s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __bf16 h, l;
+        split1(x[i], h, l);
+        s.hi[i] = h;
+        s.lo[i] = l;
+    }
+    return s;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// value of lane (l - n) inside the same 16-lane row, 0 for the first n lanes of a row
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "row_shr");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0x110 + N, 0xf, 0xf, true));
+}
+
+// inclusive prefix sum over the 16 lanes of each row
+__device__ __forceinline__ float row_scan16(float v) {
+    v += row_shr<1>(v);
+    v += row_shr<2>(v);
+    v += row_shr<4>(v);
+    v += row_shr<8>(v);
+    return v;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// 8 consecutive elements of a token row, widened to fp32
+template <bool BF16>
+__device__ __forceinline__ void load8(const void *base, size_t off, bool valid, float *out) {
+    if (BF16) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (valid) u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        }
+    } else {
+        float4 a = make_float4(0, 0, 0, 0), b = make_float4(0, 0, 0, 0);
+        if (valid) {
+            const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
+            a = p[0];
+            b = p[1];
+        }
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void *base, size_t off, bool valid) {
+    if (!valid) return 0.f;
+    if (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(base)[off]);
+    return reinterpret_cast<const float *>(base)[off];
+}
+
+// Map the launch index to a logical work index so that consecutive logical
+// indices (the value tiles of one (batch, head)) land on the same XCD and share
+// its L2: the hardware deals workgroups to the 8 XCDs round-robin.
+__device__ __forceinline__ int xcd_swizzle(int bid, int nb) {
+    if (nb % 8 != 0) return bid;
+    return (bid % 8) * (nb / 8) + bid / 8;
+}
+
+}  // namespace gdn2

@@ -1,0 +1,42 @@
+// gdn2_kernels.h -- launch interface between the C ABI (gdn2_api.cpp) and the
+// HIP kernels.  Internal to libgdn2.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn2 {
+
+// Arguments of the chunked forward sweep.  Token tensors are [B,T,H,D]
+// contiguous; states [B,H,dk,dv] fp32; chunk states [B,H,NC,dk,dv] fp32.
+struct FwdArgs {
+    const void *q, *k, *v;          // qkv dtype
+    const float *la, *bg, *wg;      // log_alpha, b, w
+    const float *S0;                // may be null (zeros)
+    float *o;                       // [B,T,H,dv] (forward) or unused (state sweep)
+    float *S_final;                 // may be null
+    float *states;                  // chunk-start states (state sweep) or null
+    int B, T, H, dv;
+    int nvt;                        // value tiles per (b, h) = dv / value-tile width
+};
+
+// Arguments of the backward kernels.
+struct BwdArgs {
+    const void *q, *k, *v;
+    const float *la, *bg, *wg;
+    const float *dO, *dS_final;     // dS_final may be null
+    const float *states;            // [B,H,NC,dk,dv] chunk-start states
+    float *dstates;                 // [B,H,NC,dk,dv] gradient w.r.t. chunk-end states
+    float *dq, *dk, *dv, *dla, *db, *dw, *dS0;
+    int B, T, H, DV;
+    int nvt;
+};
+
+// Value-tile width the forward sweep uses for this shape (16, 32 or 64).
+int fwd_value_tile(int B, int H, int dk, int dv);
+
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool state_sweep, hipStream_t st);
+hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, int vt, bool bf16, hipStream_t st);
+hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, hipStream_t st);
+
+}  // namespace gdn2

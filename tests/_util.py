@@ -1,0 +1,28 @@
+"""Test helpers: error measures and device transfer (no operator arithmetic)."""
+import numpy as np
+import torch
+
+
+def rel_err(x, ref):
+    """max |x - ref| / max |ref| over the whole tensor (max-norm relative error).
+
+    Elementwise relative error is undefined where the reference is near zero,
+    so the error is normalised by the tensor's largest reference magnitude."""
+    x = x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in the GPU result"
+    return float(np.max(np.abs(x - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def to_dev(inp, device="cuda"):
+    """Move the generator's CPU tensors to the GPU (q/k/v keep their dtype)."""
+    out = {}
+    for key in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final"):
+        t = inp.get(key)
+        out[key] = None if t is None else t.to(device).contiguous()
+    return out
+
+
+def oracle_args(inp):
+    return [inp["q32"], inp["k32"], inp["v32"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"]]
