@@ -116,9 +116,10 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     a.states = states; a.dstates = dstates;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw; a.dS0 = dS0;
     a.B = shape->B; a.T = shape->T; a.H = shape->H; a.DV = shape->dv;
-    a.nvt = f.nvt;
+    const int vt2 = gdn2::bwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
+    a.nvt = shape->dv / vt2;
     // 2) reverse sweep over chunks: gradient w.r.t. every chunk's end state, and dS0
-    e = gdn2::launch_bwd_reverse(a, shape->dk, vt, bf16, hs);
+    e = gdn2::launch_bwd_reverse(a, shape->dk, vt2, bf16, hs);
     if (e != hipSuccess) return GDN2_ERR_HIP;
     // 3) chunk-parallel gradients of all token inputs
     e = gdn2::launch_bwd_chunk(a, shape->dk, bf16, hs);

@@ -1,0 +1,131 @@
+// gdn2_chunk.h -- per-chunk building blocks shared by the forward and backward kernels.
+//
+// A workgroup has 4 waves; wave w owns tokens 16w..16w+15 of a 64-token chunk
+// (token = 16w + r, r = lane % 16).  Key-side element work keeps, per lane,
+// NE = DK/4 channels of its token.
+#pragma once
+
+#include "gdn2_device.h"
+
+namespace gdn2 {
+
+// Inclusive cumulative sum of log2-decay over the chunk's tokens, per key
+// channel, in fp32 (blog on Gated DeltaNet-2, section "Token path and parallel
+// training": the cumulative channel decay is formed in fp32).
+// x[e]: this lane's log2-decay values (already multiplied by log2(e));
+// on return x[e] = G (inclusive prefix over the chunk), tot[e] = chunk total.
+// ch(e) maps element index -> channel.  sTot: 4*DK floats of LDS.
+// Contains one workgroup barrier.
+template <int NE, int DK, typename ChanFn>
+__device__ __forceinline__ void chunk_scan(float (&x)[NE], float (&tot)[NE], float *sTot, int w, int r,
+                                           ChanFn ch) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) x[e] = row_scan16(x[e]);
+    if (r == 15) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) sTot[w * DK + ch(e)] = x[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int c = ch(e);
+        const float t0 = sTot[c], t1 = sTot[DK + c], t2 = sTot[2 * DK + c], t3 = sTot[3 * DK + c];
+        const float pre = (w > 0 ? t0 : 0.f) + (w > 1 ? t1 : 0.f) + (w > 2 ? t2 : 0.f);
+        x[e] += pre;
+        tot[e] = (t0 + t1) + (t2 + t3);
+    }
+}
+
+// T = (I + A)^-1 for the strictly lower 64x64 A of a chunk (triangular solve
+// of the WY form, fp32 values).  sA: A in fp32 [64][PA] (only the strictly lower
+// 16x16 blocks on or below the diagonal are read); sT: fp32 [64][PA], whose
+// strictly upper 16x16 blocks must already be zero.  On return sT holds T.
+// Diagonal blocks by forward substitution (one column per lane), off-diagonal
+// blocks by distance: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, on MFMA with
+// split-bf16 operands.  Contains 4 workgroup barriers; sA is not written.
+template <int PA>
+__device__ __forceinline__ void solve_T(const float *sA, float *sT, int w, int r, int g) {
+    {
+        const float *Ab = &sA[(16 * w) * PA + 16 * w];
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = (i == r) ? 1.f : 0.f;
+#pragma unroll
+            for (int kx = 0; kx < i; ++kx) s -= Ab[i * PA + kx] * t[kx];
+            t[i] = s;
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const float val = g == 0 ? t[ii] : g == 1 ? t[4 + ii] : g == 2 ? t[8 + ii] : t[12 + ii];
+            sT[(16 * w + 4 * g + ii) * PA + 16 * w + r] = val;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        if (w >= d) {
+            const int I = w, J = w - d;
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+            for (int K = J; K < I; ++K) {
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(&sA[(16 * I + r) * PA + 16 * K + 4 * g]);
+                f32x4 tv;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) tv[ii] = sT[(16 * K + 4 * g + ii) * PA + 16 * J + r];
+                Y = mfma16x3(split4(av), split4(tv), Y);
+            }
+            const f32x4 tiv = *reinterpret_cast<const f32x4 *>(&sT[(16 * I + r) * PA + 16 * I + 4 * g]);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 R = mfma16x3(split4(tiv), split4(-Y), zero);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) sT[(16 * I + 4 * g + ii) * PA + 16 * J + r] = R[ii];
+        }
+        __syncthreads();
+    }
+}
+
+// Split-bf16 MFMA fragment with the "4-group" contraction order: slots 0..3 are
+// taken from p0[0..3] and slots 4..7 from p1[0..3].
+__device__ __forceinline__ Split8 frag_2x4(const __bf16 *hi0, const __bf16 *hi1, const __bf16 *lo0,
+                                           const __bf16 *lo1) {
+    Split8 f;
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(hi0);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(hi1);
+    const bf16x4 c = *reinterpret_cast<const bf16x4 *>(lo0);
+    const bf16x4 d = *reinterpret_cast<const bf16x4 *>(lo1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.hi[i] = a[i];
+        f.hi[4 + i] = b[i];
+        f.lo[i] = c[i];
+        f.lo[4 + i] = d[i];
+    }
+    return f;
+}
+
+__device__ __forceinline__ Split8 frag_8(const __bf16 *hi, const __bf16 *lo) {
+    Split8 f;
+    f.hi = *reinterpret_cast<const bf16x8 *>(hi);
+    f.lo = *reinterpret_cast<const bf16x8 *>(lo);
+    return f;
+}
+
+__device__ __forceinline__ Split8 join(const Split4 &a, const Split4 &b) {
+    Split8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.hi[i] = a.hi[i];
+        f.hi[4 + i] = b.hi[i];
+        f.lo[i] = a.lo[i];
+        f.lo[4 + i] = b.lo[i];
+    }
+    return f;
+}
+
+// 8 fp32 values -> split fragment
+__device__ __forceinline__ Split8 split8v(const f32x4 &a, const f32x4 &b) {
+    const float t[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return split8(t);
+}
+
+}  // namespace gdn2

@@ -85,6 +85,114 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     store_state_lds();
     __syncthreads();
 
+    // Raw inputs of one chunk held in registers: the loads for chunk c + 1 are
+    // issued once chunk c's inputs have been consumed, so their latency hides
+    // behind the rest of chunk c's work.
+    struct Raw {
+        uint4 q[NKS], k[NKS];
+        float4 la[NKS][2], bg[NKS][2];
+        float4 qx[NKS][2], kx[NKS][2];   // fp32 q/k when the inputs are fp32
+        float w[NVT][4];
+        uint32_t v[NVT][4];               // raw bits (bf16 in the low half, or fp32)
+        bool vk;                          // this lane's key-side token exists
+        uint32_t vmask;                   // bit (4n+i): value-side token exists
+
+        // Loads are unconditional, from addresses clamped into the tensors, so
+        // that no branch (and no early wait) separates them; tokens past the
+        // end are zeroed when the registers are unpacked.
+        __device__ __forceinline__ void issue(const FwdArgs &a, int t0, int T, int w_, int r_, int g_,
+                                              size_t baseK, size_t tokK, size_t baseV, size_t tokV) {
+            const int tk = t0 + 16 * w_ + r_;
+            vk = tk < T;
+            const size_t offk = baseK + (size_t)(vk ? tk : T - 1) * tokK + 8 * g_;
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const size_t o = offk + 32 * j;
+                if (BF16) {
+                    if (OUT) q[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + o);
+                    k[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.k) + o);
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        if (OUT) qx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + o)[hh];
+                        kx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.k) + o)[hh];
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    la[j][hh] = reinterpret_cast<const float4 *>(a.la + o)[hh];
+                    bg[j][hh] = reinterpret_cast<const float4 *>(a.bg + o)[hh];
+                }
+            }
+            vmask = 0;
+#pragma unroll
+            for (int n = 0; n < NVT; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tv = t0 + 16 * w_ + 4 * g_ + i;
+                    const bool vv = tv < T;
+                    vmask |= vv ? (1u << (4 * n + i)) : 0u;
+                    const size_t off = baseV + (size_t)(vv ? tv : T - 1) * tokV + 16 * n + r_;
+                    w[n][i] = a.wg[off];
+                    if (BF16) v[n][i] = reinterpret_cast<const uint16_t *>(a.v)[off];
+                    else v[n][i] = reinterpret_cast<const uint32_t *>(a.v)[off];
+                }
+        }
+
+        __device__ __forceinline__ void unpack(float (&qf)[NKS][8], float (&kf)[NKS][8], float (&laf)[NKS][8],
+                                               float (&bgf)[NKS][8], float (&z)[NVT][4]) const {
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                if (BF16) {
+                    const uint32_t qw[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+                    const uint32_t kw[4] = {k[j].x, k[j].y, k[j].z, k[j].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (OUT) {
+                            qf[j][2 * i] = __builtin_bit_cast(float, qw[i] << 16);
+                            qf[j][2 * i + 1] = __builtin_bit_cast(float, qw[i] & 0xffff0000u);
+                        }
+                        kf[j][2 * i] = __builtin_bit_cast(float, kw[i] << 16);
+                        kf[j][2 * i + 1] = __builtin_bit_cast(float, kw[i] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        if (OUT) {
+                            qf[j][4 * hh + 0] = qx[j][hh].x; qf[j][4 * hh + 1] = qx[j][hh].y;
+                            qf[j][4 * hh + 2] = qx[j][hh].z; qf[j][4 * hh + 3] = qx[j][hh].w;
+                        }
+                        kf[j][4 * hh + 0] = kx[j][hh].x; kf[j][4 * hh + 1] = kx[j][hh].y;
+                        kf[j][4 * hh + 2] = kx[j][hh].z; kf[j][4 * hh + 3] = kx[j][hh].w;
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    laf[j][4 * hh + 0] = la[j][hh].x; laf[j][4 * hh + 1] = la[j][hh].y;
+                    laf[j][4 * hh + 2] = la[j][hh].z; laf[j][4 * hh + 3] = la[j][hh].w;
+                    bgf[j][4 * hh + 0] = bg[j][hh].x; bgf[j][4 * hh + 1] = bg[j][hh].y;
+                    bgf[j][4 * hh + 2] = bg[j][hh].z; bgf[j][4 * hh + 3] = bg[j][hh].w;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (OUT) qf[j][i] = vk ? qf[j][i] : 0.f;
+                    kf[j][i] = vk ? kf[j][i] : 0.f;
+                    laf[j][i] = vk ? laf[j][i] : 0.f;
+                    bgf[j][i] = vk ? bgf[j][i] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NVT; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float vf = BF16 ? __builtin_bit_cast(float, v[n][i] << 16) : __builtin_bit_cast(float, v[n][i]);
+                    z[n][i] = ((vmask >> (4 * n + i)) & 1u) ? w[n][i] * vf : 0.f;
+                }
+        }
+    };
+    Raw raw;
+    raw.issue(a, 0, T, w, r, g, baseK, tokK, baseV, tokV);
+
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * kChunk;
         if (STATES) {
@@ -97,28 +205,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             }
         }
 
-        // ---- load: key side in token-row layout, value side in D layout ----
-        const int tk = t0 + 16 * w + r;
-        const bool vk = tk < T;
-        const size_t offk = baseK + (size_t)tk * tokK + 8 * g;
-        float qf[NKS][8], kf[NKS][8], laf[NKS][8], bgf[NKS][8];
-#pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-            if (OUT) load8<BF16>(a.q, offk + 32 * j, vk, qf[j]);
-            load8<BF16>(a.k, offk + 32 * j, vk, kf[j]);
-            load8<false>(a.la, offk + 32 * j, vk, laf[j]);
-            load8<false>(a.bg, offk + 32 * j, vk, bgf[j]);
-        }
-        float z[NVT][4];
-#pragma unroll
-        for (int n = 0; n < NVT; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tv = t0 + 16 * w + 4 * g + i;
-                const bool vv = tv < T;
-                const size_t off = baseV + (size_t)tv * tokV + 16 * n + r;
-                z[n][i] = load1<false>(a.wg, off, vv) * load1<BF16>(a.v, off, vv);
-            }
+        // ---- this chunk's inputs (loaded during the previous chunk) ----
+        float qf[NKS][8], kf[NKS][8], laf[NKS][8], bgf[NKS][8], z[NVT][4];
+        raw.unpack(qf, kf, laf, bgf, z);
 
         // ---- cumulative log2-decay over the chunk (fp32) ----
         float G[NKS][8];
@@ -182,6 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             *reinterpret_cast<bf16x8 *>(&sR1[(16 * w + r) * PK + 32 * j + 8 * g]) = ks.hi;
             *reinterpret_cast<bf16x8 *>(&sR1[R1 + (16 * w + r) * PK + 32 * j + 8 * g]) = ks.lo;
         }
+        if (c + 1 < NC) raw.issue(a, t0 + kChunk, T, w, r, g, baseK, tokK, baseV, tokV);
         __syncthreads();
 
         // ---- A^T and P^T for this wave's query rows (keys from LDS) ----

@@ -34,6 +34,8 @@ struct BwdArgs {
 
 // Value-tile width the forward sweep uses for this shape (16, 32 or 64).
 int fwd_value_tile(int B, int H, int dk, int dv);
+// Value-tile width of the backward reverse sweep (16 or 32).
+int bwd_value_tile(int B, int H, int dk, int dv);
 
 hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool state_sweep, hipStream_t st);
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, int vt, bool bf16, hipStream_t st);

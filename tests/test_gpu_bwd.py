@@ -1,0 +1,53 @@
+"""GPU parity of gdn2_chunk_bwd (gate-aware backward) against the fp64 oracle's
+reverse recurrence, through the C ABI.
+
+Tolerance: max-norm relative error 5e-3 per gradient tensor (tests/_util.rel_err).
+The oracle's own gradients are pinned by finite differences in test_oracle_pins."""
+import pytest
+import torch
+
+import oracle
+import linear_attention_sequence_gdn2_amd as gdn2
+from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_inputs, make_workload
+from _util import oracle_args, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+NAMES = ["dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"]
+
+
+def _run(inp, tol=TOL, with_dsf=True):
+    d = to_dev(inp)
+    dsf = d["dS_final"] if with_dsf else None
+    g = gdn2.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"], dsf)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(*oracle_args(inp), inp["dO"], inp["dS_final"] if with_dsf else None)
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e < tol}
+    assert not bad, bad
+
+
+def test_tiny_f32_workload_grads():
+    wl = WORKLOADS["tiny_f32_B1H2T128d32"]
+    _run(make_workload(wl, grads=True, s0_std=0.02))
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,qkv,s0,dsf", [
+    (1, 1, 1, 32, 32, "f32", 0.5, True),
+    (1, 64, 2, 64, 64, "f32", 0.5, False),
+    (2, 65, 1, 128, 128, "f32", 0.5, True),
+    (1, 200, 3, 128, 128, "bf16", 0.02, True),
+    (2, 333, 2, 64, 128, "bf16", 0.0, True),
+    (1, 130, 2, 128, 32, "bf16", 0.1, False),
+    (3, 257, 2, 32, 64, "f32", 0.1, True),
+])
+def test_small_shapes_grads(B, T, H, dk, dv, qkv, s0, dsf):
+    inp = make_inputs(B, T, H, dk, dv, seed=7 * B + T + dk + 3 * dv, qkv_dtype=qkv, s0_std=s0, grads=True)
+    _run(inp, with_dsf=dsf)
+
+
+def test_full_size_fwdbwd_workload():
+    wl = WORKLOADS["fwdbwd_bf16_B4H16T4096d128"]
+    _run(make_workload(wl))
