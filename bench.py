@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN-2 chunkwise operator (forward + gate-aware backward) on one MI355X.
+
+One step = forward + gate-aware backward (gdn2_chunk_fwd_states,
+gdn2_chunk_bwd_reverse, gdn2_chunk_bwd_grads: the staged form of
+gdn2_chunk_fwd + gdn2_chunk_bwd that reuses the forward's chunk states) over one batch of the
+forward/backward workload B=8, T=2048, H=16, dk=dv=128 (bf16 q/k/v, fp32
+gates, decay and state; the 2K x 8 training shape of the Gated DeltaNet-2
+pages).  Inputs are seeded synthetic tensors (linear_attention_sequence_gdn2_amd.inputs)
+already resident in HBM when the timed region starts.
+
+Prints one JSON line (rank 0):
+  value        tokens/s of whole steps (tokens = B*T per step)
+  roofline     for the dominant kernel: algorithmic bytes per launch / its
+               average launch time (HIP events on the stream it runs on),
+               against MI355X HBM3E 8 TB/s
+  cpu_baseline the fp64 oracle (fwd + bwd) timed on the host's cores on a
+               bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "fwd_bf16_B8H16T2048d128"
+HBM_PEAK_GBS = 8000.0
+# algorithmic HBM bytes per token-head (bf16 q/k/v, fp32 gates, o and gradients):
+#   forward : q,k,v 3*256 + log_alpha,b,w 3*512 + o 512              = 2816
+#   backward: q,k,v 768 + gates 1536 + dO 512 + six gradients 6*512  = 5888
+FWD_BYTES_PER_TOKHEAD = 2816
+BWD_BYTES_PER_TOKHEAD = 5888
+# per-kernel algorithmic bytes per token-head of the three launches of a step:
+#   forward with states : 2816 + chunk states 128*128*4 / 64 tokens = 1024     -> 3840
+#   reverse sweep       : q,k 512 + log_alpha,b 1024 + dO 512 + dstates 1024   -> 3072
+#   chunk gradients     : q,k,v 768 + gates 1536 + dO 512 + states, dstates 2048
+#                         + dq,dk,dv,dlog_alpha,db,dw 3072                      -> 7936
+FWD_STATES_BYTES_PER_TOKHEAD = 3840
+BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
+BWD_GRADS_BYTES_PER_TOKHEAD = 7936
+
+
+def _kernel_sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_sequence_gdn2_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, launches_bytes):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE, if the
+    committed counter summary was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_digest") != _kernel_sources_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    if not k or k.get("workload") != WORKLOAD:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, sample_batches):
+    import numpy as np  # noqa: F401
+    import oracle
+    from linear_attention_sequence_gdn2_amd.inputs import make_workload
+    x = make_workload(wl, B=sample_batches, grads=True)
+    nthreads = oracle.default_threads()
+    args = [x["q32"], x["k32"], x["v32"], x["log_alpha"], x["b"], x["w"], x["S0"]]
+    args = [oracle._f64(t) for t in args]
+    dO = oracle._f64(x["dO"])
+    dsf = oracle._f64(x["dS_final"])
+    t0 = time.perf_counter()
+    oracle.fwd(*args, nthreads=nthreads)
+    oracle.bwd(*args, dO, dsf, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    tokens = sample_batches * wl.T
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": min(nthreads, sample_batches * wl.H),
+            "kind": "oracle",
+            "sample": "fp64 token-by-token oracle, fwd + bwd, B=%d of %d batches (T=%d, H=%d, d=%d), %.1f s"
+                      % (sample_batches, wl.B, wl.T, wl.H, wl.dk, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this operator benchmark runs on exactly one GPU; --gpus %d is not supported "
+              "(multi-GPU sharding is design-only)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[WORKLOAD]
+    x = make_workload(wl, grads=True)
+    d = {k: (v.to(dev) if v is not None and hasattr(v, "to") else None)
+         for k, v in x.items() if k in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final")}
+    fargs = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+    stream = torch.cuda.current_stream(dev)
+    sshape = gdn2.states_shape(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    states = torch.empty(sshape, dtype=torch.float32, device=dev)
+    dstates = torch.empty(sshape, dtype=torch.float32, device=dev)
+
+    # One training step = three kernel launches:
+    #   fwd_kernel     (gdn2_chunk_fwd_states: o, S_final and the chunk-start states)
+    #   bwd_reverse    (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
+    #   bwd_chunk      (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        o, sf, _ = gdn2.fwd_states(*fargs, states=states)
+        if ev is not None:
+            ev[1].record(stream)
+        _, dS0 = gdn2.bwd_reverse(d["q"], d["k"], d["log_alpha"], d["b"], d["dO"], d["dS_final"], dstates=dstates)
+        if ev is not None:
+            ev[2].record(stream)
+        g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates)
+        if ev is not None:
+            ev[3].record(stream)
+        return o, sf, g, dS0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+    step_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+    tokens = wl.B * wl.T
+    tokheads = wl.B * wl.T * wl.H
+    state_bytes = wl.B * wl.H * wl.dk * wl.dv * 4
+    value = tokens / (wall / args.steps)
+
+    # algorithmic bytes per launch of each kernel (per token-head figures times
+    # B*T*H, plus per-sequence states), from the per-token-head constants above
+    kernels = [
+        ("fwd_kernel", "gdn2_chunk_fwd_states", FWD_STATES_BYTES_PER_TOKHEAD * tokheads + state_bytes),
+        ("bwd_reverse_kernel", "gdn2_chunk_bwd_reverse", BWD_REVERSE_BYTES_PER_TOKHEAD * tokheads + 2 * state_bytes),
+        ("bwd_chunk_kernel", "gdn2_chunk_bwd_grads", BWD_GRADS_BYTES_PER_TOKHEAD * tokheads),
+    ]
+    per_kernel = {}
+    for (name, entry, nbytes), ms in zip(kernels, k_ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        per_kernel[name] = {"entry": entry, "launch_ms": round(ms, 4), "algorithmic_bytes": nbytes,
+                            "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(range(3), key=lambda j: k_ms[j])
+    name, entry, nbytes = kernels[dom]
+    achieved = nbytes / (k_ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(name, nbytes),
+            "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(k_ms[dom], 4)}
+    step_alg = (FWD_BYTES_PER_TOKHEAD + BWD_BYTES_PER_TOKHEAD) * tokheads
+    out = {
+        "metric": "GDN-2 chunk fwd+bwd tokens/s (H=16 dk=dv=128 B8xT2K)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": wl.B, "T": wl.T, "H": wl.H, "dk": wl.dk, "dv": wl.dv,
+                   "chunk": 64, "seed": wl.seed, "qkv": "bf16", "gates_state_grads": "fp32",
+                   "parallelism": "single-gpu"},
+        "breakdown": {"kernels": per_kernel, "step_event_ms": round(step_ms, 4),
+                      "fwd_tokens_per_s": round(tokens / (k_ms[0] * 1e-3), 1),
+                      "step_algorithmic_frac": round(step_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_batches)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,6 +104,45 @@ int gdn2_chunk_bwd(const gdn2_shape *shape,
                    float *dS0,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- staged form (training): each call below is exactly one kernel launch ----
+ *
+ * gdn2_chunk_bwd == gdn2_chunk_states + gdn2_chunk_bwd_reverse + gdn2_chunk_bwd_grads.
+ * A training step can instead run gdn2_chunk_fwd_states (which writes the chunk
+ * states while producing o) and skip the state sweep in the backward.
+ * `states` and `dstates` are [B, H, ceil(T/64), dk, dv] fp32 device buffers of
+ * gdn2_chunk_states_bytes() bytes each: states[c] is the state BEFORE chunk c
+ * (tokens 64c ..), dstates[c] the loss gradient w.r.t. the state AFTER chunk c. */
+
+/* Bytes of one chunk-state buffer; (size_t)-1 if the shape is invalid. */
+size_t gdn2_chunk_states_bytes(const gdn2_shape *shape);
+
+/* Forward pass as gdn2_chunk_fwd, additionally writing states (required). */
+int gdn2_chunk_fwd_states(const gdn2_shape *shape,
+                          const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *b, const float *w,
+                          const float *S0, float *o, float *S_final, float *states, void *stream);
+
+/* State sweep only: writes states (no output o).  q is not read. */
+int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v,
+                      const float *log_alpha, const float *b, const float *w,
+                      const float *S0, float *states, void *stream);
+
+/* Reverse sweep of the backward: writes dstates (required) and dS0 (optional).
+ * Reads q, k, log_alpha, b, dO and dS_final (NULL = zeros); v and w are not needed. */
+int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *q, const void *k,
+                           const float *log_alpha, const float *b,
+                           const float *dO, const float *dS_final,
+                           float *dstates, float *dS0, void *stream);
+
+/* Token gradients from states and dstates: dq, dk, dlog_alpha, db [B,T,H,dk],
+ * dv, dw [B,T,H,dv]. */
+int gdn2_chunk_bwd_grads(const gdn2_shape *shape,
+                         const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *b, const float *w,
+                         const float *dO, const float *states, const float *dstates,
+                         float *dq, float *dk, float *dv,
+                         float *dlog_alpha, float *db, float *dw, void *stream);
+
 /* Static, human-readable description of a gdn2_status value. */
 const char *gdn2_strerror(int status);
 

@@ -21,7 +21,8 @@ GDN2_BF16 = 1
 STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3: "GDN2_ERR_WORKSPACE",
           4: "GDN2_ERR_HIP"}
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
-           "gdn2_chunk_bwd_workspace_size", "gdn2_strerror"]
+           "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
+           "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -56,6 +57,16 @@ def load():
         lib.gdn2_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         lib.gdn2_chunk_bwd_workspace_size.argtypes = [SP]
         lib.gdn2_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.gdn2_chunk_states_bytes.argtypes = [SP]
+        lib.gdn2_chunk_states_bytes.restype = ctypes.c_size_t
+        lib.gdn2_chunk_fwd_states.argtypes = [SP] + [P] * 10 + [P]
+        lib.gdn2_chunk_fwd_states.restype = ctypes.c_int
+        lib.gdn2_chunk_states.argtypes = [SP] + [P] * 7 + [P]
+        lib.gdn2_chunk_states.restype = ctypes.c_int
+        lib.gdn2_chunk_bwd_reverse.argtypes = [SP] + [P] * 8 + [P]
+        lib.gdn2_chunk_bwd_reverse.restype = ctypes.c_int
+        lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 15 + [P]
+        lib.gdn2_chunk_bwd_grads.restype = ctypes.c_int
         lib.gdn2_strerror.argtypes = [ctypes.c_int]
         lib.gdn2_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -144,4 +155,76 @@ def bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, want_dS0=True, workspac
                               _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
                               _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]), _ptr(out["dw"]),
                               _ptr(out["dS0"]), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def states_shape(B, T, H, dk, dv):
+    return (B, H, (T + 63) // 64, dk, dv)
+
+
+def fwd_states(q, k, v, log_alpha, b, w, S0=None, want_state=True, states=None):
+    """Forward that also returns the chunk-start states [B,H,ceil(T/64),dk,dv] fp32
+    (one kernel): (o, S_final, states)."""
+    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0,))
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    if states is None:
+        states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check(lib.gdn2_chunk_fwd_states(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                     _ptr(w), _ptr(S0), _ptr(o), _ptr(sf), _ptr(states), _stream(q.device)))
+    return o, sf, states
+
+
+def chunk_states(k, v, log_alpha, b, w, S0=None, q_dtype=None, states=None):
+    """State sweep only (one kernel): chunk-start states [B,H,ceil(T/64),dk,dv]."""
+    B, T, H, dk, dv = _validate(k, k, v, log_alpha, b, w, (S0,))
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, k.dtype)
+    if states is None:
+        states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=k.device)
+    _check(lib.gdn2_chunk_states(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                 _ptr(S0), _ptr(states), _stream(k.device)))
+    return states
+
+
+def bwd_reverse(q, k, log_alpha, b, dO, dS_final=None, want_dS0=True, dstates=None):
+    """Reverse sweep (one kernel): (dstates, dS0)."""
+    B, T, H, dk = q.shape
+    dv = dO.shape[-1]
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    if dstates is None:
+        dstates = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=q.device)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None
+    for t in (q, k, log_alpha, b, dO) + ((dS_final,) if dS_final is not None else ()):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("gdn2: tensors must be contiguous and on one device")
+    _check(lib.gdn2_chunk_bwd_reverse(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(b), _ptr(dO),
+                                      _ptr(dS_final), _ptr(dstates), _ptr(dS0), _stream(q.device)))
+    return dstates, dS0
+
+
+def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates):
+    """Token gradients from chunk states and end-state gradients (one kernel)."""
+    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (dO, states, dstates))
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    dev = q.device
+    out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
+    out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    out["dw"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _check(lib.gdn2_chunk_bwd_grads(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                    _ptr(w), _ptr(dO), _ptr(states), _ptr(dstates), _ptr(out["dq"]),
+                                    _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
+                                    _ptr(out["dw"]), _stream(dev)))
+    return out
+
+
+def bwd_saved(q, k, v, log_alpha, b, w, states, dO, dS_final=None, want_dS0=True):
+    """Backward from the states written by fwd_states: reverse sweep + token gradients."""
+    dstates, dS0 = bwd_reverse(q, k, log_alpha, b, dO, dS_final, want_dS0)
+    out = bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates)
+    out["dS0"] = dS0
     return out

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <initializer_list>
+
 #include "gdn2.h"
 #include "gdn2_kernels.h"
 
@@ -67,14 +69,123 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
     a.B = shape->B; a.T = shape->T; a.H = shape->H; a.dv = shape->dv;
     const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
     a.nvt = shape->dv / vt;
-    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, false,
+    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gdn2::kFwdOut,
                                           reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
+size_t gdn2_chunk_states_bytes(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return (size_t)-1;
+    return (size_t)shape->B * shape->H * nchunks(shape) * (size_t)shape->dk * shape->dv * sizeof(float);
+}
+
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
-    return 2 * (size_t)shape->B * shape->H * nchunks(shape) * (size_t)shape->dk * shape->dv * sizeof(float);
+    return 2 * gdn2_chunk_states_bytes(shape);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn2::FwdArgs fwd_args(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *b, const float *w, const float *S0, float *o,
+                       float *S_final, float *states, int *vt_out) {
+    gdn2::FwdArgs f{};
+    f.q = q; f.k = k; f.v = v;
+    f.la = log_alpha; f.bg = b; f.wg = w;
+    f.S0 = S0; f.o = o; f.S_final = S_final; f.states = states;
+    f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv;
+    const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
+    f.nvt = shape->dv / vt;
+    *vt_out = vt;
+    return f;
+}
+
+gdn2::BwdArgs bwd_args(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *b, const float *w, const float *dO,
+                       const float *dS_final, const float *states, float *dstates, float *dq, float *dk,
+                       float *dv, float *dla, float *db, float *dw, float *dS0, int *vt2_out) {
+    gdn2::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_alpha; a.bg = b; a.wg = w;
+    a.dO = dO; a.dS_final = dS_final;
+    a.states = states; a.dstates = dstates;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dla; a.db = db; a.dw = dw; a.dS0 = dS0;
+    a.B = shape->B; a.T = shape->T; a.H = shape->H; a.DV = shape->dv;
+    const int vt2 = gdn2::bwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
+    a.nvt = shape->dv / vt2;
+    *vt2_out = vt2;
+    return a;
+}
+
+bool all_aligned(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return false;
+    return true;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn2_chunk_fwd_states(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *b, const float *w, const float *S0, float *o,
+                          float *S_final, float *states, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!q || !k || !v || !log_alpha || !b || !w || !o || !states) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, v, log_alpha, b, w, S0, o, S_final, states})) return GDN2_ERR_INVALID_ARG;
+    int vt;
+    const gdn2::FwdArgs f = fwd_args(shape, q, k, v, log_alpha, b, w, S0, o, S_final, states, &vt);
+    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gdn2::kFwdOutStates,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v, const float *log_alpha,
+                      const float *b, const float *w, const float *S0, float *states, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!k || !v || !log_alpha || !b || !w || !states) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({k, v, log_alpha, b, w, S0, states})) return GDN2_ERR_INVALID_ARG;
+    int vt;
+    const gdn2::FwdArgs f = fwd_args(shape, nullptr, k, v, log_alpha, b, w, S0, nullptr, nullptr, states, &vt);
+    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gdn2::kFwdStates,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *q, const void *k, const float *log_alpha,
+                           const float *b, const float *dO, const float *dS_final, float *dstates, float *dS0,
+                           void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!q || !k || !log_alpha || !b || !dO || !dstates) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, log_alpha, b, dO, dS_final, dstates, dS0})) return GDN2_ERR_INVALID_ARG;
+    int vt2;
+    const gdn2::BwdArgs a = bwd_args(shape, q, k, nullptr, log_alpha, b, nullptr, dO, dS_final, nullptr, dstates,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dS0, &vt2);
+    return launch_status(gdn2::launch_bwd_reverse(a, shape->dk, vt2, shape->qkv_dtype == GDN2_BF16,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *b, const float *w, const float *dO,
+                         const float *states, const float *dstates, float *dq, float *dk, float *dv,
+                         float *dlog_alpha, float *db, float *dw, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!q || !k || !v || !log_alpha || !b || !w || !dO || !states || !dstates || !dq || !dk || !dv ||
+        !dlog_alpha || !db || !dw)
+        return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, v, log_alpha, b, w, dO, states, dstates, dq, dk, dv, dlog_alpha, db, dw}))
+        return GDN2_ERR_INVALID_ARG;
+    int vt2;
+    const gdn2::BwdArgs a = bwd_args(shape, q, k, v, log_alpha, b, w, dO, nullptr, states, const_cast<float *>(dstates),
+                                     dq, dk, dv, dlog_alpha, db, dw, nullptr, &vt2);
+    return launch_status(gdn2::launch_bwd_chunk(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
+                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
@@ -86,44 +197,18 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     if (st != GDN2_OK) return st;
     if (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv || !dlog_alpha || !db || !dw)
         return GDN2_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_alpha, db, dw, dS0, workspace};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_alpha, db, dw, dS0, workspace}))
+        return GDN2_ERR_INVALID_ARG;
     const size_t need = gdn2_chunk_bwd_workspace_size(shape);
     if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
-
-    const size_t half = need / 2 / sizeof(float);
     float *states = reinterpret_cast<float *>(workspace);
-    float *dstates = states + half;
-    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    const bool bf16 = shape->qkv_dtype == GDN2_BF16;
-
-    // 1) forward state sweep: start state of every chunk
-    gdn2::FwdArgs f{};
-    f.q = q; f.k = k; f.v = v;
-    f.la = log_alpha; f.bg = b; f.wg = w;
-    f.S0 = S0; f.o = nullptr; f.S_final = nullptr; f.states = states;
-    f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv;
-    const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
-    f.nvt = shape->dv / vt;
-    hipError_t e = gdn2::launch_fwd(f, shape->dk, vt, bf16, true, hs);
-    if (e != hipSuccess) return GDN2_ERR_HIP;
-
-    gdn2::BwdArgs a{};
-    a.q = q; a.k = k; a.v = v;
-    a.la = log_alpha; a.bg = b; a.wg = w;
-    a.dO = dO; a.dS_final = dS_final;
-    a.states = states; a.dstates = dstates;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw; a.dS0 = dS0;
-    a.B = shape->B; a.T = shape->T; a.H = shape->H; a.DV = shape->dv;
-    const int vt2 = gdn2::bwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
-    a.nvt = shape->dv / vt2;
-    // 2) reverse sweep over chunks: gradient w.r.t. every chunk's end state, and dS0
-    e = gdn2::launch_bwd_reverse(a, shape->dk, vt2, bf16, hs);
-    if (e != hipSuccess) return GDN2_ERR_HIP;
-    // 3) chunk-parallel gradients of all token inputs
-    e = gdn2::launch_bwd_chunk(a, shape->dk, bf16, hs);
-    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    float *dstates = states + need / 2 / sizeof(float);
+    int rc = gdn2_chunk_states(shape, k, v, log_alpha, b, w, S0, states, stream);
+    if (rc != GDN2_OK) return rc;
+    rc = gdn2_chunk_bwd_reverse(shape, q, k, log_alpha, b, dO, dS_final, dstates, dS0, stream);
+    if (rc != GDN2_OK) return rc;
+    return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, dq, dk, dv, dlog_alpha, db,
+                                dw, stream);
 }
 
 }  // extern "C"

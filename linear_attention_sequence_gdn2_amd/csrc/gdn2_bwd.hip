@@ -33,6 +33,8 @@
 // i.e. channels 32j + 4g + {0..3} and 32j + 16 + 4g + {0..3}.  It equals the D
 // layout of a product whose rows are channels, so key-side gradients come out
 // of transposed products already in element layout.
+#include <type_traits>
+
 #include "gdn2_chunk.h"
 #include "gdn2_kernels.h"
 
@@ -102,7 +104,7 @@ struct KeyOps {
     Split8 E[NKS], Q[NKS], K[NKS], H[NKS];   // Et, Qt, Kt, Kh
 };
 
-template <int NE>
+template <int NE, bool WE = true, bool WQ = true, bool WK = true, bool WH = true>
 __device__ __forceinline__ void key_operands(const float (&qf)[NE], const float (&kf)[NE], const float (&bgf)[NE],
                                              const float (&G)[NE], const float (&gC)[NE], KeyOps<NE / 8> &ops) {
 #pragma unroll
@@ -111,18 +113,18 @@ __device__ __forceinline__ void key_operands(const float (&qf)[NE], const float 
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int e = 8 * j + s;
-            const float eg = exp2_fast(G[e]);
-            const float eng = exp2_fast(-G[e]);
-            const float ek = exp2_fast(gC[e] - G[e]);
+            const float eg = (WE || WQ) ? exp2_fast(G[e]) : 0.f;
+            const float eng = WK ? exp2_fast(-G[e]) : 0.f;
+            const float ek = WH ? exp2_fast(gC[e] - G[e]) : 0.f;
             et[s] = bgf[e] * kf[e] * eg;
             qt[s] = qf[e] * eg;
             kt[s] = kf[e] * eng;
             kh[s] = kf[e] * ek;
         }
-        ops.E[j] = split8(et);
-        ops.Q[j] = split8(qt);
-        ops.K[j] = split8(kt);
-        ops.H[j] = split8(kh);
+        if (WE) ops.E[j] = split8(et);
+        if (WQ) ops.Q[j] = split8(qt);
+        if (WK) ops.K[j] = split8(kt);
+        if (WH) ops.H[j] = split8(kh);
     }
 }
 
@@ -450,23 +452,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     for (int idx = tid; idx < kChunk * PA; idx += kThreads) sT[idx] = 0.f;
 
     // ---- key side, A, P, T ----
-    KeyOps<NKS> ops;
+    // Only Et (for X) and Kh (for dU) stay in registers through the value loop;
+    // Qt and Kt are formed again in the epilogue from a second read of the inputs.
+    Split8 Ekeep[NKS], Hkeep[NKS];
     Split4 Pt[4];
-    {
-        KeyRaw4<DK, BF16> raw;
-        raw.issue(a, rowK, g, vk);
-        float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
-        raw.unpack(qf, kf, laf, bgf);
-#pragma unroll
-        for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
-        chunk_scan<NE, DK>(G, gC, sTot, w, r, [&](int e) { return ch4(e, g); });
-        key_operands<NE>(qf, kf, bgf, G, gC, ops);
-    }
     float *sA = reinterpret_cast<float *>(sZ + 4 * RQ);
-    store_rows<NKS, PK>(ops.K, sZ, sZ + RQ, 16 * w + r, g);
-    store_rows<NKS, PK>(ops.Q, sZ + 2 * RQ, sZ + 3 * RQ, 16 * w + r, g);
-    __syncthreads();
-    build_A_Pt<NKS, PK, PA, FAST>(ops, sZ, sZ + RQ, sZ + 2 * RQ, sZ + 3 * RQ, sA, Pt, w, r, g);
+    {
+        KeyOps<NKS> ops;
+        {
+            KeyRaw4<DK, BF16> raw;
+            raw.issue(a, rowK, g, vk);
+            float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
+            raw.unpack(qf, kf, laf, bgf);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
+            chunk_scan<NE, DK>(G, gC, sTot, w, r, [&](int e) { return ch4(e, g); });
+            key_operands<NE>(qf, kf, bgf, G, gC, ops);
+        }
+        store_rows<NKS, PK>(ops.K, sZ, sZ + RQ, 16 * w + r, g);
+        store_rows<NKS, PK>(ops.Q, sZ + 2 * RQ, sZ + 3 * RQ, 16 * w + r, g);
+        __syncthreads();
+        build_A_Pt<NKS, PK, PA, FAST>(ops, sZ, sZ + RQ, sZ + 2 * RQ, sZ + 3 * RQ, sA, Pt, w, r, g);
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+            Ekeep[j] = ops.E[j];
+            Hkeep[j] = ops.H[j];
+        }
+    }
     __syncthreads();
     solve_T<PA>(sA, sT, w, r, g);
 
@@ -565,8 +577,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < NKS; ++j) {
                 const Split8 sf = row_frag4<PK>(S1, S1 + VT * PK, 16 * n + r, j, g);
-                if (FAST) acc = mfma32(ops.E[j].hi, sf.hi, acc);
-                else acc = mfma32x3(ops.E[j], sf, acc);
+                if (FAST) acc = mfma32(Ekeep[j].hi, sf.hi, acc);
+                else acc = mfma32x3(Ekeep[j], sf, acc);
             }
             const Split4 sp = split4(-acc);
             *reinterpret_cast<bf16x4 *>(&X1[(16 * n + r) * PT + 16 * w + 4 * g]) = sp.hi;
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
                 }
             }
 #pragma unroll
-            for (int j = 0; j < NKS; ++j) du = mfma32x3(ops.H[j], row_frag4<PK>(D1, D1 + VT * PK, 16 * n + r, j, g), du);
+            for (int j = 0; j < NKS; ++j) du = mfma32x3(Hkeep[j], row_frag4<PK>(D1, D1 + VT * PK, 16 * n + r, j, g), du);
             const Split4 sd = split4(du);
             *reinterpret_cast<bf16x4 *>(&dU1[(16 * n + r) * PT + 16 * w + 4 * g]) = sd.hi;
             *reinterpret_cast<bf16x4 *>(&dU1[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sd.lo;
@@ -677,9 +689,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
             if (!(key <= qry)) aP[n][i] = 0.f;
             if (!(key < qry)) aA[n][i] = 0.f;
         }
+    // key-side operands again (4-group layout), from a fresh read of the inputs
+    auto reload_ops = [&](float *sTotBuf, KeyOps<NKS> &o2, auto want_k) {
+        KeyRaw4<DK, BF16> raw;
+        raw.issue(a, rowK, g, vk);
+        float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
+        raw.unpack(qf, kf, laf, bgf);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
+        chunk_scan<NE, DK>(G, gC, sTotBuf, w, r, [&](int e) { return ch4(e, g); });
+        if constexpr (decltype(want_k)::value) key_operands<NE, false, false, true, false>(qf, kf, bgf, G, gC, o2);
+        else key_operands<NE, true, true, false, false>(qf, kf, bgf, G, gC, o2);
+    };
     {
         __bf16 *KtT = sZ, *dP1 = sZ + 2 * RT, *dA1 = sZ + 2 * RT + 2 * kChunk * PT;
-        store_cols<NKS, PT>(ops.K, KtT, KtT + RT, 16 * w + r, g, false);
+        {
+            KeyOps<NKS> o2;
+            reload_ops(sTot, o2, std::true_type{});
+            store_cols<NKS, PT>(o2.K, KtT, KtT + RT, 16 * w + r, g, false);
+        }
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const Split4 sp = split4(aP[n]), sa = split4(aA[n]);
@@ -712,8 +740,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     f32x4 aK[NM];
     {
         __bf16 *QtT = sZ, *EtT = sZ + 2 * RT, *dPt = sZ + 4 * RT, *dAt = sZ + 4 * RT + 2 * kChunk * PT;
-        store_cols<NKS, PT>(ops.Q, QtT, QtT + RT, 16 * w + r, g, false);
-        store_cols<NKS, PT>(ops.E, EtT, EtT + RT, 16 * w + r, g, false);
+        {
+            KeyOps<NKS> o2;
+            reload_ops(sTot2, o2, std::false_type{});
+            store_cols<NKS, PT>(o2.Q, QtT, QtT + RT, 16 * w + r, g, false);
+            store_cols<NKS, PT>(o2.E, EtT, EtT + RT, 16 * w + r, g, false);
+        }
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const Split4 sp = split4(aP[n]), sa = split4(aA[n]);
@@ -743,6 +775,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     }
 
     // ---- element-wise chain (4-group layout: token 16w + r, channel ch4(e, g)) ----
+    // The four key-side gradient accumulators are parked in LDS (each thread
+    // reads back only its own values, so no barrier is needed) to keep the
+    // chain's register footprint small.
+    __syncthreads();
+    float *sAcc = reinterpret_cast<float *>(sZ);   // [4][NE][kThreads]
+    static_assert(4 * NE * kThreads * 4 <= ZSIZE * 2, "accumulator park does not fit");
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int m = e >> 2, i = e & 3;
+        sAcc[(0 * NE + e) * kThreads + tid] = aQ[m][i];
+        sAcc[(1 * NE + e) * kThreads + tid] = aE[m][i];
+        sAcc[(2 * NE + e) * kThreads + tid] = aK[m][i];
+        sAcc[(3 * NE + e) * kThreads + tid] = aH[m][i];
+    }
     float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
     {
         KeyRaw4<DK, BF16> raw;
@@ -752,25 +798,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
     chunk_scan<NE, DK>(G, gC, sTot, w, r, [&](int e) { return ch4(e, g); });  // barrier orders sDG too
-    float xg[NE], yh[NE], base[NE], dq[NE], dkk[NE], db[NE];
+    float xg[NE], yh[NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        const int m = e >> 2, i = e & 3, ch = ch4(e, g);
-        const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]), ek = exp2_fast(gC[e] - G[e]);
-        const float gam = exp2_fast(gC[e]);
-        const float Qt = qf[e] * eg, Et = bgf[e] * kf[e] * eg, Kt = kf[e] * eng, Kh = kf[e] * ek;
-        const float dQt = aQ[m][i], dEt = aE[m][i], dKt = aK[m][i], dKh = aH[m][i];
-        dq[e] = dQt * eg;
-        const float dE = dEt * eg;
-        db[e] = dE * kf[e];
-        dkk[e] = dKt * eng + dKh * ek + dE * bgf[e];
-        xg[e] = dQt * Qt + dEt * Et - dKt * Kt - dKh * Kh;
-        yh[e] = dKh * Kh;
-        float dgam = 0.f;
+    for (int m = 0; m < NM; ++m) {
+        f32x4 vq, vk4, vb;
 #pragma unroll
-        for (int p = 0; p < TPC; ++p) dgam += sDG[ch * TPC + p];
-        base[e] = dgam * gam;
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * m + i;
+            const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]), ek = exp2_fast(gC[e] - G[e]);
+            const float Qt = qf[e] * eg, Et = bgf[e] * kf[e] * eg, Kt = kf[e] * eng, Kh = kf[e] * ek;
+            const float dQt = sAcc[(0 * NE + e) * kThreads + tid];
+            const float dEt = sAcc[(1 * NE + e) * kThreads + tid];
+            const float dKt = sAcc[(2 * NE + e) * kThreads + tid];
+            const float dKh = sAcc[(3 * NE + e) * kThreads + tid];
+            vq[i] = dQt * eg;
+            const float dE = dEt * eg;
+            vb[i] = dE * kf[e];
+            vk4[i] = dKt * eng + dKh * ek + dE * bgf[e];
+            xg[e] = dQt * Qt + dEt * Et - dKt * Kt - dKh * Kh;
+            yh[e] = dKh * Kh;
+        }
+        if (vk) {
+            const size_t off = rowK + 16 * m + 4 * g;
+            *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
+            *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
+            *reinterpret_cast<f32x4 *>(a.db + off) = vb;
+        }
     }
+    // dlog_alpha_t = sum_{s >= t} dG_s + dg_C, with dg_C = sum_s dKh_s*Kh_s + dgamma*gamma
     float xin[NE], xtot[NE], ytot[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) xin[e] = xg[e];
@@ -779,20 +834,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     if (vk) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const size_t off = rowK + 16 * m + 4 * g;
-            f32x4 vq, vk4, vb, vl;
+            f32x4 vl;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = 4 * m + i;
-                vq[i] = dq[e];
-                vk4[i] = dkk[e];
-                vb[i] = db[e];
-                vl[i] = (xtot[e] - xin[e] + xg[e]) + ytot[e] + base[e];
+                const int e = 4 * m + i, ch = ch4(e, g);
+                float dgam = 0.f;
+#pragma unroll
+                for (int p = 0; p < TPC; ++p) dgam += sDG[ch * TPC + p];
+                vl[i] = (xtot[e] - xin[e] + xg[e]) + ytot[e] + dgam * exp2_fast(gC[e]);
             }
-            *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
-            *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
-            *reinterpret_cast<f32x4 *>(a.db + off) = vb;
-            *reinterpret_cast<f32x4 *>(a.dla + off) = vl;
+            *reinterpret_cast<f32x4 *>(a.dla + rowK + 16 * m + 4 * g) = vl;
         }
     }
 }

@@ -495,37 +495,47 @@ int fwd_value_tile(int B, int H, int dk, int dv) {
     return vt;
 }
 
-template <int DK, int VT, bool BF16, bool SWEEP>
+template <int DK, int VT, bool BF16, int MODE>
 static hipError_t launch_t(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * a.nvt)), block(kThreads);
-    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, !SWEEP, SWEEP>), grid, block, 0, st, a);
+    constexpr bool OUT = MODE != kFwdStates, STATES = MODE != kFwdOut;
+    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, OUT, STATES>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DK, bool BF16, bool SWEEP>
+template <int DK, bool BF16, int MODE>
 static hipError_t launch_vt(const FwdArgs &a, int vt, hipStream_t st) {
     if constexpr (DK >= 64) {
-        if (vt == 16) return launch_t<DK, 16, BF16, SWEEP>(a, st);
+        if (vt == 16) return launch_t<DK, 16, BF16, MODE>(a, st);
     }
-    if (vt == 32) return launch_t<DK, 32, BF16, SWEEP>(a, st);
-    if (vt == 64) return launch_t<DK, 64, BF16, SWEEP>(a, st);
+    if (vt == 32) return launch_t<DK, 32, BF16, MODE>(a, st);
+    if (vt == 64) return launch_t<DK, 64, BF16, MODE>(a, st);
     return hipErrorInvalidValue;
 }
 
-template <bool BF16, bool SWEEP>
+template <bool BF16, int MODE>
 static hipError_t launch_dk(const FwdArgs &a, int dk, int vt, hipStream_t st) {
     switch (dk) {
-        case 32: return launch_vt<32, BF16, SWEEP>(a, vt, st);
-        case 64: return launch_vt<64, BF16, SWEEP>(a, vt, st);
-        case 128: return launch_vt<128, BF16, SWEEP>(a, vt, st);
+        case 32: return launch_vt<32, BF16, MODE>(a, vt, st);
+        case 64: return launch_vt<64, BF16, MODE>(a, vt, st);
+        case 128: return launch_vt<128, BF16, MODE>(a, vt, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool state_sweep, hipStream_t st) {
+template <bool BF16>
+static hipError_t launch_mode(const FwdArgs &a, int dk, int vt, FwdMode mode, hipStream_t st) {
+    switch (mode) {
+        case kFwdOut: return launch_dk<BF16, kFwdOut>(a, dk, vt, st);
+        case kFwdStates: return launch_dk<BF16, kFwdStates>(a, dk, vt, st);
+        case kFwdOutStates: return launch_dk<BF16, kFwdOutStates>(a, dk, vt, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, FwdMode mode, hipStream_t st) {
     if (!vt_ok(dk, vt, a.dv)) return hipErrorInvalidValue;
-    if (bf16) return state_sweep ? launch_dk<true, true>(a, dk, vt, st) : launch_dk<true, false>(a, dk, vt, st);
-    return state_sweep ? launch_dk<false, true>(a, dk, vt, st) : launch_dk<false, false>(a, dk, vt, st);
+    return bf16 ? launch_mode<true>(a, dk, vt, mode, st) : launch_mode<false>(a, dk, vt, mode, st);
 }
 
 }  // namespace gdn2

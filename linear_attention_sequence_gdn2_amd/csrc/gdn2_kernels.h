@@ -37,7 +37,9 @@ int fwd_value_tile(int B, int H, int dk, int dv);
 // Value-tile width of the backward reverse sweep (16 or 32).
 int bwd_value_tile(int B, int H, int dk, int dv);
 
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool state_sweep, hipStream_t st);
+// What a forward sweep produces: o only, chunk states only, or both.
+enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, FwdMode mode, hipStream_t st);
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, int vt, bool bf16, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, hipStream_t st);
 

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+Every function declared in include/gdn2.h must be exported by libgdn2.so, and
+argument checks must reject bad calls before any launch (fake, never
+dereferenced pointers are used where a check is expected to fail first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_gdn2_amd as gdn2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = ctypes.c_void_p
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_is_built():
+    assert os.path.exists(gdn2.LIB_PATH), "run python -m linear_attention_sequence_gdn2_amd.build"
+
+
+def test_every_declared_symbol_is_exported():
+    lib = gdn2.load()
+    names = _declared()
+    assert len(names) >= 10, names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(names) == sorted(gdn2.EXPORTS)
+
+
+def _shape(B=2, T=100, H=3, dk=128, dv=64, chunk=64, dt=1):
+    return gdn2.Gdn2Shape(B, T, H, dk, dv, chunk, dt)
+
+
+def test_workspace_and_state_sizes():
+    lib = gdn2.load()
+    s = _shape()
+    nc = (100 + 63) // 64
+    one = 2 * 3 * nc * 128 * 64 * 4
+    assert lib.gdn2_chunk_states_bytes(ctypes.byref(s)) == one
+    assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s)) == 2 * one
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 0
+    bad = _shape(dk=96)
+    assert lib.gdn2_chunk_states_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(H=-1), INVALID),
+    (dict(chunk=32), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
+    (dict(dt=7), UNSUPPORTED), (dict(B=1 << 14, T=1 << 14, H=16), UNSUPPORTED),
+])
+def test_shape_checks(kw, code):
+    lib = gdn2.load()
+    s = _shape(**kw)
+    fake = P(0x10000)
+    rc = lib.gdn2_chunk_fwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None, fake, None, None, 0, None)
+    assert rc == code
+
+
+def test_null_shape_and_pointers():
+    lib = gdn2.load()
+    fake = P(0x10000)
+    assert lib.gdn2_chunk_fwd(None, fake, fake, fake, fake, fake, fake, None, fake, None, None, 0, None) == INVALID
+    s = _shape()
+    for i in range(7):
+        args = [fake] * 6 + [None, fake, None]
+        idx = [0, 1, 2, 3, 4, 5, 7][i]
+        args[idx] = None
+        assert lib.gdn2_chunk_fwd(ctypes.byref(s), *args, None, 0, None) == INVALID
+
+
+def test_misaligned_pointer_rejected():
+    lib = gdn2.load()
+    s = _shape()
+    fake, odd = P(0x10000), P(0x10008)
+    assert lib.gdn2_chunk_fwd(ctypes.byref(s), fake, odd, fake, fake, fake, fake, None, fake, None, None, 0,
+                              None) == INVALID
+
+
+def test_backward_workspace_checked_before_launch():
+    lib = gdn2.load()
+    s = _shape()
+    f = P(0x10000)
+    need = lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s))
+    args = [f] * 6 + [None, f, None] + [f] * 6 + [None]
+    assert lib.gdn2_chunk_bwd(ctypes.byref(s), *args, None, need, None) == WORKSPACE
+    assert lib.gdn2_chunk_bwd(ctypes.byref(s), *args, f, need - 1, None) == WORKSPACE
+
+
+def test_staged_entry_points_check_arguments():
+    lib = gdn2.load()
+    s = _shape()
+    f = P(0x10000)
+    assert lib.gdn2_chunk_fwd_states(ctypes.byref(s), f, f, f, f, f, f, None, f, None, None, None) == INVALID
+    assert lib.gdn2_chunk_states(ctypes.byref(s), f, f, f, f, f, None, None, None) == INVALID
+    assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), f, f, f, f, f, None, None, None, None) == INVALID
+    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, f, f, f, f, None, None) == INVALID
+
+
+def test_strerror_covers_every_status():
+    lib = gdn2.load()
+    msgs = {lib.gdn2_strerror(c).decode() for c in range(5)}
+    assert len(msgs) == 5
+    assert "unknown" in lib.gdn2_strerror(99).decode()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(RuntimeError):
+        gdn2.fwd(x, x, x, x, x, x)

@@ -1,0 +1,95 @@
+"""GPU invariants of the operator (through the C ABI): the staged entry points
+agree with the one-call forms, sequences can be split across calls, results are
+bitwise reproducible, every output element is written, and permuting value
+channels permutes the outputs."""
+import pytest
+import torch
+
+import linear_attention_sequence_gdn2_amd as gdn2
+from linear_attention_sequence_gdn2_amd.inputs import make_inputs
+from _util import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(B=2, T=300, H=2, dk=128, dv=128, seed=11, qkv="bf16", s0=0.02):
+    return to_dev(make_inputs(B, T, H, dk, dv, seed=seed, qkv_dtype=qkv, s0_std=s0, grads=True))
+
+
+def _fargs(d):
+    return (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+
+
+def test_staged_forward_and_backward_match_one_call_forms():
+    d = _dev()
+    o1, s1 = gdn2.fwd(*_fargs(d))
+    o2, s2, states = gdn2.fwd_states(*_fargs(d))
+    st2 = gdn2.chunk_states(d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+    g1 = gdn2.bwd(*_fargs(d), d["dO"], d["dS_final"])
+    g2 = gdn2.bwd_saved(*_fargs(d)[:6], states, d["dO"], d["dS_final"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(states, st2)
+    for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"):
+        assert torch.equal(g1[n], g2[n]), n
+    # states[0] is the start state
+    assert torch.equal(states[:, :, 0], d["S0"])
+
+
+def test_split_sequence_chains_through_the_state():
+    d = _dev(T=320, qkv="f32", s0=0.3)
+    o, sf = gdn2.fwd(*_fargs(d))
+    c = 128  # a chunk boundary, so both halves use the same chunking
+    p1 = [t[:, :c].contiguous() for t in _fargs(d)[:6]]
+    p2 = [t[:, c:].contiguous() for t in _fargs(d)[:6]]
+    o1, s1 = gdn2.fwd(*p1, d["S0"])
+    o2, s2 = gdn2.fwd(*p2, s1)
+    torch.cuda.synchronize()
+    err_o = (torch.cat([o1, o2], 1) - o).abs().max() / o.abs().max()
+    err_s = (s2 - sf).abs().max() / sf.abs().max()
+    assert err_o < 1e-5 and err_s < 1e-5, (err_o, err_s)
+
+
+def test_results_are_bitwise_reproducible():
+    d = _dev(B=3, T=257, seed=5)
+    runs = [gdn2.fwd(*_fargs(d)) for _ in range(3)]
+    grads = [gdn2.bwd(*_fargs(d), d["dO"], d["dS_final"]) for _ in range(2)]
+    torch.cuda.synchronize()
+    for o, s in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(s, runs[0][1])
+    for n in grads[0]:
+        assert torch.equal(grads[0][n], grads[1][n]), n
+
+
+def test_every_output_element_is_written():
+    d = _dev(B=1, T=130, H=3, dk=64, dv=128, seed=9)
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    nc = (T + 63) // 64
+    states = torch.full((B, H, nc, dk, dv), float("nan"), device="cuda")
+    o, sf, states = gdn2.fwd_states(*_fargs(d), states=states)
+    dstates = torch.full_like(states, float("nan"))
+    dstates, dS0 = gdn2.bwd_reverse(d["q"], d["k"], d["log_alpha"], d["b"], d["dO"], d["dS_final"], dstates=dstates)
+    g = gdn2.bwd_grads(*_fargs(d)[:6], d["dO"], states, dstates)
+    torch.cuda.synchronize()
+    for t in [o, sf, states, dstates, dS0] + list(g.values()):
+        assert torch.isfinite(t).all()
+
+
+def test_value_channel_permutation_equivariance():
+    d = _dev(B=1, T=200, H=2, seed=21, qkv="f32")
+    perm = torch.randperm(d["v"].shape[-1], generator=torch.Generator().manual_seed(0)).cuda()
+    o, sf = gdn2.fwd(*_fargs(d))
+    o2, sf2 = gdn2.fwd(d["q"], d["k"], d["v"][..., perm].contiguous(), d["log_alpha"], d["b"],
+                       d["w"][..., perm].contiguous(), d["S0"][..., perm].contiguous())
+    torch.cuda.synchronize()
+    assert (o2 - o[..., perm]).abs().max() <= 1e-5 * o.abs().max()
+    assert (sf2 - sf[..., perm]).abs().max() <= 1e-5 * sf.abs().max()
+
+
+def test_argument_errors_surface_as_exceptions():
+    d = _dev(B=1, T=64, H=1)
+    with pytest.raises(ValueError):
+        gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"][..., :64].contiguous(), d["b"], d["w"])
+    with pytest.raises(ValueError):
+        gdn2.fwd(d["q"], d["k"].transpose(1, 2), d["v"], d["log_alpha"], d["b"], d["w"])
