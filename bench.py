@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times), to calibrate "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this operator benchmark runs on exactly one GPU; --gpus %d is not supported "
@@ -115,6 +118,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.rand(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": 3}))
+        return
     wl = WORKLOADS[WORKLOAD]
     x = make_workload(wl, grads=True)
     d = {k: (v.to(dev) if v is not None and hasattr(v, "to") else None)

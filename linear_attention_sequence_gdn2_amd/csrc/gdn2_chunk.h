@@ -36,30 +36,56 @@ __device__ __forceinline__ void chunk_scan(float (&x)[NE], float (&tot)[NE], flo
     }
 }
 
+// Inverse of one unit-lower 16x16 block, (I + N)^-1 with N strictly lower, so
+// N^16 = 0 and (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly.  The
+// powers are formed on MFMA in both the row layout (lane holds X[r][4g+i]) and
+// the column layout (lane holds X[4g+i][r]): the product of two column-layout
+// operands' transposes lands in row layout, so no data leaves the registers.
+// nA / nB: N in row / column layout.  Returns (I + N)^-1 in column layout.
+__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4 &nA, const f32x4 &nB, int r, int g) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == r) ? 1.f : 0.f;   // same in both layouts
+    const Split4 NA = split4(nA), NB = split4(nB);
+    const f32x4 n2B = mfma16x3(NA, NB, zero);        // N^2, column layout
+    const f32x4 n2A = mfma16x3(NB, NA, zero);        // (N^T N^T) = (N^2)^T, column layout = N^2 row layout
+    const Split4 N2A = split4(n2A), N2B = split4(n2B);
+    const f32x4 n4B = mfma16x3(N2A, N2B, zero);
+    const f32x4 n4A = mfma16x3(N2B, N2A, zero);
+    const Split4 N4A = split4(n4A);
+    const f32x4 n8B = mfma16x3(N4A, split4(n4B), zero);
+    f32x4 y = n8B + eye;                             // (I + N^8), column layout
+    y = mfma16x3(split4(n4A + eye), split4(y), zero);
+    y = mfma16x3(split4(n2A + eye), split4(y), zero);
+    y = mfma16x3(split4(eye - nA), split4(y), zero);
+    return y;
+}
+
 // T = (I + A)^-1 for the strictly lower 64x64 A of a chunk (triangular solve
-// of the WY form, fp32 values).  sA: A in fp32 [64][PA] (only the strictly lower
-// 16x16 blocks on or below the diagonal are read); sT: fp32 [64][PA], whose
-// strictly upper 16x16 blocks must already be zero.  On return sT holds T.
-// Diagonal blocks by forward substitution (one column per lane), off-diagonal
-// blocks by distance: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ, on MFMA with
-// split-bf16 operands.  Contains 4 workgroup barriers; sA is not written.
+// of the WY form).  sA: A in fp32 [64][PA] (only the strictly lower 16x16
+// blocks on or below the diagonal are read); sT: fp32 [64][PA], whose strictly
+// upper 16x16 blocks must already be zero.  On return sT holds T.
+// Diagonal blocks: unit_lower_inverse16 (wave w inverts block w); off-diagonal
+// blocks by block distance: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ.  All
+// products run on MFMA with split-bf16 operands (about 16 significant bits,
+// fp32 accumulation).  Contains 4 workgroup barriers; sA is not written.
 template <int PA>
 __device__ __forceinline__ void solve_T(const float *sA, float *sT, int w, int r, int g) {
     {
-        const float *Ab = &sA[(16 * w) * PA + 16 * w];
-        float t[16];
+        f32x4 nA = *reinterpret_cast<const f32x4 *>(&sA[(16 * w + r) * PA + 16 * w + 4 * g]);
+        f32x4 nB;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == r) ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i) nB[i] = sA[(16 * w + 4 * g + i) * PA + 16 * w + r];
+        // only the strictly lower part of the diagonal block is A
 #pragma unroll
-            for (int kx = 0; kx < i; ++kx) s -= Ab[i * PA + kx] * t[kx];
-            t[i] = s;
+        for (int i = 0; i < 4; ++i) {
+            if (!(4 * g + i < r)) nA[i] = 0.f;
+            if (!(r < 4 * g + i)) nB[i] = 0.f;
         }
+        const f32x4 tB = unit_lower_inverse16(nA, nB, r, g);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const float val = g == 0 ? t[ii] : g == 1 ? t[4 + ii] : g == 2 ? t[8 + ii] : t[12 + ii];
-            sT[(16 * w + 4 * g + ii) * PA + 16 * w + r] = val;
-        }
+        for (int i = 0; i < 4; ++i) sT[(16 * w + 4 * g + i) * PA + 16 * w + r] = tB[i];
     }
     __syncthreads();
 #pragma unroll

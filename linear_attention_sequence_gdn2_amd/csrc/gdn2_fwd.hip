@@ -24,7 +24,7 @@
 // Wave w owns tokens 16w..16w+15 of the chunk for the key-side element work and
 // the rows of A, P, X, U and O; the fp32 state stays in registers (D layout),
 // with a split-bf16 copy in LDS as the MFMA operand of the next chunk.
-#include "gdn2_device.h"
+#include "gdn2_chunk.h"
 #include "gdn2_kernels.h"
 
 namespace gdn2 {
@@ -100,11 +100,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         // Loads are unconditional, from addresses clamped into the tensors, so
         // that no branch (and no early wait) separates them; tokens past the
         // end are zeroed when the registers are unpacked.
-        __device__ __forceinline__ void issue(const FwdArgs &a, int t0, int T, int w_, int r_, int g_,
-                                              size_t baseK, size_t tokK, size_t baseV, size_t tokV) {
+        // decay and erase gate (the largest inputs) of the chunk starting at t0
+        __device__ __forceinline__ void issue_gates(const FwdArgs &a, int t0, int T, int w_, int r_, int g_,
+                                                    size_t baseK, size_t tokK) {
             const int tk = t0 + 16 * w_ + r_;
             vk = tk < T;
             const size_t offk = baseK + (size_t)(vk ? tk : T - 1) * tokK + 8 * g_;
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const size_t o = offk + 32 * j;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    la[j][hh] = reinterpret_cast<const float4 *>(a.la + o)[hh];
+                    bg[j][hh] = reinterpret_cast<const float4 *>(a.bg + o)[hh];
+                }
+            }
+        }
+
+        // q, k (key side) and v, w (value side) of the chunk starting at t0
+        __device__ __forceinline__ void issue_qkvw(const FwdArgs &a, int t0, int T, int w_, int r_, int g_,
+                                                   size_t baseK, size_t tokK, size_t baseV, size_t tokV) {
+            const int tk = t0 + 16 * w_ + r_;
+            const bool vkk = tk < T;
+            const size_t offk = baseK + (size_t)(vkk ? tk : T - 1) * tokK + 8 * g_;
 #pragma unroll
             for (int j = 0; j < NKS; ++j) {
                 const size_t o = offk + 32 * j;
@@ -117,11 +135,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
                         if (OUT) qx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + o)[hh];
                         kx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.k) + o)[hh];
                     }
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    la[j][hh] = reinterpret_cast<const float4 *>(a.la + o)[hh];
-                    bg[j][hh] = reinterpret_cast<const float4 *>(a.bg + o)[hh];
                 }
             }
             vmask = 0;
@@ -191,7 +204,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         }
     };
     Raw raw;
-    raw.issue(a, 0, T, w, r, g, baseK, tokK, baseV, tokV);
+    raw.issue_gates(a, 0, T, w, r, g, baseK, tokK);
+    raw.issue_qkvw(a, 0, T, w, r, g, baseK, tokK, baseV, tokV);
 
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * kChunk;
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             *reinterpret_cast<bf16x8 *>(&sR1[(16 * w + r) * PK + 32 * j + 8 * g]) = ks.hi;
             *reinterpret_cast<bf16x8 *>(&sR1[R1 + (16 * w + r) * PK + 32 * j + 8 * g]) = ks.lo;
         }
-        if (c + 1 < NC) raw.issue(a, t0 + kChunk, T, w, r, g, baseK, tokK, baseV, tokV);
+        if (c + 1 < NC) raw.issue_gates(a, t0 + kChunk, T, w, r, g, baseK, tokK);
         __syncthreads();
 
         // ---- A^T and P^T for this wave's query rows (keys from LDS) ----
@@ -327,6 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         }
         __syncthreads();
 
+        if (c + 1 < NC) raw.issue_qkvw(a, t0 + kChunk, T, w, r, g, baseK, tokK, baseV, tokV);
+
         // ---- Kh^T into R1 (Kt is no longer read) ----
 #pragma unroll
         for (int j = 0; j < NKS; ++j)
@@ -337,46 +353,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
                 sR1[R1 + ch * PT + 16 * w + r] = Kh[j].lo[i];
             }
 
-        // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution (fp32) ----
-        {
-            const float *Ab = &sA[(16 * w) * PA + 16 * w];
-            float t[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == r) ? 1.f : 0.f;
-#pragma unroll
-                for (int kx = 0; kx < i; ++kx) s -= Ab[i * PA + kx] * t[kx];
-                t[i] = s;
-            }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const float val = g == 0 ? t[ii] : g == 1 ? t[4 + ii] : g == 2 ? t[8 + ii] : t[12 + ii];
-                sT[(16 * w + 4 * g + ii) * PA + 16 * w + r] = val;
-            }
-        }
-        __syncthreads();
-        // off-diagonal blocks, one block distance per step:
-        //   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            if (w >= d) {
-                const int I = w, J = w - d;
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < I; ++K) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&sA[(16 * I + r) * PA + 16 * K + 4 * g]);
-                    f32x4 tv;
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) tv[ii] = sT[(16 * K + 4 * g + ii) * PA + 16 * J + r];
-                    Y = mfma16x3(split4(av), split4(tv), Y);
-                }
-                const f32x4 tiv = *reinterpret_cast<const f32x4 *>(&sT[(16 * I + r) * PA + 16 * I + 4 * g]);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 R = mfma16x3(split4(tiv), split4(-Y), zero);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) sT[(16 * I + 4 * g + ii) * PA + 16 * J + r] = R[ii];
-            }
-            __syncthreads();
-        }
+        // ---- T = (I + A)^-1 ----
+        solve_T<PA>(sA, sT, w, r, g);
 
         // ---- U = T X for this wave's rows ----
         const int nkk = (w >= 2) ? 2 : 1;
