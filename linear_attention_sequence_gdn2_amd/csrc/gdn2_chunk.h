@@ -110,6 +110,76 @@ __device__ __forceinline__ void solve_T(const float *sA, float *sT, int w, int r
     }
 }
 
+// Same as solve_T, with A and T sharing one fp32 [64][PA] buffer: each wave
+// first keeps its own row blocks of A in registers (only wave I ever reads
+// row block I of A), then T is written over A.  The strictly upper 16x16
+// blocks of the buffer must be zero and stay zero.  4 workgroup barriers.
+template <int PA>
+__device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g) {
+    f32x4 arow[3];
+#pragma unroll
+    for (int K = 0; K < 3; ++K)
+        if (K < w) arow[K] = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 16 * K + 4 * g]);
+    {
+        f32x4 nA = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 16 * w + 4 * g]);
+        f32x4 nB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nB[i] = sAT[(16 * w + 4 * g + i) * PA + 16 * w + r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!(4 * g + i < r)) nA[i] = 0.f;
+            if (!(r < 4 * g + i)) nB[i] = 0.f;
+        }
+        const f32x4 tB = unit_lower_inverse16(nA, nB, r, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAT[(16 * w + 4 * g + i) * PA + 16 * w + r] = tB[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        if (w >= d) {
+            const int I = w, J = w - d;
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int K = 0; K < 3; ++K) {
+                if (K >= J && K < I) {
+                    f32x4 tv;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) tv[ii] = sAT[(16 * K + 4 * g + ii) * PA + 16 * J + r];
+                    Y = mfma16x3(split4(arow[K]), split4(tv), Y);
+                }
+            }
+            const f32x4 tiv = *reinterpret_cast<const f32x4 *>(&sAT[(16 * I + r) * PA + 16 * I + 4 * g]);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 R = mfma16x3(split4(tiv), split4(-Y), zero);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) sAT[(16 * I + 4 * g + ii) * PA + 16 * J + r] = R[ii];
+        }
+        __syncthreads();
+    }
+}
+
+// A-operand fragment of X^T for the 16x16x32 MFMA, read transposed from a
+// row-major [row][col] bf16 tile (hi and lo planes): lane (r, g) receives
+// column c0 + r of rows k0 + 4g + {0..3} (slots 0..3) and k0 + 16 + 4g + {0..3}
+// (slots 4..7), the "4-group" contraction order.
+template <int P>
+__device__ __forceinline__ Split8 frag_tr(const __bf16 *hi, const __bf16 *lo, int k0, int c0, int r, int g) {
+    const int o0 = (k0 + 4 * g + (r >> 2)) * P + c0 + 4 * (r & 3);
+    const int o1 = o0 + 16 * P;
+    Split8 f;
+    const bf16x4 a = lds_read_tr(hi + o0), b = lds_read_tr(hi + o1);
+    const bf16x4 c = lds_read_tr(lo + o0), d = lds_read_tr(lo + o1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.hi[i] = a[i];
+        f.hi[4 + i] = b[i];
+        f.lo[i] = c[i];
+        f.lo[4 + i] = d[i];
+    }
+    return f;
+}
+
 // Split-bf16 MFMA fragment with the "4-group" contraction order: slots 0..3 are
 // taken from p0[0..3] and slots 4..7 from p1[0..3].
 __device__ __forceinline__ Split8 frag_2x4(const __bf16 *hi0, const __bf16 *hi1, const __bf16 *lo0,

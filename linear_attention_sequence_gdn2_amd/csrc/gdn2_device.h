@@ -64,31 +64,54 @@ __device__ __forceinline__ void split1(float x, __bf16 &hi, __bf16 &lo) {
     lo = (__bf16)(x - (float)hi);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two values at a time, so each conversion is one packed v_cvt_pk_bf16_f32
+__device__ __forceinline__ void split2(float x0, float x1, bf16x2 &hi, bf16x2 &lo) {
+    const f32x2 x = {x0, x1};
+    hi = __builtin_convertvector(x, bf16x2);
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x2), bf16x2);
+}
+
 __device__ __forceinline__ Split8 split8(const float *x) {
+    bf16x2 h0, h1, h2, h3, l0, l1, l2, l3;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    split2(x[4], x[5], h2, l2);
+    split2(x[6], x[7], h3, l3);
     Split8 s;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __bf16 h, l;
-        split1(x[i], h, l);
-        s.hi[i] = h;
-        s.lo[i] = l;
-    }
+    s.hi = __builtin_shufflevector(__builtin_shufflevector(h0, h1, 0, 1, 2, 3), __builtin_shufflevector(h2, h3, 0, 1, 2, 3),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+    s.lo = __builtin_shufflevector(__builtin_shufflevector(l0, l1, 0, 1, 2, 3), __builtin_shufflevector(l2, l3, 0, 1, 2, 3),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
     return s;
 }
 
 __device__ __forceinline__ Split4 split4(const f32x4 &x) {
+    bf16x2 h0, h1, l0, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
     Split4 s;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __bf16 h, l;
-        split1(x[i], h, l);
-        s.hi[i] = h;
-        s.lo[i] = l;
-    }
+    s.hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+    s.lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3);
     return s;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950).  Within each group of 16
+// lanes, lane p receives element (p % 4) of the 4-element bf16 segments that
+// lanes 4i + p/4 of the same group address, for i = 0..3.  If lane (p, g)
+// addresses row R0 + 4g + p/4, columns C0 + 4(p%4) .. +3 of a row-major bf16
+// tile, it receives column C0 + p of rows R0 + 4g + {0,1,2,3}: a 16x16 block
+// read transposed, in the MFMA A/B operand order (checked on gfx950).
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
+    typedef short s16x4_lds __attribute__((ext_vector_type(4)));
+    const s16x4_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_lds *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
 
 // value of lane (l - n) inside the same 16-lane row, 0 for the first n lanes of a row
 template <int N>

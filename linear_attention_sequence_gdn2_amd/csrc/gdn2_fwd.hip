@@ -15,7 +15,8 @@
 //                                                              updated state)
 //     U  = (I + A)^-1 (Z - Et S)        with Z = w * v
 //     O  = Qt S + P U
-//     S' = diag(gamma) S + Kh^T U
+//     S' = diag(gamma) S + Kh^T U = diag(gamma) (S + Kt^T U)
+// (Kh = diag-scaled Kt row by row, so the last form needs no separate Kh.)
 // Unrolling the per-token rule inside a chunk gives exactly these equations.
 //
 // Work decomposition: one workgroup (4 waves) per (batch, head, value tile of
@@ -24,13 +25,19 @@
 // Wave w owns tokens 16w..16w+15 of the chunk for the key-side element work and
 // the rows of A, P, X, U and O; the fp32 state stays in registers (D layout),
 // with a split-bf16 copy in LDS as the MFMA operand of the next chunk.
+// At VT = 32 a workgroup needs under 80 KB of LDS and 256 registers per lane,
+// so two workgroups share a CU and hide each other's load and barrier latency.
 #include "gdn2_chunk.h"
 #include "gdn2_kernels.h"
 
 namespace gdn2 {
 
+// Keep the scheduler from hoisting the next unrolled step's LDS fragment loads
+// above this point (bounds the live registers so two workgroups fit on a CU).
+#define GDN2_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 template <int DK, int VT, bool BF16, bool FAST, bool OUT, bool STATES>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     constexpr int NKS = DK / 32;           // 32-channel contraction steps
     constexpr int NVT = VT / 16;           // 16-column value tiles
     constexpr int NMT = DK / 16;           // 16-row key tiles of S
@@ -38,18 +45,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     static_assert((NMT * NVT) % 4 == 0, "S tiles must split over 4 waves");
     constexpr int PK = DK + 8;             // row pitch of [row][channel] bf16 tiles
     constexpr int PT = kChunk + 8;         // row pitch of [row][token] bf16 tiles
-    constexpr int PA = kChunk + 4;         // row pitch of fp32 64x64 tiles
-    constexpr int R1 = (DK * PT > kChunk * PK) ? DK * PT : kChunk * PK;
+    constexpr int PA = kChunk + 4;         // row pitch of the fp32 64x64 tile
+    constexpr int RK = kChunk * PK;        // one [token][channel] plane
+    constexpr int RX = 2 * VT * PT > 8 * DK ? 2 * VT * PT : 8 * DK;
 
-    // R1 holds Kt [token][channel] (hi, lo) until A and P are formed, then
-    // Kh^T [channel][token] (hi, lo) for the state update.
-    __shared__ __align__(16) __bf16 sR1[2 * R1];
+    // sK: Kt rows [token][channel] (hi, lo) until A and P are formed, then Kh rows.
+    // sXU: per-wave decay totals at the start of a chunk, then X^T, then U^T [col][token].
+    // sAT: A, then T = (I + A)^-1 in place.
+    __shared__ __align__(16) __bf16 sK[2 * RK];
     __shared__ __align__(16) __bf16 sS[2 * VT * PK];   // S^T [col][channel] hi, lo
-    __shared__ __align__(16) __bf16 sXU[2 * VT * PT];  // X^T then U^T [col][token] hi, lo
-    __shared__ __align__(16) float sA[kChunk * PA];
-    __shared__ __align__(16) float sT[kChunk * PA];
-    __shared__ __align__(16) float sTot[4 * DK];
-    __shared__ __align__(16) float sGC[DK];
+    __shared__ __align__(16) __bf16 sXU[RX];
+    __shared__ __align__(16) float sAT[kChunk * PA];
+    float *sTot = reinterpret_cast<float *>(sXU);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
     const int L = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -61,8 +68,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
     const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
     const int NC = (T + kChunk - 1) / kChunk;
+    const int nkk = (w >= 2) ? 2 : 1;
 
-    // ---- start state ----
+    // ---- start state; the strictly upper blocks of sAT stay zero for good ----
     f32x4 S[NTS];
 #pragma unroll
     for (int s = 0; s < NTS; ++s) {
@@ -71,8 +79,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         for (int i = 0; i < 4; ++i)
             S[s][i] = a.S0 ? a.S0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
     }
-    for (int idx = tid; idx < kChunk * PA; idx += kThreads) sT[idx] = 0.f;
-
+    for (int idx = tid; idx < kChunk * PA; idx += kThreads) sAT[idx] = 0.f;
     auto store_state_lds = [&]() {
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
@@ -84,128 +91,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     };
     store_state_lds();
     __syncthreads();
-
-    // Raw inputs of one chunk held in registers: the loads for chunk c + 1 are
-    // issued once chunk c's inputs have been consumed, so their latency hides
-    // behind the rest of chunk c's work.
-    struct Raw {
-        uint4 q[NKS], k[NKS];
-        float4 la[NKS][2], bg[NKS][2];
-        float4 qx[NKS][2], kx[NKS][2];   // fp32 q/k when the inputs are fp32
-        float w[NVT][4];
-        uint32_t v[NVT][4];               // raw bits (bf16 in the low half, or fp32)
-        bool vk;                          // this lane's key-side token exists
-        uint32_t vmask;                   // bit (4n+i): value-side token exists
-
-        // Loads are unconditional, from addresses clamped into the tensors, so
-        // that no branch (and no early wait) separates them; tokens past the
-        // end are zeroed when the registers are unpacked.
-        // decay and erase gate (the largest inputs) of the chunk starting at t0
-        __device__ __forceinline__ void issue_gates(const FwdArgs &a, int t0, int T, int w_, int r_, int g_,
-                                                    size_t baseK, size_t tokK) {
-            const int tk = t0 + 16 * w_ + r_;
-            vk = tk < T;
-            const size_t offk = baseK + (size_t)(vk ? tk : T - 1) * tokK + 8 * g_;
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const size_t o = offk + 32 * j;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    la[j][hh] = reinterpret_cast<const float4 *>(a.la + o)[hh];
-                    bg[j][hh] = reinterpret_cast<const float4 *>(a.bg + o)[hh];
-                }
-            }
-        }
-
-        // q, k (key side) and v, w (value side) of the chunk starting at t0
-        __device__ __forceinline__ void issue_qkvw(const FwdArgs &a, int t0, int T, int w_, int r_, int g_,
-                                                   size_t baseK, size_t tokK, size_t baseV, size_t tokV) {
-            const int tk = t0 + 16 * w_ + r_;
-            const bool vkk = tk < T;
-            const size_t offk = baseK + (size_t)(vkk ? tk : T - 1) * tokK + 8 * g_;
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const size_t o = offk + 32 * j;
-                if (BF16) {
-                    if (OUT) q[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + o);
-                    k[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.k) + o);
-                } else {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        if (OUT) qx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + o)[hh];
-                        kx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.k) + o)[hh];
-                    }
-                }
-            }
-            vmask = 0;
-#pragma unroll
-            for (int n = 0; n < NVT; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tv = t0 + 16 * w_ + 4 * g_ + i;
-                    const bool vv = tv < T;
-                    vmask |= vv ? (1u << (4 * n + i)) : 0u;
-                    const size_t off = baseV + (size_t)(vv ? tv : T - 1) * tokV + 16 * n + r_;
-                    w[n][i] = a.wg[off];
-                    if (BF16) v[n][i] = reinterpret_cast<const uint16_t *>(a.v)[off];
-                    else v[n][i] = reinterpret_cast<const uint32_t *>(a.v)[off];
-                }
-        }
-
-        __device__ __forceinline__ void unpack(float (&qf)[NKS][8], float (&kf)[NKS][8], float (&laf)[NKS][8],
-                                               float (&bgf)[NKS][8], float (&z)[NVT][4]) const {
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                if (BF16) {
-                    const uint32_t qw[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
-                    const uint32_t kw[4] = {k[j].x, k[j].y, k[j].z, k[j].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (OUT) {
-                            qf[j][2 * i] = __builtin_bit_cast(float, qw[i] << 16);
-                            qf[j][2 * i + 1] = __builtin_bit_cast(float, qw[i] & 0xffff0000u);
-                        }
-                        kf[j][2 * i] = __builtin_bit_cast(float, kw[i] << 16);
-                        kf[j][2 * i + 1] = __builtin_bit_cast(float, kw[i] & 0xffff0000u);
-                    }
-                } else {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        if (OUT) {
-                            qf[j][4 * hh + 0] = qx[j][hh].x; qf[j][4 * hh + 1] = qx[j][hh].y;
-                            qf[j][4 * hh + 2] = qx[j][hh].z; qf[j][4 * hh + 3] = qx[j][hh].w;
-                        }
-                        kf[j][4 * hh + 0] = kx[j][hh].x; kf[j][4 * hh + 1] = kx[j][hh].y;
-                        kf[j][4 * hh + 2] = kx[j][hh].z; kf[j][4 * hh + 3] = kx[j][hh].w;
-                    }
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    laf[j][4 * hh + 0] = la[j][hh].x; laf[j][4 * hh + 1] = la[j][hh].y;
-                    laf[j][4 * hh + 2] = la[j][hh].z; laf[j][4 * hh + 3] = la[j][hh].w;
-                    bgf[j][4 * hh + 0] = bg[j][hh].x; bgf[j][4 * hh + 1] = bg[j][hh].y;
-                    bgf[j][4 * hh + 2] = bg[j][hh].z; bgf[j][4 * hh + 3] = bg[j][hh].w;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (OUT) qf[j][i] = vk ? qf[j][i] : 0.f;
-                    kf[j][i] = vk ? kf[j][i] : 0.f;
-                    laf[j][i] = vk ? laf[j][i] : 0.f;
-                    bgf[j][i] = vk ? bgf[j][i] : 0.f;
-                }
-            }
-#pragma unroll
-            for (int n = 0; n < NVT; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float vf = BF16 ? __builtin_bit_cast(float, v[n][i] << 16) : __builtin_bit_cast(float, v[n][i]);
-                    z[n][i] = ((vmask >> (4 * n + i)) & 1u) ? w[n][i] * vf : 0.f;
-                }
-        }
-    };
-    Raw raw;
-    raw.issue_gates(a, 0, T, w, r, g, baseK, tokK);
-    raw.issue_qkvw(a, 0, T, w, r, g, baseK, tokK, baseV, tokV);
 
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * kChunk;
@@ -219,16 +104,60 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             }
         }
 
-        // ---- this chunk's inputs (loaded during the previous chunk) ----
-        float qf[NKS][8], kf[NKS][8], laf[NKS][8], bgf[NKS][8], z[NVT][4];
-        raw.unpack(qf, kf, laf, bgf, z);
+        // ---- inputs: key side in token-row layout (channels 32j + 8g + i), value side in D layout ----
+        // Loads are unconditional, from addresses clamped into the tensors (no branch, no early
+        // wait between them); tokens past the end are zeroed when the values are unpacked.
+        const int tk = t0 + 16 * w + r;
+        const bool vk = tk < T;
+        const size_t offk = baseK + (size_t)(vk ? tk : T - 1) * tokK + 8 * g;
+        uint4 qraw[NKS], kraw[NKS];            // bf16 q, k (8 channels per uint4)
+        float4 qx[NKS][2], kx[NKS][2];         // fp32 q, k
+        float4 la4[NKS][2], bg4[NKS][2];
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+            const size_t o = offk + 32 * j;
+            if (BF16) {
+                if (OUT) qraw[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.q) + o);
+                kraw[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.k) + o);
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    if (OUT) qx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + o)[hh];
+                    kx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.k) + o)[hh];
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                la4[j][hh] = reinterpret_cast<const float4 *>(a.la + o)[hh];
+                bg4[j][hh] = reinterpret_cast<const float4 *>(a.bg + o)[hh];
+            }
+        }
+        // element i of block j of a packed input row
+        auto unpack8 = [&](const uint4 &raw, const float4 (&fx)[2], float (&out)[8]) {
+            if (BF16) {
+                const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    out[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+                    out[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+                }
+            } else {
+                out[0] = fx[0].x; out[1] = fx[0].y; out[2] = fx[0].z; out[3] = fx[0].w;
+                out[4] = fx[1].x; out[5] = fx[1].y; out[6] = fx[1].z; out[7] = fx[1].w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) out[i] = vk ? out[i] : 0.f;
+        };
 
         // ---- cumulative log2-decay over the chunk (fp32) ----
         float G[NKS][8];
 #pragma unroll
-        for (int j = 0; j < NKS; ++j)
+        for (int j = 0; j < NKS; ++j) {
+            const float lv[8] = {la4[j][0].x, la4[j][0].y, la4[j][0].z, la4[j][0].w,
+                                 la4[j][1].x, la4[j][1].y, la4[j][1].z, la4[j][1].w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) G[j][i] = row_scan16(laf[j][i] * kLog2e);
+            for (int i = 0; i < 8; ++i) G[j][i] = row_scan16(vk ? lv[i] * kLog2e : 0.f);
+        }
         if (r == 15) {
 #pragma unroll
             for (int j = 0; j < NKS; ++j) {
@@ -239,53 +168,55 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             }
         }
         __syncthreads();
-        float gC[NKS][8];
+        // decay of the chunk, gamma = exp(g_C), for the key rows of this wave's state tiles
+        float gam[NTS][4];
 #pragma unroll
-        for (int j = 0; j < NKS; ++j) {
+        for (int s = 0; s < NTS; ++s) {
+            const int id = w * NTS + s, m = id / NVT;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) gC[j][i] = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                const float4 u0 = *reinterpret_cast<const float4 *>(&sTot[w2 * DK + 32 * j + 8 * g]);
-                const float4 u1 = *reinterpret_cast<const float4 *>(&sTot[w2 * DK + 32 * j + 8 * g + 4]);
-                const float tv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    gC[j][i] += tv[i];
-                    if (w2 < w) G[j][i] += tv[i];
-                }
-            }
-            if (w == 0 && r == 0) {
-                *reinterpret_cast<float4 *>(&sGC[32 * j + 8 * g]) =
-                    make_float4(gC[j][0], gC[j][1], gC[j][2], gC[j][3]);
-                *reinterpret_cast<float4 *>(&sGC[32 * j + 8 * g + 4]) =
-                    make_float4(gC[j][4], gC[j][5], gC[j][6], gC[j][7]);
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 16 * m + 4 * g + i;
+                gam[s][i] = exp2_fast((sTot[ch] + sTot[DK + ch]) + (sTot[2 * DK + ch] + sTot[3 * DK + ch]));
             }
         }
 
-        // ---- decay absorption and gating (fp32), split into MFMA operands ----
-        Split8 Et[NKS], Qt[NKS], Kh[NKS];
+        // ---- decay absorption and gating (fp32), split into MFMA operands, one 32-channel block at a time ----
+        Split8 Et[NKS], Qt[NKS];
 #pragma unroll
         for (int j = 0; j < NKS; ++j) {
-            float et[8], qt[8], kt[8], kh[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                float4 pre = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int w2 = 0; w2 < 3; ++w2) {
+                    if (w2 < w) {
+                        const float4 u = *reinterpret_cast<const float4 *>(&sTot[w2 * DK + 32 * j + 8 * g + 4 * hh]);
+                        pre.x += u.x; pre.y += u.y; pre.z += u.z; pre.w += u.w;
+                    }
+                }
+                G[j][4 * hh + 0] += pre.x; G[j][4 * hh + 1] += pre.y; G[j][4 * hh + 2] += pre.z; G[j][4 * hh + 3] += pre.w;
+            }
+            float qv[8], kv[8];
+            unpack8(qraw[j], qx[j], qv);
+            unpack8(kraw[j], kx[j], kv);
+            const float bv[8] = {bg4[j][0].x, bg4[j][0].y, bg4[j][0].z, bg4[j][0].w,
+                                 bg4[j][1].x, bg4[j][1].y, bg4[j][1].z, bg4[j][1].w};
+            float et[8], qt[8], kt[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float eg = exp2_fast(G[j][i]);
                 const float eng = exp2_fast(-G[j][i]);
-                const float ek = exp2_fast(gC[j][i] - G[j][i]);
-                et[i] = bgf[j][i] * kf[j][i] * eg;
-                qt[i] = OUT ? qf[j][i] * eg : 0.f;
-                kt[i] = kf[j][i] * eng;
-                kh[i] = kf[j][i] * ek;
+                et[i] = bv[i] * kv[i] * eg;       // kv is already zero past the end
+                qt[i] = OUT ? qv[i] * eg : 0.f;
+                kt[i] = kv[i] * eng;
             }
             Et[j] = split8(et);
             if (OUT) Qt[j] = split8(qt);
-            Kh[j] = split8(kh);
             const Split8 ks = split8(kt);
-            *reinterpret_cast<bf16x8 *>(&sR1[(16 * w + r) * PK + 32 * j + 8 * g]) = ks.hi;
-            *reinterpret_cast<bf16x8 *>(&sR1[R1 + (16 * w + r) * PK + 32 * j + 8 * g]) = ks.lo;
+            *reinterpret_cast<bf16x8 *>(&sK[(16 * w + r) * PK + 32 * j + 8 * g]) = ks.hi;
+            *reinterpret_cast<bf16x8 *>(&sK[RK + (16 * w + r) * PK + 32 * j + 8 * g]) = ks.lo;
+            GDN2_STEP_FENCE();
         }
-        if (c + 1 < NC) raw.issue_gates(a, t0 + kChunk, T, w, r, g, baseK, tokK);
         __syncthreads();
 
         // ---- A^T and P^T for this wave's query rows (keys from LDS) ----
@@ -296,9 +227,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < NKS; ++j) {
-                    Split8 kt;
-                    kt.hi = *reinterpret_cast<const bf16x8 *>(&sR1[(16 * mt + r) * PK + 32 * j + 8 * g]);
-                    kt.lo = *reinterpret_cast<const bf16x8 *>(&sR1[R1 + (16 * mt + r) * PK + 32 * j + 8 * g]);
+                    const Split8 kt = frag_8(&sK[(16 * mt + r) * PK + 32 * j + 8 * g],
+                                             &sK[RK + (16 * mt + r) * PK + 32 * j + 8 * g]);
                     if (FAST) accA = mfma32(kt.hi, Et[j].hi, accA);
                     else accA = mfma32x3(kt, Et[j], accA);
                     if (OUT) accP = mfma32x3(kt, Qt[j], accP);
@@ -310,14 +240,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
                     if (!(key < qry)) accA[i] = 0.f;
                     if (!(key <= qry)) accP[i] = 0.f;
                 }
-                *reinterpret_cast<f32x4 *>(&sA[(16 * w + r) * PA + 16 * mt + 4 * g]) = accA;
+                *reinterpret_cast<f32x4 *>(&sAT[(16 * w + r) * PA + 16 * mt + 4 * g]) = accA;
                 if (OUT) Pf[mt] = split4(accP);
             } else if (OUT) {
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 Pf[mt] = split4(zero);
             }
+            GDN2_STEP_FENCE();
         }
 
+        // value-side inputs of this wave's rows, D layout (z = w * v)
+        float z[NVT][4];
+#pragma unroll
+        for (int n = 0; n < NVT; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tv = t0 + 16 * w + 4 * g + i;
+                const size_t off = baseV + (size_t)(tv < T ? tv : T - 1) * tokV + 16 * n + r;
+                const float zz = a.wg[off] * load1<BF16>(a.v, off, true);
+                z[n][i] = tv < T ? zz : 0.f;
+            }
         // ---- X = Z - Et S and Qt S for this wave's rows (S from LDS) ----
         f32x4 QS[NVT];
 #pragma unroll
@@ -326,55 +268,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NKS; ++j) {
-                Split8 sf;
-                sf.hi = *reinterpret_cast<const bf16x8 *>(&sS[(16 * n + r) * PK + 32 * j + 8 * g]);
-                sf.lo = *reinterpret_cast<const bf16x8 *>(&sS[VT * PK + (16 * n + r) * PK + 32 * j + 8 * g]);
+                const Split8 sf = frag_8(&sS[(16 * n + r) * PK + 32 * j + 8 * g],
+                                         &sS[VT * PK + (16 * n + r) * PK + 32 * j + 8 * g]);
                 if (FAST) accX = mfma32(Et[j].hi, sf.hi, accX);
                 else accX = mfma32x3(Et[j], sf, accX);
                 if (OUT) accQ = mfma32x3(Qt[j], sf, accQ);
             }
-            const f32x4 X = -accX;  // lane holds X[16w + 4g + i][16n + r]
-            const Split4 xs = split4(X);
+            const Split4 xs = split4(-accX);  // lane holds X[16w + 4g + i][16n + r]
             *reinterpret_cast<bf16x4 *>(&sXU[(16 * n + r) * PT + 16 * w + 4 * g]) = xs.hi;
             *reinterpret_cast<bf16x4 *>(&sXU[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = xs.lo;
             QS[n] = accQ;
+            GDN2_STEP_FENCE();
         }
         __syncthreads();
 
-        if (c + 1 < NC) raw.issue_qkvw(a, t0 + kChunk, T, w, r, g, baseK, tokK, baseV, tokV);
-
-        // ---- Kh^T into R1 (Kt is no longer read) ----
-#pragma unroll
-        for (int j = 0; j < NKS; ++j)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int ch = 32 * j + 8 * g + i;
-                sR1[ch * PT + 16 * w + r] = Kh[j].hi[i];
-                sR1[R1 + ch * PT + 16 * w + r] = Kh[j].lo[i];
-            }
-
         // ---- T = (I + A)^-1 ----
-        solve_T<PA>(sA, sT, w, r, g);
+        solve_T_inplace<PA>(sAT, w, r, g);
 
         // ---- U = T X for this wave's rows ----
-        const int nkk = (w >= 2) ? 2 : 1;
         f32x4 accU[NVT];
 #pragma unroll
         for (int n = 0; n < NVT; ++n) accU[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             if (kk < nkk) {
-                const f32x4 t0v = *reinterpret_cast<const f32x4 *>(&sT[(16 * w + r) * PA + 32 * kk + 8 * g]);
-                const f32x4 t1v = *reinterpret_cast<const f32x4 *>(&sT[(16 * w + r) * PA + 32 * kk + 8 * g + 4]);
-                const float tr[8] = {t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
-                const Split8 ts = split8(tr);
+                const f32x4 t0v = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 32 * kk + 8 * g]);
+                const f32x4 t1v = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 32 * kk + 8 * g + 4]);
+                const Split8 ts = split8v(t0v, t1v);
 #pragma unroll
-                for (int n = 0; n < NVT; ++n) {
-                    Split8 xs;
-                    xs.hi = *reinterpret_cast<const bf16x8 *>(&sXU[(16 * n + r) * PT + 32 * kk + 8 * g]);
-                    xs.lo = *reinterpret_cast<const bf16x8 *>(&sXU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]);
-                    accU[n] = mfma32x3(ts, xs, accU[n]);
-                }
+                for (int n = 0; n < NVT; ++n)
+                    accU[n] = mfma32x3(ts, frag_8(&sXU[(16 * n + r) * PT + 32 * kk + 8 * g],
+                                                  &sXU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), accU[n]);
             }
         }
         __syncthreads();
@@ -386,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         }
         __syncthreads();
 
-        // ---- O = Qt S + P U (P from registers, key index permuted to match) ----
+        // ---- O = Qt S + P U (P from registers, key index in the 4-group order) ----
         if (OUT) {
 #pragma unroll
             for (int n = 0; n < NVT; ++n) {
@@ -394,28 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (kk < nkk) {
-                        Split8 pf, us;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pf.hi[i] = Pf[2 * kk].hi[i];
-                            pf.hi[4 + i] = Pf[2 * kk + 1].hi[i];
-                            pf.lo[i] = Pf[2 * kk].lo[i];
-                            pf.lo[4 + i] = Pf[2 * kk + 1].lo[i];
-                        }
                         const __bf16 *uh = &sXU[(16 * n + r) * PT + 32 * kk];
                         const __bf16 *ul = &sXU[VT * PT + (16 * n + r) * PT + 32 * kk];
-                        const bf16x4 h0 = *reinterpret_cast<const bf16x4 *>(uh + 4 * g);
-                        const bf16x4 h1 = *reinterpret_cast<const bf16x4 *>(uh + 16 + 4 * g);
-                        const bf16x4 l0 = *reinterpret_cast<const bf16x4 *>(ul + 4 * g);
-                        const bf16x4 l1 = *reinterpret_cast<const bf16x4 *>(ul + 16 + 4 * g);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            us.hi[i] = h0[i];
-                            us.hi[4 + i] = h1[i];
-                            us.lo[i] = l0[i];
-                            us.lo[4 + i] = l1[i];
-                        }
-                        acc = mfma32x3(pf, us, acc);
+                        acc = mfma32x3(join(Pf[2 * kk], Pf[2 * kk + 1]),
+                                       frag_2x4(uh + 4 * g, uh + 16 + 4 * g, ul + 4 * g, ul + 16 + 4 * g), acc);
                     }
                 }
 #pragma unroll
@@ -423,29 +329,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
                     const int to = t0 + 16 * w + 4 * g + i;
                     if (to < T) a.o[baseV + (size_t)to * tokV + 16 * n + r] = acc[i];
                 }
+                GDN2_STEP_FENCE();
             }
         }
 
-        // ---- S' = diag(gamma) S + Kh^T U (this wave's tiles of S) ----
+        // ---- S' = diag(gamma) S + Kh^T U = diag(gamma) (S + Kt^T U), this wave's tiles of S ----
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
             const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-            f32x4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = S[s][i] * exp2_fast(sGC[16 * m + 4 * g + i]);
+            f32x4 acc = S[s];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                Split8 kh, us;
-                kh.hi = *reinterpret_cast<const bf16x8 *>(&sR1[(16 * m + r) * PT + 32 * kk + 8 * g]);
-                kh.lo = *reinterpret_cast<const bf16x8 *>(&sR1[R1 + (16 * m + r) * PT + 32 * kk + 8 * g]);
-                us.hi = *reinterpret_cast<const bf16x8 *>(&sXU[(16 * n + r) * PT + 32 * kk + 8 * g]);
-                us.lo = *reinterpret_cast<const bf16x8 *>(&sXU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]);
-                acc = mfma32x3(kh, us, acc);
+                const Split8 kh = frag_tr<PK>(sK, sK + RK, 32 * kk, 16 * m, r, g);   // Kt^T
+                const __bf16 *uh = &sXU[(16 * n + r) * PT + 32 * kk];
+                const __bf16 *ul = &sXU[VT * PT + (16 * n + r) * PT + 32 * kk];
+                acc = mfma32x3(kh, frag_2x4(uh + 4 * g, uh + 16 + 4 * g, ul + 4 * g, ul + 16 + 4 * g), acc);
             }
-            S[s] = acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[s][i];
+            GDN2_STEP_FENCE();
         }
         store_state_lds();
-        // the next chunk's first barrier orders these writes before their reads
+        __syncthreads();
     }
 
     if (a.S_final) {
@@ -468,8 +373,9 @@ static bool vt_ok(int dk, int vt, int dv) {
 }
 
 int fwd_value_tile(int B, int H, int dk, int dv) {
-    int vt = dv < 64 ? dv : 64;
-    while (vt > 16 && (long)B * H * (dv / vt) < 256 && vt_ok(dk, vt / 2, dv)) vt /= 2;
+    // two workgroups fit on a CU at 32-column tiles; aim for >= 512 workgroups
+    int vt = dv < 32 ? dv : 32;
+    while (vt > 16 && (long)B * H * (dv / vt) < 512 && vt_ok(dk, vt / 2, dv)) vt /= 2;
     return vt;
 }
 
