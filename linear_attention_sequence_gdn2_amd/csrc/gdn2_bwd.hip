@@ -400,40 +400,59 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reverse_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // chunk-parallel gradients of every token input
 // ---------------------------------------------------------------------------
+// Eight waves in two halves of four.  Wave (hf, w) owns the 16 tokens 16w..16w+15 in
+// both halves; for the key-side element work and the key-side gradients it owns
+// channels of its half only (hf * DK/2 .. +DK/2), in the 4-group layout; on the value
+// side it computes the 16x16 tiles (token block w, column block hf) of X, U, dU and dX
+// of each 32-column value tile.  The operand rows Kt and Et stay in LDS for the whole
+// chunk, so one workgroup takes most of a CU's LDS and the two halves give every SIMD
+// two waves.
+constexpr int kChunkThreads = 2 * kThreads;
+
+// Keep the scheduler from hoisting the LDS fragment loads of later unrolled steps
+// above this point (bounds the live registers at two waves per SIMD).
+#define GDN2_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 template <int DK, bool BF16>
-__global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
-    constexpr int VT = 32, NVT = 2;
-    constexpr int NE = DK / 4, NM = DK / 16, NKS = DK / 32;
-    constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4, PC = VT + 8;
-    constexpr int RQ = kChunk * PK, RT = DK * PT;
+__global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
+    constexpr int NTH = kChunkThreads;
+    constexpr int VT = 32;                       // value columns per tile
+    constexpr int NKS = DK / 32;                 // 32-channel contraction steps
+    constexpr int NMH = DK / 32;                 // 16-channel key tiles per half
+    constexpr int NEH = 4 * NMH;                 // key elements per lane
+    constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4, PS = VT + 8;
+    constexpr int RK = kChunk * PK;              // one [token][channel] bf16 plane
+    constexpr int NSF = (DK * 8 + NTH - 1) / NTH;   // float4 of a state tile per thread
     constexpr bool FAST = BF16;
-    // loop-phase layout (bf16 element offsets), hi plane then lo plane for each
-    constexpr int oS1 = 0;                         // S  [col][channel]
-    constexpr int oS2 = oS1 + 2 * VT * PK;         // S  [channel][col]
-    constexpr int oD1 = oS2 + 2 * DK * PC;         // dS' [col][channel]
-    constexpr int oD2 = oD1 + 2 * VT * PK;         // dS' [channel][col]
-    constexpr int oO1 = oD2 + 2 * DK * PC;         // dO [col][token]
-    constexpr int oO2 = oO1 + 2 * VT * PT;         // dO [token][col]
-    constexpr int oX1 = oO2 + 2 * kChunk * PC;     // X  [col][token]
-    constexpr int oU2 = oX1 + 2 * VT * PT;         // U  [token][col]
-    constexpr int odU1 = oU2 + 2 * kChunk * PC;    // dU [col][token]
-    constexpr int odX2 = odU1 + 2 * VT * PT;       // -dX [token][col]
-    constexpr int LOOP_END = odX2 + 2 * kChunk * PC;
-    constexpr int PREP_END = 4 * RQ + 2 * kChunk * PA;     // Kt, Qt rows + fp32 A
-    constexpr int EPI_END = 4 * RT + 4 * kChunk * PT;
-    constexpr int ZSIZE = LOOP_END > PREP_END ? (LOOP_END > EPI_END ? LOOP_END : EPI_END)
-                                              : (PREP_END > EPI_END ? PREP_END : EPI_END);
-    constexpr int CPT = DK / 8;   // columns (or channels) per thread when staging state tiles
-    constexpr int TPC = kThreads / DK;
+    // LDS (byte offsets).  Whole chunk: Kt and Et rows [token][channel] (hi, lo).
+    // Value loop: S and gamma*dS' tiles as [channel][col]; dO, X then U, dU then -dX as
+    // [col][token]; A then T (fp32).  Preparation puts the Qt rows where the value tiles go;
+    // the epilogue puts Qt rows, dP^T and dA^T ([key][query]) and scratch over the value
+    // tiles and T.
+    constexpr int B_ROWS = 2 * RK * 2, B_ST = 2 * DK * PS * 2, B_VT = 2 * VT * PT * 2, B_PT = 2 * kChunk * PT * 2;
+    constexpr int oKt = 0, oEt = oKt + B_ROWS, oLoop = oEt + B_ROWS;
+    constexpr int oS1 = oLoop, oD1 = oS1 + B_ST, oO1 = oD1 + B_ST, oXU = oO1 + B_VT, odUX = oXU + B_VT;
+    constexpr int oAT = odUX + B_VT, oTot = oAT + kChunk * PA * 4, oGam = oTot + 4 * DK * 4, oDG = oGam + DK * 4;
+    constexpr int SMEM = oDG + DK * 4;
+    constexpr int oQt = oLoop, odPt = oQt + B_ROWS, odAt = odPt + B_PT;
+    constexpr int oScr = odAt + B_PT, oTotA = oScr + 8 * DK * 4, oTotB = oTotA + 4 * DK * 4;
+    static_assert(oQt + B_ROWS <= oAT, "Qt rows overlap T during preparation");
+    static_assert(oTotB + 4 * DK * 4 <= oTot, "epilogue layout overlaps the decay totals");
+    static_assert(SMEM <= 160 * 1024, "LDS budget of a CU");
 
-    __shared__ __align__(16) __bf16 sZ[ZSIZE];
-    __shared__ __align__(16) float sT[kChunk * PA];
-    __shared__ __align__(16) float sTot[4 * DK];
-    __shared__ __align__(16) float sTot2[4 * DK];
-    __shared__ __align__(16) float sTot3[4 * DK];
-    __shared__ __align__(16) float sDG[kThreads];
+    __shared__ __align__(16) char smem[SMEM];
+    __bf16 *sKt = reinterpret_cast<__bf16 *>(smem + oKt), *sEt = reinterpret_cast<__bf16 *>(smem + oEt);
+    __bf16 *sQt = reinterpret_cast<__bf16 *>(smem + oQt);
+    __bf16 *S1 = reinterpret_cast<__bf16 *>(smem + oS1), *D1 = reinterpret_cast<__bf16 *>(smem + oD1);
+    __bf16 *O1 = reinterpret_cast<__bf16 *>(smem + oO1), *XU = reinterpret_cast<__bf16 *>(smem + oXU);
+    __bf16 *dUX = reinterpret_cast<__bf16 *>(smem + odUX);
+    __bf16 *dPt = reinterpret_cast<__bf16 *>(smem + odPt), *dAt = reinterpret_cast<__bf16 *>(smem + odAt);
+    float *sAT = reinterpret_cast<float *>(smem + oAT), *sTot = reinterpret_cast<float *>(smem + oTot);
+    float *sGam = reinterpret_cast<float *>(smem + oGam), *sDG = reinterpret_cast<float *>(smem + oDG);
+    float *sScr = reinterpret_cast<float *>(smem + oScr);
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
+    const int n = hf;                            // value column block of this wave's tiles
     const int NC = (a.T + kChunk - 1) / kChunk;
     const int L = xcd_swizzle(blockIdx.x, gridDim.x);
     const int c = L % NC, bh = L / NC, h = bh % a.H, b = bh / a.H;
@@ -448,404 +467,414 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     const int tk = t0 + 16 * w + r;
     const bool vk = tk < T;
     const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
+    const int chh = hf * (DK / 2);               // first key channel of this half
+    auto ch = [&](int e) { return chh + ch4(e, g); };
 
-    for (int idx = tid; idx < kChunk * PA; idx += kThreads) sT[idx] = 0.f;
-
-    // ---- key side, A, P, T ----
-    // Only Et (for X) and Kh (for dU) stay in registers through the value loop;
-    // Qt and Kt are formed again in the epilogue from a second read of the inputs.
-    Split8 Ekeep[NKS], Hkeep[NKS];
-    Split4 Pt[4];
-    float *sA = reinterpret_cast<float *>(sZ + 4 * RQ);
-    {
-        KeyOps<NKS> ops;
-        {
-            KeyRaw4<DK, BF16> raw;
-            raw.issue(a, rowK, g, vk);
-            float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
-            raw.unpack(qf, kf, laf, bgf);
+    // ---- value-tile inputs, loaded one tile ahead into registers ----
+    struct Tile {
+        float4 s[NSF], d[NSF];   // S and dS' (channel idx/8, columns 4*(idx%8)..+3)
+        float o[4];              // dO (column tid%32, tokens 4*(tid/32)..+3)
+        float v[4], wg[4];       // v and w of this wave's X tile, D layout
+    };
+    auto load_tile = [&](int j0, Tile &x, int tid) {
+        const int w = (tid >> 6) & 3, n = tid >> 8, r = tid & 15, g = (tid >> 4) & 3;
 #pragma unroll
-            for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
-            chunk_scan<NE, DK>(G, gC, sTot, w, r, [&](int e) { return ch4(e, g); });
-            key_operands<NE>(qf, kf, bgf, G, gC, ops);
+        for (int it = 0; it < NSF; ++it) {
+            int idx = tid + NTH * it;
+            idx = idx < DK * 8 ? idx : 0;
+            const size_t off = stoff + (size_t)(idx >> 3) * DV + j0 + 4 * (idx & 7);
+            x.s[it] = *reinterpret_cast<const float4 *>(a.states + off);
+            x.d[it] = *reinterpret_cast<const float4 *>(a.dstates + off);
         }
-        store_rows<NKS, PK>(ops.K, sZ, sZ + RQ, 16 * w + r, g);
-        store_rows<NKS, PK>(ops.Q, sZ + 2 * RQ, sZ + 3 * RQ, 16 * w + r, g);
-        __syncthreads();
-        build_A_Pt<NKS, PK, PA, FAST>(ops, sZ, sZ + RQ, sZ + 2 * RQ, sZ + 3 * RQ, sA, Pt, w, r, g);
+        {
+            const int col = tid & 31, tg = tid >> 5;
 #pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-            Ekeep[j] = ops.E[j];
-            Hkeep[j] = ops.H[j];
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 4 * tg + i;
+                x.o[i] = a.dO[baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + col];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * w + 4 * g + i;
+            const size_t off = baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + 16 * n + r;
+            x.v[i] = load1<BF16>(a.v, off, true);
+            x.wg[i] = a.wg[off];
+        }
+    };
+
+    for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
+    KeyRaw4<DK / 2, BF16> raw;
+    raw.issue(a, rowK + chh, g, vk);
+    Tile cur;
+    load_tile(0, cur, tid);
+
+    // ---- preparation: decay, operand rows, A -> T, P^T rows in registers ----
+    {
+        float qf[NEH], kf[NEH], laf[NEH], bgf[NEH], G[NEH], gC[NEH];
+        raw.unpack(qf, kf, laf, bgf);
+#pragma unroll
+        for (int e = 0; e < NEH; ++e) G[e] = laf[e] * kLog2e;
+        chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
+        if (w == 0 && r == 0) {
+#pragma unroll
+            for (int e = 0; e < NEH; ++e) sGam[ch(e)] = exp2_fast(gC[e]);
+        }
+#pragma unroll
+        for (int mm = 0; mm < NMH; ++mm) {
+            f32x4 et, qt, kt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * mm + i;
+                const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]);
+                et[i] = bgf[e] * kf[e] * eg;
+                qt[i] = qf[e] * eg;
+                kt[i] = kf[e] * eng;
+            }
+            const int o = (16 * w + r) * PK + chh + 16 * mm + 4 * g;
+            const Split4 se = split4(et), sq = split4(qt), sk = split4(kt);
+            *reinterpret_cast<bf16x4 *>(&sEt[o]) = se.hi;
+            *reinterpret_cast<bf16x4 *>(&sEt[RK + o]) = se.lo;
+            *reinterpret_cast<bf16x4 *>(&sQt[o]) = sq.hi;
+            *reinterpret_cast<bf16x4 *>(&sQt[RK + o]) = sq.lo;
+            *reinterpret_cast<bf16x4 *>(&sKt[o]) = sk.hi;
+            *reinterpret_cast<bf16x4 *>(&sKt[RK + o]) = sk.lo;
         }
     }
     __syncthreads();
-    solve_T<PA>(sA, sT, w, r, g);
-
-    // ---- value tiles ----
-    f32x4 aQ[NM], aE[NM], aH[NM], aP[4], aA[4];
+    Split4 Pt[4];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) aQ[m] = aE[m] = aH[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int n = 0; n < 4; ++n) aP[n] = aA[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dgp = 0.f;
-
-    __bf16 *S1 = sZ + oS1, *S2 = sZ + oS2, *D1 = sZ + oD1, *D2 = sZ + oD2, *O1 = sZ + oO1, *O2 = sZ + oO2;
-    __bf16 *X1 = sZ + oX1, *U2 = sZ + oU2, *dU1 = sZ + odU1, *dX2 = sZ + odX2;
-
-    for (int j0 = 0; j0 < DV; j0 += VT) {
-        // S and dS' tiles, both layouts; partial of dgamma = rowsum(dS' * S)
-        {
-            const int cA = tid / TPC, cb = (tid % TPC) * CPT;
-            const float *Sg = a.states + stoff + (size_t)cA * DV + j0 + cb;
-            const float *Dg = a.dstates + stoff + (size_t)cA * DV + j0 + cb;
-#pragma unroll
-            for (int q4 = 0; q4 < CPT / 4; ++q4) {
-                const f32x4 sv = *reinterpret_cast<const f32x4 *>(Sg + 4 * q4);
-                const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(Dg + 4 * q4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dgp += sv[i] * dv4[i];
-                const Split4 ss = split4(sv), ds = split4(dv4);
-                *reinterpret_cast<bf16x4 *>(&S2[cA * PC + cb + 4 * q4]) = ss.hi;
-                *reinterpret_cast<bf16x4 *>(&S2[DK * PC + cA * PC + cb + 4 * q4]) = ss.lo;
-                *reinterpret_cast<bf16x4 *>(&D2[cA * PC + cb + 4 * q4]) = ds.hi;
-                *reinterpret_cast<bf16x4 *>(&D2[DK * PC + cA * PC + cb + 4 * q4]) = ds.lo;
-            }
-            const int cB = tid % VT, chb = (tid / VT) * CPT;
-#pragma unroll
-            for (int q4 = 0; q4 < CPT / 4; ++q4) {
-                f32x4 sv, dv4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sv[i] = a.states[stoff + (size_t)(chb + 4 * q4 + i) * DV + j0 + cB];
-                    dv4[i] = a.dstates[stoff + (size_t)(chb + 4 * q4 + i) * DV + j0 + cB];
-                }
-                const Split4 ss = split4(sv), ds = split4(dv4);
-                *reinterpret_cast<bf16x4 *>(&S1[cB * PK + chb + 4 * q4]) = ss.hi;
-                *reinterpret_cast<bf16x4 *>(&S1[VT * PK + cB * PK + chb + 4 * q4]) = ss.lo;
-                *reinterpret_cast<bf16x4 *>(&D1[cB * PK + chb + 4 * q4]) = ds.hi;
-                *reinterpret_cast<bf16x4 *>(&D1[VT * PK + cB * PK + chb + 4 * q4]) = ds.lo;
-            }
-        }
-        // dO tile, both layouts
-        {
-            const int col = tid % VT, tg = tid / VT;   // 8 tokens per thread
-            f32x4 x0, x1;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = t0 + 8 * tg + i;
-                const float vv = a.dO[baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + col];
-                if (i < 4) x0[i] = t < T ? vv : 0.f;
-                else x1[i - 4] = t < T ? vv : 0.f;
-            }
-            const Split4 p0 = split4(x0), p1 = split4(x1);
-            *reinterpret_cast<bf16x4 *>(&O1[col * PT + 8 * tg]) = p0.hi;
-            *reinterpret_cast<bf16x4 *>(&O1[col * PT + 8 * tg + 4]) = p1.hi;
-            *reinterpret_cast<bf16x4 *>(&O1[VT * PT + col * PT + 8 * tg]) = p0.lo;
-            *reinterpret_cast<bf16x4 *>(&O1[VT * PT + col * PT + 8 * tg + 4]) = p1.lo;
-            const int tok = tid / 4, cq = (tid % 4) * 8;
-            const int t = t0 + tok;
-            const float *src = a.dO + baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + cq;
-            f32x4 y0 = *reinterpret_cast<const f32x4 *>(src), y1 = *reinterpret_cast<const f32x4 *>(src + 4);
-            if (!(t < T)) y0 = y1 = f32x4{0.f, 0.f, 0.f, 0.f};
-            const Split4 q0 = split4(y0), q1 = split4(y1);
-            *reinterpret_cast<bf16x4 *>(&O2[tok * PC + cq]) = q0.hi;
-            *reinterpret_cast<bf16x4 *>(&O2[tok * PC + cq + 4]) = q1.hi;
-            *reinterpret_cast<bf16x4 *>(&O2[kChunk * PC + tok * PC + cq]) = q0.lo;
-            *reinterpret_cast<bf16x4 *>(&O2[kChunk * PC + tok * PC + cq + 4]) = q1.lo;
-        }
-        // v, w of this wave's rows in D layout
-        float vD[NVT][4], wD[NVT][4];
-#pragma unroll
-        for (int n = 0; n < NVT; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 16 * w + 4 * g + i;
-                const size_t off = baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + 16 * n + r;
-                const float vv = BF16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t *>(a.v)[off])
-                                      : reinterpret_cast<const float *>(a.v)[off];
-                const float ww = a.wg[off];
-                vD[n][i] = t < T ? vv : 0.f;
-                wD[n][i] = t < T ? ww : 0.f;
-            }
-        __syncthreads();
-
-        // X = Z - Et S
-#pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-            f32x4 acc = {-wD[n][0] * vD[n][0], -wD[n][1] * vD[n][1], -wD[n][2] * vD[n][2], -wD[n][3] * vD[n][3]};
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const Split8 sf = row_frag4<PK>(S1, S1 + VT * PK, 16 * n + r, j, g);
-                if (FAST) acc = mfma32(Ekeep[j].hi, sf.hi, acc);
-                else acc = mfma32x3(Ekeep[j], sf, acc);
-            }
-            const Split4 sp = split4(-acc);
-            *reinterpret_cast<bf16x4 *>(&X1[(16 * n + r) * PT + 16 * w + 4 * g]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&X1[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sp.lo;
-        }
-        __syncthreads();
-        // U = T X  -> [token][col];  dU = P^T dO + Kh dS' -> [col][token]
-#pragma unroll
-        for (int n = 0; n < NVT; ++n) {
+    for (int mt = 0; mt < 4; ++mt) {
+        // A block (queries of block w, keys of block mt); the two halves share them out
+        if (mt <= w && (mt & 1) == hf) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk < nkk) {
-                    const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sT[(16 * w + r) * PA + 32 * kk + 8 * g]);
-                    const f32x4 tb = *reinterpret_cast<const f32x4 *>(&sT[(16 * w + r) * PA + 32 * kk + 8 * g + 4]);
-                    acc = mfma32x3(split8v(ta, tb), frag_8(&X1[(16 * n + r) * PT + 32 * kk + 8 * g],
-                                                          &X1[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), acc);
-                }
+            for (int j = 0; j < NKS; ++j) {
+                const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g);
+                const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
+                if (FAST) acc = mfma32(kf.hi, ef.hi, acc);
+                else acc = mfma32x3(kf, ef, acc);
             }
-            const Split4 su = split4(acc);
+            // lane holds A[16w + r][16mt + 4g + i]
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                U2[(16 * w + 4 * g + i) * PC + 16 * n + r] = su.hi[i];
-                U2[kChunk * PC + (16 * w + 4 * g + i) * PC + 16 * n + r] = su.lo[i];
+            for (int i = 0; i < 4; ++i)
+                if (!(16 * mt + 4 * g + i < 16 * w + r)) acc[i] = 0.f;
+            *reinterpret_cast<f32x4 *>(&sAT[(16 * w + r) * PA + 16 * mt + 4 * g]) = acc;
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (mt >= w) {
+#pragma unroll
+            for (int j = 0; j < NKS; ++j)
+                acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
+                               row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
+            // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
+        }
+        Pt[mt] = split4(acc);
+    }
+    __syncthreads();
+    solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
+    float gm[NSF];
+#pragma unroll
+    for (int it = 0; it < NSF; ++it) {
+        const int idx = tid + NTH * it;
+        gm[it] = sGam[(idx < DK * 8 ? idx : 0) >> 3];
+    }
+
+    // ---- value tiles: X, U, dU, dX and the key-side accumulators ----
+    f32x4 aQ[NMH], aE[NMH], aH[NMH], aPA[4];     // aPA: dP (half 0) or dA (half 1)
+#pragma unroll
+    for (int m = 0; m < NMH; ++m) aQ[m] = aE[m] = aH[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) aPA[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgp[NSF];
+#pragma unroll
+    for (int it = 0; it < NSF; ++it) dgp[it] = 0.f;
+
+    for (int j0 = 0; j0 < DV; j0 += VT) {
+        // lane indices afresh from an opaque copy of the thread index: the address
+        // arithmetic is redone each tile instead of being held in registers
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
+        const int n = hf;
+        const int kk_lo = (w >= 2) ? 1 : 0;
+        const int nkk = (w >= 2) ? 2 : 1;
+        // stage S, gamma*dS' ([channel][col]) and dO ([col][token]); dgamma partial sums
+#pragma unroll
+        for (int it = 0; it < NSF; ++it) {
+            const int idx = tid + NTH * it;
+            if (idx < DK * 8) {
+                const int chn = idx >> 3, q = idx & 7;
+                const float4 sv = cur.s[it], dv = cur.d[it];
+                dgp[it] += (sv.x * dv.x + sv.y * dv.y) + (sv.z * dv.z + sv.w * dv.w);
+                const Split4 ss = split4(f32x4{sv.x, sv.y, sv.z, sv.w});
+                const Split4 ds = split4(f32x4{dv.x, dv.y, dv.z, dv.w} * gm[it]);
+                *reinterpret_cast<bf16x4 *>(&S1[chn * PS + 4 * q]) = ss.hi;
+                *reinterpret_cast<bf16x4 *>(&S1[DK * PS + chn * PS + 4 * q]) = ss.lo;
+                *reinterpret_cast<bf16x4 *>(&D1[chn * PS + 4 * q]) = ds.hi;
+                *reinterpret_cast<bf16x4 *>(&D1[DK * PS + chn * PS + 4 * q]) = ds.lo;
             }
+        }
+        {
+            const int col = tid & 31, tg = tid >> 5;
+            f32x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = (t0 + 4 * tg + i < T) ? cur.o[i] : 0.f;
+            const Split4 so = split4(ov);
+            *reinterpret_cast<bf16x4 *>(&O1[col * PT + 4 * tg]) = so.hi;
+            *reinterpret_cast<bf16x4 *>(&O1[VT * PT + col * PT + 4 * tg]) = so.lo;
+        }
+        float vD[4], wD[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = t0 + 16 * w + 4 * g + i < T;
+            vD[i] = ok ? cur.v[i] : 0.f;
+            wD[i] = ok ? cur.wg[i] : 0.f;
+        }
+        __syncthreads();
+        // next tile's loads are in flight during this tile's products
+        load_tile(j0 + VT < DV ? j0 + VT : j0, cur, tid);
+
+        // X = Z - Et S and dU = P^T dO + Kt (gamma dS'): tile (token block w, column block n)
+        {
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = -(wD[i] * vD[i]);
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
+                const Split8 sf = frag_tr<PS>(S1, S1 + DK * PS, 32 * j, 16 * n, r, g);
+                if (FAST) acc = mfma32(ef.hi, sf.hi, acc);
+                else acc = mfma32x3(ef, sf, acc);
+                if (j & 1) GDN2_SCHED_FENCE();
+            }
+            const Split4 sx = split4(-acc);    // lane holds X[16w + 4g + i][16n + r]
+            *reinterpret_cast<bf16x4 *>(&XU[(16 * n + r) * PT + 16 * w + 4 * g]) = sx.hi;
+            *reinterpret_cast<bf16x4 *>(&XU[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sx.lo;
             f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 if (kk >= kk_lo) {
-                    const Split8 of = frag_2x4(&O1[(16 * n + r) * PT + 32 * kk + 4 * g],
-                                               &O1[(16 * n + r) * PT + 32 * kk + 16 + 4 * g],
-                                               &O1[VT * PT + (16 * n + r) * PT + 32 * kk + 4 * g],
-                                               &O1[VT * PT + (16 * n + r) * PT + 32 * kk + 16 + 4 * g]);
-                    du = mfma32x3(join(Pt[2 * kk], Pt[2 * kk + 1]), of, du);
+                    const __bf16 *oh = &O1[(16 * n + r) * PT + 32 * kk], *ol = oh + VT * PT;
+                    du = mfma32x3(join(Pt[2 * kk], Pt[2 * kk + 1]),
+                                  frag_2x4(oh + 4 * g, oh + 16 + 4 * g, ol + 4 * g, ol + 16 + 4 * g), du);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < NKS; ++j) du = mfma32x3(Hkeep[j], row_frag4<PK>(D1, D1 + VT * PK, 16 * n + r, j, g), du);
+            for (int j = 0; j < NKS; ++j) {
+                du = mfma32x3(row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g),
+                              frag_tr<PS>(D1, D1 + DK * PS, 32 * j, 16 * n, r, g), du);
+                GDN2_SCHED_FENCE();
+            }
             const Split4 sd = split4(du);
-            *reinterpret_cast<bf16x4 *>(&dU1[(16 * n + r) * PT + 16 * w + 4 * g]) = sd.hi;
-            *reinterpret_cast<bf16x4 *>(&dU1[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sd.lo;
+            *reinterpret_cast<bf16x4 *>(&dUX[(16 * n + r) * PT + 16 * w + 4 * g]) = sd.hi;
+            *reinterpret_cast<bf16x4 *>(&dUX[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sd.lo;
         }
         __syncthreads();
-        // dX = T^T dU; dv, dw; -dX -> [token][col]
+        // U = T X and dX = T^T dU (registers); dv = dX * w and dw = dX * v
+        f32x4 Ur = {0.f, 0.f, 0.f, 0.f}, dXr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk >= kk_lo) {
-                    float tv[8];
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) tv[s] = sT[(32 * kk + 8 * g + s) * PA + 16 * w + r];
-                    acc = mfma32x3(split8(tv), frag_8(&dU1[(16 * n + r) * PT + 32 * kk + 8 * g],
-                                                      &dU1[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), acc);
-                }
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk < nkk) {
+                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 32 * kk + 8 * g]);
+                const f32x4 tb = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 32 * kk + 8 * g + 4]);
+                Ur = mfma32x3(split8v(ta, tb), frag_8(&XU[(16 * n + r) * PT + 32 * kk + 8 * g],
+                                                     &XU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), Ur);
             }
+            if (kk >= kk_lo) {
+                float tv[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 16 * w + 4 * g + i;
-                if (t < T) {
-                    const size_t off = baseV0 + (size_t)t * tokV + j0 + 16 * n + r;
-                    a.dv[off] = acc[i] * wD[n][i];
-                    a.dw[off] = acc[i] * vD[n][i];
-                }
-            }
-            const Split4 sx = split4(-acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dX2[(16 * w + 4 * g + i) * PC + 16 * n + r] = sx.hi[i];
-                dX2[kChunk * PC + (16 * w + 4 * g + i) * PC + 16 * n + r] = sx.lo[i];
+                for (int s = 0; s < 8; ++s) tv[s] = sAT[(32 * kk + 8 * g + s) * PA + 16 * w + r];
+                dXr = mfma32x3(split8(tv), frag_8(&dUX[(16 * n + r) * PT + 32 * kk + 8 * g],
+                                                  &dUX[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), dXr);
             }
         }
-        __syncthreads();
-        // key-side accumulators (sums over this tile's value columns)
-        {
-            const Split8 oq = frag_8(&O2[(16 * w + r) * PC + 8 * g], &O2[kChunk * PC + (16 * w + r) * PC + 8 * g]);
-            const Split8 xq = frag_8(&dX2[(16 * w + r) * PC + 8 * g], &dX2[kChunk * PC + (16 * w + r) * PC + 8 * g]);
-            const Split8 uq = frag_8(&U2[(16 * w + r) * PC + 8 * g], &U2[kChunk * PC + (16 * w + r) * PC + 8 * g]);
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const Split8 sf = frag_8(&S2[(16 * m + r) * PC + 8 * g], &S2[DK * PC + (16 * m + r) * PC + 8 * g]);
-                aQ[m] = mfma32x3(sf, oq, aQ[m]);   // (dO S^T)^T
-                aE[m] = mfma32x3(sf, xq, aE[m]);   // (-dX S^T)^T
-                const Split8 df = frag_8(&D2[(16 * m + r) * PC + 8 * g], &D2[DK * PC + (16 * m + r) * PC + 8 * g]);
-                aH[m] = mfma32x3(df, uq, aH[m]);   // (U dS'^T)^T
-            }
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                if (n <= w) {
-                    const Split8 uk = frag_8(&U2[(16 * n + r) * PC + 8 * g], &U2[kChunk * PC + (16 * n + r) * PC + 8 * g]);
-                    aP[n] = mfma32x3(oq, uk, aP[n]);   // dO U^T
-                    aA[n] = mfma32x3(xq, uk, aA[n]);   // -dX U^T
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: dgamma, masks, the A/P terms ----
-    sDG[tid] = dgp;
-    // dP = lower(dO U^T), dA = strictly-lower(-dX U^T) rows 16w + 4g + i, key cols 16n + r
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int qry = 16 * w + 4 * g + i, key = 16 * n + r;
-            if (!(key <= qry)) aP[n][i] = 0.f;
-            if (!(key < qry)) aA[n][i] = 0.f;
+            const int t = t0 + 16 * w + 4 * g + i;
+            if (t < T) {
+                const size_t off = baseV0 + (size_t)t * tokV + j0 + 16 * n + r;
+                a.dv[off] = dXr[i] * wD[i];
+                a.dw[off] = dXr[i] * vD[i];
+            }
         }
-    // key-side operands again (4-group layout), from a fresh read of the inputs
-    auto reload_ops = [&](float *sTotBuf, KeyOps<NKS> &o2, auto want_k) {
-        KeyRaw4<DK, BF16> raw;
-        raw.issue(a, rowK, g, vk);
-        float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
-        raw.unpack(qf, kf, laf, bgf);
-#pragma unroll
-        for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
-        chunk_scan<NE, DK>(G, gC, sTotBuf, w, r, [&](int e) { return ch4(e, g); });
-        if constexpr (decltype(want_k)::value) key_operands<NE, false, false, true, false>(qf, kf, bgf, G, gC, o2);
-        else key_operands<NE, true, true, false, false>(qf, kf, bgf, G, gC, o2);
-    };
-    {
-        __bf16 *KtT = sZ, *dP1 = sZ + 2 * RT, *dA1 = sZ + 2 * RT + 2 * kChunk * PT;
+        __syncthreads();
         {
-            KeyOps<NKS> o2;
-            reload_ops(sTot, o2, std::true_type{});
-            store_cols<NKS, PT>(o2.K, KtT, KtT + RT, 16 * w + r, g, false);
-        }
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const Split4 sp = split4(aP[n]), sa = split4(aA[n]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * g + i;
-                dP1[row * PT + 16 * n + r] = sp.hi[i];
-                dP1[kChunk * PT + row * PT + 16 * n + r] = sp.lo[i];
-                dA1[row * PT + 16 * n + r] = sa.hi[i];
-                dA1[kChunk * PT + row * PT + 16 * n + r] = sa.lo[i];
-            }
+            const Split4 su = split4(Ur), sx = split4(-dXr);
+            *reinterpret_cast<bf16x4 *>(&XU[(16 * n + r) * PT + 16 * w + 4 * g]) = su.hi;
+            *reinterpret_cast<bf16x4 *>(&XU[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = su.lo;
+            *reinterpret_cast<bf16x4 *>(&dUX[(16 * n + r) * PT + 16 * w + 4 * g]) = sx.hi;
+            *reinterpret_cast<bf16x4 *>(&dUX[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sx.lo;
         }
         __syncthreads();
-        // dQt^T += Kt^T dP^T ;  dEt^T += Kt^T dA^T
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk < nkk) {
-                    const Split8 kt = frag_8(&KtT[(16 * m + r) * PT + 32 * kk + 8 * g], &KtT[RT + (16 * m + r) * PT + 32 * kk + 8 * g]);
-                    aQ[m] = mfma32x3(kt, frag_8(&dP1[(16 * w + r) * PT + 32 * kk + 8 * g],
-                                                &dP1[kChunk * PT + (16 * w + r) * PT + 32 * kk + 8 * g]), aQ[m]);
-                    aE[m] = mfma32x3(kt, frag_8(&dA1[(16 * w + r) * PT + 32 * kk + 8 * g],
-                                                &dA1[kChunk * PT + (16 * w + r) * PT + 32 * kk + 8 * g]), aE[m]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    f32x4 aK[NM];
-    {
-        __bf16 *QtT = sZ, *EtT = sZ + 2 * RT, *dPt = sZ + 4 * RT, *dAt = sZ + 4 * RT + 2 * kChunk * PT;
+        // key-side accumulators, sums over this tile's columns (every operand whose
+        // contraction index is the value column is read transposed from its [col][.] tile)
         {
-            KeyOps<NKS> o2;
-            reload_ops(sTot2, o2, std::false_type{});
-            store_cols<NKS, PT>(o2.Q, QtT, QtT + RT, 16 * w + r, g, false);
-            store_cols<NKS, PT>(o2.E, EtT, EtT + RT, 16 * w + r, g, false);
-        }
+            const Split8 oT = frag_tr<PT>(O1, O1 + VT * PT, 0, 16 * w, r, g);    // dO[token 16w + r][col]
+            const Split8 xT = frag_tr<PT>(dUX, dUX + VT * PT, 0, 16 * w, r, g);  // -dX[token][col]
+            const Split8 uT = frag_tr<PT>(XU, XU + VT * PT, 0, 16 * w, r, g);    // U[token][col]
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const Split4 sp = split4(aP[n]), sa = split4(aA[n]);
-            *reinterpret_cast<bf16x4 *>(&dPt[(16 * n + r) * PT + 16 * w + 4 * g]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&dPt[kChunk * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sp.lo;
-            *reinterpret_cast<bf16x4 *>(&dAt[(16 * n + r) * PT + 16 * w + 4 * g]) = sa.hi;
-            *reinterpret_cast<bf16x4 *>(&dAt[kChunk * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sa.lo;
+            for (int mm = 0; mm < NMH; ++mm) {
+                const int m = NMH * hf + mm;
+                const __bf16 *sh = &S1[(16 * m + r) * PS], *sl = sh + DK * PS;
+                const Split8 sa = frag_2x4(sh + 4 * g, sh + 16 + 4 * g, sl + 4 * g, sl + 16 + 4 * g);
+                aQ[mm] = mfma32x3(sa, oT, aQ[mm]);   // (dO S^T)^T
+                aE[mm] = mfma32x3(sa, xT, aE[mm]);   // (-dX S^T)^T
+                const __bf16 *dh = &D1[(16 * m + r) * PS], *dl = dh + DK * PS;
+                aH[mm] = mfma32x3(frag_2x4(dh + 4 * g, dh + 16 + 4 * g, dl + 4 * g, dl + 16 + 4 * g), uT,
+                                  aH[mm]);           // (U (gamma dS')^T)^T = gamma * dKh^T
+                GDN2_SCHED_FENCE();
+            }
+            const Split8 lhs = hf ? xT : oT;         // dO U^T or -dX U^T
+#pragma unroll
+            for (int nn = 0; nn < 4; ++nn)
+                if (nn <= w) {
+                    aPA[nn] = mfma32x3(lhs, frag_tr<PT>(XU, XU + VT * PT, 0, 16 * nn, r, g), aPA[nn]);
+                    GDN2_SCHED_FENCE();
+                }
         }
         __syncthreads();
-        // dKt^T = Qt^T dP + Et^T dA   (columns = this wave's keys)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk >= kk_lo) {
-                    acc = mfma32x3(frag_8(&QtT[(16 * m + r) * PT + 32 * kk + 8 * g], &QtT[RT + (16 * m + r) * PT + 32 * kk + 8 * g]),
-                                   frag_8(&dPt[(16 * w + r) * PT + 32 * kk + 8 * g], &dPt[kChunk * PT + (16 * w + r) * PT + 32 * kk + 8 * g]),
-                                   acc);
-                    acc = mfma32x3(frag_8(&EtT[(16 * m + r) * PT + 32 * kk + 8 * g], &EtT[RT + (16 * m + r) * PT + 32 * kk + 8 * g]),
-                                   frag_8(&dAt[(16 * w + r) * PT + 32 * kk + 8 * g], &dAt[kChunk * PT + (16 * w + r) * PT + 32 * kk + 8 * g]),
-                                   acc);
-                }
-            }
-            aK[m] = acc;
-        }
     }
 
-    // ---- element-wise chain (4-group layout: token 16w + r, channel ch4(e, g)) ----
-    // The four key-side gradient accumulators are parked in LDS (each thread
-    // reads back only its own values, so no barrier is needed) to keep the
-    // chain's register footprint small.
+    // ---- epilogue: dgamma, dP/dA products, element-wise chain ----
+    // The key-side inputs are read again (rather than kept through the value loop) and
+    // the decay prefix is rebuilt from the totals the first scan left in LDS.  The lane
+    // indices are derived afresh from an opaque copy of the thread index, so that no
+    // address arithmetic of the preparation is kept live across the value loop.
+  {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
+    const int kk_lo = (w >= 2) ? 1 : 0;
+    const int nkk = (w >= 2) ? 2 : 1;
+    const int tk = t0 + 16 * w + r;
+    const bool vk = tk < T;
+    const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
+    const int chh = hf * (DK / 2);
+    auto ch = [&](int e) { return chh + ch4(e, g); };
+    raw.issue(a, rowK + chh, g, vk);
+#pragma unroll
+    for (int it = 0; it < NSF; ++it) {
+        const int idx = tid + NTH * it;
+        if (idx < DK * 8) sScr[idx] = dgp[it];
+    }
+    {
+        // dP = lower(dO U^T) (half 0), dA = strictly-lower(-dX U^T) (half 1); lane holds
+        // row 16w + 4g + i, key 16nn + r; written as [key][query]
+        __bf16 *dM = hf ? dAt : dPt;
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+            f32x4 v4 = aPA[nn];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int qry = 16 * w + 4 * g + i, key = 16 * nn + r;
+                if (!(hf ? key < qry : key <= qry)) v4[i] = 0.f;
+            }
+            const Split4 sp = split4(v4);
+            *reinterpret_cast<bf16x4 *>(&dM[(16 * nn + r) * PT + 16 * w + 4 * g]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&dM[kChunk * PT + (16 * nn + r) * PT + 16 * w + 4 * g]) = sp.lo;
+        }
+    }
+    float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
+    raw.unpack(qf, kf, G, bgf);
+#pragma unroll
+    for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
+    chunk_rescan<NEH, DK>(G, sTot, w, ch);
+    {
+        // Qt rows of this half's channels again
+#pragma unroll
+        for (int mm = 0; mm < NMH; ++mm) {
+            f32x4 qt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qt[i] = qf[4 * mm + i] * exp2_fast(G[4 * mm + i]);
+            const Split4 sq = split4(qt);
+            const int o = (16 * w + r) * PK + chh + 16 * mm + 4 * g;
+            *reinterpret_cast<bf16x4 *>(&sQt[o]) = sq.hi;
+            *reinterpret_cast<bf16x4 *>(&sQt[RK + o]) = sq.lo;
+        }
+    }
     __syncthreads();
-    float *sAcc = reinterpret_cast<float *>(sZ);   // [4][NE][kThreads]
-    static_assert(4 * NE * kThreads * 4 <= ZSIZE * 2, "accumulator park does not fit");
+    if (tid < DK) {
+        float sacc = 0.f;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        const int m = e >> 2, i = e & 3;
-        sAcc[(0 * NE + e) * kThreads + tid] = aQ[m][i];
-        sAcc[(1 * NE + e) * kThreads + tid] = aE[m][i];
-        sAcc[(2 * NE + e) * kThreads + tid] = aK[m][i];
-        sAcc[(3 * NE + e) * kThreads + tid] = aH[m][i];
+        for (int q = 0; q < 8; ++q) sacc += sScr[8 * tid + q];
+        sDG[tid] = sacc;
     }
-    float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
+    // dQt^T += Kt^T dP^T and dEt^T += Kt^T dA^T (keys up to this wave's queries);
+    // dKt^T = Qt^T dP + Et^T dA (queries from this wave's keys on)
+    f32x4 aK[NMH];
+#pragma unroll
+    for (int mm = 0; mm < NMH; ++mm) {
+        const int m = NMH * hf + mm;
+        aK[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk < nkk) {
+                const Split8 kt = frag_tr<PK>(sKt, sKt + RK, 32 * kk, 16 * m, r, g);
+                aQ[mm] = mfma32x3(kt, frag_tr<PT>(dPt, dPt + kChunk * PT, 32 * kk, 16 * w, r, g), aQ[mm]);
+                aE[mm] = mfma32x3(kt, frag_tr<PT>(dAt, dAt + kChunk * PT, 32 * kk, 16 * w, r, g), aE[mm]);
+            }
+            if (kk >= kk_lo) {
+                const __bf16 *ph = &dPt[(16 * w + r) * PT + 32 * kk], *pl = ph + kChunk * PT;
+                aK[mm] = mfma32x3(frag_tr<PK>(sQt, sQt + RK, 32 * kk, 16 * m, r, g),
+                                  frag_2x4(ph + 4 * g, ph + 16 + 4 * g, pl + 4 * g, pl + 16 + 4 * g), aK[mm]);
+                const __bf16 *ah = &dAt[(16 * w + r) * PT + 32 * kk], *al = ah + kChunk * PT;
+                aK[mm] = mfma32x3(frag_tr<PK>(sEt, sEt + RK, 32 * kk, 16 * m, r, g),
+                                  frag_2x4(ah + 4 * g, ah + 16 + 4 * g, al + 4 * g, al + 16 + 4 * g), aK[mm]);
+            }
+        }
+    }
+
+    // ---- element-wise chain (token 16w + r, channels ch(e)) ----
+    float xg[NEH], yh[NEH];
     {
-        KeyRaw4<DK, BF16> raw;
-        raw.issue(a, rowK, g, vk);
-        raw.unpack(qf, kf, laf, bgf);
-    }
 #pragma unroll
-    for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
-    chunk_scan<NE, DK>(G, gC, sTot, w, r, [&](int e) { return ch4(e, g); });  // barrier orders sDG too
-    float xg[NE], yh[NE];
+        for (int mm = 0; mm < NMH; ++mm) {
+            f32x4 vq, vk4, vb;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        f32x4 vq, vk4, vb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * m + i;
-            const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]), ek = exp2_fast(gC[e] - G[e]);
-            const float Qt = qf[e] * eg, Et = bgf[e] * kf[e] * eg, Kt = kf[e] * eng, Kh = kf[e] * ek;
-            const float dQt = sAcc[(0 * NE + e) * kThreads + tid];
-            const float dEt = sAcc[(1 * NE + e) * kThreads + tid];
-            const float dKt = sAcc[(2 * NE + e) * kThreads + tid];
-            const float dKh = sAcc[(3 * NE + e) * kThreads + tid];
-            vq[i] = dQt * eg;
-            const float dE = dEt * eg;
-            vb[i] = dE * kf[e];
-            vk4[i] = dKt * eng + dKh * ek + dE * bgf[e];
-            xg[e] = dQt * Qt + dEt * Et - dKt * Kt - dKh * Kh;
-            yh[e] = dKh * Kh;
-        }
-        if (vk) {
-            const size_t off = rowK + 16 * m + 4 * g;
-            *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
-            *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
-            *reinterpret_cast<f32x4 *>(a.db + off) = vb;
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * mm + i;
+                const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]);
+                const float Qt = qf[e] * eg, Et = bgf[e] * kf[e] * eg, Kt = kf[e] * eng;
+                const float dQt = aQ[mm][i], dEt = aE[mm][i], dKt = aK[mm][i];
+                const float dHg = aH[mm][i];      // gamma * dKh, and dKh * Kh = dHg * Kt
+                vq[i] = dQt * eg;
+                const float dE = dEt * eg;
+                vb[i] = dE * kf[e];
+                vk4[i] = (dKt + dHg) * eng + dE * bgf[e];
+                xg[e] = dQt * Qt + dEt * Et - (dKt + dHg) * Kt;
+                yh[e] = dHg * Kt;
+            }
+            if (vk) {
+                const size_t off = rowK + chh + 16 * mm + 4 * g;
+                *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
+                *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
+                *reinterpret_cast<f32x4 *>(a.db + off) = vb;
+            }
         }
     }
-    // dlog_alpha_t = sum_{s >= t} dG_s + dg_C, with dg_C = sum_s dKh_s*Kh_s + dgamma*gamma
-    float xin[NE], xtot[NE], ytot[NE];
+    // dlog_alpha_t = sum_{s >= t} dG_s + dg_C, with dg_C = sum_s dKh_s Kh_s + dgamma gamma
+    float xin[NEH], xtot[NEH], ytot[NEH];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) xin[e] = xg[e];
-    chunk_scan<NE, DK>(xin, xtot, sTot2, w, r, [&](int e) { return ch4(e, g); });
-    chunk_scan<NE, DK>(yh, ytot, sTot3, w, r, [&](int e) { return ch4(e, g); });
+    for (int e = 0; e < NEH; ++e) xin[e] = xg[e];
+    chunk_scan<NEH, DK>(xin, xtot, reinterpret_cast<float *>(smem + oTotA), w, r, ch);
+    chunk_scan<NEH, DK>(yh, ytot, reinterpret_cast<float *>(smem + oTotB), w, r, ch);
     if (vk) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
+        for (int mm = 0; mm < NMH; ++mm) {
             f32x4 vl;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = 4 * m + i, ch = ch4(e, g);
-                float dgam = 0.f;
-#pragma unroll
-                for (int p = 0; p < TPC; ++p) dgam += sDG[ch * TPC + p];
-                vl[i] = (xtot[e] - xin[e] + xg[e]) + ytot[e] + dgam * exp2_fast(gC[e]);
+                const int e = 4 * mm + i;
+                vl[i] = (xtot[e] - xin[e] + xg[e]) + ytot[e] + sDG[ch(e)] * sGam[ch(e)];
             }
-            *reinterpret_cast<f32x4 *>(a.dla + rowK + 16 * m + 4 * g) = vl;
+            *reinterpret_cast<f32x4 *>(a.dla + rowK + chh + 16 * mm + 4 * g) = vl;
         }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -881,7 +910,8 @@ hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, int vt, bool bf16, hipSt
 template <int DK, bool BF16>
 static hipError_t chunk_t(const BwdArgs &a, hipStream_t st) {
     const int NC = (a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16>), dim3((unsigned)(a.B * a.H * NC)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads), 0, st,
+                       a);
     return hipGetLastError();
 }
 

@@ -36,6 +36,20 @@ __device__ __forceinline__ void chunk_scan(float (&x)[NE], float (&tot)[NE], flo
     }
 }
 
+// The inclusive prefix of chunk_scan again, from fresh per-token values x and the
+// per-wave totals chunk_scan left in sTot: the same operations in the same order, so
+// the result is bitwise the one chunk_scan returned.  No barrier.
+template <int NE, int DK, typename ChanFn>
+__device__ __forceinline__ void chunk_rescan(float (&x)[NE], const float *sTot, int w, ChanFn ch) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        x[e] = row_scan16(x[e]);
+        const int c = ch(e);
+        const float pre = (w > 0 ? sTot[c] : 0.f) + (w > 1 ? sTot[DK + c] : 0.f) + (w > 2 ? sTot[2 * DK + c] : 0.f);
+        x[e] += pre;
+    }
+}
+
 // Inverse of one unit-lower 16x16 block, (I + N)^-1 with N strictly lower, so
 // N^16 = 0 and (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly.  The
 // powers are formed on MFMA in both the row layout (lane holds X[r][4g+i]) and
@@ -113,14 +127,16 @@ __device__ __forceinline__ void solve_T(const float *sA, float *sT, int w, int r
 // Same as solve_T, with A and T sharing one fp32 [64][PA] buffer: each wave
 // first keeps its own row blocks of A in registers (only wave I ever reads
 // row block I of A), then T is written over A.  The strictly upper 16x16
-// blocks of the buffer must be zero and stay zero.  4 workgroup barriers.
+// blocks of the buffer must be zero and stay zero.  4 workgroup barriers,
+// which every wave of the workgroup reaches; only waves with `active` set
+// (one per row block w) compute.
 template <int PA>
-__device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g) {
+__device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g, bool active = true) {
     f32x4 arow[3];
 #pragma unroll
     for (int K = 0; K < 3; ++K)
-        if (K < w) arow[K] = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 16 * K + 4 * g]);
-    {
+        if (active && K < w) arow[K] = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 16 * K + 4 * g]);
+    if (active) {
         f32x4 nA = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 16 * w + 4 * g]);
         f32x4 nB;
 #pragma unroll
@@ -137,7 +153,7 @@ __device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g)
     __syncthreads();
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
-        if (w >= d) {
+        if (active && w >= d) {
             const int I = w, J = w - d;
             f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
