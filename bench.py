@@ -2,8 +2,8 @@
 """Benchmark of the GDN-2 chunkwise operator (forward + gate-aware backward) on one MI355X.
 
 One step = forward + gate-aware backward (gdn2_chunk_fwd_states,
-gdn2_chunk_bwd_reverse, gdn2_chunk_bwd_grads: the staged form of
-gdn2_chunk_fwd + gdn2_chunk_bwd that reuses the forward's chunk states) over one batch of the
+gdn2_chunk_bwd_factors, gdn2_chunk_bwd_reverse, gdn2_chunk_bwd_grads: the staged form
+of gdn2_chunk_fwd + gdn2_chunk_bwd that reuses the forward's chunk states) over one batch of the
 forward/backward workload B=8, T=2048, H=16, dk=dv=128 (bf16 q/k/v, fp32
 gates, decay and state; the 2K x 8 training shape of the Gated DeltaNet-2
 pages).  Inputs are seeded synthetic tensors (linear_attention_sequence_gdn2_amd.inputs)
@@ -36,12 +36,15 @@ HBM_PEAK_GBS = 8000.0
 #   backward: q,k,v 768 + gates 1536 + dO 512 + six gradients 6*512  = 5888
 FWD_BYTES_PER_TOKHEAD = 2816
 BWD_BYTES_PER_TOKHEAD = 5888
-# per-kernel algorithmic bytes per token-head of the three launches of a step:
+# per-kernel algorithmic bytes per token-head of the four launches of a step:
 #   forward with states : 2816 + chunk states 128*128*4 / 64 tokens = 1024     -> 3840
-#   reverse sweep       : q,k 512 + log_alpha,b 1024 + dO 512 + dstates 1024   -> 3072
+#   adjoint factors     : q,k 512 + log_alpha,b 1024
+#                         + factors (128*128 + 64*128)*4 / 64 tokens = 1536     -> 3072
+#   reverse sweep       : factors 1536 + dO 512 + dstates 1024                  -> 3072
 #   chunk gradients     : q,k,v 768 + gates 1536 + dO 512 + states, dstates 2048
 #                         + dq,dk,dv,dlog_alpha,db,dw 3072                      -> 7936
 FWD_STATES_BYTES_PER_TOKHEAD = 3840
+BWD_FACTORS_BYTES_PER_TOKHEAD = 3072
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
 BWD_GRADS_BYTES_PER_TOKHEAD = 7936
 
@@ -138,35 +141,42 @@ def main():
     states = torch.empty(sshape, dtype=torch.float32, device=dev)
     dstates = torch.empty(sshape, dtype=torch.float32, device=dev)
 
-    # One training step = three kernel launches:
-    #   fwd_kernel     (gdn2_chunk_fwd_states: o, S_final and the chunk-start states)
-    #   bwd_reverse    (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
-    #   bwd_chunk      (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
+    factors = torch.empty(gdn2.factors_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv), dtype=torch.uint8, device=dev)
+
+    # One training step = four kernel launches:
+    #   fwd_kernel          (gdn2_chunk_fwd_states: o, S_final and the chunk-start states)
+    #   bwd_factors_kernel  (gdn2_chunk_bwd_factors: per-chunk adjoint factors R, Q2)
+    #   bwd_reverse_kernel  (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
+    #   bwd_chunk_kernel    (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         o, sf, _ = gdn2.fwd_states(*fargs, states=states)
         if ev is not None:
             ev[1].record(stream)
-        _, dS0 = gdn2.bwd_reverse(d["q"], d["k"], d["log_alpha"], d["b"], d["dO"], d["dS_final"], dstates=dstates)
+        gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"], factors=factors)
         if ev is not None:
             ev[2].record(stream)
-        g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates)
+        _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
         if ev is not None:
             ev[3].record(stream)
+        g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates)
+        if ev is not None:
+            ev[4].record(stream)
         return o, sf, g, dS0
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    nk = 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
-    step_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+    k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(nk)]
+    step_ms = sum(e[0].elapsed_time(e[nk]) for e in evs) / args.steps
     tokens = wl.B * wl.T
     tokheads = wl.B * wl.T * wl.H
     state_bytes = wl.B * wl.H * wl.dk * wl.dv * 4
@@ -176,6 +186,7 @@ def main():
     # B*T*H, plus per-sequence states), from the per-token-head constants above
     kernels = [
         ("fwd_kernel", "gdn2_chunk_fwd_states", FWD_STATES_BYTES_PER_TOKHEAD * tokheads + state_bytes),
+        ("bwd_factors_kernel", "gdn2_chunk_bwd_factors", BWD_FACTORS_BYTES_PER_TOKHEAD * tokheads),
         ("bwd_reverse_kernel", "gdn2_chunk_bwd_reverse", BWD_REVERSE_BYTES_PER_TOKHEAD * tokheads + 2 * state_bytes),
         ("bwd_chunk_kernel", "gdn2_chunk_bwd_grads", BWD_GRADS_BYTES_PER_TOKHEAD * tokheads),
     ]
@@ -184,7 +195,7 @@ def main():
         gbs = nbytes / (ms * 1e-3) / 1e9
         per_kernel[name] = {"entry": entry, "launch_ms": round(ms, 4), "algorithmic_bytes": nbytes,
                             "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    dom = max(range(3), key=lambda j: k_ms[j])
+    dom = max(range(nk), key=lambda j: k_ms[j])
     name, entry, nbytes = kernels[dom]
     achieved = nbytes / (k_ms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

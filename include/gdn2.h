@@ -86,7 +86,8 @@ int gdn2_chunk_fwd(const gdn2_shape *shape,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace gdn2_chunk_bwd needs: two fp32 states per chunk per
- * (batch, head), i.e. 2 * B*H*ceil(T/64)*dk*dv*4 bytes; (size_t)-1 if invalid. */
+ * (batch, head) and the per-chunk adjoint factors, i.e.
+ * 2 * gdn2_chunk_states_bytes() + gdn2_chunk_factors_bytes(); (size_t)-1 if invalid. */
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape);
 
 /* Gate-aware backward pass of loss = sum(dO * o) + sum(dS_final * S_final):
@@ -106,7 +107,8 @@ int gdn2_chunk_bwd(const gdn2_shape *shape,
 
 /* ---- staged form (training): each call below is exactly one kernel launch ----
  *
- * gdn2_chunk_bwd == gdn2_chunk_states + gdn2_chunk_bwd_reverse + gdn2_chunk_bwd_grads.
+ * gdn2_chunk_bwd == gdn2_chunk_states + gdn2_chunk_bwd_factors + gdn2_chunk_bwd_reverse
+ *                   + gdn2_chunk_bwd_grads.
  * A training step can instead run gdn2_chunk_fwd_states (which writes the chunk
  * states while producing o) and skip the state sweep in the backward.
  * `states` and `dstates` are [B, H, ceil(T/64), dk, dv] fp32 device buffers of
@@ -127,10 +129,24 @@ int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v,
                       const float *log_alpha, const float *b, const float *w,
                       const float *S0, float *states, void *stream);
 
-/* Reverse sweep of the backward: writes dstates (required) and dS0 (optional).
- * Reads q, k, log_alpha, b, dO and dS_final (NULL = zeros); v and w are not needed. */
-int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *q, const void *k,
-                           const float *log_alpha, const float *b,
+/* Bytes of the per-chunk adjoint factor buffer, B*H*ceil(T/64)*(dk*dk + 64*dk)*4;
+ * (size_t)-1 if the shape is invalid. */
+size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
+
+/* Per-chunk adjoint factors of the reverse sweep.  Unrolling the backward of one
+ * chunk of the chunkwise WY form (blog on Gated DeltaNet-2, section "Token path and
+ * parallel training") gives for the gradient of the chunk's start state
+ *     dS = R dS' + Q2^T dO,  R = (I - W^T Kt) diag(gamma),  Q2 = Qt - P W,  W = T Et,
+ * with dS' the gradient of its end state; R and Q2 depend on q, k, log_alpha and b
+ * only.  Writes R and Q2^T of every (batch, head, chunk) into `factors`
+ * (gdn2_chunk_factors_bytes() bytes, device memory owned by the caller, opaque
+ * layout of split-bf16 MFMA tiles, read only by gdn2_chunk_bwd_reverse). */
+int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k,
+                           const float *log_alpha, const float *b, void *factors, void *stream);
+
+/* Reverse sweep of the backward from the factors: writes dstates (required) and
+ * dS0 (optional), reading dO and dS_final (NULL = zeros). */
+int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors,
                            const float *dO, const float *dS_final,
                            float *dstates, float *dS0, void *stream);
 

@@ -4,9 +4,10 @@
 ``include/gdn2.h``); all arithmetic runs in its HIP kernels.  Build the library
 with ``python -m linear_attention_sequence_gdn2_amd.build``.
 """
-from ._binding import (EXPORTS, LIB_PATH, Gdn2Error, Gdn2Shape, bwd, bwd_grads, bwd_reverse,  # noqa: F401
-                       bwd_saved, bwd_workspace_bytes, chunk_states, fwd, fwd_states, load, make_shape,
-                       states_shape)
+from ._binding import (EXPORTS, LIB_PATH, Gdn2Error, Gdn2Shape, bwd, bwd_factors, bwd_grads,  # noqa: F401
+                       bwd_reverse, bwd_saved, bwd_workspace_bytes, chunk_states, factors_bytes, fwd, fwd_states,
+                       load, make_shape, states_shape)
 
-__all__ = ["fwd", "bwd", "fwd_states", "chunk_states", "bwd_reverse", "bwd_grads", "bwd_saved", "load",
-           "bwd_workspace_bytes", "states_shape", "Gdn2Error", "Gdn2Shape", "LIB_PATH", "EXPORTS", "make_shape"]
+__all__ = ["fwd", "bwd", "fwd_states", "chunk_states", "bwd_factors", "bwd_reverse", "bwd_grads", "bwd_saved",
+           "load", "bwd_workspace_bytes", "factors_bytes", "states_shape", "Gdn2Error", "Gdn2Shape", "LIB_PATH",
+           "EXPORTS", "make_shape"]

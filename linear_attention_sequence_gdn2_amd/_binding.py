@@ -22,7 +22,8 @@ STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3:
           4: "GDN2_ERR_HIP"}
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
-           "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads"]
+           "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
+           "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -63,7 +64,11 @@ def load():
         lib.gdn2_chunk_fwd_states.restype = ctypes.c_int
         lib.gdn2_chunk_states.argtypes = [SP] + [P] * 7 + [P]
         lib.gdn2_chunk_states.restype = ctypes.c_int
-        lib.gdn2_chunk_bwd_reverse.argtypes = [SP] + [P] * 8 + [P]
+        lib.gdn2_chunk_factors_bytes.argtypes = [SP]
+        lib.gdn2_chunk_factors_bytes.restype = ctypes.c_size_t
+        lib.gdn2_chunk_bwd_factors.argtypes = [SP] + [P] * 5 + [P]
+        lib.gdn2_chunk_bwd_factors.restype = ctypes.c_int
+        lib.gdn2_chunk_bwd_reverse.argtypes = [SP] + [P] * 5 + [P]
         lib.gdn2_chunk_bwd_reverse.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 15 + [P]
         lib.gdn2_chunk_bwd_grads.restype = ctypes.c_int
@@ -189,20 +194,56 @@ def chunk_states(k, v, log_alpha, b, w, S0=None, q_dtype=None, states=None):
     return states
 
 
-def bwd_reverse(q, k, log_alpha, b, dO, dS_final=None, want_dS0=True, dstates=None):
-    """Reverse sweep (one kernel): (dstates, dS0)."""
+def factors_bytes(B, T, H, dk, dv=None):
+    """Bytes of the per-chunk adjoint factor buffer of gdn2_chunk_bwd_factors."""
+    shape = make_shape(B, T, H, dk, dv if dv is not None else dk, torch.float32)
+    n = load().gdn2_chunk_factors_bytes(ctypes.byref(shape))
+    if n == ctypes.c_size_t(-1).value:
+        raise Gdn2Error(2, "unsupported shape")
+    return n
+
+
+def bwd_factors(q, k, log_alpha, b, factors=None):
+    """Per-chunk adjoint factors of the reverse sweep (one kernel): a uint8 device
+    tensor of factors_bytes() bytes, read only by bwd_reverse."""
     B, T, H, dk = q.shape
-    dv = dO.shape[-1]
+    for name, t, dt in (("k", k, q.dtype), ("log_alpha", log_alpha, torch.float32), ("b", b, torch.float32)):
+        if tuple(t.shape) != (B, T, H, dk) or t.dtype != dt or t.device != q.device:
+            raise ValueError("gdn2: %s must be %s %s on %s" % (name, (B, T, H, dk), dt, q.device))
+    for t in (q, k, log_alpha, b):
+        if not t.is_contiguous():
+            raise ValueError("gdn2: tensors must be contiguous")
+    if not q.is_cuda:
+        raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % q.device)
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    shape = make_shape(B, T, H, dk, dk, q.dtype)
+    need = factors_bytes(B, T, H, dk)
+    if factors is None:
+        factors = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif factors.numel() * factors.element_size() < need or not factors.is_contiguous():
+        raise ValueError("gdn2: factors buffer smaller than %d bytes" % need)
+    _check(lib.gdn2_chunk_bwd_factors(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(b),
+                                      _ptr(factors), _stream(q.device)))
+    return factors
+
+
+def bwd_reverse(factors, dO, dk, dS_final=None, want_dS0=True, dstates=None):
+    """Reverse sweep from the factors of bwd_factors (one kernel): (dstates, dS0)."""
+    B, T, H, dv = dO.shape
+    if dO.dtype != torch.float32 or not dO.is_contiguous():
+        raise ValueError("gdn2: dO must be contiguous float32 [B,T,H,dv]")
+    if dS_final is not None and (tuple(dS_final.shape) != (B, H, dk, dv) or dS_final.dtype != torch.float32
+                                 or not dS_final.is_contiguous() or dS_final.device != dO.device):
+        raise ValueError("gdn2: dS_final must be contiguous float32 [B,H,dk,dv]")
+    if factors.device != dO.device or factors.numel() * factors.element_size() < factors_bytes(B, T, H, dk, dv):
+        raise ValueError("gdn2: factors buffer does not match the shape")
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, torch.float32)
     if dstates is None:
-        dstates = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=q.device)
-    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_dS0 else None
-    for t in (q, k, log_alpha, b, dO) + ((dS_final,) if dS_final is not None else ()):
-        if not t.is_contiguous() or t.device != q.device:
-            raise ValueError("gdn2: tensors must be contiguous and on one device")
-    _check(lib.gdn2_chunk_bwd_reverse(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(b), _ptr(dO),
-                                      _ptr(dS_final), _ptr(dstates), _ptr(dS0), _stream(q.device)))
+        dstates = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=dO.device)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dO.device) if want_dS0 else None
+    _check(lib.gdn2_chunk_bwd_reverse(ctypes.byref(shape), _ptr(factors), _ptr(dO), _ptr(dS_final),
+                                      _ptr(dstates), _ptr(dS0), _stream(dO.device)))
     return dstates, dS0
 
 
@@ -223,8 +264,9 @@ def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates):
 
 
 def bwd_saved(q, k, v, log_alpha, b, w, states, dO, dS_final=None, want_dS0=True):
-    """Backward from the states written by fwd_states: reverse sweep + token gradients."""
-    dstates, dS0 = bwd_reverse(q, k, log_alpha, b, dO, dS_final, want_dS0)
+    """Backward from the states written by fwd_states: factors, reverse sweep, token gradients."""
+    factors = bwd_factors(q, k, log_alpha, b)
+    dstates, dS0 = bwd_reverse(factors, dO, q.shape[-1], dS_final, want_dS0)
     out = bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates)
     out["dS0"] = dS0
     return out

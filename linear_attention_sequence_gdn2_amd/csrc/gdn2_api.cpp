@@ -79,9 +79,15 @@ size_t gdn2_chunk_states_bytes(const gdn2_shape *shape) {
     return (size_t)shape->B * shape->H * nchunks(shape) * (size_t)shape->dk * shape->dv * sizeof(float);
 }
 
+size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return (size_t)-1;
+    const size_t dk = (size_t)shape->dk;
+    return (size_t)shape->B * shape->H * nchunks(shape) * (dk * dk + 64 * dk) * sizeof(float);
+}
+
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
-    return 2 * gdn2_chunk_states_bytes(shape);
+    return 2 * gdn2_chunk_states_bytes(shape) + gdn2_chunk_factors_bytes(shape);
 }
 
 }  // extern "C"
@@ -102,20 +108,9 @@ gdn2::FwdArgs fwd_args(const gdn2_shape *shape, const void *q, const void *k, co
     return f;
 }
 
-gdn2::BwdArgs bwd_args(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                       const float *log_alpha, const float *b, const float *w, const float *dO,
-                       const float *dS_final, const float *states, float *dstates, float *dq, float *dk,
-                       float *dv, float *dla, float *db, float *dw, float *dS0, int *vt2_out) {
+gdn2::BwdArgs bwd_args(const gdn2_shape *shape) {
     gdn2::BwdArgs a{};
-    a.q = q; a.k = k; a.v = v;
-    a.la = log_alpha; a.bg = b; a.wg = w;
-    a.dO = dO; a.dS_final = dS_final;
-    a.states = states; a.dstates = dstates;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dla; a.db = db; a.dw = dw; a.dS0 = dS0;
     a.B = shape->B; a.T = shape->T; a.H = shape->H; a.DV = shape->dv;
-    const int vt2 = gdn2::bwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
-    a.nvt = shape->dv / vt2;
-    *vt2_out = vt2;
     return a;
 }
 
@@ -156,18 +151,28 @@ int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v, con
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
-int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *q, const void *k, const float *log_alpha,
-                           const float *b, const float *dO, const float *dS_final, float *dstates, float *dS0,
-                           void *stream) {
+int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k, const float *log_alpha,
+                           const float *b, void *factors, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
-    if (!q || !k || !log_alpha || !b || !dO || !dstates) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, log_alpha, b, dO, dS_final, dstates, dS0})) return GDN2_ERR_INVALID_ARG;
-    int vt2;
-    const gdn2::BwdArgs a = bwd_args(shape, q, k, nullptr, log_alpha, b, nullptr, dO, dS_final, nullptr, dstates,
-                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dS0, &vt2);
-    return launch_status(gdn2::launch_bwd_reverse(a, shape->dk, vt2, shape->qkv_dtype == GDN2_BF16,
+    if (!q || !k || !log_alpha || !b || !factors) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, log_alpha, b, factors})) return GDN2_ERR_INVALID_ARG;
+    gdn2::BwdArgs a = bwd_args(shape);
+    a.q = q; a.k = k; a.la = log_alpha; a.bg = b; a.factors = factors;
+    return launch_status(gdn2::launch_bwd_factors(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
                                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const float *dO,
+                           const float *dS_final, float *dstates, float *dS0, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!factors || !dO || !dstates) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({factors, dO, dS_final, dstates, dS0})) return GDN2_ERR_INVALID_ARG;
+    gdn2::BwdArgs a = bwd_args(shape);
+    a.factors = const_cast<void *>(factors);
+    a.dO = dO; a.dS_final = dS_final; a.dstates = dstates; a.dS0 = dS0;
+    return launch_status(gdn2::launch_bwd_reverse(a, shape->dk, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, const void *v,
@@ -181,9 +186,11 @@ int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, 
         return GDN2_ERR_INVALID_ARG;
     if (!all_aligned({q, k, v, log_alpha, b, w, dO, states, dstates, dq, dk, dv, dlog_alpha, db, dw}))
         return GDN2_ERR_INVALID_ARG;
-    int vt2;
-    const gdn2::BwdArgs a = bwd_args(shape, q, k, v, log_alpha, b, w, dO, nullptr, states, const_cast<float *>(dstates),
-                                     dq, dk, dv, dlog_alpha, db, dw, nullptr, &vt2);
+    gdn2::BwdArgs a = bwd_args(shape);
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_alpha; a.bg = b; a.wg = w;
+    a.dO = dO; a.states = states; a.dstates = const_cast<float *>(dstates);
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
     return launch_status(gdn2::launch_bwd_chunk(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
@@ -201,11 +208,15 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
         return GDN2_ERR_INVALID_ARG;
     const size_t need = gdn2_chunk_bwd_workspace_size(shape);
     if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+    const size_t sbytes = gdn2_chunk_states_bytes(shape);
     float *states = reinterpret_cast<float *>(workspace);
-    float *dstates = states + need / 2 / sizeof(float);
+    float *dstates = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + sbytes);
+    void *factors = reinterpret_cast<char *>(workspace) + 2 * sbytes;
     int rc = gdn2_chunk_states(shape, k, v, log_alpha, b, w, S0, states, stream);
     if (rc != GDN2_OK) return rc;
-    rc = gdn2_chunk_bwd_reverse(shape, q, k, log_alpha, b, dO, dS_final, dstates, dS0, stream);
+    rc = gdn2_chunk_bwd_factors(shape, q, k, log_alpha, b, factors, stream);
+    if (rc != GDN2_OK) return rc;
+    rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     if (rc != GDN2_OK) return rc;
     return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, dq, dk, dv, dlog_alpha, db,
                                 dw, stream);

@@ -27,375 +27,12 @@
 // need no exchange; the key-side gradients sum over all value columns inside
 // one bwd_chunk_kernel workgroup.
 //
-// Element layout of key-side data in these kernels ("4-groups"): lane (w, r, g)
-// holds token 16w + r and channels 16m + 4g + i (m < DK/16, i < 4); element
-// e = 4m + i.  The MFMA fragment of contraction step j is elements 8j..8j+7,
-// i.e. channels 32j + 4g + {0..3} and 32j + 16 + 4g + {0..3}.  It equals the D
-// layout of a product whose rows are channels, so key-side gradients come out
-// of transposed products already in element layout.
 #include <type_traits>
 
 #include "gdn2_chunk.h"
 #include "gdn2_kernels.h"
 
 namespace gdn2 {
-
-__device__ __forceinline__ int ch4(int e, int g) { return 16 * (e >> 2) + 4 * g + (e & 3); }
-
-// key-side inputs of one token for the 4-group layout
-template <int DK, bool BF16>
-struct KeyRaw4 {
-    static constexpr int NM = DK / 16;
-    uint2 q[NM], k[NM];
-    float4 qx[NM], kx[NM];
-    float4 la[NM], bg[NM];
-    bool valid;
-
-    __device__ __forceinline__ void issue(const BwdArgs &a, size_t rowoff, int g, bool v) {
-        valid = v;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const size_t off = rowoff + 16 * m + 4 * g;
-            if (BF16) {
-                q[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.q) + off);
-                k[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.k) + off);
-            } else {
-                qx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + off);
-                kx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.k) + off);
-            }
-            la[m] = *reinterpret_cast<const float4 *>(a.la + off);
-            bg[m] = *reinterpret_cast<const float4 *>(a.bg + off);
-        }
-    }
-
-    __device__ __forceinline__ void unpack(float (&qf)[4 * NM], float (&kf)[4 * NM], float (&laf)[4 * NM],
-                                           float (&bgf)[4 * NM]) const {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if (BF16) {
-                qf[4 * m + 0] = __builtin_bit_cast(float, q[m].x << 16);
-                qf[4 * m + 1] = __builtin_bit_cast(float, q[m].x & 0xffff0000u);
-                qf[4 * m + 2] = __builtin_bit_cast(float, q[m].y << 16);
-                qf[4 * m + 3] = __builtin_bit_cast(float, q[m].y & 0xffff0000u);
-                kf[4 * m + 0] = __builtin_bit_cast(float, k[m].x << 16);
-                kf[4 * m + 1] = __builtin_bit_cast(float, k[m].x & 0xffff0000u);
-                kf[4 * m + 2] = __builtin_bit_cast(float, k[m].y << 16);
-                kf[4 * m + 3] = __builtin_bit_cast(float, k[m].y & 0xffff0000u);
-            } else {
-                qf[4 * m + 0] = qx[m].x; qf[4 * m + 1] = qx[m].y; qf[4 * m + 2] = qx[m].z; qf[4 * m + 3] = qx[m].w;
-                kf[4 * m + 0] = kx[m].x; kf[4 * m + 1] = kx[m].y; kf[4 * m + 2] = kx[m].z; kf[4 * m + 3] = kx[m].w;
-            }
-            laf[4 * m + 0] = la[m].x; laf[4 * m + 1] = la[m].y; laf[4 * m + 2] = la[m].z; laf[4 * m + 3] = la[m].w;
-            bgf[4 * m + 0] = bg[m].x; bgf[4 * m + 1] = bg[m].y; bgf[4 * m + 2] = bg[m].z; bgf[4 * m + 3] = bg[m].w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4 * NM; ++e) {
-            qf[e] = valid ? qf[e] : 0.f;
-            kf[e] = valid ? kf[e] : 0.f;
-            laf[e] = valid ? laf[e] : 0.f;
-            bgf[e] = valid ? bgf[e] : 0.f;
-        }
-    }
-};
-
-// Operand fragments of the key side in the 4-group layout.
-template <int NKS>
-struct KeyOps {
-    Split8 E[NKS], Q[NKS], K[NKS], H[NKS];   // Et, Qt, Kt, Kh
-};
-
-template <int NE, bool WE = true, bool WQ = true, bool WK = true, bool WH = true>
-__device__ __forceinline__ void key_operands(const float (&qf)[NE], const float (&kf)[NE], const float (&bgf)[NE],
-                                             const float (&G)[NE], const float (&gC)[NE], KeyOps<NE / 8> &ops) {
-#pragma unroll
-    for (int j = 0; j < NE / 8; ++j) {
-        float et[8], qt[8], kt[8], kh[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int e = 8 * j + s;
-            const float eg = (WE || WQ) ? exp2_fast(G[e]) : 0.f;
-            const float eng = WK ? exp2_fast(-G[e]) : 0.f;
-            const float ek = WH ? exp2_fast(gC[e] - G[e]) : 0.f;
-            et[s] = bgf[e] * kf[e] * eg;
-            qt[s] = qf[e] * eg;
-            kt[s] = kf[e] * eng;
-            kh[s] = kf[e] * ek;
-        }
-        if (WE) ops.E[j] = split8(et);
-        if (WQ) ops.Q[j] = split8(qt);
-        if (WK) ops.K[j] = split8(kt);
-        if (WH) ops.H[j] = split8(kh);
-    }
-}
-
-// Write this lane's row (token 16w + r) of an operand as [token][channel] bf16 (hi, lo planes).
-template <int NKS, int PK>
-__device__ __forceinline__ void store_rows(const Split8 (&f)[NKS], __bf16 *hi, __bf16 *lo, int row, int g) {
-#pragma unroll
-    for (int j = 0; j < NKS; ++j) {
-        bf16x4 h0, h1, l0, l1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            h0[i] = f[j].hi[i];
-            h1[i] = f[j].hi[4 + i];
-            l0[i] = f[j].lo[i];
-            l1[i] = f[j].lo[4 + i];
-        }
-        *reinterpret_cast<bf16x4 *>(&hi[row * PK + 32 * j + 4 * g]) = h0;
-        *reinterpret_cast<bf16x4 *>(&hi[row * PK + 32 * j + 16 + 4 * g]) = h1;
-        *reinterpret_cast<bf16x4 *>(&lo[row * PK + 32 * j + 4 * g]) = l0;
-        *reinterpret_cast<bf16x4 *>(&lo[row * PK + 32 * j + 16 + 4 * g]) = l1;
-    }
-}
-
-// Write this lane's row as columns of a [channel][token] bf16 tile (optionally negated).
-template <int NKS, int PT>
-__device__ __forceinline__ void store_cols(const Split8 (&f)[NKS], __bf16 *hi, __bf16 *lo, int tok, int g,
-                                           bool neg) {
-#pragma unroll
-    for (int j = 0; j < NKS; ++j)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int ch = 32 * j + 16 * (s >> 2) + 4 * g + (s & 3);
-            const __bf16 h = f[j].hi[s], l = f[j].lo[s];
-            hi[ch * PT + tok] = neg ? -h : h;
-            lo[ch * PT + tok] = neg ? -l : l;
-        }
-}
-
-// Key-side fragment (4-group contraction order) of row `row` of a [row][channel] tile.
-template <int PK>
-__device__ __forceinline__ Split8 row_frag4(const __bf16 *hi, const __bf16 *lo, int row, int j, int g) {
-    return frag_2x4(&hi[row * PK + 32 * j + 4 * g], &hi[row * PK + 32 * j + 16 + 4 * g],
-                    &lo[row * PK + 32 * j + 4 * g], &lo[row * PK + 32 * j + 16 + 4 * g]);
-}
-
-// A^T (rows of this wave's queries against key blocks mt <= w) into sA, and
-// P^T rows in registers: Pt[mt] holds P[16mt + 4g + i][16w + r] for mt >= w.
-template <int NKS, int PK, int PA, bool FAST>
-__device__ __forceinline__ void build_A_Pt(const KeyOps<NKS> &ops, const __bf16 *sKh, const __bf16 *sKl,
-                                           const __bf16 *sQh, const __bf16 *sQl, float *sA, Split4 (&Pt)[4],
-                                           int w, int r, int g) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        if (mt <= w) {
-            f32x4 acc = zero;
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const Split8 kf = row_frag4<PK>(sKh, sKl, 16 * mt + r, j, g);
-                if (FAST) acc = mfma32(kf.hi, ops.E[j].hi, acc);
-                else acc = mfma32x3(kf, ops.E[j], acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * mt + 4 * g + i < 16 * w + r)) acc[i] = 0.f;
-            *reinterpret_cast<f32x4 *>(&sA[(16 * w + r) * PA + 16 * mt + 4 * g]) = acc;
-        }
-        if (mt >= w) {
-            f32x4 acc = zero;
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) acc = mfma32x3(row_frag4<PK>(sQh, sQl, 16 * mt + r, j, g), ops.K[j], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
-            Pt[mt] = split4(acc);
-        } else {
-            Pt[mt] = split4(zero);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// reverse sweep: dS' of every chunk, and dS0
-// ---------------------------------------------------------------------------
-template <int DK, int VT, bool BF16>
-__global__ __launch_bounds__(kThreads, 1) void bwd_reverse_kernel(BwdArgs a) {
-    constexpr int NE = DK / 4, NM = DK / 16, NKS = DK / 32, NVT = VT / 16;
-    constexpr int NTS = NM * NVT / 4;
-    static_assert((NM * NVT) % 4 == 0, "state tiles must split over 4 waves");
-    constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4;
-    constexpr int RQ = kChunk * PK, RT = DK * PT;
-    constexpr int RM = RQ > RT ? RQ : RT;
-    constexpr int TPT = kChunk * VT / kThreads;  // dO tokens per thread
-    constexpr bool FAST = BF16;
-
-    __shared__ __align__(16) __bf16 sR1[4 * RM];       // Kt, Qt rows; later Qt^T, -Et^T
-    __shared__ __align__(16) float sA[kChunk * PA];
-    __shared__ __align__(16) float sT[kChunk * PA];
-    __shared__ __align__(16) __bf16 sD[2 * VT * PK];    // dS' [col][channel]
-    __shared__ __align__(16) __bf16 sO[2 * VT * PT];    // dO [col][token]
-    __shared__ __align__(16) __bf16 sdU[2 * VT * PT];   // dU [col][token]
-    __shared__ __align__(16) __bf16 sdX[2 * VT * PT];   // dX [col][token]
-    __shared__ __align__(16) float sTot[4 * DK];
-    __shared__ __align__(16) float sGam[DK];
-
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-    const int L = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int vt = L % a.nvt, bh = L / a.nvt, h = bh % a.H, b = bh / a.H;
-    const int T = a.T, H = a.H, DV = a.DV;
-    const int j0 = vt * VT;
-    const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
-    const size_t baseK = ((size_t)b * T * H + h) * DK;
-    const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
-    const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
-    const int NC = (T + kChunk - 1) / kChunk;
-    const int kk_lo = (w >= 2) ? 1 : 0;
-
-    f32x4 DS[NTS];
-#pragma unroll
-    for (int s = 0; s < NTS; ++s) {
-        const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            DS[s][i] = a.dS_final ? a.dS_final[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
-    }
-    for (int idx = tid; idx < kChunk * PA; idx += kThreads) sT[idx] = 0.f;
-    auto store_dS_lds = [&]() {
-#pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-            const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-            const Split4 sp = split4(DS[s]);
-            *reinterpret_cast<bf16x4 *>(&sD[(16 * n + r) * PK + 16 * m + 4 * g]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&sD[VT * PK + (16 * n + r) * PK + 16 * m + 4 * g]) = sp.lo;
-        }
-    };
-    store_dS_lds();
-    __syncthreads();
-
-    for (int c = NC - 1; c >= 0; --c) {
-        const int t0 = c * kChunk;
-        // gradient w.r.t. this chunk's end state
-        {
-            float *dst = a.dstates + (((size_t)b * H + h) * NC + c) * (size_t)DK * DV + j0;
-#pragma unroll
-            for (int s = 0; s < NTS; ++s) {
-                const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
-            }
-        }
-        // key side of the chunk
-        KeyRaw4<DK, BF16> raw;
-        {
-            const int tk = t0 + 16 * w + r;
-            const bool vk = tk < T;
-            raw.issue(a, baseK + (size_t)(vk ? tk : T - 1) * tokK, g, vk);
-        }
-        // dO tile -> [col][token]
-        {
-            const int col = tid % VT, tg = tid / VT;
-            float x[TPT];
-#pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                const int t = t0 + tg * TPT + i;
-                const float vv = a.dO[baseV + (size_t)(t < T ? t : T - 1) * tokV + col];
-                x[i] = t < T ? vv : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < TPT; ++i) {
-                __bf16 hh, ll;
-                split1(x[i], hh, ll);
-                sO[col * PT + tg * TPT + i] = hh;
-                sO[VT * PT + col * PT + tg * TPT + i] = ll;
-            }
-        }
-        float qf[NE], kf[NE], laf[NE], bgf[NE], G[NE], gC[NE];
-        raw.unpack(qf, kf, laf, bgf);
-#pragma unroll
-        for (int e = 0; e < NE; ++e) G[e] = laf[e] * kLog2e;
-        chunk_scan<NE, DK>(G, gC, sTot, w, r, [&](int e) { return ch4(e, g); });
-        if (w == 0 && r == 0) {
-#pragma unroll
-            for (int e = 0; e < NE; ++e) sGam[ch4(e, g)] = exp2_fast(gC[e]);
-        }
-        KeyOps<NKS> ops;
-        key_operands<NE>(qf, kf, bgf, G, gC, ops);
-        store_rows<NKS, PK>(ops.K, sR1, sR1 + RQ, 16 * w + r, g);
-        store_rows<NKS, PK>(ops.Q, sR1 + 2 * RQ, sR1 + 3 * RQ, 16 * w + r, g);
-        __syncthreads();
-
-        Split4 Pt[4];
-        build_A_Pt<NKS, PK, PA, FAST>(ops, sR1, sR1 + RQ, sR1 + 2 * RQ, sR1 + 3 * RQ, sA, Pt, w, r, g);
-        __syncthreads();
-        // Qt^T and -Et^T replace the row tiles
-        store_cols<NKS, PT>(ops.Q, sR1, sR1 + RT, 16 * w + r, g, false);
-        store_cols<NKS, PT>(ops.E, sR1 + 2 * RT, sR1 + 3 * RT, 16 * w + r, g, true);
-        solve_T<PA>(sA, sT, w, r, g);
-
-        // dU = P^T dO + Kh dS'
-#pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk >= kk_lo) {
-                    const Split8 of = frag_2x4(&sO[(16 * n + r) * PT + 32 * kk + 4 * g],
-                                               &sO[(16 * n + r) * PT + 32 * kk + 16 + 4 * g],
-                                               &sO[VT * PT + (16 * n + r) * PT + 32 * kk + 4 * g],
-                                               &sO[VT * PT + (16 * n + r) * PT + 32 * kk + 16 + 4 * g]);
-                    acc = mfma32x3(join(Pt[2 * kk], Pt[2 * kk + 1]), of, acc);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < NKS; ++j)
-                acc = mfma32x3(ops.H[j], row_frag4<PK>(sD, sD + VT * PK, 16 * n + r, j, g), acc);
-            const Split4 sp = split4(acc);
-            *reinterpret_cast<bf16x4 *>(&sdU[(16 * n + r) * PT + 16 * w + 4 * g]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&sdU[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sp.lo;
-        }
-        __syncthreads();
-        // dX = T^T dU
-#pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (kk >= kk_lo) {
-                    float tv[8];
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) tv[s] = sT[(32 * kk + 8 * g + s) * PA + 16 * w + r];
-                    acc = mfma32x3(split8(tv), frag_8(&sdU[(16 * n + r) * PT + 32 * kk + 8 * g],
-                                                      &sdU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), acc);
-                }
-            }
-            const Split4 sp = split4(acc);
-            *reinterpret_cast<bf16x4 *>(&sdX[(16 * n + r) * PT + 16 * w + 4 * g]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&sdX[VT * PT + (16 * n + r) * PT + 16 * w + 4 * g]) = sp.lo;
-        }
-        __syncthreads();
-        // dS <- diag(gamma) dS' + Qt^T dO - Et^T dX
-#pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-            const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-            f32x4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = sGam[16 * m + 4 * g + i] * DS[s][i];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                acc = mfma32x3(frag_8(&sR1[(16 * m + r) * PT + 32 * kk + 8 * g], &sR1[RT + (16 * m + r) * PT + 32 * kk + 8 * g]),
-                               frag_8(&sO[(16 * n + r) * PT + 32 * kk + 8 * g], &sO[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]),
-                               acc);
-                acc = mfma32x3(frag_8(&sR1[2 * RT + (16 * m + r) * PT + 32 * kk + 8 * g],
-                                      &sR1[3 * RT + (16 * m + r) * PT + 32 * kk + 8 * g]),
-                               frag_8(&sdX[(16 * n + r) * PT + 32 * kk + 8 * g], &sdX[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]),
-                               acc);
-            }
-            DS[s] = acc;
-        }
-        store_dS_lds();
-        __syncthreads();
-    }
-
-    if (a.dS0) {
-#pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-            const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.dS0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // chunk-parallel gradients of every token input
@@ -407,11 +44,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reverse_kernel(BwdArgs a) {
 // of each 32-column value tile.  The operand rows Kt and Et stay in LDS for the whole
 // chunk, so one workgroup takes most of a CU's LDS and the two halves give every SIMD
 // two waves.
-constexpr int kChunkThreads = 2 * kThreads;
-
-// Keep the scheduler from hoisting the LDS fragment loads of later unrolled steps
-// above this point (bounds the live registers at two waves per SIMD).
-#define GDN2_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <int DK, bool BF16>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
@@ -505,7 +137,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
     KeyRaw4<DK / 2, BF16> raw;
-    raw.issue(a, rowK + chh, g, vk);
+    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
     Tile cur;
     load_tile(0, cur, tid);
 
@@ -755,7 +387,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
-    raw.issue(a, rowK + chh, g, vk);
+    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
 #pragma unroll
     for (int it = 0; it < NSF; ++it) {
         const int idx = tid + NTH * it;
@@ -880,33 +512,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <int DK, int VT, bool BF16>
-static hipError_t rev_t(const BwdArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((bwd_reverse_kernel<DK, VT, BF16>), dim3((unsigned)(a.B * a.H * a.nvt)), dim3(kThreads), 0,
-                       st, a);
-    return hipGetLastError();
-}
-
-template <bool BF16>
-static hipError_t rev_dk(const BwdArgs &a, int dk, int vt, hipStream_t st) {
-    switch (dk) {
-        case 32: return vt == 32 ? rev_t<32, 32, BF16>(a, st) : hipErrorInvalidValue;
-        case 64: return vt == 16 ? rev_t<64, 16, BF16>(a, st) : vt == 32 ? rev_t<64, 32, BF16>(a, st) : hipErrorInvalidValue;
-        case 128: return vt == 16 ? rev_t<128, 16, BF16>(a, st) : vt == 32 ? rev_t<128, 32, BF16>(a, st) : hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-    }
-}
-
-int bwd_value_tile(int B, int H, int dk, int dv) {
-    int vt = dv < 32 ? dv : 32;
-    if (vt == 32 && dk >= 64 && (long)B * H * (dv / 32) < 256) vt = 16;
-    return vt;
-}
-
-hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, int vt, bool bf16, hipStream_t st) {
-    return bf16 ? rev_dk<true>(a, dk, vt, st) : rev_dk<false>(a, dk, vt, st);
-}
-
 template <int DK, bool BF16>
 static hipError_t chunk_t(const BwdArgs &a, hipStream_t st) {
     const int NC = (a.T + kChunk - 1) / kChunk;

@@ -240,4 +240,80 @@ __device__ __forceinline__ Split8 split8v(const f32x4 &a, const f32x4 &b) {
     return split8(t);
 }
 
+
+// ---------------------------------------------------------------------------
+// Key-side element layout of the backward kernels ("4-groups"): lane (w, r, g)
+// holds token 16w + r and channels 16m + 4g + i (i < 4); element e = 4m + i.  The
+// MFMA fragment of contraction step j is elements 8j..8j+7, i.e. channels
+// 32j + 4g + {0..3} and 32j + 16 + 4g + {0..3}.  It equals the D layout of a
+// product whose rows are channels, so key-side gradients come out of transposed
+// products already in element layout.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ch4(int e, int g) { return 16 * (e >> 2) + 4 * g + (e & 3); }
+
+// key-side inputs of one token for the 4-group layout
+template <int DK, bool BF16>
+struct KeyRaw4 {
+    static constexpr int NM = DK / 16;
+    uint2 q[NM], k[NM];
+    float4 qx[NM], kx[NM];
+    float4 la[NM], bg[NM];
+    bool valid;
+
+    // q, k: qkv dtype; la, bg: fp32; rowoff: element offset of channel 0 of the token row
+    __device__ __forceinline__ void issue(const void *qp, const void *kp, const float *lap, const float *bgp,
+                                          size_t rowoff, int g, bool v) {
+        valid = v;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const size_t off = rowoff + 16 * m + 4 * g;
+            if (BF16) {
+                q[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(qp) + off);
+                k[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(kp) + off);
+            } else {
+                qx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qp) + off);
+                kx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(kp) + off);
+            }
+            la[m] = *reinterpret_cast<const float4 *>(lap + off);
+            bg[m] = *reinterpret_cast<const float4 *>(bgp + off);
+        }
+    }
+
+    __device__ __forceinline__ void unpack(float (&qf)[4 * NM], float (&kf)[4 * NM], float (&laf)[4 * NM],
+                                           float (&bgf)[4 * NM]) const {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (BF16) {
+                qf[4 * m + 0] = __builtin_bit_cast(float, q[m].x << 16);
+                qf[4 * m + 1] = __builtin_bit_cast(float, q[m].x & 0xffff0000u);
+                qf[4 * m + 2] = __builtin_bit_cast(float, q[m].y << 16);
+                qf[4 * m + 3] = __builtin_bit_cast(float, q[m].y & 0xffff0000u);
+                kf[4 * m + 0] = __builtin_bit_cast(float, k[m].x << 16);
+                kf[4 * m + 1] = __builtin_bit_cast(float, k[m].x & 0xffff0000u);
+                kf[4 * m + 2] = __builtin_bit_cast(float, k[m].y << 16);
+                kf[4 * m + 3] = __builtin_bit_cast(float, k[m].y & 0xffff0000u);
+            } else {
+                qf[4 * m + 0] = qx[m].x; qf[4 * m + 1] = qx[m].y; qf[4 * m + 2] = qx[m].z; qf[4 * m + 3] = qx[m].w;
+                kf[4 * m + 0] = kx[m].x; kf[4 * m + 1] = kx[m].y; kf[4 * m + 2] = kx[m].z; kf[4 * m + 3] = kx[m].w;
+            }
+            laf[4 * m + 0] = la[m].x; laf[4 * m + 1] = la[m].y; laf[4 * m + 2] = la[m].z; laf[4 * m + 3] = la[m].w;
+            bgf[4 * m + 0] = bg[m].x; bgf[4 * m + 1] = bg[m].y; bgf[4 * m + 2] = bg[m].z; bgf[4 * m + 3] = bg[m].w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4 * NM; ++e) {
+            qf[e] = valid ? qf[e] : 0.f;
+            kf[e] = valid ? kf[e] : 0.f;
+            laf[e] = valid ? laf[e] : 0.f;
+            bgf[e] = valid ? bgf[e] : 0.f;
+        }
+    }
+};
+
+// Key-side fragment (4-group contraction order) of row `row` of a [row][channel] tile.
+template <int PK>
+__device__ __forceinline__ Split8 row_frag4(const __bf16 *hi, const __bf16 *lo, int row, int j, int g) {
+    return frag_2x4(&hi[row * PK + 32 * j + 4 * g], &hi[row * PK + 32 * j + 16 + 4 * g],
+                    &lo[row * PK + 32 * j + 4 * g], &lo[row * PK + 32 * j + 16 + 4 * g]);
+}
+
 }  // namespace gdn2

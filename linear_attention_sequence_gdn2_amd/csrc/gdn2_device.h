@@ -29,6 +29,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 64;
 constexpr int kThreads = 256;
+constexpr int kChunkThreads = 2 * kThreads;   // workgroup of the chunk-parallel backward kernels
+
+// Keep the scheduler from hoisting the LDS fragment loads of later unrolled steps
+// above this point (bounds the live registers of a wave).
+#define GDN2_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 struct Split8 {
     bf16x8 hi, lo;

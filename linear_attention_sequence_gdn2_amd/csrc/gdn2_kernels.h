@@ -28,19 +28,18 @@ struct BwdArgs {
     const float *states;            // [B,H,NC,dk,dv] chunk-start states
     float *dstates;                 // [B,H,NC,dk,dv] gradient w.r.t. chunk-end states
     float *dq, *dk, *dv, *dla, *db, *dw, *dS0;
+    void *factors;                  // [B,H,NC] per-chunk adjoint factors (bf16 tiles)
     int B, T, H, DV;
-    int nvt;
 };
 
 // Value-tile width the forward sweep uses for this shape (16, 32 or 64).
 int fwd_value_tile(int B, int H, int dk, int dv);
-// Value-tile width of the backward reverse sweep (16 or 32).
-int bwd_value_tile(int B, int H, int dk, int dv);
 
 // What a forward sweep produces: o only, chunk states only, or both.
 enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
 hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, FwdMode mode, hipStream_t st);
-hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, int vt, bool bf16, hipStream_t st);
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, hipStream_t st);
+hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, hipStream_t st);
 
 }  // namespace gdn2

@@ -1,0 +1,401 @@
+// gdn2_reverse.hip -- reverse sweep of the gate-aware backward on gfx950: per-chunk
+// adjoint factors (chunk-parallel), then the chunk-to-chunk recurrence of the state
+// gradient (sequential over chunks).
+//
+// Chunk notation of gdn2_fwd.hip (blog on Gated DeltaNet-2, section "Token path and
+// parallel training"): start state S, end state S' = diag(gamma)(S + Kt^T U),
+// U = T X, X = Z - Et S, O = Qt S + P U.  The adjoint of one chunk gives for the
+// gradient of its start state
+//     dS = Qt^T dO + diag(gamma) dS' - Et^T dX,   dX = T^T (P^T dO + Kt diag(gamma) dS').
+// With W = T Et (the WY factor of the erase keys) this is
+//     dS = R dS' + Q2^T dO,   R = (I - W^T Kt) diag(gamma),   Q2 = Qt - P W,
+// where R (dk x dk) and Q2 (64 x dk) depend on the key side of the chunk only.
+// bwd_factors_kernel forms them for every (batch, head, chunk) at once, and
+// bwd_reverse_kernel is left with two dense products per chunk on its critical path.
+//
+// Factor buffer of one (batch, head, chunk): NM*NM tiles of R, then NM*4 tiles of
+// Q2^T (NM = dk/16).  Tile (m, kb) of a matrix X holds X[16m + r'][16kb + c'] for
+// r', c' < 16 in MFMA fragment order: 64 lanes x 8 bf16, lane (r, g) storing
+// X[16m + r][16kb + 4g + i] split as hi (i < 4) then lo (i < 4).  Two tiles kb = 2j,
+// 2j + 1 give a lane its whole A operand of contraction step j in the 4-group order,
+// with one 16-byte load each.
+#include "gdn2_chunk.h"
+#include "gdn2_kernels.h"
+
+namespace gdn2 {
+
+constexpr int kFragTile = 64 * 8;   // bf16 per stored 16x16 factor tile
+
+template <int DK>
+constexpr size_t factor_elems_per_chunk() {
+    return (size_t)((DK / 16) * (DK / 16) + (DK / 16) * 4) * kFragTile;
+}
+
+// 16x16 tile from its D-layout transpose: the lane holds X[16m + r][16kb + 4g + i] (i < 4)
+__device__ __forceinline__ void store_frag_tile(__bf16 *tile, int l, const f32x4 &v) {
+    const Split4 s = split4(v);
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[i] = s.hi[i];
+        o[4 + i] = s.lo[i];
+    }
+    *reinterpret_cast<bf16x8 *>(tile + 8 * l) = o;
+}
+
+// A operand of contraction step j from the two stored tiles kb = 2j, 2j + 1
+__device__ __forceinline__ Split8 frag_from_tiles(const uint4 &t0, const uint4 &t1) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, t0), b = __builtin_bit_cast(bf16x8, t1);
+    Split8 f;
+    f.hi = __builtin_shufflevector(a, b, 0, 1, 2, 3, 8, 9, 10, 11);
+    f.lo = __builtin_shufflevector(a, b, 4, 5, 6, 7, 12, 13, 14, 15);
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// adjoint factors R and Q2^T of every (batch, head, chunk)
+// ---------------------------------------------------------------------------
+// Eight waves in two halves, as in bwd_chunk_kernel: wave (hf, w) owns tokens
+// 16w..16w+15 and, for the element work, the channels of half hf.
+template <int DK, bool BF16>
+__global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
+    constexpr int NTH = kChunkThreads;
+    constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
+    constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4;
+    constexpr int RK = kChunk * PK;
+    constexpr bool FAST = BF16;
+    // LDS (bytes): Kt, Et, Qt rows [token][channel] (hi, lo); the decay totals after the
+    // Et rows; W^T [channel][token] (hi, lo) later over the Et rows and the totals;
+    // A then T (fp32); gamma per channel.
+    constexpr int B_ROWS = 2 * RK * 2, B_WT = 2 * DK * PT * 2, B_TOT = 4 * DK * 4;
+    constexpr int oKt = 0, oEt = oKt + B_ROWS, oTot = oEt + B_ROWS;
+    constexpr int oQt0 = (oTot + B_TOT > oEt + B_WT) ? oTot + B_TOT : oEt + B_WT;
+    constexpr int oQt = (oQt0 + 15) / 16 * 16;
+    constexpr int oAT = oQt + B_ROWS, oGam = oAT + kChunk * PA * 4;
+    constexpr int SMEM = oGam + DK * 4;
+    static_assert(SMEM <= 160 * 1024, "LDS budget of a CU");
+
+    __shared__ __align__(16) char smem[SMEM];
+    __bf16 *sKt = reinterpret_cast<__bf16 *>(smem + oKt), *sEt = reinterpret_cast<__bf16 *>(smem + oEt);
+    __bf16 *sQt = reinterpret_cast<__bf16 *>(smem + oQt), *sWT = reinterpret_cast<__bf16 *>(smem + oEt);
+    float *sTot = reinterpret_cast<float *>(smem + oTot), *sAT = reinterpret_cast<float *>(smem + oAT);
+    float *sGam = reinterpret_cast<float *>(smem + oGam);
+
+    const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
+    const int NC = (a.T + kChunk - 1) / kChunk;
+    const int L = xcd_swizzle(blockIdx.x, gridDim.x);   // (b * H + h) * NC + c
+    const int c = L % NC, bh = L / NC, h = bh % a.H, b = bh / a.H;
+    const int T = a.T, H = a.H;
+    const int t0 = c * kChunk;
+    const size_t tokK = (size_t)H * DK;
+    const size_t baseK = ((size_t)b * T * H + h) * DK;
+    const int nkk = (w >= 2) ? 2 : 1;
+    const int tk = t0 + 16 * w + r;
+    const bool vk = tk < T;
+    const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
+    const int chh = hf * (DK / 2);
+    auto ch = [&](int e) { return chh + ch4(e, g); };
+    __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
+
+    for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
+    {
+        KeyRaw4<DK / 2, BF16> raw;
+        raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
+        float qf[NEH], kf[NEH], G[NEH], bgf[NEH], gC[NEH];
+        raw.unpack(qf, kf, G, bgf);
+#pragma unroll
+        for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
+        chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
+        if (w == 0 && r == 0) {
+#pragma unroll
+            for (int e = 0; e < NEH; ++e) sGam[ch(e)] = exp2_fast(gC[e]);
+        }
+#pragma unroll
+        for (int mm = 0; mm < NMH; ++mm) {
+            f32x4 et, qt, kt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * mm + i;
+                const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]);
+                et[i] = bgf[e] * kf[e] * eg;
+                qt[i] = qf[e] * eg;
+                kt[i] = kf[e] * eng;
+            }
+            const int o = (16 * w + r) * PK + chh + 16 * mm + 4 * g;
+            const Split4 se = split4(et), sq = split4(qt), sk = split4(kt);
+            *reinterpret_cast<bf16x4 *>(&sEt[o]) = se.hi;
+            *reinterpret_cast<bf16x4 *>(&sEt[RK + o]) = se.lo;
+            *reinterpret_cast<bf16x4 *>(&sQt[o]) = sq.hi;
+            *reinterpret_cast<bf16x4 *>(&sQt[RK + o]) = sq.lo;
+            *reinterpret_cast<bf16x4 *>(&sKt[o]) = sk.hi;
+            *reinterpret_cast<bf16x4 *>(&sKt[RK + o]) = sk.lo;
+        }
+    }
+    __syncthreads();
+
+    // ---- A (shared out between the halves) and the rows of P of query block w ----
+    Split4 Pf[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        if (mt <= w && (mt & 1) == hf) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g);
+                const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
+                if (FAST) acc = mfma32(kf.hi, ef.hi, acc);
+                else acc = mfma32x3(kf, ef, acc);
+            }
+            // lane holds A[16w + r][16mt + 4g + i]
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(16 * mt + 4 * g + i < 16 * w + r)) acc[i] = 0.f;
+            *reinterpret_cast<f32x4 *>(&sAT[(16 * w + r) * PA + 16 * mt + 4 * g]) = acc;
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (mt <= w) {
+#pragma unroll
+            for (int j = 0; j < NKS; ++j)
+                acc = mfma32x3(row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g),
+                               row_frag4<PK>(sQt, sQt + RK, 16 * w + r, j, g), acc);
+            // lane holds P[16w + r][16mt + 4g + i]; the query reads the updated state: key <= query
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(16 * mt + 4 * g + i <= 16 * w + r)) acc[i] = 0.f;
+        }
+        Pf[mt] = split4(acc);
+    }
+    __syncthreads();
+    solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
+
+    // ---- W = T Et: tiles (token block w, channel blocks of half hf) ----
+    f32x4 Wt[NMH];
+#pragma unroll
+    for (int aa = 0; aa < NMH; ++aa) {
+        const int am = NMH * hf + aa;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk < nkk) {
+                const float *trow = &sAT[(16 * w + r) * PA + 32 * kk];
+                const Split8 tf = split8v(*reinterpret_cast<const f32x4 *>(trow + 4 * g),
+                                          *reinterpret_cast<const f32x4 *>(trow + 16 + 4 * g));
+                acc = mfma32x3(tf, frag_tr<PK>(sEt, sEt + RK, 32 * kk, 16 * am, r, g), acc);
+            }
+        }
+        Wt[aa] = acc;   // lane holds W[16w + 4g + i][16am + r]
+    }
+    __syncthreads();    // the Et rows and the decay totals are dead: W^T goes over them
+#pragma unroll
+    for (int aa = 0; aa < NMH; ++aa) {
+        const int am = NMH * hf + aa;
+        const Split4 sw = split4(Wt[aa]);
+        *reinterpret_cast<bf16x4 *>(&sWT[(16 * am + r) * PT + 16 * w + 4 * g]) = sw.hi;
+        *reinterpret_cast<bf16x4 *>(&sWT[DK * PT + (16 * am + r) * PT + 16 * w + 4 * g]) = sw.lo;
+    }
+    __syncthreads();
+
+    // ---- Q2 = Qt - P W: tiles (token block w, channel blocks of half hf), stored as Q2^T ----
+#pragma unroll
+    for (int aa = 0; aa < NMH; ++aa) {
+        const int am = NMH * hf + aa;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk < nkk) {
+                const __bf16 *wh = &sWT[(16 * am + r) * PT + 32 * kk], *wl = wh + DK * PT;
+                acc = mfma32x3(join(Pf[2 * kk], Pf[2 * kk + 1]),
+                               frag_2x4(wh + 4 * g, wh + 16 + 4 * g, wl + 4 * g, wl + 16 + 4 * g), acc);
+            }
+        }
+        // lane holds (P W)[16w + 4g + i][16am + r] = (W^T P^T)[16am + r][16w + 4g + i]
+        f32x4 q2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int o = (16 * w + 4 * g + i) * PK + 16 * am + r;
+            q2[i] = ((float)sQt[o] + (float)sQt[RK + o]) - acc[i];
+        }
+        store_frag_tile(fac + (size_t)(NM * NM + am * 4 + w) * kFragTile, l, q2);
+    }
+
+    // ---- R = (I - W^T Kt) diag(gamma), tile (row block am, column block bm) ----
+    for (int t = wv; t < NM * NM; t += NTH / 64) {
+        const int bm = t / NM, am = t % NM;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const __bf16 *wh = &sWT[(16 * am + r) * PT + 32 * kk], *wl = wh + DK * PT;
+            acc = mfma32x3(frag_tr<PK>(sKt, sKt + RK, 32 * kk, 16 * bm, r, g),
+                           frag_2x4(wh + 4 * g, wh + 16 + 4 * g, wl + 4 * g, wl + 16 + 4 * g), acc);
+        }
+        // lane holds (Kt^T W)[16bm + 4g + i][16am + r] = (W^T Kt)[16am + r][16bm + 4g + i]
+        f32x4 rt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = 16 * bm + 4 * g + i, rr = 16 * am + r;
+            rt[i] = sGam[cc] * ((cc == rr ? 1.f : 0.f) - acc[i]);
+        }
+        store_frag_tile(fac + (size_t)(am * NM + bm) * kFragTile, l, rt);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reverse sweep: dS' of every chunk (dstates) and dS0
+// ---------------------------------------------------------------------------
+// One workgroup per (batch, head, 32-column value tile); each wave owns state tiles
+// of one 16-row block.  Per chunk, going backwards: store dS', stage it and dO in
+// LDS (double-buffered, so one barrier per chunk), then dS = R dS' + Q2^T dO.
+template <int DK>
+struct ReverseCfg {
+    static constexpr int NM = DK / 16;
+    static constexpr int NWAVES = (2 * NM >= 8) ? 8 : 2 * NM;
+    static constexpr int NTH = 64 * NWAVES;
+    static constexpr int TPW = 2 * NM / NWAVES;   // state tiles per wave, all in one row block
+};
+
+template <int DK>
+__global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(BwdArgs a) {
+    constexpr int NM = DK / 16, NKS = DK / 32;
+    constexpr int NTH = ReverseCfg<DK>::NTH, TPW = ReverseCfg<DK>::TPW;
+    constexpr int VT = 32, PK = DK + 8, PT = kChunk + 8;
+    constexpr int OPT = VT * kChunk / NTH;          // dO elements per thread per chunk
+    static_assert(OPT == 4 || OPT == 8, "dO staging");
+    constexpr size_t FPC = factor_elems_per_chunk<DK>();
+
+    __shared__ __align__(16) __bf16 sD[2][2 * VT * PK];   // dS' as [col][channel] (hi, lo)
+    __shared__ __align__(16) __bf16 sO[2][2 * VT * PT];   // dO as [col][token] (hi, lo)
+
+    const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    const int nvt = a.DV / VT;
+    const int L = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int vt = L % nvt, bh = L / nvt, h = bh % a.H, b = bh / a.H;
+    const int T = a.T, H = a.H, DV = a.DV;
+    const int NC = (T + kChunk - 1) / kChunk;
+    const int j0 = vt * VT;
+    const size_t tokV = (size_t)H * DV;
+    const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
+    const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
+    const int m = (wv * TPW) >> 1;                  // row block of this wave's state tiles
+    const __bf16 *fbh = reinterpret_cast<const __bf16 *>(a.factors) + (size_t)bh * NC * FPC;
+
+    f32x4 DS[TPW];
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+        const int n = (wv * TPW + s) & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            DS[s][i] = a.dS_final ? a.dS_final[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
+    }
+    // dO staging: column tid % 32, tokens OPT * (tid / 32) .. + OPT - 1 of the chunk
+    const int ocol = tid & 31, otg = tid >> 5;
+    float ox[OPT];
+    auto load_dO = [&](int cc) {
+#pragma unroll
+        for (int i = 0; i < OPT; ++i) {
+            const int t = cc * kChunk + OPT * otg + i;
+            ox[i] = a.dO[baseV + (size_t)(t < T ? t : T - 1) * tokV + ocol];
+        }
+    };
+    load_dO(NC - 1);
+
+    for (int c = NC - 1; c >= 0; --c) {
+        const int buf = c & 1;
+        const __bf16 *fc = fbh + (size_t)c * FPC;
+        uint4 fr[NM], fq[4];
+#pragma unroll
+        for (int kb = 0; kb < NM; ++kb)
+            fr[kb] = *reinterpret_cast<const uint4 *>(fc + (size_t)(m * NM + kb) * kFragTile + 8 * l);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            fq[kb] = *reinterpret_cast<const uint4 *>(fc + (size_t)(NM * NM + m * 4 + kb) * kFragTile + 8 * l);
+
+        // gradient w.r.t. the end state of chunk c
+        float *dst = a.dstates + ((size_t)bh * NC + c) * (size_t)DK * DV + j0;
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int n = (wv * TPW + s) & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
+            const Split4 sp = split4(DS[s]);
+            *reinterpret_cast<bf16x4 *>(&sD[buf][(16 * n + r) * PK + 16 * m + 4 * g]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&sD[buf][VT * PK + (16 * n + r) * PK + 16 * m + 4 * g]) = sp.lo;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < OPT / 4; ++q4) {
+            f32x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = (c * kChunk + OPT * otg + 4 * q4 + i < T) ? ox[4 * q4 + i] : 0.f;
+            const Split4 so = split4(ov);
+            *reinterpret_cast<bf16x4 *>(&sO[buf][ocol * PT + OPT * otg + 4 * q4]) = so.hi;
+            *reinterpret_cast<bf16x4 *>(&sO[buf][VT * PT + ocol * PT + OPT * otg + 4 * q4]) = so.lo;
+        }
+        load_dO(c > 0 ? c - 1 : 0);   // the next chunk's dO is in flight during this chunk's products
+        __syncthreads();
+
+        // dS = R dS' + Q2^T dO
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int n = (wv * TPW + s) & 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKS; ++j)
+                acc = mfma32x3(frag_from_tiles(fr[2 * j], fr[2 * j + 1]),
+                               row_frag4<PK>(sD[buf], sD[buf] + VT * PK, 16 * n + r, j, g), acc);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const __bf16 *oh = &sO[buf][(16 * n + r) * PT + 32 * kk], *ol = oh + VT * PT;
+                acc = mfma32x3(frag_from_tiles(fq[2 * kk], fq[2 * kk + 1]),
+                               frag_2x4(oh + 4 * g, oh + 16 + 4 * g, ol + 4 * g, ol + 16 + 4 * g), acc);
+            }
+            DS[s] = acc;
+        }
+    }
+
+    if (a.dS0) {
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int n = (wv * TPW + s) & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.dS0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch
+// ---------------------------------------------------------------------------
+template <int DK, bool BF16>
+static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
+    const int NC = (a.T + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads), 0,
+                       st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, hipStream_t st) {
+    switch (dk) {
+        case 32: return bf16 ? factors_t<32, true>(a, st) : factors_t<32, false>(a, st);
+        case 64: return bf16 ? factors_t<64, true>(a, st) : factors_t<64, false>(a, st);
+        case 128: return bf16 ? factors_t<128, true>(a, st) : factors_t<128, false>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DK>
+static hipError_t reverse_t(const BwdArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL((bwd_reverse_kernel<DK>), dim3((unsigned)(a.B * a.H * (a.DV / 32))),
+                       dim3(ReverseCfg<DK>::NTH), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st) {
+    if (a.DV % 32 != 0) return hipErrorInvalidValue;
+    switch (dk) {
+        case 32: return reverse_t<32>(a, st);
+        case 64: return reverse_t<64>(a, st);
+        case 128: return reverse_t<128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn2

@@ -46,7 +46,9 @@ def test_workspace_and_state_sizes():
     nc = (100 + 63) // 64
     one = 2 * 3 * nc * 128 * 64 * 4
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(s)) == one
-    assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s)) == 2 * one
+    factors = 2 * 3 * nc * (128 * 128 + 64 * 128) * 4
+    assert lib.gdn2_chunk_factors_bytes(ctypes.byref(s)) == factors
+    assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s)) == 2 * one + factors
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 0
     bad = _shape(dk=96)
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
@@ -101,7 +103,10 @@ def test_staged_entry_points_check_arguments():
     f = P(0x10000)
     assert lib.gdn2_chunk_fwd_states(ctypes.byref(s), f, f, f, f, f, f, None, f, None, None, None) == INVALID
     assert lib.gdn2_chunk_states(ctypes.byref(s), f, f, f, f, f, None, None, None) == INVALID
-    assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), f, f, f, f, f, None, None, None, None) == INVALID
+    assert lib.gdn2_chunk_bwd_factors(ctypes.byref(s), f, f, f, f, None, None) == INVALID
+    assert lib.gdn2_chunk_bwd_factors(ctypes.byref(s), f, f, f, P(0x10008), f, None) == INVALID
+    assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), f, f, None, None, None, None) == INVALID
+    assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), None, f, None, f, None, None) == INVALID
     assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, f, f, f, f, None, None) == INVALID
 
 

@@ -69,7 +69,8 @@ def test_every_output_element_is_written():
     states = torch.full((B, H, nc, dk, dv), float("nan"), device="cuda")
     o, sf, states = gdn2.fwd_states(*_fargs(d), states=states)
     dstates = torch.full_like(states, float("nan"))
-    dstates, dS0 = gdn2.bwd_reverse(d["q"], d["k"], d["log_alpha"], d["b"], d["dO"], d["dS_final"], dstates=dstates)
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], dk, d["dS_final"], dstates=dstates)
     g = gdn2.bwd_grads(*_fargs(d)[:6], d["dO"], states, dstates)
     torch.cuda.synchronize()
     for t in [o, sf, states, dstates, dS0] + list(g.values()):
