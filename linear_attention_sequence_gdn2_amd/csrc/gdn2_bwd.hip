@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     load_tile(0, cur, tid);
 
     // ---- preparation: decay, operand rows, A -> T, P^T rows in registers ----
+    float Gk[NEH], bk[NEH];        // kept for the element-wise chain of the epilogue
     {
         float qf[NEH], kf[NEH], laf[NEH], bgf[NEH], G[NEH], gC[NEH];
         raw.unpack(qf, kf, laf, bgf);
@@ -151,6 +152,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         if (w == 0 && r == 0) {
 #pragma unroll
             for (int e = 0; e < NEH; ++e) sGam[ch(e)] = exp2_fast(gC[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < NEH; ++e) {
+            Gk[e] = G[e];
+            bk[e] = bgf[e];
         }
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
@@ -372,10 +378,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     }
 
     // ---- epilogue: dgamma, dP/dA products, element-wise chain ----
-    // The key-side inputs are read again (rather than kept through the value loop) and
-    // the decay prefix is rebuilt from the totals the first scan left in LDS.  The lane
-    // indices are derived afresh from an opaque copy of the thread index, so that no
-    // address arithmetic of the preparation is kept live across the value loop.
+    // q and k (packed), b and the decay prefix G stayed in registers through the value
+    // loop.  The lane indices are derived afresh from an opaque copy of the thread
+    // index, so that no address arithmetic of the preparation is kept live across it.
   {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -387,7 +392,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
-    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
 #pragma unroll
     for (int it = 0; it < NSF; ++it) {
         const int idx = tid + NTH * it;
@@ -411,10 +415,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
-    raw.unpack(qf, kf, G, bgf);
+    raw.unpack_qk(qf, kf);
 #pragma unroll
-    for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
-    chunk_rescan<NEH, DK>(G, sTot, w, ch);
+    for (int e = 0; e < NEH; ++e) {
+        G[e] = Gk[e];
+        bgf[e] = bk[e];
+    }
     {
         // Qt rows of this half's channels again
 #pragma unroll

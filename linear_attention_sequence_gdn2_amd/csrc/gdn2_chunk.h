@@ -36,20 +36,6 @@ __device__ __forceinline__ void chunk_scan(float (&x)[NE], float (&tot)[NE], flo
     }
 }
 
-// The inclusive prefix of chunk_scan again, from fresh per-token values x and the
-// per-wave totals chunk_scan left in sTot: the same operations in the same order, so
-// the result is bitwise the one chunk_scan returned.  No barrier.
-template <int NE, int DK, typename ChanFn>
-__device__ __forceinline__ void chunk_rescan(float (&x)[NE], const float *sTot, int w, ChanFn ch) {
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        x[e] = row_scan16(x[e]);
-        const int c = ch(e);
-        const float pre = (w > 0 ? sTot[c] : 0.f) + (w > 1 ? sTot[DK + c] : 0.f) + (w > 2 ? sTot[2 * DK + c] : 0.f);
-        x[e] += pre;
-    }
-}
-
 // Inverse of one unit-lower 16x16 block, (I + N)^-1 with N strictly lower, so
 // N^16 = 0 and (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly.  The
 // powers are formed on MFMA in both the row layout (lane holds X[r][4g+i]) and
@@ -276,6 +262,31 @@ struct KeyRaw4 {
             }
             la[m] = *reinterpret_cast<const float4 *>(lap + off);
             bg[m] = *reinterpret_cast<const float4 *>(bgp + off);
+        }
+    }
+
+    // q and k only (zero for a missing token)
+    __device__ __forceinline__ void unpack_qk(float (&qf)[4 * NM], float (&kf)[4 * NM]) const {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (BF16) {
+                qf[4 * m + 0] = __builtin_bit_cast(float, q[m].x << 16);
+                qf[4 * m + 1] = __builtin_bit_cast(float, q[m].x & 0xffff0000u);
+                qf[4 * m + 2] = __builtin_bit_cast(float, q[m].y << 16);
+                qf[4 * m + 3] = __builtin_bit_cast(float, q[m].y & 0xffff0000u);
+                kf[4 * m + 0] = __builtin_bit_cast(float, k[m].x << 16);
+                kf[4 * m + 1] = __builtin_bit_cast(float, k[m].x & 0xffff0000u);
+                kf[4 * m + 2] = __builtin_bit_cast(float, k[m].y << 16);
+                kf[4 * m + 3] = __builtin_bit_cast(float, k[m].y & 0xffff0000u);
+            } else {
+                qf[4 * m + 0] = qx[m].x; qf[4 * m + 1] = qx[m].y; qf[4 * m + 2] = qx[m].z; qf[4 * m + 3] = qx[m].w;
+                kf[4 * m + 0] = kx[m].x; kf[4 * m + 1] = kx[m].y; kf[4 * m + 2] = kx[m].z; kf[4 * m + 3] = kx[m].w;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4 * NM; ++e) {
+            qf[e] = valid ? qf[e] : 0.f;
+            kf[e] = valid ? kf[e] : 0.f;
         }
     }
 

@@ -83,26 +83,55 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 
     const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int NC = (a.T + kChunk - 1) / kChunk;
-    const int L = xcd_swizzle(blockIdx.x, gridDim.x);   // (b * H + h) * NC + c
-    const int c = L % NC, bh = L / NC, h = bh % a.H, b = bh / a.H;
     const int T = a.T, H = a.H;
-    const int t0 = c * kChunk;
+    const int nitems = a.B * H * NC;                    // item L = (b * H + h) * NC + c
     const size_t tokK = (size_t)H * DK;
-    const size_t baseK = ((size_t)b * T * H + h) * DK;
     const int nkk = (w >= 2) ? 2 : 1;
-    const int tk = t0 + 16 * w + r;
-    const bool vk = tk < T;
-    const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
+    // this lane's token row (channel 0 of its half) in item L, and whether the token exists
+    auto item_row = [&](int L, bool &valid) {
+        const int c = L % NC, bh = L / NC, h = bh % H, b = bh / H;
+        const int tk = c * kChunk + 16 * w + r;
+        valid = tk < T;
+        return ((size_t)b * T * H + h) * DK + (size_t)(valid ? tk : T - 1) * tokK + chh;
+    };
+
+    // Persistent: the workgroup walks items blockIdx.x, + gridDim.x, ...; the key-side
+    // inputs of the next item are loaded while the current one is in its products.
+    KeyRaw4<DK / 2, BF16> raw;
+    {
+        bool v0;
+        const size_t row0 = item_row(blockIdx.x < nitems ? blockIdx.x : 0, v0);
+        raw.issue(a.q, a.k, a.la, a.bg, row0, g, v0);
+    }
+    for (int L = blockIdx.x; L < nitems; L += gridDim.x) {
+    // lane indices afresh from an opaque copy of the thread index: the address
+    // arithmetic is redone per item instead of being held in registers across items
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
+    const int nkk = (w >= 2) ? 2 : 1;
+    const int chh = hf * (DK / 2);
+    auto ch = [&](int e) { return chh + ch4(e, g); };
+    auto item_row = [&](int L, bool &valid) {
+        const int c = L % NC, bh = L / NC, h = bh % H, b = bh / H;
+        const int tk = c * kChunk + 16 * w + r;
+        valid = tk < T;
+        return ((size_t)b * T * H + h) * DK + (size_t)(valid ? tk : T - 1) * tokK + chh;
+    };
     __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
     {
-        KeyRaw4<DK / 2, BF16> raw;
-        raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
         float qf[NEH], kf[NEH], G[NEH], bgf[NEH], gC[NEH];
         raw.unpack(qf, kf, G, bgf);
+        {
+            const int Ln = L + (int)gridDim.x < nitems ? L + (int)gridDim.x : L;
+            bool vn;
+            const size_t rown = item_row(Ln, vn);
+            raw.issue(a.q, a.k, a.la, a.bg, rown, g, vn);
+        }
 #pragma unroll
         for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
         chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
@@ -237,29 +266,39 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         }
         store_frag_tile(fac + (size_t)(am * NM + bm) * kFragTile, l, rt);
     }
+    __syncthreads();   // the next item overwrites the LDS this one still reads
+    }
 }
 
 // ---------------------------------------------------------------------------
 // reverse sweep: dS' of every chunk (dstates) and dS0
 // ---------------------------------------------------------------------------
-// One workgroup per (batch, head, 32-column value tile); each wave owns state tiles
-// of one 16-row block.  Per chunk, going backwards: store dS', stage it and dO in
-// LDS (double-buffered, so one barrier per chunk), then dS = R dS' + Q2^T dO.
-template <int DK>
+// One workgroup per (batch, head, value tile of VT columns); each wave owns the
+// state tiles of one 16-row block.  Per chunk, going backwards: store dS', stage it
+// and dO in LDS (double-buffered, so one barrier per chunk), then
+// dS = R dS' + Q2^T dO.  The factors are chunk-local, so at VT = 64 (one workgroup
+// per CU, registers to spare) the next chunk's fragments are loaded while the
+// current chunk's products run; at VT = 32 two workgroups share a CU instead.
+template <int DK, int VT>
 struct ReverseCfg {
-    static constexpr int NM = DK / 16;
-    static constexpr int NWAVES = (2 * NM >= 8) ? 8 : 2 * NM;
+    static constexpr int NM = DK / 16, NVT = VT / 16;
+    static constexpr int NWAVES = (NM * NVT >= 8) ? 8 : NM * NVT;
     static constexpr int NTH = 64 * NWAVES;
-    static constexpr int TPW = 2 * NM / NWAVES;   // state tiles per wave, all in one row block
+    static constexpr int TPW = NM * NVT / NWAVES;   // state tiles per wave, all in one row block
+    static constexpr bool PREFETCH = VT == 64;
+    static constexpr int WG_PER_CU = VT == 64 ? 1 : 2;
+    static_assert(TPW <= NVT, "a wave's tiles must share one row block");
 };
 
-template <int DK>
-__global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(BwdArgs a) {
-    constexpr int NM = DK / 16, NKS = DK / 32;
-    constexpr int NTH = ReverseCfg<DK>::NTH, TPW = ReverseCfg<DK>::TPW;
-    constexpr int VT = 32, PK = DK + 8, PT = kChunk + 8;
+template <int DK, int VT>
+__global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_PER_CU)) void bwd_reverse_kernel(
+    BwdArgs a) {
+    using Cfg = ReverseCfg<DK, VT>;
+    constexpr int NM = DK / 16, NKS = DK / 32, NVT = VT / 16;
+    constexpr int NTH = Cfg::NTH, TPW = Cfg::TPW;
+    constexpr int PK = DK + 8, PT = kChunk + 8;
     constexpr int OPT = VT * kChunk / NTH;          // dO elements per thread per chunk
-    static_assert(OPT == 4 || OPT == 8, "dO staging");
+    static_assert(OPT % 4 == 0, "dO staging");
     constexpr size_t FPC = factor_elems_per_chunk<DK>();
 
     __shared__ __align__(16) __bf16 sD[2][2 * VT * PK];   // dS' as [col][channel] (hi, lo)
@@ -275,19 +314,20 @@ __global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(Bwd
     const size_t tokV = (size_t)H * DV;
     const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
     const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
-    const int m = (wv * TPW) >> 1;                  // row block of this wave's state tiles
+    const int m = (wv * TPW) / NVT;                 // row block of this wave's state tiles
     const __bf16 *fbh = reinterpret_cast<const __bf16 *>(a.factors) + (size_t)bh * NC * FPC;
+    auto col_block = [&](int s) { return (wv * TPW + s) % NVT; };
 
     f32x4 DS[TPW];
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
-        const int n = (wv * TPW + s) & 1;
+        const int n = col_block(s);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             DS[s][i] = a.dS_final ? a.dS_final[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
     }
-    // dO staging: column tid % 32, tokens OPT * (tid / 32) .. + OPT - 1 of the chunk
-    const int ocol = tid & 31, otg = tid >> 5;
+    // dO staging: column tid % VT, tokens OPT * (tid / VT) .. + OPT - 1 of the chunk
+    const int ocol = tid % VT, otg = tid / VT;
     float ox[OPT];
     auto load_dO = [&](int cc) {
 #pragma unroll
@@ -296,24 +336,29 @@ __global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(Bwd
             ox[i] = a.dO[baseV + (size_t)(t < T ? t : T - 1) * tokV + ocol];
         }
     };
+    // factor fragments of row block m: R tiles (m, kb) and Q2^T tiles (m, kb)
+    uint4 fr[NM], fq[4];
+    auto load_factors = [&](int cc, uint4 (&xr)[NM], uint4 (&xq)[4]) {
+        const __bf16 *fc = fbh + (size_t)cc * FPC;
+#pragma unroll
+        for (int kb = 0; kb < NM; ++kb)
+            xr[kb] = *reinterpret_cast<const uint4 *>(fc + (size_t)(m * NM + kb) * kFragTile + 8 * l);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            xq[kb] = *reinterpret_cast<const uint4 *>(fc + (size_t)(NM * NM + m * 4 + kb) * kFragTile + 8 * l);
+    };
     load_dO(NC - 1);
+    if (Cfg::PREFETCH) load_factors(NC - 1, fr, fq);
 
     for (int c = NC - 1; c >= 0; --c) {
         const int buf = c & 1;
-        const __bf16 *fc = fbh + (size_t)c * FPC;
-        uint4 fr[NM], fq[4];
-#pragma unroll
-        for (int kb = 0; kb < NM; ++kb)
-            fr[kb] = *reinterpret_cast<const uint4 *>(fc + (size_t)(m * NM + kb) * kFragTile + 8 * l);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            fq[kb] = *reinterpret_cast<const uint4 *>(fc + (size_t)(NM * NM + m * 4 + kb) * kFragTile + 8 * l);
+        if (!Cfg::PREFETCH) load_factors(c, fr, fq);
 
         // gradient w.r.t. the end state of chunk c
         float *dst = a.dstates + ((size_t)bh * NC + c) * (size_t)DK * DV + j0;
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
-            const int n = (wv * TPW + s) & 1;
+            const int n = col_block(s);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
             const Split4 sp = split4(DS[s]);
@@ -331,11 +376,13 @@ __global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(Bwd
         }
         load_dO(c > 0 ? c - 1 : 0);   // the next chunk's dO is in flight during this chunk's products
         __syncthreads();
+        uint4 nr[NM], nq[4];
+        if (Cfg::PREFETCH) load_factors(c > 0 ? c - 1 : 0, nr, nq);
 
         // dS = R dS' + Q2^T dO
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
-            const int n = (wv * TPW + s) & 1;
+            const int n = col_block(s);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NKS; ++j)
@@ -349,12 +396,18 @@ __global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(Bwd
             }
             DS[s] = acc;
         }
+        if (Cfg::PREFETCH) {
+#pragma unroll
+            for (int kb = 0; kb < NM; ++kb) fr[kb] = nr[kb];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) fq[kb] = nq[kb];
+        }
     }
 
     if (a.dS0) {
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
-            const int n = (wv * TPW + s) & 1;
+            const int n = col_block(s);
 #pragma unroll
             for (int i = 0; i < 4; ++i) a.dS0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
         }
@@ -366,9 +419,14 @@ __global__ __launch_bounds__(ReverseCfg<DK>::NTH, 2) void bwd_reverse_kernel(Bwd
 // ---------------------------------------------------------------------------
 template <int DK, bool BF16>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
-    const int NC = (a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads), 0,
-                       st, a);
+    const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);
+    // one persistent workgroup per CU (the kernel's LDS allows no second one)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const long grid = items < cus ? items : cus;
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -381,19 +439,26 @@ hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, hipStream_t s
     }
 }
 
-template <int DK>
+template <int DK, int VT>
 static hipError_t reverse_t(const BwdArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((bwd_reverse_kernel<DK>), dim3((unsigned)(a.B * a.H * (a.DV / 32))),
-                       dim3(ReverseCfg<DK>::NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_reverse_kernel<DK, VT>), dim3((unsigned)(a.B * a.H * (a.DV / VT))),
+                       dim3(ReverseCfg<DK, VT>::NTH), 0, st, a);
     return hipGetLastError();
+}
+
+// 64-column tiles when they still give every CU a workgroup, else 32
+template <int DK>
+static hipError_t reverse_vt(const BwdArgs &a, hipStream_t st) {
+    if (a.DV >= 64 && (long)a.B * a.H * (a.DV / 64) >= 256) return reverse_t<DK, 64>(a, st);
+    return reverse_t<DK, 32>(a, st);
 }
 
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st) {
     if (a.DV % 32 != 0) return hipErrorInvalidValue;
     switch (dk) {
-        case 32: return reverse_t<32>(a, st);
-        case 64: return reverse_t<64>(a, st);
-        case 128: return reverse_t<128>(a, st);
+        case 32: return reverse_vt<32>(a, st);
+        case 64: return reverse_vt<64>(a, st);
+        case 128: return reverse_vt<128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
