@@ -96,12 +96,44 @@ def cpu_baseline(wl, sample_batches):
                       % (sample_batches, wl.B, wl.T, wl.H, wl.dk, dt)}
 
 
+def decode_bench(dev, B=64, H=16, dk=128, dv=128, iters=100):
+    """The recurrent step (gdn2_step) on a decode batch: one token per (batch, head), the
+    state read and written in place.  Bytes per step are the state (2*dk*dv*4 per head)
+    plus the token vectors."""
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    q = torch.nn.functional.normalize(torch.randn(B, H, dk, generator=g), dim=-1).to(torch.bfloat16).to(dev)
+    k = torch.nn.functional.normalize(torch.randn(B, H, dk, generator=g), dim=-1).to(torch.bfloat16).to(dev)
+    v = torch.randn(B, H, dv, generator=g).to(torch.bfloat16).to(dev)
+    la = torch.nn.functional.logsigmoid(torch.randn(B, H, dk, generator=g) + 3.0).to(dev)
+    b = torch.sigmoid(torch.randn(B, H, dk, generator=g)).to(dev)
+    w = torch.sigmoid(torch.randn(B, H, dv, generator=g)).to(dev)
+    S = (0.02 * torch.randn(B, H, dk, dv, generator=g)).to(dev)
+    for _ in range(5):
+        gdn2.step(q, k, v, la, b, w, S, in_place=True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        gdn2.step(q, k, v, la, b, w, S, in_place=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    nbytes = B * H * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + (2 * dk + dv) * 4 + dv * 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"entry": "gdn2_step", "B": B, "H": H, "dk": dk, "dv": dv, "qkv": "bf16", "us_per_step": round(us, 2),
+            "tokens_per_s": round(B / (us * 1e-6), 1), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-step (decode) measurement")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
@@ -223,6 +255,8 @@ def main():
                       "step_algorithmic_frac": round(step_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
     }
+    if not args.no_decode:
+        out["breakdown"]["decode_step"] = decode_bench(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_batches)
     print(json.dumps(out), flush=True)

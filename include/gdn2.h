@@ -159,6 +159,20 @@ int gdn2_chunk_bwd_grads(const gdn2_shape *shape,
                          float *dq, float *dk, float *dv,
                          float *dlog_alpha, float *db, float *dw, void *stream);
 
+/* ---- recurrent step (decode) ----
+ *
+ * One token per (batch, head), the per-token rule of the blog on Gated DeltaNet-2,
+ * section "Independent control on two axes": decay, read through the erase key
+ * e = b*k, write z - r along the raw key with z = w*v, then the query reads the
+ * updated state.  shape->T must be 1; q, k, log_alpha, b are [B,1,H,dk], v, w and
+ * o are [B,1,H,dv]; S_in and S_out are [B,H,dk,dv] fp32.  S_in == NULL means a zero
+ * state.  S_out may be the same buffer as S_in (in-place update); otherwise the two
+ * must not overlap.  One kernel launch, no workspace; all buffers are device memory
+ * owned by the caller.  Returns GDN2_ERR_INVALID_ARG for T != 1. */
+int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+              const float *log_alpha, const float *b, const float *w,
+              const float *S_in, float *S_out, float *o, void *stream);
+
 /* Static, human-readable description of a gdn2_status value. */
 const char *gdn2_strerror(int status);
 

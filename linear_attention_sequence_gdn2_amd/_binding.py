@@ -23,7 +23,7 @@ STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3:
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
            "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
-           "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads"]
+           "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -72,6 +72,8 @@ def load():
         lib.gdn2_chunk_bwd_reverse.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 15 + [P]
         lib.gdn2_chunk_bwd_grads.restype = ctypes.c_int
+        lib.gdn2_step.argtypes = [SP] + [P] * 9 + [P]
+        lib.gdn2_step.restype = ctypes.c_int
         lib.gdn2_strerror.argtypes = [ctypes.c_int]
         lib.gdn2_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -270,3 +272,32 @@ def bwd_saved(q, k, v, log_alpha, b, w, states, dO, dS_final=None, want_dS0=True
     out = bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates)
     out["dS0"] = dS0
     return out
+
+
+def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
+    """One recurrent step (decode, one kernel): q, k, log_alpha, b [B,H,dk], v, w [B,H,dv]
+    (q/k/v fp32 or bf16, gates fp32), S [B,H,dk,dv] fp32 or None (zeros).
+    Returns (o [B,H,dv] fp32, S_new).  With in_place=True, S is updated in place."""
+    if not q.is_cuda:
+        raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % q.device)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t, shp, dt in (("k", k, (B, H, dk), q.dtype), ("v", v, (B, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (B, H, dk), torch.float32),
+                             ("b", b, (B, H, dk), torch.float32), ("w", w, (B, H, dv), torch.float32)):
+        if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device or not t.is_contiguous():
+            raise ValueError("gdn2: %s must be contiguous %s %s on %s" % (name, shp, dt, q.device))
+    if not q.is_contiguous():
+        raise ValueError("gdn2: tensors must be contiguous")
+    if S is not None and (tuple(S.shape) != (B, H, dk, dv) or S.dtype != torch.float32 or not S.is_contiguous()):
+        raise ValueError("gdn2: S must be contiguous float32 [B,H,dk,dv]")
+    if in_place and S is None:
+        raise ValueError("gdn2: in_place needs a state")
+    lib = load()
+    shape = make_shape(B, 1, H, dk, dv, q.dtype)
+    o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    S_new = S if in_place else (out if out is not None else
+                                torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device))
+    _check(lib.gdn2_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                         _ptr(S), _ptr(S_new), _ptr(o), _stream(q.device)))
+    return o, S_new

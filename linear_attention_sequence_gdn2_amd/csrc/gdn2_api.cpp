@@ -222,4 +222,20 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
                                 dw, stream);
 }
 
+int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void *v, const float *log_alpha,
+              const float *b, const float *w, const float *S_in, float *S_out, float *o, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (shape->T != 1) return GDN2_ERR_INVALID_ARG;
+    if (!q || !k || !v || !log_alpha || !b || !w || !S_out || !o) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, v, log_alpha, b, w, S_in, S_out, o})) return GDN2_ERR_INVALID_ARG;
+    gdn2::StepArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_alpha; a.bg = b; a.wg = w;
+    a.S_in = S_in; a.S_out = S_out; a.o = o;
+    a.BH = shape->B * shape->H; a.dv = shape->dv;
+    return launch_status(gdn2::launch_step(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -19,13 +19,13 @@
 // Kt = k*exp(-G), Kh = k*exp(g_C - G), Z = w*v and the reverse cumulative sum
 // of dG into dlog_alpha.
 //
-// Three launches: the forward state sweep (gdn2_fwd.hip) stores every chunk's
-// start state; bwd_reverse_kernel walks the chunks backwards per (batch, head,
-// value tile), storing each chunk's dS' and finally dS0; bwd_chunk_kernel then
-// treats every (batch, head, chunk) independently and writes all token
-// gradients.  Value columns are independent in S, dS and dS', so value tiles
-// need no exchange; the key-side gradients sum over all value columns inside
-// one bwd_chunk_kernel workgroup.
+// Launches of the backward: the forward state sweep (gdn2_fwd.hip) stores every
+// chunk's start state; the reverse sweep (gdn2_reverse.hip) walks the chunks
+// backwards per (batch, head, value tile) and stores each chunk's dS'; bwd_chunk_kernel
+// (this file) then treats every (batch, head, chunk) independently and writes all token
+// gradients.  Value columns are independent in S, dS and dS', so value tiles need no
+// exchange; the key-side gradients sum over all value columns inside one
+// bwd_chunk_kernel workgroup.
 //
 #include <type_traits>
 
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     constexpr int NKS = DK / 32;                 // 32-channel contraction steps
     constexpr int NMH = DK / 32;                 // 16-channel key tiles per half
     constexpr int NEH = 4 * NMH;                 // key elements per lane
-    constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4, PS = VT + 8;
+    constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4, PS = VT + 4;   // PS: 18-bank rows, conflict-free transposed reads
     constexpr int RK = kChunk * PK;              // one [token][channel] bf16 plane
     constexpr int NSF = (DK * 8 + NTH - 1) / NTH;   // float4 of a state tile per thread
     constexpr bool FAST = BF16;
@@ -64,7 +64,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     constexpr int B_ROWS = 2 * RK * 2, B_ST = 2 * DK * PS * 2, B_VT = 2 * VT * PT * 2, B_PT = 2 * kChunk * PT * 2;
     constexpr int oKt = 0, oEt = oKt + B_ROWS, oLoop = oEt + B_ROWS;
     constexpr int oS1 = oLoop, oD1 = oS1 + B_ST, oO1 = oD1 + B_ST, oXU = oO1 + B_VT, odUX = oXU + B_VT;
-    constexpr int oAT = odUX + B_VT, oTot = oAT + kChunk * PA * 4, oGam = oTot + 4 * DK * 4, oDG = oGam + DK * 4;
+    // After the solve, T is kept as split bf16 [row][col] over A/T and the (by then dead)
+    // decay totals, for the value loop.
+    constexpr int B_TS = 2 * kChunk * PT * 2;
+    constexpr int oAT = odUX + B_VT, oTot = oAT + kChunk * PA * 4, oTs = oAT;
+    constexpr int oGam = (oTot + 4 * DK * 4 > oTs + B_TS) ? oTot + 4 * DK * 4 : oTs + B_TS;
+    constexpr int oDG = oGam + DK * 4;
     constexpr int SMEM = oDG + DK * 4;
     constexpr int oQt = oLoop, odPt = oQt + B_ROWS, odAt = odPt + B_PT;
     constexpr int oScr = odAt + B_PT, oTotA = oScr + 8 * DK * 4, oTotB = oTotA + 4 * DK * 4;
@@ -82,6 +87,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float *sAT = reinterpret_cast<float *>(smem + oAT), *sTot = reinterpret_cast<float *>(smem + oTot);
     float *sGam = reinterpret_cast<float *>(smem + oGam), *sDG = reinterpret_cast<float *>(smem + oDG);
     float *sScr = reinterpret_cast<float *>(smem + oScr);
+    __bf16 *sTs = reinterpret_cast<__bf16 *>(smem + oTs);
 
     const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int n = hf;                            // value column block of this wave's tiles
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     load_tile(0, cur, tid);
 
     // ---- preparation: decay, operand rows, A -> T, P^T rows in registers ----
-    float Gk[NEH], bk[NEH];        // kept for the element-wise chain of the epilogue
+    float Gk[NEH];                 // decay prefix, kept for the element-wise chain of the epilogue
     {
         float qf[NEH], kf[NEH], laf[NEH], bgf[NEH], G[NEH], gC[NEH];
         raw.unpack(qf, kf, laf, bgf);
@@ -154,10 +160,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             for (int e = 0; e < NEH; ++e) sGam[ch(e)] = exp2_fast(gC[e]);
         }
 #pragma unroll
-        for (int e = 0; e < NEH; ++e) {
-            Gk[e] = G[e];
-            bk[e] = bgf[e];
-        }
+        for (int e = 0; e < NEH; ++e) Gk[e] = G[e];
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
             f32x4 et, qt, kt;
@@ -214,6 +217,18 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     }
     __syncthreads();
     solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
+    {
+        // T as split bf16 [row][col], once per chunk: the value loop reads its rows (U = T X)
+        // and, transposed, its columns (dX = T^T dU) without converting again per tile
+        const int row = tid >> 3, c8 = 8 * (tid & 7);
+        const f32x4 t0v = *reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8]);
+        const f32x4 t1v = *reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8 + 4]);
+        __syncthreads();
+        const Split8 ts = split8v(t0v, t1v);
+        *reinterpret_cast<bf16x8 *>(&sTs[row * PT + c8]) = ts.hi;
+        *reinterpret_cast<bf16x8 *>(&sTs[kChunk * PT + row * PT + c8]) = ts.lo;
+    }
+    static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
     float gm[NSF];
 #pragma unroll
     for (int it = 0; it < NSF; ++it) {
@@ -316,18 +331,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         f32x4 Ur = {0.f, 0.f, 0.f, 0.f}, dXr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            if (kk < nkk) {
-                const f32x4 ta = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 32 * kk + 8 * g]);
-                const f32x4 tb = *reinterpret_cast<const f32x4 *>(&sAT[(16 * w + r) * PA + 32 * kk + 8 * g + 4]);
-                Ur = mfma32x3(split8v(ta, tb), frag_8(&XU[(16 * n + r) * PT + 32 * kk + 8 * g],
-                                                     &XU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), Ur);
-            }
+            if (kk < nkk)
+                Ur = mfma32x3(frag_8(&sTs[(16 * w + r) * PT + 32 * kk + 8 * g],
+                                     &sTs[kChunk * PT + (16 * w + r) * PT + 32 * kk + 8 * g]),
+                              frag_8(&XU[(16 * n + r) * PT + 32 * kk + 8 * g],
+                                     &XU[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), Ur);
             if (kk >= kk_lo) {
-                float tv[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) tv[s] = sAT[(32 * kk + 8 * g + s) * PA + 16 * w + r];
-                dXr = mfma32x3(split8(tv), frag_8(&dUX[(16 * n + r) * PT + 32 * kk + 8 * g],
-                                                  &dUX[VT * PT + (16 * n + r) * PT + 32 * kk + 8 * g]), dXr);
+                const __bf16 *dh = &dUX[(16 * n + r) * PT + 32 * kk], *dl = dh + VT * PT;
+                dXr = mfma32x3(frag_tr<PT>(sTs, sTs + kChunk * PT, 32 * kk, 16 * w, r, g),   // T^T rows
+                               frag_2x4(dh + 4 * g, dh + 16 + 4 * g, dl + 4 * g, dl + 16 + 4 * g), dXr);
             }
         }
 #pragma unroll
@@ -378,9 +390,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     }
 
     // ---- epilogue: dgamma, dP/dA products, element-wise chain ----
-    // q and k (packed), b and the decay prefix G stayed in registers through the value
-    // loop.  The lane indices are derived afresh from an opaque copy of the thread
-    // index, so that no address arithmetic of the preparation is kept live across it.
+    // The decay prefix G stayed in registers through the value loop; q, k and b are read
+    // again (their log-decay values are not used, so those loads are dropped).  The lane
+    // indices are derived afresh from an opaque copy of the thread index, so that no
+    // address arithmetic of the preparation is kept live across the value loop.
   {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -415,12 +428,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
-    raw.unpack_qk(qf, kf);
+    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
+    raw.unpack(qf, kf, G, bgf);
 #pragma unroll
-    for (int e = 0; e < NEH; ++e) {
-        G[e] = Gk[e];
-        bgf[e] = bk[e];
-    }
+    for (int e = 0; e < NEH; ++e) G[e] = Gk[e];
     {
         // Qt rows of this half's channels again
 #pragma unroll

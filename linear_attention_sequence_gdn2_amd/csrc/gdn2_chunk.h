@@ -265,6 +265,22 @@ struct KeyRaw4 {
         }
     }
 
+    // q and k only
+    __device__ __forceinline__ void issue_qk(const void *qp, const void *kp, size_t rowoff, int g, bool v) {
+        valid = v;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const size_t off = rowoff + 16 * m + 4 * g;
+            if (BF16) {
+                q[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(qp) + off);
+                k[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(kp) + off);
+            } else {
+                qx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qp) + off);
+                kx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(kp) + off);
+            }
+        }
+    }
+
     // q and k only (zero for a missing token)
     __device__ __forceinline__ void unpack_qk(float (&qf)[4 * NM], float (&kf)[4 * NM]) const {
 #pragma unroll

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             S[s][i] = a.S0 ? a.S0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
     }
     for (int idx = tid; idx < kChunk * PA; idx += kThreads) sAT[idx] = 0.f;
-    auto store_state_lds = [&]() {
+    auto store_state_lds = [&](int w, int r, int g) {
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
             const int id = w * NTS + s, m = id / NVT, n = id % NVT;
@@ -89,10 +89,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             *reinterpret_cast<bf16x4 *>(&sS[VT * PK + (16 * n + r) * PK + 16 * m + 4 * g]) = sp.lo;
         }
     };
-    store_state_lds();
+    store_state_lds(w, r, g);
     __syncthreads();
 
     for (int c = 0; c < NC; ++c) {
+        // lane indices afresh from an opaque copy of the thread index: the address
+        // arithmetic is redone each chunk instead of being held in registers
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+        const int nkk = (w >= 2) ? 2 : 1;
         const int t0 = c * kChunk;
         if (STATES) {
             float *dst = a.states + (((size_t)b * H + h) * NC + c) * (size_t)DK * DV + j0;
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[s][i];
             GDN2_STEP_FENCE();
         }
-        store_state_lds();
+        store_state_lds(w, r, g);
         __syncthreads();
     }
 

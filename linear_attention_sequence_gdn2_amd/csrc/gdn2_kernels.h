@@ -32,6 +32,26 @@ struct BwdArgs {
     int B, T, H, DV;
 };
 
+// Arguments of the recurrent step (one token per (batch, head)); token tensors [BH, D].
+struct StepArgs {
+    const void *q, *k, *v;
+    const float *la, *bg, *wg;
+    const float *S_in;              // may be null (zeros)
+    float *S_out;                   // may equal S_in
+    float *o;
+    int BH, dv;
+};
+hipError_t launch_step(const StepArgs &a, int dk, bool bf16, hipStream_t st);
+
+// Compute units of the current device (256 if the runtime cannot tell).
+inline int cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return 256;
+    return cus;
+}
+
 // Value-tile width the forward sweep uses for this shape (16, 32 or 64).
 int fwd_value_tile(int B, int H, int dk, int dv);
 

@@ -421,11 +421,7 @@ template <int DK, bool BF16>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
     const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);
     // one persistent workgroup per CU (the kernel's LDS allows no second one)
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
-    const long grid = items < cus ? items : cus;
+    const long grid = items < cu_count() ? items : cu_count();
     hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
     return hipGetLastError();
 }

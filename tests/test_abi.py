@@ -110,6 +110,18 @@ def test_staged_entry_points_check_arguments():
     assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, f, f, f, f, None, None) == INVALID
 
 
+def test_step_checks_arguments():
+    lib = gdn2.load()
+    f = P(0x10000)
+    s = _shape(T=2)
+    assert lib.gdn2_step(ctypes.byref(s), f, f, f, f, f, f, None, f, f, None) == INVALID   # T must be 1
+    s = _shape(T=1)
+    assert lib.gdn2_step(ctypes.byref(s), f, f, f, f, f, f, None, None, f, None) == INVALID
+    assert lib.gdn2_step(ctypes.byref(s), f, f, f, f, f, P(0x10004), None, f, f, None) == INVALID
+    s = _shape(T=1, dk=96)
+    assert lib.gdn2_step(ctypes.byref(s), f, f, f, f, f, f, None, f, f, None) == UNSUPPORTED
+
+
 def test_strerror_covers_every_status():
     lib = gdn2.load()
     msgs = {lib.gdn2_strerror(c).decode() for c in range(5)}
