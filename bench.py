@@ -43,6 +43,9 @@ BWD_BYTES_PER_TOKHEAD = 5888
 #   reverse sweep       : factors 1536 + dO 512 + dstates 1024                  -> 3072
 #   chunk gradients     : q,k,v 768 + gates 1536 + dO 512 + states, dstates 2048
 #                         + dq,dk,dv,dlog_alpha,db,dw 3072                      -> 7936
+# with the gates given as bf16 logits each pass reads 1536 -> 768 gate bytes per token-head
+GATE_BYTES_SAVED_PER_TOKHEAD = 768
+LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
 FWD_STATES_BYTES_PER_TOKHEAD = 3840
 BWD_FACTORS_BYTES_PER_TOKHEAD = 3072
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
@@ -134,6 +137,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-step (decode) measurement")
+    ap.add_argument("--no-logit-gates", action="store_true", help="skip the step with bf16 logit gates")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
@@ -164,51 +168,56 @@ def main():
                           "launches": 3}))
         return
     wl = WORKLOADS[WORKLOAD]
-    x = make_workload(wl, grads=True)
-    d = {k: (v.to(dev) if v is not None and hasattr(v, "to") else None)
-         for k, v in x.items() if k in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final")}
-    fargs = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
     stream = torch.cuda.current_stream(dev)
-    sshape = gdn2.states_shape(wl.B, wl.T, wl.H, wl.dk, wl.dv)
-    states = torch.empty(sshape, dtype=torch.float32, device=dev)
-    dstates = torch.empty(sshape, dtype=torch.float32, device=dev)
-
-    factors = torch.empty(gdn2.factors_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv), dtype=torch.uint8, device=dev)
-
-    # One training step = four kernel launches:
-    #   fwd_kernel          (gdn2_chunk_fwd_states: o, S_final and the chunk-start states)
-    #   bwd_factors_kernel  (gdn2_chunk_bwd_factors: per-chunk adjoint factors R, Q2)
-    #   bwd_reverse_kernel  (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
-    #   bwd_chunk_kernel    (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        o, sf, _ = gdn2.fwd_states(*fargs, states=states)
-        if ev is not None:
-            ev[1].record(stream)
-        gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"], factors=factors)
-        if ev is not None:
-            ev[2].record(stream)
-        _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
-        if ev is not None:
-            ev[3].record(stream)
-        g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates)
-        if ev is not None:
-            ev[4].record(stream)
-        return o, sf, g, dS0
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     nk = 4
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(nk)]
-    step_ms = sum(e[0].elapsed_time(e[nk]) for e in evs) / args.steps
+
+    def timed_steps(x, steps, warmup):
+        """Run `warmup` then `steps` training steps on the inputs x; returns (wall seconds,
+        per-kernel event ms averaged over the steps, whole-step event ms)."""
+        d = {k: (v.to(dev) if v is not None and hasattr(v, "to") else None)
+             for k, v in x.items() if k in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final")}
+        fargs = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+        sshape = gdn2.states_shape(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+        states = torch.empty(sshape, dtype=torch.float32, device=dev)
+        dstates = torch.empty(sshape, dtype=torch.float32, device=dev)
+        factors = torch.empty(gdn2.factors_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv), dtype=torch.uint8, device=dev)
+
+        # One training step = four kernel launches:
+        #   fwd_kernel          (gdn2_chunk_fwd_states: o, S_final and the chunk-start states)
+        #   bwd_factors_kernel  (gdn2_chunk_bwd_factors: per-chunk adjoint factors R, Q2)
+        #   bwd_reverse_kernel  (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
+        #   bwd_chunk_kernel    (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            o, sf, _ = gdn2.fwd_states(*fargs, states=states)
+            if ev is not None:
+                ev[1].record(stream)
+            gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"], factors=factors)
+            if ev is not None:
+                ev[2].record(stream)
+            _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
+            if ev is not None:
+                ev[3].record(stream)
+            g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates)
+            if ev is not None:
+                ev[4].record(stream)
+            return o, sf, g, dS0
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(nk)]
+        step_ms = sum(e[0].elapsed_time(e[nk]) for e in evs) / steps
+        return wall, k_ms, step_ms
+
+    wall, k_ms, step_ms = timed_steps(make_workload(wl, grads=True), args.steps, args.warmup)
     tokens = wl.B * wl.T
     tokheads = wl.B * wl.T * wl.H
     state_bytes = wl.B * wl.H * wl.dk * wl.dv * 4
@@ -255,6 +264,17 @@ def main():
                       "step_algorithmic_frac": round(step_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
     }
+    if not args.no_logit_gates:
+        # the same step with the gates given as bf16 logits (activated in the kernels)
+        lwl = WORKLOADS[LOGIT_WORKLOAD]
+        lwall, lk_ms, lstep_ms = timed_steps(make_workload(lwl), args.steps, args.warmup)
+        lalg = (FWD_BYTES_PER_TOKHEAD + BWD_BYTES_PER_TOKHEAD - 2 * GATE_BYTES_SAVED_PER_TOKHEAD) * tokheads
+        out["breakdown"]["logit_gates_step"] = {
+            "workload": LOGIT_WORKLOAD, "ms_per_step": round(lwall / args.steps * 1e3, 4),
+            "tokens_per_s": round(tokens / (lwall / args.steps), 1),
+            "kernel_ms": {kn[0]: round(ms, 4) for kn, ms in zip(kernels, lk_ms)},
+            "step_event_ms": round(lstep_ms, 4),
+            "step_algorithmic_frac": round(lalg / (lstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_decode:
         out["breakdown"]["decode_step"] = decode_bench(dev)
     if not args.no_cpu_baseline:

@@ -27,11 +27,13 @@
  * - Token tensors are [B, T, H, D]: q, k, log_alpha, b and the key-side
  *   gradients use D = dk; v, w, o and the value-side gradients use D = dv.
  *   States are [B, H, dk, dv] fp32 (key channel = row).
- * - q, k, v have dtype shape->qkv_dtype (fp32 or bf16).  log_alpha, b, w, S0,
- *   dO, dS_final and every output are fp32.
- * - log_alpha is the natural log of the per-channel decay (alpha = exp).  b and
- *   w are gate VALUES (after any sigmoid), not logits, and are not clamped.
- *   Gradients are taken with respect to exactly these inputs.  q is not scaled.
+ * - q, k, v have dtype shape->qkv_dtype (fp32 or bf16).  S0, dO, dS_final and
+ *   every output are fp32.  log_alpha, b, w are fp32 values or bf16 logits as
+ *   shape->gate_dtype says (see gdn2_gate_dtype).
+ * - With fp32 gates, log_alpha is the natural log of the per-channel decay
+ *   (alpha = exp), and b and w are gate VALUES (after any sigmoid), not clamped.
+ *   Gradients are taken with respect to exactly the inputs given (values or
+ *   logits).  q is not scaled.
  * - Any T >= 1 is accepted; a ragged tail chunk is padded internally with
  *   identity tokens (k = 0, log_alpha = 0) that leave the state unchanged.
  * - Supported sizes: B, H >= 1, T >= 1, chunk == 64, dk and dv in {32, 64, 128},
@@ -64,11 +66,21 @@ typedef enum {
 
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
 
+/* How the gates log_alpha, b and w are given.
+ *   GDN2_GATES_F32: fp32 values (log_alpha is the natural-log decay, b and w the gate values).
+ *   GDN2_GATES_BF16_LOGITS: bf16 pre-activation logits x_a, x_b, x_w; the kernels form
+ *     b = sigmoid(x_b), w = sigmoid(x_w) and log_alpha = log(sigmoid(x_a)) in fp32 (the gates
+ *     are sigmoid outputs of linear projections: blog on Gated DeltaNet-2, section
+ *     "Independent control on two axes"), and the gradients dlog_alpha, db, dw are taken
+ *     w.r.t. the logits.  Requires qkv_dtype == GDN2_BF16.  Halves the gate bytes. */
+typedef enum { GDN2_GATES_F32 = 0, GDN2_GATES_BF16_LOGITS = 1 } gdn2_gate_dtype;
+
 typedef struct {
     int B, T, H;      /* batch, tokens, heads */
     int dk, dv;       /* key and value head dimensions */
     int chunk;        /* must be 64 */
     int qkv_dtype;    /* a gdn2_dtype: dtype of q, k and v */
+    int gate_dtype;   /* a gdn2_gate_dtype: how log_alpha, b and w are given */
 } gdn2_shape;
 
 /* Bytes of device workspace gdn2_chunk_fwd needs (0 for every supported shape);
@@ -80,7 +92,7 @@ size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);
  * workspace may be NULL when gdn2_chunk_fwd_workspace_size() is 0. */
 int gdn2_chunk_fwd(const gdn2_shape *shape,
                    const void *q, const void *k, const void *v,
-                   const float *log_alpha, const float *b, const float *w,
+                   const void *log_alpha, const void *b, const void *w,
                    const float *S0,
                    float *o, float *S_final,
                    void *workspace, size_t workspace_bytes, void *stream);
@@ -97,7 +109,7 @@ size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape);
  * gdn2_chunk_fwd call is needed.  The workspace (see above) is overwritten. */
 int gdn2_chunk_bwd(const gdn2_shape *shape,
                    const void *q, const void *k, const void *v,
-                   const float *log_alpha, const float *b, const float *w,
+                   const void *log_alpha, const void *b, const void *w,
                    const float *S0,
                    const float *dO, const float *dS_final,
                    float *dq, float *dk, float *dv,
@@ -121,12 +133,12 @@ size_t gdn2_chunk_states_bytes(const gdn2_shape *shape);
 /* Forward pass as gdn2_chunk_fwd, additionally writing states (required). */
 int gdn2_chunk_fwd_states(const gdn2_shape *shape,
                           const void *q, const void *k, const void *v,
-                          const float *log_alpha, const float *b, const float *w,
+                          const void *log_alpha, const void *b, const void *w,
                           const float *S0, float *o, float *S_final, float *states, void *stream);
 
 /* State sweep only: writes states (no output o).  q is not read. */
 int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v,
-                      const float *log_alpha, const float *b, const float *w,
+                      const void *log_alpha, const void *b, const void *w,
                       const float *S0, float *states, void *stream);
 
 /* Bytes of the per-chunk adjoint factor buffer, B*H*ceil(T/64)*(dk*dk + 64*dk)*4;
@@ -142,7 +154,7 @@ size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
  * (gdn2_chunk_factors_bytes() bytes, device memory owned by the caller, opaque
  * layout of split-bf16 MFMA tiles, read only by gdn2_chunk_bwd_reverse). */
 int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k,
-                           const float *log_alpha, const float *b, void *factors, void *stream);
+                           const void *log_alpha, const void *b, void *factors, void *stream);
 
 /* Reverse sweep of the backward from the factors: writes dstates (required) and
  * dS0 (optional), reading dO and dS_final (NULL = zeros). */
@@ -154,7 +166,7 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors,
  * dv, dw [B,T,H,dv]. */
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape,
                          const void *q, const void *k, const void *v,
-                         const float *log_alpha, const float *b, const float *w,
+                         const void *log_alpha, const void *b, const void *w,
                          const float *dO, const float *states, const float *dstates,
                          float *dq, float *dk, float *dv,
                          float *dlog_alpha, float *db, float *dw, void *stream);
@@ -170,7 +182,7 @@ int gdn2_chunk_bwd_grads(const gdn2_shape *shape,
  * must not overlap.  One kernel launch, no workspace; all buffers are device memory
  * owned by the caller.  Returns GDN2_ERR_INVALID_ARG for T != 1. */
 int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-              const float *log_alpha, const float *b, const float *w,
+              const void *log_alpha, const void *b, const void *w,
               const float *S_in, float *S_out, float *o, void *stream);
 
 /* Static, human-readable description of a gdn2_status value. */

@@ -1,5 +1,9 @@
 """ctypes binding of libgdn2.so (the C ABI in include/gdn2.h).
 
+Gates (log_alpha, b, w) are fp32 values, or -- as bfloat16 tensors -- pre-activation
+logits (log_alpha = log sigmoid, b, w = sigmoid, formed in the kernels; gradients are
+then w.r.t. the logits).
+
 Argument marshalling only: checks dtypes, devices and contiguity, allocates
 the outputs and the workspace with torch on the inputs' device, and passes raw
 device pointers plus the current HIP stream.  Every step of the operator runs
@@ -18,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn2.so")
 
 GDN2_F32 = 0
 GDN2_BF16 = 1
+GDN2_GATES_F32 = 0
+GDN2_GATES_BF16_LOGITS = 1
 STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3: "GDN2_ERR_WORKSPACE",
           4: "GDN2_ERR_HIP"}
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
@@ -28,7 +34,8 @@ EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
 
 class Gdn2Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
-                ("dv", ctypes.c_int), ("chunk", ctypes.c_int), ("qkv_dtype", ctypes.c_int)]
+                ("dv", ctypes.c_int), ("chunk", ctypes.c_int), ("qkv_dtype", ctypes.c_int),
+                ("gate_dtype", ctypes.c_int)]
 
 
 class Gdn2Error(RuntimeError):
@@ -93,8 +100,20 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def make_shape(B, T, H, dk, dv, qkv_dtype):
-    return Gdn2Shape(B, T, H, dk, dv, 64, GDN2_BF16 if qkv_dtype == torch.bfloat16 else GDN2_F32)
+def make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32):
+    """Gates given as bf16 tensors are pre-activation logits (gdn2_gate_dtype)."""
+    return Gdn2Shape(B, T, H, dk, dv, 64, GDN2_BF16 if qkv_dtype == torch.bfloat16 else GDN2_F32,
+                     GDN2_GATES_BF16_LOGITS if gate_dtype == torch.bfloat16 else GDN2_GATES_F32)
+
+
+def _gate_dtype(q, *gates):
+    """fp32 gate values, or bf16 gate logits (all three alike; only with bf16 q/k/v)."""
+    gd = gates[0].dtype
+    if gd not in (torch.float32, torch.bfloat16) or any(g.dtype != gd for g in gates):
+        raise TypeError("gdn2: the gates must all be float32 values or all bfloat16 logits")
+    if gd == torch.bfloat16 and q.dtype != torch.bfloat16:
+        raise TypeError("gdn2: bfloat16 gate logits need bfloat16 q/k/v")
+    return gd
 
 
 def _validate(q, k, v, log_alpha, b, w, extra=()):
@@ -104,9 +123,10 @@ def _validate(q, k, v, log_alpha, b, w, extra=()):
     dv = v.shape[-1]
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q/k/v must be float32 or bfloat16")
+    gd = _gate_dtype(q, log_alpha, b, w)
     for name, t, shp, dt in (("k", k, (B, T, H, dk), q.dtype), ("v", v, (B, T, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
-                             ("b", b, (B, T, H, dk), torch.float32), ("w", w, (B, T, H, dv), torch.float32)):
+                             ("log_alpha", log_alpha, (B, T, H, dk), gd),
+                             ("b", b, (B, T, H, dk), gd), ("w", w, (B, T, H, dv), gd)):
         if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device:
             raise ValueError("gdn2: %s has shape %s dtype %s device %s, expected %s %s %s"
                              % (name, tuple(t.shape), t.dtype, t.device, shp, dt, q.device))
@@ -122,7 +142,7 @@ def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
     if S0 is not None and (tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32):
         raise ValueError("gdn2: S0 must be float32 [B,H,dk,dv]")
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
     ws_bytes = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(shape))
@@ -134,8 +154,8 @@ def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
     return o, sf
 
 
-def bwd_workspace_bytes(B, T, H, dk, dv, qkv_dtype):
-    shape = make_shape(B, T, H, dk, dv, qkv_dtype)
+def bwd_workspace_bytes(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32):
+    shape = make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype)
     return load().gdn2_chunk_bwd_workspace_size(ctypes.byref(shape))
 
 
@@ -149,7 +169,7 @@ def bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, want_dS0=True, workspac
         if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
             raise ValueError("gdn2: %s must be float32 [B,H,dk,dv]" % name)
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
     dev = q.device
     out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
     out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
@@ -174,7 +194,7 @@ def fwd_states(q, k, v, log_alpha, b, w, S0=None, want_state=True, states=None):
     (one kernel): (o, S_final, states)."""
     B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0,))
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
     if states is None:
@@ -188,7 +208,7 @@ def chunk_states(k, v, log_alpha, b, w, S0=None, q_dtype=None, states=None):
     """State sweep only (one kernel): chunk-start states [B,H,ceil(T/64),dk,dv]."""
     B, T, H, dk, dv = _validate(k, k, v, log_alpha, b, w, (S0,))
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, k.dtype)
+    shape = make_shape(B, T, H, dk, dv, k.dtype, log_alpha.dtype)
     if states is None:
         states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=k.device)
     _check(lib.gdn2_chunk_states(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
@@ -209,7 +229,8 @@ def bwd_factors(q, k, log_alpha, b, factors=None):
     """Per-chunk adjoint factors of the reverse sweep (one kernel): a uint8 device
     tensor of factors_bytes() bytes, read only by bwd_reverse."""
     B, T, H, dk = q.shape
-    for name, t, dt in (("k", k, q.dtype), ("log_alpha", log_alpha, torch.float32), ("b", b, torch.float32)):
+    gd = _gate_dtype(q, log_alpha, b)
+    for name, t, dt in (("k", k, q.dtype), ("log_alpha", log_alpha, gd), ("b", b, gd)):
         if tuple(t.shape) != (B, T, H, dk) or t.dtype != dt or t.device != q.device:
             raise ValueError("gdn2: %s must be %s %s on %s" % (name, (B, T, H, dk), dt, q.device))
     for t in (q, k, log_alpha, b):
@@ -218,7 +239,7 @@ def bwd_factors(q, k, log_alpha, b, factors=None):
     if not q.is_cuda:
         raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % q.device)
     lib = load()
-    shape = make_shape(B, T, H, dk, dk, q.dtype)
+    shape = make_shape(B, T, H, dk, dk, q.dtype, gd)
     need = factors_bytes(B, T, H, dk)
     if factors is None:
         factors = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -253,7 +274,7 @@ def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates):
     """Token gradients from chunk states and end-state gradients (one kernel)."""
     B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (dO, states, dstates))
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
     dev = q.device
     out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
     out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
@@ -276,15 +297,17 @@ def bwd_saved(q, k, v, log_alpha, b, w, states, dO, dS_final=None, want_dS0=True
 
 def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
     """One recurrent step (decode, one kernel): q, k, log_alpha, b [B,H,dk], v, w [B,H,dv]
-    (q/k/v fp32 or bf16, gates fp32), S [B,H,dk,dv] fp32 or None (zeros).
+    (q/k/v fp32 or bf16; gates fp32 values, or bf16 logits with bf16 q/k/v),
+    S [B,H,dk,dv] fp32 or None (zeros).
     Returns (o [B,H,dv] fp32, S_new).  With in_place=True, S is updated in place."""
     if not q.is_cuda:
         raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % q.device)
     B, H, dk = q.shape
     dv = v.shape[-1]
+    gd = _gate_dtype(q, log_alpha, b, w)
     for name, t, shp, dt in (("k", k, (B, H, dk), q.dtype), ("v", v, (B, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (B, H, dk), torch.float32),
-                             ("b", b, (B, H, dk), torch.float32), ("w", w, (B, H, dv), torch.float32)):
+                             ("log_alpha", log_alpha, (B, H, dk), gd),
+                             ("b", b, (B, H, dk), gd), ("w", w, (B, H, dv), gd)):
         if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device or not t.is_contiguous():
             raise ValueError("gdn2: %s must be contiguous %s %s on %s" % (name, shp, dt, q.device))
     if not q.is_contiguous():
@@ -294,7 +317,7 @@ def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
     if in_place and S is None:
         raise ValueError("gdn2: in_place needs a state")
     lib = load()
-    shape = make_shape(B, 1, H, dk, dv, q.dtype)
+    shape = make_shape(B, 1, H, dk, dv, q.dtype, gd)
     o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     S_new = S if in_place else (out if out is not None else
                                 torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device))

@@ -14,12 +14,16 @@ bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool gate_logits(const gdn2_shape *s) { return s->gate_dtype == GDN2_GATES_BF16_LOGITS; }
+
 int check_shape(const gdn2_shape *s) {
     if (!s) return GDN2_ERR_INVALID_ARG;
     if (s->B < 1 || s->T < 1 || s->H < 1 || s->dk < 1 || s->dv < 1) return GDN2_ERR_INVALID_ARG;
     if (s->chunk != 64) return GDN2_ERR_UNSUPPORTED;
     if (!dim_ok(s->dk) || !dim_ok(s->dv)) return GDN2_ERR_UNSUPPORTED;
     if (s->qkv_dtype != GDN2_F32 && s->qkv_dtype != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (s->gate_dtype != GDN2_GATES_F32 && s->gate_dtype != GDN2_GATES_BF16_LOGITS) return GDN2_ERR_UNSUPPORTED;
+    if (s->gate_dtype == GDN2_GATES_BF16_LOGITS && s->qkv_dtype != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
     const int dmax = s->dk > s->dv ? s->dk : s->dv;
     const unsigned long long n = (unsigned long long)s->B * s->T * s->H * dmax;
     if (n >= (1ull << 31)) return GDN2_ERR_UNSUPPORTED;
@@ -51,7 +55,7 @@ size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape) {
 }
 
 int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                   const float *log_alpha, const float *b, const float *w, const float *S0, float *o,
+                   const void *log_alpha, const void *b, const void *w, const float *S0, float *o,
                    float *S_final, void *workspace, size_t workspace_bytes, void *stream) {
     (void)workspace;
     (void)workspace_bytes;
@@ -69,7 +73,7 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
     a.B = shape->B; a.T = shape->T; a.H = shape->H; a.dv = shape->dv;
     const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
     a.nvt = shape->dv / vt;
-    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gdn2::kFwdOut,
+    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape), gdn2::kFwdOut,
                                           reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
@@ -95,7 +99,7 @@ size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape) {
 namespace {
 
 gdn2::FwdArgs fwd_args(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                       const float *log_alpha, const float *b, const float *w, const float *S0, float *o,
+                       const void *log_alpha, const void *b, const void *w, const float *S0, float *o,
                        float *S_final, float *states, int *vt_out) {
     gdn2::FwdArgs f{};
     f.q = q; f.k = k; f.v = v;
@@ -127,7 +131,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HI
 extern "C" {
 
 int gdn2_chunk_fwd_states(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                          const float *log_alpha, const float *b, const float *w, const float *S0, float *o,
+                          const void *log_alpha, const void *b, const void *w, const float *S0, float *o,
                           float *S_final, float *states, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
@@ -135,31 +139,33 @@ int gdn2_chunk_fwd_states(const gdn2_shape *shape, const void *q, const void *k,
     if (!all_aligned({q, k, v, log_alpha, b, w, S0, o, S_final, states})) return GDN2_ERR_INVALID_ARG;
     int vt;
     const gdn2::FwdArgs f = fwd_args(shape, q, k, v, log_alpha, b, w, S0, o, S_final, states, &vt);
-    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gdn2::kFwdOutStates,
+    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
+                                          gdn2::kFwdOutStates,
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
-int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v, const float *log_alpha,
-                      const float *b, const float *w, const float *S0, float *states, void *stream) {
+int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v, const void *log_alpha,
+                      const void *b, const void *w, const float *S0, float *states, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!k || !v || !log_alpha || !b || !w || !states) return GDN2_ERR_INVALID_ARG;
     if (!all_aligned({k, v, log_alpha, b, w, S0, states})) return GDN2_ERR_INVALID_ARG;
     int vt;
     const gdn2::FwdArgs f = fwd_args(shape, nullptr, k, v, log_alpha, b, w, S0, nullptr, nullptr, states, &vt);
-    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gdn2::kFwdStates,
+    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
+                                          gdn2::kFwdStates,
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
-int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k, const float *log_alpha,
-                           const float *b, void *factors, void *stream) {
+int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k, const void *log_alpha,
+                           const void *b, void *factors, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!q || !k || !log_alpha || !b || !factors) return GDN2_ERR_INVALID_ARG;
     if (!all_aligned({q, k, log_alpha, b, factors})) return GDN2_ERR_INVALID_ARG;
     gdn2::BwdArgs a = bwd_args(shape);
     a.q = q; a.k = k; a.la = log_alpha; a.bg = b; a.factors = factors;
-    return launch_status(gdn2::launch_bwd_factors(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
+    return launch_status(gdn2::launch_bwd_factors(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -176,7 +182,7 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const f
 }
 
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                         const float *log_alpha, const float *b, const float *w, const float *dO,
+                         const void *log_alpha, const void *b, const void *w, const float *dO,
                          const float *states, const float *dstates, float *dq, float *dk, float *dv,
                          float *dlog_alpha, float *db, float *dw, void *stream) {
     const int st = check_shape(shape);
@@ -191,12 +197,12 @@ int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, 
     a.la = log_alpha; a.bg = b; a.wg = w;
     a.dO = dO; a.states = states; a.dstates = const_cast<float *>(dstates);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
-    return launch_status(gdn2::launch_bwd_chunk(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
+    return launch_status(gdn2::launch_bwd_chunk(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                   const float *log_alpha, const float *b, const float *w, const float *S0,
+                   const void *log_alpha, const void *b, const void *w, const float *S0,
                    const float *dO, const float *dS_final, float *dq, float *dk, float *dv,
                    float *dlog_alpha, float *db, float *dw, float *dS0, void *workspace,
                    size_t workspace_bytes, void *stream) {
@@ -222,8 +228,8 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
                                 dw, stream);
 }
 
-int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void *v, const float *log_alpha,
-              const float *b, const float *w, const float *S_in, float *S_out, float *o, void *stream) {
+int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void *v, const void *log_alpha,
+              const void *b, const void *w, const float *S_in, float *S_out, float *o, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (shape->T != 1) return GDN2_ERR_INVALID_ARG;
@@ -234,7 +240,7 @@ int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void 
     a.la = log_alpha; a.bg = b; a.wg = w;
     a.S_in = S_in; a.S_out = S_out; a.o = o;
     a.BH = shape->B * shape->H; a.dv = shape->dv;
-    return launch_status(gdn2::launch_step(a, shape->dk, shape->qkv_dtype == GDN2_BF16,
+    return launch_status(gdn2::launch_step(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -45,7 +45,7 @@ namespace gdn2 {
 // chunk, so one workgroup takes most of a CU's LDS and the two halves give every SIMD
 // two waves.
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool GL>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int VT = 32;                       // value columns per tile
@@ -137,12 +137,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             const int t = t0 + 16 * w + 4 * g + i;
             const size_t off = baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + 16 * n + r;
             x.v[i] = load1<BF16>(a.v, off, true);
-            x.wg[i] = a.wg[off];
+            x.wg[i] = load_gate1<GL>(a.wg, off);   // as stored (activated at use)
         }
     };
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
-    KeyRaw4<DK / 2, BF16> raw;
+    KeyRaw4<DK / 2, BF16, GL> raw;
     raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
     Tile cur;
     load_tile(0, cur, tid);
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         for (int i = 0; i < 4; ++i) {
             const bool ok = t0 + 16 * w + 4 * g + i < T;
             vD[i] = ok ? cur.v[i] : 0.f;
-            wD[i] = ok ? cur.wg[i] : 0.f;
+            wD[i] = ok ? gate_act<GL>(cur.wg[i]) : 0.f;
         }
         __syncthreads();
         // next tile's loads are in flight during this tile's products
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             if (t < T) {
                 const size_t off = baseV0 + (size_t)t * tokV + j0 + 16 * n + r;
                 a.dv[off] = dXr[i] * wD[i];
-                a.dw[off] = dXr[i] * vD[i];
+                a.dw[off] = dXr[i] * vD[i] * gate_dact<GL>(wD[i]);
             }
         }
         __syncthreads();
@@ -430,6 +430,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
     raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
     raw.unpack(qf, kf, G, bgf);
+    float dact[NEH];               // d log_alpha / d stored decay input
+    raw.decay_dact_all(dact);
 #pragma unroll
     for (int e = 0; e < NEH; ++e) G[e] = Gk[e];
     {
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 const float dHg = aH[mm][i];      // gamma * dKh, and dKh * Kh = dHg * Kt
                 vq[i] = dQt * eg;
                 const float dE = dEt * eg;
-                vb[i] = dE * kf[e];
+                vb[i] = dE * kf[e] * gate_dact<GL>(bgf[e]);
                 vk4[i] = (dKt + dHg) * eng + dE * bgf[e];
                 xg[e] = dQt * Qt + dEt * Et - (dKt + dHg) * Kt;
                 yh[e] = dHg * Kt;
@@ -518,7 +520,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * mm + i;
-                vl[i] = (xtot[e] - xin[e] + xg[e]) + ytot[e] + sDG[ch(e)] * sGam[ch(e)];
+                vl[i] = ((xtot[e] - xin[e] + xg[e]) + ytot[e] + sDG[ch(e)] * sGam[ch(e)]) * dact[e];
             }
             *reinterpret_cast<f32x4 *>(a.dla + rowK + chh + 16 * mm + 4 * g) = vl;
         }
@@ -529,22 +531,28 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool GL>
 static hipError_t chunk_t(const BwdArgs &a, hipStream_t st) {
     const int NC = (a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads), 0, st,
-                       a);
+    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads), 0,
+                       st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, hipStream_t st) {
-    if (a.DV % 32 != 0) return hipErrorInvalidValue;
+template <bool BF16, bool GL>
+static hipError_t chunk_dk(const BwdArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return bf16 ? chunk_t<32, true>(a, st) : chunk_t<32, false>(a, st);
-        case 64: return bf16 ? chunk_t<64, true>(a, st) : chunk_t<64, false>(a, st);
-        case 128: return bf16 ? chunk_t<128, true>(a, st) : chunk_t<128, false>(a, st);
+        case 32: return chunk_t<32, BF16, GL>(a, st);
+        case 64: return chunk_t<64, BF16, GL>(a, st);
+        case 128: return chunk_t<128, BF16, GL>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st) {
+    if (a.DV % 32 != 0) return hipErrorInvalidValue;
+    if (gl) return bf16 ? chunk_dk<true, true>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? chunk_dk<true, false>(a, dk, st) : chunk_dk<false, false>(a, dk, st);
 }
 
 }  // namespace gdn2

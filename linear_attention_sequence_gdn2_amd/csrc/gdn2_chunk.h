@@ -237,17 +237,18 @@ __device__ __forceinline__ Split8 split8v(const f32x4 &a, const f32x4 &b) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int ch4(int e, int g) { return 16 * (e >> 2) + 4 * g + (e & 3); }
 
-// key-side inputs of one token for the 4-group layout
-template <int DK, bool BF16>
+// key-side inputs of one token for the 4-group layout; GL: log_alpha and b are bf16 logits
+template <int DK, bool BF16, bool GL = false>
 struct KeyRaw4 {
     static constexpr int NM = DK / 16;
     uint2 q[NM], k[NM];
     float4 qx[NM], kx[NM];
-    float4 la[NM], bg[NM];
+    float4 la[NM], bg[NM];          // fp32 gate values
+    uint2 la16[NM], bg16[NM];       // bf16 gate logits
     bool valid;
 
-    // q, k: qkv dtype; la, bg: fp32; rowoff: element offset of channel 0 of the token row
-    __device__ __forceinline__ void issue(const void *qp, const void *kp, const float *lap, const float *bgp,
+    // q, k: qkv dtype; rowoff: element offset of channel 0 of the token row
+    __device__ __forceinline__ void issue(const void *qp, const void *kp, const void *lap, const void *bgp,
                                           size_t rowoff, int g, bool v) {
         valid = v;
 #pragma unroll
@@ -260,25 +261,21 @@ struct KeyRaw4 {
                 qx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qp) + off);
                 kx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(kp) + off);
             }
-            la[m] = *reinterpret_cast<const float4 *>(lap + off);
-            bg[m] = *reinterpret_cast<const float4 *>(bgp + off);
+            if (GL) {
+                la16[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(lap) + off);
+                bg16[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(bgp) + off);
+            } else {
+                la[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(lap) + off);
+                bg[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(bgp) + off);
+            }
         }
     }
 
-    // q and k only
-    __device__ __forceinline__ void issue_qk(const void *qp, const void *kp, size_t rowoff, int g, bool v) {
-        valid = v;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const size_t off = rowoff + 16 * m + 4 * g;
-            if (BF16) {
-                q[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(qp) + off);
-                k[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(kp) + off);
-            } else {
-                qx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qp) + off);
-                kx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(kp) + off);
-            }
-        }
+    static __device__ __forceinline__ void bf16x4_to(const uint2 &u, float *o) {
+        o[0] = __builtin_bit_cast(float, u.x << 16);
+        o[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+        o[2] = __builtin_bit_cast(float, u.y << 16);
+        o[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
     }
 
     // q and k only (zero for a missing token)
@@ -286,14 +283,8 @@ struct KeyRaw4 {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             if (BF16) {
-                qf[4 * m + 0] = __builtin_bit_cast(float, q[m].x << 16);
-                qf[4 * m + 1] = __builtin_bit_cast(float, q[m].x & 0xffff0000u);
-                qf[4 * m + 2] = __builtin_bit_cast(float, q[m].y << 16);
-                qf[4 * m + 3] = __builtin_bit_cast(float, q[m].y & 0xffff0000u);
-                kf[4 * m + 0] = __builtin_bit_cast(float, k[m].x << 16);
-                kf[4 * m + 1] = __builtin_bit_cast(float, k[m].x & 0xffff0000u);
-                kf[4 * m + 2] = __builtin_bit_cast(float, k[m].y << 16);
-                kf[4 * m + 3] = __builtin_bit_cast(float, k[m].y & 0xffff0000u);
+                bf16x4_to(q[m], &qf[4 * m]);
+                bf16x4_to(k[m], &kf[4 * m]);
             } else {
                 qf[4 * m + 0] = qx[m].x; qf[4 * m + 1] = qx[m].y; qf[4 * m + 2] = qx[m].z; qf[4 * m + 3] = qx[m].w;
                 kf[4 * m + 0] = kx[m].x; kf[4 * m + 1] = kx[m].y; kf[4 * m + 2] = kx[m].z; kf[4 * m + 3] = kx[m].w;
@@ -306,32 +297,46 @@ struct KeyRaw4 {
         }
     }
 
+    // q, k, log_alpha and b (activated when the gates are logits); zero for a missing token
     __device__ __forceinline__ void unpack(float (&qf)[4 * NM], float (&kf)[4 * NM], float (&laf)[4 * NM],
                                            float (&bgf)[4 * NM]) const {
+        unpack_qk(qf, kf);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            if (BF16) {
-                qf[4 * m + 0] = __builtin_bit_cast(float, q[m].x << 16);
-                qf[4 * m + 1] = __builtin_bit_cast(float, q[m].x & 0xffff0000u);
-                qf[4 * m + 2] = __builtin_bit_cast(float, q[m].y << 16);
-                qf[4 * m + 3] = __builtin_bit_cast(float, q[m].y & 0xffff0000u);
-                kf[4 * m + 0] = __builtin_bit_cast(float, k[m].x << 16);
-                kf[4 * m + 1] = __builtin_bit_cast(float, k[m].x & 0xffff0000u);
-                kf[4 * m + 2] = __builtin_bit_cast(float, k[m].y << 16);
-                kf[4 * m + 3] = __builtin_bit_cast(float, k[m].y & 0xffff0000u);
+            if (GL) {
+                float x[4], y[4];
+                bf16x4_to(la16[m], x);
+                bf16x4_to(bg16[m], y);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    laf[4 * m + i] = decay_act<GL>(x[i]);
+                    bgf[4 * m + i] = gate_act<GL>(y[i]);
+                }
             } else {
-                qf[4 * m + 0] = qx[m].x; qf[4 * m + 1] = qx[m].y; qf[4 * m + 2] = qx[m].z; qf[4 * m + 3] = qx[m].w;
-                kf[4 * m + 0] = kx[m].x; kf[4 * m + 1] = kx[m].y; kf[4 * m + 2] = kx[m].z; kf[4 * m + 3] = kx[m].w;
+                laf[4 * m + 0] = la[m].x; laf[4 * m + 1] = la[m].y; laf[4 * m + 2] = la[m].z; laf[4 * m + 3] = la[m].w;
+                bgf[4 * m + 0] = bg[m].x; bgf[4 * m + 1] = bg[m].y; bgf[4 * m + 2] = bg[m].z; bgf[4 * m + 3] = bg[m].w;
             }
-            laf[4 * m + 0] = la[m].x; laf[4 * m + 1] = la[m].y; laf[4 * m + 2] = la[m].z; laf[4 * m + 3] = la[m].w;
-            bgf[4 * m + 0] = bg[m].x; bgf[4 * m + 1] = bg[m].y; bgf[4 * m + 2] = bg[m].z; bgf[4 * m + 3] = bg[m].w;
         }
 #pragma unroll
         for (int e = 0; e < 4 * NM; ++e) {
-            qf[e] = valid ? qf[e] : 0.f;
-            kf[e] = valid ? kf[e] : 0.f;
             laf[e] = valid ? laf[e] : 0.f;
             bgf[e] = valid ? bgf[e] : 0.f;
+        }
+    }
+
+    // d log_alpha / d stored decay input (1 for fp32 values)
+    __device__ __forceinline__ void decay_dact_all(float (&d)[4 * NM]) const {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (GL) {
+                float x[4];
+                bf16x4_to(la16[m], x);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[4 * m + i] = decay_dact<GL>(x[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[4 * m + i] = 1.f;
+            }
         }
     }
 };

@@ -170,6 +170,32 @@ __device__ __forceinline__ float load1(const void *base, size_t off, bool valid)
     return reinterpret_cast<const float *>(base)[off];
 }
 
+// ---- gate inputs: fp32 values, or bf16 logits activated in-kernel ----
+// With logits (GL), b = sigmoid(x_b), w = sigmoid(x_w) and log_alpha = log(sigmoid(x_a))
+// (the gates are sigmoid outputs of linear projections: blog on Gated DeltaNet-2,
+// section "Independent control on two axes"; the decay keeps an fp32 log form).
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * kLog2e)); }
+
+// log(sigmoid(x)) = min(x, 0) - log(1 + exp(-|x|)), in base-2 hardware exp/log
+__device__ __forceinline__ float log_sigmoid_f(float x) {
+    return fminf(x, 0.f) - __builtin_amdgcn_logf(1.f + exp2_fast(-fabsf(x) * kLog2e)) * kLn2;
+}
+
+// one gate element as stored: fp32 value or bf16 logit widened to fp32
+template <bool GL>
+__device__ __forceinline__ float load_gate1(const void *base, size_t off) {
+    if (GL) return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(base)[off]);
+    return reinterpret_cast<const float *>(base)[off];
+}
+// stored decay -> log_alpha, and d log_alpha / d stored
+template <bool GL> __device__ __forceinline__ float decay_act(float x) { return GL ? log_sigmoid_f(x) : x; }
+template <bool GL> __device__ __forceinline__ float decay_dact(float x) { return GL ? sigmoid_f(-x) : 1.f; }
+// stored erase/write gate -> gate value, and d gate / d stored as a function of the gate value
+template <bool GL> __device__ __forceinline__ float gate_act(float x) { return GL ? sigmoid_f(x) : x; }
+template <bool GL> __device__ __forceinline__ float gate_dact(float v) { return GL ? v * (1.f - v) : 1.f; }
+
 // Map the launch index to a logical work index so that consecutive logical
 // indices (the value tiles of one (batch, head)) land on the same XCD and share
 // its L2: the hardware deals workgroups to the 8 XCDs round-robin.

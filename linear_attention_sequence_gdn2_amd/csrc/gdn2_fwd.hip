@@ -36,7 +36,7 @@ namespace gdn2 {
 // above this point (bounds the live registers so two workgroups fit on a CU).
 #define GDN2_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <int DK, int VT, bool BF16, bool FAST, bool OUT, bool STATES>
+template <int DK, int VT, bool BF16, bool FAST, bool OUT, bool STATES, bool GL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     constexpr int NKS = DK / 32;           // 32-channel contraction steps
     constexpr int NVT = VT / 16;           // 16-column value tiles
@@ -118,7 +118,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         const size_t offk = baseK + (size_t)(vk ? tk : T - 1) * tokK + 8 * g;
         uint4 qraw[NKS], kraw[NKS];            // bf16 q, k (8 channels per uint4)
         float4 qx[NKS][2], kx[NKS][2];         // fp32 q, k
-        float4 la4[NKS][2], bg4[NKS][2];
+        float4 la4[NKS][2], bg4[NKS][2];       // fp32 gate values
+        uint4 la8[NKS], bg8[NKS];              // bf16 gate logits (GL)
 #pragma unroll
         for (int j = 0; j < NKS; ++j) {
             const size_t o = offk + 32 * j;
@@ -132,12 +133,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
                     kx[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.k) + o)[hh];
                 }
             }
+            if (GL) {
+                la8[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.la) + o);
+                bg8[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.bg) + o);
+            } else {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                la4[j][hh] = reinterpret_cast<const float4 *>(a.la + o)[hh];
-                bg4[j][hh] = reinterpret_cast<const float4 *>(a.bg + o)[hh];
+                for (int hh = 0; hh < 2; ++hh) {
+                    la4[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.la) + o)[hh];
+                    bg4[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.bg) + o)[hh];
+                }
             }
         }
+        // 8 gate elements of block j: fp32 values, or bf16 logits widened (activation applied by the caller)
+        auto gate8 = [&](const float4 (&fx)[2], const uint4 &raw, float (&out)[8]) {
+            if (GL) {
+                const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    out[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+                    out[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+                }
+            } else {
+                out[0] = fx[0].x; out[1] = fx[0].y; out[2] = fx[0].z; out[3] = fx[0].w;
+                out[4] = fx[1].x; out[5] = fx[1].y; out[6] = fx[1].z; out[7] = fx[1].w;
+            }
+        };
         // element i of block j of a packed input row
         auto unpack8 = [&](const uint4 &raw, const float4 (&fx)[2], float (&out)[8]) {
             if (BF16) {
@@ -159,10 +179,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         float G[NKS][8];
 #pragma unroll
         for (int j = 0; j < NKS; ++j) {
-            const float lv[8] = {la4[j][0].x, la4[j][0].y, la4[j][0].z, la4[j][0].w,
-                                 la4[j][1].x, la4[j][1].y, la4[j][1].z, la4[j][1].w};
+            float lv[8];
+            gate8(la4[j], la8[j], lv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) G[j][i] = row_scan16(vk ? lv[i] * kLog2e : 0.f);
+            for (int i = 0; i < 8; ++i) G[j][i] = row_scan16(vk ? decay_act<GL>(lv[i]) * kLog2e : 0.f);
         }
         if (r == 15) {
 #pragma unroll
@@ -205,8 +225,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             float qv[8], kv[8];
             unpack8(qraw[j], qx[j], qv);
             unpack8(kraw[j], kx[j], kv);
-            const float bv[8] = {bg4[j][0].x, bg4[j][0].y, bg4[j][0].z, bg4[j][0].w,
-                                 bg4[j][1].x, bg4[j][1].y, bg4[j][1].z, bg4[j][1].w};
+            float bv[8];
+            gate8(bg4[j], bg8[j], bv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bv[i] = gate_act<GL>(bv[i]);
             float et[8], qt[8], kt[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -263,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int tv = t0 + 16 * w + 4 * g + i;
                 const size_t off = baseV + (size_t)(tv < T ? tv : T - 1) * tokV + 16 * n + r;
-                const float zz = a.wg[off] * load1<BF16>(a.v, off, true);
+                const float zz = gate_act<GL>(load_gate1<GL>(a.wg, off)) * load1<BF16>(a.v, off, true);
                 z[n][i] = tv < T ? zz : 0.f;
             }
         // ---- X = Z - Et S and Qt S for this wave's rows (S from LDS) ----
@@ -385,47 +407,48 @@ int fwd_value_tile(int B, int H, int dk, int dv) {
     return vt;
 }
 
-template <int DK, int VT, bool BF16, int MODE>
+template <int DK, int VT, bool BF16, bool GL, int MODE>
 static hipError_t launch_t(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * a.nvt)), block(kThreads);
     constexpr bool OUT = MODE != kFwdStates, STATES = MODE != kFwdOut;
-    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, OUT, STATES>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, OUT, STATES, GL>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DK, bool BF16, int MODE>
+template <int DK, bool BF16, bool GL, int MODE>
 static hipError_t launch_vt(const FwdArgs &a, int vt, hipStream_t st) {
     if constexpr (DK >= 64) {
-        if (vt == 16) return launch_t<DK, 16, BF16, MODE>(a, st);
+        if (vt == 16) return launch_t<DK, 16, BF16, GL, MODE>(a, st);
     }
-    if (vt == 32) return launch_t<DK, 32, BF16, MODE>(a, st);
-    if (vt == 64) return launch_t<DK, 64, BF16, MODE>(a, st);
+    if (vt == 32) return launch_t<DK, 32, BF16, GL, MODE>(a, st);
+    if (vt == 64) return launch_t<DK, 64, BF16, GL, MODE>(a, st);
     return hipErrorInvalidValue;
 }
 
-template <bool BF16, int MODE>
+template <bool BF16, bool GL, int MODE>
 static hipError_t launch_dk(const FwdArgs &a, int dk, int vt, hipStream_t st) {
     switch (dk) {
-        case 32: return launch_vt<32, BF16, MODE>(a, vt, st);
-        case 64: return launch_vt<64, BF16, MODE>(a, vt, st);
-        case 128: return launch_vt<128, BF16, MODE>(a, vt, st);
+        case 32: return launch_vt<32, BF16, GL, MODE>(a, vt, st);
+        case 64: return launch_vt<64, BF16, GL, MODE>(a, vt, st);
+        case 128: return launch_vt<128, BF16, GL, MODE>(a, vt, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool GL>
 static hipError_t launch_mode(const FwdArgs &a, int dk, int vt, FwdMode mode, hipStream_t st) {
     switch (mode) {
-        case kFwdOut: return launch_dk<BF16, kFwdOut>(a, dk, vt, st);
-        case kFwdStates: return launch_dk<BF16, kFwdStates>(a, dk, vt, st);
-        case kFwdOutStates: return launch_dk<BF16, kFwdOutStates>(a, dk, vt, st);
+        case kFwdOut: return launch_dk<BF16, GL, kFwdOut>(a, dk, vt, st);
+        case kFwdStates: return launch_dk<BF16, GL, kFwdStates>(a, dk, vt, st);
+        case kFwdOutStates: return launch_dk<BF16, GL, kFwdOutStates>(a, dk, vt, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, FwdMode mode, hipStream_t st) {
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, FwdMode mode, hipStream_t st) {
     if (!vt_ok(dk, vt, a.dv)) return hipErrorInvalidValue;
-    return bf16 ? launch_mode<true>(a, dk, vt, mode, st) : launch_mode<false>(a, dk, vt, mode, st);
+    if (gl) return bf16 ? launch_mode<true, true>(a, dk, vt, mode, st) : hipErrorInvalidValue;
+    return bf16 ? launch_mode<true, false>(a, dk, vt, mode, st) : launch_mode<false, false>(a, dk, vt, mode, st);
 }
 
 }  // namespace gdn2

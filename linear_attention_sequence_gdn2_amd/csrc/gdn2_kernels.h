@@ -11,7 +11,7 @@ namespace gdn2 {
 // contiguous; states [B,H,dk,dv] fp32; chunk states [B,H,NC,dk,dv] fp32.
 struct FwdArgs {
     const void *q, *k, *v;          // qkv dtype
-    const float *la, *bg, *wg;      // log_alpha, b, w
+    const void *la, *bg, *wg;       // log_alpha, b, w: fp32 values or bf16 logits
     const float *S0;                // may be null (zeros)
     float *o;                       // [B,T,H,dv] (forward) or unused (state sweep)
     float *S_final;                 // may be null
@@ -23,7 +23,7 @@ struct FwdArgs {
 // Arguments of the backward kernels.
 struct BwdArgs {
     const void *q, *k, *v;
-    const float *la, *bg, *wg;
+    const void *la, *bg, *wg;       // fp32 values or bf16 logits
     const float *dO, *dS_final;     // dS_final may be null
     const float *states;            // [B,H,NC,dk,dv] chunk-start states
     float *dstates;                 // [B,H,NC,dk,dv] gradient w.r.t. chunk-end states
@@ -35,13 +35,13 @@ struct BwdArgs {
 // Arguments of the recurrent step (one token per (batch, head)); token tensors [BH, D].
 struct StepArgs {
     const void *q, *k, *v;
-    const float *la, *bg, *wg;
+    const void *la, *bg, *wg;       // fp32 values or bf16 logits
     const float *S_in;              // may be null (zeros)
     float *S_out;                   // may equal S_in
     float *o;
     int BH, dv;
 };
-hipError_t launch_step(const StepArgs &a, int dk, bool bf16, hipStream_t st);
+hipError_t launch_step(const StepArgs &a, int dk, bool bf16, bool gl, hipStream_t st);
 
 // Compute units of the current device (256 if the runtime cannot tell).
 inline int cu_count() {
@@ -57,9 +57,10 @@ int fwd_value_tile(int B, int H, int dk, int dv);
 
 // What a forward sweep produces: o only, chunk states only, or both.
 enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, FwdMode mode, hipStream_t st);
-hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, hipStream_t st);
+// gl: the gates are bf16 logits (only with bf16 q/k/v)
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, FwdMode mode, hipStream_t st);
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st);
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st);
-hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, hipStream_t st);
+hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st);
 
 }  // namespace gdn2

@@ -57,7 +57,7 @@ __device__ __forceinline__ Split8 frag_from_tiles(const uint4 &t0, const uint4 &
 // ---------------------------------------------------------------------------
 // Eight waves in two halves, as in bwd_chunk_kernel: wave (hf, w) owns tokens
 // 16w..16w+15 and, for the element work, the channels of half hf.
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool GL>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 
     // Persistent: the workgroup walks items blockIdx.x, + gridDim.x, ...; the key-side
     // inputs of the next item are loaded while the current one is in its products.
-    KeyRaw4<DK / 2, BF16> raw;
+    KeyRaw4<DK / 2, BF16, GL> raw;
     {
         bool v0;
         const size_t row0 = item_row(blockIdx.x < nitems ? blockIdx.x : 0, v0);
@@ -417,22 +417,28 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool GL>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
     const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);
     // one persistent workgroup per CU (the kernel's LDS allows no second one)
     const long grid = items < cu_count() ? items : cu_count();
-    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, hipStream_t st) {
+template <bool BF16, bool GL>
+static hipError_t factors_dk(const BwdArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return bf16 ? factors_t<32, true>(a, st) : factors_t<32, false>(a, st);
-        case 64: return bf16 ? factors_t<64, true>(a, st) : factors_t<64, false>(a, st);
-        case 128: return bf16 ? factors_t<128, true>(a, st) : factors_t<128, false>(a, st);
+        case 32: return factors_t<32, BF16, GL>(a, st);
+        case 64: return factors_t<64, BF16, GL>(a, st);
+        case 128: return factors_t<128, BF16, GL>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st) {
+    if (gl) return bf16 ? factors_dk<true, true>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? factors_dk<true, false>(a, dk, st) : factors_dk<false, false>(a, dk, st);
 }
 
 template <int DK, int VT>

@@ -18,7 +18,7 @@
 
 namespace gdn2 {
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool GL>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     constexpr int VT = 32, NS = kThreads / VT, RPS = DK / NS;   // slices, rows per slice
     __shared__ float sAlpha[DK], sE[DK], sK[DK], sQ[DK];
@@ -32,8 +32,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 
     if (tid < DK) {
         const float kk = load1<BF16>(a.k, kbase + tid, true);
-        sAlpha[tid] = exp2_fast(a.la[kbase + tid] * kLog2e);
-        sE[tid] = a.bg[kbase + tid] * kk;
+        sAlpha[tid] = exp2_fast(decay_act<GL>(load_gate1<GL>(a.la, kbase + tid)) * kLog2e);
+        sE[tid] = gate_act<GL>(load_gate1<GL>(a.bg, kbase + tid)) * kk;
         sK[tid] = kk;
         sQ[tid] = load1<BF16>(a.q, kbase + tid, true);
     }
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int i = 0; i < RPS; ++i)
         x[i] = a.S_in ? a.S_in[sbase + (size_t)(s * RPS + i) * a.dv + j] : 0.f;
-    const float z = a.wg[vbase + j] * load1<BF16>(a.v, vbase + j, true);
+    const float z = gate_act<GL>(load_gate1<GL>(a.wg, vbase + j)) * load1<BF16>(a.v, vbase + j, true);
     __syncthreads();
 
     // decay, then the read through the erase key
@@ -77,20 +77,26 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     }
 }
 
-template <int DK, bool BF16>
+template <int DK, bool BF16, bool GL>
 static hipError_t step_t(const StepArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((step_kernel<DK, BF16>), dim3((unsigned)(a.BH * (a.dv / 32))), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((step_kernel<DK, BF16, GL>), dim3((unsigned)(a.BH * (a.dv / 32))), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs &a, int dk, bool bf16, hipStream_t st) {
-    if (a.dv % 32 != 0) return hipErrorInvalidValue;
+template <bool BF16, bool GL>
+static hipError_t step_dk(const StepArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return bf16 ? step_t<32, true>(a, st) : step_t<32, false>(a, st);
-        case 64: return bf16 ? step_t<64, true>(a, st) : step_t<64, false>(a, st);
-        case 128: return bf16 ? step_t<128, true>(a, st) : step_t<128, false>(a, st);
+        case 32: return step_t<32, BF16, GL>(a, st);
+        case 64: return step_t<64, BF16, GL>(a, st);
+        case 128: return step_t<128, BF16, GL>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_step(const StepArgs &a, int dk, bool bf16, bool gl, hipStream_t st) {
+    if (a.dv % 32 != 0) return hipErrorInvalidValue;
+    if (gl) return bf16 ? step_dk<true, true>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? step_dk<true, false>(a, dk, st) : step_dk<false, false>(a, dk, st);
 }
 
 }  // namespace gdn2

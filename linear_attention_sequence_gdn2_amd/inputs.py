@@ -19,6 +19,10 @@ section "Ablations and training throughput", Figure 2):
   broadcast to b and w.  ``"gdn"``: as ``"kda"`` and log_alpha drawn once per
   (b,t,h) and broadcast over key channels.
 * S0 ~ N(0, s0_std) (zeros when s0_std == 0), dO ~ N(0, 1), dS_final ~ N(0, 0.01).
+* ``gate_logits=True`` (channel gates, log-sigmoid decay): the same normal draws are
+  returned before their activation, rounded to bf16, as ``x_a`` = N(3,1), ``x_b``,
+  ``x_w`` = N(0,1); the gate values are then left to the consumer (the operator forms
+  log(sigmoid(x_a)), sigmoid(x_b), sigmoid(x_w) itself).
 
 The second argument of every N(mu, sigma) is a standard deviation.  Draw order
 is fixed: q, k, v, log_alpha, b, w, S0, dO, dS_final.
@@ -64,11 +68,14 @@ WORKLOADS = {
                                         gates="gdn"),
     "fwdbwd_bf16_B4H16T4096d128": Workload("fwdbwd_bf16_B4H16T4096d128", 4, 4096, 16, 128, 128, 1005,
                                            s0_std=0.02, grads=True),
+    # the training shape with the gates given as bf16 logits (activated in the kernels)
+    "logits_bf16_B8H16T2048d128": Workload("logits_bf16_B8H16T2048d128", 8, 2048, 16, 128, 128, 1006,
+                                           grads=True, extra={"gate_logits": True}),
 }
 
 
 def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", gates="channel",
-                s0_std=0.0, grads=False):
+                s0_std=0.0, grads=False, gate_logits=False):
     """Return a dict of CPU tensors.
 
     ``q``, ``k``, ``v`` have dtype bf16 (or fp32 when ``qkv_dtype == "f32"``);
@@ -88,7 +95,15 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
     k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-30)
     v = randn(*shp_v)
 
-    if gates == "gdn":
+    if gate_logits:
+        if gates != "channel" or decay != "logsigmoid":
+            raise ValueError("gate logits are drawn for channel gates with a log-sigmoid decay")
+        x_a = (randn(*shp_k) + 3.0).to(torch.bfloat16)
+        x_b = randn(*shp_k).to(torch.bfloat16)
+        x_w = randn(*shp_v).to(torch.bfloat16)
+    if gate_logits:
+        la = b = w = None
+    elif gates == "gdn":
         la = F.logsigmoid(randn(B, T, H, 1) + 3.0).expand(shp_k).contiguous()
     elif decay == "softplus":
         la = -F.softplus(randn(*shp_k)) * 0.1
@@ -97,7 +112,9 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
     else:
         raise ValueError(decay)
 
-    if gates == "channel":
+    if gate_logits:
+        pass
+    elif gates == "channel":
         b = torch.sigmoid(randn(*shp_k))
         w = torch.sigmoid(randn(*shp_v))
     elif gates in ("kda", "gdn"):
@@ -124,7 +141,10 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
             out[name + "32"] = t
     else:
         raise ValueError(qkv_dtype)
-    out.update(log_alpha=la.contiguous(), b=b.contiguous(), w=w.contiguous(), S0=S0)
+    if gate_logits:
+        out.update(log_alpha=x_a.contiguous(), b=x_b.contiguous(), w=x_w.contiguous(), S0=S0, gate_logits=True)
+    else:
+        out.update(log_alpha=la.contiguous(), b=b.contiguous(), w=w.contiguous(), S0=S0)
 
     if grads:
         out["dO"] = randn(*shp_v)
@@ -134,6 +154,7 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
 
 def make_workload(wl: Workload, **override):
     kw = dict(B=wl.B, T=wl.T, H=wl.H, dk=wl.dk, dv=wl.dv, seed=wl.seed, qkv_dtype=wl.qkv_dtype,
-              decay=wl.decay, gates=wl.gates, s0_std=wl.s0_std, grads=wl.grads)
+              decay=wl.decay, gates=wl.gates, s0_std=wl.s0_std, grads=wl.grads,
+              gate_logits=wl.extra.get("gate_logits", False))
     kw.update(override)
     return make_inputs(**kw)

@@ -119,3 +119,36 @@ def bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, nthreads=None):
     if rc != 0:
         raise RuntimeError("gdn2_oracle_bwd failed (%d)" % rc)
     return out
+
+
+# ---- gates given as pre-activation logits ----
+# The erase and write gates are sigmoid outputs of their own linear projections (blog on
+# Gated DeltaNet-2, section "Independent control on two axes"); the decay keeps an fp32
+# log form (section "Token path and parallel training").  With logits x_a, x_b, x_w the
+# operator's gates are
+#     log_alpha = log(sigmoid(x_a)),   b = sigmoid(x_b),   w = sigmoid(x_w),
+# and gradients w.r.t. the logits follow by the chain rule:
+#     d/dx log(sigmoid(x)) = sigmoid(-x),   d/dx sigmoid(x) = sigmoid(x) (1 - sigmoid(x)).
+
+def _sigmoid(x):
+    # exp(log sigmoid(x)): relative accuracy at both tails
+    return np.exp(-np.logaddexp(0.0, -x))
+
+
+def gates_from_logits(x_a, x_b, x_w):
+    """(log_alpha, b, w) in float64 from the three logit tensors (any float dtype)."""
+    xa, xb, xw = (_f64(t) for t in (x_a, x_b, x_w))
+    log_alpha = -np.logaddexp(0.0, -xa)
+    return log_alpha, _sigmoid(xb), _sigmoid(xw)
+
+
+def logit_grads(x_a, x_b, x_w, grads):
+    """Gradients w.r.t. the logits from the oracle's gradients w.r.t. the gate values
+    (a dict as returned by bwd); returns a new dict with dlog_alpha, db, dw replaced."""
+    xa, xb, xw = (_f64(t) for t in (x_a, x_b, x_w))
+    sb, sw = _sigmoid(xb), _sigmoid(xw)
+    out = dict(grads)
+    out["dlog_alpha"] = grads["dlog_alpha"] * _sigmoid(-xa)
+    out["db"] = grads["db"] * sb * (1.0 - sb)
+    out["dw"] = grads["dw"] * sw * (1.0 - sw)
+    return out

@@ -36,8 +36,8 @@ def test_every_declared_symbol_is_exported():
     assert sorted(names) == sorted(gdn2.EXPORTS)
 
 
-def _shape(B=2, T=100, H=3, dk=128, dv=64, chunk=64, dt=1):
-    return gdn2.Gdn2Shape(B, T, H, dk, dv, chunk, dt)
+def _shape(B=2, T=100, H=3, dk=128, dv=64, chunk=64, dt=1, gates=0):
+    return gdn2.Gdn2Shape(B, T, H, dk, dv, chunk, dt, gates)
 
 
 def test_workspace_and_state_sizes():
@@ -58,6 +58,7 @@ def test_workspace_and_state_sizes():
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(H=-1), INVALID),
     (dict(chunk=32), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED), (dict(B=1 << 14, T=1 << 14, H=16), UNSUPPORTED),
+    (dict(gates=2), UNSUPPORTED), (dict(gates=1, dt=0), UNSUPPORTED),
 ])
 def test_shape_checks(kw, code):
     lib = gdn2.load()

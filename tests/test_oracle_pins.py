@@ -342,3 +342,56 @@ def test_golden_regression_fixture():
     for name, samples in rec["samples"].items():
         for ix, val in samples:
             assert abs(arrs[name][tuple(ix)] - val) <= 1e-12 * max(1.0, abs(val)), (name, ix)
+
+
+# ---------------------------------------------------------------------------
+# gates given as logits (log_alpha = log sigmoid, b, w = sigmoid)
+# ---------------------------------------------------------------------------
+
+def test_logit_gates_closed_forms():
+    la, b, w = oracle.gates_from_logits(np.zeros(3), np.zeros(3), np.zeros(3))
+    assert np.allclose(la, -np.log(2.0), rtol=0, atol=1e-15)
+    assert np.allclose(b, 0.5, rtol=0, atol=1e-15) and np.allclose(w, 0.5, rtol=0, atol=1e-15)
+    x = np.array([-60.0, -5.0, 2.0, 60.0])
+    la, b, w = oracle.gates_from_logits(x, x, x)
+    assert np.all(np.isfinite(la)) and np.all(np.isfinite(b))
+    # log sigmoid(x) -> x for x -> -inf and -> -exp(-x) for x -> +inf; sigmoid(-x) = 1 - sigmoid(x)
+    assert abs(la[0] - (-60.0)) < 1e-20 and abs(la[3] + np.exp(-60.0)) < 1e-40
+    _, bm, _ = oracle.gates_from_logits(x, -x, x)
+    assert np.allclose(bm, 1.0 - b, rtol=0, atol=1e-15)
+    assert np.allclose(np.exp(la), b, rtol=1e-14, atol=0)
+
+
+def test_logit_gate_gradients_match_central_differences():
+    """Gradients w.r.t. the three logit tensors: the oracle's backward composed with
+    the gate activations, against central differences of the composed forward."""
+    q, k, v, _, _, _, S0 = _case(34, B=1, T=10, H=1, dk=4, dv=4, s0=0.5)
+    r = _rng(35)
+    xa = r.standard_normal(q.shape) + 3.0
+    xb = r.standard_normal(q.shape)
+    xw = r.standard_normal(v.shape)
+    dO = r.standard_normal(v.shape)
+    dSf = r.standard_normal(S0.shape) * 0.5
+
+    def loss(xa_, xb_, xw_):
+        o, sf = oracle.fwd(q, k, v, *oracle.gates_from_logits(xa_, xb_, xw_), S0, nthreads=1)
+        return float(np.sum(o * dO) + np.sum(sf * dSf))
+
+    g = oracle.bwd(q, k, v, *oracle.gates_from_logits(xa, xb, xw), S0, dO, dSf, nthreads=1)
+    gl = oracle.logit_grads(xa, xb, xw, g)
+    for pos, name in ((0, "dlog_alpha"), (1, "db"), (2, "dw")):
+        xs = [xa, xb, xw]
+        x = xs[pos]
+        fd = np.empty(x.size)
+        for n, ix in enumerate(np.ndindex(x.shape)):
+            h = 1e-6 * max(1.0, abs(x[ix]))
+            xp = [t.copy() for t in xs]
+            xm = [t.copy() for t in xs]
+            xp[pos][ix] += h
+            xm[pos][ix] -= h
+            fd[n] = (loss(*xp) - loss(*xm)) / (2 * h)
+        an = gl[name].reshape(-1)
+        err = np.max(np.abs(fd - an)) / max(np.max(np.abs(fd)), 1e-30)
+        assert err < 1e-6, (name, err)
+    for name in ("dq", "dk", "dv", "dS0"):
+        assert gl[name] is g[name]
