@@ -46,6 +46,10 @@ BWD_BYTES_PER_TOKHEAD = 5888
 # with the gates given as bf16 logits each pass reads 1536 -> 768 gate bytes per token-head
 GATE_BYTES_SAVED_PER_TOKHEAD = 768
 LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
+# with all three gates given per token ([B,T,H] fp32) each gate read, and each gate
+# gradient written, moves 12 instead of 1536 bytes per token-head
+TOKEN_GATE_BYTES_SAVED_PER_TOKHEAD = 1536 - 12
+TOKEN_WORKLOAD = "gdn_token_bf16_B8H16T2048d128"
 FWD_STATES_BYTES_PER_TOKHEAD = 3840
 BWD_FACTORS_BYTES_PER_TOKHEAD = 3072
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
@@ -138,6 +142,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-step (decode) measurement")
     ap.add_argument("--no-logit-gates", action="store_true", help="skip the step with bf16 logit gates")
+    ap.add_argument("--no-token-gates", action="store_true", help="skip the step with per-token gates")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
@@ -275,6 +280,17 @@ def main():
             "kernel_ms": {kn[0]: round(ms, 4) for kn, ms in zip(kernels, lk_ms)},
             "step_event_ms": round(lstep_ms, 4),
             "step_algorithmic_frac": round(lalg / (lstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_token_gates:
+        # the same step with Gated DeltaNet's gates, one value per token ([B,T,H])
+        twl = WORKLOADS[TOKEN_WORKLOAD]
+        twall, tk_ms, tstep_ms = timed_steps(make_workload(twl), args.steps, args.warmup)
+        talg = (FWD_BYTES_PER_TOKHEAD + BWD_BYTES_PER_TOKHEAD - 3 * TOKEN_GATE_BYTES_SAVED_PER_TOKHEAD) * tokheads
+        out["breakdown"]["token_gates_step"] = {
+            "workload": TOKEN_WORKLOAD, "ms_per_step": round(twall / args.steps * 1e3, 4),
+            "tokens_per_s": round(tokens / (twall / args.steps), 1),
+            "kernel_ms": {kn[0]: round(ms, 4) for kn, ms in zip(kernels, tk_ms)},
+            "step_event_ms": round(tstep_ms, 4),
+            "step_algorithmic_frac": round(talg / (tstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_decode:
         out["breakdown"]["decode_step"] = decode_bench(dev)
     if not args.no_cpu_baseline:

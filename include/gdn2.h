@@ -26,6 +26,7 @@
  *   run concurrently.
  * - Token tensors are [B, T, H, D]: q, k, log_alpha, b and the key-side
  *   gradients use D = dk; v, w, o and the value-side gradients use D = dv.
+ *   A gate flagged in shape->gate_scalar, and its gradient, is [B, T, H] instead.
  *   States are [B, H, dk, dv] fp32 (key channel = row).
  * - q, k, v have dtype shape->qkv_dtype (fp32 or bf16).  S0, dO, dS_final and
  *   every output are fp32.  log_alpha, b, w are fp32 values or bf16 logits as
@@ -75,12 +76,28 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
  *     w.r.t. the logits.  Requires qkv_dtype == GDN2_BF16.  Halves the gate bytes. */
 typedef enum { GDN2_GATES_F32 = 0, GDN2_GATES_BF16_LOGITS = 1 } gdn2_gate_dtype;
 
+/* Per-token gates (bits of gdn2_shape.gate_scalar).  A gate whose bit is set is given as
+ * ONE fp32 value per (batch, token, head), a [B, T, H] tensor, that applies to every
+ * channel of its axis; its gradient output is then [B, T, H] too (the sum over the
+ * channels of the per-channel gradient).  This covers the special cases of the rule:
+ * erase and write gate both one beta per token (KDA), also a scalar decay (Gated
+ * DeltaNet) (blog on Gated DeltaNet-2, section "Independent control on two axes"), and
+ * the gate ablations that use the channel mean of the erase or the write gate (same
+ * blog, section "Ablations and training throughput").  The per-token tensors need only
+ * 4-byte alignment.  Requires qkv_dtype == GDN2_BF16 and gate_dtype == GDN2_GATES_F32. */
+typedef enum {
+    GDN2_SCALAR_DECAY = 1,   /* log_alpha and dlog_alpha are [B, T, H] */
+    GDN2_SCALAR_ERASE = 2,   /* b and db are [B, T, H] */
+    GDN2_SCALAR_WRITE = 4    /* w and dw are [B, T, H] */
+} gdn2_gate_scalar;
+
 typedef struct {
     int B, T, H;      /* batch, tokens, heads */
     int dk, dv;       /* key and value head dimensions */
     int chunk;        /* must be 64 */
     int qkv_dtype;    /* a gdn2_dtype: dtype of q, k and v */
     int gate_dtype;   /* a gdn2_gate_dtype: how log_alpha, b and w are given */
+    int gate_scalar;  /* OR of gdn2_gate_scalar bits; 0 = every gate per channel */
 } gdn2_shape;
 
 /* Bytes of device workspace gdn2_chunk_fwd needs (0 for every supported shape);

@@ -2,7 +2,9 @@
 
 Gates (log_alpha, b, w) are fp32 values, or -- as bfloat16 tensors -- pre-activation
 logits (log_alpha = log sigmoid, b, w = sigmoid, formed in the kernels; gradients are
-then w.r.t. the logits).
+then w.r.t. the logits).  An fp32 gate may also be given per token, as a [B, T, H]
+tensor without the channel axis (one value for all channels of its axis; with bf16
+q/k/v); its gradient then comes back as [B, T, H] as well.
 
 Argument marshalling only: checks dtypes, devices and contiguity, allocates
 the outputs and the workspace with torch on the inputs' device, and passes raw
@@ -24,6 +26,7 @@ GDN2_F32 = 0
 GDN2_BF16 = 1
 GDN2_GATES_F32 = 0
 GDN2_GATES_BF16_LOGITS = 1
+GDN2_SCALAR_DECAY, GDN2_SCALAR_ERASE, GDN2_SCALAR_WRITE = 1, 2, 4
 STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3: "GDN2_ERR_WORKSPACE",
           4: "GDN2_ERR_HIP"}
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
@@ -35,7 +38,7 @@ EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
 class Gdn2Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
                 ("dv", ctypes.c_int), ("chunk", ctypes.c_int), ("qkv_dtype", ctypes.c_int),
-                ("gate_dtype", ctypes.c_int)]
+                ("gate_dtype", ctypes.c_int), ("gate_scalar", ctypes.c_int)]
 
 
 class Gdn2Error(RuntimeError):
@@ -100,10 +103,30 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32):
-    """Gates given as bf16 tensors are pre-activation logits (gdn2_gate_dtype)."""
+def make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32, gate_scalar=0):
+    """Gates given as bf16 tensors are pre-activation logits (gdn2_gate_dtype);
+    gate_scalar holds the GDN2_SCALAR_* bits of the gates given per token."""
     return Gdn2Shape(B, T, H, dk, dv, 64, GDN2_BF16 if qkv_dtype == torch.bfloat16 else GDN2_F32,
-                     GDN2_GATES_BF16_LOGITS if gate_dtype == torch.bfloat16 else GDN2_GATES_F32)
+                     GDN2_GATES_BF16_LOGITS if gate_dtype == torch.bfloat16 else GDN2_GATES_F32, gate_scalar)
+
+
+_GATE_BITS = (("log_alpha", GDN2_SCALAR_DECAY), ("b", GDN2_SCALAR_ERASE), ("w", GDN2_SCALAR_WRITE))
+
+
+def _gate_scalar(lead, gates):
+    """GDN2_SCALAR_* bits of the gates given per token: shape `lead` ([B,T,H], or [B,H]
+    for a step) without the channel axis.  `gates` maps gate name -> tensor."""
+    sc = 0
+    for name, bit in _GATE_BITS:
+        t = gates.get(name)
+        if t is not None and tuple(t.shape) == tuple(lead):
+            sc |= bit
+    return sc
+
+
+def _gate_shape(name, lead, d, sc):
+    bit = dict(_GATE_BITS)[name]
+    return tuple(lead) if sc & bit else tuple(lead) + (d,)
 
 
 def _gate_dtype(q, *gates):
@@ -124,25 +147,36 @@ def _validate(q, k, v, log_alpha, b, w, extra=()):
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q/k/v must be float32 or bfloat16")
     gd = _gate_dtype(q, log_alpha, b, w)
+    sc = _gate_scalar((B, T, H), dict(log_alpha=log_alpha, b=b, w=w))
     for name, t, shp, dt in (("k", k, (B, T, H, dk), q.dtype), ("v", v, (B, T, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (B, T, H, dk), gd),
-                             ("b", b, (B, T, H, dk), gd), ("w", w, (B, T, H, dv), gd)):
+                             ("log_alpha", log_alpha, _gate_shape("log_alpha", (B, T, H), dk, sc), gd),
+                             ("b", b, _gate_shape("b", (B, T, H), dk, sc), gd),
+                             ("w", w, _gate_shape("w", (B, T, H), dv, sc), gd)):
         if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device:
             raise ValueError("gdn2: %s has shape %s dtype %s device %s, expected %s %s %s"
                              % (name, tuple(t.shape), t.dtype, t.device, shp, dt, q.device))
     for t in (q, k, v, log_alpha, b, w) + tuple(x for x in extra if x is not None):
         if not t.is_contiguous():
             raise ValueError("gdn2: tensors must be contiguous")
-    return B, T, H, dk, dv
+    return B, T, H, dk, dv, sc
+
+
+def _grad_outputs(B, T, H, dk, dv, sc, dev):
+    """Empty fp32 gradient tensors; a per-token gate's gradient is [B,T,H]."""
+    out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk")}
+    out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    for gname, name, d in (("log_alpha", "dlog_alpha", dk), ("b", "db", dk), ("w", "dw", dv)):
+        out[name] = torch.empty(_gate_shape(gname, (B, T, H), d, sc), dtype=torch.float32, device=dev)
+    return out
 
 
 def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
     """o [B,T,H,dv] fp32 and S_final [B,H,dk,dv] fp32 (None if not wanted)."""
-    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0,))
+    B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (S0,))
     if S0 is not None and (tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32):
         raise ValueError("gdn2: S0 must be float32 [B,H,dk,dv]")
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
     ws_bytes = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(shape))
@@ -154,26 +188,24 @@ def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
     return o, sf
 
 
-def bwd_workspace_bytes(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32):
-    shape = make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype)
+def bwd_workspace_bytes(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32, gate_scalar=0):
+    shape = make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype, gate_scalar)
     return load().gdn2_chunk_bwd_workspace_size(ctypes.byref(shape))
 
 
 def bwd(q, k, v, log_alpha, b, w, S0, dO, dS_final=None, want_dS0=True, workspace=None):
     """Gradients of sum(dO*o) + sum(dS_final*S_final): dict of fp32 tensors
     dq, dk, dv, dlog_alpha, db, dw (input shapes) and dS0 (or None)."""
-    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0, dO, dS_final))
+    B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (S0, dO, dS_final))
     if tuple(dO.shape) != (B, T, H, dv) or dO.dtype != torch.float32:
         raise ValueError("gdn2: dO must be float32 [B,T,H,dv]")
     for name, t in (("S0", S0), ("dS_final", dS_final)):
         if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
             raise ValueError("gdn2: %s must be float32 [B,H,dk,dv]" % name)
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
     dev = q.device
-    out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
-    out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-    out["dw"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    out = _grad_outputs(B, T, H, dk, dv, sc, dev)
     out["dS0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
     ws_bytes = lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(shape))
     if workspace is None:
@@ -192,9 +224,9 @@ def states_shape(B, T, H, dk, dv):
 def fwd_states(q, k, v, log_alpha, b, w, S0=None, want_state=True, states=None):
     """Forward that also returns the chunk-start states [B,H,ceil(T/64),dk,dv] fp32
     (one kernel): (o, S_final, states)."""
-    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (S0,))
+    B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (S0,))
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
     if states is None:
@@ -206,9 +238,9 @@ def fwd_states(q, k, v, log_alpha, b, w, S0=None, want_state=True, states=None):
 
 def chunk_states(k, v, log_alpha, b, w, S0=None, q_dtype=None, states=None):
     """State sweep only (one kernel): chunk-start states [B,H,ceil(T/64),dk,dv]."""
-    B, T, H, dk, dv = _validate(k, k, v, log_alpha, b, w, (S0,))
+    B, T, H, dk, dv, sc = _validate(k, k, v, log_alpha, b, w, (S0,))
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, k.dtype, log_alpha.dtype)
+    shape = make_shape(B, T, H, dk, dv, k.dtype, log_alpha.dtype, sc)
     if states is None:
         states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=k.device)
     _check(lib.gdn2_chunk_states(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
@@ -230,16 +262,19 @@ def bwd_factors(q, k, log_alpha, b, factors=None):
     tensor of factors_bytes() bytes, read only by bwd_reverse."""
     B, T, H, dk = q.shape
     gd = _gate_dtype(q, log_alpha, b)
-    for name, t, dt in (("k", k, q.dtype), ("log_alpha", log_alpha, gd), ("b", b, gd)):
-        if tuple(t.shape) != (B, T, H, dk) or t.dtype != dt or t.device != q.device:
-            raise ValueError("gdn2: %s must be %s %s on %s" % (name, (B, T, H, dk), dt, q.device))
+    sc = _gate_scalar((B, T, H), dict(log_alpha=log_alpha, b=b))
+    for name, t, shp, dt in (("k", k, (B, T, H, dk), q.dtype),
+                             ("log_alpha", log_alpha, _gate_shape("log_alpha", (B, T, H), dk, sc), gd),
+                             ("b", b, _gate_shape("b", (B, T, H), dk, sc), gd)):
+        if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device:
+            raise ValueError("gdn2: %s must be %s %s on %s" % (name, shp, dt, q.device))
     for t in (q, k, log_alpha, b):
         if not t.is_contiguous():
             raise ValueError("gdn2: tensors must be contiguous")
     if not q.is_cuda:
         raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % q.device)
     lib = load()
-    shape = make_shape(B, T, H, dk, dk, q.dtype, gd)
+    shape = make_shape(B, T, H, dk, dk, q.dtype, gd, sc)
     need = factors_bytes(B, T, H, dk)
     if factors is None:
         factors = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -272,13 +307,11 @@ def bwd_reverse(factors, dO, dk, dS_final=None, want_dS0=True, dstates=None):
 
 def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates):
     """Token gradients from chunk states and end-state gradients (one kernel)."""
-    B, T, H, dk, dv = _validate(q, k, v, log_alpha, b, w, (dO, states, dstates))
+    B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (dO, states, dstates))
     lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype)
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
     dev = q.device
-    out = {n: torch.empty((B, T, H, dk), dtype=torch.float32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
-    out["dv"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-    out["dw"] = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    out = _grad_outputs(B, T, H, dk, dv, sc, dev)
     _check(lib.gdn2_chunk_bwd_grads(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
                                     _ptr(w), _ptr(dO), _ptr(states), _ptr(dstates), _ptr(out["dq"]),
                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
@@ -297,7 +330,8 @@ def bwd_saved(q, k, v, log_alpha, b, w, states, dO, dS_final=None, want_dS0=True
 
 def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
     """One recurrent step (decode, one kernel): q, k, log_alpha, b [B,H,dk], v, w [B,H,dv]
-    (q/k/v fp32 or bf16; gates fp32 values, or bf16 logits with bf16 q/k/v),
+    (q/k/v fp32 or bf16; gates fp32 values, or bf16 logits with bf16 q/k/v; an fp32
+    gate may be [B,H], one value for all its channels, with bf16 q/k/v),
     S [B,H,dk,dv] fp32 or None (zeros).
     Returns (o [B,H,dv] fp32, S_new).  With in_place=True, S is updated in place."""
     if not q.is_cuda:
@@ -305,9 +339,11 @@ def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
     B, H, dk = q.shape
     dv = v.shape[-1]
     gd = _gate_dtype(q, log_alpha, b, w)
+    sc = _gate_scalar((B, H), dict(log_alpha=log_alpha, b=b, w=w))
     for name, t, shp, dt in (("k", k, (B, H, dk), q.dtype), ("v", v, (B, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (B, H, dk), gd),
-                             ("b", b, (B, H, dk), gd), ("w", w, (B, H, dv), gd)):
+                             ("log_alpha", log_alpha, _gate_shape("log_alpha", (B, H), dk, sc), gd),
+                             ("b", b, _gate_shape("b", (B, H), dk, sc), gd),
+                             ("w", w, _gate_shape("w", (B, H), dv, sc), gd)):
         if tuple(t.shape) != shp or t.dtype != dt or t.device != q.device or not t.is_contiguous():
             raise ValueError("gdn2: %s must be contiguous %s %s on %s" % (name, shp, dt, q.device))
     if not q.is_contiguous():
@@ -317,7 +353,7 @@ def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
     if in_place and S is None:
         raise ValueError("gdn2: in_place needs a state")
     lib = load()
-    shape = make_shape(B, 1, H, dk, dv, q.dtype, gd)
+    shape = make_shape(B, 1, H, dk, dv, q.dtype, gd, sc)
     o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     S_new = S if in_place else (out if out is not None else
                                 torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device))

@@ -13,8 +13,16 @@ namespace {
 bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool gate_logits(const gdn2_shape *s) { return s->gate_dtype == GDN2_GATES_BF16_LOGITS; }
+
+static_assert(GDN2_SCALAR_DECAY == gdn2::kScalarDecay && GDN2_SCALAR_ERASE == gdn2::kScalarErase &&
+                  GDN2_SCALAR_WRITE == gdn2::kScalarWrite,
+              "per-token gate bits of the ABI and the kernels agree");
+constexpr int kScalarAll = GDN2_SCALAR_DECAY | GDN2_SCALAR_ERASE | GDN2_SCALAR_WRITE;
+
+bool gate_scalar(const gdn2_shape *s) { return s->gate_scalar != 0; }
 
 int check_shape(const gdn2_shape *s) {
     if (!s) return GDN2_ERR_INVALID_ARG;
@@ -24,6 +32,8 @@ int check_shape(const gdn2_shape *s) {
     if (s->qkv_dtype != GDN2_F32 && s->qkv_dtype != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
     if (s->gate_dtype != GDN2_GATES_F32 && s->gate_dtype != GDN2_GATES_BF16_LOGITS) return GDN2_ERR_UNSUPPORTED;
     if (s->gate_dtype == GDN2_GATES_BF16_LOGITS && s->qkv_dtype != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (s->gate_scalar & ~kScalarAll) return GDN2_ERR_UNSUPPORTED;
+    if (s->gate_scalar && (s->qkv_dtype != GDN2_BF16 || s->gate_dtype != GDN2_GATES_F32)) return GDN2_ERR_UNSUPPORTED;
     const int dmax = s->dk > s->dv ? s->dk : s->dv;
     const unsigned long long n = (unsigned long long)s->B * s->T * s->H * dmax;
     if (n >= (1ull << 31)) return GDN2_ERR_UNSUPPORTED;
@@ -33,6 +43,16 @@ int check_shape(const gdn2_shape *s) {
 }
 
 int nchunks(const gdn2_shape *s) { return (s->T + 63) / 64; }
+
+// the alignment a gate tensor (or its gradient) needs: 4 bytes when it is per token
+bool gate_aligned(const gdn2_shape *s, int bit, const void *p) {
+    return !p || ((s->gate_scalar & bit) ? aligned4(p) : aligned16(p));
+}
+
+bool gates_aligned(const gdn2_shape *s, const void *la, const void *b, const void *w) {
+    return gate_aligned(s, GDN2_SCALAR_DECAY, la) && gate_aligned(s, GDN2_SCALAR_ERASE, b) &&
+           gate_aligned(s, GDN2_SCALAR_WRITE, w);
+}
 
 }  // namespace
 
@@ -62,9 +82,10 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, o, S_final};
+    const void *ptrs[] = {q, k, v, S0, o, S_final};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
+    if (!gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
 
     gdn2::FwdArgs a{};
     a.q = q; a.k = k; a.v = v;
@@ -73,8 +94,9 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
     a.B = shape->B; a.T = shape->T; a.H = shape->H; a.dv = shape->dv;
     const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
     a.nvt = shape->dv / vt;
-    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape), gdn2::kFwdOut,
-                                          reinterpret_cast<hipStream_t>(stream));
+    a.scalar = shape->gate_scalar;
+    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
+                                          gate_scalar(shape), gdn2::kFwdOut, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
@@ -108,6 +130,7 @@ gdn2::FwdArgs fwd_args(const gdn2_shape *shape, const void *q, const void *k, co
     f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv;
     const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
     f.nvt = shape->dv / vt;
+    f.scalar = shape->gate_scalar;
     *vt_out = vt;
     return f;
 }
@@ -115,6 +138,7 @@ gdn2::FwdArgs fwd_args(const gdn2_shape *shape, const void *q, const void *k, co
 gdn2::BwdArgs bwd_args(const gdn2_shape *shape) {
     gdn2::BwdArgs a{};
     a.B = shape->B; a.T = shape->T; a.H = shape->H; a.DV = shape->dv;
+    a.scalar = shape->gate_scalar;
     return a;
 }
 
@@ -136,11 +160,12 @@ int gdn2_chunk_fwd_states(const gdn2_shape *shape, const void *q, const void *k,
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!q || !k || !v || !log_alpha || !b || !w || !o || !states) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, v, log_alpha, b, w, S0, o, S_final, states})) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, v, S0, o, S_final, states}) || !gates_aligned(shape, log_alpha, b, w))
+        return GDN2_ERR_INVALID_ARG;
     int vt;
     const gdn2::FwdArgs f = fwd_args(shape, q, k, v, log_alpha, b, w, S0, o, S_final, states, &vt);
     return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                          gdn2::kFwdOutStates,
+                                          gate_scalar(shape), gdn2::kFwdOutStates,
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -149,11 +174,11 @@ int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v, con
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!k || !v || !log_alpha || !b || !w || !states) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({k, v, log_alpha, b, w, S0, states})) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({k, v, S0, states}) || !gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
     int vt;
     const gdn2::FwdArgs f = fwd_args(shape, nullptr, k, v, log_alpha, b, w, S0, nullptr, nullptr, states, &vt);
     return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                          gdn2::kFwdStates,
+                                          gate_scalar(shape), gdn2::kFwdStates,
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -162,11 +187,11 @@ int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!q || !k || !log_alpha || !b || !factors) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, log_alpha, b, factors})) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, factors}) || !gates_aligned(shape, log_alpha, b, nullptr)) return GDN2_ERR_INVALID_ARG;
     gdn2::BwdArgs a = bwd_args(shape);
     a.q = q; a.k = k; a.la = log_alpha; a.bg = b; a.factors = factors;
     return launch_status(gdn2::launch_bwd_factors(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                                  reinterpret_cast<hipStream_t>(stream)));
+                                                  gate_scalar(shape), reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const float *dO,
@@ -190,7 +215,8 @@ int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, 
     if (!q || !k || !v || !log_alpha || !b || !w || !dO || !states || !dstates || !dq || !dk || !dv ||
         !dlog_alpha || !db || !dw)
         return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, v, log_alpha, b, w, dO, states, dstates, dq, dk, dv, dlog_alpha, db, dw}))
+    if (!all_aligned({q, k, v, dO, states, dstates, dq, dk, dv}) || !gates_aligned(shape, log_alpha, b, w) ||
+        !gates_aligned(shape, dlog_alpha, db, dw))
         return GDN2_ERR_INVALID_ARG;
     gdn2::BwdArgs a = bwd_args(shape);
     a.q = q; a.k = k; a.v = v;
@@ -198,7 +224,7 @@ int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, 
     a.dO = dO; a.states = states; a.dstates = const_cast<float *>(dstates);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
     return launch_status(gdn2::launch_bwd_chunk(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                                reinterpret_cast<hipStream_t>(stream)));
+                                                gate_scalar(shape), reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
@@ -210,7 +236,8 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     if (st != GDN2_OK) return st;
     if (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv || !dlog_alpha || !db || !dw)
         return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, v, log_alpha, b, w, S0, dO, dS_final, dq, dk, dv, dlog_alpha, db, dw, dS0, workspace}))
+    if (!all_aligned({q, k, v, S0, dO, dS_final, dq, dk, dv, dS0, workspace}) ||
+        !gates_aligned(shape, log_alpha, b, w) || !gates_aligned(shape, dlog_alpha, db, dw))
         return GDN2_ERR_INVALID_ARG;
     const size_t need = gdn2_chunk_bwd_workspace_size(shape);
     if (!workspace || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
@@ -234,14 +261,15 @@ int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void 
     if (st != GDN2_OK) return st;
     if (shape->T != 1) return GDN2_ERR_INVALID_ARG;
     if (!q || !k || !v || !log_alpha || !b || !w || !S_out || !o) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, v, log_alpha, b, w, S_in, S_out, o})) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({q, k, v, S_in, S_out, o}) || !gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
     gdn2::StepArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.la = log_alpha; a.bg = b; a.wg = w;
     a.S_in = S_in; a.S_out = S_out; a.o = o;
     a.BH = shape->B * shape->H; a.dv = shape->dv;
+    a.scalar = shape->gate_scalar;
     return launch_status(gdn2::launch_step(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                           reinterpret_cast<hipStream_t>(stream)));
+                                           gate_scalar(shape), reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -45,7 +45,7 @@ namespace gdn2 {
 // chunk, so one workgroup takes most of a CU's LDS and the two halves give every SIMD
 // two waves.
 
-template <int DK, bool BF16, bool GL>
+template <int DK, bool BF16, bool GL, bool SG>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int VT = 32;                       // value columns per tile
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     constexpr int oAT = odUX + B_VT, oTot = oAT + kChunk * PA * 4, oTs = oAT;
     constexpr int oGam = (oTot + 4 * DK * 4 > oTs + B_TS) ? oTot + 4 * DK * 4 : oTs + B_TS;
     constexpr int oDG = oGam + DK * 4;
-    constexpr int SMEM = oDG + DK * 4;
+    constexpr int oRed = oDG + DK * 4;           // per-token gate gradients of half 1 (SG)
+    constexpr int SMEM = oRed + (SG ? 3 * kChunk * 4 : 0);
     constexpr int oQt = oLoop, odPt = oQt + B_ROWS, odAt = odPt + B_PT;
     constexpr int oScr = odAt + B_PT, oTotA = oScr + 8 * DK * 4, oTotB = oTotA + 4 * DK * 4;
     static_assert(oQt + B_ROWS <= oAT, "Qt rows overlap T during preparation");
@@ -87,6 +88,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float *sAT = reinterpret_cast<float *>(smem + oAT), *sTot = reinterpret_cast<float *>(smem + oTot);
     float *sGam = reinterpret_cast<float *>(smem + oGam), *sDG = reinterpret_cast<float *>(smem + oDG);
     float *sScr = reinterpret_cast<float *>(smem + oScr);
+    float *sRed = reinterpret_cast<float *>(smem + oRed);
     __bf16 *sTs = reinterpret_cast<__bf16 *>(smem + oTs);
 
     const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const int tk = t0 + 16 * w + r;
     const bool vk = tk < T;
     const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
+    const size_t srowK = baseK / DK + (size_t)(vk ? tk : T - 1) * H;   // per-token gate offset (SG)
     const int chh = hf * (DK / 2);               // first key channel of this half
     auto ch = [&](int e) { return chh + ch4(e, g); };
 
@@ -136,14 +139,16 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 16 * w + 4 * g + i;
             const size_t off = baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + 16 * n + r;
+            const size_t offw = (SG && (a.scalar & kScalarWrite)) ? baseK / DK + (size_t)(t < T ? t : T - 1) * H
+                                                                   : off;
             x.v[i] = load1<BF16>(a.v, off, true);
-            x.wg[i] = load_gate1<GL>(a.wg, off);   // as stored (activated at use)
+            x.wg[i] = load_gate1<GL>(a.wg, offw);   // as stored (activated at use)
         }
     };
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
-    KeyRaw4<DK / 2, BF16, GL> raw;
-    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
+    KeyRaw4<DK / 2, BF16, GL, SG> raw;
+    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk, srowK, a.scalar);
     Tile cur;
     load_tile(0, cur, tid);
 
@@ -242,6 +247,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     for (int m = 0; m < NMH; ++m) aQ[m] = aE[m] = aH[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) aPA[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float pw[4] = {0.f, 0.f, 0.f, 0.f};          // per-token dw partial sums (write gate per token)
     float dgp[NSF];
 #pragma unroll
     for (int it = 0; it < NSF; ++it) dgp[it] = 0.f;
@@ -345,10 +351,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 16 * w + 4 * g + i;
+            if (SG && (a.scalar & kScalarWrite)) pw[i] += dXr[i] * vD[i];
             if (t < T) {
                 const size_t off = baseV0 + (size_t)t * tokV + j0 + 16 * n + r;
                 a.dv[off] = dXr[i] * wD[i];
-                a.dw[off] = dXr[i] * vD[i] * gate_dact<GL>(wD[i]);
+                if (!(SG && (a.scalar & kScalarWrite))) a.dw[off] = dXr[i] * vD[i] * gate_dact<GL>(wD[i]);
             }
         }
         __syncthreads();
@@ -403,8 +410,31 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const int tk = t0 + 16 * w + r;
     const bool vk = tk < T;
     const size_t rowK = baseK + (size_t)(vk ? tk : T - 1) * tokK;
+    const size_t srowK = baseK / DK + (size_t)(vk ? tk : T - 1) * H;
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
+    // a per-token gate's gradient is the sum over its channels: sum this lane's part, then
+    // over the lanes of the token (shuffles) and over the two halves (LDS)
+    auto lane_sum16 = [](float x) {   // over the 16 lanes of a row
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        return x;
+    };
+    auto group_sum4 = [](float x) {   // over g: lanes r, r + 16, r + 32, r + 48
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        return x;
+    };
+    if (SG && (a.scalar & kScalarWrite)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[i] = lane_sum16(pw[i]);   // tokens 16w + 4g + i, columns of half hf
+        if (hf == 1 && r == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sRed[2 * kChunk + 16 * w + 4 * g + i] = pw[i];
+        }
+    }
 #pragma unroll
     for (int it = 0; it < NSF; ++it) {
         const int idx = tid + NTH * it;
@@ -428,7 +458,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
-    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk);
+    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk, srowK, a.scalar);
     raw.unpack(qf, kf, G, bgf);
     float dact[NEH];               // d log_alpha / d stored decay input
     raw.decay_dact_all(dact);
@@ -448,6 +478,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     __syncthreads();
+    if (SG && (a.scalar & kScalarWrite) && hf == 0 && r == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * w + 4 * g + i;
+            if (t < T) a.dw[baseK / DK + (size_t)t * H] = pw[i] + sRed[2 * kChunk + 16 * w + 4 * g + i];
+        }
+    }
     if (tid < DK) {
         float sacc = 0.f;
 #pragma unroll
@@ -481,6 +518,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 
     // ---- element-wise chain (token 16w + r, channels ch(e)) ----
     float xg[NEH], yh[NEH];
+    float sb = 0.f;                // per-token db partial (erase gate per token)
     {
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
@@ -499,11 +537,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 xg[e] = dQt * Qt + dEt * Et - (dKt + dHg) * Kt;
                 yh[e] = dHg * Kt;
             }
+            if (SG && (a.scalar & kScalarErase)) sb += (vb[0] + vb[1]) + (vb[2] + vb[3]);
             if (vk) {
                 const size_t off = rowK + chh + 16 * mm + 4 * g;
                 *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
                 *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
-                *reinterpret_cast<f32x4 *>(a.db + off) = vb;
+                if (!(SG && (a.scalar & kScalarErase))) *reinterpret_cast<f32x4 *>(a.db + off) = vb;
             }
         }
     }
@@ -511,19 +550,30 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float xin[NEH], xtot[NEH], ytot[NEH];
 #pragma unroll
     for (int e = 0; e < NEH; ++e) xin[e] = xg[e];
+    if (SG && (a.scalar & kScalarErase)) {
+        sb = group_sum4(sb);
+        if (hf == 1 && g == 0) sRed[16 * w + r] = sb;
+    }
     chunk_scan<NEH, DK>(xin, xtot, reinterpret_cast<float *>(smem + oTotA), w, r, ch);
+    if (SG && (a.scalar & kScalarErase) && hf == 0 && g == 0 && vk) a.db[srowK] = sb + sRed[16 * w + r];
     chunk_scan<NEH, DK>(yh, ytot, reinterpret_cast<float *>(smem + oTotB), w, r, ch);
-    if (vk) {
+    float sl = 0.f;                // per-token dlog_alpha partial (decay per token)
 #pragma unroll
-        for (int mm = 0; mm < NMH; ++mm) {
-            f32x4 vl;
+    for (int mm = 0; mm < NMH; ++mm) {
+        f32x4 vl;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * mm + i;
-                vl[i] = ((xtot[e] - xin[e] + xg[e]) + ytot[e] + sDG[ch(e)] * sGam[ch(e)]) * dact[e];
-            }
-            *reinterpret_cast<f32x4 *>(a.dla + rowK + chh + 16 * mm + 4 * g) = vl;
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * mm + i;
+            vl[i] = ((xtot[e] - xin[e] + xg[e]) + ytot[e] + sDG[ch(e)] * sGam[ch(e)]) * dact[e];
         }
+        if (SG && (a.scalar & kScalarDecay)) sl += (vl[0] + vl[1]) + (vl[2] + vl[3]);
+        else if (vk) *reinterpret_cast<f32x4 *>(a.dla + rowK + chh + 16 * mm + 4 * g) = vl;
+    }
+    if (SG && (a.scalar & kScalarDecay)) {
+        sl = group_sum4(sl);
+        if (hf == 1 && g == 0) sRed[kChunk + 16 * w + r] = sl;
+        __syncthreads();
+        if (hf == 0 && g == 0 && vk) a.dla[srowK] = sl + sRed[kChunk + 16 * w + r];
     }
   }
 }
@@ -531,28 +581,30 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <int DK, bool BF16, bool GL>
+template <int DK, bool BF16, bool GL, bool SG>
 static hipError_t chunk_t(const BwdArgs &a, hipStream_t st) {
     const int NC = (a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads),
+                       0, st, a);
     return hipGetLastError();
 }
 
-template <bool BF16, bool GL>
+template <bool BF16, bool GL, bool SG>
 static hipError_t chunk_dk(const BwdArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return chunk_t<32, BF16, GL>(a, st);
-        case 64: return chunk_t<64, BF16, GL>(a, st);
-        case 128: return chunk_t<128, BF16, GL>(a, st);
+        case 32: return chunk_t<32, BF16, GL, SG>(a, st);
+        case 64: return chunk_t<64, BF16, GL, SG>(a, st);
+        case 128: return chunk_t<128, BF16, GL, SG>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st) {
+hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
     if (a.DV % 32 != 0) return hipErrorInvalidValue;
-    if (gl) return bf16 ? chunk_dk<true, true>(a, dk, st) : hipErrorInvalidValue;
-    return bf16 ? chunk_dk<true, false>(a, dk, st) : chunk_dk<false, false>(a, dk, st);
+    if (gl && sg) return hipErrorInvalidValue;
+    if (gl) return bf16 ? chunk_dk<true, true, false>(a, dk, st) : hipErrorInvalidValue;
+    if (sg) return bf16 ? chunk_dk<true, false, true>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? chunk_dk<true, false, false>(a, dk, st) : chunk_dk<false, false, false>(a, dk, st);
 }
 
 }  // namespace gdn2

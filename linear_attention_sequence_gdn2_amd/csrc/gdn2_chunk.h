@@ -237,8 +237,9 @@ __device__ __forceinline__ Split8 split8v(const f32x4 &a, const f32x4 &b) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int ch4(int e, int g) { return 16 * (e >> 2) + 4 * g + (e & 3); }
 
-// key-side inputs of one token for the 4-group layout; GL: log_alpha and b are bf16 logits
-template <int DK, bool BF16, bool GL = false>
+// key-side inputs of one token for the 4-group layout; GL: log_alpha and b are bf16 logits;
+// SG: log_alpha and/or b may be given per token (broadcast over the channels)
+template <int DK, bool BF16, bool GL = false, bool SG = false>
 struct KeyRaw4 {
     static constexpr int NM = DK / 16;
     uint2 q[NM], k[NM];
@@ -247,10 +248,16 @@ struct KeyRaw4 {
     uint2 la16[NM], bg16[NM];       // bf16 gate logits
     bool valid;
 
-    // q, k: qkv dtype; rowoff: element offset of channel 0 of the token row
+    // q, k: qkv dtype; rowoff: element offset of channel 0 of the token row; srow: the
+    // token's offset in per-token gate tensors; scalar: kScalar* bits (SG only)
     __device__ __forceinline__ void issue(const void *qp, const void *kp, const void *lap, const void *bgp,
-                                          size_t rowoff, int g, bool v) {
+                                          size_t rowoff, int g, bool v, size_t srow = 0, int scalar = 0) {
         valid = v;
+        float sla = 0.f, sbg = 0.f;
+        if (SG) {
+            sla = reinterpret_cast<const float *>(lap)[(scalar & 1) ? srow : rowoff];
+            sbg = reinterpret_cast<const float *>(bgp)[(scalar & 2) ? srow : rowoff];
+        }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const size_t off = rowoff + 16 * m + 4 * g;
@@ -264,6 +271,11 @@ struct KeyRaw4 {
             if (GL) {
                 la16[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(lap) + off);
                 bg16[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(bgp) + off);
+            } else if (SG) {
+                la[m] = (scalar & 1) ? make_float4(sla, sla, sla, sla)
+                                     : *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(lap) + off);
+                bg[m] = (scalar & 2) ? make_float4(sbg, sbg, sbg, sbg)
+                                     : *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(bgp) + off);
             } else {
                 la[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(lap) + off);
                 bg[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(bgp) + off);

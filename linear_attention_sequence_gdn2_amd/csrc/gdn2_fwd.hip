@@ -36,7 +36,7 @@ namespace gdn2 {
 // above this point (bounds the live registers so two workgroups fit on a CU).
 #define GDN2_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <int DK, int VT, bool BF16, bool FAST, bool OUT, bool STATES, bool GL>
+template <int DK, int VT, bool BF16, bool FAST, bool OUT, bool STATES, bool GL, bool SG>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     constexpr int NKS = DK / 32;           // 32-channel contraction steps
     constexpr int NVT = VT / 16;           // 16-column value tiles
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         const int tk = t0 + 16 * w + r;
         const bool vk = tk < T;
         const size_t offk = baseK + (size_t)(vk ? tk : T - 1) * tokK + 8 * g;
+        const size_t offs = baseK / DK + (size_t)(vk ? tk : T - 1) * H;   // the token's per-token gate (SG)
         uint4 qraw[NKS], kraw[NKS];            // bf16 q, k (8 channels per uint4)
         float4 qx[NKS][2], kx[NKS][2];         // fp32 q, k
         float4 la4[NKS][2], bg4[NKS][2];       // fp32 gate values
@@ -136,6 +137,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             if (GL) {
                 la8[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.la) + o);
                 bg8[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.bg) + o);
+            } else if (SG) {
+                // a gate given per token is broadcast over the key channels
+                if (a.scalar & kScalarDecay) {
+                    const float x = reinterpret_cast<const float *>(a.la)[offs];
+                    la4[j][0] = la4[j][1] = make_float4(x, x, x, x);
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        la4[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.la) + o)[hh];
+                }
+                if (a.scalar & kScalarErase) {
+                    const float x = reinterpret_cast<const float *>(a.bg)[offs];
+                    bg4[j][0] = bg4[j][1] = make_float4(x, x, x, x);
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        bg4[j][hh] = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.bg) + o)[hh];
+                }
             } else {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
@@ -285,7 +304,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int tv = t0 + 16 * w + 4 * g + i;
                 const size_t off = baseV + (size_t)(tv < T ? tv : T - 1) * tokV + 16 * n + r;
-                const float zz = gate_act<GL>(load_gate1<GL>(a.wg, off)) * load1<BF16>(a.v, off, true);
+                const size_t offw = (SG && (a.scalar & kScalarWrite)) ? baseK / DK + (size_t)(tv < T ? tv : T - 1) * H
+                                                                       : off;
+                const float zz = gate_act<GL>(load_gate1<GL>(a.wg, offw)) * load1<BF16>(a.v, off, true);
                 z[n][i] = tv < T ? zz : 0.f;
             }
         // ---- X = Z - Et S and Qt S for this wave's rows (S from LDS) ----
@@ -407,48 +428,51 @@ int fwd_value_tile(int B, int H, int dk, int dv) {
     return vt;
 }
 
-template <int DK, int VT, bool BF16, bool GL, int MODE>
+template <int DK, int VT, bool BF16, bool GL, bool SG, int MODE>
 static hipError_t launch_t(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * a.nvt)), block(kThreads);
     constexpr bool OUT = MODE != kFwdStates, STATES = MODE != kFwdOut;
-    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, OUT, STATES, GL>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, OUT, STATES, GL, SG>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int DK, bool BF16, bool GL, int MODE>
+template <int DK, bool BF16, bool GL, bool SG, int MODE>
 static hipError_t launch_vt(const FwdArgs &a, int vt, hipStream_t st) {
     if constexpr (DK >= 64) {
-        if (vt == 16) return launch_t<DK, 16, BF16, GL, MODE>(a, st);
+        if (vt == 16) return launch_t<DK, 16, BF16, GL, SG, MODE>(a, st);
     }
-    if (vt == 32) return launch_t<DK, 32, BF16, GL, MODE>(a, st);
-    if (vt == 64) return launch_t<DK, 64, BF16, GL, MODE>(a, st);
+    if (vt == 32) return launch_t<DK, 32, BF16, GL, SG, MODE>(a, st);
+    if (vt == 64) return launch_t<DK, 64, BF16, GL, SG, MODE>(a, st);
     return hipErrorInvalidValue;
 }
 
-template <bool BF16, bool GL, int MODE>
+template <bool BF16, bool GL, bool SG, int MODE>
 static hipError_t launch_dk(const FwdArgs &a, int dk, int vt, hipStream_t st) {
     switch (dk) {
-        case 32: return launch_vt<32, BF16, GL, MODE>(a, vt, st);
-        case 64: return launch_vt<64, BF16, GL, MODE>(a, vt, st);
-        case 128: return launch_vt<128, BF16, GL, MODE>(a, vt, st);
+        case 32: return launch_vt<32, BF16, GL, SG, MODE>(a, vt, st);
+        case 64: return launch_vt<64, BF16, GL, SG, MODE>(a, vt, st);
+        case 128: return launch_vt<128, BF16, GL, SG, MODE>(a, vt, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool BF16, bool GL>
+template <bool BF16, bool GL, bool SG>
 static hipError_t launch_mode(const FwdArgs &a, int dk, int vt, FwdMode mode, hipStream_t st) {
     switch (mode) {
-        case kFwdOut: return launch_dk<BF16, GL, kFwdOut>(a, dk, vt, st);
-        case kFwdStates: return launch_dk<BF16, GL, kFwdStates>(a, dk, vt, st);
-        case kFwdOutStates: return launch_dk<BF16, GL, kFwdOutStates>(a, dk, vt, st);
+        case kFwdOut: return launch_dk<BF16, GL, SG, kFwdOut>(a, dk, vt, st);
+        case kFwdStates: return launch_dk<BF16, GL, SG, kFwdStates>(a, dk, vt, st);
+        case kFwdOutStates: return launch_dk<BF16, GL, SG, kFwdOutStates>(a, dk, vt, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, FwdMode mode, hipStream_t st) {
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode, hipStream_t st) {
     if (!vt_ok(dk, vt, a.dv)) return hipErrorInvalidValue;
-    if (gl) return bf16 ? launch_mode<true, true>(a, dk, vt, mode, st) : hipErrorInvalidValue;
-    return bf16 ? launch_mode<true, false>(a, dk, vt, mode, st) : launch_mode<false, false>(a, dk, vt, mode, st);
+    if (gl && sg) return hipErrorInvalidValue;
+    if (gl) return bf16 ? launch_mode<true, true, false>(a, dk, vt, mode, st) : hipErrorInvalidValue;
+    if (sg) return bf16 ? launch_mode<true, false, true>(a, dk, vt, mode, st) : hipErrorInvalidValue;
+    return bf16 ? launch_mode<true, false, false>(a, dk, vt, mode, st)
+                : launch_mode<false, false, false>(a, dk, vt, mode, st);
 }
 
 }  // namespace gdn2

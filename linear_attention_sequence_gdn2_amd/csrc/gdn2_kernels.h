@@ -7,6 +7,9 @@
 
 namespace gdn2 {
 
+// Gates given as one value per token (broadcast over their channels), a bit each.
+constexpr int kScalarDecay = 1, kScalarErase = 2, kScalarWrite = 4;
+
 // Arguments of the chunked forward sweep.  Token tensors are [B,T,H,D]
 // contiguous; states [B,H,dk,dv] fp32; chunk states [B,H,NC,dk,dv] fp32.
 struct FwdArgs {
@@ -18,6 +21,7 @@ struct FwdArgs {
     float *states;                  // chunk-start states (state sweep) or null
     int B, T, H, dv;
     int nvt;                        // value tiles per (b, h) = dv / value-tile width
+    int scalar;                     // kScalar* bits: gates given per token [B,T,H]
 };
 
 // Arguments of the backward kernels.
@@ -30,6 +34,7 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dla, *db, *dw, *dS0;
     void *factors;                  // [B,H,NC] per-chunk adjoint factors (bf16 tiles)
     int B, T, H, DV;
+    int scalar;                     // kScalar* bits: gates (and their gradients) per token [B,T,H]
 };
 
 // Arguments of the recurrent step (one token per (batch, head)); token tensors [BH, D].
@@ -40,8 +45,10 @@ struct StepArgs {
     float *S_out;                   // may equal S_in
     float *o;
     int BH, dv;
+    int scalar;                     // kScalar* bits: gates given per (batch, head) [B,H]
 };
-hipError_t launch_step(const StepArgs &a, int dk, bool bf16, bool gl, hipStream_t st);
+// sg: some gates are given per token (a.scalar), only with bf16 q/k/v and fp32 gate values
+hipError_t launch_step(const StepArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 
 // Compute units of the current device (256 if the runtime cannot tell).
 inline int cu_count() {
@@ -57,10 +64,11 @@ int fwd_value_tile(int B, int H, int dk, int dv);
 
 // What a forward sweep produces: o only, chunk states only, or both.
 enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
-// gl: the gates are bf16 logits (only with bf16 q/k/v)
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, FwdMode mode, hipStream_t st);
-hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st);
+// gl: the gates are bf16 logits (only with bf16 q/k/v); sg: some gates are given per token
+// (a.scalar; only with bf16 q/k/v and fp32 gate values)
+hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode, hipStream_t st);
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st);
-hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st);
+hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 
 }  // namespace gdn2

@@ -57,7 +57,7 @@ __device__ __forceinline__ Split8 frag_from_tiles(const uint4 &t0, const uint4 &
 // ---------------------------------------------------------------------------
 // Eight waves in two halves, as in bwd_chunk_kernel: wave (hf, w) owns tokens
 // 16w..16w+15 and, for the element work, the channels of half hf.
-template <int DK, bool BF16, bool GL>
+template <int DK, bool BF16, bool GL, bool SG>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
@@ -99,11 +99,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 
     // Persistent: the workgroup walks items blockIdx.x, + gridDim.x, ...; the key-side
     // inputs of the next item are loaded while the current one is in its products.
-    KeyRaw4<DK / 2, BF16, GL> raw;
+    KeyRaw4<DK / 2, BF16, GL, SG> raw;
     {
         bool v0;
         const size_t row0 = item_row(blockIdx.x < nitems ? blockIdx.x : 0, v0);
-        raw.issue(a.q, a.k, a.la, a.bg, row0, g, v0);
+        raw.issue(a.q, a.k, a.la, a.bg, row0, g, v0, (row0 - chh) / DK, a.scalar);
     }
     for (int L = blockIdx.x; L < nitems; L += gridDim.x) {
     // lane indices afresh from an opaque copy of the thread index: the address
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
             const int Ln = L + (int)gridDim.x < nitems ? L + (int)gridDim.x : L;
             bool vn;
             const size_t rown = item_row(Ln, vn);
-            raw.issue(a.q, a.k, a.la, a.bg, rown, g, vn);
+            raw.issue(a.q, a.k, a.la, a.bg, rown, g, vn, (rown - chh) / DK, a.scalar);
         }
 #pragma unroll
         for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
@@ -417,28 +417,30 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <int DK, bool BF16, bool GL>
+template <int DK, bool BF16, bool GL, bool SG>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
     const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);
     // one persistent workgroup per CU (the kernel's LDS allows no second one)
     const long grid = items < cu_count() ? items : cu_count();
-    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL, SG>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <bool BF16, bool GL>
+template <bool BF16, bool GL, bool SG>
 static hipError_t factors_dk(const BwdArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return factors_t<32, BF16, GL>(a, st);
-        case 64: return factors_t<64, BF16, GL>(a, st);
-        case 128: return factors_t<128, BF16, GL>(a, st);
+        case 32: return factors_t<32, BF16, GL, SG>(a, st);
+        case 64: return factors_t<64, BF16, GL, SG>(a, st);
+        case 128: return factors_t<128, BF16, GL, SG>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, hipStream_t st) {
-    if (gl) return bf16 ? factors_dk<true, true>(a, dk, st) : hipErrorInvalidValue;
-    return bf16 ? factors_dk<true, false>(a, dk, st) : factors_dk<false, false>(a, dk, st);
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
+    if (gl && sg) return hipErrorInvalidValue;
+    if (gl) return bf16 ? factors_dk<true, true, false>(a, dk, st) : hipErrorInvalidValue;
+    if (sg) return bf16 ? factors_dk<true, false, true>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? factors_dk<true, false, false>(a, dk, st) : factors_dk<false, false, false>(a, dk, st);
 }
 
 template <int DK, int VT>

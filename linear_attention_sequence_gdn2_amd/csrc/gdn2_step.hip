@@ -18,7 +18,7 @@
 
 namespace gdn2 {
 
-template <int DK, bool BF16, bool GL>
+template <int DK, bool BF16, bool GL, bool SG>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     constexpr int VT = 32, NS = kThreads / VT, RPS = DK / NS;   // slices, rows per slice
     __shared__ float sAlpha[DK], sE[DK], sK[DK], sQ[DK];
@@ -30,10 +30,14 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     const size_t kbase = (size_t)bh * DK, vbase = (size_t)bh * a.dv + vt * VT;
     const size_t sbase = (size_t)bh * DK * a.dv + vt * VT;
 
+    // a per-token gate (SG) is one value per (batch, head), broadcast over its channels
+    const size_t offa = (SG && (a.scalar & kScalarDecay)) ? (size_t)bh : kbase + tid;
+    const size_t offb = (SG && (a.scalar & kScalarErase)) ? (size_t)bh : kbase + tid;
+    const size_t offw = (SG && (a.scalar & kScalarWrite)) ? (size_t)bh : vbase + j;
     if (tid < DK) {
         const float kk = load1<BF16>(a.k, kbase + tid, true);
-        sAlpha[tid] = exp2_fast(decay_act<GL>(load_gate1<GL>(a.la, kbase + tid)) * kLog2e);
-        sE[tid] = gate_act<GL>(load_gate1<GL>(a.bg, kbase + tid)) * kk;
+        sAlpha[tid] = exp2_fast(decay_act<GL>(load_gate1<GL>(a.la, offa)) * kLog2e);
+        sE[tid] = gate_act<GL>(load_gate1<GL>(a.bg, offb)) * kk;
         sK[tid] = kk;
         sQ[tid] = load1<BF16>(a.q, kbase + tid, true);
     }
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int i = 0; i < RPS; ++i)
         x[i] = a.S_in ? a.S_in[sbase + (size_t)(s * RPS + i) * a.dv + j] : 0.f;
-    const float z = gate_act<GL>(load_gate1<GL>(a.wg, vbase + j)) * load1<BF16>(a.v, vbase + j, true);
+    const float z = gate_act<GL>(load_gate1<GL>(a.wg, offw)) * load1<BF16>(a.v, vbase + j, true);
     __syncthreads();
 
     // decay, then the read through the erase key
@@ -77,26 +81,28 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     }
 }
 
-template <int DK, bool BF16, bool GL>
+template <int DK, bool BF16, bool GL, bool SG>
 static hipError_t step_t(const StepArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((step_kernel<DK, BF16, GL>), dim3((unsigned)(a.BH * (a.dv / 32))), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((step_kernel<DK, BF16, GL, SG>), dim3((unsigned)(a.BH * (a.dv / 32))), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <bool BF16, bool GL>
+template <bool BF16, bool GL, bool SG>
 static hipError_t step_dk(const StepArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return step_t<32, BF16, GL>(a, st);
-        case 64: return step_t<64, BF16, GL>(a, st);
-        case 128: return step_t<128, BF16, GL>(a, st);
+        case 32: return step_t<32, BF16, GL, SG>(a, st);
+        case 64: return step_t<64, BF16, GL, SG>(a, st);
+        case 128: return step_t<128, BF16, GL, SG>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_step(const StepArgs &a, int dk, bool bf16, bool gl, hipStream_t st) {
+hipError_t launch_step(const StepArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
     if (a.dv % 32 != 0) return hipErrorInvalidValue;
-    if (gl) return bf16 ? step_dk<true, true>(a, dk, st) : hipErrorInvalidValue;
-    return bf16 ? step_dk<true, false>(a, dk, st) : step_dk<false, false>(a, dk, st);
+    if (gl && sg) return hipErrorInvalidValue;
+    if (gl) return bf16 ? step_dk<true, true, false>(a, dk, st) : hipErrorInvalidValue;
+    if (sg) return bf16 ? step_dk<true, false, true>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? step_dk<true, false, false>(a, dk, st) : step_dk<false, false, false>(a, dk, st);
 }
 
 }  // namespace gdn2

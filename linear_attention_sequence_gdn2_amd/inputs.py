@@ -17,7 +17,13 @@ section "Ablations and training throughput", Figure 2):
 * gates ``"channel"``: b = sigmoid(N(0,1)) per key channel, w = sigmoid(N(0,1))
   per value channel.  ``"kda"``: one beta = sigmoid(N(0,1)) per (b,t,h),
   broadcast to b and w.  ``"gdn"``: as ``"kda"`` and log_alpha drawn once per
-  (b,t,h) and broadcast over key channels.
+  (b,t,h) and broadcast over key channels.  The gate ablations (blog section
+  "Ablations and training throughput"): ``"erase_mean"`` / ``"write_mean"`` draw as
+  ``"channel"`` and replace b (resp. w) by its mean over the channels;
+  ``"erase2"`` draws as ``"channel"`` with b = 2 * sigmoid(N(0,1)) in [0, 2].
+* ``token_gates=True``: a gate that is one value per (b,t,h) is returned as a
+  [B, T, H] tensor instead of being broadcast over its channels, and
+  ``gate_scalar`` holds its bits (1 decay, 2 erase, 4 write).
 * S0 ~ N(0, s0_std) (zeros when s0_std == 0), dO ~ N(0, 1), dS_final ~ N(0, 0.01).
 * ``gate_logits=True`` (channel gates, log-sigmoid decay): the same normal draws are
   returned before their activation, rounded to bf16, as ``x_a`` = N(3,1), ``x_b``,
@@ -71,11 +77,14 @@ WORKLOADS = {
     # the training shape with the gates given as bf16 logits (activated in the kernels)
     "logits_bf16_B8H16T2048d128": Workload("logits_bf16_B8H16T2048d128", 8, 2048, 16, 128, 128, 1006,
                                            grads=True, extra={"gate_logits": True}),
+    # the training shape with Gated DeltaNet's gates given once per token ([B,T,H])
+    "gdn_token_bf16_B8H16T2048d128": Workload("gdn_token_bf16_B8H16T2048d128", 8, 2048, 16, 128, 128, 1007,
+                                              gates="gdn", grads=True, extra={"token_gates": True}),
 }
 
 
 def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", gates="channel",
-                s0_std=0.0, grads=False, gate_logits=False):
+                s0_std=0.0, grads=False, gate_logits=False, token_gates=False):
     """Return a dict of CPU tensors.
 
     ``q``, ``k``, ``v`` have dtype bf16 (or fp32 when ``qkv_dtype == "f32"``);
@@ -114,15 +123,32 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
 
     if gate_logits:
         pass
-    elif gates == "channel":
+    elif gates in ("channel", "erase_mean", "write_mean", "erase2"):
         b = torch.sigmoid(randn(*shp_k))
         w = torch.sigmoid(randn(*shp_v))
+        if gates == "erase_mean":
+            b = b.mean(dim=-1, keepdim=True).expand(shp_k).contiguous()
+        elif gates == "write_mean":
+            w = w.mean(dim=-1, keepdim=True).expand(shp_v).contiguous()
+        elif gates == "erase2":
+            b = 2.0 * b
     elif gates in ("kda", "gdn"):
         beta = torch.sigmoid(randn(B, T, H, 1))
         b = beta.expand(shp_k).contiguous()
         w = beta.expand(shp_v).contiguous()
     else:
         raise ValueError(gates)
+    scalar = 0
+    if token_gates:
+        if gate_logits:
+            raise ValueError("per-token gates are fp32 values")
+        scalar = {"gdn": 7, "kda": 6, "erase_mean": 2, "write_mean": 4}.get(gates, 0)
+        if scalar & 1:
+            la = la[..., 0]
+        if scalar & 2:
+            b = b[..., 0]
+        if scalar & 4:
+            w = w[..., 0]
 
     if s0_std > 0:
         S0 = randn(B, H, dk, dv) * s0_std
@@ -144,7 +170,7 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
     if gate_logits:
         out.update(log_alpha=x_a.contiguous(), b=x_b.contiguous(), w=x_w.contiguous(), S0=S0, gate_logits=True)
     else:
-        out.update(log_alpha=la.contiguous(), b=b.contiguous(), w=w.contiguous(), S0=S0)
+        out.update(log_alpha=la.contiguous(), b=b.contiguous(), w=w.contiguous(), S0=S0, gate_scalar=scalar)
 
     if grads:
         out["dO"] = randn(*shp_v)
@@ -155,6 +181,6 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
 def make_workload(wl: Workload, **override):
     kw = dict(B=wl.B, T=wl.T, H=wl.H, dk=wl.dk, dv=wl.dv, seed=wl.seed, qkv_dtype=wl.qkv_dtype,
               decay=wl.decay, gates=wl.gates, s0_std=wl.s0_std, grads=wl.grads,
-              gate_logits=wl.extra.get("gate_logits", False))
+              gate_logits=wl.extra.get("gate_logits", False), token_gates=wl.extra.get("token_gates", False))
     kw.update(override)
     return make_inputs(**kw)

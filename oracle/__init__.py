@@ -152,3 +152,35 @@ def logit_grads(x_a, x_b, x_w, grads):
     out["db"] = grads["db"] * sb * (1.0 - sb)
     out["dw"] = grads["dw"] * sw * (1.0 - sw)
     return out
+
+
+# Gates given per token.  The rule's special cases use one value per (batch, token,
+# head) for a gate: one beta for both the erase and the write gate (KDA), a scalar
+# decay as well (Gated DeltaNet) -- blog on Gated DeltaNet-2, section "Independent
+# control on two axes"; the gate ablations replace the erase or the write gate by its
+# mean over the channels (same blog, section "Ablations and training throughput").  A
+# per-token gate g[b,t,h] is the per-channel gate g[b,t,h] * ones(D); by the chain rule
+# its gradient is the sum over the D channels of the per-channel gradient.
+SCALAR_DECAY, SCALAR_ERASE, SCALAR_WRITE = 1, 2, 4
+_SCALAR_GATES = (("log_alpha", "dlog_alpha", SCALAR_DECAY), ("b", "db", SCALAR_ERASE), ("w", "dw", SCALAR_WRITE))
+
+
+def gates_per_token(log_alpha, b, w, dk, dv, scalar):
+    """Per-channel float64 gates from gates of which those flagged in `scalar`
+    (SCALAR_* bits) are [B, T, H] (one value per token)."""
+    out = []
+    for (name, _, bit), g, d in zip(_SCALAR_GATES, (log_alpha, b, w), (dk, dk, dv)):
+        g = _f64(g)
+        out.append(np.repeat(g[..., None], d, axis=-1) if scalar & bit else g)
+    return tuple(out)
+
+
+def per_token_grads(grads, scalar):
+    """Gradients w.r.t. the per-token gates flagged in `scalar`, from the oracle's
+    per-channel gradients (a dict as returned by bwd): summed over the channel axis."""
+    out = dict(grads)
+    for _, gname, bit in _SCALAR_GATES:
+        if scalar & bit:
+            out[gname] = grads[gname].sum(axis=-1)
+    return out
+

@@ -36,8 +36,18 @@ def test_every_declared_symbol_is_exported():
     assert sorted(names) == sorted(gdn2.EXPORTS)
 
 
-def _shape(B=2, T=100, H=3, dk=128, dv=64, chunk=64, dt=1, gates=0):
-    return gdn2.Gdn2Shape(B, T, H, dk, dv, chunk, dt, gates)
+def _shape(B=2, T=100, H=3, dk=128, dv=64, chunk=64, dt=1, gates=0, scalar=0):
+    return gdn2.Gdn2Shape(B, T, H, dk, dv, chunk, dt, gates, scalar)
+
+
+def test_shape_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} gdn2_shape;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = [f.strip() for decl in body.split(";") if decl.strip()
+              for f in decl.strip()[len("int "):].split(",")]
+    assert fields == [f[0] for f in gdn2.Gdn2Shape._fields_]
+    assert ctypes.sizeof(gdn2.Gdn2Shape) == 4 * len(fields)
 
 
 def test_workspace_and_state_sizes():
@@ -59,6 +69,7 @@ def test_workspace_and_state_sizes():
     (dict(chunk=32), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED), (dict(B=1 << 14, T=1 << 14, H=16), UNSUPPORTED),
     (dict(gates=2), UNSUPPORTED), (dict(gates=1, dt=0), UNSUPPORTED),
+    (dict(scalar=8), UNSUPPORTED), (dict(scalar=1, dt=0), UNSUPPORTED), (dict(scalar=6, gates=1), UNSUPPORTED),
 ])
 def test_shape_checks(kw, code):
     lib = gdn2.load()
@@ -86,6 +97,21 @@ def test_misaligned_pointer_rejected():
     fake, odd = P(0x10000), P(0x10008)
     assert lib.gdn2_chunk_fwd(ctypes.byref(s), fake, odd, fake, fake, fake, fake, None, fake, None, None, 0,
                               None) == INVALID
+
+
+def test_per_token_gates_need_only_word_alignment():
+    """A per-token gate may sit at any 4-byte address; the others still need 16 bytes."""
+    lib = gdn2.load()
+    f, word, odd = P(0x10000), P(0x10004), P(0x10002)
+    s = _shape(scalar=1)   # log_alpha per token
+    # a gate that is not per token and is only word-aligned is rejected before any launch
+    assert lib.gdn2_chunk_fwd(ctypes.byref(s), f, f, f, f, word, f, None, f, None, None, 0, None) == INVALID
+    assert lib.gdn2_chunk_fwd(ctypes.byref(s), f, f, f, odd, f, f, None, f, None, None, 0, None) == INVALID
+    g = [f] * 6 + [f] * 3 + [f] * 3
+    g[9] = odd   # dlog_alpha per token, not word aligned
+    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), *g[:6], *g[6:9], f, f, f, *g[9:], None) == INVALID
+    s = _shape(T=1, scalar=4)   # w per token in a step; b misaligned
+    assert lib.gdn2_step(ctypes.byref(s), f, f, f, f, word, word, None, f, f, None) == INVALID
 
 
 def test_backward_workspace_checked_before_launch():

@@ -1,0 +1,145 @@
+"""GPU parity with gates given per token ([B, T, H] tensors, gdn2_shape.gate_scalar).
+
+The special cases of the rule use one value per (batch, token, head) for a gate:
+KDA one beta for both gates, Gated DeltaNet a scalar decay as well; the gate
+ablations use the channel mean of the erase or the write gate, or an erase gate in
+[0, 2].  The kernels broadcast a per-token gate over its channels and return its
+gradient summed over them.  The reference is the fp64 oracle on the broadcast
+gates (oracle.gates_per_token) with its gradients summed over the channels
+(oracle.per_token_grads; both pinned in test_oracle_pins).  Tolerances as for bf16
+inputs: 3e-3 forward, 5e-3 gradients (max-norm relative)."""
+import pytest
+import torch
+
+import oracle
+import linear_attention_sequence_gdn2_amd as gdn2
+from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_inputs, make_workload
+from _util import rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"]
+
+
+def _oracle_inputs(inp):
+    dk, dv = inp["q"].shape[-1], inp["v"].shape[-1]
+    g = oracle.gates_per_token(inp["log_alpha"], inp["b"], inp["w"], dk, dv, inp["gate_scalar"])
+    return [inp["q32"], inp["k32"], inp["v32"], *g, inp["S0"]]
+
+
+def _check_fwd(inp, o, sf):
+    o_ref, sf_ref = oracle.fwd(*_oracle_inputs(inp))
+    eo, es = rel_err(o, o_ref), rel_err(sf, sf_ref)
+    print("token gates %d: o err %.3e  S_final err %.3e" % (inp["gate_scalar"], eo, es))
+    assert eo < 3e-3 and es < 3e-3, (eo, es)
+
+
+def _check_bwd(inp, g):
+    ref = oracle.per_token_grads(oracle.bwd(*_oracle_inputs(inp), inp["dO"], inp["dS_final"]), inp["gate_scalar"])
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e < 5e-3}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("gates,B,T,H,dk,dv,s0", [
+    ("gdn", 1, 1, 1, 32, 32, 0.5),
+    ("kda", 2, 65, 2, 64, 128, 0.3),
+    ("gdn", 1, 200, 3, 128, 128, 0.02),
+    ("erase_mean", 2, 130, 1, 128, 32, 0.0),
+    ("write_mean", 1, 100, 2, 64, 64, 0.1),
+    ("gdn", 2, 64, 1, 128, 64, 0.2),
+])
+def test_token_gates_fwd_bwd(gates, B, T, H, dk, dv, s0):
+    inp = make_inputs(B, T, H, dk, dv, seed=8300 + T + dk, gates=gates, s0_std=s0, grads=True, token_gates=True)
+    assert inp["gate_scalar"] != 0
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o, sf = gdn2.fwd(*args, d["S0"])
+    g = gdn2.bwd(*args, d["S0"], d["dO"], d["dS_final"])
+    torch.cuda.synchronize()
+    for name, gname in (("log_alpha", "dlog_alpha"), ("b", "db"), ("w", "dw")):
+        assert g[gname].shape == d[name].shape
+    _check_fwd(inp, o, sf)
+    _check_bwd(inp, g)
+    # the staged training form gives the same results
+    o2, sf2, states = gdn2.fwd_states(*args, d["S0"])
+    g2 = gdn2.bwd_saved(*args, states, d["dO"], d["dS_final"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(sf, sf2)
+    for n in NAMES:
+        assert rel_err(g2[n], g[n].double().cpu().numpy()) < 1e-5, n
+
+
+def test_token_gates_training_workload():
+    """Gated DeltaNet's gates per token at the B8 T2048 H16 d128 training shape, staged
+    as in a training step, against the oracle."""
+    inp = make_workload(WORKLOADS["gdn_token_bf16_B8H16T2048d128"])
+    assert inp["gate_scalar"] == 7
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o, sf, states = gdn2.fwd_states(*args)
+    g = gdn2.bwd_saved(*args, states, d["dO"], d["dS_final"])
+    torch.cuda.synchronize()
+    _check_fwd(inp, o, sf)
+    _check_bwd(inp, g)
+
+
+def test_token_gates_agree_with_broadcast_gates():
+    """The per-token path against the per-channel path on the same gates broadcast
+    (materialised): the same forward arithmetic, gradients equal to the channel sums."""
+    inp = make_inputs(2, 300, 4, 128, 128, seed=8400, gates="gdn", s0_std=0.05, grads=True, token_gates=True)
+    d = to_dev(inp)
+    dk, dv = 128, 128
+    wide = dict(log_alpha=d["log_alpha"][..., None].expand(*d["log_alpha"].shape, dk).contiguous(),
+                b=d["b"][..., None].expand(*d["b"].shape, dk).contiguous(),
+                w=d["w"][..., None].expand(*d["w"].shape, dv).contiguous())
+    base = (d["q"], d["k"], d["v"])
+    o1, s1 = gdn2.fwd(*base, d["log_alpha"], d["b"], d["w"], d["S0"])
+    o2, s2 = gdn2.fwd(*base, wide["log_alpha"], wide["b"], wide["w"], d["S0"])
+    g1 = gdn2.bwd(*base, d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"], d["dS_final"])
+    g2 = gdn2.bwd(*base, wide["log_alpha"], wide["b"], wide["w"], d["S0"], d["dO"], d["dS_final"])
+    torch.cuda.synchronize()
+    eo, es = rel_err(o1, o2.double().cpu().numpy()), rel_err(s1, s2.double().cpu().numpy())
+    print("per-token vs broadcast: o %.2e S %.2e" % (eo, es))
+    assert eo < 1e-6 and es < 1e-6
+    for n in ("dq", "dk", "dv", "dS0"):
+        assert rel_err(g1[n], g2[n].double().cpu().numpy()) < 1e-6, n
+    for n in ("dlog_alpha", "db", "dw"):
+        e = rel_err(g1[n], g2[n].double().sum(-1).cpu().numpy())
+        print("%s per-token vs channel sum %.2e" % (n, e))
+        assert e < 1e-5, n
+
+
+def test_token_gates_decode_step():
+    inp = make_inputs(4, 1, 8, 128, 64, seed=8500, gates="gdn", s0_std=0.3, token_gates=True)
+    d = to_dev(inp)
+    tk = {n: d[n][:, 0].contiguous() for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    assert tk["b"].shape == (4, 8)
+    o, S1 = gdn2.step(tk["q"], tk["k"], tk["v"], tk["log_alpha"], tk["b"], tk["w"], d["S0"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.fwd(*_oracle_inputs(inp))
+    eo, es = rel_err(o, o_ref[:, 0]), rel_err(S1, s_ref)
+    print("token-gate step: o %.3e S %.3e" % (eo, es))
+    assert eo < 1e-5 and es < 1e-5
+
+
+def test_erase_gate_in_zero_two():
+    """The erase-range ablation: b = 2 sigmoid(.) in [0, 2], per channel."""
+    inp = make_inputs(2, 150, 2, 128, 64, seed=8600, gates="erase2", s0_std=0.1, grads=True)
+    assert float(inp["b"].max()) > 1.0
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o, sf = gdn2.fwd(*args, d["S0"])
+    g = gdn2.bwd(*args, d["S0"], d["dO"], d["dS_final"])
+    torch.cuda.synchronize()
+    inp = dict(inp, gate_scalar=0)
+    _check_fwd(inp, o, sf)
+    _check_bwd(inp, g)
+
+
+def test_token_gates_need_bf16_qkv():
+    inp = make_inputs(1, 8, 1, 32, 32, seed=8700, qkv_dtype="f32", gates="kda", token_gates=True)
+    d = to_dev(inp)
+    with pytest.raises(gdn2.Gdn2Error):
+        gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])

@@ -395,3 +395,61 @@ def test_logit_gate_gradients_match_central_differences():
         assert err < 1e-6, (name, err)
     for name in ("dq", "dk", "dv", "dS0"):
         assert gl[name] is g[name]
+
+
+# ---------------------------------------------------------------------------
+# gates given per token (one value per (b, t, h) for all channels of its axis)
+# ---------------------------------------------------------------------------
+
+def test_per_token_gates_reduce_to_kda_and_gated_deltanet():
+    """beta per token on both gates is KDA; a per-token decay as well is Gated
+    DeltaNet: checked against the dense matrix form written independently above."""
+    q, k, v, la, _, _, S0 = _case(36, T=9)
+    r = _rng(37)
+    B, T, H, dk = q.shape
+    beta = 1 / (1 + np.exp(-r.standard_normal((B, T, H))))
+    la_tok = -np.abs(r.standard_normal((B, T, H))) * 0.3
+    g = oracle.gates_per_token(la, beta, beta, dk, v.shape[-1], oracle.SCALAR_ERASE | oracle.SCALAR_WRITE)
+    o, sf = oracle.fwd(q, k, v, *g, S0)
+    o2, s2 = _kda_matrix_form(q, k, v, la, beta, S0)
+    assert np.allclose(o, o2, rtol=0, atol=1e-12) and np.allclose(sf, s2, rtol=0, atol=1e-12)
+    g = oracle.gates_per_token(la_tok, beta, beta, dk, v.shape[-1], 7)
+    o, sf = oracle.fwd(q, k, v, *g, S0)
+    o2, s2 = _kda_matrix_form(q, k, v, np.repeat(la_tok[..., None], dk, axis=-1), beta, S0)
+    assert np.allclose(o, o2, rtol=0, atol=1e-12) and np.allclose(sf, s2, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("scalar", [1, 2, 4, 6, 7])
+def test_per_token_gate_gradients_match_central_differences(scalar):
+    """Gradients w.r.t. one scalar per token (perturbing all of its channels at once)."""
+    q, k, v, la, b, w, S0 = _case(38, B=1, T=10, H=2, dk=4, dv=3, s0=0.5)
+    r = _rng(39)
+    tok = {1: la[..., 0].copy(), 2: b[..., 1].copy(), 4: w[..., 2].copy()}
+    gates = [tok[1] if scalar & 1 else la, tok[2] if scalar & 2 else b, tok[4] if scalar & 4 else w]
+    dO = r.standard_normal(v.shape)
+    dSf = r.standard_normal(S0.shape) * 0.5
+    dk, dv = q.shape[-1], v.shape[-1]
+
+    def loss(gs):
+        o, sf = oracle.fwd(q, k, v, *oracle.gates_per_token(*gs, dk, dv, scalar), S0, nthreads=1)
+        return float(np.sum(o * dO) + np.sum(sf * dSf))
+
+    g = oracle.bwd(q, k, v, *oracle.gates_per_token(*gates, dk, dv, scalar), S0, dO, dSf, nthreads=1)
+    gt = oracle.per_token_grads(g, scalar)
+    for pos, (name, bit) in enumerate((("dlog_alpha", 1), ("db", 2), ("dw", 4))):
+        x = gates[pos]
+        assert gt[name].shape == x.shape
+        if not scalar & bit:
+            assert gt[name] is g[name]
+            continue
+        fd = np.empty(x.size)
+        for n, ix in enumerate(np.ndindex(x.shape)):
+            h = 1e-6 * max(1.0, abs(x[ix]))
+            xp = [t.copy() for t in gates]
+            xm = [t.copy() for t in gates]
+            xp[pos][ix] += h
+            xm[pos][ix] -= h
+            fd[n] = (loss(xp) - loss(xm)) / (2 * h)
+        err = np.max(np.abs(fd - gt[name].reshape(-1))) / max(np.max(np.abs(fd)), 1e-30)
+        assert err < 1e-6, (name, err)
+
