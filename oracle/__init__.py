@@ -13,7 +13,8 @@ r = S^T e, write S += k (z - r)^T, and the query reads the updated state.
 
 Pins (see tests/test_oracle_pins.py): KDA and Gated DeltaNet reductions,
 read-after-write, brute-force transition products, causal linear attention,
-pure decay, finite-difference gradients.
+pure decay, finite-difference gradients; for the gate helpers and the output
+epilogue below, closed forms, invariances and finite differences.
 """
 from __future__ import annotations
 
@@ -183,4 +184,35 @@ def per_token_grads(grads, scalar):
         if scalar & bit:
             out[gname] = grads[gname].sum(axis=-1)
     return out
+
+
+# Output epilogue.  The operator's output o of each (batch, token, head) goes through an
+# RMS normalisation, then an output gate of its own (not the write gate), then the output
+# projection (blog on Gated DeltaNet-2, section "Token path and parallel training").  The
+# normalisation is taken over the dv value channels of the head, with a learnable
+# per-channel weight and a small eps inside the root; the gate is given as values (its
+# activation belongs to its projection, as for the other gates); the projection is a
+# plain matrix product outside the operator:
+#     y = o / sqrt(mean_j o_j^2 + eps) * weight * g
+# The gradients are those of this composition (r = 1 / sqrt(mean o^2 + eps), u = o r):
+#     dg = dy * u * weight,   dweight = sum over rows of dy * u * g,
+#     du = dy * weight * g,   do = r * (du - u * mean_j(du_j u_j)).
+
+def output_fwd(o, g, weight=None, eps=1e-6):
+    """y in float64 (same shape as o [..., dv]); weight [dv] or None (ones)."""
+    o, g = _f64(o), _f64(g)
+    wt = np.ones(o.shape[-1]) if weight is None else _f64(weight)
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o * r * wt * g
+
+
+def output_bwd(o, g, weight, eps, dy):
+    """Gradients of sum(dy * y) w.r.t. o, g and weight (dict do, dg, dweight; float64)."""
+    o, g, dy = _f64(o), _f64(g), _f64(dy)
+    wt = np.ones(o.shape[-1]) if weight is None else _f64(weight)
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    u = o * r
+    du = dy * wt * g
+    do = r * (du - u * np.mean(du * u, axis=-1, keepdims=True))
+    return {"do": do, "dg": dy * u * wt, "dweight": (dy * u * g).reshape(-1, o.shape[-1]).sum(axis=0)}
 

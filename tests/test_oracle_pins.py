@@ -453,3 +453,63 @@ def test_per_token_gate_gradients_match_central_differences(scalar):
         err = np.max(np.abs(fd - gt[name].reshape(-1))) / max(np.max(np.abs(fd)), 1e-30)
         assert err < 1e-6, (name, err)
 
+
+# ---------------------------------------------------------------------------
+# output epilogue: RMS normalisation over the value channels, output gate
+# ---------------------------------------------------------------------------
+
+def test_output_epilogue_closed_forms():
+    r = _rng(40)
+    o = r.standard_normal((3, 5, 2, 16))
+    ones = np.ones_like(o)
+    # eps = 0, unit weight and gate: every row has mean square exactly 1
+    y = oracle.output_fwd(o, ones, None, eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-14)
+    # scale invariance of the normalisation (positive scale, eps = 0), sign flip is odd
+    assert np.allclose(oracle.output_fwd(7.5 * o, ones, None, 0.0), y, rtol=0, atol=1e-14)
+    assert np.allclose(oracle.output_fwd(-o, ones, None, 0.0), -y, rtol=0, atol=1e-14)
+    # a constant row c * 1: y = c / sqrt(c^2 + eps) on every channel
+    c = np.full((1, 1, 1, 8), 0.01)
+    y = oracle.output_fwd(c, np.ones_like(c), None, eps=1e-4)
+    assert np.allclose(y, 0.01 / np.sqrt(1e-4 + 1e-4), rtol=1e-14, atol=0)
+    # weight and gate act per channel after the normalisation (a zero gate channel is zero)
+    wt = r.uniform(0.5, 1.5, 16)
+    g = r.uniform(0, 1, o.shape)
+    g[..., 3] = 0.0
+    y2 = oracle.output_fwd(o, g, wt, eps=0.0)
+    assert np.allclose(y2, oracle.output_fwd(o, ones, None, 0.0) * wt * g, rtol=1e-14, atol=1e-14)
+    assert np.all(y2[..., 3] == 0.0)
+    # the gate is not normalised: scaling it scales y
+    assert np.allclose(oracle.output_fwd(o, 3 * g, wt, 1e-6), 3 * oracle.output_fwd(o, g, wt, 1e-6), rtol=1e-14)
+
+
+def test_output_epilogue_gradients_match_central_differences():
+    r = _rng(41)
+    o = r.standard_normal((2, 3, 2, 8))
+    g = r.uniform(0, 1, o.shape)
+    wt = r.uniform(0.5, 1.5, 8)
+    dy = r.standard_normal(o.shape)
+    eps = 1e-3
+    gr = oracle.output_bwd(o, g, wt, eps, dy)
+
+    def loss(o_, g_, w_):
+        return float(np.sum(oracle.output_fwd(o_, g_, w_, eps) * dy))
+
+    xs = [o, g, wt]
+    for pos, name in enumerate(("do", "dg", "dweight")):
+        x = xs[pos]
+        fd = np.empty(x.size)
+        for n, ix in enumerate(np.ndindex(x.shape)):
+            h = 1e-6
+            xp = [t.copy() for t in xs]
+            xm = [t.copy() for t in xs]
+            xp[pos][ix] += h
+            xm[pos][ix] -= h
+            fd[n] = (loss(*xp) - loss(*xm)) / (2 * h)
+        err = np.max(np.abs(fd - gr[name].reshape(-1))) / np.max(np.abs(fd))
+        assert err < 1e-7, (name, err)
+    # weight None means ones
+    g0 = oracle.output_bwd(o, g, None, eps, dy)
+    g1 = oracle.output_bwd(o, g, np.ones(8), eps, dy)
+    assert all(np.array_equal(g0[n], g1[n]) for n in ("do", "dg", "dweight"))
+
