@@ -202,6 +202,35 @@ int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void 
               const void *log_alpha, const void *b, const void *w,
               const float *S_in, float *S_out, float *o, void *stream);
 
+/* ---- output epilogue ----
+ *
+ * The operator's output of each (batch, token, head) goes through an RMS normalisation,
+ * then an output gate of its own (not the write gate), then the output projection
+ * (blog on Gated DeltaNet-2, section "Token path and parallel training").  The
+ * normalisation runs over the dv value channels of one row with a per-channel weight;
+ * the gate is given as values (its activation belongs to its projection); the
+ * projection is a plain matrix product left to the caller.  Per row o of
+ * o [B,T,H,dv] (shape->B, T, H, dv are used; dk must still be valid):
+ *     y = o / sqrt(mean_j o_j^2 + eps) * weight * g
+ * o is fp32; g [B,T,H,dv] has dtype g_dtype (GDN2_F32 or GDN2_BF16); weight [dv] fp32,
+ * NULL = ones; y has dtype y_dtype (GDN2_F32 or GDN2_BF16, round to nearest even).
+ * eps must be finite and >= 0.  One kernel launch, no workspace. */
+int gdn2_output_fwd(const gdn2_shape *shape, const float *o, const void *g, int g_dtype,
+                    const float *weight, float eps, void *y, int y_dtype, void *stream);
+
+/* Bytes of device workspace gdn2_output_bwd needs when dweight is wanted (a partial
+ * dweight row per workgroup, at most 1024 * dv floats); (size_t)-1 if invalid. */
+size_t gdn2_output_bwd_workspace_size(const gdn2_shape *shape);
+
+/* Backward of the output epilogue for loss = sum(dy * y): writes dO = dloss/do and
+ * dg [B,T,H,dv] fp32 and, unless dweight == NULL, dweight [dv] fp32 (a sum over all
+ * rows, added in a fixed order: reproducible bit for bit).  dy is fp32 [B,T,H,dv].
+ * dO is the upstream gradient the operator's backward takes.  The workspace is needed
+ * (and overwritten) only when dweight != NULL.  One launch, two with dweight. */
+int gdn2_output_bwd(const gdn2_shape *shape, const float *o, const void *g, int g_dtype,
+                    const float *weight, float eps, const float *dy, float *dO, float *dg,
+                    float *dweight, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable description of a gdn2_status value. */
 const char *gdn2_strerror(int status);
 

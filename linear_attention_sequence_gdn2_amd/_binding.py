@@ -32,7 +32,8 @@ STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3:
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
            "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
-           "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step"]
+           "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step", "gdn2_output_fwd",
+           "gdn2_output_bwd_workspace_size", "gdn2_output_bwd"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -84,6 +85,13 @@ def load():
         lib.gdn2_chunk_bwd_grads.restype = ctypes.c_int
         lib.gdn2_step.argtypes = [SP] + [P] * 9 + [P]
         lib.gdn2_step.restype = ctypes.c_int
+        I, F = ctypes.c_int, ctypes.c_float
+        lib.gdn2_output_fwd.argtypes = [SP, P, P, I, P, F, P, I, P]
+        lib.gdn2_output_fwd.restype = ctypes.c_int
+        lib.gdn2_output_bwd_workspace_size.argtypes = [SP]
+        lib.gdn2_output_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.gdn2_output_bwd.argtypes = [SP, P, P, I, P, F, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.gdn2_output_bwd.restype = ctypes.c_int
         lib.gdn2_strerror.argtypes = [ctypes.c_int]
         lib.gdn2_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -360,3 +368,54 @@ def step(q, k, v, log_alpha, b, w, S=None, out=None, in_place=False):
     _check(lib.gdn2_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                          _ptr(S), _ptr(S_new), _ptr(o), _stream(q.device)))
     return o, S_new
+
+
+def _output_check(o, g, weight, extra=()):
+    if not o.is_cuda:
+        raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % o.device)
+    if o.dim() != 4 or o.dtype != torch.float32:
+        raise ValueError("gdn2: o must be float32 [B,T,H,dv]")
+    if tuple(g.shape) != tuple(o.shape) or g.dtype not in (torch.float32, torch.bfloat16) or g.device != o.device:
+        raise ValueError("gdn2: the output gate must be float32 or bfloat16 with the shape of o")
+    if weight is not None and (tuple(weight.shape) != (o.shape[-1],) or weight.dtype != torch.float32
+                               or weight.device != o.device):
+        raise ValueError("gdn2: weight must be float32 [dv]")
+    for t in (o, g, weight) + tuple(extra):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("gdn2: tensors must be contiguous")
+    B, T, H, dv = o.shape
+    # dk is not used by the epilogue; any supported value keeps the shape valid
+    return make_shape(B, T, H, 32, dv, torch.float32), GDN2_BF16 if g.dtype == torch.bfloat16 else GDN2_F32
+
+
+def output_fwd(o, g, weight=None, eps=1e-6, out_dtype=torch.float32):
+    """Output epilogue (one kernel): y = o / sqrt(mean(o^2 over dv) + eps) * weight * g.
+    o fp32 [B,T,H,dv]; g output gate values fp32 or bf16, same shape; weight fp32 [dv]
+    or None (ones); y has dtype out_dtype (fp32 or bf16)."""
+    shape, gdt = _output_check(o, g, weight)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gdn2: the epilogue writes float32 or bfloat16")
+    y = torch.empty(o.shape, dtype=out_dtype, device=o.device)
+    _check(load().gdn2_output_fwd(ctypes.byref(shape), _ptr(o), _ptr(g), gdt, _ptr(weight), float(eps), _ptr(y),
+                                  GDN2_BF16 if out_dtype == torch.bfloat16 else GDN2_F32, _stream(o.device)))
+    return y
+
+
+def output_bwd(o, g, weight, eps, dy, want_dweight=True, workspace=None):
+    """Backward of the output epilogue for sum(dy * y): dict dO, dg (fp32, the shape of o)
+    and dweight (fp32 [dv], or None).  dO is the operator's upstream gradient."""
+    shape, gdt = _output_check(o, g, weight, (dy,))
+    if tuple(dy.shape) != tuple(o.shape) or dy.dtype != torch.float32 or dy.device != o.device:
+        raise ValueError("gdn2: dy must be float32 with the shape of o")
+    lib = load()
+    dO = torch.empty_like(o)
+    dg = torch.empty(o.shape, dtype=torch.float32, device=o.device)
+    dweight = torch.empty(o.shape[-1], dtype=torch.float32, device=o.device) if want_dweight else None
+    ws_bytes = lib.gdn2_output_bwd_workspace_size(ctypes.byref(shape)) if want_dweight else 0
+    if want_dweight and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gdn2_output_bwd(ctypes.byref(shape), _ptr(o), _ptr(g), gdt, _ptr(weight), float(eps), _ptr(dy),
+                               _ptr(dO), _ptr(dg), _ptr(dweight), _ptr(workspace), nbytes, _stream(o.device)))
+    return {"dO": dO, "dg": dg, "dweight": dweight}
+

@@ -1,5 +1,6 @@
 // gdn2_api.cpp -- the C ABI of libgdn2.so: argument checks, workspace sizing and
 // kernel dispatch.  No allocation, no global mutable state, no exceptions.
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -270,6 +271,47 @@ int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void 
     a.scalar = shape->gate_scalar;
     return launch_status(gdn2::launch_step(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                            gate_scalar(shape), reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t gdn2_output_bwd_workspace_size(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return (size_t)-1;
+    const long rows = (long)shape->B * shape->T * shape->H;
+    return (size_t)gdn2::out_bwd_blocks(rows, shape->dv) * shape->dv * sizeof(float);
+}
+
+int gdn2_output_fwd(const gdn2_shape *shape, const float *o, const void *g, int g_dtype, const float *weight,
+                    float eps, void *y, int y_dtype, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!o || !g || !y || !(eps >= 0.f) || !isfinite(eps)) return GDN2_ERR_INVALID_ARG;
+    if ((g_dtype != GDN2_F32 && g_dtype != GDN2_BF16) || (y_dtype != GDN2_F32 && y_dtype != GDN2_BF16))
+        return GDN2_ERR_UNSUPPORTED;
+    if (!all_aligned({o, g, weight, y})) return GDN2_ERR_INVALID_ARG;
+    gdn2::OutArgs a{};
+    a.o = o; a.g = g; a.weight = weight; a.y = y;
+    a.rows = (long)shape->B * shape->T * shape->H;
+    a.eps = eps;
+    return launch_status(gdn2::launch_out_fwd(a, shape->dv, g_dtype == GDN2_BF16, y_dtype == GDN2_BF16,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gdn2_output_bwd(const gdn2_shape *shape, const float *o, const void *g, int g_dtype, const float *weight,
+                    float eps, const float *dy, float *dO, float *dg, float *dweight, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!o || !g || !dy || !dO || !dg || !(eps >= 0.f) || !isfinite(eps)) return GDN2_ERR_INVALID_ARG;
+    if (g_dtype != GDN2_F32 && g_dtype != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (!all_aligned({o, g, weight, dy, dO, dg, dweight, workspace})) return GDN2_ERR_INVALID_ARG;
+    if (dweight && (!workspace || workspace_bytes < gdn2_output_bwd_workspace_size(shape))) return GDN2_ERR_WORKSPACE;
+    gdn2::OutArgs a{};
+    a.o = o; a.g = g; a.weight = weight; a.dy = dy; a.dO = dO; a.dg = dg;
+    a.partial = dweight ? reinterpret_cast<float *>(workspace) : nullptr;
+    a.dweight = dweight;
+    a.rows = (long)shape->B * shape->T * shape->H;
+    a.eps = eps;
+    return launch_status(gdn2::launch_out_bwd(a, shape->dv, g_dtype == GDN2_BF16,
+                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

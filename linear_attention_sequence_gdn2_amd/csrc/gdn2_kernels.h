@@ -71,4 +71,24 @@ hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 
+// Arguments of the output epilogue (RMS norm over the dv channels of a row, weight, output
+// gate).  Row tensors are [rows, dv] contiguous, rows = B*T*H.
+struct OutArgs {
+    const float *o;                 // operator output, fp32
+    const void *g;                  // output gate values, fp32 or bf16
+    const float *weight;            // [dv] or null (ones)
+    const float *dy;                // backward: upstream gradient of y, fp32
+    void *y;                        // forward: fp32 or bf16
+    float *dO, *dg;                 // backward outputs, fp32
+    float *partial;                 // backward: [blocks, dv] partial dweight rows, or null (no dweight)
+    float *dweight;                 // backward: [dv], written when partial is set
+    long rows;
+    float eps;
+};
+// workgroups of the backward epilogue (so the partial-row workspace is blocks * dv floats)
+constexpr int kOutMaxBlocks = 1024;
+int out_bwd_blocks(long rows, int dv);
+hipError_t launch_out_fwd(const OutArgs &a, int dv, bool g_bf16, bool y_bf16, hipStream_t st);
+hipError_t launch_out_bwd(const OutArgs &a, int dv, bool g_bf16, hipStream_t st);
+
 }  // namespace gdn2

@@ -184,3 +184,20 @@ def make_workload(wl: Workload, **override):
               gate_logits=wl.extra.get("gate_logits", False), token_gates=wl.extra.get("token_gates", False))
     kw.update(override)
     return make_inputs(**kw)
+
+
+def make_output_inputs(B, T, H, dv, seed, *, g_dtype="f32"):
+    """Inputs of the output epilogue (CPU tensors): the operator output o ~ N(0, 0.5) fp32,
+    the output gate g = sigmoid(N(0,1)) (fp32, or rounded to bf16 with g_dtype="bf16"),
+    the norm weight ~ U(0.5, 1.5) [dv] fp32 and the upstream gradient dy ~ N(0,1) fp32.
+    Draw order: o, g, weight, dy."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    o = torch.randn(B, T, H, dv, generator=gen) * 0.5
+    g = torch.sigmoid(torch.randn(B, T, H, dv, generator=gen))
+    if g_dtype == "bf16":
+        g = g.to(torch.bfloat16)
+    elif g_dtype != "f32":
+        raise ValueError(g_dtype)
+    weight = torch.rand(dv, generator=gen) + 0.5
+    dy = torch.randn(B, T, H, dv, generator=gen)
+    return {"o": o, "g": g, "weight": weight, "dy": dy}

@@ -161,3 +161,28 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 1, 32)
     with pytest.raises(RuntimeError):
         gdn2.fwd(x, x, x, x, x, x)
+
+
+def test_output_epilogue_checks_arguments():
+    lib = gdn2.load()
+    f = P(0x10000)
+    s = _shape(B=2, T=100, H=3, dv=128)
+    F = ctypes.c_float
+    # workspace: one partial dweight row per workgroup (256 threads, 32 lanes a row, 4 rows in flight)
+    rows = 2 * 100 * 3
+    blocks = min((rows + 31) // 32, 1024)
+    assert lib.gdn2_output_bwd_workspace_size(ctypes.byref(s)) == blocks * 128 * 4
+    assert lib.gdn2_output_bwd_workspace_size(ctypes.byref(_shape(dv=96))) == ctypes.c_size_t(-1).value
+    assert lib.gdn2_output_fwd(ctypes.byref(s), f, f, 0, None, F(-1.0), f, 0, None) == INVALID
+    assert lib.gdn2_output_fwd(ctypes.byref(s), f, f, 0, None, F(float("nan")), f, 0, None) == INVALID
+    assert lib.gdn2_output_fwd(ctypes.byref(s), f, f, 0, None, F(float("inf")), f, 0, None) == INVALID
+    assert lib.gdn2_output_fwd(ctypes.byref(s), f, f, 2, None, F(1e-6), f, 0, None) == UNSUPPORTED
+    assert lib.gdn2_output_fwd(ctypes.byref(s), f, f, 0, None, F(1e-6), f, 5, None) == UNSUPPORTED
+    assert lib.gdn2_output_fwd(ctypes.byref(s), None, f, 0, None, F(1e-6), f, 0, None) == INVALID
+    assert lib.gdn2_output_fwd(ctypes.byref(s), f, f, 0, P(0x10008), F(1e-6), f, 0, None) == INVALID
+    assert lib.gdn2_output_fwd(ctypes.byref(_shape(dv=96)), f, f, 0, None, F(1e-6), f, 0, None) == UNSUPPORTED
+    need = lib.gdn2_output_bwd_workspace_size(ctypes.byref(s))
+    assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 0, None, F(1e-6), f, f, f, f, None, 0, None) == WORKSPACE
+    assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 0, None, F(1e-6), f, f, f, f, f, need - 1, None) == WORKSPACE
+    assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 0, None, F(1e-6), f, None, f, None, None, 0, None) == INVALID
+    assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 1, None, F(-0.5), f, f, f, None, None, 0, None) == INVALID
