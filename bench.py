@@ -134,6 +134,61 @@ def decode_bench(dev, B=64, H=16, dk=128, dv=128, iters=100):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+# output epilogue (RMS norm, weight, output gate) per token-head at dv = 128, bf16 gate and y:
+#   forward : o 512 + g 256 + y 256                      = 1024
+#   backward: o 512 + g 256 + dy 512 + dO 512 + dg 512   = 2304  (+ dweight partials per workgroup)
+OUT_FWD_BYTES_PER_TOKHEAD = 1024
+OUT_BWD_BYTES_PER_TOKHEAD = 2304
+
+
+def output_bench(dev, wl, iters=20):
+    """The output epilogue (gdn2_output_fwd / gdn2_output_bwd with dweight) on the
+    operator's output shape of the training workload."""
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import make_output_inputs
+    x = {k: v.to(dev) for k, v in make_output_inputs(wl.B, wl.T, wl.H, wl.dv, seed=4343, g_dtype="bf16").items()}
+    ws = torch.empty(gdn2.output_bwd_workspace_bytes(wl.B, wl.T, wl.H, wl.dv), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        return gdn2.output_fwd(x["o"], x["g"], x["weight"], 1e-6, out_dtype=torch.bfloat16)
+
+    def bwd():
+        return gdn2.output_bwd(x["o"], x["g"], x["weight"], 1e-6, x["dy"], workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    tokheads = wl.B * wl.T * wl.H
+    for name, fn, per in (("fwd", fwd, OUT_FWD_BYTES_PER_TOKHEAD), ("bwd", bwd, OUT_BWD_BYTES_PER_TOKHEAD)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        gbs = per * tokheads / (ms * 1e-3) / 1e9
+        res[name] = {"entry": "gdn2_output_" + name, "ms": round(ms, 4), "algorithmic_bytes": per * tokheads,
+                     "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    res["shape"] = {"B": wl.B, "T": wl.T, "H": wl.H, "dv": wl.dv, "g": "bf16", "y": "bf16", "dy": "f32"}
+    # a plain device copy of 512 MiB (read + write bytes / time): what a write-heavy stream reaches
+    src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    res["copy_reference_GBs"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +198,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-step (decode) measurement")
     ap.add_argument("--no-logit-gates", action="store_true", help="skip the step with bf16 logit gates")
     ap.add_argument("--no-token-gates", action="store_true", help="skip the step with per-token gates")
+    ap.add_argument("--no-output", action="store_true", help="skip the output epilogue measurement")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
@@ -291,6 +347,8 @@ def main():
             "kernel_ms": {kn[0]: round(ms, 4) for kn, ms in zip(kernels, tk_ms)},
             "step_event_ms": round(tstep_ms, 4),
             "step_algorithmic_frac": round(talg / (tstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_output:
+        out["breakdown"]["output_epilogue"] = output_bench(dev, wl)
     if not args.no_decode:
         out["breakdown"]["decode_step"] = decode_bench(dev)
     if not args.no_cpu_baseline:

@@ -401,6 +401,14 @@ def output_fwd(o, g, weight=None, eps=1e-6, out_dtype=torch.float32):
     return y
 
 
+def output_bwd_workspace_bytes(B, T, H, dv):
+    """Bytes of the workspace output_bwd uses for dweight."""
+    n = load().gdn2_output_bwd_workspace_size(ctypes.byref(make_shape(B, T, H, 32, dv, torch.float32)))
+    if n == ctypes.c_size_t(-1).value:
+        raise Gdn2Error(2, "unsupported shape")
+    return n
+
+
 def output_bwd(o, g, weight, eps, dy, want_dweight=True, workspace=None):
     """Backward of the output epilogue for sum(dy * y): dict dO, dg (fp32, the shape of o)
     and dweight (fp32 [dv], or None).  dO is the operator's upstream gradient."""
@@ -411,9 +419,9 @@ def output_bwd(o, g, weight, eps, dy, want_dweight=True, workspace=None):
     dO = torch.empty_like(o)
     dg = torch.empty(o.shape, dtype=torch.float32, device=o.device)
     dweight = torch.empty(o.shape[-1], dtype=torch.float32, device=o.device) if want_dweight else None
-    ws_bytes = lib.gdn2_output_bwd_workspace_size(ctypes.byref(shape)) if want_dweight else 0
     if want_dweight and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
+        workspace = torch.empty(lib.gdn2_output_bwd_workspace_size(ctypes.byref(shape)), dtype=torch.uint8,
+                                device=o.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gdn2_output_bwd(ctypes.byref(shape), _ptr(o), _ptr(g), gdt, _ptr(weight), float(eps), _ptr(dy),
                                _ptr(dO), _ptr(dg), _ptr(dweight), _ptr(workspace), nbytes, _stream(o.device)))

@@ -101,17 +101,24 @@ __global__ __launch_bounds__(kOutThreads) void out_bwd_kernel(OutArgs a) {
     const float4 wt = a.weight ? reinterpret_cast<const float4 *>(a.weight)[lane] : make_float4(1.f, 1.f, 1.f, 1.f);
     const long nrb = (a.rows + C::RPB - 1) / C::RPB;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);   // this lane's columns of the dweight partial
-    for (long rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-        const long base = rb * C::RPB + rg;
-        float4 ov[kOutUnroll], gv[kOutUnroll], dy[kOutUnroll];
+    // rows of row block rb (clamped addresses: every load is issued, none is out of bounds)
+    float4 ov[kOutUnroll], gv[kOutUnroll], dy[kOutUnroll];
+    auto load_rows = [&](long rb, float4 (&o4)[kOutUnroll], float4 (&g4)[kOutUnroll], float4 (&d4)[kOutUnroll]) {
 #pragma unroll
         for (int u = 0; u < kOutUnroll; ++u) {
-            const long row = base + (long)u * C::RPI;
+            const long row = rb * C::RPB + rg + (long)u * C::RPI;
             const size_t off = (size_t)(row < a.rows ? row : a.rows - 1) * DV + 4 * lane;
-            ov[u] = *reinterpret_cast<const float4 *>(a.o + off);
-            gv[u] = load_gate4<GB>(a.g, off);
-            dy[u] = *reinterpret_cast<const float4 *>(a.dy + off);
+            o4[u] = *reinterpret_cast<const float4 *>(a.o + off);
+            g4[u] = load_gate4<GB>(a.g, off);
+            d4[u] = *reinterpret_cast<const float4 *>(a.dy + off);
         }
+    };
+    load_rows(blockIdx.x, ov, gv, dy);
+    for (long rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+        const long base = rb * C::RPB + rg;
+        // the next row block's loads are in flight while this one is computed and stored
+        float4 on[kOutUnroll], gn[kOutUnroll], dn[kOutUnroll];
+        load_rows(rb + gridDim.x < nrb ? rb + gridDim.x : rb, on, gn, dn);
 #pragma unroll
         for (int u = 0; u < kOutUnroll; ++u) {
             const long row = base + (long)u * C::RPI;
@@ -134,6 +141,12 @@ __global__ __launch_bounds__(kOutThreads) void out_bwd_kernel(OutArgs a) {
                 acc.w += dy[u].w * uu.w * gv[u].w;
             }
         }
+#pragma unroll
+        for (int u = 0; u < kOutUnroll; ++u) {
+            ov[u] = on[u];
+            gv[u] = gn[u];
+            dy[u] = dn[u];
+        }
     }
     if (!a.partial) return;   // uniform over the launch
     // this workgroup's partial dweight row: the RPI row groups added in a fixed order
@@ -151,20 +164,30 @@ __global__ __launch_bounds__(kOutThreads) void out_bwd_kernel(OutArgs a) {
     }
 }
 
-// dweight[c] = sum over the nblk partial rows, in a fixed order: 32 columns per
-// workgroup, 8 strided groups of partial rows, then the groups in order.
-__global__ __launch_bounds__(kOutThreads) void out_dweight_kernel(const float *partial, int nblk, int dv,
+// dweight[c] = sum over the nblk partial rows, in a fixed order: 16 columns per
+// workgroup of 1024 threads, 64 strided groups of partial rows (each loads its rows in
+// batches of 8 before adding, so the loads overlap), then the groups in order.
+constexpr int kRedThreads = 1024, kRedCols = 16, kRedGroups = kRedThreads / kRedCols, kRedBatch = 8;
+__global__ __launch_bounds__(kRedThreads) void out_dweight_kernel(const float *partial, int nblk, int dv,
                                                                    float *dweight) {
-    __shared__ float sPart[kOutThreads];
-    const int col = blockIdx.x * 32 + threadIdx.x % 32, grp = threadIdx.x / 32;
+    __shared__ float sPart[kRedThreads];
+    const int col = blockIdx.x * kRedCols + threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols;
     float s = 0.f;
-    for (int i = grp; i < nblk; i += kOutThreads / 32) s += partial[(size_t)i * dv + col];
+    for (int i0 = grp; i0 < nblk; i0 += kRedGroups * kRedBatch) {
+        float x[kRedBatch];
+#pragma unroll
+        for (int j = 0; j < kRedBatch; ++j) {
+            const int i = i0 + j * kRedGroups;
+            x[j] = i < nblk ? partial[(size_t)i * dv + col] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kRedBatch; ++j) s += x[j];
+    }
     sPart[threadIdx.x] = s;
     __syncthreads();
     if (grp == 0) {
         float t = sPart[threadIdx.x];
-#pragma unroll
-        for (int j = 1; j < kOutThreads / 32; ++j) t += sPart[j * 32 + threadIdx.x];
+        for (int j = 1; j < kRedGroups; ++j) t += sPart[j * kRedCols + threadIdx.x];
         dweight[col] = t;
     }
 }
@@ -188,8 +211,8 @@ static hipError_t out_bwd_t(const OutArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((out_bwd_kernel<DV, GB>), dim3((unsigned)nblk), dim3(kOutThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.partial) return e;
-    hipLaunchKernelGGL(out_dweight_kernel, dim3((unsigned)(DV / 32)), dim3(kOutThreads), 0, st, a.partial, nblk, DV,
-                       a.dweight);
+    hipLaunchKernelGGL(out_dweight_kernel, dim3((unsigned)(DV / kRedCols)), dim3(kRedThreads), 0, st, a.partial, nblk,
+                       DV, a.dweight);
     return hipGetLastError();
 }
 
