@@ -39,10 +39,11 @@ BWD_BYTES_PER_TOKHEAD = 5888
 # per-kernel algorithmic bytes per token-head of the four launches of a step:
 #   forward with states : 2816 + chunk states 128*128*4 / 64 tokens = 1024     -> 3840
 #   adjoint factors     : q,k 512 + log_alpha,b 1024
-#                         + factors (128*128 + 64*128)*4 / 64 tokens = 1536     -> 3072
+#                         + factors (128*128 + 64*128)*4 / 64 tokens = 1536
+#                         + chunk operand record 131584 / 64 tokens = 2056      -> 5128
 #   reverse sweep       : factors 1536 + dO 512 + dstates 1024                  -> 3072
-#   chunk gradients     : q,k,v 768 + gates 1536 + dO 512 + states, dstates 2048
-#                         + dq,dk,dv,dlog_alpha,db,dw 3072                      -> 7936
+#   chunk gradients     : q,k,v 768 + b,w 1024 + dO 512 + states, dstates 2048
+#                         + record 2056 + dq,dk,dv,dlog_alpha,db,dw 3072        -> 9480
 # with the gates given as bf16 logits each pass reads 1536 -> 768 gate bytes per token-head
 GATE_BYTES_SAVED_PER_TOKHEAD = 768
 LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
@@ -51,9 +52,9 @@ LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
 TOKEN_GATE_BYTES_SAVED_PER_TOKHEAD = 1536 - 12
 TOKEN_WORKLOAD = "gdn_token_bf16_B8H16T2048d128"
 FWD_STATES_BYTES_PER_TOKHEAD = 3840
-BWD_FACTORS_BYTES_PER_TOKHEAD = 3072
+BWD_FACTORS_BYTES_PER_TOKHEAD = 5128
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
-BWD_GRADS_BYTES_PER_TOKHEAD = 7936
+BWD_GRADS_BYTES_PER_TOKHEAD = 9480
 
 
 def _kernel_sources_digest():
@@ -260,7 +261,7 @@ def main():
             _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
             if ev is not None:
                 ev[3].record(stream)
-            g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates)
+            g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates, factors)
             if ev is not None:
                 ev[4].record(stream)
             return o, sf, g, dS0

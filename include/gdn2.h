@@ -158,8 +158,9 @@ int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v,
                       const void *log_alpha, const void *b, const void *w,
                       const float *S0, float *states, void *stream);
 
-/* Bytes of the per-chunk adjoint factor buffer, B*H*ceil(T/64)*(dk*dk + 64*dk)*4;
- * (size_t)-1 if the shape is invalid. */
+/* Bytes of the factor buffer of gdn2_chunk_bwd_factors: per (batch, head, chunk) the
+ * adjoint factors, (dk*dk + 64*dk)*4 bytes, and the chunk's key-side operands,
+ * about 772*dk + 33000 bytes (rounded up to 256); (size_t)-1 if the shape is invalid. */
 size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
 
 /* Per-chunk adjoint factors of the reverse sweep.  Unrolling the backward of one
@@ -169,7 +170,10 @@ size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
  * with dS' the gradient of its end state; R and Q2 depend on q, k, log_alpha and b
  * only.  Writes R and Q2^T of every (batch, head, chunk) into `factors`
  * (gdn2_chunk_factors_bytes() bytes, device memory owned by the caller, opaque
- * layout of split-bf16 MFMA tiles, read only by gdn2_chunk_bwd_reverse). */
+ * layout of split-bf16 MFMA tiles), followed by the key-side operands of every chunk
+ * that the token gradients need as well (the decay-absorbed key and erase-key rows,
+ * T = (I + A)^-1, P, the decay prefix), so that they are formed once.  Read by
+ * gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads. */
 int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k,
                            const void *log_alpha, const void *b, void *factors, void *stream);
 
@@ -179,12 +183,14 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors,
                            const float *dO, const float *dS_final,
                            float *dstates, float *dS0, void *stream);
 
-/* Token gradients from states and dstates: dq, dk, dlog_alpha, db [B,T,H,dk],
+/* Token gradients from states, dstates and the factor buffer of
+ * gdn2_chunk_bwd_factors (same shape and inputs): dq, dk, dlog_alpha, db [B,T,H,dk],
  * dv, dw [B,T,H,dv]. */
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape,
                          const void *q, const void *k, const void *v,
                          const void *log_alpha, const void *b, const void *w,
                          const float *dO, const float *states, const float *dstates,
+                         const void *factors,
                          float *dq, float *dk, float *dv,
                          float *dlog_alpha, float *db, float *dw, void *stream);
 

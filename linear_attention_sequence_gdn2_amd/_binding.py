@@ -81,7 +81,7 @@ def load():
         lib.gdn2_chunk_bwd_factors.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_reverse.argtypes = [SP] + [P] * 5 + [P]
         lib.gdn2_chunk_bwd_reverse.restype = ctypes.c_int
-        lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 15 + [P]
+        lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 16 + [P]
         lib.gdn2_chunk_bwd_grads.restype = ctypes.c_int
         lib.gdn2_step.argtypes = [SP] + [P] * 9 + [P]
         lib.gdn2_step.restype = ctypes.c_int
@@ -313,15 +313,18 @@ def bwd_reverse(factors, dO, dk, dS_final=None, want_dS0=True, dstates=None):
     return dstates, dS0
 
 
-def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates):
-    """Token gradients from chunk states and end-state gradients (one kernel)."""
+def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates, factors):
+    """Token gradients from chunk states, end-state gradients and the factor buffer of
+    bwd_factors on the same inputs (one kernel)."""
     B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (dO, states, dstates))
+    if factors.device != q.device or factors.numel() * factors.element_size() < factors_bytes(B, T, H, dk, dv):
+        raise ValueError("gdn2: factors buffer does not match the shape")
     lib = load()
     shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
     dev = q.device
     out = _grad_outputs(B, T, H, dk, dv, sc, dev)
     _check(lib.gdn2_chunk_bwd_grads(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
-                                    _ptr(w), _ptr(dO), _ptr(states), _ptr(dstates), _ptr(out["dq"]),
+                                    _ptr(w), _ptr(dO), _ptr(states), _ptr(dstates), _ptr(factors), _ptr(out["dq"]),
                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
                                     _ptr(out["dw"]), _stream(dev)))
     return out
@@ -331,7 +334,7 @@ def bwd_saved(q, k, v, log_alpha, b, w, states, dO, dS_final=None, want_dS0=True
     """Backward from the states written by fwd_states: factors, reverse sweep, token gradients."""
     factors = bwd_factors(q, k, log_alpha, b)
     dstates, dS0 = bwd_reverse(factors, dO, q.shape[-1], dS_final, want_dS0)
-    out = bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates)
+    out = bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates, factors)
     out["dS0"] = dS0
     return out
 

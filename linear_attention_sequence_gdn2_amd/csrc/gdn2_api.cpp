@@ -108,8 +108,7 @@ size_t gdn2_chunk_states_bytes(const gdn2_shape *shape) {
 
 size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
-    const size_t dk = (size_t)shape->dk;
-    return (size_t)shape->B * shape->H * nchunks(shape) * (dk * dk + 64 * dk) * sizeof(float);
+    return gdn2::factor_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk);
 }
 
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape) {
@@ -209,20 +208,21 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const f
 
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, const void *v,
                          const void *log_alpha, const void *b, const void *w, const float *dO,
-                         const float *states, const float *dstates, float *dq, float *dk, float *dv,
-                         float *dlog_alpha, float *db, float *dw, void *stream) {
+                         const float *states, const float *dstates, const void *factors, float *dq, float *dk,
+                         float *dv, float *dlog_alpha, float *db, float *dw, void *stream) {
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
-    if (!q || !k || !v || !log_alpha || !b || !w || !dO || !states || !dstates || !dq || !dk || !dv ||
+    if (!q || !k || !v || !log_alpha || !b || !w || !dO || !states || !dstates || !factors || !dq || !dk || !dv ||
         !dlog_alpha || !db || !dw)
         return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, v, dO, states, dstates, dq, dk, dv}) || !gates_aligned(shape, log_alpha, b, w) ||
+    if (!all_aligned({q, k, v, dO, states, dstates, factors, dq, dk, dv}) || !gates_aligned(shape, log_alpha, b, w) ||
         !gates_aligned(shape, dlog_alpha, db, dw))
         return GDN2_ERR_INVALID_ARG;
     gdn2::BwdArgs a = bwd_args(shape);
     a.q = q; a.k = k; a.v = v;
     a.la = log_alpha; a.bg = b; a.wg = w;
     a.dO = dO; a.states = states; a.dstates = const_cast<float *>(dstates);
+    a.factors = const_cast<void *>(factors);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
     return launch_status(gdn2::launch_bwd_chunk(a, shape->dk, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                                 gate_scalar(shape), reinterpret_cast<hipStream_t>(stream)));
@@ -252,8 +252,8 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     if (rc != GDN2_OK) return rc;
     rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     if (rc != GDN2_OK) return rc;
-    return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, dq, dk, dv, dlog_alpha, db,
-                                dw, stream);
+    return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, factors, dq, dk, dv,
+                                dlog_alpha, db, dw, stream);
 }
 
 int gdn2_step(const gdn2_shape *shape, const void *q, const void *k, const void *v, const void *log_alpha,

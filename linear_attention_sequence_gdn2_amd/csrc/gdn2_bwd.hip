@@ -146,94 +146,55 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     };
 
-    for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
-    KeyRaw4<DK / 2, BF16, GL, SG> raw;
-    raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk, srowK, a.scalar);
     Tile cur;
     load_tile(0, cur, tid);
 
-    // ---- preparation: decay, operand rows, A -> T, P^T rows in registers ----
+    // ---- preparation: the chunk operand record that the adjoint-factor kernel wrote
+    // (Kt and Et rows, T, P^T fragments, the decay prefix G and gamma), into LDS and registers
+    using Rec = ChunkRecord<DK>;
+    const char *rec = reinterpret_cast<const char *>(a.factors) +
+                      (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)L * Rec::BYTES;
     float Gk[NEH];                 // decay prefix, kept for the element-wise chain of the epilogue
+    Split4 Pt[4];                  // lane holds P[16mt + 4g + i][16w + r] (zero for mt < w)
     {
-        float qf[NEH], kf[NEH], laf[NEH], bgf[NEH], G[NEH], gC[NEH];
-        raw.unpack(qf, kf, laf, bgf);
+        constexpr int NROW = DK / 16;   // 16-byte pieces per thread of the four row planes
+        uint4 rv[NROW];
 #pragma unroll
-        for (int e = 0; e < NEH; ++e) G[e] = laf[e] * kLog2e;
-        chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
-        if (w == 0 && r == 0) {
+        for (int it = 0; it < NROW; ++it)
+            rv[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKt + (size_t)(tid + NTH * it) * 16);
+        static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
+        const int trow = tid >> 3, tc8 = 8 * (tid & 7);
+        const uint4 th = *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(trow * kChunk + tc8) * 2);
+        const uint4 tl =
+            *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(kChunk * kChunk + trow * kChunk + tc8) * 2);
+        uint4 pv[4];
 #pragma unroll
-            for (int e = 0; e < NEH; ++e) sGam[ch(e)] = exp2_fast(gC[e]);
+        for (int mt = 0; mt < 4; ++mt)
+            pv[mt] = mt >= w ? *reinterpret_cast<const uint4 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16)
+                             : make_uint4(0u, 0u, 0u, 0u);
+        f32x4 gv[NEH / 4];
+#pragma unroll
+        for (int e4 = 0; e4 < NEH / 4; ++e4)
+            gv[e4] = *reinterpret_cast<const f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + 4 * e4) * 4);
+        if (tid < DK) sGam[tid] = reinterpret_cast<const float *>(rec + Rec::oGam)[tid];
+#pragma unroll
+        for (int it = 0; it < NROW; ++it) {
+            const int idx = tid + NTH * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
+            const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
+            *reinterpret_cast<uint4 *>((plane < 2 ? sKt : sEt) + (plane & 1) * RK + row * PK + c8) = rv[it];
+        }
+        *reinterpret_cast<uint4 *>(&sTs[trow * PT + tc8]) = th;
+        *reinterpret_cast<uint4 *>(&sTs[kChunk * PT + trow * PT + tc8]) = tl;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const bf16x8 o = __builtin_bit_cast(bf16x8, pv[mt]);
+            Pt[mt].hi = __builtin_shufflevector(o, o, 0, 1, 2, 3);
+            Pt[mt].lo = __builtin_shufflevector(o, o, 4, 5, 6, 7);
         }
 #pragma unroll
-        for (int e = 0; e < NEH; ++e) Gk[e] = G[e];
-#pragma unroll
-        for (int mm = 0; mm < NMH; ++mm) {
-            f32x4 et, qt, kt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * mm + i;
-                const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]);
-                et[i] = bgf[e] * kf[e] * eg;
-                qt[i] = qf[e] * eg;
-                kt[i] = kf[e] * eng;
-            }
-            const int o = (16 * w + r) * PK + chh + 16 * mm + 4 * g;
-            const Split4 se = split4(et), sq = split4(qt), sk = split4(kt);
-            *reinterpret_cast<bf16x4 *>(&sEt[o]) = se.hi;
-            *reinterpret_cast<bf16x4 *>(&sEt[RK + o]) = se.lo;
-            *reinterpret_cast<bf16x4 *>(&sQt[o]) = sq.hi;
-            *reinterpret_cast<bf16x4 *>(&sQt[RK + o]) = sq.lo;
-            *reinterpret_cast<bf16x4 *>(&sKt[o]) = sk.hi;
-            *reinterpret_cast<bf16x4 *>(&sKt[RK + o]) = sk.lo;
-        }
+        for (int e = 0; e < NEH; ++e) Gk[e] = gv[e / 4][e % 4];
     }
     __syncthreads();
-    Split4 Pt[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        // A block (queries of block w, keys of block mt); the two halves share them out
-        if (mt <= w && (mt & 1) == hf) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g);
-                const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
-                if (FAST) acc = mfma32(kf.hi, ef.hi, acc);
-                else acc = mfma32x3(kf, ef, acc);
-            }
-            // lane holds A[16w + r][16mt + 4g + i]
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * mt + 4 * g + i < 16 * w + r)) acc[i] = 0.f;
-            *reinterpret_cast<f32x4 *>(&sAT[(16 * w + r) * PA + 16 * mt + 4 * g]) = acc;
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (mt >= w) {
-#pragma unroll
-            for (int j = 0; j < NKS; ++j)
-                acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
-                               row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
-            // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
-        }
-        Pt[mt] = split4(acc);
-    }
-    __syncthreads();
-    solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
-    {
-        // T as split bf16 [row][col], once per chunk: the value loop reads its rows (U = T X)
-        // and, transposed, its columns (dX = T^T dU) without converting again per tile
-        const int row = tid >> 3, c8 = 8 * (tid & 7);
-        const f32x4 t0v = *reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8]);
-        const f32x4 t1v = *reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8 + 4]);
-        __syncthreads();
-        const Split8 ts = split8v(t0v, t1v);
-        *reinterpret_cast<bf16x8 *>(&sTs[row * PT + c8]) = ts.hi;
-        *reinterpret_cast<bf16x8 *>(&sTs[kChunk * PT + row * PT + c8]) = ts.lo;
-    }
-    static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
     float gm[NSF];
 #pragma unroll
     for (int it = 0; it < NSF; ++it) {
@@ -458,6 +419,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
+    KeyRaw4<DK / 2, BF16, GL, SG> raw;
     raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk, srowK, a.scalar);
     raw.unpack(qf, kf, G, bgf);
     float dact[NEH];               // d log_alpha / d stored decay input

@@ -360,4 +360,34 @@ __device__ __forceinline__ Split8 row_frag4(const __bf16 *hi, const __bf16 *lo, 
                     &lo[row * PK + 32 * j + 4 * g], &lo[row * PK + 32 * j + 16 + 4 * g]);
 }
 
+// ---- adjoint factor tiles (R and Q2^T of a chunk, MFMA fragment order) ----
+constexpr int kFragTile = 64 * 8;   // bf16 per stored 16x16 factor tile
+
+template <int DK>
+constexpr size_t factor_elems_per_chunk() {
+    return (size_t)((DK / 16) * (DK / 16) + (DK / 16) * 4) * kFragTile;
+}
+
+// ---- chunk operand record ----
+// The key-side operands of one (batch, head, chunk) that the adjoint-factor kernel forms
+// anyway and the chunk-gradient kernel needs as well, so that they are formed once:
+//   Kt and Et rows     [token][channel] split bf16, hi plane then lo plane, pitch DK
+//   T = (I + A)^-1     [row][col] split bf16, hi then lo, pitch 64
+//   P^T fragments      tile (key block w, query block mt) at (4w + mt) * 64 lanes * 8 bf16:
+//                      lane (r, g) holds P[16mt + 4g + i][16w + r], hi (i < 4) then lo;
+//                      only tiles with mt >= w are written (the others are zero)
+//   G                  the log2 decay prefix, per thread of the 512-thread workgroup in
+//                      its element order (token 16w + r, channels DK/2 * hf + ch4(e, g))
+//   gamma              [DK] fp32, the chunk's total decay per key channel
+template <int DK>
+struct ChunkRecord {
+    static constexpr int ROWS = kChunk * DK * 2 * 2;           // bytes of one operand's two row planes
+    static constexpr int oKt = 0, oEt = oKt + ROWS;
+    static constexpr int oT = oEt + ROWS, B_T = kChunk * kChunk * 2 * 2;
+    static constexpr int oPt = oT + B_T, B_PT = 16 * 64 * 8 * 2;
+    static constexpr int oG = oPt + B_PT, B_G = kChunkThreads * (DK / 8) * 4;
+    static constexpr int oGam = oG + B_G;
+    static constexpr int BYTES = (oGam + DK * 4 + 255) / 256 * 256;
+};
+
 }  // namespace gdn2

@@ -32,7 +32,7 @@ struct BwdArgs {
     const float *states;            // [B,H,NC,dk,dv] chunk-start states
     float *dstates;                 // [B,H,NC,dk,dv] gradient w.r.t. chunk-end states
     float *dq, *dk, *dv, *dla, *db, *dw, *dS0;
-    void *factors;                  // [B,H,NC] per-chunk adjoint factors (bf16 tiles)
+    void *factors;                  // per-chunk adjoint factors (bf16 tiles), then chunk operand records
     int B, T, H, DV;
     int scalar;                     // kScalar* bits: gates (and their gradients) per token [B,T,H]
 };
@@ -67,6 +67,9 @@ enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
 // gl: the gates are bf16 logits (only with bf16 q/k/v); sg: some gates are given per token
 // (a.scalar; only with bf16 q/k/v and fp32 gate values)
 hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode, hipStream_t st);
+// Bytes of the factor buffer of `items` chunks: the adjoint factors R, Q2^T of every chunk,
+// then the chunk operand record of every chunk (read by the chunk-gradient kernel).
+size_t factor_buffer_bytes(long items, int dk);
 hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);

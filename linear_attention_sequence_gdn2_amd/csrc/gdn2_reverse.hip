@@ -24,13 +24,6 @@
 
 namespace gdn2 {
 
-constexpr int kFragTile = 64 * 8;   // bf16 per stored 16x16 factor tile
-
-template <int DK>
-constexpr size_t factor_elems_per_chunk() {
-    return (size_t)((DK / 16) * (DK / 16) + (DK / 16) * 4) * kFragTile;
-}
-
 // 16x16 tile from its D-layout transpose: the lane holds X[16m + r][16kb + 4g + i] (i < 4)
 __device__ __forceinline__ void store_frag_tile(__bf16 *tile, int l, const f32x4 &v) {
     const Split4 s = split4(v);
@@ -64,6 +57,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4;
     constexpr int RK = kChunk * PK;
     constexpr bool FAST = BF16;
+    using Rec = ChunkRecord<DK>;
     // LDS (bytes): Kt, Et, Qt rows [token][channel] (hi, lo); the decay totals after the
     // Et rows; W^T [channel][token] (hi, lo) later over the Et rows and the totals;
     // A then T (fp32); gamma per channel.
@@ -121,6 +115,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         return ((size_t)b * T * H + h) * DK + (size_t)(valid ? tk : T - 1) * tokK + chh;
     };
     __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
+    // this item's chunk operand record, after the factors of all items
+    char *rec = reinterpret_cast<char *>(a.factors) + (size_t)nitems * factor_elems_per_chunk<DK>() * 2 +
+                (size_t)L * Rec::BYTES;
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
     {
@@ -137,8 +134,16 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
         if (w == 0 && r == 0) {
 #pragma unroll
-            for (int e = 0; e < NEH; ++e) sGam[ch(e)] = exp2_fast(gC[e]);
+            for (int e = 0; e < NEH; ++e) {
+                const float gm = exp2_fast(gC[e]);
+                sGam[ch(e)] = gm;
+                reinterpret_cast<float *>(rec + Rec::oGam)[ch(e)] = gm;
+            }
         }
+#pragma unroll
+        for (int e = 0; e < NEH; e += 4)
+            *reinterpret_cast<f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + e) * 4) =
+                f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
             f32x4 et, qt, kt;
@@ -161,6 +166,38 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         }
     }
     __syncthreads();
+
+    // ---- record: Kt and Et rows (dense pitch), P^T fragments ----
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) {
+        const int idx = tid + NTH * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
+        const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
+        const __bf16 *src = (plane < 2 ? sKt : sEt) + (plane & 1) * RK + row * PK + c8;
+        *reinterpret_cast<uint4 *>(rec + Rec::oKt + (size_t)plane * (kChunk * DK * 2) + (size_t)(row * DK + c8) * 2) =
+            *reinterpret_cast<const uint4 *>(src);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= w && (mt & 1) == hf) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKS; ++j)
+                acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
+                               row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
+            // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
+            const Split4 sp = split4(acc);
+            bf16x8 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = sp.hi[i];
+                o[4 + i] = sp.lo[i];
+            }
+            *reinterpret_cast<bf16x8 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
+        }
+    }
 
     // ---- A (shared out between the halves) and the rows of P of query block w ----
     Split4 Pf[4];
@@ -196,6 +233,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     }
     __syncthreads();
     solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
+    {
+        // record: T as split bf16 [row][col], one thread per 8 elements
+        static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
+        const int row = tid >> 3, c8 = 8 * (tid & 7);
+        const Split8 ts = split8v(*reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8]),
+                                  *reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8 + 4]));
+        *reinterpret_cast<bf16x8 *>(rec + Rec::oT + (size_t)(row * kChunk + c8) * 2) = ts.hi;
+        *reinterpret_cast<bf16x8 *>(rec + Rec::oT + (size_t)(kChunk * kChunk + row * kChunk + c8) * 2) = ts.lo;
+    }
 
     // ---- W = T Et: tiles (token block w, channel blocks of half hf) ----
     f32x4 Wt[NMH];
@@ -417,6 +463,15 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+size_t factor_buffer_bytes(long items, int dk) {
+    switch (dk) {
+        case 32: return (size_t)items * (factor_elems_per_chunk<32>() * 2 + ChunkRecord<32>::BYTES);
+        case 64: return (size_t)items * (factor_elems_per_chunk<64>() * 2 + ChunkRecord<64>::BYTES);
+        case 128: return (size_t)items * (factor_elems_per_chunk<128>() * 2 + ChunkRecord<128>::BYTES);
+        default: return 0;
+    }
+}
+
 template <int DK, bool BF16, bool GL, bool SG>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
     const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);

@@ -56,7 +56,11 @@ def test_workspace_and_state_sizes():
     nc = (100 + 63) // 64
     one = 2 * 3 * nc * 128 * 64 * 4
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(s)) == one
-    factors = 2 * 3 * nc * (128 * 128 + 64 * 128) * 4
+    # per chunk: the adjoint factors R, Q2^T, then the chunk operand record (Kt, Et rows and
+    # T split in bf16, 16 P^T fragment tiles, the decay prefix, gamma; rounded up to 256)
+    record = 4 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4
+    record = (record + 255) // 256 * 256
+    factors = 2 * 3 * nc * ((128 * 128 + 64 * 128) * 4 + record)
     assert lib.gdn2_chunk_factors_bytes(ctypes.byref(s)) == factors
     assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s)) == 2 * one + factors
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 0
@@ -109,7 +113,7 @@ def test_per_token_gates_need_only_word_alignment():
     assert lib.gdn2_chunk_fwd(ctypes.byref(s), f, f, f, odd, f, f, None, f, None, None, 0, None) == INVALID
     g = [f] * 6 + [f] * 3 + [f] * 3
     g[9] = odd   # dlog_alpha per token, not word aligned
-    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), *g[:6], *g[6:9], f, f, f, *g[9:], None) == INVALID
+    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), *g[:6], *g[6:9], f, f, f, f, *g[9:], None) == INVALID
     s = _shape(T=1, scalar=4)   # w per token in a step; b misaligned
     assert lib.gdn2_step(ctypes.byref(s), f, f, f, f, word, word, None, f, f, None) == INVALID
 
@@ -134,7 +138,11 @@ def test_staged_entry_points_check_arguments():
     assert lib.gdn2_chunk_bwd_factors(ctypes.byref(s), f, f, f, P(0x10008), f, None) == INVALID
     assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), f, f, None, None, None, None) == INVALID
     assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), None, f, None, f, None, None) == INVALID
-    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, f, f, f, f, None, None) == INVALID
+    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, f, f, f, f, f, f, None, None) == INVALID
+    # the factor buffer is required and checked before any launch
+    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, None, f, f, f, f, f, f, None) == INVALID
+    assert lib.gdn2_chunk_bwd_grads(ctypes.byref(s), f, f, f, f, f, f, f, f, f, P(0x10008), f, f, f, f, f, f,
+                                    None) == INVALID
 
 
 def test_step_checks_arguments():

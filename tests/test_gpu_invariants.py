@@ -71,7 +71,7 @@ def test_every_output_element_is_written():
     dstates = torch.full_like(states, float("nan"))
     factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
     dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], dk, d["dS_final"], dstates=dstates)
-    g = gdn2.bwd_grads(*_fargs(d)[:6], d["dO"], states, dstates)
+    g = gdn2.bwd_grads(*_fargs(d)[:6], d["dO"], states, dstates, factors)
     torch.cuda.synchronize()
     for t in [o, sf, states, dstates, dS0] + list(g.values()):
         assert torch.isfinite(t).all()
