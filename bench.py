@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the GDN-2 chunkwise operator (forward + gate-aware backward) on one MI355X.
 
-One step = forward + gate-aware backward (gdn2_chunk_fwd_states,
-gdn2_chunk_bwd_factors, gdn2_chunk_bwd_reverse, gdn2_chunk_bwd_grads: the staged form
-of gdn2_chunk_fwd + gdn2_chunk_bwd that reuses the forward's chunk states) over one batch of the
+One step = forward + gate-aware backward (gdn2_chunk_bwd_factors, gdn2_chunk_fwd_factored,
+gdn2_chunk_bwd_reverse, gdn2_chunk_bwd_grads: the staged form of gdn2_chunk_fwd +
+gdn2_chunk_bwd in which the key-side chunk operands are formed once and the backward
+reuses the forward's chunk states) over one batch of the
 forward/backward workload B=8, T=2048, H=16, dk=dv=128 (bf16 q/k/v, fp32
 gates, decay and state; the 2K x 8 training shape of the Gated DeltaNet-2
 pages).  Inputs are seeded synthetic tensors (linear_attention_sequence_gdn2_amd.inputs)
@@ -37,13 +38,16 @@ HBM_PEAK_GBS = 8000.0
 FWD_BYTES_PER_TOKHEAD = 2816
 BWD_BYTES_PER_TOKHEAD = 5888
 # per-kernel algorithmic bytes per token-head of the four launches of a step:
-#   forward with states : 2816 + chunk states 128*128*4 / 64 tokens = 1024     -> 3840
 #   adjoint factors     : q,k 512 + log_alpha,b 1024
 #                         + factors (128*128 + 64*128)*4 / 64 tokens = 1536
-#                         + chunk operand record 131584 / 64 tokens = 2056      -> 5128
+#                         + chunk operand record 180736 / 64 tokens = 2824      -> 5896
+#   forward sweep       : record operands it reads (Kt, Qt split, Et hi, T, P,
+#                         gamma: 115200 / 64 tokens) 1800 + v 256 + w 512
+#                         + o 512 + chunk states 1024                           -> 4104
 #   reverse sweep       : factors 1536 + dO 512 + dstates 1024                  -> 3072
 #   chunk gradients     : q,k,v 768 + b,w 1024 + dO 512 + states, dstates 2048
-#                         + record 2056 + dq,dk,dv,dlog_alpha,db,dw 3072        -> 9480
+#                         + record (Kt, Et split, T, P^T, G, gamma: 131584 / 64)
+#                         2056 + dq,dk,dv,dlog_alpha,db,dw 3072                 -> 9480
 # with the gates given as bf16 logits each pass reads 1536 -> 768 gate bytes per token-head
 GATE_BYTES_SAVED_PER_TOKHEAD = 768
 LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
@@ -51,8 +55,8 @@ LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
 # gradient written, moves 12 instead of 1536 bytes per token-head
 TOKEN_GATE_BYTES_SAVED_PER_TOKHEAD = 1536 - 12
 TOKEN_WORKLOAD = "gdn_token_bf16_B8H16T2048d128"
-FWD_STATES_BYTES_PER_TOKHEAD = 3840
-BWD_FACTORS_BYTES_PER_TOKHEAD = 5128
+FWD_SWEEP_BYTES_PER_TOKHEAD = 4104
+BWD_FACTORS_BYTES_PER_TOKHEAD = 5896
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
 BWD_GRADS_BYTES_PER_TOKHEAD = 9480
 
@@ -245,17 +249,18 @@ def main():
         factors = torch.empty(gdn2.factors_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv), dtype=torch.uint8, device=dev)
 
         # One training step = four kernel launches:
-        #   fwd_kernel          (gdn2_chunk_fwd_states: o, S_final and the chunk-start states)
-        #   bwd_factors_kernel  (gdn2_chunk_bwd_factors: per-chunk adjoint factors R, Q2)
+        #   bwd_factors_kernel  (gdn2_chunk_bwd_factors: per-chunk adjoint factors R, Q2 and the
+        #                        key-side chunk operands)
+        #   fwd_sweep_kernel    (gdn2_chunk_fwd_factored: o, S_final and the chunk-start states)
         #   bwd_reverse_kernel  (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
         #   bwd_chunk_kernel    (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            o, sf, _ = gdn2.fwd_states(*fargs, states=states)
+            gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"], factors=factors)
             if ev is not None:
                 ev[1].record(stream)
-            gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"], factors=factors)
+            o, sf, _ = gdn2.fwd_factored(factors, d["v"], d["w"], wl.dk, d["S0"], states=states)
             if ev is not None:
                 ev[2].record(stream)
             _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
@@ -288,8 +293,8 @@ def main():
     # algorithmic bytes per launch of each kernel (per token-head figures times
     # B*T*H, plus per-sequence states), from the per-token-head constants above
     kernels = [
-        ("fwd_kernel", "gdn2_chunk_fwd_states", FWD_STATES_BYTES_PER_TOKHEAD * tokheads + state_bytes),
         ("bwd_factors_kernel", "gdn2_chunk_bwd_factors", BWD_FACTORS_BYTES_PER_TOKHEAD * tokheads),
+        ("fwd_sweep_kernel", "gdn2_chunk_fwd_factored", FWD_SWEEP_BYTES_PER_TOKHEAD * tokheads + state_bytes),
         ("bwd_reverse_kernel", "gdn2_chunk_bwd_reverse", BWD_REVERSE_BYTES_PER_TOKHEAD * tokheads + 2 * state_bytes),
         ("bwd_chunk_kernel", "gdn2_chunk_bwd_grads", BWD_GRADS_BYTES_PER_TOKHEAD * tokheads),
     ]
@@ -322,7 +327,7 @@ def main():
                    "chunk": 64, "seed": wl.seed, "qkv": "bf16", "gates_state_grads": "fp32",
                    "parallelism": "single-gpu"},
         "breakdown": {"kernels": per_kernel, "step_event_ms": round(step_ms, 4),
-                      "fwd_tokens_per_s": round(tokens / (k_ms[0] * 1e-3), 1),
+                      "fwd_tokens_per_s": round(tokens / ((k_ms[0] + k_ms[1]) * 1e-3), 1),
                       "step_algorithmic_frac": round(step_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
     }

@@ -136,10 +136,13 @@ int gdn2_chunk_bwd(const gdn2_shape *shape,
 
 /* ---- staged form (training): each call below is exactly one kernel launch ----
  *
- * gdn2_chunk_bwd == gdn2_chunk_states + gdn2_chunk_bwd_factors + gdn2_chunk_bwd_reverse
- *                   + gdn2_chunk_bwd_grads.
- * A training step can instead run gdn2_chunk_fwd_states (which writes the chunk
- * states while producing o) and skip the state sweep in the backward.
+ * gdn2_chunk_bwd == gdn2_chunk_bwd_factors + gdn2_chunk_fwd_factored (states only)
+ *                   + gdn2_chunk_bwd_reverse + gdn2_chunk_bwd_grads.
+ * A training step runs gdn2_chunk_bwd_factors, then gdn2_chunk_fwd_factored (o and the
+ * chunk states), and after the loss gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads,
+ * all on the one factor buffer; the key-side work of every chunk is done once.
+ * gdn2_chunk_fwd_states and gdn2_chunk_states are the same sweeps without a factor
+ * buffer (they form the key-side operands themselves, once per value tile).
  * `states` and `dstates` are [B, H, ceil(T/64), dk, dv] fp32 device buffers of
  * gdn2_chunk_states_bytes() bytes each: states[c] is the state BEFORE chunk c
  * (tokens 64c ..), dstates[c] the loss gradient w.r.t. the state AFTER chunk c. */
@@ -176,6 +179,18 @@ size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
  * gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads. */
 int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k,
                            const void *log_alpha, const void *b, void *factors, void *stream);
+
+/* Forward sweep from the factor buffer that gdn2_chunk_bwd_factors wrote for the same
+ * shape and the same q, k, log_alpha and b (their key-side chunk operands are taken
+ * from it; q, k, log_alpha and b are not read again).  Reads v, w and S0 (NULL =
+ * zeros); writes o [B,T,H,dv] unless NULL, S_final unless NULL, and the chunk-start
+ * states unless NULL; o and states cannot both be NULL.  Results as gdn2_chunk_fwd /
+ * gdn2_chunk_fwd_states.  A training step runs gdn2_chunk_bwd_factors first and uses
+ * the one factor buffer for this forward, gdn2_chunk_bwd_reverse and
+ * gdn2_chunk_bwd_grads.  shape->gate_dtype and gate_scalar describe w. */
+int gdn2_chunk_fwd_factored(const gdn2_shape *shape, const void *factors, const void *v,
+                            const void *w, const float *S0, float *o, float *S_final,
+                            float *states, void *stream);
 
 /* Reverse sweep of the backward from the factors: writes dstates (required) and
  * dS0 (optional), reading dO and dS_final (NULL = zeros). */

@@ -5,11 +5,12 @@
 with ``python -m linear_attention_sequence_gdn2_amd.build``.
 """
 from ._binding import (EXPORTS, LIB_PATH, Gdn2Error, Gdn2Shape, bwd, bwd_factors, bwd_grads,  # noqa: F401
-                       bwd_reverse, bwd_saved, bwd_workspace_bytes, chunk_states, factors_bytes, fwd, fwd_states,
+                       bwd_reverse, bwd_saved, bwd_workspace_bytes, chunk_states, factors_bytes, fwd, fwd_factored,
+                       fwd_states,
                        load, make_shape, output_bwd, output_bwd_workspace_bytes, output_fwd, states_shape,
                        step)
 
 __all__ = ["fwd", "bwd", "fwd_states", "chunk_states", "bwd_factors", "bwd_reverse", "bwd_grads", "bwd_saved",
            "load", "bwd_workspace_bytes", "factors_bytes", "states_shape", "Gdn2Error", "Gdn2Shape", "LIB_PATH",
            "EXPORTS", "make_shape", "step", "output_fwd", "output_bwd",
-           "output_bwd_workspace_bytes"]
+           "output_bwd_workspace_bytes", "fwd_factored"]

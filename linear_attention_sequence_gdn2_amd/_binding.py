@@ -33,7 +33,7 @@ EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
            "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
            "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step", "gdn2_output_fwd",
-           "gdn2_output_bwd_workspace_size", "gdn2_output_bwd"]
+           "gdn2_output_bwd_workspace_size", "gdn2_output_bwd", "gdn2_chunk_fwd_factored"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -79,6 +79,8 @@ def load():
         lib.gdn2_chunk_factors_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_bwd_factors.argtypes = [SP] + [P] * 5 + [P]
         lib.gdn2_chunk_bwd_factors.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_factored.argtypes = [SP] + [P] * 7 + [P]
+        lib.gdn2_chunk_fwd_factored.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_reverse.argtypes = [SP] + [P] * 5 + [P]
         lib.gdn2_chunk_bwd_reverse.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 16 + [P]
@@ -291,6 +293,42 @@ def bwd_factors(q, k, log_alpha, b, factors=None):
     _check(lib.gdn2_chunk_bwd_factors(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(log_alpha), _ptr(b),
                                       _ptr(factors), _stream(q.device)))
     return factors
+
+
+def fwd_factored(factors, v, w, dk, S0=None, want_o=True, want_state=True, states=None, want_states=True):
+    """Forward sweep from the factor buffer of bwd_factors on the same q, k, log_alpha, b
+    (one kernel; q, k, log_alpha, b are not read again): (o or None, S_final or None,
+    states or None).  w is fp32 values [B,T,H,dv] or [B,T,H] (per token), or bf16 logits."""
+    if not v.is_cuda:
+        raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % v.device)
+    B, T, H, dv = v.shape
+    if v.dtype not in (torch.float32, torch.bfloat16) or w.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gdn2: v must be float32 or bfloat16, w float32 values or bfloat16 logits")
+    if w.dtype == torch.bfloat16 and v.dtype != torch.bfloat16:
+        raise TypeError("gdn2: bfloat16 gate logits need bfloat16 q/k/v")
+    sc = _gate_scalar((B, T, H), dict(w=w))
+    if tuple(w.shape) != _gate_shape("w", (B, T, H), dv, sc) or w.device != v.device:
+        raise ValueError("gdn2: w has shape %s, expected %s" % (tuple(w.shape), _gate_shape("w", (B, T, H), dv, sc)))
+    for t in (v, w, S0):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("gdn2: tensors must be contiguous")
+    if S0 is not None and (tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("gdn2: S0 must be float32 [B,H,dk,dv]")
+    if factors.device != v.device or factors.numel() * factors.element_size() < factors_bytes(B, T, H, dk, dv):
+        raise ValueError("gdn2: factors buffer does not match the shape")
+    if not (want_o or want_states):
+        raise ValueError("gdn2: nothing to compute (want_o and want_states are both false)")
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, v.dtype, w.dtype, sc)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=v.device) if want_o else None
+    sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device) if want_state else None
+    if want_states and states is None:
+        states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=v.device)
+    if not want_states:
+        states = None
+    _check(lib.gdn2_chunk_fwd_factored(ctypes.byref(shape), _ptr(factors), _ptr(v), _ptr(w), _ptr(S0), _ptr(o),
+                                       _ptr(sf), _ptr(states), _stream(v.device)))
+    return o, sf, states
 
 
 def bwd_reverse(factors, dO, dk, dS_final=None, want_dS0=True, dstates=None):

@@ -194,6 +194,21 @@ int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k
                                                   gate_scalar(shape), reinterpret_cast<hipStream_t>(stream)));
 }
 
+int gdn2_chunk_fwd_factored(const gdn2_shape *shape, const void *factors, const void *v, const void *w,
+                            const float *S0, float *o, float *S_final, float *states, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!factors || !v || !w || (!o && !states)) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({factors, v, S0, o, S_final, states}) || !gates_aligned(shape, nullptr, nullptr, w))
+        return GDN2_ERR_INVALID_ARG;
+    int vt;
+    gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, o, S_final, states, &vt);
+    f.factors = factors;
+    const gdn2::FwdMode mode = !o ? gdn2::kFwdStates : states ? gdn2::kFwdOutStates : gdn2::kFwdOut;
+    return launch_status(gdn2::launch_fwd_sweep(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
+                                                gate_scalar(shape), mode, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const float *dO,
                            const float *dS_final, float *dstates, float *dS0, void *stream) {
     const int st = check_shape(shape);
@@ -246,9 +261,10 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     float *states = reinterpret_cast<float *>(workspace);
     float *dstates = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + sbytes);
     void *factors = reinterpret_cast<char *>(workspace) + 2 * sbytes;
-    int rc = gdn2_chunk_states(shape, k, v, log_alpha, b, w, S0, states, stream);
+    // the key-side chunk operands once, then the state sweep from them
+    int rc = gdn2_chunk_bwd_factors(shape, q, k, log_alpha, b, factors, stream);
     if (rc != GDN2_OK) return rc;
-    rc = gdn2_chunk_bwd_factors(shape, q, k, log_alpha, b, factors, stream);
+    rc = gdn2_chunk_fwd_factored(shape, factors, v, w, S0, nullptr, nullptr, states, stream);
     if (rc != GDN2_OK) return rc;
     rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     if (rc != GDN2_OK) return rc;

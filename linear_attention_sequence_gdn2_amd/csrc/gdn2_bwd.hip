@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         uint4 rv[NROW];
 #pragma unroll
         for (int it = 0; it < NROW; ++it)
-            rv[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKt + (size_t)(tid + NTH * it) * 16);
+            rv[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKt + (size_t)(tid + NTH * it) * 16);   // Kt, Et planes
         static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
         const int trow = tid >> 3, tc8 = 8 * (tid & 7);
         const uint4 th = *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(trow * kChunk + tc8) * 2);

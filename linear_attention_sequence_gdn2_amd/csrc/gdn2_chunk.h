@@ -369,23 +369,27 @@ constexpr size_t factor_elems_per_chunk() {
 }
 
 // ---- chunk operand record ----
-// The key-side operands of one (batch, head, chunk) that the adjoint-factor kernel forms
-// anyway and the chunk-gradient kernel needs as well, so that they are formed once:
-//   Kt and Et rows     [token][channel] split bf16, hi plane then lo plane, pitch DK
+// The key-side operands of one (batch, head, chunk), formed once by the adjoint-factor
+// kernel and read by the forward sweep and the chunk-gradient kernel:
+//   Kt, Et, Qt rows    [token][channel] split bf16, hi plane then lo plane, pitch DK
 //   T = (I + A)^-1     [row][col] split bf16, hi then lo, pitch 64
 //   P^T fragments      tile (key block w, query block mt) at (4w + mt) * 64 lanes * 8 bf16:
 //                      lane (r, g) holds P[16mt + 4g + i][16w + r], hi (i < 4) then lo;
 //                      only tiles with mt >= w are written (the others are zero)
+//   P fragments        tile (query block w, key block mt) at (4w + mt) * 64 lanes * 8 bf16:
+//                      lane (r, g) holds P[16w + r][16mt + 4g + i], hi then lo; only mt <= w
 //   G                  the log2 decay prefix, per thread of the 512-thread workgroup in
 //                      its element order (token 16w + r, channels DK/2 * hf + ch4(e, g))
 //   gamma              [DK] fp32, the chunk's total decay per key channel
 template <int DK>
 struct ChunkRecord {
-    static constexpr int ROWS = kChunk * DK * 2 * 2;           // bytes of one operand's two row planes
-    static constexpr int oKt = 0, oEt = oKt + ROWS;
-    static constexpr int oT = oEt + ROWS, B_T = kChunk * kChunk * 2 * 2;
-    static constexpr int oPt = oT + B_T, B_PT = 16 * 64 * 8 * 2;
-    static constexpr int oG = oPt + B_PT, B_G = kChunkThreads * (DK / 8) * 4;
+    static constexpr int PLANE = kChunk * DK * 2;               // bytes of one [token][channel] bf16 plane
+    static constexpr int ROWS = 2 * PLANE;                      // an operand's hi and lo planes
+    static constexpr int oKt = 0, oEt = oKt + ROWS, oQt = oEt + ROWS;
+    static constexpr int oT = oQt + ROWS, B_T = kChunk * kChunk * 2 * 2;
+    static constexpr int B_FR = 16 * 64 * 8 * 2;                // 16 fragment tiles of 64 lanes x 8 bf16
+    static constexpr int oPt = oT + B_T, oP = oPt + B_FR;
+    static constexpr int oG = oP + B_FR, B_G = kChunkThreads * (DK / 8) * 4;
     static constexpr int oGam = oG + B_G;
     static constexpr int BYTES = (oGam + DK * 4 + 255) / 256 * 256;
 };

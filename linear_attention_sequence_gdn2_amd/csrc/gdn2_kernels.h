@@ -19,6 +19,7 @@ struct FwdArgs {
     float *o;                       // [B,T,H,dv] (forward) or unused (state sweep)
     float *S_final;                 // may be null
     float *states;                  // chunk-start states (state sweep) or null
+    const void *factors;            // factor buffer with the chunk operand records (sweep from records)
     int B, T, H, dv;
     int nvt;                        // value tiles per (b, h) = dv / value-tile width
     int scalar;                     // kScalar* bits: gates given per token [B,T,H]
@@ -67,6 +68,10 @@ enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
 // gl: the gates are bf16 logits (only with bf16 q/k/v); sg: some gates are given per token
 // (a.scalar; only with bf16 q/k/v and fp32 gate values)
 hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode, hipStream_t st);
+// The same sweep with the key-side operands of every chunk taken from the chunk operand
+// records of the factor buffer (a.factors); q, k, log_alpha and b are not read.
+hipError_t launch_fwd_sweep(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
+                            hipStream_t st);
 // Bytes of the factor buffer of `items` chunks: the adjoint factors R, Q2^T of every chunk,
 // then the chunk operand record of every chunk (read by the chunk-gradient kernel).
 size_t factor_buffer_bytes(long items, int dk);

@@ -167,13 +167,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     }
     __syncthreads();
 
-    // ---- record: Kt and Et rows (dense pitch), P^T fragments ----
+    // ---- record: Kt, Et and Qt rows (dense pitch), P^T fragments ----
+    static_assert((6 * 8 * DK) % NTH == 0, "row planes split evenly over the threads");
 #pragma unroll
-    for (int it = 0; it < DK / 16; ++it) {
+    for (int it = 0; it < 6 * 8 * DK / NTH; ++it) {
         const int idx = tid + NTH * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
         const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
-        const __bf16 *src = (plane < 2 ? sKt : sEt) + (plane & 1) * RK + row * PK + c8;
-        *reinterpret_cast<uint4 *>(rec + Rec::oKt + (size_t)plane * (kChunk * DK * 2) + (size_t)(row * DK + c8) * 2) =
+        const __bf16 *src = (plane < 2 ? sKt : plane < 4 ? sEt : sQt) + (plane & 1) * RK + row * PK + c8;
+        *reinterpret_cast<uint4 *>(rec + Rec::oKt + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
             *reinterpret_cast<const uint4 *>(src);
     }
 #pragma unroll
@@ -230,6 +231,16 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
                 if (!(16 * mt + 4 * g + i <= 16 * w + r)) acc[i] = 0.f;
         }
         Pf[mt] = split4(acc);
+        if (hf == 0 && mt <= w) {
+            // record: P fragment of tile (query block w, key block mt)
+            bf16x8 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = Pf[mt].hi[i];
+                o[4 + i] = Pf[mt].lo[i];
+            }
+            *reinterpret_cast<bf16x8 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
+        }
     }
     __syncthreads();
     solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier

@@ -56,9 +56,10 @@ def test_workspace_and_state_sizes():
     nc = (100 + 63) // 64
     one = 2 * 3 * nc * 128 * 64 * 4
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(s)) == one
-    # per chunk: the adjoint factors R, Q2^T, then the chunk operand record (Kt, Et rows and
-    # T split in bf16, 16 P^T fragment tiles, the decay prefix, gamma; rounded up to 256)
-    record = 4 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4
+    # per chunk: the adjoint factors R, Q2^T, then the chunk operand record (Kt, Et, Qt rows
+    # and T split in bf16, 16 P^T and 16 P fragment tiles, the decay prefix, gamma; rounded
+    # up to 256)
+    record = 6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4
     record = (record + 255) // 256 * 256
     factors = 2 * 3 * nc * ((128 * 128 + 64 * 128) * 4 + record)
     assert lib.gdn2_chunk_factors_bytes(ctypes.byref(s)) == factors
@@ -194,3 +195,18 @@ def test_output_epilogue_checks_arguments():
     assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 0, None, F(1e-6), f, f, f, f, f, need - 1, None) == WORKSPACE
     assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 0, None, F(1e-6), f, None, f, None, None, 0, None) == INVALID
     assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 1, None, F(-0.5), f, f, f, None, None, 0, None) == INVALID
+
+
+def test_factored_forward_checks_arguments():
+    lib = gdn2.load()
+    f = P(0x10000)
+    s = _shape()
+    # factors, v, w required; o and states cannot both be NULL
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), None, f, f, None, f, None, None, None) == INVALID
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, None, f, None, f, None, None, None) == INVALID
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, f, None, None, f, None, None, None) == INVALID
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, f, f, None, None, f, None, None) == INVALID
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), P(0x10008), f, f, None, f, None, None, None) == INVALID
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(_shape(dv=96)), f, f, f, None, f, None, None, None) == UNSUPPORTED
+    # a per-token write gate needs only word alignment; a per-channel one 16 bytes
+    assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, f, P(0x10004), None, f, None, None, None) == INVALID

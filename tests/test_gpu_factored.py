@@ -1,0 +1,123 @@
+"""GPU parity of the forward sweep from the factor buffer (gdn2_chunk_fwd_factored).
+
+The adjoint-factor kernel (gdn2_chunk_bwd_factors) writes the key-side operands of
+every chunk; the sweep takes them from there and reads only v, w and S0.  Outputs
+are checked against the fp64 oracle at the forward's tolerances (1e-4 fp32 q/k/v,
+3e-3 bf16; max-norm relative), states against the oracle's state after every chunk,
+and the whole training chain (factors, this forward, reverse sweep, token gradients)
+against the oracle's gradients (5e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_attention_sequence_gdn2_amd as gdn2
+from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_inputs, make_workload
+from _util import oracle_args, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 3e-3}
+NAMES = ["dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"]
+
+
+def _oracle_inputs(inp):
+    if inp.get("gate_logits"):
+        return [inp["q32"], inp["k32"], inp["v32"], *oracle.gates_from_logits(inp["log_alpha"], inp["b"], inp["w"]),
+                inp["S0"]]
+    if inp.get("gate_scalar"):
+        dk, dv = inp["q"].shape[-1], inp["v"].shape[-1]
+        return [inp["q32"], inp["k32"], inp["v32"],
+                *oracle.gates_per_token(inp["log_alpha"], inp["b"], inp["w"], dk, dv, inp["gate_scalar"]), inp["S0"]]
+    return oracle_args(inp)
+
+
+def _oracle_states(args, T):
+    """States before every chunk: the oracle chained over the input one chunk at a time."""
+    q, k, v, la, b, w, S0 = [oracle._f64(x) if x is not None else None for x in args]
+    B, _, H, dk = q.shape
+    dv = v.shape[-1]
+    out = []
+    S = S0
+    for c0 in range(0, T, 64):
+        out.append(np.zeros((B, H, dk, dv)) if S is None else S)
+        sl = slice(c0, min(c0 + 64, T))
+        _, S = oracle.fwd(q[:, sl], k[:, sl], v[:, sl], la[:, sl], b[:, sl], w[:, sl], S)
+    return np.stack(out, axis=2)
+
+
+def _run(inp, tol, check_states=False):
+    d = to_dev(inp)
+    dk = d["q"].shape[-1]
+    T = d["q"].shape[1]
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    o, sf, states = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"])
+    torch.cuda.synchronize()
+    args = _oracle_inputs(inp)
+    o_ref, sf_ref = oracle.fwd(*args)
+    eo, es = rel_err(o, o_ref), rel_err(sf, sf_ref)
+    print("factored forward: o err %.3e  S_final err %.3e" % (eo, es))
+    assert eo < tol and es < tol, (eo, es)
+    if check_states:
+        et = rel_err(states, _oracle_states(args, T))
+        print("states err %.3e" % et)
+        assert et < tol
+    return d, factors, states
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,qkv,s0", [
+    (1, 1, 1, 32, 32, "f32", 0.5),
+    (1, 64, 2, 64, 64, "f32", 0.5),
+    (2, 65, 1, 128, 128, "f32", 0.5),
+    (1, 200, 3, 128, 128, "bf16", 0.02),
+    (2, 333, 2, 64, 128, "bf16", 0.0),
+    (1, 130, 2, 128, 32, "bf16", 0.1),
+    (3, 257, 2, 32, 64, "f32", 0.1),
+])
+def test_factored_forward_small_shapes(B, T, H, dk, dv, qkv, s0):
+    inp = make_inputs(B, T, H, dk, dv, seed=11 * B + T + dk + dv, qkv_dtype=qkv, s0_std=s0)
+    _run(inp, TOL[qkv], check_states=True)
+
+
+def test_factored_forward_modes_agree():
+    """o only, states only, and both: the same values."""
+    inp = make_inputs(2, 150, 2, 128, 64, seed=4711, s0_std=0.1)
+    d = to_dev(inp)
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    o1, s1, st1 = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"])
+    o2, s2, _ = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"], want_states=False)
+    _, s3, st3 = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"], want_o=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(s1, s3) and torch.equal(st1, st3)
+
+
+@pytest.mark.parametrize("name", ["fwd_bf16_B8H16T2048d128", "long_bf16_B1H16T16384d128",
+                                  "kda_bf16_B4H16T4096d128"])
+def test_factored_forward_full_size(name):
+    wl = WORKLOADS[name]
+    _run(make_workload(wl), TOL[wl.qkv_dtype])
+
+
+@pytest.mark.parametrize("variant", ["logits", "token_gates"])
+def test_factored_forward_gate_formats(variant):
+    if variant == "logits":
+        inp = make_inputs(2, 130, 2, 128, 128, seed=4712, s0_std=0.1, gate_logits=True)
+    else:
+        inp = make_inputs(2, 130, 2, 128, 128, seed=4713, s0_std=0.1, gates="gdn", token_gates=True)
+    _run(inp, TOL["bf16"], check_states=True)
+
+
+def test_training_chain_from_factors():
+    """factors -> factored forward (o, states) -> reverse sweep -> token gradients, on the
+    B4 T4096 H16 d128 training workload, against the oracle's forward and gradients."""
+    inp = make_workload(WORKLOADS["fwdbwd_bf16_B4H16T4096d128"])
+    d, factors, states = _run(inp, TOL["bf16"])
+    dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], 128, d["dS_final"])
+    g = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates, factors)
+    g["dS0"] = dS0
+    torch.cuda.synchronize()
+    ref = oracle.bwd(*_oracle_inputs(inp), inp["dO"], inp["dS_final"])
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e < 5e-3}
+    assert not bad, bad
