@@ -167,11 +167,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         const uint4 th = *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(trow * kChunk + tc8) * 2);
         const uint4 tl =
             *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(kChunk * kChunk + trow * kChunk + tc8) * 2);
-        uint4 pv[4];
+        uint4 pv[4];   // all four tiles, those with mt < w hold zeros
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-            pv[mt] = mt >= w ? *reinterpret_cast<const uint4 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16)
-                             : make_uint4(0u, 0u, 0u, 0u);
+            pv[mt] = *reinterpret_cast<const uint4 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16);
         f32x4 gv[NEH / 4];
 #pragma unroll
         for (int e4 = 0; e4 < NEH / 4; ++e4)

@@ -374,10 +374,12 @@ constexpr size_t factor_elems_per_chunk() {
 //   Kt, Et, Qt rows    [token][channel] split bf16, hi plane then lo plane, pitch DK
 //   T = (I + A)^-1     [row][col] split bf16, hi then lo, pitch 64
 //   P^T fragments      tile (key block w, query block mt) at (4w + mt) * 64 lanes * 8 bf16:
-//                      lane (r, g) holds P[16mt + 4g + i][16w + r], hi (i < 4) then lo;
-//                      only tiles with mt >= w are written (the others are zero)
+//                      lane (r, g) holds P[16mt + 4g + i][16w + r], hi (i < 4) then lo
+//                      (tiles with mt < w are zero and written as such)
 //   P fragments        tile (query block w, key block mt) at (4w + mt) * 64 lanes * 8 bf16:
-//                      lane (r, g) holds P[16w + r][16mt + 4g + i], hi then lo; only mt <= w
+//                      lane (r, g) holds P[16w + r][16mt + 4g + i], hi then lo (zero for mt > w)
+//   Every tile is written, so readers load all four of a block row unconditionally (a
+//   load under a branch would make the compiler wait for all loads in flight).
 //   G                  the log2 decay prefix, per thread of the 512-thread workgroup in
 //                      its element order (token 16w + r, channels DK/2 * hf + ch4(e, g))
 //   gamma              [DK] fp32, the chunk's total decay per key channel

@@ -204,4 +204,32 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nb) {
     return (bid % 8) * (nb / 8) + bid / 8;
 }
 
+// value of lane (quad base + perm[lane & 3]) for a DPP quad permutation
+template <int QPERM>
+__device__ __forceinline__ float quad_perm(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), QPERM, 0xf, 0xf, false));
+}
+
+// 4x4 transpose inside each quad of lanes (lanes 4q .. 4q + 3).  Before, lane j of the
+// quad holds column j of a 4x4 block, x[i] = M[i][j]; after, it holds row j,
+// x[i] = M[j][i].  Two exchange rounds (partner j ^ 1, then j ^ 2, as DPP quad
+// permutations), each swapping 2x2 sub-blocks.  Used to turn the MFMA D layout (a lane
+// holds four rows of one column) into four consecutive columns of one row, for 16-byte
+// global loads and stores.
+__device__ __forceinline__ void quad_transpose4(float (&x)[4]) {
+    const int j = __lane_id() & 3;
+    const bool odd = j & 1, hi = j & 2;
+    constexpr int kXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);   // quad_perm [1, 0, 3, 2]
+    constexpr int kXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);   // quad_perm [2, 3, 0, 1]
+    const float t0 = quad_perm<kXor1>(x[0]), t1 = quad_perm<kXor1>(x[1]);
+    const float t2 = quad_perm<kXor1>(x[2]), t3 = quad_perm<kXor1>(x[3]);
+    const float y0 = odd ? t1 : x[0], y1 = odd ? x[1] : t0, y2 = odd ? t3 : x[2], y3 = odd ? x[3] : t2;
+    const float u0 = quad_perm<kXor2>(y0), u1 = quad_perm<kXor2>(y1);
+    const float u2 = quad_perm<kXor2>(y2), u3 = quad_perm<kXor2>(y3);
+    x[0] = hi ? u2 : y0;
+    x[1] = hi ? u3 : y1;
+    x[2] = hi ? y2 : u0;
+    x[3] = hi ? y3 : u1;
+}
+
 }  // namespace gdn2

@@ -179,16 +179,18 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        if (mt >= w && (mt & 1) == hf) {
+        if ((mt & 1) == hf) {   // every tile is written (zero for mt < w): readers load all four
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (mt >= w) {
 #pragma unroll
-            for (int j = 0; j < NKS; ++j)
-                acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
-                               row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
-            // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
+                for (int j = 0; j < NKS; ++j)
+                    acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
+                                   row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
+                // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
+                for (int i = 0; i < 4; ++i)
+                    if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
+            }
             const Split4 sp = split4(acc);
             bf16x8 o;
 #pragma unroll
@@ -231,8 +233,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
                 if (!(16 * mt + 4 * g + i <= 16 * w + r)) acc[i] = 0.f;
         }
         Pf[mt] = split4(acc);
-        if (hf == 0 && mt <= w) {
-            // record: P fragment of tile (query block w, key block mt)
+        if (hf == 0) {
+            // record: P fragment of tile (query block w, key block mt), zero for mt > w
             bf16x8 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

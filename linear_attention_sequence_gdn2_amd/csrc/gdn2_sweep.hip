@@ -122,13 +122,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
             Tf[kk].hi = *reinterpret_cast<const bf16x8 *>(rec + Rec::oT + o);
             Tf[kk].lo = *reinterpret_cast<const bf16x8 *>(rec + Rec::oT + kChunk * kChunk * 2 + o);
         }
-        // P fragments of query block w (key blocks mt <= w; the rest is zero)
+        // P fragments of query block w (the tiles with mt > w hold zeros)
         Split4 Pf[4];
         if (OUT) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const uint4 u = mt <= w ? *reinterpret_cast<const uint4 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16)
-                                        : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 u = *reinterpret_cast<const uint4 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16);
                 const bf16x8 o = __builtin_bit_cast(bf16x8, u);
                 Pf[mt].hi = __builtin_shufflevector(o, o, 0, 1, 2, 3);
                 Pf[mt].lo = __builtin_shufflevector(o, o, 4, 5, 6, 7);
@@ -261,6 +260,326 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 64-column value tiles: eight waves, one workgroup per CU, next chunk prefetched
+// ---------------------------------------------------------------------------
+// With 32-column tiles the four workgroups of a (batch, head) each read the whole
+// record of every chunk, and every wave its own copy of the Et and Qt rows, right when
+// the chunk starts; the sweep then waits on those loads.  Here a workgroup of eight
+// waves takes 64 columns (half the record reads per head), stages the Kt, Et and Qt
+// rows in LDS once for all waves, and loads each chunk's rows and value inputs while
+// the previous chunk is in its products:
+//   chunk c start      issue T, P, gamma of chunk c; Kt rows, v, w of chunk c + 1
+//   [A] X, Qt S        (Et, Qt rows and S from LDS)                 barrier
+//   [B] U = T X        then Et, Qt rows of chunk c + 1 into LDS      barrier
+//   [C] O; S'          issue Et, Qt rows of chunk c + 2; S' into LDS barrier
+//   Kt rows of chunk c + 1 into LDS
+// Wave (hf, w) owns tokens 16w..16w+15 and columns 32hf..32hf+31 of X, U and O, and
+// the state tiles of one 16-row block (at DK = 128).  bf16 q/k/v only (the X product
+// uses the hi part of Et, so one Et plane is staged); about 155 KB of LDS.
+template <int DK, bool OUT, bool STATES, bool GL, bool SG>
+__global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a) {
+    using Rec = ChunkRecord<DK>;
+    constexpr int VT = 64, NTH = kChunkThreads;
+    constexpr int NKS = DK / 32, NMT = DK / 16;
+    constexpr int NTS = NMT * 4 / 8;                     // state tiles per wave
+    static_assert((NMT * 4) % 8 == 0 && 4 % NTS == 0, "a wave's state tiles share one row block");
+    constexpr int PK = DK + 8, PT = kChunk + 8, RK = kChunk * PK;
+    constexpr int PL16 = kChunk * DK / 8;                // 16-byte pieces of one row plane
+    constexpr int NKP = 2 * PL16 / NTH;                  // Kt pieces per thread
+    constexpr int NEQ = 1 + (OUT ? 2 : 0);               // Et hi, Qt hi and lo
+    constexpr int NEP = NEQ * PL16 / NTH;                // Et/Qt pieces per thread
+    static_assert(NKP * NTH == 2 * PL16 && NEP * NTH == NEQ * PL16, "row planes split evenly");
+
+    __shared__ __align__(16) __bf16 sK[2 * RK];          // Kt rows [token][channel] (hi, lo)
+    __shared__ __align__(16) __bf16 sE[RK];              // Et rows, hi
+    __shared__ __align__(16) __bf16 sQ[OUT ? 2 * RK : 8];   // Qt rows (hi, lo)
+    __shared__ __align__(16) __bf16 sS[2 * VT * PK];     // S^T [col][channel] (hi, lo)
+    __shared__ __align__(16) __bf16 sX[2 * VT * PT];     // X^T [col][token] (hi, lo)
+    __shared__ __align__(16) __bf16 sU[2 * VT * PT];     // U^T [col][token] (hi, lo)
+
+    const int L = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int vt = L % a.nvt, bh = L / a.nvt, h = bh % a.H, b = bh / a.H;
+    const int T = a.T, H = a.H, DV = a.dv;
+    const int j0 = vt * VT;
+    const size_t tokV = (size_t)H * DV;
+    const size_t baseK = ((size_t)b * T * H + h) * DK;
+    const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
+    const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
+    const int NC = (T + kChunk - 1) / kChunk;
+    const char *recs = reinterpret_cast<const char *>(a.factors) +
+                       (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)bh * NC * Rec::BYTES;
+
+    // record pieces of the Kt planes and of the Et/Qt planes, and where they go in LDS
+    auto kt_piece = [&](int c, int it, int tid) {
+        return *reinterpret_cast<const uint4 *>(recs + (size_t)c * Rec::BYTES + Rec::oKt +
+                                                 (size_t)(tid + NTH * it) * 16);
+    };
+    auto kt_store = [&](const uint4 &u, int it, int tid) {
+        const int idx = tid + NTH * it, p = idx / PL16, rem = idx % PL16;
+        *reinterpret_cast<uint4 *>(&sK[p * RK + (rem / (DK / 8)) * PK + 8 * (rem % (DK / 8))]) = u;
+    };
+    auto eq_piece = [&](int c, int it, int tid) {
+        const int idx = tid + NTH * it, p = idx / PL16, rem = idx % PL16;
+        // plane 0: Et hi; planes 1, 2: Qt hi, lo
+        const int src = p == 0 ? Rec::oEt : Rec::oQt + (p - 1) * Rec::PLANE;
+        return *reinterpret_cast<const uint4 *>(recs + (size_t)c * Rec::BYTES + src + (size_t)rem * 16);
+    };
+    auto eq_store = [&](const uint4 &u, int it, int tid) {
+        const int idx = tid + NTH * it, p = idx / PL16, rem = idx % PL16;
+        __bf16 *dst = p == 0 ? sE : sQ + (p - 1) * RK;
+        *reinterpret_cast<uint4 *>(&dst[(rem / (DK / 8)) * PK + 8 * (rem % (DK / 8))]) = u;
+    };
+    // v and w of this wave's X rows: each lane loads four consecutive columns of one token
+    // row (token 16w + 4g + (r & 3), columns 32hf + 16n + 4(r >> 2) ..), and a quad
+    // transpose turns them into the D layout (token 16w + 4g + i, column 32hf + 16n + r)
+    auto load_vw = [&](int c, float (&vv)[2][4], float (&ww)[2][4], int w, int hf, int r, int g) {
+        const int tv = c * kChunk + 16 * w + 4 * g + (r & 3);
+        const size_t row = (size_t)(tv < T ? tv : T - 1);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const size_t off = baseV + row * tokV + 32 * hf + 16 * n + 4 * (r >> 2);
+            const uint2 vr = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.v) + off);
+            vv[n][0] = __builtin_bit_cast(float, vr.x << 16);
+            vv[n][1] = __builtin_bit_cast(float, vr.x & 0xffff0000u);
+            vv[n][2] = __builtin_bit_cast(float, vr.y << 16);
+            vv[n][3] = __builtin_bit_cast(float, vr.y & 0xffff0000u);
+            if (SG && (a.scalar & kScalarWrite)) {
+                const float wt = reinterpret_cast<const float *>(a.wg)[baseK / DK + row * H];
+                ww[n][0] = ww[n][1] = ww[n][2] = ww[n][3] = wt;
+            } else if (GL) {
+                const uint2 wr = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.wg) + off);
+                ww[n][0] = __builtin_bit_cast(float, wr.x << 16);
+                ww[n][1] = __builtin_bit_cast(float, wr.x & 0xffff0000u);
+                ww[n][2] = __builtin_bit_cast(float, wr.y << 16);
+                ww[n][3] = __builtin_bit_cast(float, wr.y & 0xffff0000u);
+            } else {
+                const float4 wr = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.wg) + off);
+                ww[n][0] = wr.x; ww[n][1] = wr.y; ww[n][2] = wr.z; ww[n][3] = wr.w;
+            }
+        }
+    };
+    auto to_d_layout = [](float (&vv)[2][4], float (&ww)[2][4]) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            quad_transpose4(vv[n]);
+            quad_transpose4(ww[n]);
+        }
+    };
+
+    int tid = threadIdx.x;
+    int wv = tid >> 6, w = wv & 3, hf = wv >> 2, l = tid & 63, r = l & 15, g = l >> 4;
+    f32x4 S[NTS];
+#pragma unroll
+    for (int s = 0; s < NTS; ++s) {
+        const int id = wv * NTS + s, m = id / 4, n = id % 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[s][i] = a.S0 ? a.S0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
+    }
+    auto store_state_lds = [&](int wv, int r, int g) {
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+            const int id = wv * NTS + s, m = id / 4, n = id % 4;
+            const Split4 sp = split4(S[s]);
+            *reinterpret_cast<bf16x4 *>(&sS[(16 * n + r) * PK + 16 * m + 4 * g]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&sS[VT * PK + (16 * n + r) * PK + 16 * m + 4 * g]) = sp.lo;
+        }
+    };
+    // prologue: chunk 0's rows into LDS, its value inputs, chunk 1's Et/Qt rows in flight
+    float vv[2][4], ww[2][4], z[2][4];
+    load_vw(0, vv, ww, w, hf, r, g);
+    to_d_layout(vv, ww);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[n][i] = 16 * w + 4 * g + i < T ? gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
+    {
+        uint4 kp[NKP], ep[NEP];
+#pragma unroll
+        for (int it = 0; it < NKP; ++it) kp[it] = kt_piece(0, it, tid);
+#pragma unroll
+        for (int it = 0; it < NEP; ++it) ep[it] = eq_piece(0, it, tid);
+#pragma unroll
+        for (int it = 0; it < NKP; ++it) kt_store(kp[it], it, tid);
+#pragma unroll
+        for (int it = 0; it < NEP; ++it) eq_store(ep[it], it, tid);
+    }
+    uint4 eqn[NEP];                                      // Et/Qt rows of the next chunk
+#pragma unroll
+    for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(NC > 1 ? 1 : 0, it, tid);
+    store_state_lds(wv, r, g);
+    __syncthreads();
+
+    const int nkk = (w >= 2) ? 2 : 1;
+    for (int c = 0; c < NC; ++c) {
+        const int t0 = c * kChunk;
+        const char *rec = recs + (size_t)c * Rec::BYTES;
+        const int cn = c + 1 < NC ? c + 1 : c;           // the next chunk (itself at the end)
+        const int cn2 = c + 2 < NC ? c + 2 : cn;         // the one after
+
+        // ---- loads: T, P, gamma of this chunk; Kt rows, v, w of the next ----
+        Split8 Tf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const size_t o = (size_t)((16 * w + r) * kChunk + (kk < nkk ? 32 * kk : 0) + 8 * g) * 2;
+            Tf[kk].hi = *reinterpret_cast<const bf16x8 *>(rec + Rec::oT + o);
+            Tf[kk].lo = *reinterpret_cast<const bf16x8 *>(rec + Rec::oT + kChunk * kChunk * 2 + o);
+        }
+        uint4 pv[4];
+        if (OUT) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)   // the tiles with mt > w hold zeros
+                pv[mt] = *reinterpret_cast<const uint4 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16);
+        }
+        const f32x4 gam =
+            *reinterpret_cast<const f32x4 *>(rec + Rec::oGam + (size_t)(16 * ((wv * NTS) / 4) + 4 * g) * 4);
+        uint4 ktn[NKP];
+#pragma unroll
+        for (int it = 0; it < NKP; ++it) ktn[it] = kt_piece(cn, it, tid);
+        load_vw(cn, vv, ww, w, hf, r, g);   // z of the next chunk is formed at this chunk's end
+        if (STATES) {
+            // one 16-byte store per tile: the quad transpose gives the lane row 16m + 4g + (r & 3),
+            // columns 16n + 4(r >> 2) ..
+            float *dst = a.states + (((size_t)b * H + h) * NC + c) * (size_t)DK * DV + j0;
+#pragma unroll
+            for (int s = 0; s < NTS; ++s) {
+                const int id = wv * NTS + s, m = id / 4, n = id % 4;
+                float x[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
+                quad_transpose4(x);
+                *reinterpret_cast<float4 *>(&dst[(size_t)(16 * m + 4 * g + (r & 3)) * DV + 16 * n + 4 * (r >> 2)]) =
+                    make_float4(x[0], x[1], x[2], x[3]);
+            }
+        }
+
+        // ---- [A] X = Z - Et S and Qt S: tiles (token block w, column blocks 2hf, 2hf + 1) ----
+        f32x4 QS[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int cb = 2 * hf + n;
+            f32x4 accX = {-z[n][0], -z[n][1], -z[n][2], -z[n][3]};
+            f32x4 accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const Split8 sf = frag_8(&sS[(16 * cb + r) * PK + 32 * j + 8 * g],
+                                         &sS[VT * PK + (16 * cb + r) * PK + 32 * j + 8 * g]);
+                accX = mfma32(*reinterpret_cast<const bf16x8 *>(&sE[(16 * w + r) * PK + 32 * j + 8 * g]), sf.hi, accX);
+                if (OUT)
+                    accQ = mfma32x3(frag_8(&sQ[(16 * w + r) * PK + 32 * j + 8 * g],
+                                           &sQ[RK + (16 * w + r) * PK + 32 * j + 8 * g]), sf, accQ);
+            }
+            const Split4 xs = split4(-accX);  // lane holds X[16w + 4g + i][16cb + r]
+            *reinterpret_cast<bf16x4 *>(&sX[(16 * cb + r) * PT + 16 * w + 4 * g]) = xs.hi;
+            *reinterpret_cast<bf16x4 *>(&sX[VT * PT + (16 * cb + r) * PT + 16 * w + 4 * g]) = xs.lo;
+            QS[n] = accQ;
+            GDN2_SWEEP_FENCE();
+        }
+        __syncthreads();
+
+        // ---- [B] U = T X; then the next chunk's Et/Qt rows into LDS ----
+        {
+            f32x4 accU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk < nkk) {
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        const int cb = 2 * hf + n;
+                        accU[n] = mfma32x3(Tf[kk], frag_8(&sX[(16 * cb + r) * PT + 32 * kk + 8 * g],
+                                                          &sX[VT * PT + (16 * cb + r) * PT + 32 * kk + 8 * g]),
+                                           accU[n]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int cb = 2 * hf + n;
+                const Split4 us = split4(accU[n]);
+                *reinterpret_cast<bf16x4 *>(&sU[(16 * cb + r) * PT + 16 * w + 4 * g]) = us.hi;
+                *reinterpret_cast<bf16x4 *>(&sU[VT * PT + (16 * cb + r) * PT + 16 * w + 4 * g]) = us.lo;
+            }
+        }
+        if (c + 1 < NC) {
+#pragma unroll
+            for (int it = 0; it < NEP; ++it) eq_store(eqn[it], it, tid);
+        }
+        __syncthreads();
+
+        // ---- [C] O = Qt S + P U; S' = diag(gamma) (S + Kt^T U) ----
+#pragma unroll
+        for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(cn2, it, tid);
+        if (OUT) {
+            Split4 Pf[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 o = __builtin_bit_cast(bf16x8, pv[mt]);
+                Pf[mt].hi = __builtin_shufflevector(o, o, 0, 1, 2, 3);
+                Pf[mt].lo = __builtin_shufflevector(o, o, 4, 5, 6, 7);
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int cb = 2 * hf + n;
+                f32x4 acc = QS[n];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (kk < nkk) {
+                        const __bf16 *uh = &sU[(16 * cb + r) * PT + 32 * kk];
+                        const __bf16 *ul = &sU[VT * PT + (16 * cb + r) * PT + 32 * kk];
+                        acc = mfma32x3(join(Pf[2 * kk], Pf[2 * kk + 1]),
+                                       frag_2x4(uh + 4 * g, uh + 16 + 4 * g, ul + 4 * g, ul + 16 + 4 * g), acc);
+                    }
+                }
+                float x[4] = {acc[0], acc[1], acc[2], acc[3]};
+                quad_transpose4(x);   // row 16w + 4g + (r & 3), columns 16cb + 4(r >> 2) ..
+                const int to = t0 + 16 * w + 4 * g + (r & 3);
+                if (to < T)
+                    *reinterpret_cast<float4 *>(&a.o[baseV + (size_t)to * tokV + 16 * cb + 4 * (r >> 2)]) =
+                        make_float4(x[0], x[1], x[2], x[3]);
+                GDN2_SWEEP_FENCE();
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+            const int id = wv * NTS + s, m = id / 4, n = id % 4;
+            f32x4 acc = S[s];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const Split8 kh = frag_tr<PK>(sK, sK + RK, 32 * kk, 16 * m, r, g);   // Kt^T
+                const __bf16 *uh = &sU[(16 * n + r) * PT + 32 * kk];
+                const __bf16 *ul = &sU[VT * PT + (16 * n + r) * PT + 32 * kk];
+                acc = mfma32x3(kh, frag_2x4(uh + 4 * g, uh + 16 + 4 * g, ul + 4 * g, ul + 16 + 4 * g), acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[i];
+            GDN2_SWEEP_FENCE();
+        }
+        store_state_lds(wv, r, g);     // sS is not read again in this chunk
+        __syncthreads();
+        // the next chunk's Kt rows (sK is not read again in this chunk) and its z = w * v,
+        // from loads issued at this chunk's start
+        if (c + 1 < NC) {
+#pragma unroll
+            for (int it = 0; it < NKP; ++it) kt_store(ktn[it], it, tid);
+        }
+        to_d_layout(vv, ww);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                z[n][i] = (c + 1) * kChunk + 16 * w + 4 * g + i < T ? gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
+    }
+
+    if (a.S_final) {
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+            const int id = wv * NTS + s, m = id / 4, n = id % 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.S_final[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = S[s][i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
 
@@ -302,10 +621,49 @@ static hipError_t sweep_mode(const FwdArgs &a, int dk, int vt, FwdMode mode, hip
     }
 }
 
-hipError_t launch_fwd_sweep(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
+template <int DK, bool GL, bool SG, int MODE>
+static hipError_t sweep64_t(const FwdArgs &a, hipStream_t st) {
+    constexpr bool OUT = MODE != kFwdStates, STATES = MODE != kFwdOut;
+    hipLaunchKernelGGL((fwd_sweep64_kernel<DK, OUT, STATES, GL, SG>), dim3((unsigned)(a.B * a.H * a.nvt)),
+                       dim3(kChunkThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <bool GL, bool SG>
+static hipError_t sweep64_mode(const FwdArgs &a, int dk, FwdMode mode, hipStream_t st) {
+    if (dk == 128) {
+        switch (mode) {
+            case kFwdOut: return sweep64_t<128, GL, SG, kFwdOut>(a, st);
+            case kFwdStates: return sweep64_t<128, GL, SG, kFwdStates>(a, st);
+            case kFwdOutStates: return sweep64_t<128, GL, SG, kFwdOutStates>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (dk == 64) {
+        switch (mode) {
+            case kFwdOut: return sweep64_t<64, GL, SG, kFwdOut>(a, st);
+            case kFwdStates: return sweep64_t<64, GL, SG, kFwdStates>(a, st);
+            case kFwdOutStates: return sweep64_t<64, GL, SG, kFwdOutStates>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
                             hipStream_t st) {
-    if (vt > a.dv || a.dv % vt != 0 || ((dk / 16) * (vt / 16)) % 4 != 0) return hipErrorInvalidValue;
     if (gl && sg) return hipErrorInvalidValue;
+    // 64-column tiles (eight waves, one workgroup per CU) when that still gives every CU
+    // a workgroup; otherwise the four-wave kernel at the given tile width
+    if (bf16 && (dk == 64 || dk == 128) && a_in.dv % 64 == 0 && (long)a_in.B * a_in.H * (a_in.dv / 64) >= cu_count()) {
+        FwdArgs a = a_in;
+        a.nvt = a.dv / 64;
+        if (gl) return sweep64_mode<true, false>(a, dk, mode, st);
+        if (sg) return sweep64_mode<false, true>(a, dk, mode, st);
+        return sweep64_mode<false, false>(a, dk, mode, st);
+    }
+    const FwdArgs &a = a_in;
+    if (vt > a.dv || a.dv % vt != 0 || ((dk / 16) * (vt / 16)) % 4 != 0) return hipErrorInvalidValue;
     if (gl) return bf16 ? sweep_mode<true, true, false>(a, dk, vt, mode, st) : hipErrorInvalidValue;
     if (sg) return bf16 ? sweep_mode<true, false, true>(a, dk, vt, mode, st) : hipErrorInvalidValue;
     return bf16 ? sweep_mode<true, false, false>(a, dk, vt, mode, st) : sweep_mode<false, false, false>(a, dk, vt, mode, st);

@@ -121,3 +121,22 @@ def test_training_chain_from_factors():
     print(" ".join("%s=%.2e" % kv for kv in errs.items()))
     bad = {n: e for n, e in errs.items() if not e < 5e-3}
     assert not bad, bad
+
+
+# Shapes with at least one 64-column value tile per CU take the eight-wave sweep
+# (B*H*dv/64 >= 256); ragged T, both key widths it covers, every gate format and mode.
+@pytest.mark.parametrize("B,T,H,dk,dv,extra", [
+    (8, 200, 16, 128, 128, {}),
+    (4, 130, 32, 64, 128, {}),
+    (2, 65, 64, 128, 128, {"s0_std": 0.1}),
+    (8, 150, 16, 128, 128, {"gate_logits": True}),
+    (8, 150, 16, 128, 128, {"gates": "gdn", "token_gates": True}),
+    (8, 150, 16, 128, 128, {"gates": "erase_mean", "token_gates": True}),
+])
+def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
+    inp = make_inputs(B, T, H, dk, dv, seed=B + T + H + dk, **extra)
+    d, factors, states = _run(inp, TOL["bf16"], check_states=True)
+    # states-only mode writes the same states
+    _, _, st2 = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_o=False)
+    torch.cuda.synchronize()
+    assert torch.equal(states, st2)
