@@ -471,7 +471,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
             *reinterpret_cast<bf16x4 *>(&sX[(16 * cb + r) * PT + 16 * w + 4 * g]) = xs.hi;
             *reinterpret_cast<bf16x4 *>(&sX[VT * PT + (16 * cb + r) * PT + 16 * w + 4 * g]) = xs.lo;
             QS[n] = accQ;
-            GDN2_SWEEP_FENCE();
         }
         __syncthreads();
 
@@ -534,8 +533,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
                 if (to < T)
                     *reinterpret_cast<float4 *>(&a.o[baseV + (size_t)to * tokV + 16 * cb + 4 * (r >> 2)]) =
                         make_float4(x[0], x[1], x[2], x[3]);
-                GDN2_SWEEP_FENCE();
-            }
+                }
         }
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
@@ -550,7 +548,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[i];
-            GDN2_SWEEP_FENCE();
         }
         store_state_lds(wv, r, g);     // sS is not read again in this chunk
         __syncthreads();
