@@ -126,6 +126,8 @@ def test_training_chain_from_factors():
 # Shapes with at least one 64-column value tile per CU take the eight-wave sweep
 # (B*H*dv/64 >= 256); ragged T, both key widths it covers, every gate format and mode.
 @pytest.mark.parametrize("B,T,H,dk,dv,extra", [
+    (8, 33, 16, 128, 128, {"s0_std": 0.2}),     # one partial chunk
+    (8, 64, 16, 128, 128, {}),                  # exactly one chunk
     (8, 200, 16, 128, 128, {}),
     (4, 130, 32, 64, 128, {}),
     (2, 65, 64, 128, 128, {"s0_std": 0.1}),
