@@ -139,6 +139,67 @@ def decode_bench(dev, B=64, H=16, dk=128, dv=128, iters=100):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+# MI355X dense bf16 MFMA peak (TFLOP/s) and the forward's useful flops per token-head at
+# dk = dv = 128, chunk C = 64 (the chunk equations, per chunk and head, / 64 tokens):
+#   A = strictly-lower(Et Kt^T)  d C (C - 1)      = 516,096
+#   P = lower(Qt Kt^T)           d C (C + 1)      = 532,480
+#   T = (I + A)^-1               C^3 / 3          =  87,381
+#   X = Z - Et S, Qt S, Kt^T U   3 x 2 C d^2      = 6,291,456
+#   U = T X, P U                 2 x d C (C + 1)  = 1,064,960
+#   -> 8,492,373 per chunk and head = 132,693 per token-head
+MFMA_PEAK_TFLOPS = 2500.0
+FWD_USEFUL_FLOPS_PER_TOKHEAD = 8492373 / 64
+
+
+def _mfma_insts(kernel_key):
+    """MFMA instructions per launch from the committed counter profile (SQ_INSTS_MFMA),
+    if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_digest") != _kernel_sources_digest():
+        return None
+    return rec.get("kernels", {}).get(kernel_key, {}).get("mfma_insts_per_launch")
+
+
+def forward_bench(dev, wl, iters=20):
+    """The inference forward gdn2_chunk_fwd (one fused sweep, o and S_final, no workspace)
+    on the training shape, timed with HIP events."""
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import make_workload
+    x = make_workload(wl)
+    d = {k: x[k].to(dev) for k in ("q", "k", "v", "log_alpha", "b", "w")}
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    for _ in range(3):
+        gdn2.fwd(*args)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        gdn2.fwd(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tokheads = wl.B * wl.T * wl.H
+    nbytes = FWD_BYTES_PER_TOKHEAD * tokheads + wl.B * wl.H * wl.dk * wl.dv * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfl = FWD_USEFUL_FLOPS_PER_TOKHEAD * tokheads / (ms * 1e-3) / 1e12
+    out = {"entry": "gdn2_chunk_fwd", "kernel": "fwd_kernel", "ms": round(ms, 4),
+           "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
+           "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
+           "mfma_useful": {"achieved_TFLOPs": round(tfl, 1), "peak": MFMA_PEAK_TFLOPS,
+                           "frac": round(tfl / MFMA_PEAK_TFLOPS, 4)}}
+    insts = _mfma_insts("fwd_kernel")
+    if insts:
+        ex = insts * 16384 / (ms * 1e-3) / 1e12
+        out["mfma_executed"] = {"achieved_TFLOPs": round(ex, 1), "frac": round(ex / MFMA_PEAK_TFLOPS, 4)}
+    return out
+
+
 # output epilogue (RMS norm, weight, output gate) per token-head at dv = 128, bf16 gate and y:
 #   forward : o 512 + g 256 + y 256                      = 1024
 #   backward: o 512 + g 256 + dy 512 + dO 512 + dg 512   = 2304  (+ dweight partials per workgroup)
@@ -204,6 +265,7 @@ def main():
     ap.add_argument("--no-logit-gates", action="store_true", help="skip the step with bf16 logit gates")
     ap.add_argument("--no-token-gates", action="store_true", help="skip the step with per-token gates")
     ap.add_argument("--no-output", action="store_true", help="skip the output epilogue measurement")
+    ap.add_argument("--no-forward", action="store_true", help="skip the inference-forward measurement")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
@@ -303,6 +365,11 @@ def main():
         gbs = nbytes / (ms * 1e-3) / 1e9
         per_kernel[name] = {"entry": entry, "launch_ms": round(ms, 4), "algorithmic_bytes": nbytes,
                             "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        insts = _mfma_insts(name)
+        if insts:   # executed bf16 MFMA (16x16x32: 16384 flops each), split operands included
+            ex = insts * 16384 / (ms * 1e-3) / 1e12
+            per_kernel[name]["mfma_executed_TFLOPs"] = round(ex, 1)
+            per_kernel[name]["mfma_frac"] = round(ex / MFMA_PEAK_TFLOPS, 4)
     dom = max(range(nk), key=lambda j: k_ms[j])
     name, entry, nbytes = kernels[dom]
     achieved = nbytes / (k_ms[dom] * 1e-3) / 1e9
@@ -353,6 +420,8 @@ def main():
             "kernel_ms": {kn[0]: round(ms, 4) for kn, ms in zip(kernels, tk_ms)},
             "step_event_ms": round(tstep_ms, 4),
             "step_algorithmic_frac": round(talg / (tstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_forward:
+        out["breakdown"]["forward_only"] = forward_bench(dev, wl)
     if not args.no_output:
         out["breakdown"]["output_epilogue"] = output_bench(dev, wl)
     if not args.no_decode:
