@@ -56,6 +56,12 @@ LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
 TOKEN_GATE_BYTES_SAVED_PER_TOKHEAD = 1536 - 12
 TOKEN_WORKLOAD = "gdn_token_bf16_B8H16T2048d128"
 FWD_SWEEP_BYTES_PER_TOKHEAD = 4104
+# the inference forward on shapes with a 64-column value tile per CU: two launches
+#   forward-only records: q,k 512 + log_alpha,b 1024 + the record operands the sweep
+#                         reads (115200 / 64 tokens) 1800                        -> 3336
+#   sweep (o, S_final)  : record operands 1800 + v 256 + w 512 + o 512           -> 3080
+FWD_RECORDS_BYTES_PER_TOKHEAD = 3336
+FWD_INFER_SWEEP_BYTES_PER_TOKHEAD = 3080
 BWD_FACTORS_BYTES_PER_TOKHEAD = 5896
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
 BWD_GRADS_BYTES_PER_TOKHEAD = 9480
@@ -166,8 +172,10 @@ def _mfma_insts(kernel_key):
 
 
 def forward_bench(dev, wl, iters=20):
-    """The inference forward gdn2_chunk_fwd (one fused sweep, o and S_final, no workspace)
-    on the training shape, timed with HIP events."""
+    """The inference forward gdn2_chunk_fwd (o and S_final) on the training shape, timed
+    with HIP events.  At this shape it launches the forward-only chunk-record kernel, then
+    the eight-wave sweep, with the records in a workspace; `hbm` counts the operator's own
+    inputs and outputs, `hbm_with_records` adds the records written and read back."""
     import torch
     import linear_attention_sequence_gdn2_amd as gdn2
     from linear_attention_sequence_gdn2_amd.inputs import make_workload
@@ -185,17 +193,20 @@ def forward_bench(dev, wl, iters=20):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     tokheads = wl.B * wl.T * wl.H
-    nbytes = FWD_BYTES_PER_TOKHEAD * tokheads + wl.B * wl.H * wl.dk * wl.dv * 4
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    state = wl.B * wl.H * wl.dk * wl.dv * 4
+    nbytes = FWD_BYTES_PER_TOKHEAD * tokheads + state
+    kbytes = (FWD_RECORDS_BYTES_PER_TOKHEAD + FWD_INFER_SWEEP_BYTES_PER_TOKHEAD) * tokheads + state
+    gbs, kgbs = nbytes / (ms * 1e-3) / 1e9, kbytes / (ms * 1e-3) / 1e9
     tfl = FWD_USEFUL_FLOPS_PER_TOKHEAD * tokheads / (ms * 1e-3) / 1e12
-    out = {"entry": "gdn2_chunk_fwd", "kernel": "fwd_kernel", "ms": round(ms, 4),
-           "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
+    out = {"entry": "gdn2_chunk_fwd", "kernels": ["bwd_factors_kernel (forward-only records)", "fwd_sweep64_kernel"],
+           "ms": round(ms, 4), "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
            "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
+           "hbm_with_records": {"achieved_GBs": round(kgbs, 1), "frac": round(kgbs / HBM_PEAK_GBS, 4)},
            "mfma_useful": {"achieved_TFLOPs": round(tfl, 1), "peak": MFMA_PEAK_TFLOPS,
                            "frac": round(tfl / MFMA_PEAK_TFLOPS, 4)}}
-    insts = _mfma_insts("fwd_kernel")
-    if insts:
-        ex = insts * 16384 / (ms * 1e-3) / 1e12
+    i1, i2 = _mfma_insts("fwd_records_kernel"), _mfma_insts("fwd_infer_sweep_kernel")
+    if i1 and i2:
+        ex = (i1 + i2) * 16384 / (ms * 1e-3) / 1e12
         out["mfma_executed"] = {"achieved_TFLOPs": round(ex, 1), "frac": round(ex / MFMA_PEAK_TFLOPS, 4)}
     return out
 

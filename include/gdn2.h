@@ -100,13 +100,17 @@ typedef struct {
     int gate_scalar;  /* OR of gdn2_gate_scalar bits; 0 = every gate per channel */
 } gdn2_shape;
 
-/* Bytes of device workspace gdn2_chunk_fwd needs (0 for every supported shape);
- * (size_t)-1 if the shape is invalid. */
+/* Bytes of device workspace gdn2_chunk_fwd needs; (size_t)-1 if the shape is invalid.
+ * 0 when the forward runs as one fused sweep.  With bf16 q/k/v, dk in {64, 128},
+ * dv a multiple of 64 and B*H*dv/64 >= 256 it first writes forward-only chunk
+ * records (the key-side operands of every chunk, about 2.8 KB per token-head at
+ * dk = 128) and then sweeps over them; the workspace holds those records. */
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);
 
 /* Forward pass: o [B,T,H,dv] and the final state S_final [B,H,dk,dv].
  * S0 == NULL means a zero start state; S_final == NULL means it is not wanted.
- * workspace may be NULL when gdn2_chunk_fwd_workspace_size() is 0. */
+ * workspace may be NULL when gdn2_chunk_fwd_workspace_size() is 0; otherwise it must
+ * hold that many bytes (GDN2_ERR_WORKSPACE if not) and is overwritten. */
 int gdn2_chunk_fwd(const gdn2_shape *shape,
                    const void *q, const void *k, const void *v,
                    const void *log_alpha, const void *b, const void *w,

@@ -45,6 +45,14 @@ int check_shape(const gdn2_shape *s) {
 
 int nchunks(const gdn2_shape *s) { return (s->T + 63) / 64; }
 
+// The inference forward takes the record path (forward-only chunk records, then the wide
+// sweep) when the heads give every CU a 64-column tile of its own; otherwise one fused
+// sweep that forms the key-side operands itself.
+bool fwd_uses_records(const gdn2_shape *s) {
+    return s->qkv_dtype == GDN2_BF16 && (s->dk == 64 || s->dk == 128) && s->dv % 64 == 0 &&
+           (long)s->B * s->H * (s->dv / 64) >= 256;
+}
+
 // the alignment a gate tensor (or its gradient) needs: 4 bytes when it is per token
 bool gate_aligned(const gdn2_shape *s, int bit, const void *p) {
     return !p || ((s->gate_scalar & bit) ? aligned4(p) : aligned16(p));
@@ -72,21 +80,38 @@ const char *gdn2_strerror(int status) {
 
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
-    return 0;
+    if (!fwd_uses_records(shape)) return 0;
+    return gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk);
 }
 
 int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
                    const void *log_alpha, const void *b, const void *w, const float *S0, float *o,
                    float *S_final, void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     const int st = check_shape(shape);
     if (st != GDN2_OK) return st;
     if (!q || !k || !v || !log_alpha || !b || !w || !o) return GDN2_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, k, v, S0, o, S_final};
+    const void *ptrs[] = {q, k, v, S0, o, S_final, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
     if (!gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
+    if (fwd_uses_records(shape)) {
+        // forward-only chunk records into the workspace, then the sweep from them
+        if (!workspace || workspace_bytes < gdn2_chunk_fwd_workspace_size(shape)) return GDN2_ERR_WORKSPACE;
+        gdn2::BwdArgs r{};
+        r.B = shape->B; r.T = shape->T; r.H = shape->H; r.DV = shape->dv; r.scalar = shape->gate_scalar;
+        r.q = q; r.k = k; r.la = log_alpha; r.bg = b; r.factors = workspace;
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        const hipError_t e = gdn2::launch_fwd_records(r, shape->dk, true, gate_logits(shape), gate_scalar(shape), hs);
+        if (e != hipSuccess) return GDN2_ERR_HIP;
+        gdn2::FwdArgs f{};
+        f.v = v; f.wg = w; f.S0 = S0; f.o = o; f.S_final = S_final; f.states = nullptr; f.records = workspace;
+        f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv; f.scalar = shape->gate_scalar;
+        const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
+        f.nvt = shape->dv / vt;
+        const hipError_t e2 = gdn2::launch_fwd_sweep(f, shape->dk, vt, true, gate_logits(shape), gate_scalar(shape),
+                                                     gdn2::kFwdOut, hs);
+        return e2 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    }
 
     gdn2::FwdArgs a{};
     a.q = q; a.k = k; a.v = v;
@@ -203,7 +228,11 @@ int gdn2_chunk_fwd_factored(const gdn2_shape *shape, const void *factors, const 
         return GDN2_ERR_INVALID_ARG;
     int vt;
     gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, o, S_final, states, &vt);
-    f.factors = factors;
+    {
+        const long items = (long)shape->B * shape->H * nchunks(shape);
+        f.records = reinterpret_cast<const char *>(factors) + (gdn2::factor_buffer_bytes(items, shape->dk) -
+                                                               gdn2::record_buffer_bytes(items, shape->dk));
+    }
     const gdn2::FwdMode mode = !o ? gdn2::kFwdStates : states ? gdn2::kFwdOutStates : gdn2::kFwdOut;
     return launch_status(gdn2::launch_fwd_sweep(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                                 gate_scalar(shape), mode, reinterpret_cast<hipStream_t>(stream)));

@@ -19,7 +19,7 @@ struct FwdArgs {
     float *o;                       // [B,T,H,dv] (forward) or unused (state sweep)
     float *S_final;                 // may be null
     float *states;                  // chunk-start states (state sweep) or null
-    const void *factors;            // factor buffer with the chunk operand records (sweep from records)
+    const void *records;            // chunk operand records of (b, h, c) at (b * H + h) * NC + c (sweep)
     int B, T, H, dv;
     int nvt;                        // value tiles per (b, h) = dv / value-tile width
     int scalar;                     // kScalar* bits: gates given per token [B,T,H]
@@ -75,7 +75,11 @@ hipError_t launch_fwd_sweep(const FwdArgs &a, int dk, int vt, bool bf16, bool gl
 // Bytes of the factor buffer of `items` chunks: the adjoint factors R, Q2^T of every chunk,
 // then the chunk operand record of every chunk (read by the chunk-gradient kernel).
 size_t factor_buffer_bytes(long items, int dk);
+// Bytes of `items` chunk operand records alone (the forward-only buffer).
+size_t record_buffer_bytes(long items, int dk);
 hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
+// Forward-only records: a.factors receives just the records the forward sweep reads.
+hipError_t launch_fwd_records(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 hipError_t launch_bwd_reverse(const BwdArgs &a, int dk, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 

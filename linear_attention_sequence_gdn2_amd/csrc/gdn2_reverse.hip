@@ -50,7 +50,9 @@ __device__ __forceinline__ Split8 frag_from_tiles(const uint4 &t0, const uint4 &
 // ---------------------------------------------------------------------------
 // Eight waves in two halves, as in bwd_chunk_kernel: wave (hf, w) owns tokens
 // 16w..16w+15 and, for the element work, the channels of half hf.
-template <int DK, bool BF16, bool GL, bool SG>
+// FWD: forward-only records (a.factors holds just the records): the rows, T, P and gamma
+// that the forward sweep reads, without the adjoint factors, P^T, G or the Et lo plane.
+template <int DK, bool BF16, bool GL, bool SG, bool FWD>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     };
     __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
     // this item's chunk operand record, after the factors of all items
-    char *rec = reinterpret_cast<char *>(a.factors) + (size_t)nitems * factor_elems_per_chunk<DK>() * 2 +
+    char *rec = reinterpret_cast<char *>(a.factors) + (FWD ? 0 : (size_t)nitems * factor_elems_per_chunk<DK>() * 2) +
                 (size_t)L * Rec::BYTES;
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
@@ -140,10 +142,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
                 reinterpret_cast<float *>(rec + Rec::oGam)[ch(e)] = gm;
             }
         }
+        if (!FWD) {
 #pragma unroll
-        for (int e = 0; e < NEH; e += 4)
-            *reinterpret_cast<f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + e) * 4) =
-                f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
+            for (int e = 0; e < NEH; e += 4)
+                *reinterpret_cast<f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + e) * 4) =
+                    f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
+        }
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
             f32x4 et, qt, kt;
@@ -174,12 +178,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         const int idx = tid + NTH * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
         const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
         const __bf16 *src = (plane < 2 ? sKt : plane < 4 ? sEt : sQt) + (plane & 1) * RK + row * PK + c8;
-        *reinterpret_cast<uint4 *>(rec + Rec::oKt + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
-            *reinterpret_cast<const uint4 *>(src);
+        if (!(FWD && plane == 3))   // the forward sweep reads the hi plane of Et only
+            *reinterpret_cast<uint4 *>(rec + Rec::oKt + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
+                *reinterpret_cast<const uint4 *>(src);
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        if ((mt & 1) == hf) {   // every tile is written (zero for mt < w): readers load all four
+        if (!FWD && (mt & 1) == hf) {   // every tile is written (zero for mt < w): readers load all four
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (mt >= w) {
 #pragma unroll
@@ -254,6 +259,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
                                   *reinterpret_cast<const f32x4 *>(&sAT[row * PA + c8 + 4]));
         *reinterpret_cast<bf16x8 *>(rec + Rec::oT + (size_t)(row * kChunk + c8) * 2) = ts.hi;
         *reinterpret_cast<bf16x8 *>(rec + Rec::oT + (size_t)(kChunk * kChunk + row * kChunk + c8) * 2) = ts.lo;
+    }
+    if (FWD) {
+        __syncthreads();   // the next item overwrites the LDS this one still reads
+        continue;
     }
 
     // ---- W = T Et: tiles (token block w, channel blocks of half hf) ----
@@ -485,30 +494,49 @@ size_t factor_buffer_bytes(long items, int dk) {
     }
 }
 
-template <int DK, bool BF16, bool GL, bool SG>
+size_t record_buffer_bytes(long items, int dk) {
+    switch (dk) {
+        case 32: return (size_t)items * ChunkRecord<32>::BYTES;
+        case 64: return (size_t)items * ChunkRecord<64>::BYTES;
+        case 128: return (size_t)items * ChunkRecord<128>::BYTES;
+        default: return 0;
+    }
+}
+
+template <int DK, bool BF16, bool GL, bool SG, bool FWD>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
     const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);
     // one persistent workgroup per CU (the kernel's LDS allows no second one)
     const long grid = items < cu_count() ? items : cu_count();
-    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL, SG>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL, SG, FWD>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st,
+                       a);
     return hipGetLastError();
 }
 
-template <bool BF16, bool GL, bool SG>
+template <bool BF16, bool GL, bool SG, bool FWD>
 static hipError_t factors_dk(const BwdArgs &a, int dk, hipStream_t st) {
     switch (dk) {
-        case 32: return factors_t<32, BF16, GL, SG>(a, st);
-        case 64: return factors_t<64, BF16, GL, SG>(a, st);
-        case 128: return factors_t<128, BF16, GL, SG>(a, st);
+        case 32: return factors_t<32, BF16, GL, SG, FWD>(a, st);
+        case 64: return factors_t<64, BF16, GL, SG, FWD>(a, st);
+        case 128: return factors_t<128, BF16, GL, SG, FWD>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
+template <bool FWD>
+static hipError_t factors_any(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
     if (gl && sg) return hipErrorInvalidValue;
-    if (gl) return bf16 ? factors_dk<true, true, false>(a, dk, st) : hipErrorInvalidValue;
-    if (sg) return bf16 ? factors_dk<true, false, true>(a, dk, st) : hipErrorInvalidValue;
-    return bf16 ? factors_dk<true, false, false>(a, dk, st) : factors_dk<false, false, false>(a, dk, st);
+    if (gl) return bf16 ? factors_dk<true, true, false, FWD>(a, dk, st) : hipErrorInvalidValue;
+    if (sg) return bf16 ? factors_dk<true, false, true, FWD>(a, dk, st) : hipErrorInvalidValue;
+    return bf16 ? factors_dk<true, false, false, FWD>(a, dk, st) : factors_dk<false, false, false, FWD>(a, dk, st);
+}
+
+hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
+    return factors_any<false>(a, dk, bf16, gl, sg, st);
+}
+
+hipError_t launch_fwd_records(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st) {
+    return factors_any<true>(a, dk, bf16, gl, sg, st);
 }
 
 template <int DK, int VT>

@@ -56,9 +56,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
     const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
     const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
     const int NC = (T + kChunk - 1) / kChunk;
-    // records of this (batch, head), after the adjoint factors of all chunks
-    const char *recs = reinterpret_cast<const char *>(a.factors) +
-                       (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)bh * NC * Rec::BYTES;
+    // records of this (batch, head)
+    const char *recs = reinterpret_cast<const char *>(a.records) + (size_t)bh * NC * Rec::BYTES;
 
     f32x4 S[NTS];
 #pragma unroll
@@ -306,8 +305,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
     const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
     const int NC = (T + kChunk - 1) / kChunk;
-    const char *recs = reinterpret_cast<const char *>(a.factors) +
-                       (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)bh * NC * Rec::BYTES;
+    const char *recs = reinterpret_cast<const char *>(a.records) + (size_t)bh * NC * Rec::BYTES;
 
     // record pieces of the Kt planes and of the Et/Qt planes, and where they go in LDS
     auto kt_piece = [&](int c, int it, int tid) {

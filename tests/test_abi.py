@@ -210,3 +210,22 @@ def test_factored_forward_checks_arguments():
     assert lib.gdn2_chunk_fwd_factored(ctypes.byref(_shape(dv=96)), f, f, f, None, f, None, None, None) == UNSUPPORTED
     # a per-token write gate needs only word alignment; a per-channel one 16 bytes
     assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, f, P(0x10004), None, f, None, None, None) == INVALID
+
+
+def test_forward_workspace_on_wide_shapes():
+    """With one 64-column tile per CU or more, the forward writes forward-only chunk
+    records first: it needs a workspace of one record per (batch, head, chunk)."""
+    lib = gdn2.load()
+    f = P(0x10000)
+    wide = _shape(B=8, T=2048, H=16, dk=128, dv=128)
+    record = 6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4
+    record = (record + 255) // 256 * 256
+    need = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(wide))
+    assert need == 8 * 16 * 32 * record
+    F = ctypes.c_size_t
+    assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, None, F(0), None) == WORKSPACE
+    assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, f, F(need - 1), None) == WORKSPACE
+    # fp32 q/k/v, or too few heads for the wide tiles: one fused sweep, no workspace
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0))) == 0
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=16384, H=16, dk=128, dv=128))) == 0
+

@@ -140,5 +140,9 @@ def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
     d, factors, states = _run(inp, TOL["bf16"], check_states=True)
     # states-only mode writes the same states
     _, _, st2 = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_o=False)
+    # the inference forward takes forward-only records at these shapes: the same arithmetic
+    o_f, sf_f, _ = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_states=False)
+    o_i, sf_i = gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
     torch.cuda.synchronize()
     assert torch.equal(states, st2)
+    assert torch.equal(o_i, o_f) and torch.equal(sf_i, sf_f)
