@@ -268,7 +268,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 const Split8 sf = frag_tr<PS>(S1, S1 + DK * PS, 32 * j, 16 * n, r, g);
                 if (FAST) acc = mfma32(ef.hi, sf.hi, acc);
                 else acc = mfma32x3(ef, sf, acc);
-                if (j & 1) GDN2_SCHED_FENCE();
             }
             const Split4 sx = split4(-acc);    // lane holds X[16w + 4g + i][16n + r]
             *reinterpret_cast<bf16x4 *>(&XU[(16 * n + r) * PT + 16 * w + 4 * g]) = sx.hi;
@@ -286,7 +285,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             for (int j = 0; j < NKS; ++j) {
                 du = mfma32x3(row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g),
                               frag_tr<PS>(D1, D1 + DK * PS, 32 * j, 16 * n, r, g), du);
-                GDN2_SCHED_FENCE();
             }
             const Split4 sd = split4(du);
             *reinterpret_cast<bf16x4 *>(&dUX[(16 * n + r) * PT + 16 * w + 4 * g]) = sd.hi;
@@ -343,14 +341,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 const __bf16 *dh = &D1[(16 * m + r) * PS], *dl = dh + DK * PS;
                 aH[mm] = mfma32x3(frag_2x4(dh + 4 * g, dh + 16 + 4 * g, dl + 4 * g, dl + 16 + 4 * g), uT,
                                   aH[mm]);           // (U (gamma dS')^T)^T = gamma * dKh^T
-                GDN2_SCHED_FENCE();
             }
             const Split8 lhs = hf ? xT : oT;         // dO U^T or -dX U^T
 #pragma unroll
             for (int nn = 0; nn < 4; ++nn)
                 if (nn <= w) {
                     aPA[nn] = mfma32x3(lhs, frag_tr<PT>(XU, XU + VT * PT, 0, 16 * nn, r, g), aPA[nn]);
-                    GDN2_SCHED_FENCE();
                 }
         }
         __syncthreads();
