@@ -102,10 +102,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         raw.issue(a.q, a.k, a.la, a.bg, row0, g, v0, (row0 - chh) / DK, a.scalar);
     }
     for (int L = blockIdx.x; L < nitems; L += gridDim.x) {
-    // lane indices afresh from an opaque copy of the thread index: the address
-    // arithmetic is redone per item instead of being held in registers across items
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
+    const int tid = threadIdx.x;
     const int wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int nkk = (w >= 2) ? 2 : 1;
     const int chh = hf * (DK / 2);
@@ -125,12 +122,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     {
         float qf[NEH], kf[NEH], G[NEH], bgf[NEH], gC[NEH];
         raw.unpack(qf, kf, G, bgf);
-        {
-            const int Ln = L + (int)gridDim.x < nitems ? L + (int)gridDim.x : L;
-            bool vn;
-            const size_t rown = item_row(Ln, vn);
-            raw.issue(a.q, a.k, a.la, a.bg, rown, g, vn, (rown - chh) / DK, a.scalar);
-        }
 #pragma unroll
         for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
         chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
@@ -205,6 +196,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
             }
             *reinterpret_cast<bf16x8 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
         }
+    }
+
+    {
+        // the next item's key-side inputs, issued after this item's row stores: issued at the
+        // top of the item they would queue behind the previous item's factor stores
+        const int Ln = L + (int)gridDim.x < nitems ? L + (int)gridDim.x : L;
+        bool vn;
+        const size_t rown = item_row(Ln, vn);
+        raw.issue(a.q, a.k, a.la, a.bg, rown, g, vn, (rown - chh) / DK, a.scalar);
     }
 
     // ---- A (shared out between the halves) and the rows of P of query block w ----
