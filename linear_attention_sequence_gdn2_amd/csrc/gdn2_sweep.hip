@@ -409,28 +409,35 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     __syncthreads();
 
     const int nkk = (w >= 2) ? 2 : 1;
-    for (int c = 0; c < NC; ++c) {
-        const int t0 = c * kChunk;
-        const char *rec = recs + (size_t)c * Rec::BYTES;
-        const int cn = c + 1 < NC ? c + 1 : c;           // the next chunk (itself at the end)
-        const int cn2 = c + 2 < NC ? c + 2 : cn;         // the one after
-
-        // ---- loads: T, P, gamma of this chunk; Kt rows, v, w of the next ----
-        Split8 Tf[2];
+    // T, P and gamma of a chunk are loaded during the previous chunk, each right after its last
+    // use there, so they are in flight across a whole stage without extra registers
+    auto load_T = [&](const char *rc, Split8 (&tf)[2]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const size_t o = (size_t)((16 * w + r) * kChunk + (kk < nkk ? 32 * kk : 0) + 8 * g) * 2;
-            Tf[kk].hi = *reinterpret_cast<const bf16x8 *>(rec + Rec::oT + o);
-            Tf[kk].lo = *reinterpret_cast<const bf16x8 *>(rec + Rec::oT + kChunk * kChunk * 2 + o);
+            tf[kk].hi = *reinterpret_cast<const bf16x8 *>(rc + Rec::oT + o);
+            tf[kk].lo = *reinterpret_cast<const bf16x8 *>(rc + Rec::oT + kChunk * kChunk * 2 + o);
         }
-        uint4 pv[4];
-        if (OUT) {
+    };
+    auto load_P = [&](const char *rc, uint4 (&p)[4]) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)   // the tiles with mt > w hold zeros
-                pv[mt] = *reinterpret_cast<const uint4 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16);
-        }
-        const f32x4 gam =
-            *reinterpret_cast<const f32x4 *>(rec + Rec::oGam + (size_t)(16 * ((wv * NTS) / 4) + 4 * g) * 4);
+        for (int mt = 0; mt < 4; ++mt)   // the tiles with mt > w hold zeros
+            p[mt] = *reinterpret_cast<const uint4 *>(rc + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16);
+    };
+    auto load_gam = [&](const char *rc) {
+        return *reinterpret_cast<const f32x4 *>(rc + Rec::oGam + (size_t)(16 * ((wv * NTS) / 4) + 4 * g) * 4);
+    };
+    Split8 Tf[2];
+    uint4 pv[4];
+    load_T(recs, Tf);
+    if (OUT) load_P(recs, pv);
+    f32x4 gam = load_gam(recs);
+    for (int c = 0; c < NC; ++c) {
+        const int t0 = c * kChunk;
+        const int cn = c + 1 < NC ? c + 1 : c;           // the next chunk (itself at the end)
+        const int cn2 = c + 2 < NC ? c + 2 : cn;         // the one after
+
+        // ---- loads: Kt rows, v, w of the next chunk (T, P and gamma of this one are in flight) ----
         uint4 ktn[NKP];
 #pragma unroll
         for (int it = 0; it < NKP; ++it) ktn[it] = kt_piece(cn, it, tid);
@@ -487,6 +494,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
                     }
                 }
             }
+            load_T(recs + (size_t)cn * Rec::BYTES, Tf);
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int cb = 2 * hf + n;
@@ -532,6 +540,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
                     *reinterpret_cast<float4 *>(&a.o[baseV + (size_t)to * tokV + 16 * cb + 4 * (r >> 2)]) =
                         make_float4(x[0], x[1], x[2], x[3]);
                 }
+            load_P(recs + (size_t)cn * Rec::BYTES, pv);
         }
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
@@ -547,6 +556,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[i];
         }
+        gam = load_gam(recs + (size_t)cn * Rec::BYTES);
         store_state_lds(wv, r, g);     // sS is not read again in this chunk
         __syncthreads();
         // the next chunk's Kt rows (sK is not read again in this chunk) and its z = w * v,
