@@ -150,11 +150,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     load_tile(0, cur, tid);
 
     // ---- preparation: the chunk operand record that the adjoint-factor kernel wrote
-    // (Kt and Et rows, T, P^T fragments, the decay prefix G and gamma), into LDS and registers
+    // (Kt and Et rows, T, P^T fragments and gamma), into LDS and registers
     using Rec = ChunkRecord<DK>;
     const char *rec = reinterpret_cast<const char *>(a.factors) +
                       (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)L * Rec::BYTES;
-    float Gk[NEH];                 // decay prefix, kept for the element-wise chain of the epilogue
     Split4 Pt[4];                  // lane holds P[16mt + 4g + i][16w + r] (zero for mt < w)
     {
         constexpr int NROW = DK / 16;   // 16-byte pieces per thread of the four row planes
@@ -171,10 +170,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
             pv[mt] = *reinterpret_cast<const uint4 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16);
-        f32x4 gv[NEH / 4];
-#pragma unroll
-        for (int e4 = 0; e4 < NEH / 4; ++e4)
-            gv[e4] = *reinterpret_cast<const f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + 4 * e4) * 4);
         if (tid < DK) sGam[tid] = reinterpret_cast<const float *>(rec + Rec::oGam)[tid];
 #pragma unroll
         for (int it = 0; it < NROW; ++it) {
@@ -190,8 +185,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             Pt[mt].hi = __builtin_shufflevector(o, o, 0, 1, 2, 3);
             Pt[mt].lo = __builtin_shufflevector(o, o, 4, 5, 6, 7);
         }
-#pragma unroll
-        for (int e = 0; e < NEH; ++e) Gk[e] = gv[e / 4][e % 4];
     }
     __syncthreads();
     float gm[NSF];
@@ -353,8 +346,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     }
 
     // ---- epilogue: dgamma, dP/dA products, element-wise chain ----
-    // The decay prefix G stayed in registers through the value loop; q, k and b are read
-    // again (their log-decay values are not used, so those loads are dropped).  The lane
+    // q, k and b are read again (their log-decay values are not used, so those loads are
+    // dropped), and the decay prefix G comes from the record here: only this chain uses it, and
+    // leaving it out of the preparation shortens the loads the first value tile waits for.  The lane
     // indices are derived afresh from an opaque copy of the thread index, so that no
     // address arithmetic of the preparation is kept live across the value loop.
   {
@@ -416,11 +410,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
     KeyRaw4<DK / 2, BF16, GL, SG> raw;
     raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk, srowK, a.scalar);
+    f32x4 gv[NEH / 4];             // the decay prefix of this thread's elements, from the record
+#pragma unroll
+    for (int e4 = 0; e4 < NEH / 4; ++e4)
+        gv[e4] = *reinterpret_cast<const f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + 4 * e4) * 4);
     raw.unpack(qf, kf, G, bgf);
     float dact[NEH];               // d log_alpha / d stored decay input
     raw.decay_dact_all(dact);
 #pragma unroll
-    for (int e = 0; e < NEH; ++e) G[e] = Gk[e];
+    for (int e = 0; e < NEH; ++e) G[e] = gv[e / 4][e % 4];
     {
         // Qt rows of this half's channels again
 #pragma unroll
