@@ -114,35 +114,67 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     // ---- value-tile inputs, loaded one tile ahead into registers ----
     struct Tile {
         float4 s[NSF], d[NSF];   // S and dS' (channel idx/8, columns 4*(idx%8)..+3)
-        float o[4];              // dO (column tid%32, tokens 4*(tid/32)..+3)
-        float v[4], wg[4];       // v and w of this wave's X tile, D layout
+        float o[4];              // dO; after the quad transpose: column tid%32, tokens 4*(tid/32)..+3
+        float v[4], wg[4];       // v and w of this wave's X tile; D layout after the quad transpose
     };
+    // Addresses: a base pointer common to the workgroup (this item's chunk and the tile's first
+    // column) plus a 32-bit byte offset per lane; the offsets stay inside one chunk of one (b, h),
+    // so they fit, and the loads take the scalar-base + vector-offset form.
+    const unsigned last = (unsigned)(T - 1 - t0);   // last existing token of the chunk, from t0
+    const size_t tokBase = baseV0 + (size_t)t0 * tokV;
+    constexpr unsigned ES = BF16 ? 2u : 4u, GS = GL ? 2u : 4u;
     auto load_tile = [&](int j0, Tile &x, int tid) {
         const int w = (tid >> 6) & 3, n = tid >> 8, r = tid & 15, g = (tid >> 4) & 3;
+        const char *sb = reinterpret_cast<const char *>(a.states + stoff + j0);
+        const char *db = reinterpret_cast<const char *>(a.dstates + stoff + j0);
 #pragma unroll
         for (int it = 0; it < NSF; ++it) {
             int idx = tid + NTH * it;
             idx = idx < DK * 8 ? idx : 0;
-            const size_t off = stoff + (size_t)(idx >> 3) * DV + j0 + 4 * (idx & 7);
-            x.s[it] = *reinterpret_cast<const float4 *>(a.states + off);
-            x.d[it] = *reinterpret_cast<const float4 *>(a.dstates + off);
+            const unsigned o = (unsigned)((idx >> 3) * DV + 4 * (idx & 7)) * 4u;
+            x.s[it] = *reinterpret_cast<const float4 *>(sb + o);
+            x.d[it] = *reinterpret_cast<const float4 *>(db + o);
         }
+        // Wide loads: a lane reads 4 consecutive columns of one token; the 4x4 transpose inside
+        // each quad of lanes, done at staging, turns that into one column of 4 tokens.
         {
-            const int col = tid & 31, tg = tid >> 5;
+            // dO: token 4 (tid / 32) + (tid % 4), columns 4 ((tid / 4) % 8) ..; after the
+            // transpose: column tid % 32, tokens 4 (tid / 32) ..
+            const char *ob = reinterpret_cast<const char *>(a.dO + tokBase + j0);
+            const unsigned tr = min((unsigned)(4 * (tid >> 5) + (tid & 3)), last);
+            const float4 o4 =
+                *reinterpret_cast<const float4 *>(ob + (tr * (unsigned)tokV + 4u * ((tid >> 2) & 7)) * 4u);
+            x.o[0] = o4.x, x.o[1] = o4.y, x.o[2] = o4.z, x.o[3] = o4.w;
+        }
+        // v and w of the X tile: row 16w + 4g + (r % 4), columns 16n + 4 (r / 4) ..; after the
+        // transpose: rows 16w + 4g + i, column 16n + r (the D layout)
+        const unsigned vr = min((unsigned)(16 * w + 4 * g + (r & 3)), last);
+        const unsigned vo = vr * (unsigned)tokV + (unsigned)(16 * n + 4 * (r >> 2));
+        auto load4 = [](const char *p, bool b16, float (&y)[4]) {
+            if (b16) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(p);
+                y[0] = __uint_as_float(u.x << 16), y[1] = __uint_as_float(u.x & 0xffff0000u);
+                y[2] = __uint_as_float(u.y << 16), y[3] = __uint_as_float(u.y & 0xffff0000u);
+            } else {
+                const float4 f = *reinterpret_cast<const float4 *>(p);
+                y[0] = f.x, y[1] = f.y, y[2] = f.z, y[3] = f.w;
+            }
+        };
+        load4(reinterpret_cast<const char *>(a.v) + ((tokBase + j0) + vo) * ES, BF16, x.v);
+        if constexpr (SG) {
+            // gates per token or per channel (decided at run time): element loads, D layout as loaded
+            const bool wtok = a.scalar & kScalarWrite;
+            const char *wb = reinterpret_cast<const char *>(a.wg) +
+                             (wtok ? baseK / DK + (size_t)t0 * H : tokBase + j0) * GS;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 4 * tg + i;
-                x.o[i] = a.dO[baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + col];
+                const unsigned tr = min((unsigned)(16 * w + 4 * g + i), last);
+                const unsigned ow = wtok ? tr * (unsigned)H : tr * (unsigned)tokV + (unsigned)(16 * n + r);
+                x.wg[i] = GL ? bf16_bits_to_float(*reinterpret_cast<const uint16_t *>(wb + ow * GS))
+                             : *reinterpret_cast<const float *>(wb + ow * GS);
             }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * w + 4 * g + i;
-            const size_t off = baseV0 + (size_t)(t < T ? t : T - 1) * tokV + j0 + 16 * n + r;
-            const size_t offw = (SG && (a.scalar & kScalarWrite)) ? baseK / DK + (size_t)(t < T ? t : T - 1) * H
-                                                                   : off;
-            x.v[i] = load1<BF16>(a.v, off, true);
-            x.wg[i] = load_gate1<GL>(a.wg, offw);   // as stored (activated at use)
+        } else {
+            load4(reinterpret_cast<const char *>(a.wg) + ((tokBase + j0) + vo) * GS, GL, x.wg);   // as stored
         }
     };
 
@@ -230,6 +262,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 *reinterpret_cast<bf16x4 *>(&D1[DK * PS + chn * PS + 4 * q]) = ds.lo;
             }
         }
+        quad_transpose4(cur.o);
+        quad_transpose4(cur.v);
+        if constexpr (!SG) quad_transpose4(cur.wg);
         {
             const int col = tid & 31, tg = tid >> 5;
             f32x4 ov;
@@ -299,14 +334,19 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                                frag_2x4(dh + 4 * g, dh + 16 + 4 * g, dl + 4 * g, dl + 16 + 4 * g), dXr);
             }
         }
+        {
+            char *dvb = reinterpret_cast<char *>(a.dv + tokBase + j0);
+            char *dwb = reinterpret_cast<char *>(a.dw + tokBase + j0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * w + 4 * g + i;
-            if (SG && (a.scalar & kScalarWrite)) pw[i] += dXr[i] * vD[i];
-            if (t < T) {
-                const size_t off = baseV0 + (size_t)t * tokV + j0 + 16 * n + r;
-                a.dv[off] = dXr[i] * wD[i];
-                if (!(SG && (a.scalar & kScalarWrite))) a.dw[off] = dXr[i] * vD[i] * gate_dact<GL>(wD[i]);
+            for (int i = 0; i < 4; ++i) {
+                const int tr = 16 * w + 4 * g + i;
+                if (SG && (a.scalar & kScalarWrite)) pw[i] += dXr[i] * vD[i];
+                if (t0 + tr < T) {
+                    const unsigned o = ((unsigned)tr * (unsigned)tokV + (unsigned)(16 * n + r)) * 4u;
+                    *reinterpret_cast<float *>(dvb + o) = dXr[i] * wD[i];
+                    if (!(SG && (a.scalar & kScalarWrite)))
+                        *reinterpret_cast<float *>(dwb + o) = dXr[i] * vD[i] * gate_dact<GL>(wD[i]);
+                }
             }
         }
         __syncthreads();
