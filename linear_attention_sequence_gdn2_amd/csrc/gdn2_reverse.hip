@@ -394,14 +394,19 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
         for (int i = 0; i < 4; ++i)
             DS[s][i] = a.dS_final ? a.dS_final[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
     }
-    // dO staging: column tid % VT, tokens OPT * (tid / VT) .. + OPT - 1 of the chunk
+    // dO staging: column tid % VT, tokens OPT * (tid / VT) .. + OPT - 1 of the chunk.  Loaded
+    // 16 bytes at a time: for each group of 4 tokens a lane reads token + (tid % 4) at columns
+    // 4 ((tid / 4) % (VT / 4)) ..; the 4x4 transpose inside each quad of lanes (at staging) gives
+    // the lane its column.
     const int ocol = tid % VT, otg = tid / VT;
     float ox[OPT];
     auto load_dO = [&](int cc) {
 #pragma unroll
-        for (int i = 0; i < OPT; ++i) {
-            const int t = cc * kChunk + OPT * otg + i;
-            ox[i] = a.dO[baseV + (size_t)(t < T ? t : T - 1) * tokV + ocol];
+        for (int q4 = 0; q4 < OPT / 4; ++q4) {
+            const int t = cc * kChunk + OPT * otg + 4 * q4 + (tid & 3);
+            const float4 f = *reinterpret_cast<const float4 *>(
+                a.dO + baseV + (size_t)(t < T ? t : T - 1) * tokV + 4 * ((tid >> 2) % (VT / 4)));
+            ox[4 * q4] = f.x, ox[4 * q4 + 1] = f.y, ox[4 * q4 + 2] = f.z, ox[4 * q4 + 3] = f.w;
         }
     };
     // factor fragments of row block m: R tiles (m, kb) and Q2^T tiles (m, kb)
@@ -427,11 +432,24 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
             const int n = col_block(s);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = DS[s][i];
+            {
+                // one 16-byte store: the quad transpose gives the lane row 16m + 4g + (r % 4),
+                // columns 16n + 4 (r / 4) ..
+                float x[4] = {DS[s][0], DS[s][1], DS[s][2], DS[s][3]};
+                quad_transpose4(x);
+                *reinterpret_cast<float4 *>(&dst[(size_t)(16 * m + 4 * g + (r & 3)) * DV + 16 * n + 4 * (r >> 2)]) =
+                    make_float4(x[0], x[1], x[2], x[3]);
+            }
             const Split4 sp = split4(DS[s]);
             *reinterpret_cast<bf16x4 *>(&sD[buf][(16 * n + r) * PK + 16 * m + 4 * g]) = sp.hi;
             *reinterpret_cast<bf16x4 *>(&sD[buf][VT * PK + (16 * n + r) * PK + 16 * m + 4 * g]) = sp.lo;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < OPT / 4; ++q4) {
+            float x[4] = {ox[4 * q4], ox[4 * q4 + 1], ox[4 * q4 + 2], ox[4 * q4 + 3]};
+            quad_transpose4(x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ox[4 * q4 + i] = x[i];
         }
 #pragma unroll
         for (int q4 = 0; q4 < OPT / 4; ++q4) {
