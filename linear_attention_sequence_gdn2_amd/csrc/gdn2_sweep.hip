@@ -267,10 +267,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 // waves takes 64 columns (half the record reads per head), stages the Kt, Et and Qt
 // rows in LDS once for all waves, and loads each chunk's rows and value inputs while
 // the previous chunk is in its products:
-//   chunk c start      issue T, P, gamma of chunk c; Kt rows, v, w of chunk c + 1
+//   chunk c start      issue Kt rows, v, w of chunk c + 1
 //   [A] X, Qt S        (Et, Qt rows and S from LDS)                 barrier
-//   [B] U = T X        then Et, Qt rows of chunk c + 1 into LDS      barrier
-//   [C] O; S'          issue Et, Qt rows of chunk c + 2; S' into LDS barrier
+//   [B] U = T X        issue T of chunk c + 1; Et, Qt rows of chunk c + 1 into LDS
+//                                                                    barrier
+//   [C] O; S'          issue Et, Qt rows of chunk c + 2; after O, P of chunk c + 1;
+//                      after S', gamma of chunk c + 1; S' into LDS   barrier
 //   Kt rows of chunk c + 1 into LDS
 // Wave (hf, w) owns tokens 16w..16w+15 and columns 32hf..32hf+31 of X, U and O, and
 // the state tiles of one 16-row block (at DK = 128).  bf16 q/k/v only (the X product
