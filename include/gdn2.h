@@ -101,10 +101,10 @@ typedef struct {
 } gdn2_shape;
 
 /* Bytes of device workspace gdn2_chunk_fwd needs; (size_t)-1 if the shape is invalid.
- * 0 when the forward runs as one fused sweep.  With bf16 q/k/v, dk in {64, 128},
- * dv a multiple of 64 and B*H*dv/64 >= 256 it first writes forward-only chunk
- * records (the key-side operands of every chunk, about 2.8 KB per token-head at
- * dk = 128) and then sweeps over them; the workspace holds those records. */
+ * 0 when the forward runs as one fused sweep.  With bf16 q/k/v, dk in {64, 128} and
+ * dv a multiple of 64 it first writes forward-only chunk records (the key-side
+ * operands of every chunk, about 2.8 KB per token-head at dk = 128) and then sweeps
+ * over them; the workspace holds those records. */
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);
 
 /* Forward pass: o [B,T,H,dv] and the final state S_final [B,H,dk,dv].

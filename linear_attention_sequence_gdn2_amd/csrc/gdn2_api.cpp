@@ -46,11 +46,10 @@ int check_shape(const gdn2_shape *s) {
 int nchunks(const gdn2_shape *s) { return (s->T + 63) / 64; }
 
 // The inference forward takes the record path (forward-only chunk records, then the wide
-// sweep) when the heads give every CU a 64-column tile of its own; otherwise one fused
-// sweep that forms the key-side operands itself.
+// sweep) wherever the wide sweep applies: bf16 q/k/v, dk 64 or 128, dv a multiple of 64.
+// Otherwise one fused sweep forms the key-side operands itself.
 bool fwd_uses_records(const gdn2_shape *s) {
-    return s->qkv_dtype == GDN2_BF16 && (s->dk == 64 || s->dk == 128) && s->dv % 64 == 0 &&
-           (long)s->B * s->H * (s->dv / 64) >= 256;
+    return s->qkv_dtype == GDN2_BF16 && (s->dk == 64 || s->dk == 128) && s->dv % 64 == 0;
 }
 
 // the alignment a gate tensor (or its gradient) needs: 4 bytes when it is per token

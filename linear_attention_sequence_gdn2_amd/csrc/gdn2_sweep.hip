@@ -660,9 +660,14 @@ static hipError_t sweep64_mode(const FwdArgs &a, int dk, FwdMode mode, hipStream
 hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
                             hipStream_t st) {
     if (gl && sg) return hipErrorInvalidValue;
-    // 64-column tiles (eight waves, one workgroup per CU) when that still gives every CU
-    // a workgroup; otherwise the four-wave kernel at the given tile width
-    if (bf16 && (dk == 64 || dk == 128) && a_in.dv % 64 == 0 && (long)a_in.B * a_in.H * (a_in.dv / 64) >= cu_count()) {
+    // 64-column tiles (eight waves, one workgroup per CU) whenever o is written: a sequential
+    // chain is paced by its per-chunk latency, and the eight-wave chunk step is about half that of
+    // the four-wave one, which more than pays for leaving CUs idle when there are few heads
+    // (B1 T16K H16: 1.56 against 2.33 ms).  The states-only sweep has less per-chunk work and
+    // takes the narrower tiles of the four-wave kernel unless the wide ones fill every CU
+    // (B1 T16K H16: 0.85 against 1.13 ms).
+    const bool wide_fills = (long)a_in.B * a_in.H * (a_in.dv / 64) >= cu_count();
+    if (bf16 && (dk == 64 || dk == 128) && a_in.dv % 64 == 0 && (mode != kFwdStates || wide_fills)) {
         FwdArgs a = a_in;
         a.nvt = a.dv / 64;
         if (gl) return sweep64_mode<true, false>(a, dk, mode, st);

@@ -64,7 +64,7 @@ def test_workspace_and_state_sizes():
     factors = 2 * 3 * nc * ((128 * 128 + 64 * 128) * 4 + record)
     assert lib.gdn2_chunk_factors_bytes(ctypes.byref(s)) == factors
     assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s)) == 2 * one + factors
-    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 0
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 2 * 3 * nc * record   # forward-only records
     bad = _shape(dk=96)
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
 
@@ -213,8 +213,8 @@ def test_factored_forward_checks_arguments():
 
 
 def test_forward_workspace_on_wide_shapes():
-    """With one 64-column tile per CU or more, the forward writes forward-only chunk
-    records first: it needs a workspace of one record per (batch, head, chunk)."""
+    """With bf16 q/k/v, dk 64 or 128 and dv a multiple of 64, the forward writes forward-only
+    chunk records first: it needs a workspace of one record per (batch, head, chunk)."""
     lib = gdn2.load()
     f = P(0x10000)
     wide = _shape(B=8, T=2048, H=16, dk=128, dv=128)
@@ -225,7 +225,11 @@ def test_forward_workspace_on_wide_shapes():
     F = ctypes.c_size_t
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, None, F(0), None) == WORKSPACE
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, f, F(need - 1), None) == WORKSPACE
-    # fp32 q/k/v, or too few heads for the wide tiles: one fused sweep, no workspace
+    # few heads: still the record path (the sweep is paced by its per-chunk latency)
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=16384, H=16, dk=128, dv=128))) == \
+        1 * 16 * 256 * record
+    # fp32 q/k/v, dk = 32, or dv not a multiple of 64: one fused sweep, no workspace
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0))) == 0
-    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=16384, H=16, dk=128, dv=128))) == 0
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == 0
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=32))) == 0
 

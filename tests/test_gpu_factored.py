@@ -80,7 +80,9 @@ def test_factored_forward_small_shapes(B, T, H, dk, dv, qkv, s0):
 
 
 def test_factored_forward_modes_agree():
-    """o only, states only, and both: the same values."""
+    """o only and o + states: the same values (one kernel).  With few heads the states-only
+    sweep takes narrower tiles in another kernel: equal up to rounding there (the wide-tile
+    test below checks it bit for bit where both take the same kernel)."""
     inp = make_inputs(2, 150, 2, 128, 64, seed=4711, s0_std=0.1)
     d = to_dev(inp)
     factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
@@ -88,7 +90,9 @@ def test_factored_forward_modes_agree():
     o2, s2, _ = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"], want_states=False)
     _, s3, st3 = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"], want_o=False)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(s1, s3) and torch.equal(st1, st3)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    for x, y in ((s3, s1), (st3, st1)):
+        assert float((x - y).abs().max()) <= 1e-3 * float(y.abs().max())
 
 
 @pytest.mark.parametrize("name", ["fwd_bf16_B8H16T2048d128", "long_bf16_B1H16T16384d128",
@@ -123,7 +127,7 @@ def test_training_chain_from_factors():
     assert not bad, bad
 
 
-# Shapes with at least one 64-column value tile per CU take the eight-wave sweep
+# Shapes with at least one 64-column value tile per CU take the eight-wave sweep in every mode
 # (B*H*dv/64 >= 256); ragged T, both key widths it covers, every gate format and mode.
 @pytest.mark.parametrize("B,T,H,dk,dv,extra", [
     (8, 33, 16, 128, 128, {"s0_std": 0.2}),     # one partial chunk

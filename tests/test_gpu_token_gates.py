@@ -62,11 +62,13 @@ def test_token_gates_fwd_bwd(gates, B, T, H, dk, dv, s0):
         assert g[gname].shape == d[name].shape
     _check_fwd(inp, o, sf)
     _check_bwd(inp, g)
-    # the staged training form gives the same results
+    # the staged training form gives the same results (its forward is the fused sweep, the
+    # inference forward may take the record path: equal up to rounding)
     o2, sf2, states = gdn2.fwd_states(*args, d["S0"])
     g2 = gdn2.bwd_saved(*args, states, d["dO"], d["dS_final"])
     torch.cuda.synchronize()
-    assert torch.equal(o, o2) and torch.equal(sf, sf2)
+    for x, y in ((o, o2), (sf, sf2)):
+        assert float((x - y).abs().max()) <= 1e-3 * float(y.abs().max())
     for n in NAMES:
         assert rel_err(g2[n], g[n].double().cpu().numpy()) < 1e-5, n
 
