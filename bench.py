@@ -211,6 +211,59 @@ def forward_bench(dev, wl, iters=20):
     return out
 
 
+# the other configurations of the operator, measured beside the headline: forward of the long
+# sequence and of the per-token (KDA) gates, and the whole training step at B4 T4096
+OTHER_FORWARD = ("long_bf16_B1H16T16384d128", "kda_bf16_B4H16T4096d128", "fwdbwd_bf16_B4H16T4096d128")
+OTHER_STEP = ("fwdbwd_bf16_B4H16T4096d128",)
+
+
+def _nbytes(*ts):
+    return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
+
+def configs_bench(dev, timed_steps, iters=10, steps=10, warmup=3):
+    """Forward (gdn2_chunk_fwd) and training-step times of the other configurations, HIP events.
+    HBM fractions count the operator's own inputs and outputs (the tensors as given: bf16 q/k/v,
+    fp32 gates, per-token gates where the workload has them)."""
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_workload
+    res = {}
+    for name in OTHER_FORWARD:
+        wl = WORKLOADS[name]
+        x = make_workload(wl, grads=name in OTHER_STEP)
+        d = {k: (v.to(dev) if v is not None and hasattr(v, "to") else None) for k, v in x.items()
+             if k in ("q", "k", "v", "log_alpha", "b", "w", "S0")}
+        args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+        o, sf = gdn2.fwd(*args)
+        for _ in range(2):
+            gdn2.fwd(*args)
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            gdn2.fwd(*args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        io = _nbytes(*args, o, sf)
+        r = {"B": wl.B, "T": wl.T, "H": wl.H, "dk": wl.dk, "dv": wl.dv,
+             "forward_ms": round(ms, 4), "forward_tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
+             "forward_hbm_frac": round(io / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if name in OTHER_STEP:
+            wall, k_ms, step_ms = timed_steps(x, steps, warmup, wl=wl)
+            # the backward reads the forward's inputs, dO and dS_final, and writes the seven fp32
+            # gradients (dq, dk, dv in fp32 whatever the dtype of q, k, v)
+            grads = 4 * (d["q"].numel() + d["k"].numel() + d["v"].numel()) + _nbytes(*args[3:6], sf)
+            bwd_io = _nbytes(*args) + _nbytes(o, sf) + grads
+            r.update({"step_ms": round(wall / steps * 1e3, 4),
+                      "step_tokens_per_s": round(wl.B * wl.T / (wall / steps), 1),
+                      "kernel_ms": [round(v, 4) for v in k_ms],
+                      "step_algorithmic_frac": round((io + bwd_io) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        res[name] = r
+    return res
+
+
 # output epilogue (RMS norm, weight, output gate) per token-head at dv = 128, bf16 gate and y:
 #   forward : o 512 + g 256 + y 256                      = 1024
 #   backward: o 512 + g 256 + dy 512 + dO 512 + dg 512   = 2304  (+ dweight partials per workgroup)
@@ -277,6 +330,8 @@ def main():
     ap.add_argument("--no-token-gates", action="store_true", help="skip the step with per-token gates")
     ap.add_argument("--no-output", action="store_true", help="skip the output epilogue measurement")
     ap.add_argument("--no-forward", action="store_true", help="skip the inference-forward measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the long-sequence, per-token-gate and B4 T4096 training measurements")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
@@ -310,9 +365,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     nk = 4
 
-    def timed_steps(x, steps, warmup):
-        """Run `warmup` then `steps` training steps on the inputs x; returns (wall seconds,
-        per-kernel event ms averaged over the steps, whole-step event ms)."""
+    def timed_steps(x, steps, warmup, wl=wl):
+        """Run `warmup` then `steps` training steps on the inputs x (of workload wl); returns
+        (wall seconds, per-kernel event ms averaged over the steps, whole-step event ms)."""
         d = {k: (v.to(dev) if v is not None and hasattr(v, "to") else None)
              for k, v in x.items() if k in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final")}
         fargs = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
@@ -433,6 +488,8 @@ def main():
             "step_algorithmic_frac": round(talg / (tstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_forward:
         out["breakdown"]["forward_only"] = forward_bench(dev, wl)
+    if not args.no_configs:
+        out["breakdown"]["other_configs"] = configs_bench(dev, timed_steps)
     if not args.no_output:
         out["breakdown"]["output_epilogue"] = output_bench(dev, wl)
     if not args.no_decode:
