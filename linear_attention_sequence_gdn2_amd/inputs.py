@@ -14,6 +14,8 @@ section "Ablations and training throughput", Figure 2):
   bf16 (round-to-nearest-even).  v ~ N(0, 1), same rounding.
 * log_alpha: ``"softplus"``  -> -softplus(N(0,1)) * 0.1   (tiny fp32 workload)
              ``"logsigmoid"`` -> log(sigmoid(N(3,1)))      (decay ~0.9-0.99)
+             ``"strong"``     -> -1.15 + 0.03 N(0,1), clamped to [-1.2, -1.1] (a chunk's
+                                 cumulative log-decay near the kernels' supported -80)
 * gates ``"channel"``: b = sigmoid(N(0,1)) per key channel, w = sigmoid(N(0,1))
   per value channel.  ``"kda"``: one beta = sigmoid(N(0,1)) per (b,t,h),
   broadcast to b and w.  ``"gdn"``: as ``"kda"`` and log_alpha drawn once per
@@ -51,7 +53,7 @@ class Workload:
     dv: int
     seed: int
     qkv_dtype: str = "bf16"          # "bf16" or "f32"
-    decay: str = "logsigmoid"        # "softplus" or "logsigmoid"
+    decay: str = "logsigmoid"        # "softplus", "logsigmoid" or "strong"
     gates: str = "channel"           # "channel", "kda" or "gdn"
     s0_std: float = 0.0
     grads: bool = False              # also draw dO and dS_final
@@ -118,6 +120,9 @@ def make_inputs(B, T, H, dk, dv, seed, *, qkv_dtype="bf16", decay="logsigmoid", 
         la = -F.softplus(randn(*shp_k)) * 0.1
     elif decay == "logsigmoid":
         la = F.logsigmoid(randn(*shp_k) + 3.0)
+    elif decay == "strong":
+        # about -1.15 per token: a 64-token chunk sums to between -76.8 and -70.4
+        la = (-1.15 + 0.03 * randn(*shp_k)).clamp(-1.2, -1.1)
     else:
         raise ValueError(decay)
 
