@@ -112,3 +112,35 @@ def test_argument_errors_surface_as_exceptions():
         gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"][..., :64].contiguous(), d["b"], d["w"])
     with pytest.raises(ValueError):
         gdn2.fwd(d["q"], d["k"].transpose(1, 2), d["v"], d["log_alpha"], d["b"], d["w"])
+
+
+def test_every_output_is_written_over_poisoned_memory(monkeypatch):
+    """Every tensor the binding allocates (outputs, workspaces, factor buffers) starts out as
+    NaN (bytes as 0xFF); every output of every entry point must come back finite: the kernels
+    write all of it and read nothing they have not written."""
+    real_empty = torch.empty
+
+    def poisoned_empty(*shape, **kw):
+        t = real_empty(*shape, **kw)
+        if t.is_floating_point():
+            t.fill_(float("nan"))
+        else:
+            t.fill_(255)
+        return t
+
+    monkeypatch.setattr(torch, "empty", poisoned_empty)
+    for qkv, dv in (("bf16", 128), ("f32", 64), ("bf16", 32)):   # record path, fused sweep, narrow tiles
+        d = _dev(B=2, T=150, H=3, dk=128, dv=dv, seed=31, qkv=qkv)
+        outs = list(gdn2.fwd(*_fargs(d)))
+        outs += list(gdn2.fwd_states(*_fargs(d)))
+        g = gdn2.bwd(*_fargs(d), d["dO"], d["dS_final"])
+        outs += list(g.values())
+        factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+        o, sf, states = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"])
+        _, _, st_s = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"], want_o=False)
+        dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], 128, d["dS_final"])
+        outs += [o, sf, states, st_s, dstates, dS0]
+        outs += list(gdn2.bwd_grads(*_fargs(d)[:6], d["dO"], states, dstates, factors).values())
+        torch.cuda.synchronize()
+        for t in outs:
+            assert t is not None and bool(torch.isfinite(t).all()), qkv
