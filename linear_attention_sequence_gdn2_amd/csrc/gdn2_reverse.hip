@@ -566,7 +566,7 @@ static hipError_t reverse_t(const BwdArgs &a, hipStream_t st) {
 
 // 64-column tiles when they still give every CU a workgroup, else 32 (two workgroups per CU):
 // with few heads the 64-column reverse step is slower than two 32-column ones (B1 T16K H16:
-// about 1.2 against 0.79 ms)
+// about 1.35 against 0.79 ms)
 template <int DK>
 static hipError_t reverse_vt(const BwdArgs &a, hipStream_t st) {
     if (a.DV >= 64 && (long)a.B * a.H * (a.DV / 64) >= cu_count()) return reverse_t<DK, 64>(a, st);
