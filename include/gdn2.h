@@ -104,7 +104,10 @@ typedef struct {
  * 0 when the forward runs as one fused sweep.  With bf16 q/k/v, dk in {64, 128} and
  * dv a multiple of 64 it first writes forward-only chunk records (the key-side
  * operands of every chunk, about 2.8 KB per token-head at dk = 128) and then sweeps
- * over them; the workspace holds those records. */
+ * over them; the workspace holds those records.  With so few heads that the sweep
+ * would keep at most one CU in eight busy and 64 chunks or more, the sequence is also
+ * split into segments swept side by side; every segment's state map and start state
+ * (dk * (2 dv + dk) fp32 per batch, head and segment) follow the records. */
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);
 
 /* Forward pass: o [B,T,H,dv] and the final state S_final [B,H,dk,dv].

@@ -52,6 +52,31 @@ bool fwd_uses_records(const gdn2_shape *s) {
     return s->qkv_dtype == GDN2_BF16 && (s->dk == 64 || s->dk == 128) && s->dv % 64 == 0;
 }
 
+// Segments of the record-path forward.  With so few heads that the wide sweep keeps at most
+// one CU in eight busy, and a long sequence, the sequence is split into segments swept side by
+// side: a pass for every segment's state map (its value tiles plus DK / 64 identity tiles), the
+// maps composed in order, and a pass from the true start states.  About three sweeps' work at
+// an eighth or less of the depth.  1 = no segments.
+int fwd_segments(const gdn2_shape *s, int *seg_len) {
+    *seg_len = nchunks(s);
+    if (!fwd_uses_records(s)) return 1;
+    const long wide = (long)s->B * s->H * (s->dv / 64);
+    const int nc = nchunks(s), cus = gdn2::cu_count();
+    if (wide * 8 > cus || nc < 64) return 1;
+    int nseg = (int)(cus / wide);
+    if (nseg > nc / 8) nseg = nc / 8;             // at least 8 chunks a segment
+    const int len = (nc + nseg - 1) / nseg;
+    *seg_len = len;
+    return (nc + len - 1) / len;
+}
+
+// bytes after the records: every segment's [N | M] block, then the composed start states
+size_t fwd_segment_bytes(const gdn2_shape *s, int nseg) {
+    if (nseg <= 1) return 0;
+    const size_t blocks = (size_t)s->B * s->H * nseg * s->dk;
+    return blocks * (s->dv + s->dk) * sizeof(float) + blocks * s->dv * sizeof(float);
+}
+
 // the alignment a gate tensor (or its gradient) needs: 4 bytes when it is per token
 bool gate_aligned(const gdn2_shape *s, int bit, const void *p) {
     return !p || ((s->gate_scalar & bit) ? aligned4(p) : aligned16(p));
@@ -80,7 +105,10 @@ const char *gdn2_strerror(int status) {
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
     if (!fwd_uses_records(shape)) return 0;
-    return gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk);
+    int seg_len;
+    const int nseg = fwd_segments(shape, &seg_len);
+    return gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk) +
+           fwd_segment_bytes(shape, nseg);
 }
 
 int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const void *v,
@@ -105,6 +133,20 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
         gdn2::FwdArgs f{};
         f.v = v; f.wg = w; f.S0 = S0; f.o = o; f.S_final = S_final; f.states = nullptr; f.records = workspace;
         f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv; f.scalar = shape->gate_scalar;
+        int seg_len;
+        const int nseg = fwd_segments(shape, &seg_len);
+        if (nseg > 1) {
+            // segments side by side: the maps, their composition, o
+            f.nseg = nseg;
+            f.seg_len = seg_len;
+            char *rest = reinterpret_cast<char *>(workspace) +
+                         gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk);
+            float *E = reinterpret_cast<float *>(rest);
+            float *Sin = E + (size_t)shape->B * shape->H * nseg * shape->dk * (shape->dv + shape->dk);
+            const hipError_t e3 = gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E,
+                                                            Sin, hs);
+            return e3 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+        }
         const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
         f.nvt = shape->dv / vt;
         const hipError_t e2 = gdn2::launch_fwd_sweep(f, shape->dk, vt, true, gate_logits(shape), gate_scalar(shape),

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 // Wave (hf, w) owns tokens 16w..16w+15 and columns 32hf..32hf+31 of X, U and O, and
 // the state tiles of one 16-row block (at DK = 128).  bf16 q/k/v only (the X product
 // uses the hi part of Et, so one Et plane is staged); about 155 KB of LDS.
-template <int DK, bool OUT, bool STATES, bool GL, bool SG>
+template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG>
 __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a) {
     using Rec = ChunkRecord<DK>;
     constexpr int VT = 64, NTH = kChunkThreads;
@@ -298,15 +298,27 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     __shared__ __align__(16) __bf16 sX[2 * VT * PT];     // X^T [col][token] (hi, lo)
     __shared__ __align__(16) __bf16 sU[2 * VT * PT];     // U^T [col][token] (hi, lo)
 
+    // Segments (SEG 1, 2): each (b, h) is split into nseg runs of seg_len chunks.  SEG 1 sweeps a
+    // segment from a zero state (value tiles) and, in DK / 64 more tiles, from the identity with
+    // z = 0: the end states N and M give the segment's map S -> M S + N.  SEG 2 sweeps a segment
+    // from its true start state (the maps composed in order) and writes o.
     const int L = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int vt = L % a.nvt, bh = L / a.nvt, h = bh % a.H, b = bh / a.H;
+    const int ntile = SEG == 1 ? a.nvt + DK / 64 : a.nvt;
+    const int vt = L % ntile, rest = L / ntile;
+    const int seg = SEG ? rest % a.nseg : 0, bh = SEG ? rest / a.nseg : rest;
+    const bool ident = SEG == 1 && vt >= a.nvt;         // a tile of the segment's state map
+    const int h = bh % a.H, b = bh / a.H;
     const int T = a.T, H = a.H, DV = a.dv;
-    const int j0 = vt * VT;
+    const int j0 = (ident ? 0 : vt) * VT;               // identity tiles read column 0's v and w
+    const int jI = ident ? (vt - a.nvt) * VT : 0;       // and hold columns jI.. of the DK x DK map
     const size_t tokV = (size_t)H * DV;
     const size_t baseK = ((size_t)b * T * H + h) * DK;
     const size_t baseV = ((size_t)b * T * H + h) * DV + j0;
     const size_t sbase = ((size_t)b * H + h) * (size_t)DK * DV + j0;
     const int NC = (T + kChunk - 1) / kChunk;
+    const int c_lo = SEG ? seg * a.seg_len : 0;
+    const int c_hi = SEG ? min(c_lo + a.seg_len, NC) : NC;
+    const float zon = ident ? 0.f : 1.f;                // z = w * v, zero on identity tiles
     const char *recs = reinterpret_cast<const char *>(a.records) + (size_t)bh * NC * Rec::BYTES;
 
     // record pieces of the Kt planes and of the Et/Qt planes, and where they go in LDS
@@ -373,8 +385,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     for (int s = 0; s < NTS; ++s) {
         const int id = wv * NTS + s, m = id / 4, n = id % 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[s][i] = a.S0 ? a.S0[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * m + 4 * g + i, col = 16 * n + r;
+            if (SEG == 0) S[s][i] = a.S0 ? a.S0[sbase + (size_t)row * DV + col] : 0.f;
+            else if (SEG == 1) S[s][i] = (ident && row == jI + col) ? 1.f : 0.f;
+            else S[s][i] = a.S0[(((size_t)bh * a.nseg + seg) * DK + row) * DV + j0 + col];
+        }
     }
     auto store_state_lds = [&](int wv, int r, int g) {
 #pragma unroll
@@ -387,18 +403,19 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     };
     // prologue: chunk 0's rows into LDS, its value inputs, chunk 1's Et/Qt rows in flight
     float vv[2][4], ww[2][4], z[2][4];
-    load_vw(0, vv, ww, w, hf, r, g);
+    load_vw(c_lo, vv, ww, w, hf, r, g);
     to_d_layout(vv, ww);
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[n][i] = 16 * w + 4 * g + i < T ? gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
+        for (int i = 0; i < 4; ++i)
+            z[n][i] = c_lo * kChunk + 16 * w + 4 * g + i < T ? zon * gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
     {
         uint4 kp[NKP], ep[NEP];
 #pragma unroll
-        for (int it = 0; it < NKP; ++it) kp[it] = kt_piece(0, it, tid);
+        for (int it = 0; it < NKP; ++it) kp[it] = kt_piece(c_lo, it, tid);
 #pragma unroll
-        for (int it = 0; it < NEP; ++it) ep[it] = eq_piece(0, it, tid);
+        for (int it = 0; it < NEP; ++it) ep[it] = eq_piece(c_lo, it, tid);
 #pragma unroll
         for (int it = 0; it < NKP; ++it) kt_store(kp[it], it, tid);
 #pragma unroll
@@ -406,7 +423,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     }
     uint4 eqn[NEP];                                      // Et/Qt rows of the next chunk
 #pragma unroll
-    for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(NC > 1 ? 1 : 0, it, tid);
+    for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(c_lo + 1 < c_hi ? c_lo + 1 : c_lo, it, tid);
     store_state_lds(wv, r, g);
     __syncthreads();
 
@@ -431,13 +448,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     };
     Split8 Tf[2];
     uint4 pv[4];
-    load_T(recs, Tf);
-    if (OUT) load_P(recs, pv);
-    f32x4 gam = load_gam(recs);
-    for (int c = 0; c < NC; ++c) {
+    load_T(recs + (size_t)c_lo * Rec::BYTES, Tf);
+    if (OUT) load_P(recs + (size_t)c_lo * Rec::BYTES, pv);
+    f32x4 gam = load_gam(recs + (size_t)c_lo * Rec::BYTES);
+    for (int c = c_lo; c < c_hi; ++c) {
         const int t0 = c * kChunk;
-        const int cn = c + 1 < NC ? c + 1 : c;           // the next chunk (itself at the end)
-        const int cn2 = c + 2 < NC ? c + 2 : cn;         // the one after
+        const int cn = c + 1 < c_hi ? c + 1 : c;         // the next chunk (itself at the end)
+        const int cn2 = c + 2 < c_hi ? c + 2 : cn;       // the one after
 
         // ---- loads: Kt rows, v, w of the next chunk (T, P and gamma of this one are in flight) ----
         uint4 ktn[NKP];
@@ -505,7 +522,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
                 *reinterpret_cast<bf16x4 *>(&sU[VT * PT + (16 * cb + r) * PT + 16 * w + 4 * g]) = us.lo;
             }
         }
-        if (c + 1 < NC) {
+        if (c + 1 < c_hi) {
 #pragma unroll
             for (int it = 0; it < NEP; ++it) eq_store(eqn[it], it, tid);
         }
@@ -563,7 +580,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
         __syncthreads();
         // the next chunk's Kt rows (sK is not read again in this chunk) and its z = w * v,
         // from loads issued at this chunk's start
-        if (c + 1 < NC) {
+        if (c + 1 < c_hi) {
 #pragma unroll
             for (int it = 0; it < NKP; ++it) kt_store(ktn[it], it, tid);
         }
@@ -572,10 +589,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
         for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                z[n][i] = (c + 1) * kChunk + 16 * w + 4 * g + i < T ? gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
+                z[n][i] = (c + 1) * kChunk + 16 * w + 4 * g + i < T ? zon * gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
     }
 
-    if (a.S_final) {
+    if (SEG == 1) {
+        // the segment's end-state block [N | M], DK x (DV + DK), of this (b, h) and segment
+        const int ldE = DV + DK;
+        float *e = a.states + ((size_t)bh * a.nseg + seg) * DK * ldE + (ident ? DV + jI : j0);
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+            const int id = wv * NTS + s, m = id / 4, n = id % 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[(size_t)(16 * m + 4 * g + i) * ldE + 16 * n + r] = S[s][i];
+        }
+    } else if (a.S_final && (SEG == 0 || seg == a.nseg - 1)) {
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
             const int id = wv * NTS + s, m = id / 4, n = id % 4;
@@ -583,6 +610,70 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
             for (int i = 0; i < 4; ++i)
                 a.S_final[sbase + (size_t)(16 * m + 4 * g + i) * DV + 16 * n + r] = S[s][i];
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// segment composition: the start state of every segment of a (b, h)
+// ---------------------------------------------------------------------------
+// The chunk map is affine in the state (S' = M S + N, the form the multi-GPU design splits a
+// sequence by), so a segment's is too.  Given each segment's end-state block [N_s | M_s]
+// (DK x (DV + DK), from the SEG 1 sweep), the start states follow in order:
+//     S_0 = S0 (or zero),   S_{s+1} = M_s S_s + N_s.
+// One workgroup per (b, h) and 16 state columns; fp32 FMA, M_s staged in LDS.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_combine_kernel(const float *E, const float *S0, float *Sin, int DV,
+                                                          int nseg) {
+    constexpr int NCB = 16;                       // state columns per workgroup
+    constexpr int PM = DK + 4;                    // row pitch of M in LDS
+    constexpr int RPT = DK / 64;                  // rows per thread: 64 row blocks x 4 column blocks
+    __shared__ __align__(16) float sS[DK * NCB];
+    __shared__ __align__(16) float sM[DK * PM];
+    const int ncb = DV / NCB;
+    const int bh = blockIdx.x / ncb, j0 = NCB * (blockIdx.x % ncb);
+    const int tid = threadIdx.x, rb = tid >> 2, cb = tid & 3;
+    const int ldE = DV + DK;
+    for (int idx = tid; idx < DK * NCB; idx += 256) {
+        const int row = idx / NCB, col = idx % NCB;
+        sS[idx] = S0 ? S0[((size_t)bh * DK + row) * DV + j0 + col] : 0.f;
+    }
+    __syncthreads();
+    for (int s = 0; s < nseg; ++s) {
+        const size_t blk = (size_t)bh * nseg + s;
+        for (int idx = tid; idx < DK * NCB; idx += 256) {
+            const int row = idx / NCB, col = idx % NCB;
+            Sin[(blk * DK + row) * DV + j0 + col] = sS[idx];
+        }
+        if (s + 1 == nseg) break;
+        for (int idx = tid; idx < DK * DK / 4; idx += 256) {
+            const int row = idx / (DK / 4), k4 = idx % (DK / 4);
+            *reinterpret_cast<float4 *>(&sM[row * PM + 4 * k4]) =
+                *reinterpret_cast<const float4 *>(&E[(blk * DK + row) * ldE + DV + 4 * k4]);
+        }
+        __syncthreads();
+        float acc[RPT][4];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float4 nv = *reinterpret_cast<const float4 *>(&E[(blk * DK + RPT * rb + i) * ldE + j0 + 4 * cb]);
+            acc[i][0] = nv.x, acc[i][1] = nv.y, acc[i][2] = nv.z, acc[i][3] = nv.w;
+        }
+        for (int kx = 0; kx < DK; ++kx) {
+            const float4 sv = *reinterpret_cast<const float4 *>(&sS[kx * NCB + 4 * cb]);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float mv = sM[(RPT * rb + i) * PM + kx];
+                acc[i][0] = fmaf(mv, sv.x, acc[i][0]);
+                acc[i][1] = fmaf(mv, sv.y, acc[i][1]);
+                acc[i][2] = fmaf(mv, sv.z, acc[i][2]);
+                acc[i][3] = fmaf(mv, sv.w, acc[i][3]);
+            }
+        }
+        __syncthreads();   // every thread has read this segment's state and map
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<float4 *>(&sS[(RPT * rb + i) * NCB + 4 * cb]) =
+                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        __syncthreads();
     }
 }
 
@@ -631,7 +722,7 @@ static hipError_t sweep_mode(const FwdArgs &a, int dk, int vt, FwdMode mode, hip
 template <int DK, bool GL, bool SG, int MODE>
 static hipError_t sweep64_t(const FwdArgs &a, hipStream_t st) {
     constexpr bool OUT = MODE != kFwdStates, STATES = MODE != kFwdOut;
-    hipLaunchKernelGGL((fwd_sweep64_kernel<DK, OUT, STATES, GL, SG>), dim3((unsigned)(a.B * a.H * a.nvt)),
+    hipLaunchKernelGGL((fwd_sweep64_kernel<DK, OUT, STATES, GL, SG, 0>), dim3((unsigned)(a.B * a.H * a.nvt)),
                        dim3(kChunkThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -655,6 +746,45 @@ static hipError_t sweep64_mode(const FwdArgs &a, int dk, FwdMode mode, hipStream
         }
     }
     return hipErrorInvalidValue;
+}
+
+template <int DK, bool GL, bool SG, int SEG>
+static hipError_t seg_t(const FwdArgs &a, hipStream_t st) {
+    const int ntile = SEG == 1 ? a.nvt + DK / 64 : a.nvt;
+    hipLaunchKernelGGL((fwd_sweep64_kernel<DK, SEG == 2, false, GL, SG, SEG>),
+                       dim3((unsigned)(a.B * a.H * a.nseg * ntile)), dim3(kChunkThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int SEG>
+static hipError_t seg_dk(const FwdArgs &a, int dk, bool gl, bool sg, hipStream_t st) {
+    if (gl && sg) return hipErrorInvalidValue;
+    if (dk == 128) return gl ? seg_t<128, true, false, SEG>(a, st) : sg ? seg_t<128, false, true, SEG>(a, st)
+                                                                          : seg_t<128, false, false, SEG>(a, st);
+    if (dk == 64) return gl ? seg_t<64, true, false, SEG>(a, st) : sg ? seg_t<64, false, true, SEG>(a, st)
+                                                                        : seg_t<64, false, false, SEG>(a, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_segments(const FwdArgs &a_in, int dk, bool gl, bool sg, float *E, float *Sin,
+                               hipStream_t st) {
+    if (a_in.dv % 64 != 0 || a_in.nseg < 1 || a_in.seg_len < 1) return hipErrorInvalidValue;
+    FwdArgs a = a_in;
+    a.nvt = a.dv / 64;
+    // 1: every segment's map from zero and identity starts
+    a.S0 = nullptr, a.o = nullptr, a.S_final = nullptr, a.states = E;
+    hipError_t e = seg_dk<1>(a, dk, gl, sg, st);
+    if (e != hipSuccess) return e;
+    // 2: the start states, composed in order
+    const unsigned ncomb = (unsigned)(a.B * a.H * (a.dv / 16));
+    if (dk == 128) hipLaunchKernelGGL((seg_combine_kernel<128>), dim3(ncomb), dim3(256), 0, st, E, a_in.S0, Sin, a.dv, a.nseg);
+    else if (dk == 64) hipLaunchKernelGGL((seg_combine_kernel<64>), dim3(ncomb), dim3(256), 0, st, E, a_in.S0, Sin, a.dv, a.nseg);
+    else return hipErrorInvalidValue;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 3: every segment again from its start state, writing o (and S_final from the last)
+    a.S0 = Sin, a.o = a_in.o, a.S_final = a_in.S_final, a.states = nullptr;
+    return seg_dk<2>(a, dk, gl, sg, st);
 }
 
 hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,

@@ -225,9 +225,15 @@ def test_forward_workspace_on_wide_shapes():
     F = ctypes.c_size_t
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, None, F(0), None) == WORKSPACE
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, f, F(need - 1), None) == WORKSPACE
-    # few heads: still the record path (the sweep is paced by its per-chunk latency)
+    # few heads: still the record path; with at most one CU in eight busy and a long sequence
+    # the sequence is split into segments (here 8 of 32 chunks), whose [N | M] blocks and start
+    # states follow the records
+    seg = 1 * 16 * 8 * 128 * ((128 + 128) + 128) * 4
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=16384, H=16, dk=128, dv=128))) == \
-        1 * 16 * 256 * record
+        1 * 16 * 256 * record + seg
+    # few heads but a short sequence (under 64 chunks): no segments
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=4000, H=16, dk=128, dv=128))) == \
+        1 * 16 * 63 * record
     # fp32 q/k/v, dk = 32, or dv not a multiple of 64: one fused sweep, no workspace
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0))) == 0
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == 0
