@@ -105,7 +105,7 @@ typedef struct {
  * dv a multiple of 64 it first writes forward-only chunk records (the key-side
  * operands of every chunk, about 2.8 KB per token-head at dk = 128) and then sweeps
  * over them; the workspace holds those records.  With so few heads that the sweep
- * would keep at most one CU in eight busy and 64 chunks or more, the sequence is also
+ * would keep at most one CU in four busy and 64 chunks or more, the sequence is also
  * split into segments swept side by side; every segment's state map and start state
  * (dk * (2 dv + dk) fp32 per batch, head and segment) follow the records. */
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);

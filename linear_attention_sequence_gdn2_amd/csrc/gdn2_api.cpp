@@ -53,16 +53,18 @@ bool fwd_uses_records(const gdn2_shape *s) {
 }
 
 // Segments of the record-path forward.  With so few heads that the wide sweep keeps at most
-// one CU in eight busy, and a long sequence, the sequence is split into segments swept side by
+// one CU in four busy, and a long sequence, the sequence is split into segments swept side by
 // side: a pass for every segment's state map (its value tiles plus DK / 64 identity tiles), the
-// maps composed in order, and a pass from the true start states.  About three sweeps' work at
-// an eighth or less of the depth.  1 = no segments.
+// maps composed in order, and a pass from the true start states.  About three sweeps' work at a
+// quarter or less of the depth; enough segments to give every CU a workgroup in the last pass
+// (more only add passes).  B1 T16K H16: 1.47 -> 0.78 ms; B2 T16K H16: 1.66 -> 1.36 ms; at half
+// the CUs busy (B4 T8K H16) two segments are slower, 1.09 -> 1.33 ms.  1 = no segments.
 int fwd_segments(const gdn2_shape *s, int *seg_len) {
     *seg_len = nchunks(s);
     if (!fwd_uses_records(s)) return 1;
     const long wide = (long)s->B * s->H * (s->dv / 64);
     const int nc = nchunks(s), cus = gdn2::cu_count();
-    if (wide * 8 > cus || nc < 64) return 1;
+    if (wide * 4 > cus || nc < 64) return 1;
     int nseg = (int)(cus / wide);
     if (nseg > nc / 8) nseg = nc / 8;             // at least 8 chunks a segment
     const int len = (nc + nseg - 1) / nseg;

@@ -225,7 +225,7 @@ def test_forward_workspace_on_wide_shapes():
     F = ctypes.c_size_t
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, None, F(0), None) == WORKSPACE
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, f, F(need - 1), None) == WORKSPACE
-    # few heads: still the record path; with at most one CU in eight busy and a long sequence
+    # few heads: still the record path; with at most one CU in four busy and a long sequence
     # the sequence is split into segments (here 8 of 32 chunks), whose [N | M] blocks and start
     # states follow the records
     seg = 1 * 16 * 8 * 128 * ((128 + 128) + 128) * 4

@@ -1,5 +1,5 @@
 """GPU parity of the segmented inference forward: with so few heads that the wide sweep would
-keep at most one CU in eight busy, gdn2_chunk_fwd splits each sequence into segments swept side
+keep at most one CU in four busy, gdn2_chunk_fwd splits each sequence into segments swept side
 by side.  It sweeps every segment's state map from zero and identity starts, composes the maps
 in order (S_{s+1} = M_s S_s + N_s) and sweeps again from the true start states.  Checked against
 the fp64 oracle (3e-3, bf16) and against the unsegmented factored sweep (1e-3) on ragged T, with
@@ -33,6 +33,7 @@ def _oracle_inputs(inp):
     (1, 64 * 70 + 17, 2, 128, 128, {}),                 # zero start state
     (1, 64 * 64, 4, 64, 128, {"s0_std": 0.1}),          # dk = 64: 8 segments of 8
     (2, 64 * 80, 1, 128, 64, {"s0_std": 0.1}),          # dv = 64, two sequences
+    (2, 64 * 64 + 5, 16, 128, 128, {"s0_std": 0.1}),    # a quarter of the CUs: 4 segments of 17
     (1, 64 * 72, 2, 128, 128, {"gate_logits": True, "s0_std": 0.1}),
     (1, 64 * 72, 2, 128, 128, {"gates": "gdn", "token_gates": True, "s0_std": 0.1}),
 ])
