@@ -181,7 +181,9 @@ size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape) {
 
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
-    return 2 * gdn2_chunk_states_bytes(shape) + gdn2_chunk_factors_bytes(shape);
+    int seg_len;
+    return 2 * gdn2_chunk_states_bytes(shape) + gdn2_chunk_factors_bytes(shape) +
+           fwd_segment_bytes(shape, fwd_segments(shape, &seg_len));
 }
 
 }  // extern "C"
@@ -336,7 +338,24 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     // the key-side chunk operands once, then the state sweep from them
     int rc = gdn2_chunk_bwd_factors(shape, q, k, log_alpha, b, factors, stream);
     if (rc != GDN2_OK) return rc;
-    rc = gdn2_chunk_fwd_factored(shape, factors, v, w, S0, nullptr, nullptr, states, stream);
+    int seg_len;
+    const int nseg = fwd_segments(shape, &seg_len);
+    if (nseg > 1) {
+        // few heads, long sequence: the state sweep in segments side by side (as the forward's)
+        int vt;
+        gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, nullptr, nullptr, states, &vt);
+        const long items = (long)shape->B * shape->H * nchunks(shape);
+        const size_t fbytes = gdn2_chunk_factors_bytes(shape);
+        f.records = reinterpret_cast<const char *>(factors) + (fbytes - gdn2::record_buffer_bytes(items, shape->dk));
+        f.nseg = nseg;
+        f.seg_len = seg_len;
+        float *E = reinterpret_cast<float *>(reinterpret_cast<char *>(factors) + fbytes);
+        float *Sin = E + (size_t)shape->B * shape->H * nseg * shape->dk * (shape->dv + shape->dk);
+        rc = launch_status(gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E, Sin,
+                                                     reinterpret_cast<hipStream_t>(stream)));
+    } else {
+        rc = gdn2_chunk_fwd_factored(shape, factors, v, w, S0, nullptr, nullptr, states, stream);
+    }
     if (rc != GDN2_OK) return rc;
     rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     if (rc != GDN2_OK) return rc;

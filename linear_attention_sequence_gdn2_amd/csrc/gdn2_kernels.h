@@ -71,10 +71,12 @@ enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
 hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode, hipStream_t st);
 // The same sweep with the key-side operands of every chunk taken from the chunk operand
 // records of the factor buffer (a.factors); q, k, log_alpha and b are not read.
-// The inference forward over few heads, sequence split into a.nseg segments of a.seg_len chunks
+// The forward sweep over few heads, sequence split into a.nseg segments of a.seg_len chunks
 // (bf16 q/k/v, dk 64 or 128, dv a multiple of 64): every segment's state map into E
-// [B, H, nseg, dk, dv + dk], the composed start states into Sin [B, H, nseg, dk, dv], then o and
-// S_final.  a.records holds the forward-only chunk records; a.S0 may be null.
+// [B, H, nseg, dk, dv + dk], the composed start states into Sin [B, H, nseg, dk, dv], then
+// either o (a.o; a.states null) or the state before every chunk (a.states; a.o null), and S_final
+// if a.S_final is set.  a.records holds the chunk records (forward-only ones or those of the
+// factor buffer); a.S0 may be null.
 hipError_t launch_fwd_segments(const FwdArgs &a, int dk, bool gl, bool sg, float *E, float *Sin, hipStream_t st);
 hipError_t launch_fwd_sweep(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
                             hipStream_t st);

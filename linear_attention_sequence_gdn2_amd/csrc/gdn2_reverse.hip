@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 // and dO in LDS (double-buffered, so one barrier per chunk), then
 // dS = R dS' + Q2^T dO.  The factors are chunk-local, so at VT = 64 (one workgroup
 // per CU, registers to spare) the next chunk's fragments are loaded while the
-// current chunk's products run; at VT = 32 two workgroups share a CU instead.
+// current chunk's products run; at VT = 32 and 16 two workgroups may share a CU instead.
 template <int DK, int VT>
 struct ReverseCfg {
     static constexpr int NM = DK / 16, NVT = VT / 16;
@@ -365,8 +365,10 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
     constexpr int NM = DK / 16, NKS = DK / 32, NVT = VT / 16;
     constexpr int NTH = Cfg::NTH, TPW = Cfg::TPW;
     constexpr int PK = DK + 8, PT = kChunk + 8;
-    constexpr int OPT = VT * kChunk / NTH;          // dO elements per thread per chunk
-    static_assert(OPT % 4 == 0, "dO staging");
+    // dO elements per thread per chunk (at least 4: with more threads than that needs, the
+    // upper ones load and stage a copy of the lower ones' values)
+    constexpr int OPT = VT * kChunk / NTH >= 4 ? VT * kChunk / NTH : 4, OTG = kChunk / OPT;
+    static_assert(OPT % 4 == 0 && OTG * OPT == kChunk, "dO staging");
     constexpr size_t FPC = factor_elems_per_chunk<DK>();
 
     __shared__ __align__(16) __bf16 sD[2][2 * VT * PK];   // dS' as [col][channel] (hi, lo)
@@ -398,7 +400,7 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
     // 16 bytes at a time: for each group of 4 tokens a lane reads token + (tid % 4) at columns
     // 4 ((tid / 4) % (VT / 4)) ..; the 4x4 transpose inside each quad of lanes (at staging) gives
     // the lane its column.
-    const int ocol = tid % VT, otg = tid / VT;
+    const int ocol = tid % VT, otg = (tid / VT) % OTG;
     float ox[OPT];
     auto load_dO = [&](int cc) {
 #pragma unroll
@@ -564,12 +566,17 @@ static hipError_t reverse_t(const BwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// 64-column tiles when they still give every CU a workgroup, else 32 (two workgroups per CU):
-// with few heads the 64-column reverse step is slower than two 32-column ones (B1 T16K H16:
-// about 1.35 against 0.79 ms)
+// 64-column tiles when they still give every CU a workgroup; else 32 (two workgroups per CU),
+// or 16 when even 16-column tiles leave CUs without one.  A sequential chain is paced by its
+// per-chunk latency, which narrower tiles shorten: B1 T16K H16 takes about 1.35, 0.78 and
+// 0.57 ms at 64, 32 and 16 columns.  At B4 T4K H16 the 32-column tiles beat the 16-column
+// ones (0.24 against 0.30 ms); prefetching the next chunk's factors gains nothing at 32 columns.
 template <int DK>
 static hipError_t reverse_vt(const BwdArgs &a, hipStream_t st) {
-    if (a.DV >= 64 && (long)a.B * a.H * (a.DV / 64) >= cu_count()) return reverse_t<DK, 64>(a, st);
+    const long bh = (long)a.B * a.H;
+    const int cus = cu_count();
+    if (a.DV >= 64 && bh * (a.DV / 64) >= cus) return reverse_t<DK, 64>(a, st);
+    if (bh * (a.DV / 16) <= cus) return reverse_t<DK, 16>(a, st);
     return reverse_t<DK, 32>(a, st);
 }
 

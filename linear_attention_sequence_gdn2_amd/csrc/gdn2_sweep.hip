@@ -748,32 +748,34 @@ static hipError_t sweep64_mode(const FwdArgs &a, int dk, FwdMode mode, hipStream
     return hipErrorInvalidValue;
 }
 
-template <int DK, bool GL, bool SG, int SEG>
+// SEG 1: the maps; SEG 2: o (ST false) or the state before every chunk (ST true)
+template <int DK, bool GL, bool SG, int SEG, bool ST>
 static hipError_t seg_t(const FwdArgs &a, hipStream_t st) {
     const int ntile = SEG == 1 ? a.nvt + DK / 64 : a.nvt;
-    hipLaunchKernelGGL((fwd_sweep64_kernel<DK, SEG == 2, false, GL, SG, SEG>),
+    hipLaunchKernelGGL((fwd_sweep64_kernel<DK, SEG == 2 && !ST, SEG == 2 && ST, GL, SG, SEG>),
                        dim3((unsigned)(a.B * a.H * a.nseg * ntile)), dim3(kChunkThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <int SEG>
+template <int SEG, bool ST>
 static hipError_t seg_dk(const FwdArgs &a, int dk, bool gl, bool sg, hipStream_t st) {
     if (gl && sg) return hipErrorInvalidValue;
-    if (dk == 128) return gl ? seg_t<128, true, false, SEG>(a, st) : sg ? seg_t<128, false, true, SEG>(a, st)
-                                                                          : seg_t<128, false, false, SEG>(a, st);
-    if (dk == 64) return gl ? seg_t<64, true, false, SEG>(a, st) : sg ? seg_t<64, false, true, SEG>(a, st)
-                                                                        : seg_t<64, false, false, SEG>(a, st);
+    if (dk == 128) return gl ? seg_t<128, true, false, SEG, ST>(a, st) : sg ? seg_t<128, false, true, SEG, ST>(a, st)
+                                                                              : seg_t<128, false, false, SEG, ST>(a, st);
+    if (dk == 64) return gl ? seg_t<64, true, false, SEG, ST>(a, st) : sg ? seg_t<64, false, true, SEG, ST>(a, st)
+                                                                            : seg_t<64, false, false, SEG, ST>(a, st);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_segments(const FwdArgs &a_in, int dk, bool gl, bool sg, float *E, float *Sin,
                                hipStream_t st) {
     if (a_in.dv % 64 != 0 || a_in.nseg < 1 || a_in.seg_len < 1) return hipErrorInvalidValue;
+    if ((a_in.o == nullptr) == (a_in.states == nullptr)) return hipErrorInvalidValue;   // o or states
     FwdArgs a = a_in;
     a.nvt = a.dv / 64;
     // 1: every segment's map from zero and identity starts
     a.S0 = nullptr, a.o = nullptr, a.S_final = nullptr, a.states = E;
-    hipError_t e = seg_dk<1>(a, dk, gl, sg, st);
+    hipError_t e = seg_dk<1, false>(a, dk, gl, sg, st);
     if (e != hipSuccess) return e;
     // 2: the start states, composed in order
     const unsigned ncomb = (unsigned)(a.B * a.H * (a.dv / 16));
@@ -782,9 +784,10 @@ hipError_t launch_fwd_segments(const FwdArgs &a_in, int dk, bool gl, bool sg, fl
     else return hipErrorInvalidValue;
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // 3: every segment again from its start state, writing o (and S_final from the last)
-    a.S0 = Sin, a.o = a_in.o, a.S_final = a_in.S_final, a.states = nullptr;
-    return seg_dk<2>(a, dk, gl, sg, st);
+    // 3: every segment again from its start state, writing o or the chunk states (and S_final
+    // from the last segment)
+    a.S0 = Sin, a.o = a_in.o, a.S_final = a_in.S_final, a.states = a_in.states;
+    return a_in.states ? seg_dk<2, true>(a, dk, gl, sg, st) : seg_dk<2, false>(a, dk, gl, sg, st);
 }
 
 hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,

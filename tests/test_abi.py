@@ -231,9 +231,18 @@ def test_forward_workspace_on_wide_shapes():
     seg = 1 * 16 * 8 * 128 * ((128 + 128) + 128) * 4
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=16384, H=16, dk=128, dv=128))) == \
         1 * 16 * 256 * record + seg
+    # the one-call backward splits its state sweep the same way: the same blocks after the
+    # states, their gradients and the factor buffer
+    long = _shape(B=1, T=16384, H=16, dk=128, dv=128)
+    states = 16 * 256 * 128 * 128 * 4
+    factors = 16 * 256 * ((128 * 128 + 64 * 128) * 4 + record)
+    assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(long)) == 2 * states + factors + seg
     # few heads but a short sequence (under 64 chunks): no segments
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=4000, H=16, dk=128, dv=128))) == \
         1 * 16 * 63 * record
+    short = _shape(B=1, T=4000, H=16, dk=128, dv=128)
+    assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(short)) == \
+        2 * 16 * 63 * 128 * 128 * 4 + 16 * 63 * ((128 * 128 + 64 * 128) * 4 + record)
     # fp32 q/k/v, dk = 32, or dv not a multiple of 64: one fused sweep, no workspace
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0))) == 0
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == 0

@@ -48,6 +48,19 @@ def test_small_shapes_grads(B, T, H, dk, dv, qkv, s0, dsf):
     _run(inp, with_dsf=dsf)
 
 
+# The reverse sweep's value-tile width follows the number of heads (on 256 CUs): 64 columns
+# when B*H*dv/64 >= 256, 16 when B*H*dv/16 <= 256, else 32.  Ragged T at each width.
+@pytest.mark.parametrize("B,T,H,dk,dv", [
+    (8, 100, 16, 128, 128),   # 64 columns
+    (3, 130, 16, 128, 128),   # 32
+    (1, 300, 16, 128, 128),   # 16
+    (2, 129, 16, 64, 128),    # 16, dk 64
+])
+def test_reverse_tile_widths(B, T, H, dk, dv):
+    inp = make_inputs(B, T, H, dk, dv, seed=B * T + H + dk, s0_std=0.05, grads=True)
+    _run(inp)
+
+
 def test_full_size_fwdbwd_workload():
     wl = WORKLOADS["fwdbwd_bf16_B4H16T4096d128"]
     _run(make_workload(wl))

@@ -3,7 +3,9 @@ keep at most one CU in four busy, gdn2_chunk_fwd splits each sequence into segme
 by side.  It sweeps every segment's state map from zero and identity starts, composes the maps
 in order (S_{s+1} = M_s S_s + N_s) and sweeps again from the true start states.  Checked against
 the fp64 oracle (3e-3, bf16) and against the unsegmented factored sweep (1e-3) on ragged T, with
-and without S0, both key widths and every gate format."""
+and without S0, both key widths and every gate format.  The one-call backward (gdn2_chunk_bwd)
+splits its state sweep the same way: its gradients are checked against the oracle's (5e-3) and
+against the unsegmented chain of entry points (1e-3)."""
 import ctypes
 
 import pytest
@@ -60,3 +62,36 @@ def test_segmented_forward(B, T, H, dk, dv, extra):
     assert eo < 3e-3 and es < 3e-3, (eo, es)
     for x, y in ((o, o2), (sf, sf2)):
         assert float((x - y).abs().max()) <= 1e-3 * float(y.abs().max())
+
+
+NAMES = ["dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,extra", [
+    (1, 64 * 70 + 17, 2, 128, 128, {"s0_std": 0.2}),   # 8 segments of 9, ragged tail
+    (1, 64 * 64, 4, 64, 128, {}),                       # dk = 64, zero start state
+    (2, 64 * 64 + 5, 16, 128, 128, {"s0_std": 0.1}),    # a quarter of the CUs: 4 segments of 17
+    (1, 64 * 72, 2, 128, 128, {"gate_logits": True, "s0_std": 0.1}),
+    (1, 64 * 72, 2, 128, 128, {"gates": "gdn", "token_gates": True, "s0_std": 0.1}),
+])
+def test_segmented_backward(B, T, H, dk, dv, extra):
+    inp = make_inputs(B, T, H, dk, dv, seed=9400 + T + dk + dv, grads=True, **extra)
+    d = to_dev(inp)
+    g = gdn2.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"], d["dS_final"])
+    # the same gradients from the entry points one by one, with the unsegmented state sweep
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    _, _, states = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_o=False)
+    dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], dk, d["dS_final"])
+    g2 = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates, factors)
+    g2["dS0"] = dS0
+    torch.cuda.synchronize()
+    for n in NAMES:
+        x, y = g[n], g2[n]
+        assert float((x - y).abs().max()) <= 1e-3 * float(y.abs().max()), n
+    if extra.get("gate_logits") or extra.get("token_gates"):
+        return   # the gate formats' oracle gradients are checked on the unsegmented path
+    ref = oracle.bwd(*oracle_args(inp), inp["dO"], inp["dS_final"])
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e < 5e-3}
+    assert not bad, bad
