@@ -123,7 +123,10 @@ int gdn2_chunk_fwd(const gdn2_shape *shape,
 
 /* Bytes of device workspace gdn2_chunk_bwd needs: two fp32 states per chunk per
  * (batch, head) and the per-chunk adjoint factors, i.e.
- * 2 * gdn2_chunk_states_bytes() + gdn2_chunk_factors_bytes(); (size_t)-1 if invalid. */
+ * 2 * gdn2_chunk_states_bytes() + gdn2_chunk_factors_bytes(); (size_t)-1 if invalid.
+ * On the shapes where gdn2_chunk_fwd splits the sequence into segments, the backward's
+ * state sweep is split the same way, and the same per-segment maps and start states
+ * (dk*(2dv+dk) fp32 per batch, head and segment) follow the factors. */
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_shape *shape);
 
 /* Gate-aware backward pass of loss = sum(dO * o) + sum(dS_final * S_final):
