@@ -4,7 +4,8 @@
 One step = forward + gate-aware backward (gdn2_chunk_bwd_factors, gdn2_chunk_fwd_factored,
 gdn2_chunk_bwd_reverse, gdn2_chunk_bwd_grads: the staged form of gdn2_chunk_fwd +
 gdn2_chunk_bwd in which the key-side chunk operands are formed once and the backward
-reuses the forward's chunk states) over one batch of the
+reuses the forward's chunk states; on shapes where gdn2_chunk_sweeps runs the two sweeps
+as one launch, that entry replaces the middle two) over one batch of the
 forward/backward workload B=8, T=2048, H=16, dk=dv=128 (bf16 q/k/v, fp32
 gates, decay and state; the 2K x 8 training shape of the Gated DeltaNet-2
 pages).  Inputs are seeded synthetic tensors (linear_attention_sequence_gdn2_amd.inputs)
@@ -259,6 +260,7 @@ def configs_bench(dev, timed_steps, iters=10, steps=10, warmup=3):
             r.update({"step_ms": round(wall / steps * 1e3, 4),
                       "step_tokens_per_s": round(wl.B * wl.T / (wall / steps), 1),
                       "kernel_ms": [round(v, 4) for v in k_ms],
+                      "sweeps_one_launch": gdn2.sweeps_fused(wl.B, wl.T, wl.H, wl.dk, wl.dv, d["q"].dtype),
                       "step_algorithmic_frac": round((io + bwd_io) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         res[name] = r
     return res
@@ -382,16 +384,26 @@ def main():
         #   fwd_sweep_kernel    (gdn2_chunk_fwd_factored: o, S_final and the chunk-start states)
         #   bwd_reverse_kernel  (gdn2_chunk_bwd_reverse: end-state gradient of every chunk, dS0)
         #   bwd_chunk_kernel    (gdn2_chunk_bwd_grads: dq, dk, dv, dlog_alpha, db, dw)
+        # With few heads gdn2_chunk_sweeps runs the middle two as one launch (fwd_rev_sweep_kernel);
+        # the step then calls it, and its time is the second entry of the breakdown (the third is 0).
+        fused = gdn2.sweeps_fused(wl.B, wl.T, wl.H, wl.dk, wl.dv, d["q"].dtype)
+
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
             gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"], factors=factors)
             if ev is not None:
                 ev[1].record(stream)
-            o, sf, _ = gdn2.fwd_factored(factors, d["v"], d["w"], wl.dk, d["S0"], states=states)
-            if ev is not None:
-                ev[2].record(stream)
-            _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
+            if fused:
+                o, sf, _, _, dS0 = gdn2.sweeps(factors, d["v"], d["w"], wl.dk, d["S0"], d["dO"], d["dS_final"],
+                                               states=states, dstates=dstates)
+                if ev is not None:
+                    ev[2].record(stream)
+            else:
+                o, sf, _ = gdn2.fwd_factored(factors, d["v"], d["w"], wl.dk, d["S0"], states=states)
+                if ev is not None:
+                    ev[2].record(stream)
+                _, dS0 = gdn2.bwd_reverse(factors, d["dO"], wl.dk, d["dS_final"], dstates=dstates)
             if ev is not None:
                 ev[3].record(stream)
             g = gdn2.bwd_grads(*fargs[:6], d["dO"], states, dstates, factors)

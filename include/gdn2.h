@@ -208,6 +208,24 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors,
                            const float *dO, const float *dS_final,
                            float *dstates, float *dS0, void *stream);
 
+/* The training step's two sweeps from one factor buffer of gdn2_chunk_bwd_factors: the
+ * forward sweep of gdn2_chunk_fwd_factored (o, S_final, the state before every chunk) and the
+ * reverse sweep of gdn2_chunk_bwd_reverse (dS' of every chunk, dS0), with the same arguments,
+ * layouts and results as those two calls (chunk map and its adjoint: blog on Gated DeltaNet-2,
+ * section "Token path and parallel training").  The sweeps are independent; where
+ * gdn2_chunk_sweeps_fused() is 1 (bf16 q/k/v, dk 64 or 128, dv a multiple of 64, and few enough
+ * heads that the two sweeps' 64-column tiles together need at most one workgroup per CU) they
+ * run as one launch, side by side; otherwise one after the other.  o, states and dstates are
+ * required; S0, dS_final (NULL = zeros), S_final and dS0 (NULL = not wanted) are optional.
+ * Errors as for those two entry points; nothing is launched if an argument check fails. */
+int gdn2_chunk_sweeps(const gdn2_shape *shape, const void *factors, const void *v, const void *w,
+                      const float *S0, const float *dO, const float *dS_final,
+                      float *o, float *S_final, float *states, float *dstates, float *dS0, void *stream);
+
+/* 1 if gdn2_chunk_sweeps runs its two sweeps as one launch for this shape, 0 if as two,
+ * -1 if the shape is invalid. */
+int gdn2_chunk_sweeps_fused(const gdn2_shape *shape);
+
 /* Token gradients from states, dstates and the factor buffer of
  * gdn2_chunk_bwd_factors (same shape and inputs): dq, dk, dlog_alpha, db [B,T,H,dk],
  * dv, dw [B,T,H,dv]. */

@@ -8,9 +8,9 @@ from ._binding import (EXPORTS, LIB_PATH, Gdn2Error, Gdn2Shape, bwd, bwd_factors
                        bwd_reverse, bwd_saved, bwd_workspace_bytes, chunk_states, factors_bytes, fwd, fwd_factored,
                        fwd_states,
                        load, make_shape, output_bwd, output_bwd_workspace_bytes, output_fwd, states_shape,
-                       step)
+                       step, sweeps, sweeps_fused)
 
 __all__ = ["fwd", "bwd", "fwd_states", "chunk_states", "bwd_factors", "bwd_reverse", "bwd_grads", "bwd_saved",
            "load", "bwd_workspace_bytes", "factors_bytes", "states_shape", "Gdn2Error", "Gdn2Shape", "LIB_PATH",
            "EXPORTS", "make_shape", "step", "output_fwd", "output_bwd",
-           "output_bwd_workspace_bytes", "fwd_factored"]
+           "output_bwd_workspace_bytes", "fwd_factored", "sweeps", "sweeps_fused"]

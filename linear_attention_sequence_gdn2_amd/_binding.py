@@ -33,7 +33,8 @@ EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
            "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
            "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step", "gdn2_output_fwd",
-           "gdn2_output_bwd_workspace_size", "gdn2_output_bwd", "gdn2_chunk_fwd_factored"]
+           "gdn2_output_bwd_workspace_size", "gdn2_output_bwd", "gdn2_chunk_fwd_factored",
+           "gdn2_chunk_sweeps", "gdn2_chunk_sweeps_fused"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -83,6 +84,10 @@ def load():
         lib.gdn2_chunk_fwd_factored.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_reverse.argtypes = [SP] + [P] * 5 + [P]
         lib.gdn2_chunk_bwd_reverse.restype = ctypes.c_int
+        lib.gdn2_chunk_sweeps.argtypes = [SP] + [P] * 11 + [P]
+        lib.gdn2_chunk_sweeps.restype = ctypes.c_int
+        lib.gdn2_chunk_sweeps_fused.argtypes = [SP]
+        lib.gdn2_chunk_sweeps_fused.restype = ctypes.c_int
         lib.gdn2_chunk_bwd_grads.argtypes = [SP] + [P] * 16 + [P]
         lib.gdn2_chunk_bwd_grads.restype = ctypes.c_int
         lib.gdn2_step.argtypes = [SP] + [P] * 9 + [P]
@@ -349,6 +354,51 @@ def bwd_reverse(factors, dO, dk, dS_final=None, want_dS0=True, dstates=None):
     _check(lib.gdn2_chunk_bwd_reverse(ctypes.byref(shape), _ptr(factors), _ptr(dO), _ptr(dS_final),
                                       _ptr(dstates), _ptr(dS0), _stream(dO.device)))
     return dstates, dS0
+
+
+def sweeps_fused(B, T, H, dk, dv, qkv_dtype=torch.bfloat16):
+    """Whether sweeps() runs its two sweeps as one launch for this shape."""
+    return load().gdn2_chunk_sweeps_fused(ctypes.byref(make_shape(B, T, H, dk, dv, qkv_dtype))) == 1
+
+
+def sweeps(factors, v, w, dk, S0, dO, dS_final=None, want_state=True, want_dS0=True, states=None, dstates=None):
+    """Both sweeps of the training step from the factor buffer of bwd_factors (gdn2_chunk_sweeps):
+    (o, S_final or None, states, dstates, dS0 or None), the results of fwd_factored and
+    bwd_reverse.  One launch where sweeps_fused() holds, else two."""
+    if not v.is_cuda:
+        raise RuntimeError("gdn2: tensors must live on a GPU (HIP device); got %s" % v.device)
+    B, T, H, dv = v.shape
+    if v.dtype not in (torch.float32, torch.bfloat16) or w.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gdn2: v must be float32 or bfloat16, w float32 values or bfloat16 logits")
+    if w.dtype == torch.bfloat16 and v.dtype != torch.bfloat16:
+        raise TypeError("gdn2: bfloat16 gate logits need bfloat16 q/k/v")
+    sc = _gate_scalar((B, T, H), dict(w=w))
+    if tuple(w.shape) != _gate_shape("w", (B, T, H), dv, sc) or w.device != v.device:
+        raise ValueError("gdn2: w has shape %s, expected %s" % (tuple(w.shape), _gate_shape("w", (B, T, H), dv, sc)))
+    if tuple(dO.shape) != (B, T, H, dv) or dO.dtype != torch.float32 or dO.device != v.device:
+        raise ValueError("gdn2: dO must be float32 [B,T,H,dv]")
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32 or t.device != v.device):
+            raise ValueError("gdn2: %s must be float32 [B,H,dk,dv]" % name)
+    for t in (v, w, S0, dO, dS_final):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("gdn2: tensors must be contiguous")
+    if factors.device != v.device or factors.numel() * factors.element_size() < factors_bytes(B, T, H, dk, dv):
+        raise ValueError("gdn2: factors buffer does not match the shape")
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, v.dtype, w.dtype, sc)
+    dev = v.device
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_state else None
+    if states is None:
+        states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=dev)
+    if dstates is None:
+        dstates = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=dev)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    _check(lib.gdn2_chunk_sweeps(ctypes.byref(shape), _ptr(factors), _ptr(v), _ptr(w), _ptr(S0), _ptr(dO),
+                                 _ptr(dS_final), _ptr(o), _ptr(sf), _ptr(states), _ptr(dstates), _ptr(dS0),
+                                 _stream(dev)))
+    return o, sf, states, dstates, dS0
 
 
 def bwd_grads(q, k, v, log_alpha, b, w, dO, states, dstates, factors):

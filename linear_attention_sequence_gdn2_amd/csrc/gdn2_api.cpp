@@ -295,6 +295,38 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const f
     return launch_status(gdn2::launch_bwd_reverse(a, shape->dk, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int gdn2_chunk_sweeps_fused(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return -1;
+    return gdn2::fwd_rev_fused(shape->B, shape->H, shape->dk, shape->dv, shape->qkv_dtype == GDN2_BF16) ? 1 : 0;
+}
+
+int gdn2_chunk_sweeps(const gdn2_shape *shape, const void *factors, const void *v, const void *w, const float *S0,
+                      const float *dO, const float *dS_final, float *o, float *S_final, float *states,
+                      float *dstates, float *dS0, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!factors || !v || !w || !dO || !o || !states || !dstates) return GDN2_ERR_INVALID_ARG;
+    if (!all_aligned({factors, v, S0, dO, dS_final, o, S_final, states, dstates, dS0}) ||
+        !gates_aligned(shape, nullptr, nullptr, w))
+        return GDN2_ERR_INVALID_ARG;
+    if (gdn2_chunk_sweeps_fused(shape) != 1) {
+        // the two sweeps one after the other
+        const int rc = gdn2_chunk_fwd_factored(shape, factors, v, w, S0, o, S_final, states, stream);
+        if (rc != GDN2_OK) return rc;
+        return gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
+    }
+    int vt;
+    gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, o, S_final, states, &vt);
+    const long items = (long)shape->B * shape->H * nchunks(shape);
+    f.records = reinterpret_cast<const char *>(factors) +
+                (gdn2::factor_buffer_bytes(items, shape->dk) - gdn2::record_buffer_bytes(items, shape->dk));
+    gdn2::BwdArgs a = bwd_args(shape);
+    a.factors = const_cast<void *>(factors);
+    a.dO = dO; a.dS_final = dS_final; a.dstates = dstates; a.dS0 = dS0;
+    return launch_status(gdn2::launch_fwd_rev_sweeps(f, a, shape->dk, gate_logits(shape), gate_scalar(shape),
+                                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape, const void *q, const void *k, const void *v,
                          const void *log_alpha, const void *b, const void *w, const float *dO,
                          const float *states, const float *dstates, const void *factors, float *dq, float *dk,
@@ -353,6 +385,21 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
         float *Sin = E + (size_t)shape->B * shape->H * nseg * shape->dk * (shape->dv + shape->dk);
         rc = launch_status(gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E, Sin,
                                                      reinterpret_cast<hipStream_t>(stream)));
+    } else if (gdn2_chunk_sweeps_fused(shape) == 1) {
+        // few heads: the state sweep and the reverse sweep side by side in one launch
+        int vt;
+        gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, nullptr, nullptr, states, &vt);
+        const long items = (long)shape->B * shape->H * nchunks(shape);
+        f.records = reinterpret_cast<const char *>(factors) +
+                    (gdn2_chunk_factors_bytes(shape) - gdn2::record_buffer_bytes(items, shape->dk));
+        gdn2::BwdArgs r = bwd_args(shape);
+        r.factors = factors;
+        r.dO = dO; r.dS_final = dS_final; r.dstates = dstates; r.dS0 = dS0;
+        rc = launch_status(gdn2::launch_fwd_rev_sweeps(f, r, shape->dk, gate_logits(shape), gate_scalar(shape),
+                                                       reinterpret_cast<hipStream_t>(stream)));
+        if (rc != GDN2_OK) return rc;
+        return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, factors, dq, dk, dv,
+                                    dlog_alpha, db, dw, stream);
     } else {
         rc = gdn2_chunk_fwd_factored(shape, factors, v, w, S0, nullptr, nullptr, states, stream);
     }

@@ -80,6 +80,14 @@ hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool
 hipError_t launch_fwd_segments(const FwdArgs &a, int dk, bool gl, bool sg, float *E, float *Sin, hipStream_t st);
 hipError_t launch_fwd_sweep(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
                             hipStream_t st);
+// Whether the forward sweep (o, S_final, chunk states) and the reverse sweep from one factor
+// buffer run as one launch: bf16 q/k/v, dk 64 or 128, dv a multiple of 64, and 64-column tiles of
+// both sweeps together at most one workgroup per CU.
+bool fwd_rev_fused(int B, int H, int dk, int dv, bool bf16);
+// That launch (fa: v, w, S0, o, S_final, states, records of the factor buffer; ba: factors, dO,
+// dS_final, dstates, dS0; o may be null: the states only).  hipErrorInvalidValue where
+// fwd_rev_fused is false.
+hipError_t launch_fwd_rev_sweeps(const FwdArgs &fa, const BwdArgs &ba, int dk, bool gl, bool sg, hipStream_t st);
 // Bytes of the factor buffer of `items` chunks: the adjoint factors R, Q2^T of every chunk,
 // then the chunk operand record of every chunk (read by the chunk-gradient kernel).
 size_t factor_buffer_bytes(long items, int dk);

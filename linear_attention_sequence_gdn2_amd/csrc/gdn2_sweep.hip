@@ -21,6 +21,7 @@
 // every wave done with the chunk's LDS.
 #include "gdn2_chunk.h"
 #include "gdn2_kernels.h"
+#include "gdn2_rsweep.h"
 
 namespace gdn2 {
 
@@ -277,8 +278,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 // Wave (hf, w) owns tokens 16w..16w+15 and columns 32hf..32hf+31 of X, U and O, and
 // the state tiles of one 16-row block (at DK = 128).  bf16 q/k/v only (the X product
 // uses the hi part of Et, so one Et plane is staged); about 155 KB of LDS.
+// LDS arrays of the wide sweep (bf16 elements): Kt rows [token][channel] (hi, lo), Et rows (hi),
+// Qt rows (hi, lo; only when o is written), S^T [col][channel], X^T and U^T [col][token] (hi, lo)
+template <int DK, bool OUT>
+struct Sweep64Lds {
+    static constexpr int RK = kChunk * (DK + 8);
+    static constexpr int K = 2 * RK, E = RK, Q = OUT ? 2 * RK : 8;
+    static constexpr int S = 2 * 64 * (DK + 8), X = 2 * 64 * (kChunk + 8), U = X;
+};
+
+// One workgroup's sweep: L is its (batch, head[, segment], value tile) index in launch order
 template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG>
-__global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, __bf16 *sK, __bf16 *sE,
+                                                 __bf16 *sQ, __bf16 *sS, __bf16 *sX, __bf16 *sU) {
     using Rec = ChunkRecord<DK>;
     constexpr int VT = 64, NTH = kChunkThreads;
     constexpr int NKS = DK / 32, NMT = DK / 16;
@@ -291,18 +303,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     constexpr int NEP = NEQ * PL16 / NTH;                // Et/Qt pieces per thread
     static_assert(NKP * NTH == 2 * PL16 && NEP * NTH == NEQ * PL16, "row planes split evenly");
 
-    __shared__ __align__(16) __bf16 sK[2 * RK];          // Kt rows [token][channel] (hi, lo)
-    __shared__ __align__(16) __bf16 sE[RK];              // Et rows, hi
-    __shared__ __align__(16) __bf16 sQ[OUT ? 2 * RK : 8];   // Qt rows (hi, lo)
-    __shared__ __align__(16) __bf16 sS[2 * VT * PK];     // S^T [col][channel] (hi, lo)
-    __shared__ __align__(16) __bf16 sX[2 * VT * PT];     // X^T [col][token] (hi, lo)
-    __shared__ __align__(16) __bf16 sU[2 * VT * PT];     // U^T [col][token] (hi, lo)
-
     // Segments (SEG 1, 2): each (b, h) is split into nseg runs of seg_len chunks.  SEG 1 sweeps a
     // segment from a zero state (value tiles) and, in DK / 64 more tiles, from the identity with
     // z = 0: the end states N and M give the segment's map S -> M S + N.  SEG 2 sweeps a segment
     // from its true start state (the maps composed in order) and writes o.
-    const int L = xcd_swizzle(blockIdx.x, gridDim.x);
     const int ntile = SEG == 1 ? a.nvt + DK / 64 : a.nvt;
     const int vt = L % ntile, rest = L / ntile;
     const int seg = SEG ? rest % a.nseg : 0, bh = SEG ? rest / a.nseg : rest;
@@ -613,6 +617,32 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
     }
 }
 
+template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG>
+__global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a) {
+    using Lds = Sweep64Lds<DK, OUT>;
+    __shared__ __align__(16) __bf16 sK[Lds::K], sE[Lds::E], sQ[Lds::Q], sS[Lds::S], sX[Lds::X], sU[Lds::U];
+    fwd_sweep64_body<DK, OUT, STATES, GL, SG, SEG>(a, xcd_swizzle(blockIdx.x, gridDim.x), sK, sE, sQ, sS, sX, sU);
+}
+
+// The training step's two sweeps in one launch: the forward sweep (the state before every chunk,
+// and o and S_final when OUT) and the reverse sweep (dS' of every chunk, dS0), both from one factor
+// buffer.  Neither reads what the other writes, and with few heads each alone leaves CUs idle.
+// The first nfwd workgroups (in the swizzled order) sweep forward with 64-column tiles, the
+// others backward with 64-column tiles; the reverse role keeps its dS' and dO buffers in the
+// forward role's arrays.
+template <int DK, bool OUT, bool GL, bool SG>
+__global__ __launch_bounds__(kChunkThreads, 1) void fwd_rev_sweep_kernel(FwdArgs fa, BwdArgs ba, int nfwd) {
+    using Lds = Sweep64Lds<DK, OUT>;
+    using RL = RevLds<DK, 64>;
+    static_assert(RL::D <= Lds::K && RL::D <= Lds::S && RL::O <= Lds::X && RL::O <= Lds::U,
+                  "the reverse role's buffers fit the forward role's arrays");
+    static_assert(ReverseCfg<DK, 64>::NTH == kChunkThreads, "both roles take the whole workgroup");
+    __shared__ __align__(16) __bf16 sK[Lds::K], sE[Lds::E], sQ[Lds::Q], sS[Lds::S], sX[Lds::X], sU[Lds::U];
+    const int L = xcd_swizzle(blockIdx.x, gridDim.x);
+    if (L < nfwd) fwd_sweep64_body<DK, OUT, true, GL, SG, 0>(fa, L, sK, sE, sQ, sS, sX, sU);
+    else bwd_reverse_body<DK, 64>(ba, L - nfwd, sK, sS, sX, sU);
+}
+
 // ---------------------------------------------------------------------------
 // segment composition: the start state of every segment of a (b, h)
 // ---------------------------------------------------------------------------
@@ -812,6 +842,34 @@ hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool
     if (gl) return bf16 ? sweep_mode<true, true, false>(a, dk, vt, mode, st) : hipErrorInvalidValue;
     if (sg) return bf16 ? sweep_mode<true, false, true>(a, dk, vt, mode, st) : hipErrorInvalidValue;
     return bf16 ? sweep_mode<true, false, false>(a, dk, vt, mode, st) : sweep_mode<false, false, false>(a, dk, vt, mode, st);
+}
+
+template <int DK, bool GL, bool SG>
+static hipError_t fwd_rev_t(const FwdArgs &fa, const BwdArgs &ba, hipStream_t st) {
+    const int nfwd = fa.B * fa.H * fa.nvt;
+    if (fa.o)
+        hipLaunchKernelGGL((fwd_rev_sweep_kernel<DK, true, GL, SG>), dim3((unsigned)(2 * nfwd)), dim3(kChunkThreads), 0,
+                           st, fa, ba, nfwd);
+    else
+        hipLaunchKernelGGL((fwd_rev_sweep_kernel<DK, false, GL, SG>), dim3((unsigned)(2 * nfwd)), dim3(kChunkThreads),
+                           0, st, fa, ba, nfwd);
+    return hipGetLastError();
+}
+
+bool fwd_rev_fused(int B, int H, int dk, int dv, bool bf16) {
+    return bf16 && (dk == 64 || dk == 128) && dv % 64 == 0 && 2L * B * H * (dv / 64) <= cu_count();
+}
+
+hipError_t launch_fwd_rev_sweeps(const FwdArgs &fa_in, const BwdArgs &ba, int dk, bool gl, bool sg, hipStream_t st) {
+    if (gl && sg) return hipErrorInvalidValue;
+    if (!fwd_rev_fused(fa_in.B, fa_in.H, dk, fa_in.dv, true) || !fa_in.states || !ba.dstates)
+        return hipErrorInvalidValue;
+    FwdArgs fa = fa_in;
+    fa.nvt = fa.dv / 64;
+    if (dk == 128) return gl ? fwd_rev_t<128, true, false>(fa, ba, st) : sg ? fwd_rev_t<128, false, true>(fa, ba, st)
+                                                                           : fwd_rev_t<128, false, false>(fa, ba, st);
+    return gl ? fwd_rev_t<64, true, false>(fa, ba, st) : sg ? fwd_rev_t<64, false, true>(fa, ba, st)
+                                                             : fwd_rev_t<64, false, false>(fa, ba, st);
 }
 
 }  // namespace gdn2

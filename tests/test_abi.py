@@ -197,6 +197,33 @@ def test_output_epilogue_checks_arguments():
     assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 1, None, F(-0.5), f, f, f, None, None, 0, None) == INVALID
 
 
+def test_sweeps_entry_checks_arguments_and_fusion_rule():
+    lib = gdn2.load()
+    f = P(0x10000)
+    s = _shape()
+    # factors, v, w, S0, dO, dS_final, o, S_final, states, dstates, dS0: all but S0, dS_final,
+    # S_final and dS0 required, and checked before any launch
+    args = [f] * 11
+    for i in (0, 1, 2, 4, 6, 8, 9):
+        a = list(args)
+        a[i] = None
+        assert lib.gdn2_chunk_sweeps(ctypes.byref(s), *a, None) == INVALID
+    a = list(args)
+    a[0] = P(0x10008)
+    assert lib.gdn2_chunk_sweeps(ctypes.byref(s), *a, None) == INVALID
+    assert lib.gdn2_chunk_sweeps(ctypes.byref(_shape(dv=96)), *args, None) == UNSUPPORTED
+    # one launch where both sweeps' 64-column tiles take at most one workgroup per CU (256 CUs)
+    def fused(**kw):
+        return lib.gdn2_chunk_sweeps_fused(ctypes.byref(_shape(**kw)))
+    assert fused(B=4, T=4096, H=16, dk=128, dv=128) == 1
+    assert fused(B=1, T=16384, H=16, dk=64, dv=128) == 1
+    assert fused(B=8, T=2048, H=16, dk=128, dv=128) == 0
+    assert fused(B=4, T=4096, H=16, dk=128, dv=128, dt=0) == 0    # fp32 q/k/v
+    assert fused(B=4, T=4096, H=16, dk=32, dv=128) == 0
+    assert fused(B=4, T=4096, H=16, dk=128, dv=32) == 0
+    assert fused(dk=96) == -1
+
+
 def test_factored_forward_checks_arguments():
     lib = gdn2.load()
     f = P(0x10000)

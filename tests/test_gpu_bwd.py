@@ -49,7 +49,8 @@ def test_small_shapes_grads(B, T, H, dk, dv, qkv, s0, dsf):
 
 
 # The reverse sweep's value-tile width follows the number of heads (on 256 CUs): 64 columns
-# when B*H*dv/64 >= 256, 16 when B*H*dv/16 <= 256, else 32.  Ragged T at each width.
+# when B*H*dv/64 >= 256, 16 when B*H*dv/16 <= 256, else 32.  Ragged T at each width, through
+# the staged entry points (gdn2_chunk_bwd_reverse on its own).
 @pytest.mark.parametrize("B,T,H,dk,dv", [
     (8, 100, 16, 128, 128),   # 64 columns
     (3, 130, 16, 128, 128),   # 32
@@ -58,7 +59,42 @@ def test_small_shapes_grads(B, T, H, dk, dv, qkv, s0, dsf):
 ])
 def test_reverse_tile_widths(B, T, H, dk, dv):
     inp = make_inputs(B, T, H, dk, dv, seed=B * T + H + dk, s0_std=0.05, grads=True)
-    _run(inp)
+    d = to_dev(inp)
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    _, _, states = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_o=False)
+    dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], dk, d["dS_final"])
+    g = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates, factors)
+    g["dS0"] = dS0
+    torch.cuda.synchronize()
+    ref = oracle.bwd(*oracle_args(inp), inp["dO"], inp["dS_final"])
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e < TOL}
+    assert not bad, bad
+
+
+# The one-call backward runs its state sweep and the reverse sweep in one launch where both
+# sweeps' 64-column tiles fit one workgroup per CU (and the sequence is not segmented): the
+# same gradients as the staged entry points, whose states-only sweep takes narrower tiles there.
+@pytest.mark.parametrize("B,T,H,dk,dv,extra", [
+    (4, 200, 16, 128, 128, {"s0_std": 0.1}),
+    (2, 129, 8, 64, 128, {}),
+    (2, 150, 4, 128, 128, {"gate_logits": True}),
+    (2, 150, 4, 128, 128, {"gates": "gdn", "token_gates": True}),
+])
+def test_one_call_backward_with_fused_sweeps(B, T, H, dk, dv, extra):
+    inp = make_inputs(B, T, H, dk, dv, seed=B * T + H + dk + 1, grads=True, **extra)
+    d = to_dev(inp)
+    assert gdn2.sweeps_fused(B, T, H, dk, dv)
+    g = gdn2.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"], d["dS_final"])
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    _, _, states = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_o=False)
+    dstates, dS0 = gdn2.bwd_reverse(factors, d["dO"], dk, d["dS_final"])
+    g2 = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates, factors)
+    g2["dS0"] = dS0
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert float((g[n] - g2[n]).abs().max()) <= 1e-3 * float(g2[n].abs().max()), n
 
 
 def test_full_size_fwdbwd_workload():

@@ -150,3 +150,48 @@ def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
     torch.cuda.synchronize()
     assert torch.equal(states, st2)
     assert torch.equal(o_i, o_f) and torch.equal(sf_i, sf_f)
+
+
+# gdn2_chunk_sweeps: both sweeps of the training step from one factor buffer; one launch where
+# their 64-column tiles together take at most one workgroup per CU (256 CUs), two otherwise.  The
+# same bodies run as in the two separate entry points, so the results are the same bit for bit.
+@pytest.mark.parametrize("B,T,H,dk,dv,extra,one", [
+    (4, 130, 16, 128, 128, {"s0_std": 0.1}, True),      # 256 workgroups: one launch
+    (2, 200, 8, 64, 128, {}, True),                      # dk = 64
+    (1, 64 * 20 + 3, 2, 128, 64, {"s0_std": 0.2}, True),
+    (2, 150, 4, 128, 128, {"gate_logits": True}, True),
+    (2, 150, 4, 128, 128, {"gates": "gdn", "token_gates": True}, True),
+    (8, 100, 16, 128, 128, {}, False),                   # 512 workgroups: two launches
+    (2, 70, 2, 128, 128, {"qkv_dtype": "f32"}, False),   # fp32 q/k/v: two launches
+])
+def test_sweeps_entry_matches_separate_calls(B, T, H, dk, dv, extra, one):
+    inp = make_inputs(B, T, H, dk, dv, seed=B * 31 + T + H + dk, grads=True, **extra)
+    d = to_dev(inp)
+    assert gdn2.sweeps_fused(B, T, H, dk, dv, d["q"].dtype) == one
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    o, sf, st, dst, dS0 = gdn2.sweeps(factors, d["v"], d["w"], dk, d["S0"], d["dO"], d["dS_final"])
+    o2, sf2, st2 = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"])
+    dst2, dS02 = gdn2.bwd_reverse(factors, d["dO"], dk, d["dS_final"])
+    torch.cuda.synchronize()
+    for x, y in ((o, o2), (sf, sf2), (st, st2), (dst, dst2), (dS0, dS02)):
+        assert torch.equal(x, y)
+
+
+def test_training_chain_through_fused_sweeps():
+    """factors -> both sweeps in one launch -> token gradients, on a shape the one launch takes,
+    against the oracle's forward and gradients."""
+    inp = make_inputs(4, 333, 16, 128, 128, seed=4714, s0_std=0.05, grads=True)
+    d = to_dev(inp)
+    assert gdn2.sweeps_fused(4, 333, 16, 128, 128)
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    o, sf, states, dstates, dS0 = gdn2.sweeps(factors, d["v"], d["w"], 128, d["S0"], d["dO"], d["dS_final"])
+    g = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates, factors)
+    g["dS0"] = dS0
+    torch.cuda.synchronize()
+    o_ref, sf_ref = oracle.fwd(*oracle_args(inp))
+    assert rel_err(o, o_ref) < TOL["bf16"] and rel_err(sf, sf_ref) < TOL["bf16"]
+    ref = oracle.bwd(*oracle_args(inp), inp["dO"], inp["dS_final"])
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e < 5e-3}
+    assert not bad, bad
