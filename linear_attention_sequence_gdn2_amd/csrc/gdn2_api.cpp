@@ -212,6 +212,27 @@ gdn2::BwdArgs bwd_args(const gdn2_shape *shape) {
     return a;
 }
 
+// Sweep arguments from a factor buffer of gdn2_chunk_bwd_factors: its chunk operand records
+// follow the adjoint factors of every chunk.
+gdn2::FwdArgs factored_args(const gdn2_shape *shape, const void *factors, const void *v, const void *w,
+                            const float *S0, float *o, float *S_final, float *states) {
+    int vt;
+    gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, o, S_final, states, &vt);
+    const long items = (long)shape->B * shape->H * nchunks(shape);
+    f.records = reinterpret_cast<const char *>(factors) +
+                (gdn2::factor_buffer_bytes(items, shape->dk) - gdn2::record_buffer_bytes(items, shape->dk));
+    return f;
+}
+
+// Reverse-sweep arguments: the factor buffer, dO, dS_final and the outputs dS' of every chunk, dS0
+gdn2::BwdArgs reverse_args(const gdn2_shape *shape, const void *factors, const float *dO, const float *dS_final,
+                           float *dstates, float *dS0) {
+    gdn2::BwdArgs a = bwd_args(shape);
+    a.factors = const_cast<void *>(factors);
+    a.dO = dO; a.dS_final = dS_final; a.dstates = dstates; a.dS0 = dS0;
+    return a;
+}
+
 bool all_aligned(std::initializer_list<const void *> ptrs) {
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return false;
@@ -271,13 +292,8 @@ int gdn2_chunk_fwd_factored(const gdn2_shape *shape, const void *factors, const 
     if (!factors || !v || !w || (!o && !states)) return GDN2_ERR_INVALID_ARG;
     if (!all_aligned({factors, v, S0, o, S_final, states}) || !gates_aligned(shape, nullptr, nullptr, w))
         return GDN2_ERR_INVALID_ARG;
-    int vt;
-    gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, o, S_final, states, &vt);
-    {
-        const long items = (long)shape->B * shape->H * nchunks(shape);
-        f.records = reinterpret_cast<const char *>(factors) + (gdn2::factor_buffer_bytes(items, shape->dk) -
-                                                               gdn2::record_buffer_bytes(items, shape->dk));
-    }
+    const gdn2::FwdArgs f = factored_args(shape, factors, v, w, S0, o, S_final, states);
+    const int vt = shape->dv / f.nvt;
     const gdn2::FwdMode mode = !o ? gdn2::kFwdStates : states ? gdn2::kFwdOutStates : gdn2::kFwdOut;
     return launch_status(gdn2::launch_fwd_sweep(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
                                                 gate_scalar(shape), mode, reinterpret_cast<hipStream_t>(stream)));
@@ -289,10 +305,8 @@ int gdn2_chunk_bwd_reverse(const gdn2_shape *shape, const void *factors, const f
     if (st != GDN2_OK) return st;
     if (!factors || !dO || !dstates) return GDN2_ERR_INVALID_ARG;
     if (!all_aligned({factors, dO, dS_final, dstates, dS0})) return GDN2_ERR_INVALID_ARG;
-    gdn2::BwdArgs a = bwd_args(shape);
-    a.factors = const_cast<void *>(factors);
-    a.dO = dO; a.dS_final = dS_final; a.dstates = dstates; a.dS0 = dS0;
-    return launch_status(gdn2::launch_bwd_reverse(a, shape->dk, reinterpret_cast<hipStream_t>(stream)));
+    return launch_status(gdn2::launch_bwd_reverse(reverse_args(shape, factors, dO, dS_final, dstates, dS0), shape->dk,
+                                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
 int gdn2_chunk_sweeps_fused(const gdn2_shape *shape) {
@@ -315,15 +329,9 @@ int gdn2_chunk_sweeps(const gdn2_shape *shape, const void *factors, const void *
         if (rc != GDN2_OK) return rc;
         return gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     }
-    int vt;
-    gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, o, S_final, states, &vt);
-    const long items = (long)shape->B * shape->H * nchunks(shape);
-    f.records = reinterpret_cast<const char *>(factors) +
-                (gdn2::factor_buffer_bytes(items, shape->dk) - gdn2::record_buffer_bytes(items, shape->dk));
-    gdn2::BwdArgs a = bwd_args(shape);
-    a.factors = const_cast<void *>(factors);
-    a.dO = dO; a.dS_final = dS_final; a.dstates = dstates; a.dS0 = dS0;
-    return launch_status(gdn2::launch_fwd_rev_sweeps(f, a, shape->dk, gate_logits(shape), gate_scalar(shape),
+    return launch_status(gdn2::launch_fwd_rev_sweeps(factored_args(shape, factors, v, w, S0, o, S_final, states),
+                                                     reverse_args(shape, factors, dO, dS_final, dstates, dS0),
+                                                     shape->dk, gate_logits(shape), gate_scalar(shape),
                                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -367,44 +375,32 @@ int gdn2_chunk_bwd(const gdn2_shape *shape, const void *q, const void *k, const 
     float *states = reinterpret_cast<float *>(workspace);
     float *dstates = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + sbytes);
     void *factors = reinterpret_cast<char *>(workspace) + 2 * sbytes;
-    // the key-side chunk operands once, then the state sweep from them
+    // the key-side chunk operands once; then the state before every chunk and dS' of every chunk
     int rc = gdn2_chunk_bwd_factors(shape, q, k, log_alpha, b, factors, stream);
     if (rc != GDN2_OK) return rc;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     int seg_len;
     const int nseg = fwd_segments(shape, &seg_len);
     if (nseg > 1) {
-        // few heads, long sequence: the state sweep in segments side by side (as the forward's)
-        int vt;
-        gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, nullptr, nullptr, states, &vt);
-        const long items = (long)shape->B * shape->H * nchunks(shape);
-        const size_t fbytes = gdn2_chunk_factors_bytes(shape);
-        f.records = reinterpret_cast<const char *>(factors) + (fbytes - gdn2::record_buffer_bytes(items, shape->dk));
+        // few heads, long sequence: the state sweep in segments side by side (as the forward's),
+        // the segment blocks after the factors
+        gdn2::FwdArgs f = factored_args(shape, factors, v, w, S0, nullptr, nullptr, states);
         f.nseg = nseg;
         f.seg_len = seg_len;
-        float *E = reinterpret_cast<float *>(reinterpret_cast<char *>(factors) + fbytes);
+        float *E = reinterpret_cast<float *>(reinterpret_cast<char *>(factors) + gdn2_chunk_factors_bytes(shape));
         float *Sin = E + (size_t)shape->B * shape->H * nseg * shape->dk * (shape->dv + shape->dk);
-        rc = launch_status(gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E, Sin,
-                                                     reinterpret_cast<hipStream_t>(stream)));
+        rc = launch_status(gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E, Sin, hs));
+        if (rc == GDN2_OK) rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     } else if (gdn2_chunk_sweeps_fused(shape) == 1) {
         // few heads: the state sweep and the reverse sweep side by side in one launch
-        int vt;
-        gdn2::FwdArgs f = fwd_args(shape, nullptr, nullptr, v, nullptr, nullptr, w, S0, nullptr, nullptr, states, &vt);
-        const long items = (long)shape->B * shape->H * nchunks(shape);
-        f.records = reinterpret_cast<const char *>(factors) +
-                    (gdn2_chunk_factors_bytes(shape) - gdn2::record_buffer_bytes(items, shape->dk));
-        gdn2::BwdArgs r = bwd_args(shape);
-        r.factors = factors;
-        r.dO = dO; r.dS_final = dS_final; r.dstates = dstates; r.dS0 = dS0;
-        rc = launch_status(gdn2::launch_fwd_rev_sweeps(f, r, shape->dk, gate_logits(shape), gate_scalar(shape),
-                                                       reinterpret_cast<hipStream_t>(stream)));
-        if (rc != GDN2_OK) return rc;
-        return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, factors, dq, dk, dv,
-                                    dlog_alpha, db, dw, stream);
+        rc = launch_status(gdn2::launch_fwd_rev_sweeps(
+            factored_args(shape, factors, v, w, S0, nullptr, nullptr, states),
+            reverse_args(shape, factors, dO, dS_final, dstates, dS0), shape->dk, gate_logits(shape),
+            gate_scalar(shape), hs));
     } else {
         rc = gdn2_chunk_fwd_factored(shape, factors, v, w, S0, nullptr, nullptr, states, stream);
+        if (rc == GDN2_OK) rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     }
-    if (rc != GDN2_OK) return rc;
-    rc = gdn2_chunk_bwd_reverse(shape, factors, dO, dS_final, dstates, dS0, stream);
     if (rc != GDN2_OK) return rc;
     return gdn2_chunk_bwd_grads(shape, q, k, v, log_alpha, b, w, dO, states, dstates, factors, dq, dk, dv,
                                 dlog_alpha, db, dw, stream);
