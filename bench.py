@@ -69,9 +69,13 @@ BWD_GRADS_BYTES_PER_TOKHEAD = 9480
 
 
 def _kernel_sources_digest():
+    """Digest of the device code (the .hip sources and the headers they include); the host-side
+    C-ABI file does not change what a kernel reads or writes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_sequence_gdn2_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
