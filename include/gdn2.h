@@ -38,7 +38,8 @@
  * - Any T >= 1 is accepted; a ragged tail chunk is padded internally with
  *   identity tokens (k = 0, log_alpha = 0) that leave the state unchanged.
  * - Supported sizes: B, H >= 1, T >= 1, chunk == 64, dk and dv in {32, 64, 128},
- *   B*T*H*max(dk,dv) < 2^31.
+ *   B*T*H*max(dk,dv) < 2^31 and H*max(dk,dv) < 2^24 (64 tokens of one fp32
+ *   tensor span less than 4 GiB); GDN2_ERR_UNSUPPORTED otherwise.
  * - Numerical range: within one 64-token chunk the cumulative log-decay of a
  *   key channel must stay above -80 (the factorised decay exp(-G) is formed in
  *   fp32).  Outside that range results are undefined (non-finite values).

@@ -38,6 +38,9 @@ int check_shape(const gdn2_shape *s) {
     const int dmax = s->dk > s->dv ? s->dk : s->dv;
     const unsigned long long n = (unsigned long long)s->B * s->T * s->H * dmax;
     if (n >= (1ull << 31)) return GDN2_ERR_UNSUPPORTED;
+    // the kernels address a chunk's rows of a token tensor by 32-bit byte offsets from the
+    // chunk's first row: 64 tokens of H * dmax fp32 values must span less than 4 GiB
+    if ((unsigned long long)s->H * dmax >= (1ull << 24)) return GDN2_ERR_UNSUPPORTED;
     // grid size (workgroups) must fit in 32 bits; chunk-state workspace indexing uses size_t
     if ((unsigned long long)s->B * s->H * s->dv / 16 >= (1ull << 31)) return GDN2_ERR_UNSUPPORTED;
     return GDN2_OK;

@@ -67,12 +67,17 @@ def test_workspace_and_state_sizes():
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 2 * 3 * nc * record   # forward-only records
     bad = _shape(dk=96)
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+    # the widest rows accepted: H * max(dk, dv) just under 2^24
+    wide = _shape(B=1, T=64, H=(1 << 17) - 1, dk=128, dv=128)
+    assert lib.gdn2_chunk_states_bytes(ctypes.byref(wide)) == ((1 << 17) - 1) * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(H=-1), INVALID),
     (dict(chunk=32), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED), (dict(B=1 << 14, T=1 << 14, H=16), UNSUPPORTED),
+    (dict(B=1, T=64, H=1 << 17, dk=128, dv=128), UNSUPPORTED),   # 64 rows of H*d fp32 span 4 GiB
+    (dict(B=1, T=64, H=1 << 18, dk=64, dv=32), UNSUPPORTED),
     (dict(gates=2), UNSUPPORTED), (dict(gates=1, dt=0), UNSUPPORTED),
     (dict(scalar=8), UNSUPPORTED), (dict(scalar=1, dt=0), UNSUPPORTED), (dict(scalar=6, gates=1), UNSUPPORTED),
 ])
