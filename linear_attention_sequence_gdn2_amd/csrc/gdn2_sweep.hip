@@ -10,7 +10,16 @@
 // keeps them in the chunk operand records; what is left for this sequential sweep are
 // the products with the state, which cannot run ahead of the previous chunk.
 //
-// Work decomposition as in the fused forward (gdn2_fwd.hip): one workgroup of 4 waves
+// Kernels here:
+//   fwd_sweep_kernel      4 waves per (batch, head, value tile of 16/32/64 columns), two per CU
+//                         (fp32 q/k/v, dk = 32, dv not a multiple of 64, states-only with few heads)
+//   fwd_sweep64_kernel    8 waves per 64-column tile, one per CU (body fwd_sweep64_body); its SEG
+//                         modes are the passes of the segmented sweep
+//   seg_combine_kernel    the segments' start states from their affine maps
+//   fwd_rev_sweep_kernel  the wide forward sweep and the reverse sweep (gdn2_rsweep.h) side by
+//                         side in one launch
+//
+// fwd_sweep_kernel: work decomposition as in the fused forward (gdn2_fwd.hip): one workgroup of 4 waves
 // per (batch, head, value tile of VT columns), wave w owning tokens 16w..16w+15 for the
 // rows of X, U and O and NTS tiles of the state; the fp32 state stays in registers (D
 // layout) with a split-bf16 copy in LDS as the next chunk's operand.  Per chunk the
