@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             for (int j = 0; j < NKS; ++j) {
                 const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
                 const Split8 sf = frag_tr<PS>(S1, S1 + DK * PS, 32 * j, 16 * n, r, g);
-                if (FAST) acc = mfma32(ef.hi, sf.hi, acc);
+                if (FAST) acc = mfma32(ef.hi, sf.lo, mfma32(ef.hi, sf.hi, acc));   // Et (hi part) times S
                 else acc = mfma32x3(ef, sf, acc);
             }
             const Split4 sx = split4(-acc);    // lane holds X[16w + 4g + i][16n + r]

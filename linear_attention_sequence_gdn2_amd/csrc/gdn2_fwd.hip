@@ -36,7 +36,7 @@ namespace gdn2 {
 // above this point (bounds the live registers so two workgroups fit on a CU).
 #define GDN2_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <int DK, int VT, bool BF16, bool FAST, bool OUT, bool STATES, bool GL, bool SG>
+template <int DK, int VT, bool BF16, bool OUT, bool STATES, bool GL, bool SG>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     constexpr int NKS = DK / 32;           // 32-channel contraction steps
     constexpr int NVT = VT / 16;           // 16-column value tiles
@@ -276,8 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
                 for (int j = 0; j < NKS; ++j) {
                     const Split8 kt = frag_8(&sK[(16 * mt + r) * PK + 32 * j + 8 * g],
                                              &sK[RK + (16 * mt + r) * PK + 32 * j + 8 * g]);
-                    if (FAST) accA = mfma32(kt.hi, Et[j].hi, accA);
-                    else accA = mfma32x3(kt, Et[j], accA);
+                    accA = mfma32x3(kt, Et[j], accA);
                     if (OUT) accP = mfma32x3(kt, Qt[j], accP);
                 }
                 // lane holds A[16w + r][16mt + 4g + i] and P[16w + r][16mt + 4g + i]
@@ -319,8 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
             for (int j = 0; j < NKS; ++j) {
                 const Split8 sf = frag_8(&sS[(16 * n + r) * PK + 32 * j + 8 * g],
                                          &sS[VT * PK + (16 * n + r) * PK + 32 * j + 8 * g]);
-                if (FAST) accX = mfma32(Et[j].hi, sf.hi, accX);
-                else accX = mfma32x3(Et[j], sf, accX);
+                accX = mfma32x3(Et[j], sf, accX);
                 if (OUT) accQ = mfma32x3(Qt[j], sf, accQ);
             }
             const Split4 xs = split4(-accX);  // lane holds X[16w + 4g + i][16n + r]
@@ -432,7 +430,7 @@ template <int DK, int VT, bool BF16, bool GL, bool SG, int MODE>
 static hipError_t launch_t(const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * a.nvt)), block(kThreads);
     constexpr bool OUT = MODE != kFwdStates, STATES = MODE != kFwdOut;
-    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, BF16, OUT, STATES, GL, SG>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<DK, VT, BF16, OUT, STATES, GL, SG>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 

@@ -50,7 +50,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
     constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4;
     constexpr int RK = kChunk * PK;
-    constexpr bool FAST = BF16;
     using Rec = ChunkRecord<DK>;
     // LDS (bytes): Kt, Et, Qt rows [token][channel] (hi, lo); the decay totals after the
     // Et rows; W^T [channel][token] (hi, lo) later over the Et rows and the totals;
@@ -209,8 +208,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
             for (int j = 0; j < NKS; ++j) {
                 const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g);
                 const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
-                if (FAST) acc = mfma32(kf.hi, ef.hi, acc);
-                else acc = mfma32x3(kf, ef, acc);
+                acc = mfma32x3(kf, ef, acc);
             }
             // lane holds A[16w + r][16mt + 4g + i]
 #pragma unroll

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
     constexpr int NMT = DK / 16;           // 16-row key tiles of S
     constexpr int NTS = NMT * NVT / 4;     // S tiles per wave
     static_assert((NMT * NVT) % 4 == 0, "S tiles must split over 4 waves");
-    constexpr bool FAST = BF16;            // X = Z - Et S with the hi part of Et only
+    constexpr bool FAST = BF16;            // X = Z - Et S with the hi part of Et (and all of S)
     constexpr int PK = DK + 8;             // row pitch of [row][channel] bf16 tiles
     constexpr int PT = kChunk + 8;         // row pitch of [col][token] bf16 tiles
     constexpr int RK = kChunk * PK;        // one [token][channel] plane
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
             for (int j = 0; j < NKS; ++j) {
                 const Split8 sf = frag_8(&sS[(16 * n + r) * PK + 32 * j + 8 * g],
                                          &sS[VT * PK + (16 * n + r) * PK + 32 * j + 8 * g]);
-                if (FAST) accX = mfma32(Et[j].hi, sf.hi, accX);
+                if (FAST) accX = mfma32(Et[j].hi, sf.lo, mfma32(Et[j].hi, sf.hi, accX));
                 else accX = mfma32x3(Et[j], sf, accX);
                 if (OUT) accQ = mfma32x3(Qt[j], sf, accQ);
             }
@@ -499,7 +499,8 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
             for (int j = 0; j < NKS; ++j) {
                 const Split8 sf = frag_8(&sS[(16 * cb + r) * PK + 32 * j + 8 * g],
                                          &sS[VT * PK + (16 * cb + r) * PK + 32 * j + 8 * g]);
-                accX = mfma32(*reinterpret_cast<const bf16x8 *>(&sE[(16 * w + r) * PK + 32 * j + 8 * g]), sf.hi, accX);
+                const bf16x8 eh = *reinterpret_cast<const bf16x8 *>(&sE[(16 * w + r) * PK + 32 * j + 8 * g]);
+                accX = mfma32(eh, sf.lo, mfma32(eh, sf.hi, accX));   // Et (hi part) times S (hi and lo)
                 if (OUT)
                     accQ = mfma32x3(frag_8(&sQ[(16 * w + r) * PK + 32 * j + 8 * g],
                                            &sQ[RK + (16 * w + r) * PK + 32 * j + 8 * g]), sf, accQ);
