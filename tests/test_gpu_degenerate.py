@@ -14,7 +14,10 @@ Read-after-write: with b = 1 and a unit-norm key, S_t^T k_t = z_t whatever S_{t-
 decay were (the erase removes exactly what the key reads).  Taking q = k makes every output
 o_t = w_t * v_t.  One-hot keys are unit-norm exactly in bf16, so this holds for the bf16 path
 up to its arithmetic; it is checked at the configurations' full sizes on every forward path
-(forward-only records and wide sweep, the segmented sweep, the fused fp32 sweep)."""
+(forward-only records and wide sweep, the segmented sweep, the fused fp32 sweep).  Each output
+then depends on its own token's v and w only, so with dS_final = 0 the backward must give
+dv = dO * w and dw = dO * v exactly: checked at full size on the one-call backward (segmented
+and one-launch state sweeps) and the staged training step."""
 import pytest
 import torch
 
@@ -92,3 +95,30 @@ def test_read_after_write_identity_at_full_size(name, B):
     err = float((o - z).abs().max()) / float(z.abs().max())
     print("%s: max |o - w v| / max |w v| = %.2e" % (name, err))
     assert err < FWD_TOL[wl.qkv_dtype], err
+
+
+@pytest.mark.parametrize("name,staged", [
+    ("fwdbwd_bf16_B4H16T4096d128", False),   # one-call backward (state and reverse sweeps in one launch)
+    ("fwd_bf16_B8H16T2048d128", True),       # the staged training step of the bench
+    ("long_bf16_B1H16T16384d128", False),    # one-call backward with the segmented state sweep
+])
+def test_read_after_write_gradients_at_full_size(name, staged):
+    """With b = 1 and q = k one-hot, o_t = w_t * v_t depends on no other token, so for
+    L = sum(dO * o) (dS_final = 0): dv = dO * w and dw = dO * v exactly."""
+    wl = WORKLOADS[name]
+    x = _read_after_write(make_workload(wl, grads=True), seed=8300)
+    d = to_dev(x)
+    if staged:
+        factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+        _, _, states, dstates, _ = gdn2.sweeps(factors, d["v"], d["w"], wl.dk, d["S0"], d["dO"], None)
+        g = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates,
+                           factors)
+    else:
+        g = gdn2.bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], d["dO"], None)
+    dv_ref = d["dO"] * d["w"]
+    dw_ref = d["dO"] * d["v"].float()
+    torch.cuda.synchronize()
+    ev = float((g["dv"] - dv_ref).abs().max()) / float(dv_ref.abs().max())
+    ew = float((g["dw"] - dw_ref).abs().max()) / float(dw_ref.abs().max())
+    print("%s: dv %.2e dw %.2e" % (name, ev, ew))
+    assert ev < 5e-3 and ew < 5e-3, (ev, ew)
