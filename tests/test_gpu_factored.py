@@ -195,3 +195,30 @@ def test_training_chain_through_fused_sweeps():
     print(" ".join("%s=%.2e" % kv for kv in errs.items()))
     bad = {n: e for n, e in errs.items() if not e < 5e-3}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("with_s0,with_dsf,want_state,want_dS0", [
+    (False, False, False, False),
+    (True, False, True, False),
+    (False, True, False, True),
+])
+def test_sweeps_entry_optional_arguments(with_s0, with_dsf, want_state, want_dS0):
+    """The one launch with S0 / dS_final absent (zeros) and S_final / dS0 not wanted."""
+    B, T, H, dk, dv = 2, 140, 8, 128, 128
+    inp = make_inputs(B, T, H, dk, dv, seed=4715, s0_std=0.1, grads=True)
+    d = to_dev(inp)
+    assert gdn2.sweeps_fused(B, T, H, dk, dv)
+    S0 = d["S0"] if with_s0 else None
+    dsf = d["dS_final"] if with_dsf else None
+    factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
+    o, sf, st, dst, dS0 = gdn2.sweeps(factors, d["v"], d["w"], dk, S0, d["dO"], dsf, want_state=want_state,
+                                      want_dS0=want_dS0)
+    o2, sf2, st2 = gdn2.fwd_factored(factors, d["v"], d["w"], dk, S0)
+    dst2, dS02 = gdn2.bwd_reverse(factors, d["dO"], dk, dsf)
+    torch.cuda.synchronize()
+    assert (sf is None) != want_state and (dS0 is None) != want_dS0
+    assert torch.equal(o, o2) and torch.equal(st, st2) and torch.equal(dst, dst2)
+    if want_state:
+        assert torch.equal(sf, sf2)
+    if want_dS0:
+        assert torch.equal(dS0, dS02)
