@@ -157,6 +157,8 @@ def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
 # same bodies run as in the two separate entry points, so the results are the same bit for bit.
 @pytest.mark.parametrize("B,T,H,dk,dv,extra,one", [
     (4, 130, 16, 128, 128, {"s0_std": 0.1}, True),      # 256 workgroups: one launch
+    (2, 1, 8, 128, 128, {"s0_std": 0.1}, True),         # T = 1
+    (1, 64, 4, 64, 64, {"s0_std": 0.1}, True),          # exactly one chunk, dk = dv = 64
     (2, 200, 8, 64, 128, {}, True),                      # dk = 64
     (1, 64 * 20 + 3, 2, 128, 64, {"s0_std": 0.2}, True),
     (2, 150, 4, 128, 128, {"gate_logits": True}, True),
