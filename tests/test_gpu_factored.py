@@ -148,8 +148,26 @@ def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
     o_f, sf_f, _ = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_states=False)
     o_i, sf_i = gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
     torch.cuda.synchronize()
-    assert torch.equal(states, st2)
+    if B * H * (dv // 64) >= 256:
+        assert torch.equal(states, st2)
+    else:   # the states-only sweep takes the four-wave kernel below full occupancy
+        assert float((states - st2).abs().max()) <= 1e-3 * float(st2.abs().max())
     assert torch.equal(o_i, o_f) and torch.equal(sf_i, sf_f)
+
+
+# With at most half the CUs given a 64-column tile (B*H*dv/64 <= 128), the eight-wave sweep takes
+# 32-column tiles: ragged T, both key widths, every gate format, against the oracle (outputs and
+# every chunk state) and the inference forward against the factored one bit for bit.
+@pytest.mark.parametrize("B,T,H,dk,dv,extra", [
+    (4, 150, 16, 128, 128, {"s0_std": 0.2}),
+    (2, 65, 16, 64, 128, {}),
+    (1, 64, 8, 128, 64, {"s0_std": 0.1}),
+    (4, 150, 16, 128, 128, {"gate_logits": True}),
+    (4, 150, 16, 128, 128, {"gates": "gdn", "token_gates": True}),
+])
+def test_factored_forward_32_column_tiles(B, T, H, dk, dv, extra):
+    assert 2 * B * H * (dv // 64) <= 256
+    test_factored_forward_wide_tiles(B, T, H, dk, dv, extra)
 
 
 # gdn2_chunk_sweeps: both sweeps of the training step from one factor buffer; one launch where
