@@ -643,20 +643,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
 // The training step's two sweeps in one launch: the forward sweep (the state before every chunk,
 // and o and S_final when OUT) and the reverse sweep (dS' of every chunk, dS0), both from one factor
 // buffer.  Neither reads what the other writes, and with few heads each alone leaves CUs idle.
-// The first nfwd workgroups (in the swizzled order) sweep forward with 64-column tiles, the
-// others backward with 64-column tiles; the reverse role keeps its dS' and dO buffers in the
-// forward role's arrays.
-template <int DK, bool OUT, bool GL, bool SG>
+// The first nfwd workgroups (in the swizzled order) sweep forward, the others backward, both on
+// VT-column tiles (64, or 32 when even those leave every workgroup a CU of its own); the reverse
+// role keeps its dS' and dO buffers in the forward role's arrays.
+template <int DK, bool OUT, bool GL, bool SG, int VT>
 __global__ __launch_bounds__(kChunkThreads, 1) void fwd_rev_sweep_kernel(FwdArgs fa, BwdArgs ba, int nfwd) {
-    using Lds = Sweep64Lds<DK, OUT>;
-    using RL = RevLds<DK, 64>;
+    using Lds = Sweep64Lds<DK, OUT, VT>;
+    using RL = RevLds<DK, VT>;
     static_assert(RL::D <= Lds::K && RL::D <= Lds::S && RL::O <= Lds::X && RL::O <= Lds::U,
                   "the reverse role's buffers fit the forward role's arrays");
-    static_assert(ReverseCfg<DK, 64>::NTH == kChunkThreads, "both roles take the whole workgroup");
+    static_assert(ReverseCfg<DK, VT>::NTH == kChunkThreads, "both roles take the whole workgroup");
     __shared__ __align__(16) __bf16 sK[Lds::K], sE[Lds::E], sQ[Lds::Q], sS[Lds::S], sX[Lds::X], sU[Lds::U];
     const int L = xcd_swizzle(blockIdx.x, gridDim.x);
-    if (L < nfwd) fwd_sweep64_body<DK, OUT, true, GL, SG, 0>(fa, L, sK, sE, sQ, sS, sX, sU);
-    else bwd_reverse_body<DK, 64>(ba, L - nfwd, sK, sS, sX, sU);
+    if (L < nfwd) fwd_sweep64_body<DK, OUT, true, GL, SG, 0, VT>(fa, L, sK, sE, sQ, sS, sX, sU);
+    else bwd_reverse_body<DK, VT>(ba, L - nfwd, sK, sS, sX, sU);
 }
 
 // ---------------------------------------------------------------------------
@@ -864,16 +864,26 @@ hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool
     return bf16 ? sweep_mode<true, false, false>(a, dk, vt, mode, st) : sweep_mode<false, false, false>(a, dk, vt, mode, st);
 }
 
-template <int DK, bool GL, bool SG>
-static hipError_t fwd_rev_t(const FwdArgs &fa, const BwdArgs &ba, hipStream_t st) {
+template <int DK, bool GL, bool SG, int VT>
+static hipError_t fwd_rev_vt(const FwdArgs &fa_in, const BwdArgs &ba, hipStream_t st) {
+    FwdArgs fa = fa_in;
+    fa.nvt = fa.dv / VT;
     const int nfwd = fa.B * fa.H * fa.nvt;
     if (fa.o)
-        hipLaunchKernelGGL((fwd_rev_sweep_kernel<DK, true, GL, SG>), dim3((unsigned)(2 * nfwd)), dim3(kChunkThreads), 0,
-                           st, fa, ba, nfwd);
-    else
-        hipLaunchKernelGGL((fwd_rev_sweep_kernel<DK, false, GL, SG>), dim3((unsigned)(2 * nfwd)), dim3(kChunkThreads),
+        hipLaunchKernelGGL((fwd_rev_sweep_kernel<DK, true, GL, SG, VT>), dim3((unsigned)(2 * nfwd)), dim3(kChunkThreads),
                            0, st, fa, ba, nfwd);
+    else
+        hipLaunchKernelGGL((fwd_rev_sweep_kernel<DK, false, GL, SG, VT>), dim3((unsigned)(2 * nfwd)),
+                           dim3(kChunkThreads), 0, st, fa, ba, nfwd);
     return hipGetLastError();
+}
+
+// 32-column tiles for both roles where they still give every workgroup a CU of its own (the
+// chunk steps of both sweeps are shorter at 32 columns), else 64
+template <int DK, bool GL, bool SG>
+static hipError_t fwd_rev_t(const FwdArgs &fa, const BwdArgs &ba, hipStream_t st) {
+    if (4L * fa.B * fa.H * (fa.dv / 64) <= cu_count()) return fwd_rev_vt<DK, GL, SG, 32>(fa, ba, st);
+    return fwd_rev_vt<DK, GL, SG, 64>(fa, ba, st);
 }
 
 bool fwd_rev_fused(int B, int H, int dk, int dv, bool bf16) {
@@ -884,8 +894,7 @@ hipError_t launch_fwd_rev_sweeps(const FwdArgs &fa_in, const BwdArgs &ba, int dk
     if (gl && sg) return hipErrorInvalidValue;
     if (!fwd_rev_fused(fa_in.B, fa_in.H, dk, fa_in.dv, true) || !fa_in.states || !ba.dstates)
         return hipErrorInvalidValue;
-    FwdArgs fa = fa_in;
-    fa.nvt = fa.dv / 64;
+    const FwdArgs &fa = fa_in;
     if (dk == 128) return gl ? fwd_rev_t<128, true, false>(fa, ba, st) : sg ? fwd_rev_t<128, false, true>(fa, ba, st)
                                                                            : fwd_rev_t<128, false, false>(fa, ba, st);
     return gl ? fwd_rev_t<64, true, false>(fa, ba, st) : sg ? fwd_rev_t<64, false, true>(fa, ba, st)
