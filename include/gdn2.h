@@ -40,9 +40,15 @@
  * - Supported sizes: B, H >= 1, T >= 1, chunk == 64, dk and dv in {32, 64, 128},
  *   B*T*H*max(dk,dv) < 2^31 and H*max(dk,dv) < 2^24 (64 tokens of one fp32
  *   tensor span less than 4 GiB); GDN2_ERR_UNSUPPORTED otherwise.
- * - Numerical range: within one 64-token chunk the cumulative log-decay of a
- *   key channel must stay above -80 (the factorised decay exp(-G) is formed in
- *   fp32).  Outside that range results are undefined (non-finite values).
+ * - Decay range: any log_alpha <= 0 is accepted, -inf (alpha = 0) included; the
+ *   blog puts no floor under alpha.  The chunk form factors the decay between two
+ *   tokens of a chunk as exp(G_i) exp(-G_j); on a chunk in which some key channel
+ *   decays by more than about exp(-64) that factor would leave fp32 range, so such
+ *   chunks are found on the device and their intra-chunk products are recomputed
+ *   with the pairwise decay exp(G_i - G_j) itself (a second, exact pass over the
+ *   flagged chunks only; results stay within the stated tolerances).  A per-token
+ *   log_alpha below -30 is computed as -30: the difference, a factor below 1e-13 on
+ *   what the state held, is beneath fp32 resolution.  NaN inputs propagate.
  * - Execution is asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream).  Results are valid once the stream has reached the call.
  * - Errors: arguments are checked on the host before any launch; on failure
@@ -102,19 +108,19 @@ typedef struct {
 } gdn2_shape;
 
 /* Bytes of device workspace gdn2_chunk_fwd needs; (size_t)-1 if the shape is invalid.
- * 0 when the forward runs as one fused sweep.  With bf16 q/k/v, dk in {64, 128} and
- * dv a multiple of 64 it first writes forward-only chunk records (the key-side
- * operands of every chunk, about 2.8 KB per token-head at dk = 128) and then sweeps
- * over them; the workspace holds those records.  With so few heads that the sweep
- * would keep at most one CU in four busy and 64 chunks or more, the sequence is also
- * split into segments swept side by side; every segment's state map and start state
- * (dk * (2 dv + dk) fp32 per batch, head and segment) follow the records. */
+ * The forward first writes forward-only chunk records (the key-side operands of every
+ * chunk, about 2.8 KB per token-head at dk = 128, and one strong-decay flag per chunk)
+ * and then sweeps over them; the workspace holds those records.  With bf16 q/k/v,
+ * dk in {64, 128}, dv a multiple of 64, so few heads that the sweep would keep at most
+ * one CU in four busy and 64 chunks or more, the sequence is also split into segments
+ * swept side by side; every segment's state map and start state (dk * (2 dv + dk) fp32
+ * per batch, head and segment) follow the records. */
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape);
 
 /* Forward pass: o [B,T,H,dv] and the final state S_final [B,H,dk,dv].
  * S0 == NULL means a zero start state; S_final == NULL means it is not wanted.
- * workspace may be NULL when gdn2_chunk_fwd_workspace_size() is 0; otherwise it must
- * hold that many bytes (GDN2_ERR_WORKSPACE if not) and is overwritten. */
+ * The workspace must hold gdn2_chunk_fwd_workspace_size() bytes (GDN2_ERR_WORKSPACE if
+ * not, or if NULL) and is overwritten. */
 int gdn2_chunk_fwd(const gdn2_shape *shape,
                    const void *q, const void *k, const void *v,
                    const void *log_alpha, const void *b, const void *w,
@@ -145,15 +151,13 @@ int gdn2_chunk_bwd(const gdn2_shape *shape,
                    float *dS0,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* ---- staged form (training): each call below is exactly one kernel launch ----
+/* ---- staged form (training): each call below is one or two kernel launches ----
  *
  * gdn2_chunk_bwd == gdn2_chunk_bwd_factors + gdn2_chunk_fwd_factored (states only)
  *                   + gdn2_chunk_bwd_reverse + gdn2_chunk_bwd_grads.
  * A training step runs gdn2_chunk_bwd_factors, then gdn2_chunk_fwd_factored (o and the
  * chunk states), and after the loss gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads,
  * all on the one factor buffer; the key-side work of every chunk is done once.
- * gdn2_chunk_fwd_states and gdn2_chunk_states are the same sweeps without a factor
- * buffer (they form the key-side operands themselves, once per value tile).
  * `states` and `dstates` are [B, H, ceil(T/64), dk, dv] fp32 device buffers of
  * gdn2_chunk_states_bytes() bytes each: states[c] is the state BEFORE chunk c
  * (tokens 64c ..), dstates[c] the loss gradient w.r.t. the state AFTER chunk c. */
@@ -161,20 +165,10 @@ int gdn2_chunk_bwd(const gdn2_shape *shape,
 /* Bytes of one chunk-state buffer; (size_t)-1 if the shape is invalid. */
 size_t gdn2_chunk_states_bytes(const gdn2_shape *shape);
 
-/* Forward pass as gdn2_chunk_fwd, additionally writing states (required). */
-int gdn2_chunk_fwd_states(const gdn2_shape *shape,
-                          const void *q, const void *k, const void *v,
-                          const void *log_alpha, const void *b, const void *w,
-                          const float *S0, float *o, float *S_final, float *states, void *stream);
-
-/* State sweep only: writes states (no output o).  q is not read. */
-int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v,
-                      const void *log_alpha, const void *b, const void *w,
-                      const float *S0, float *states, void *stream);
-
 /* Bytes of the factor buffer of gdn2_chunk_bwd_factors: per (batch, head, chunk) the
- * adjoint factors, (dk*dk + 64*dk)*4 bytes, and the chunk's key-side operands,
- * about 772*dk + 33000 bytes (rounded up to 256); (size_t)-1 if the shape is invalid. */
+ * adjoint factors, (dk*dk + 64*dk)*4 bytes, the chunk's key-side operands, about
+ * 772*dk + 33000 bytes (rounded up to 256), and a strong-decay flag (4 bytes; the flags
+ * rounded up to 256); (size_t)-1 if the shape is invalid. */
 size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
 
 /* Per-chunk adjoint factors of the reverse sweep.  Unrolling the backward of one
@@ -186,8 +180,9 @@ size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
  * (gdn2_chunk_factors_bytes() bytes, device memory owned by the caller, opaque
  * layout of split-bf16 MFMA tiles), followed by the key-side operands of every chunk
  * that the token gradients need as well (the decay-absorbed key and erase-key rows,
- * T = (I + A)^-1, P, the decay prefix), so that they are formed once.  Read by
- * gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads. */
+ * T = (I + A)^-1, P, the decay prefix) and each chunk's strong-decay flag, so that they
+ * are formed once.  Two launches: every chunk, then the exact pass over flagged chunks.
+ * Read by gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads. */
 int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k,
                            const void *log_alpha, const void *b, void *factors, void *stream);
 
@@ -195,8 +190,8 @@ int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k
  * shape and the same q, k, log_alpha and b (their key-side chunk operands are taken
  * from it; q, k, log_alpha and b are not read again).  Reads v, w and S0 (NULL =
  * zeros); writes o [B,T,H,dv] unless NULL, S_final unless NULL, and the chunk-start
- * states unless NULL; o and states cannot both be NULL.  Results as gdn2_chunk_fwd /
- * gdn2_chunk_fwd_states.  A training step runs gdn2_chunk_bwd_factors first and uses
+ * states unless NULL; o and states cannot both be NULL.  Results as gdn2_chunk_fwd, plus
+ * the state before every chunk.  A training step runs gdn2_chunk_bwd_factors first and uses
  * the one factor buffer for this forward, gdn2_chunk_bwd_reverse and
  * gdn2_chunk_bwd_grads.  shape->gate_dtype and gate_scalar describe w. */
 int gdn2_chunk_fwd_factored(const gdn2_shape *shape, const void *factors, const void *v,
@@ -229,7 +224,8 @@ int gdn2_chunk_sweeps_fused(const gdn2_shape *shape);
 
 /* Token gradients from states, dstates and the factor buffer of
  * gdn2_chunk_bwd_factors (same shape and inputs): dq, dk, dlog_alpha, db [B,T,H,dk],
- * dv, dw [B,T,H,dv]. */
+ * dv, dw [B,T,H,dv].  Two launches: every chunk, then the exact pass over the chunks the
+ * factor buffer flags (their gradients are written again). */
 int gdn2_chunk_bwd_grads(const gdn2_shape *shape,
                          const void *q, const void *k, const void *v,
                          const void *log_alpha, const void *b, const void *w,

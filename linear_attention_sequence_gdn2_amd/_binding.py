@@ -31,7 +31,7 @@ STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3:
           4: "GDN2_ERR_HIP"}
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
-           "gdn2_chunk_fwd_states", "gdn2_chunk_states", "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
+           "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
            "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step", "gdn2_output_fwd",
            "gdn2_output_bwd_workspace_size", "gdn2_output_bwd", "gdn2_chunk_fwd_factored",
            "gdn2_chunk_sweeps", "gdn2_chunk_sweeps_fused"]
@@ -72,10 +72,6 @@ def load():
         lib.gdn2_chunk_bwd_workspace_size.restype = ctypes.c_size_t
         lib.gdn2_chunk_states_bytes.argtypes = [SP]
         lib.gdn2_chunk_states_bytes.restype = ctypes.c_size_t
-        lib.gdn2_chunk_fwd_states.argtypes = [SP] + [P] * 10 + [P]
-        lib.gdn2_chunk_fwd_states.restype = ctypes.c_int
-        lib.gdn2_chunk_states.argtypes = [SP] + [P] * 7 + [P]
-        lib.gdn2_chunk_states.restype = ctypes.c_int
         lib.gdn2_chunk_factors_bytes.argtypes = [SP]
         lib.gdn2_chunk_factors_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_bwd_factors.argtypes = [SP] + [P] * 5 + [P]
@@ -197,7 +193,7 @@ def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
     ws_bytes = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(shape))
     if ws_bytes == ctypes.c_size_t(-1).value:
         raise Gdn2Error(2, "unsupported shape")
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     _check(lib.gdn2_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
                               _ptr(w), _ptr(S0), _ptr(o), _ptr(sf), _ptr(ws), ws_bytes, _stream(q.device)))
     return o, sf
@@ -237,30 +233,19 @@ def states_shape(B, T, H, dk, dv):
 
 
 def fwd_states(q, k, v, log_alpha, b, w, S0=None, want_state=True, states=None):
-    """Forward that also returns the chunk-start states [B,H,ceil(T/64),dk,dv] fp32
-    (one kernel): (o, S_final, states)."""
+    """Forward that also returns the chunk-start states [B,H,ceil(T/64),dk,dv] fp32:
+    (o, S_final, states), from a factor buffer (bwd_factors, then fwd_factored)."""
     B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (S0,))
-    lib = load()
-    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
-    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
-    sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
-    if states is None:
-        states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=q.device)
-    _check(lib.gdn2_chunk_fwd_states(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
-                                     _ptr(w), _ptr(S0), _ptr(o), _ptr(sf), _ptr(states), _stream(q.device)))
-    return o, sf, states
+    factors = bwd_factors(q, k, log_alpha, b)
+    return fwd_factored(factors, v, w, dk, S0, want_o=True, want_state=want_state, states=states)
 
 
 def chunk_states(k, v, log_alpha, b, w, S0=None, q_dtype=None, states=None):
-    """State sweep only (one kernel): chunk-start states [B,H,ceil(T/64),dk,dv]."""
+    """Chunk-start states [B,H,ceil(T/64),dk,dv] only, from a factor buffer (the states do not
+    depend on q; k stands in for it)."""
     B, T, H, dk, dv, sc = _validate(k, k, v, log_alpha, b, w, (S0,))
-    lib = load()
-    shape = make_shape(B, T, H, dk, dv, k.dtype, log_alpha.dtype, sc)
-    if states is None:
-        states = torch.empty(states_shape(B, T, H, dk, dv), dtype=torch.float32, device=k.device)
-    _check(lib.gdn2_chunk_states(ctypes.byref(shape), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                                 _ptr(S0), _ptr(states), _stream(k.device)))
-    return states
+    factors = bwd_factors(k, k, log_alpha, b)
+    return fwd_factored(factors, v, w, dk, S0, want_o=False, want_state=False, states=states)[2]
 
 
 def factors_bytes(B, T, H, dk, dv=None):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn2.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["gdn2_api.cpp", "gdn2_fwd.hip", "gdn2_bwd.hip", "gdn2_reverse.hip", "gdn2_step.hip", "gdn2_output.hip",
+SOURCES = ["gdn2_api.cpp", "gdn2_bwd.hip", "gdn2_reverse.hip", "gdn2_step.hip", "gdn2_output.hip",
            "gdn2_sweep.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -48,10 +48,11 @@ int check_shape(const gdn2_shape *s) {
 
 int nchunks(const gdn2_shape *s) { return (s->T + 63) / 64; }
 
-// The inference forward takes the record path (forward-only chunk records, then the wide
-// sweep) wherever the wide sweep applies: bf16 q/k/v, dk 64 or 128, dv a multiple of 64.
-// Otherwise one fused sweep forms the key-side operands itself.
-bool fwd_uses_records(const gdn2_shape *s) {
+// The inference forward always takes the record path: the chunk records of every chunk
+// (the fast pass of the factor kernel, then its exact pass over chunks with strong decay),
+// then a sweep over them.  The wide eight-wave sweep applies with bf16 q/k/v, dk 64 or 128
+// and dv a multiple of 64; the four-wave sweep takes every other shape.
+bool wide_sweep_shape(const gdn2_shape *s) {
     return s->qkv_dtype == GDN2_BF16 && (s->dk == 64 || s->dk == 128) && s->dv % 64 == 0;
 }
 
@@ -64,7 +65,7 @@ bool fwd_uses_records(const gdn2_shape *s) {
 // the CUs busy (B4 T8K H16) two segments are slower, 1.09 -> 1.33 ms.  1 = no segments.
 int fwd_segments(const gdn2_shape *s, int *seg_len) {
     *seg_len = nchunks(s);
-    if (!fwd_uses_records(s)) return 1;
+    if (!wide_sweep_shape(s)) return 1;
     const long wide = (long)s->B * s->H * (s->dv / 64);
     const int nc = nchunks(s), cus = gdn2::cu_count();
     if (wide * 4 > cus || nc < 64) return 1;
@@ -109,7 +110,6 @@ const char *gdn2_strerror(int status) {
 
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_shape *shape) {
     if (check_shape(shape) != GDN2_OK) return (size_t)-1;
-    if (!fwd_uses_records(shape)) return 0;
     int seg_len;
     const int nseg = fwd_segments(shape, &seg_len);
     return gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk) +
@@ -126,50 +126,37 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
     if (!gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
-    if (fwd_uses_records(shape)) {
-        // forward-only chunk records into the workspace, then the sweep from them
-        if (!workspace || workspace_bytes < gdn2_chunk_fwd_workspace_size(shape)) return GDN2_ERR_WORKSPACE;
-        gdn2::BwdArgs r{};
-        r.B = shape->B; r.T = shape->T; r.H = shape->H; r.DV = shape->dv; r.scalar = shape->gate_scalar;
-        r.q = q; r.k = k; r.la = log_alpha; r.bg = b; r.factors = workspace;
-        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-        const hipError_t e = gdn2::launch_fwd_records(r, shape->dk, true, gate_logits(shape), gate_scalar(shape), hs);
-        if (e != hipSuccess) return GDN2_ERR_HIP;
-        gdn2::FwdArgs f{};
-        f.v = v; f.wg = w; f.S0 = S0; f.o = o; f.S_final = S_final; f.states = nullptr; f.records = workspace;
-        f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv; f.scalar = shape->gate_scalar;
-        int seg_len;
-        const int nseg = fwd_segments(shape, &seg_len);
-        if (nseg > 1) {
-            // segments side by side: the maps, their composition, o
-            f.nseg = nseg;
-            f.seg_len = seg_len;
-            char *rest = reinterpret_cast<char *>(workspace) +
-                         gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk);
-            float *E = reinterpret_cast<float *>(rest);
-            float *Sin = E + (size_t)shape->B * shape->H * nseg * shape->dk * (shape->dv + shape->dk);
-            const hipError_t e3 = gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E,
-                                                            Sin, hs);
-            return e3 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
-        }
-        const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
-        f.nvt = shape->dv / vt;
-        const hipError_t e2 = gdn2::launch_fwd_sweep(f, shape->dk, vt, true, gate_logits(shape), gate_scalar(shape),
-                                                     gdn2::kFwdOut, hs);
-        return e2 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    if (!workspace || workspace_bytes < gdn2_chunk_fwd_workspace_size(shape)) return GDN2_ERR_WORKSPACE;
+    const bool bf16 = shape->qkv_dtype == GDN2_BF16;
+    // forward-only chunk records into the workspace, then the sweep from them
+    gdn2::BwdArgs r{};
+    r.B = shape->B; r.T = shape->T; r.H = shape->H; r.DV = shape->dv; r.scalar = shape->gate_scalar;
+    r.q = q; r.k = k; r.la = log_alpha; r.bg = b; r.factors = workspace;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = gdn2::launch_fwd_records(r, shape->dk, bf16, gate_logits(shape), gate_scalar(shape), hs);
+    if (e != hipSuccess) return GDN2_ERR_HIP;
+    gdn2::FwdArgs f{};
+    f.v = v; f.wg = w; f.S0 = S0; f.o = o; f.S_final = S_final; f.states = nullptr; f.records = workspace;
+    f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv; f.scalar = shape->gate_scalar;
+    int seg_len;
+    const int nseg = fwd_segments(shape, &seg_len);
+    if (nseg > 1) {
+        // segments side by side: the maps, their composition, o
+        f.nseg = nseg;
+        f.seg_len = seg_len;
+        char *rest = reinterpret_cast<char *>(workspace) +
+                     gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk);
+        float *E = reinterpret_cast<float *>(rest);
+        float *Sin = E + (size_t)shape->B * shape->H * nseg * shape->dk * (shape->dv + shape->dk);
+        const hipError_t e3 = gdn2::launch_fwd_segments(f, shape->dk, gate_logits(shape), gate_scalar(shape), E,
+                                                        Sin, hs);
+        return e3 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
     }
-
-    gdn2::FwdArgs a{};
-    a.q = q; a.k = k; a.v = v;
-    a.la = log_alpha; a.bg = b; a.wg = w;
-    a.S0 = S0; a.o = o; a.S_final = S_final; a.states = nullptr;
-    a.B = shape->B; a.T = shape->T; a.H = shape->H; a.dv = shape->dv;
     const int vt = gdn2::fwd_value_tile(shape->B, shape->H, shape->dk, shape->dv);
-    a.nvt = shape->dv / vt;
-    a.scalar = shape->gate_scalar;
-    const hipError_t e = gdn2::launch_fwd(a, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                          gate_scalar(shape), gdn2::kFwdOut, reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+    f.nvt = shape->dv / vt;
+    const hipError_t e2 = gdn2::launch_fwd_sweep(f, shape->dk, vt, bf16, gate_logits(shape), gate_scalar(shape),
+                                                 gdn2::kFwdOut, hs);
+    return e2 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
 }
 
 size_t gdn2_chunk_states_bytes(const gdn2_shape *shape) {
@@ -247,34 +234,6 @@ int launch_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HI
 }  // namespace
 
 extern "C" {
-
-int gdn2_chunk_fwd_states(const gdn2_shape *shape, const void *q, const void *k, const void *v,
-                          const void *log_alpha, const void *b, const void *w, const float *S0, float *o,
-                          float *S_final, float *states, void *stream) {
-    const int st = check_shape(shape);
-    if (st != GDN2_OK) return st;
-    if (!q || !k || !v || !log_alpha || !b || !w || !o || !states) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({q, k, v, S0, o, S_final, states}) || !gates_aligned(shape, log_alpha, b, w))
-        return GDN2_ERR_INVALID_ARG;
-    int vt;
-    const gdn2::FwdArgs f = fwd_args(shape, q, k, v, log_alpha, b, w, S0, o, S_final, states, &vt);
-    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                          gate_scalar(shape), gdn2::kFwdOutStates,
-                                          reinterpret_cast<hipStream_t>(stream)));
-}
-
-int gdn2_chunk_states(const gdn2_shape *shape, const void *k, const void *v, const void *log_alpha,
-                      const void *b, const void *w, const float *S0, float *states, void *stream) {
-    const int st = check_shape(shape);
-    if (st != GDN2_OK) return st;
-    if (!k || !v || !log_alpha || !b || !w || !states) return GDN2_ERR_INVALID_ARG;
-    if (!all_aligned({k, v, S0, states}) || !gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
-    int vt;
-    const gdn2::FwdArgs f = fwd_args(shape, nullptr, k, v, log_alpha, b, w, S0, nullptr, nullptr, states, &vt);
-    return launch_status(gdn2::launch_fwd(f, shape->dk, vt, shape->qkv_dtype == GDN2_BF16, gate_logits(shape),
-                                          gate_scalar(shape), gdn2::kFwdStates,
-                                          reinterpret_cast<hipStream_t>(stream)));
-}
 
 int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k, const void *log_alpha,
                            const void *b, void *factors, void *stream) {

@@ -6,7 +6,7 @@
 // chunkwise WY structure; the paper abstract (OpenAlex record) calls it the
 // gate-aware backward pass.
 //
-// Per chunk (start state S, end-state gradient dS', notation of gdn2_fwd.hip),
+// Per chunk (start state S, end-state gradient dS', notation of gdn2_sweep.hip),
 // the adjoint of
 //     X = Z - Et S,  U = T X,  O = Qt S + P U,  S' = diag(gamma) S + Kh^T U
 // is
@@ -17,7 +17,13 @@
 //     dKt = dA^T Et + dP^T Qt             dKh = U dS'^T          dgamma = rowsum(dS' * S)
 // followed by the element-wise chain through Et = b*k*exp(G), Qt = q*exp(G),
 // Kt = k*exp(-G), Kh = k*exp(g_C - G), Z = w*v and the reverse cumulative sum
-// of dG into dlog_alpha.
+// of dG into dlog_alpha.  The record holds Kh (decay factors at most 1); the products with
+// Kt = Kh diag(1/gamma) are formed as (dP Kh) diag(1/gamma), the channel factor applied to
+// the accumulator.  On chunks whose decay the factor kernel flagged (some gamma below
+// kGamMin, where exp(-G) leaves fp32 range) the exact pass (EX) forms the three intra-chunk
+// products with the pairwise decays instead (gdn2_exact.h):
+//     dq_i += sum_{j<=i} dP_ij k_j x_ij,   dE_i += sum_{j<i} dA_ij k_j x_ij,
+//     dk_j += sum_{i>=j} (dA_ij e_i + dP_ij q_i) x_ij,    x_ij = exp(G_i - G_j) per channel.
 //
 // Launches of the backward: the forward state sweep (gdn2_fwd.hip) stores every
 // chunk's start state; the reverse sweep (gdn2_reverse.hip) walks the chunks
@@ -30,6 +36,7 @@
 #include <type_traits>
 
 #include "gdn2_chunk.h"
+#include "gdn2_exact.h"
 #include "gdn2_kernels.h"
 
 namespace gdn2 {
@@ -41,11 +48,13 @@ namespace gdn2 {
 // both halves; for the key-side element work and the key-side gradients it owns
 // channels of its half only (hf * DK/2 .. +DK/2), in the 4-group layout; on the value
 // side it computes the 16x16 tiles (token block w, column block hf) of X, U, dU and dX
-// of each 32-column value tile.  The operand rows Kt and Et stay in LDS for the whole
+// of each 32-column value tile.  The operand rows Kh and Et stay in LDS for the whole
 // chunk, so one workgroup takes most of a CU's LDS and the two halves give every SIMD
 // two waves.
+// EX: the exact pass, persistent over the chunks the factor kernel flagged; it redoes
+// those chunks whole and writes all their gradients over the fast pass's.
 
-template <int DK, bool BF16, bool GL, bool SG>
+template <int DK, bool BF16, bool GL, bool SG, bool EX>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int VT = 32;                       // value columns per tile
@@ -56,8 +65,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     constexpr int RK = kChunk * PK;              // one [token][channel] bf16 plane
     constexpr int NSF = (DK * 8 + NTH - 1) / NTH;   // float4 of a state tile per thread
     constexpr bool FAST = BF16;
-    // LDS (byte offsets).  Whole chunk: Kt and Et rows [token][channel] (hi, lo).
-    // Value loop: S and gamma*dS' tiles as [channel][col]; dO, X then U, dU then -dX as
+    // LDS (byte offsets).  Whole chunk: Kh and Et rows [token][channel] (hi, lo); in the
+    // epilogue of the exact pass the channel slices go over them.
+    // Value loop: S and dS' tiles as [channel][col]; dO, X then U, dU then -dX as
     // [col][token]; A then T (fp32).  Preparation puts the Qt rows where the value tiles go;
     // the epilogue puts Qt rows, dP^T and dA^T ([key][query]) and scratch over the value
     // tiles and T.
@@ -71,7 +81,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     constexpr int oGam = (oTot + 4 * DK * 4 > oTs + B_TS) ? oTot + 4 * DK * 4 : oTs + B_TS;
     constexpr int oDG = oGam + DK * 4;
     constexpr int oRed = oDG + DK * 4;           // per-token gate gradients of half 1 (SG)
-    constexpr int SMEM = oRed + (SG ? 3 * kChunk * 4 : 0);
+    constexpr int oList = oRed + (SG ? 3 * kChunk * 4 : 0);   // work list of the exact pass
+    // the channel slices of the exact pass go over the Kh and Et rows where they fit (dk >= 64)
+    constexpr bool SL_OVER = kSliceFloats * 4 <= 2 * B_ROWS;
+    constexpr int oSl = SL_OVER ? oKt : oList + (NTH + 4) * 4;
+    constexpr int SMEM = oList + (EX ? (NTH + 4) * 4 + (SL_OVER ? 0 : kSliceFloats * 4) : 0);
     constexpr int oQt = oLoop, odPt = oQt + B_ROWS, odAt = odPt + B_PT;
     constexpr int oScr = odAt + B_PT, oTotA = oScr + 8 * DK * 4, oTotB = oTotA + 4 * DK * 4;
     static_assert(oQt + B_ROWS <= oAT, "Qt rows overlap T during preparation");
@@ -90,11 +104,21 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float *sScr = reinterpret_cast<float *>(smem + oScr);
     float *sRed = reinterpret_cast<float *>(smem + oRed);
     __bf16 *sTs = reinterpret_cast<__bf16 *>(smem + oTs);
+    int *sList = reinterpret_cast<int *>(smem + oList);
+    const int NC = (a.T + kChunk - 1) / kChunk;
 
+    // Work list: the fast pass takes its one chunk; the exact pass walks the flagged chunks of
+    // its share, gathered NTH candidates at a time.  Chunk L = (b * H + h) * NC + c.
+    const long nitems = (long)a.B * a.H * NC;
+    const int *flags = reinterpret_cast<const int *>(reinterpret_cast<const char *>(a.factors) +
+                                                     (size_t)nitems * factor_elems_per_chunk<DK>() * 2 +
+                                                     record_flags_offset<DK>(nitems));
+    for (long base = blockIdx.x; base < (EX ? nitems : (long)blockIdx.x + 1); base += (long)gridDim.x * NTH) {
+    const int nwork = EX ? gather_flagged<NTH>(flags, nitems, base, gridDim.x, sList, sList + NTH) : 1;
+    for (int wi = 0; wi < nwork; ++wi) {
+    const int L = EX ? sList[wi] : xcd_swizzle(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int n = hf;                            // value column block of this wave's tiles
-    const int NC = (a.T + kChunk - 1) / kChunk;
-    const int L = xcd_swizzle(blockIdx.x, gridDim.x);
     const int c = L % NC, bh = L / NC, h = bh % a.H, b = bh / a.H;
     const int T = a.T, H = a.H, DV = a.DV;
     const int t0 = c * kChunk;
@@ -182,7 +206,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     load_tile(0, cur, tid);
 
     // ---- preparation: the chunk operand record that the adjoint-factor kernel wrote
-    // (Kt and Et rows, T, P^T fragments and gamma), into LDS and registers
+    // (Kh and Et rows, T, P^T fragments and gamma), into LDS and registers
     using Rec = ChunkRecord<DK>;
     const char *rec = reinterpret_cast<const char *>(a.factors) +
                       (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)L * Rec::BYTES;
@@ -192,7 +216,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         uint4 rv[NROW];
 #pragma unroll
         for (int it = 0; it < NROW; ++it)
-            rv[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKt + (size_t)(tid + NTH * it) * 16);   // Kt, Et planes
+            rv[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKh + (size_t)(tid + NTH * it) * 16);   // Kh, Et planes
         static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
         const int trow = tid >> 3, tc8 = 8 * (tid & 7);
         const uint4 th = *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(trow * kChunk + tc8) * 2);
@@ -219,12 +243,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     __syncthreads();
-    float gm[NSF];
-#pragma unroll
-    for (int it = 0; it < NSF; ++it) {
-        const int idx = tid + NTH * it;
-        gm[it] = sGam[(idx < DK * 8 ? idx : 0) >> 3];
-    }
 
     // ---- value tiles: X, U, dU, dX and the key-side accumulators ----
     f32x4 aQ[NMH], aE[NMH], aH[NMH], aPA[4];     // aPA: dP (half 0) or dA (half 1)
@@ -246,7 +264,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         const int n = hf;
         const int kk_lo = (w >= 2) ? 1 : 0;
         const int nkk = (w >= 2) ? 2 : 1;
-        // stage S, gamma*dS' ([channel][col]) and dO ([col][token]); dgamma partial sums
+        // stage S, dS' ([channel][col]) and dO ([col][token]); dgamma partial sums
 #pragma unroll
         for (int it = 0; it < NSF; ++it) {
             const int idx = tid + NTH * it;
@@ -255,7 +273,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 const float4 sv = cur.s[it], dv = cur.d[it];
                 dgp[it] += (sv.x * dv.x + sv.y * dv.y) + (sv.z * dv.z + sv.w * dv.w);
                 const Split4 ss = split4(f32x4{sv.x, sv.y, sv.z, sv.w});
-                const Split4 ds = split4(f32x4{dv.x, dv.y, dv.z, dv.w} * gm[it]);
+                const Split4 ds = split4(f32x4{dv.x, dv.y, dv.z, dv.w});
                 *reinterpret_cast<bf16x4 *>(&S1[chn * PS + 4 * q]) = ss.hi;
                 *reinterpret_cast<bf16x4 *>(&S1[DK * PS + chn * PS + 4 * q]) = ss.lo;
                 *reinterpret_cast<bf16x4 *>(&D1[chn * PS + 4 * q]) = ds.hi;
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         // next tile's loads are in flight during this tile's products
         load_tile(j0 + VT < DV ? j0 + VT : j0, cur, tid);
 
-        // X = Z - Et S and dU = P^T dO + Kt (gamma dS'): tile (token block w, column block n)
+        // X = Z - Et S and dU = P^T dO + Kh dS': tile (token block w, column block n)
         {
             f32x4 acc;
 #pragma unroll
@@ -373,7 +391,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 aE[mm] = mfma32x3(sa, xT, aE[mm]);   // (-dX S^T)^T
                 const __bf16 *dh = &D1[(16 * m + r) * PS], *dl = dh + DK * PS;
                 aH[mm] = mfma32x3(frag_2x4(dh + 4 * g, dh + 16 + 4 * g, dl + 4 * g, dl + 16 + 4 * g), uT,
-                                  aH[mm]);           // (U (gamma dS')^T)^T = gamma * dKh^T
+                                  aH[mm]);           // (U dS'^T)^T = dKh^T
             }
             const Split8 lhs = hf ? xT : oT;         // dO U^T or -dX U^T
 #pragma unroll
@@ -459,7 +477,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     raw.decay_dact_all(dact);
 #pragma unroll
     for (int e = 0; e < NEH; ++e) G[e] = gv[e / 4][e % 4];
-    {
+    if constexpr (!EX) {
         // Qt rows of this half's channels again
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
@@ -486,59 +504,124 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         for (int q = 0; q < 8; ++q) sacc += sScr[8 * tid + q];
         sDG[tid] = sacc;
     }
-    // dQt^T += Kt^T dP^T and dEt^T += Kt^T dA^T (keys up to this wave's queries);
-    // dKt^T = Qt^T dP + Et^T dA (queries from this wave's keys on)
-    f32x4 aK[NMH];
-#pragma unroll
-    for (int mm = 0; mm < NMH; ++mm) {
-        const int m = NMH * hf + mm;
-        aK[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk < nkk) {
-                const Split8 kt = frag_tr<PK>(sKt, sKt + RK, 32 * kk, 16 * m, r, g);
-                aQ[mm] = mfma32x3(kt, frag_tr<PT>(dPt, dPt + kChunk * PT, 32 * kk, 16 * w, r, g), aQ[mm]);
-                aE[mm] = mfma32x3(kt, frag_tr<PT>(dAt, dAt + kChunk * PT, 32 * kk, 16 * w, r, g), aE[mm]);
-            }
-            if (kk >= kk_lo) {
-                const __bf16 *ph = &dPt[(16 * w + r) * PT + 32 * kk], *pl = ph + kChunk * PT;
-                aK[mm] = mfma32x3(frag_tr<PK>(sQt, sQt + RK, 32 * kk, 16 * m, r, g),
-                                  frag_2x4(ph + 4 * g, ph + 16 + 4 * g, pl + 4 * g, pl + 16 + 4 * g), aK[mm]);
-                const __bf16 *ah = &dAt[(16 * w + r) * PT + 32 * kk], *al = ah + kChunk * PT;
-                aK[mm] = mfma32x3(frag_tr<PK>(sEt, sEt + RK, 32 * kk, 16 * m, r, g),
-                                  frag_2x4(ah + 4 * g, ah + 16 + 4 * g, al + 4 * g, al + 16 + 4 * g), aK[mm]);
-            }
-        }
-    }
 
     // ---- element-wise chain (token 16w + r, channels ch(e)) ----
+    // chain(mm, dq, dE, dK, h) for elements 4mm .. 4mm + 3, in the natural variables: dq, dE (the
+    // gradient of e = b k), dK (k's gradient through A and P) and h = exp(g_C - G), so that
+    // Kh = k h; writes dq, dk, db and leaves dG (xg) and dKh * Kh (yh) for the decay scan.
     float xg[NEH], yh[NEH];
     float sb = 0.f;                // per-token db partial (erase gate per token)
-    {
+    auto chain = [&](int mm, const float (&dq)[4], const float (&dE)[4], const float (&dK)[4],
+                     const float (&h)[4]) __attribute__((always_inline)) {
+        f32x4 vq, vk4, vb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * mm + i;
+            const float dKh = aH[mm][i];
+            vq[i] = dq[i];
+            vb[i] = dE[i] * kf[e] * gate_dact<GL>(bgf[e]);
+            vk4[i] = dK[i] + dKh * h[i] + dE[i] * bgf[e];
+            yh[e] = dKh * kf[e] * h[i];
+            xg[e] = dq[i] * qf[e] + dE[i] * bgf[e] * kf[e] - dK[i] * kf[e] - yh[e];
+        }
+        if (SG && (a.scalar & kScalarErase)) sb += (vb[0] + vb[1]) + (vb[2] + vb[3]);
+        if (vk) {
+            const size_t off = rowK + chh + 16 * mm + 4 * g;
+            *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
+            *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
+            if (!(SG && (a.scalar & kScalarErase))) *reinterpret_cast<f32x4 *>(a.db + off) = vb;
+        }
+    };
+    if constexpr (!EX) {
+        // dQt^T = gamma^-1 (gamma dQt_S^T + Kh^T dP^T) and dEt^T likewise with dA (keys up to this
+        // wave's queries); dKt^T = Qt^T dP + Et^T dA (queries from this wave's keys on)
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
-            f32x4 vq, vk4, vb;
+            const int m = NMH * hf + mm;
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sGam[16 * m + 4 * g]);
+            aQ[mm] *= gam;
+            aE[mm] *= gam;
+            f32x4 aK = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (kk < nkk) {
+                    const Split8 kh = frag_tr<PK>(sKt, sKt + RK, 32 * kk, 16 * m, r, g);
+                    aQ[mm] = mfma32x3(kh, frag_tr<PT>(dPt, dPt + kChunk * PT, 32 * kk, 16 * w, r, g), aQ[mm]);
+                    aE[mm] = mfma32x3(kh, frag_tr<PT>(dAt, dAt + kChunk * PT, 32 * kk, 16 * w, r, g), aE[mm]);
+                }
+                if (kk >= kk_lo) {
+                    const __bf16 *ph = &dPt[(16 * w + r) * PT + 32 * kk], *pl = ph + kChunk * PT;
+                    aK = mfma32x3(frag_tr<PK>(sQt, sQt + RK, 32 * kk, 16 * m, r, g),
+                                  frag_2x4(ph + 4 * g, ph + 16 + 4 * g, pl + 4 * g, pl + 16 + 4 * g), aK);
+                    const __bf16 *ah = &dAt[(16 * w + r) * PT + 32 * kk], *al = ah + kChunk * PT;
+                    aK = mfma32x3(frag_tr<PK>(sEt, sEt + RK, 32 * kk, 16 * m, r, g),
+                                  frag_2x4(ah + 4 * g, ah + 16 + 4 * g, al + 4 * g, al + 16 + 4 * g), aK);
+                }
+            }
+            float dq[4], dE[4], dK[4], h[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * mm + i;
                 const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]);
-                const float Qt = qf[e] * eg, Et = bgf[e] * kf[e] * eg, Kt = kf[e] * eng;
-                const float dQt = aQ[mm][i], dEt = aE[mm][i], dKt = aK[mm][i];
-                const float dHg = aH[mm][i];      // gamma * dKh, and dKh * Kh = dHg * Kt
-                vq[i] = dQt * eg;
-                const float dE = dEt * eg;
-                vb[i] = dE * kf[e] * gate_dact<GL>(bgf[e]);
-                vk4[i] = (dKt + dHg) * eng + dE * bgf[e];
-                xg[e] = dQt * Qt + dEt * Et - (dKt + dHg) * Kt;
-                yh[e] = dHg * Kt;
+                const float rg = eg * __builtin_amdgcn_rcpf(gam[i]);   // exp(G - g_C): finite on unflagged chunks
+                dq[i] = aQ[mm][i] * rg;
+                dE[i] = aE[mm][i] * rg;
+                dK[i] = aK[i] * eng;
+                h[i] = gam[i] * eng;
             }
-            if (SG && (a.scalar & kScalarErase)) sb += (vb[0] + vb[1]) + (vb[2] + vb[3]);
-            if (vk) {
-                const size_t off = rowK + chh + 16 * mm + 4 * g;
-                *reinterpret_cast<f32x4 *>(a.dq + off) = vq;
-                *reinterpret_cast<f32x4 *>(a.dk + off) = vk4;
-                if (!(SG && (a.scalar & kScalarErase))) *reinterpret_cast<f32x4 *>(a.db + off) = vb;
+            chain(mm, dq, dE, dK, h);
+        }
+    } else {
+        // exact pairwise decays, one slice of 16 channels per half at a time (over the Kh and
+        // Et rows, which this pass no longer reads, where they fit)
+        float *slc = reinterpret_cast<float *>(smem + oSl);
+        float ev[NEH];
+#pragma unroll
+        for (int e = 0; e < NEH; ++e) ev[e] = bgf[e] * kf[e];
+        const int t = 16 * w + r;
+        const int jhi = 16 * w + 16;                  // keys j <= t of this wave's queries: j < jhi
+#pragma unroll
+        for (int mm = 0; mm < NMH; ++mm) {
+            __syncthreads();
+            slice_put<NEH>(slc, mm, hf, w, r, g, ev, qf, kf, G);
+            __syncthreads();
+            float rq[4] = {0.f, 0.f, 0.f, 0.f}, ra[4] = {0.f, 0.f, 0.f, 0.f}, ck[4] = {0.f, 0.f, 0.f, 0.f};
+            // row side: dq_t += sum_{j <= t} dP_tj k_j x_tj, dE_t += sum_{j < t} dA_tj k_j x_tj
+            for (int j = 0; j < jhi; ++j) {
+                const float dp = (float)dPt[j * PT + t] + (float)dPt[kChunk * PT + j * PT + t];
+                const float da = (float)dAt[j * PT + t] + (float)dAt[kChunk * PT + j * PT + t];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int cc = 4 * g + i;
+                    const float kx = slc[slice_idx(hf, 2, cc, j)] * exp2_fast(G[4 * mm + i] - slc[slice_idx(hf, 3, cc, j)]);
+                    const bool on = j <= t;   // beyond it the factor may be inf
+                    rq[i] += on ? dp * kx : 0.f;
+                    ra[i] += on ? da * kx : 0.f;
+                }
             }
+            // column side: dk_t += sum_{i >= t} (dA_it e_i + dP_it q_i) x_it
+            for (int q = 16 * w; q < kChunk; ++q) {
+                const float dp = (float)dPt[t * PT + q] + (float)dPt[kChunk * PT + t * PT + q];
+                const float da = (float)dAt[t * PT + q] + (float)dAt[kChunk * PT + t * PT + q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int cc = 4 * g + i;
+                    const float x = exp2_fast(slc[slice_idx(hf, 3, cc, q)] - G[4 * mm + i]);
+                    const float y = (da * slc[slice_idx(hf, 0, cc, q)] + dp * slc[slice_idx(hf, 1, cc, q)]) * x;
+                    ck[i] += q >= t ? y : 0.f;
+                }
+            }
+            float dq[4], dE[4], h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * mm + i;
+                const float eg = exp2_fast(G[e]);
+                const float gC = slc[slice_idx(hf, 3, 4 * g + i, kChunk - 1)];
+                dq[i] = aQ[mm][i] * eg + rq[i];
+                dE[i] = aE[mm][i] * eg + ra[i];
+                h[i] = exp2_fast(gC - G[e]);
+            }
+            chain(mm, dq, dE, ck, h);
         }
     }
     // dlog_alpha_t = sum_{s >= t} dG_s + dg_C, with dg_C = sum_s dKh_s Kh_s + dgamma gamma
@@ -571,16 +654,28 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         if (hf == 0 && g == 0 && vk) a.dla[srowK] = sl + sRed[kChunk + 16 * w + r];
     }
   }
+    if (EX) __syncthreads();   // the next chunk of the exact pass overwrites this one's LDS
+    }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+// The fast pass over every chunk, then the exact pass (persistent, one workgroup per CU) over
+// the chunks the factor kernel flagged; its workgroups read their share of the flags and end
+// when none is set.
 template <int DK, bool BF16, bool GL, bool SG>
 static hipError_t chunk_t(const BwdArgs &a, hipStream_t st) {
     const int NC = (a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG>), dim3((unsigned)(a.B * a.H * NC)), dim3(kChunkThreads),
-                       0, st, a);
+    const long items = (long)a.B * a.H * NC;
+    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG, false>), dim3((unsigned)items), dim3(kChunkThreads), 0, st,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long grid = items < cu_count() ? items : cu_count();
+    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG, true>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st,
+                       a);
     return hipGetLastError();
 }
 

@@ -331,7 +331,7 @@ struct KeyRaw4 {
         }
 #pragma unroll
         for (int e = 0; e < 4 * NM; ++e) {
-            laf[e] = valid ? laf[e] : 0.f;
+            laf[e] = valid ? floor_log_decay(laf[e]) : 0.f;
             bgf[e] = valid ? bgf[e] : 0.f;
         }
     }
@@ -371,7 +371,8 @@ constexpr size_t factor_elems_per_chunk() {
 // ---- chunk operand record ----
 // The key-side operands of one (batch, head, chunk), formed once by the adjoint-factor
 // kernel and read by the forward sweep and the chunk-gradient kernel:
-//   Kt, Et, Qt rows    [token][channel] split bf16, hi plane then lo plane, pitch DK
+//   Kh, Et, Qt rows    [token][channel] split bf16, hi plane then lo plane, pitch DK
+//                      (Kh = k exp(g_C - G), Et = b k exp(G), Qt = q exp(G): factors <= 1)
 //   T = (I + A)^-1     [row][col] split bf16, hi then lo, pitch 64
 //   P^T fragments      tile (key block w, query block mt) at (4w + mt) * 64 lanes * 8 bf16:
 //                      lane (r, g) holds P[16mt + 4g + i][16w + r], hi (i < 4) then lo
@@ -387,7 +388,7 @@ template <int DK>
 struct ChunkRecord {
     static constexpr int PLANE = kChunk * DK * 2;               // bytes of one [token][channel] bf16 plane
     static constexpr int ROWS = 2 * PLANE;                      // an operand's hi and lo planes
-    static constexpr int oKt = 0, oEt = oKt + ROWS, oQt = oEt + ROWS;
+    static constexpr int oKh = 0, oEt = oKh + ROWS, oQt = oEt + ROWS;
     static constexpr int oT = oQt + ROWS, B_T = kChunk * kChunk * 2 * 2;
     static constexpr int B_FR = 16 * 64 * 8 * 2;                // 16 fragment tiles of 64 lanes x 8 bf16
     static constexpr int oPt = oT + B_T, oP = oPt + B_FR;
@@ -395,5 +396,27 @@ struct ChunkRecord {
     static constexpr int oGam = oG + B_G;
     static constexpr int BYTES = (oGam + DK * 4 + 255) / 256 * 256;
 };
+
+// A buffer of `items` records is followed by one int per record: 1 if the chunk's decay is
+// too strong for the factorised operands (some gamma below kGamMin), else 0.
+template <int DK>
+__host__ __device__ constexpr size_t record_flags_offset(long items) {
+    return (size_t)items * ChunkRecord<DK>::BYTES;
+}
+__host__ __device__ constexpr size_t record_flags_bytes(long items) { return ((size_t)items * 4 + 255) / 256 * 256; }
+
+// Work list of an exact pass: the flagged items among base, base + stride, ...,
+// base + (NTH - 1) stride (one candidate per thread), gathered into sList (NTH ints of LDS);
+// returns their number (uniform over the workgroup).  *sCount: one int of LDS.  Two barriers.
+template <int NTH>
+__device__ __forceinline__ int gather_flagged(const int *flags, long nitems, long base, int stride, int *sList,
+                                              int *sCount) {
+    if (threadIdx.x == 0) *sCount = 0;
+    __syncthreads();
+    const long L = base + (long)threadIdx.x * stride;
+    if (L < nitems && flags[L] != 0) sList[atomicAdd(sCount, 1)] = (int)L;
+    __syncthreads();
+    return *sCount;
+}
 
 }  // namespace gdn2

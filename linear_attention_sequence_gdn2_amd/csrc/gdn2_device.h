@@ -28,6 +28,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 64;
+
+// Decay range.  The rule puts no floor under alpha (blog on Gated DeltaNet-2, section
+// "Independent control on two axes"), so the chunk kernels take any log_alpha <= 0:
+//  - a per-token log-decay below kLogDecayFloor is computed as kLogDecayFloor.  A factor
+//    exp(-30) = 9.4e-14 on whatever the state held is far below fp32 resolution, and the
+//    floor keeps alpha = 0 (log_alpha = -inf) from turning cumulative sums into -inf - -inf;
+//  - a chunk in which some key channel's total decay gamma = exp(g_C) is below kGamMin
+//    (2^-92, g_C < -63.8) is flagged.  The factorised operands of the chunk form, whose
+//    exp(-G) would leave fp32 range there, are then replaced by the exact pairwise decays
+//    exp(G_i - G_j) (i >= j, at most 1) in a second, exact pass over the flagged chunks.
+// A NaN log-decay passes the floor unchanged, so it propagates.
+constexpr float kLogDecayFloor = -30.f;
+constexpr float kGamMin = 0x1p-92f;
+__device__ __forceinline__ float floor_log_decay(float x) { return x < kLogDecayFloor ? kLogDecayFloor : x; }
 constexpr int kThreads = 256;
 constexpr int kChunkThreads = 2 * kThreads;   // workgroup of the chunk-parallel backward kernels
 

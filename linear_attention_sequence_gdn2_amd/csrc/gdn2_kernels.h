@@ -61,16 +61,15 @@ inline int cu_count() {
     return cus;
 }
 
-// Value-tile width the forward sweep uses for this shape (16, 32 or 64).
+// Value-tile width the four-wave forward sweep uses for this shape (16 or 32).
 int fwd_value_tile(int B, int H, int dk, int dv);
 
 // What a forward sweep produces: o only, chunk states only, or both.
 enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
 // gl: the gates are bf16 logits (only with bf16 q/k/v); sg: some gates are given per token
-// (a.scalar; only with bf16 q/k/v and fp32 gate values)
-hipError_t launch_fwd(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode, hipStream_t st);
-// The same sweep with the key-side operands of every chunk taken from the chunk operand
-// records of the factor buffer (a.factors); q, k, log_alpha and b are not read.
+// (a.scalar; only with bf16 q/k/v and fp32 gate values).
+// The forward sweep with the key-side operands of every chunk taken from chunk operand
+// records (a.records); q, k, log_alpha and b are not read.
 // The forward sweep over few heads, sequence split into a.nseg segments of a.seg_len chunks
 // (bf16 q/k/v, dk 64 or 128, dv a multiple of 64): every segment's state map into E
 // [B, H, nseg, dk, dv + dk], the composed start states into Sin [B, H, nseg, dk, dv], then
@@ -89,9 +88,10 @@ bool fwd_rev_fused(int B, int H, int dk, int dv, bool bf16);
 // fwd_rev_fused is false.
 hipError_t launch_fwd_rev_sweeps(const FwdArgs &fa, const BwdArgs &ba, int dk, bool gl, bool sg, hipStream_t st);
 // Bytes of the factor buffer of `items` chunks: the adjoint factors R, Q2^T of every chunk,
-// then the chunk operand record of every chunk (read by the chunk-gradient kernel).
+// then the chunk operand record of every chunk (read by the chunk-gradient kernel), then the
+// strong-decay flag of every chunk.
 size_t factor_buffer_bytes(long items, int dk);
-// Bytes of `items` chunk operand records alone (the forward-only buffer).
+// Bytes of `items` chunk operand records and their flags (the forward-only buffer).
 size_t record_buffer_bytes(long items, int dk);
 hipError_t launch_bwd_factors(const BwdArgs &a, int dk, bool bf16, bool gl, bool sg, hipStream_t st);
 // Forward-only records: a.factors receives just the records the forward sweep reads.

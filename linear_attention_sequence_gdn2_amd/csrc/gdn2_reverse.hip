@@ -2,13 +2,13 @@
 // adjoint factors (chunk-parallel), then the chunk-to-chunk recurrence of the state
 // gradient (sequential over chunks).
 //
-// Chunk notation of gdn2_fwd.hip (blog on Gated DeltaNet-2, section "Token path and
-// parallel training"): start state S, end state S' = diag(gamma)(S + Kt^T U),
+// Chunk notation of gdn2_sweep.hip (blog on Gated DeltaNet-2, section "Token path and
+// parallel training"): start state S, end state S' = diag(gamma) S + Kh^T U,
 // U = T X, X = Z - Et S, O = Qt S + P U.  The adjoint of one chunk gives for the
 // gradient of its start state
-//     dS = Qt^T dO + diag(gamma) dS' - Et^T dX,   dX = T^T (P^T dO + Kt diag(gamma) dS').
+//     dS = Qt^T dO + diag(gamma) dS' - Et^T dX,   dX = T^T (P^T dO + Kh dS').
 // With W = T Et (the WY factor of the erase keys) this is
-//     dS = R dS' + Q2^T dO,   R = (I - W^T Kt) diag(gamma),   Q2 = Qt - P W,
+//     dS = R dS' + Q2^T dO,   R = diag(gamma) - W^T Kh,   Q2 = Qt - P W,
 // where R (dk x dk) and Q2 (64 x dk) depend on the key side of the chunk only.
 // bwd_factors_kernel forms them for every (batch, head, chunk) at once, and
 // bwd_reverse_kernel is left with two dense products per chunk on its critical path.
@@ -20,6 +20,7 @@
 // 2j + 1 give a lane its whole A operand of contraction step j in the 4-group order,
 // with one 16-byte load each.
 #include "gdn2_chunk.h"
+#include "gdn2_exact.h"
 #include "gdn2_kernels.h"
 #include "gdn2_rsweep.h"
 
@@ -43,79 +44,98 @@ __device__ __forceinline__ void store_frag_tile(__bf16 *tile, int l, const f32x4
 // Eight waves in two halves, as in bwd_chunk_kernel: wave (hf, w) owns tokens
 // 16w..16w+15 and, for the element work, the channels of half hf.
 // FWD: forward-only records (a.factors holds just the records): the rows, T, P and gamma
-// that the forward sweep reads, without the adjoint factors, P^T, G or the Et lo plane.
-template <int DK, bool BF16, bool GL, bool SG, bool FWD>
+// that the forward sweep reads, without the adjoint factors, P^T or G (and without the Et lo
+// plane for bf16 q/k/v, whose sweep reads the hi plane only).
+// EX: the exact pass.  The fast pass (EX false) forms A = Et Kt^T and P = Qt Kt^T from the
+// factorised rows Kt = k exp(-G), and flags every chunk in which some channel's decay gamma
+// is below kGamMin, where exp(-G) may leave fp32 range; the exact pass then redoes only the
+// flagged chunks, with A and P from the pairwise decays (gdn2_exact.h) and R = diag(gamma) -
+// W^T Kh.  The record's Kh, Et, Qt rows, gamma and G are the same in both passes.
+template <int DK, bool BF16, bool GL, bool SG, bool FWD, bool EX>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
     constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
     constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4;
     constexpr int RK = kChunk * PK;
     using Rec = ChunkRecord<DK>;
-    // LDS (bytes): Kt, Et, Qt rows [token][channel] (hi, lo); the decay totals after the
-    // Et rows; W^T [channel][token] (hi, lo) later over the Et rows and the totals;
-    // A then T (fp32); gamma per channel.
+    // LDS (bytes): Kt (Kh in the exact pass), Et, Qt rows [token][channel] (hi, lo); the decay
+    // totals after the Et rows; W^T [channel][token] (hi, lo) later over the Et rows and the
+    // totals; A then T (fp32); gamma per channel; in the exact pass the channel slices (then
+    // P, fp32) and the work list.
     constexpr int B_ROWS = 2 * RK * 2, B_WT = 2 * DK * PT * 2, B_TOT = 4 * DK * 4;
     constexpr int oKt = 0, oEt = oKt + B_ROWS, oTot = oEt + B_ROWS;
     constexpr int oQt0 = (oTot + B_TOT > oEt + B_WT) ? oTot + B_TOT : oEt + B_WT;
     constexpr int oQt = (oQt0 + 15) / 16 * 16;
     constexpr int oAT = oQt + B_ROWS, oGam = oAT + kChunk * PA * 4;
-    constexpr int SMEM = oGam + DK * 4;
+    constexpr int oEx = oGam + DK * 4, B_EX = EX ? kSliceFloats * 4 : 0;
+    constexpr int oList = oEx + B_EX, B_LIST = EX ? (NTH + 4) * 4 : 0;
+    constexpr int SMEM = oList + B_LIST;
     static_assert(SMEM <= 160 * 1024, "LDS budget of a CU");
+    static_assert(kChunk * PA <= kSliceFloats, "P fits over the slices");
 
     __shared__ __align__(16) char smem[SMEM];
     __bf16 *sKt = reinterpret_cast<__bf16 *>(smem + oKt), *sEt = reinterpret_cast<__bf16 *>(smem + oEt);
     __bf16 *sQt = reinterpret_cast<__bf16 *>(smem + oQt), *sWT = reinterpret_cast<__bf16 *>(smem + oEt);
     float *sTot = reinterpret_cast<float *>(smem + oTot), *sAT = reinterpret_cast<float *>(smem + oAT);
     float *sGam = reinterpret_cast<float *>(smem + oGam);
+    float *sEx = reinterpret_cast<float *>(smem + oEx);
+    int *sList = reinterpret_cast<int *>(smem + oList);
 
-    const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int NC = (a.T + kChunk - 1) / kChunk;
     const int T = a.T, H = a.H;
     const int nitems = a.B * H * NC;                    // item L = (b * H + h) * NC + c
     const size_t tokK = (size_t)H * DK;
-    const int nkk = (w >= 2) ? 2 : 1;
-    const int chh = hf * (DK / 2);
-    auto ch = [&](int e) { return chh + ch4(e, g); };
+    char *const recs = reinterpret_cast<char *>(a.factors) + (FWD ? 0 : (size_t)nitems * factor_elems_per_chunk<DK>() * 2);
+    int *const flags = reinterpret_cast<int *>(recs + record_flags_offset<DK>(nitems));
     // this lane's token row (channel 0 of its half) in item L, and whether the token exists
     auto item_row = [&](int L, bool &valid) {
+        const int tid = threadIdx.x, w = (tid >> 6) & 3, r = tid & 15, chh = (tid >> 8) * (DK / 2);
         const int c = L % NC, bh = L / NC, h = bh % H, b = bh / H;
         const int tk = c * kChunk + 16 * w + r;
         valid = tk < T;
         return ((size_t)b * T * H + h) * DK + (size_t)(valid ? tk : T - 1) * tokK + chh;
     };
 
-    // Persistent: the workgroup walks items blockIdx.x, + gridDim.x, ...; the key-side
-    // inputs of the next item are loaded while the current one is in its products.
     KeyRaw4<DK / 2, BF16, GL, SG> raw;
-    {
-        bool v0;
-        const size_t row0 = item_row(blockIdx.x < nitems ? blockIdx.x : 0, v0);
-        raw.issue(a.q, a.k, a.la, a.bg, row0, g, v0, (row0 - chh) / DK, a.scalar);
-    }
-    for (int L = blockIdx.x; L < nitems; L += gridDim.x) {
+    auto issue = [&](int L) {
+        bool v;
+        const size_t row = item_row(L, v);
+        raw.issue(a.q, a.k, a.la, a.bg, row, (threadIdx.x >> 4) & 3, v, (row - (threadIdx.x >> 8) * (DK / 2)) / DK,
+                  a.scalar);
+    };
+
+    // Work list.  Fast pass: persistent, items blockIdx.x, + gridDim.x, ...; the key-side inputs
+    // of the next item (Ln) are loaded while the current one is in its products.  Exact pass: the
+    // flagged items of the same share, gathered NTH candidates at a time, each loading its
+    // inputs at its start.
+    const int nmine = blockIdx.x < (unsigned)nitems ? (nitems - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    if (!EX) issue(blockIdx.x < (unsigned)nitems ? blockIdx.x : 0);
+    for (long base = blockIdx.x; base < (EX ? nitems : (long)blockIdx.x + 1); base += (long)gridDim.x * NTH) {
+    const int nwork = EX ? gather_flagged<NTH>(flags, nitems, base, gridDim.x, sList, sList + NTH) : nmine;
+    for (int wi = 0; wi < nwork; ++wi) {
+    const int L = EX ? sList[wi] : (int)blockIdx.x + wi * (int)gridDim.x;
+    const int Ln = EX ? L : (L + (int)gridDim.x < nitems ? L + (int)gridDim.x : L);
+    if (EX) issue(L);
     const int tid = threadIdx.x;
     const int wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int nkk = (w >= 2) ? 2 : 1;
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
-    auto item_row = [&](int L, bool &valid) {
-        const int c = L % NC, bh = L / NC, h = bh % H, b = bh / H;
-        const int tk = c * kChunk + 16 * w + r;
-        valid = tk < T;
-        return ((size_t)b * T * H + h) * DK + (size_t)(valid ? tk : T - 1) * tokK + chh;
-    };
     __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
-    // this item's chunk operand record, after the factors of all items
-    char *rec = reinterpret_cast<char *>(a.factors) + (FWD ? 0 : (size_t)nitems * factor_elems_per_chunk<DK>() * 2) +
-                (size_t)L * Rec::BYTES;
+    char *rec = recs + (size_t)L * Rec::BYTES;
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
+    float qf[NEH], kf[NEH], G[NEH], bgf[NEH], ev[NEH];   // ev (e = b k) and G kept for the exact products
+    int unsafe;
     {
-        float qf[NEH], kf[NEH], G[NEH], bgf[NEH], gC[NEH];
+        float gC[NEH];
         raw.unpack(qf, kf, G, bgf);
 #pragma unroll
         for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
         chunk_scan<NEH, DK>(G, gC, sTot, w, r, ch);
+        bool strong = false;
+#pragma unroll
+        for (int e = 0; e < NEH; ++e) strong |= exp2_fast(gC[e]) < kGamMin;
         if (w == 0 && r == 0) {
 #pragma unroll
             for (int e = 0; e < NEH; ++e) {
@@ -136,10 +156,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * mm + i;
-                const float eg = exp2_fast(G[e]), eng = exp2_fast(-G[e]);
-                et[i] = bgf[e] * kf[e] * eg;
+                const float eg = exp2_fast(G[e]);
+                ev[e] = bgf[e] * kf[e];
+                et[i] = ev[e] * eg;
                 qt[i] = qf[e] * eg;
-                kt[i] = kf[e] * eng;
+                // the exact pass stages Kh = k exp(g_C - G) (its Kt may leave fp32 range)
+                kt[i] = kf[e] * exp2_fast(EX ? gC[e] - G[e] : -G[e]);
             }
             const int o = (16 * w + r) * PK + chh + 16 * mm + 4 * g;
             const Split4 se = split4(et), sq = split4(qt), sk = split4(kt);
@@ -150,96 +172,136 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
             *reinterpret_cast<bf16x4 *>(&sKt[o]) = sk.hi;
             *reinterpret_cast<bf16x4 *>(&sKt[RK + o]) = sk.lo;
         }
+        unsafe = __syncthreads_or(strong);
     }
-    __syncthreads();
+    if (!EX && tid == 0) flags[L] = unsafe ? 1 : 0;
 
-    // ---- record: Kt, Et and Qt rows (dense pitch), P^T fragments ----
-    static_assert((6 * 8 * DK) % NTH == 0, "row planes split evenly over the threads");
+    // ---- record: Kh rows (Kt diag(gamma) from the fast pass's Kt rows; the exact pass's LDS
+    // rows are Kh already), one thread per 8 channels of a row (hi and lo) ----
 #pragma unroll
-    for (int it = 0; it < 6 * 8 * DK / NTH; ++it) {
-        const int idx = tid + NTH * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
+    for (int it = 0; it < (8 * DK + NTH - 1) / NTH; ++it) {
+        const int idx = tid + NTH * it, row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+        if (idx >= 8 * DK) break;
+        Split8 kh = frag_8(&sKt[row * PK + c8], &sKt[RK + row * PK + c8]);
+        if (!EX) {
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&sGam[c8]);
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&sGam[c8 + 4]);
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = ((float)kh.hi[i] + (float)kh.lo[i]) * (i < 4 ? g0[i] : g1[i - 4]);
+            kh = split8(x);
+        }
+        const size_t ro = (size_t)(row * DK + c8) * 2;
+        *reinterpret_cast<bf16x8 *>(rec + Rec::oKh + ro) = kh.hi;
+        *reinterpret_cast<bf16x8 *>(rec + Rec::oKh + Rec::PLANE + ro) = kh.lo;
+    }
+    // ---- record: Et and Qt rows (dense pitch) ----
+    static_assert((4 * 8 * DK) % NTH == 0, "row planes split evenly over the threads");
+#pragma unroll
+    for (int it = 0; it < 4 * 8 * DK / NTH; ++it) {
+        const int idx = tid + NTH * it, plane = 2 + idx / (8 * DK), rem = idx % (8 * DK);
         const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
-        const __bf16 *src = (plane < 2 ? sKt : plane < 4 ? sEt : sQt) + (plane & 1) * RK + row * PK + c8;
-        if (!(FWD && plane == 3))   // the forward sweep reads the hi plane of Et only
-            *reinterpret_cast<uint4 *>(rec + Rec::oKt + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
+        const __bf16 *src = (plane < 4 ? sEt : sQt) + (plane & 1) * RK + row * PK + c8;
+        if (!(FWD && BF16 && plane == 3))   // the bf16 forward sweep reads the hi plane of Et only
+            *reinterpret_cast<uint4 *>(rec + Rec::oKh + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
                 *reinterpret_cast<const uint4 *>(src);
     }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        if (!FWD && (mt & 1) == hf) {   // every tile is written (zero for mt < w): readers load all four
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (mt >= w) {
-#pragma unroll
-                for (int j = 0; j < NKS; ++j)
-                    acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
-                                   row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
-                // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
-            }
-            const Split4 sp = split4(acc);
-            bf16x8 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[i] = sp.hi[i];
-                o[4 + i] = sp.lo[i];
-            }
-            *reinterpret_cast<bf16x8 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
-        }
-    }
 
-    {
+    Split4 Pf[4];
+    if constexpr (EX) {
+        // ---- A and P with the exact pairwise decays; P fp32 over the slices ----
+        float *sP = sEx;
+        exact_AP<NEH, PA>(sEx, sAT, sP, hf, w, r, g, ev, qf, kf, G);
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            // lane holds P[16w + r][16mt + 4g + i] (zero for mt > w)
+            const f32x4 pv = *reinterpret_cast<const f32x4 *>(&sP[(16 * w + r) * PA + 16 * mt + 4 * g]);
+            Pf[mt] = split4(pv);
+            if (hf == 0) {
+                bf16x8 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = Pf[mt].hi[i];
+                    o[4 + i] = Pf[mt].lo[i];
+                }
+                *reinterpret_cast<bf16x8 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
+            }
+            if (!FWD && (mt & 1) == hf) {
+                // P^T fragment: lane holds P[16mt + 4g + i][16w + r] (zero for mt < w)
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = sP[(16 * mt + 4 * g + i) * PA + 16 * w + r];
+                store_frag_tile(reinterpret_cast<__bf16 *>(rec + Rec::oPt) + (size_t)((4 * w + mt) * 64) * 8, l, acc);
+            }
+        }
+        __syncthreads();
+    } else {
+        // ---- record: P^T fragments ----
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            if (!FWD && (mt & 1) == hf) {   // every tile is written (zero for mt < w): readers load all four
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (mt >= w) {
+#pragma unroll
+                    for (int j = 0; j < NKS; ++j)
+                        acc = mfma32x3(row_frag4<PK>(sQt, sQt + RK, 16 * mt + r, j, g),
+                                       row_frag4<PK>(sKt, sKt + RK, 16 * w + r, j, g), acc);
+                    // lane holds P[16mt + 4g + i][16w + r]; the query reads the updated state: key <= query
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!(16 * w + r <= 16 * mt + 4 * g + i)) acc[i] = 0.f;
+                }
+                store_frag_tile(reinterpret_cast<__bf16 *>(rec + Rec::oPt) + (size_t)((4 * w + mt) * 64) * 8, l, acc);
+            }
+        }
+
         // the next item's key-side inputs, issued after this item's row stores: issued at the
         // top of the item they would queue behind the previous item's factor stores
-        const int Ln = L + (int)gridDim.x < nitems ? L + (int)gridDim.x : L;
-        bool vn;
-        const size_t rown = item_row(Ln, vn);
-        raw.issue(a.q, a.k, a.la, a.bg, rown, g, vn, (rown - chh) / DK, a.scalar);
-    }
+        issue(Ln);
 
-    // ---- A (shared out between the halves) and the rows of P of query block w ----
-    Split4 Pf[4];
+        // ---- A (shared out between the halves) and the rows of P of query block w ----
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        if (mt <= w && (mt & 1) == hf) {
+        for (int mt = 0; mt < 4; ++mt) {
+            if (mt <= w && (mt & 1) == hf) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < NKS; ++j) {
+                    const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g);
+                    const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
+                    acc = mfma32x3(kf, ef, acc);
+                }
+                // lane holds A[16w + r][16mt + 4g + i]
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!(16 * mt + 4 * g + i < 16 * w + r)) acc[i] = 0.f;
+                *reinterpret_cast<f32x4 *>(&sAT[(16 * w + r) * PA + 16 * mt + 4 * g]) = acc;
+            }
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (mt <= w) {
 #pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g);
-                const Split8 ef = row_frag4<PK>(sEt, sEt + RK, 16 * w + r, j, g);
-                acc = mfma32x3(kf, ef, acc);
+                for (int j = 0; j < NKS; ++j)
+                    acc = mfma32x3(row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g),
+                                   row_frag4<PK>(sQt, sQt + RK, 16 * w + r, j, g), acc);
+                // lane holds P[16w + r][16mt + 4g + i]; the query reads the updated state: key <= query
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!(16 * mt + 4 * g + i <= 16 * w + r)) acc[i] = 0.f;
             }
-            // lane holds A[16w + r][16mt + 4g + i]
+            Pf[mt] = split4(acc);
+            if (hf == 0) {
+                // record: P fragment of tile (query block w, key block mt), zero for mt > w
+                bf16x8 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * mt + 4 * g + i < 16 * w + r)) acc[i] = 0.f;
-            *reinterpret_cast<f32x4 *>(&sAT[(16 * w + r) * PA + 16 * mt + 4 * g]) = acc;
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (mt <= w) {
-#pragma unroll
-            for (int j = 0; j < NKS; ++j)
-                acc = mfma32x3(row_frag4<PK>(sKt, sKt + RK, 16 * mt + r, j, g),
-                               row_frag4<PK>(sQt, sQt + RK, 16 * w + r, j, g), acc);
-            // lane holds P[16w + r][16mt + 4g + i]; the query reads the updated state: key <= query
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(16 * mt + 4 * g + i <= 16 * w + r)) acc[i] = 0.f;
-        }
-        Pf[mt] = split4(acc);
-        if (hf == 0) {
-            // record: P fragment of tile (query block w, key block mt), zero for mt > w
-            bf16x8 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[i] = Pf[mt].hi[i];
-                o[4 + i] = Pf[mt].lo[i];
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = Pf[mt].hi[i];
+                    o[4 + i] = Pf[mt].lo[i];
+                }
+                *reinterpret_cast<bf16x8 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
             }
-            *reinterpret_cast<bf16x8 *>(rec + Rec::oP + (size_t)((4 * w + mt) * 64 + l) * 16) = o;
         }
+        __syncthreads();
     }
-    __syncthreads();
     solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
     {
         // record: T as split bf16 [row][col], one thread per 8 elements
@@ -305,7 +367,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         store_frag_tile(fac + (size_t)(NM * NM + am * 4 + w) * kFragTile, l, q2);
     }
 
-    // ---- R = (I - W^T Kt) diag(gamma), tile (row block am, column block bm) ----
+    // ---- R = (I - W^T Kt) diag(gamma) = diag(gamma) - W^T Kh, tile (row block am, column block bm) ----
     for (int t = wv; t < NM * NM; t += NTH / 64) {
         const int bm = t / NM, am = t % NM;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -315,16 +377,17 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
             acc = mfma32x3(frag_tr<PK>(sKt, sKt + RK, 32 * kk, 16 * bm, r, g),
                            frag_2x4(wh + 4 * g, wh + 16 + 4 * g, wl + 4 * g, wl + 16 + 4 * g), acc);
         }
-        // lane holds (Kt^T W)[16bm + 4g + i][16am + r] = (W^T Kt)[16am + r][16bm + 4g + i]
+        // lane holds (K^T W)[16bm + 4g + i][16am + r] = (W^T K)[16am + r][16bm + 4g + i], K = Kt or Kh
         f32x4 rt;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int cc = 16 * bm + 4 * g + i, rr = 16 * am + r;
-            rt[i] = sGam[cc] * ((cc == rr ? 1.f : 0.f) - acc[i]);
+            rt[i] = EX ? sGam[cc] * (cc == rr ? 1.f : 0.f) - acc[i] : sGam[cc] * ((cc == rr ? 1.f : 0.f) - acc[i]);
         }
         store_frag_tile(fac + (size_t)(am * NM + bm) * kFragTile, l, rt);
     }
     __syncthreads();   // the next item overwrites the LDS this one still reads
+    }
     }
 }
 
@@ -342,31 +405,37 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-size_t factor_buffer_bytes(long items, int dk) {
-    switch (dk) {
-        case 32: return (size_t)items * (factor_elems_per_chunk<32>() * 2 + ChunkRecord<32>::BYTES);
-        case 64: return (size_t)items * (factor_elems_per_chunk<64>() * 2 + ChunkRecord<64>::BYTES);
-        case 128: return (size_t)items * (factor_elems_per_chunk<128>() * 2 + ChunkRecord<128>::BYTES);
-        default: return 0;
-    }
-}
-
 size_t record_buffer_bytes(long items, int dk) {
     switch (dk) {
-        case 32: return (size_t)items * ChunkRecord<32>::BYTES;
-        case 64: return (size_t)items * ChunkRecord<64>::BYTES;
-        case 128: return (size_t)items * ChunkRecord<128>::BYTES;
+        case 32: return (size_t)items * ChunkRecord<32>::BYTES + record_flags_bytes(items);
+        case 64: return (size_t)items * ChunkRecord<64>::BYTES + record_flags_bytes(items);
+        case 128: return (size_t)items * ChunkRecord<128>::BYTES + record_flags_bytes(items);
         default: return 0;
     }
 }
 
+size_t factor_buffer_bytes(long items, int dk) {
+    switch (dk) {
+        case 32: return (size_t)items * factor_elems_per_chunk<32>() * 2 + record_buffer_bytes(items, 32);
+        case 64: return (size_t)items * factor_elems_per_chunk<64>() * 2 + record_buffer_bytes(items, 64);
+        case 128: return (size_t)items * factor_elems_per_chunk<128>() * 2 + record_buffer_bytes(items, 128);
+        default: return 0;
+    }
+}
+
+// The fast pass over every chunk, then the exact pass over the chunks it flagged (a workgroup
+// whose share holds no flagged chunk reads its flags and ends).
 template <int DK, bool BF16, bool GL, bool SG, bool FWD>
 static hipError_t factors_t(const BwdArgs &a, hipStream_t st) {
     const long items = (long)a.B * a.H * ((a.T + kChunk - 1) / kChunk);
     // one persistent workgroup per CU (the kernel's LDS allows no second one)
     const long grid = items < cu_count() ? items : cu_count();
-    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL, SG, FWD>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st,
-                       a);
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL, SG, FWD, false>), dim3((unsigned)grid), dim3(kChunkThreads),
+                       0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_factors_kernel<DK, BF16, GL, SG, FWD, true>), dim3((unsigned)grid), dim3(kChunkThreads),
+                       0, st, a);
     return hipGetLastError();
 }
 

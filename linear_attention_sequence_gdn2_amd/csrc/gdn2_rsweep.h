@@ -2,7 +2,7 @@
 // the reverse-sweep kernel and the combined forward/reverse sweep launch share one body.
 //
 // Per chunk, going backwards, the gradient of the chunk's start state is
-//     dS = R dS' + Q2^T dO,   R = (I - W^T Kt) diag(gamma),   Q2 = Qt - P W,   W = T Et
+//     dS = R dS' + Q2^T dO,   R = diag(gamma) - W^T Kh,   Q2 = Qt - P W,   W = T Et
 // (the adjoint of the chunk equations of the blog on Gated DeltaNet-2, section "Token path and
 // parallel training"), with R and Q2 read from the factor buffer that bwd_factors_kernel wrote.
 #pragma once

@@ -4,9 +4,10 @@
 // Chunk form (blog on Gated DeltaNet-2, section "Token path and parallel training":
 // cumulative channel decay absorbed into asymmetric erase factors, a triangular solve
 // and dense products).  For a chunk with start state S:
-//     X = Z - Et S,   U = T X,   O = Qt S + P U,   S' = diag(gamma) (S + Kt^T U),
-// with Z = w * v and Et, Kt, Qt, T = (I + A)^-1, P, gamma depending on the key side of
-// the chunk only.  The adjoint-factor kernel forms those for every chunk at once and
+//     X = Z - Et S,   U = T X,   O = Qt S + P U,   S' = diag(gamma) S + Kh^T U,
+// with Z = w * v and Et, Kh, Qt, T = (I + A)^-1, P, gamma depending on the key side of
+// the chunk only (Et = b k exp(G), Qt = q exp(G), Kh = k exp(g_C - G): every decay factor
+// is at most 1, so these products stay in range whatever the decay).  The adjoint-factor kernel forms those for every chunk at once and
 // keeps them in the chunk operand records; what is left for this sequential sweep are
 // the products with the state, which cannot run ahead of the previous chunk.
 //
@@ -24,9 +25,9 @@
 // rows of X, U and O and NTS tiles of the state; the fp32 state stays in registers (D
 // layout) with a split-bf16 copy in LDS as the next chunk's operand.  Per chunk the
 // wave loads its A operands (rows of Et, Qt, T and P) straight from the record into
-// registers, and the workgroup stages the Kt rows in LDS for the transposed reads of
+// registers, and the workgroup stages the Kh rows in LDS for the transposed reads of
 // the state update.  At VT = 32 a workgroup needs about 71 KB of LDS, so two share a CU.
-// Four barriers per chunk: Kt rows and the state copy written; X written; U written;
+// Four barriers per chunk: Kh rows and the state copy written; X written; U written;
 // every wave done with the chunk's LDS.
 #include "gdn2_chunk.h"
 #include "gdn2_kernels.h"
@@ -48,10 +49,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
     constexpr int PK = DK + 8;             // row pitch of [row][channel] bf16 tiles
     constexpr int PT = kChunk + 8;         // row pitch of [col][token] bf16 tiles
     constexpr int RK = kChunk * PK;        // one [token][channel] plane
-    constexpr int NKT = 2 * kChunk * DK / 8 / kThreads;   // 16-byte pieces per thread of the Kt planes
-    static_assert(NKT * kThreads * 8 == 2 * kChunk * DK, "Kt planes split evenly over the threads");
+    constexpr int NKT = 2 * kChunk * DK / 8 / kThreads;   // 16-byte pieces per thread of the Kh planes
+    static_assert(NKT * kThreads * 8 == 2 * kChunk * DK, "Kh planes split evenly over the threads");
 
-    __shared__ __align__(16) __bf16 sK[2 * RK];         // Kt rows [token][channel] (hi, lo)
+    __shared__ __align__(16) __bf16 sK[2 * RK];         // Kh rows [token][channel] (hi, lo)
     __shared__ __align__(16) __bf16 sS[2 * VT * PK];    // S^T [col][channel] (hi, lo)
     __shared__ __align__(16) __bf16 sX[2 * VT * PT];    // X^T [col][token] (hi, lo)
     __shared__ __align__(16) __bf16 sU[2 * VT * PT];    // U^T [col][token] (hi, lo)
@@ -106,11 +107,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
             }
         }
 
-        // ---- loads: Kt rows (for LDS), this wave's A operands, gamma, z = w * v ----
+        // ---- loads: Kh rows (for LDS), this wave's A operands, gamma, z = w * v ----
         uint4 kraw[NKT];
 #pragma unroll
         for (int it = 0; it < NKT; ++it)
-            kraw[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKt + (size_t)(tid + kThreads * it) * 16);
+            kraw[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKh + (size_t)(tid + kThreads * it) * 16);
         // Et, Qt rows 16w + r, channels 32j + 8g .. + 7 (the contraction order of the S reads)
         Split8 Et[NKS], Qt[NKS];
 #pragma unroll
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
                 z[n][i] = tv < T ? zz : 0.f;
             }
 
-        // ---- Kt rows into LDS (pitch PK); with the state copy of the previous chunk's end ----
+        // ---- Kh rows into LDS (pitch PK); with the state copy of the previous chunk's end ----
 #pragma unroll
         for (int it = 0; it < NKT; ++it) {
             const int idx = tid + kThreads * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
@@ -237,20 +238,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
             }
         }
 
-        // ---- S' = diag(gamma) (S + Kt^T U), this wave's tiles of S ----
+        // ---- S' = diag(gamma) S + Kh^T U, this wave's tiles of S ----
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
             const int id = w * NTS + s, m = id / NVT, n = id % NVT;
-            f32x4 acc = S[s];
+            f32x4 acc = S[s] * gam[s];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const Split8 kh = frag_tr<PK>(sK, sK + RK, 32 * kk, 16 * m, r, g);   // Kt^T
+                const Split8 kh = frag_tr<PK>(sK, sK + RK, 32 * kk, 16 * m, r, g);   // Kh^T
                 const __bf16 *uh = &sU[(16 * n + r) * PT + 32 * kk];
                 const __bf16 *ul = &sU[VT * PT + (16 * n + r) * PT + 32 * kk];
                 acc = mfma32x3(kh, frag_2x4(uh + 4 * g, uh + 16 + 4 * g, ul + 4 * g, ul + 16 + 4 * g), acc);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[s][i];
+            S[s] = acc;
             GDN2_SWEEP_FENCE();
         }
         __syncthreads();   // every wave is done with sK, sS, sX and sU of this chunk
@@ -274,20 +274,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 // With 32-column tiles the four workgroups of a (batch, head) each read the whole
 // record of every chunk, and every wave its own copy of the Et and Qt rows, right when
 // the chunk starts; the sweep then waits on those loads.  Here a workgroup of eight
-// waves takes 64 columns (half the record reads per head), stages the Kt, Et and Qt
+// waves takes 64 columns (half the record reads per head), stages the Kh, Et and Qt
 // rows in LDS once for all waves, and loads each chunk's rows and value inputs while
 // the previous chunk is in its products:
-//   chunk c start      issue Kt rows, v, w of chunk c + 1
+//   chunk c start      issue Kh rows, v, w of chunk c + 1
 //   [A] X, Qt S        (Et, Qt rows and S from LDS)                 barrier
 //   [B] U = T X        issue T of chunk c + 1; Et, Qt rows of chunk c + 1 into LDS
 //                                                                    barrier
 //   [C] O; S'          issue Et, Qt rows of chunk c + 2; after O, P of chunk c + 1;
 //                      after S', gamma of chunk c + 1; S' into LDS   barrier
-//   Kt rows of chunk c + 1 into LDS
+//   Kh rows of chunk c + 1 into LDS
 // Wave (hf, w) owns tokens 16w..16w+15 and columns 32hf..32hf+31 of X, U and O, and
 // the state tiles of one 16-row block (at DK = 128).  bf16 q/k/v only (the X product
 // uses the hi part of Et, so one Et plane is staged); about 155 KB of LDS.
-// LDS arrays of the wide sweep (bf16 elements): Kt rows [token][channel] (hi, lo), Et rows (hi),
+// LDS arrays of the wide sweep (bf16 elements): Kh rows [token][channel] (hi, lo), Et rows (hi),
 // Qt rows (hi, lo; only when o is written), S^T [col][channel], X^T and U^T [col][token] (hi, lo)
 template <int DK, bool OUT, int VT = 64>
 struct Sweep64Lds {
@@ -310,7 +310,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
     static_assert((NMT * NCB) % 8 == 0 && NCB % NTS == 0, "a wave's state tiles share one row block");
     constexpr int PK = DK + 8, PT = kChunk + 8, RK = kChunk * PK;
     constexpr int PL16 = kChunk * DK / 8;                // 16-byte pieces of one row plane
-    constexpr int NKP = 2 * PL16 / NTH;                  // Kt pieces per thread
+    constexpr int NKP = 2 * PL16 / NTH;                  // Kh pieces per thread
     constexpr int NEQ = 1 + (OUT ? 2 : 0);               // Et hi, Qt hi and lo
     constexpr int NEP = NEQ * PL16 / NTH;                // Et/Qt pieces per thread
     static_assert(NKP * NTH == 2 * PL16 && NEP * NTH == NEQ * PL16, "row planes split evenly");
@@ -337,9 +337,9 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
     const float zon = ident ? 0.f : 1.f;                // z = w * v, zero on identity tiles
     const char *recs = reinterpret_cast<const char *>(a.records) + (size_t)bh * NC * Rec::BYTES;
 
-    // record pieces of the Kt planes and of the Et/Qt planes, and where they go in LDS
+    // record pieces of the Kh planes and of the Et/Qt planes, and where they go in LDS
     auto kt_piece = [&](int c, int it, int tid) {
-        return *reinterpret_cast<const uint4 *>(recs + (size_t)c * Rec::BYTES + Rec::oKt +
+        return *reinterpret_cast<const uint4 *>(recs + (size_t)c * Rec::BYTES + Rec::oKh +
                                                  (size_t)(tid + NTH * it) * 16);
     };
     auto kt_store = [&](const uint4 &u, int it, int tid) {
@@ -472,7 +472,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         const int cn = c + 1 < c_hi ? c + 1 : c;         // the next chunk (itself at the end)
         const int cn2 = c + 2 < c_hi ? c + 2 : cn;       // the one after
 
-        // ---- loads: Kt rows, v, w of the next chunk (T, P and gamma of this one are in flight) ----
+        // ---- loads: Kh rows, v, w of the next chunk (T, P and gamma of this one are in flight) ----
         uint4 ktn[NKP];
 #pragma unroll
         for (int it = 0; it < NKP; ++it) ktn[it] = kt_piece(cn, it, tid);
@@ -547,7 +547,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         }
         __syncthreads();
 
-        // ---- [C] O = Qt S + P U; S' = diag(gamma) (S + Kt^T U) ----
+        // ---- [C] O = Qt S + P U; S' = diag(gamma) S + Kh^T U ----
 #pragma unroll
         for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(cn2, it, tid);
         if (OUT) {
@@ -583,21 +583,20 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
             const int id = wv * NTS + s, m = id / NCB, n = id % NCB;
-            f32x4 acc = S[s];
+            f32x4 acc = S[s] * gam;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const Split8 kh = frag_tr<PK>(sK, sK + RK, 32 * kk, 16 * m, r, g);   // Kt^T
+                const Split8 kh = frag_tr<PK>(sK, sK + RK, 32 * kk, 16 * m, r, g);   // Kh^T
                 const __bf16 *uh = &sU[(16 * n + r) * PT + 32 * kk];
                 const __bf16 *ul = &sU[VT * PT + (16 * n + r) * PT + 32 * kk];
                 acc = mfma32x3(kh, frag_2x4(uh + 4 * g, uh + 16 + 4 * g, ul + 4 * g, ul + 16 + 4 * g), acc);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[s][i] = acc[i] * gam[i];
+            S[s] = acc;
         }
         gam = load_gam(recs + (size_t)cn * Rec::BYTES);
         store_state_lds(wv, r, g);     // sS is not read again in this chunk
         __syncthreads();
-        // the next chunk's Kt rows (sK is not read again in this chunk) and its z = w * v,
+        // the next chunk's Kh rows (sK is not read again in this chunk) and its z = w * v,
         // from loads issued at this chunk's start
         if (c + 1 < c_hi) {
 #pragma unroll
@@ -726,6 +725,15 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const float *E, const 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+
+// Value-tile width of the four-wave sweep: 32 columns (two workgroups share a CU), 16 where that
+// gives too few workgroups (aiming at 512 or more).
+int fwd_value_tile(int B, int H, int dk, int dv) {
+    auto ok = [&](int vt) { return vt <= dv && dv % vt == 0 && ((dk / 16) * (vt / 16)) % 4 == 0; };
+    int vt = dv < 32 ? dv : 32;
+    while (vt > 16 && (long)B * H * (dv / vt) < 512 && ok(vt / 2)) vt /= 2;
+    return vt;
+}
 
 template <int DK, int VT, bool BF16, bool GL, bool SG, int MODE>
 static hipError_t sweep_t(const FwdArgs &a, hipStream_t st) {

@@ -50,21 +50,29 @@ def test_shape_struct_matches_header():
     assert ctypes.sizeof(gdn2.Gdn2Shape) == 4 * len(fields)
 
 
+def _flags(items):
+    # one strong-decay flag (int) per chunk after the records, rounded up to 256 bytes
+    return (items * 4 + 255) // 256 * 256
+
+
+# per chunk: the chunk operand record (Kh, Et, Qt rows and T split in bf16, 16 P^T and 16 P
+# fragment tiles, the decay prefix, gamma; rounded up to 256)
+RECORD = (6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4 + 255) // 256 * 256
+
+
 def test_workspace_and_state_sizes():
     lib = gdn2.load()
     s = _shape()
     nc = (100 + 63) // 64
     one = 2 * 3 * nc * 128 * 64 * 4
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(s)) == one
-    # per chunk: the adjoint factors R, Q2^T, then the chunk operand record (Kt, Et, Qt rows
-    # and T split in bf16, 16 P^T and 16 P fragment tiles, the decay prefix, gamma; rounded
-    # up to 256)
-    record = 6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4
-    record = (record + 255) // 256 * 256
-    factors = 2 * 3 * nc * ((128 * 128 + 64 * 128) * 4 + record)
+    # per chunk: the adjoint factors R, Q2^T, then the chunk operand records, then the flags
+    items = 2 * 3 * nc
+    factors = items * ((128 * 128 + 64 * 128) * 4 + RECORD) + _flags(items)
     assert lib.gdn2_chunk_factors_bytes(ctypes.byref(s)) == factors
     assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(s)) == 2 * one + factors
-    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == 2 * 3 * nc * record   # forward-only records
+    # forward-only records and their flags
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == items * RECORD + _flags(items)
     bad = _shape(dk=96)
     assert lib.gdn2_chunk_states_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
     # the widest rows accepted: H * max(dk, dv) just under 2^24
@@ -138,8 +146,6 @@ def test_staged_entry_points_check_arguments():
     lib = gdn2.load()
     s = _shape()
     f = P(0x10000)
-    assert lib.gdn2_chunk_fwd_states(ctypes.byref(s), f, f, f, f, f, f, None, f, None, None, None) == INVALID
-    assert lib.gdn2_chunk_states(ctypes.byref(s), f, f, f, f, f, None, None, None) == INVALID
     assert lib.gdn2_chunk_bwd_factors(ctypes.byref(s), f, f, f, f, None, None) == INVALID
     assert lib.gdn2_chunk_bwd_factors(ctypes.byref(s), f, f, f, P(0x10008), f, None) == INVALID
     assert lib.gdn2_chunk_bwd_reverse(ctypes.byref(s), f, f, None, None, None, None) == INVALID
@@ -244,16 +250,16 @@ def test_factored_forward_checks_arguments():
     assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, f, P(0x10004), None, f, None, None, None) == INVALID
 
 
-def test_forward_workspace_on_wide_shapes():
-    """With bf16 q/k/v, dk 64 or 128 and dv a multiple of 64, the forward writes forward-only
-    chunk records first: it needs a workspace of one record per (batch, head, chunk)."""
+def test_forward_workspace():
+    """The forward writes forward-only chunk records first: it needs a workspace of one record
+    per (batch, head, chunk) and their flags.  The segment expectations assume 256 CUs, the
+    count the library takes when no device answers."""
     lib = gdn2.load()
     f = P(0x10000)
+    record = RECORD
     wide = _shape(B=8, T=2048, H=16, dk=128, dv=128)
-    record = 6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4
-    record = (record + 255) // 256 * 256
     need = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(wide))
-    assert need == 8 * 16 * 32 * record
+    assert need == 8 * 16 * 32 * record + _flags(8 * 16 * 32)
     F = ctypes.c_size_t
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, None, F(0), None) == WORKSPACE
     assert lib.gdn2_chunk_fwd(ctypes.byref(wide), f, f, f, f, f, f, None, f, None, f, F(need - 1), None) == WORKSPACE
@@ -262,21 +268,27 @@ def test_forward_workspace_on_wide_shapes():
     # states follow the records
     seg = 1 * 16 * 8 * 128 * ((128 + 128) + 128) * 4
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=16384, H=16, dk=128, dv=128))) == \
-        1 * 16 * 256 * record + seg
+        1 * 16 * 256 * record + _flags(16 * 256) + seg
     # the one-call backward splits its state sweep the same way: the same blocks after the
     # states, their gradients and the factor buffer
     long = _shape(B=1, T=16384, H=16, dk=128, dv=128)
     states = 16 * 256 * 128 * 128 * 4
-    factors = 16 * 256 * ((128 * 128 + 64 * 128) * 4 + record)
+    factors = 16 * 256 * ((128 * 128 + 64 * 128) * 4 + record) + _flags(16 * 256)
     assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(long)) == 2 * states + factors + seg
     # few heads but a short sequence (under 64 chunks): no segments
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=1, T=4000, H=16, dk=128, dv=128))) == \
-        1 * 16 * 63 * record
+        1 * 16 * 63 * record + _flags(16 * 63)
     short = _shape(B=1, T=4000, H=16, dk=128, dv=128)
     assert lib.gdn2_chunk_bwd_workspace_size(ctypes.byref(short)) == \
-        2 * 16 * 63 * 128 * 128 * 4 + 16 * 63 * ((128 * 128 + 64 * 128) * 4 + record)
-    # fp32 q/k/v, dk = 32, or dv not a multiple of 64: one fused sweep, no workspace
-    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0))) == 0
-    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == 0
-    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=32))) == 0
+        2 * 16 * 63 * 128 * 128 * 4 + 16 * 63 * ((128 * 128 + 64 * 128) * 4 + record) + _flags(16 * 63)
+    # fp32 q/k/v and dv not a multiple of 64: the same records, swept by the four-wave sweep
+    items = 8 * 16 * 32
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0))) == \
+        items * record + _flags(items)
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=32))) == \
+        items * record + _flags(items)
+    # dk = 32: the smaller record of that width
+    rec32 = (6 * 64 * 32 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 32 * 4 + 32 * 4 + 255) // 256 * 256
+    assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == \
+        items * rec32 + _flags(items)
 

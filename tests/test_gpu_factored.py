@@ -13,7 +13,7 @@ import torch
 import oracle
 import linear_attention_sequence_gdn2_amd as gdn2
 from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_inputs, make_workload
-from _util import oracle_args, rel_err, to_dev
+from _util import device_cus, oracle_args, rel_err, sweeps_fuse, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -148,7 +148,7 @@ def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
     o_f, sf_f, _ = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"], want_states=False)
     o_i, sf_i = gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
     torch.cuda.synchronize()
-    if B * H * (dv // 64) >= 256:
+    if B * H * (dv // 64) >= device_cus():
         assert torch.equal(states, st2)
     else:   # the states-only sweep takes the four-wave kernel below full occupancy
         assert float((states - st2).abs().max()) <= 1e-3 * float(st2.abs().max())
@@ -166,7 +166,8 @@ def test_factored_forward_wide_tiles(B, T, H, dk, dv, extra):
     (4, 150, 16, 128, 128, {"gates": "gdn", "token_gates": True}),
 ])
 def test_factored_forward_32_column_tiles(B, T, H, dk, dv, extra):
-    assert 2 * B * H * (dv // 64) <= 256
+    if 2 * B * H * (dv // 64) > device_cus():
+        pytest.skip("32-column tiles are taken at most at half the CUs of this device")
     test_factored_forward_wide_tiles(B, T, H, dk, dv, extra)
 
 
@@ -187,7 +188,8 @@ def test_factored_forward_32_column_tiles(B, T, H, dk, dv, extra):
 def test_sweeps_entry_matches_separate_calls(B, T, H, dk, dv, extra, one):
     inp = make_inputs(B, T, H, dk, dv, seed=B * 31 + T + H + dk, grads=True, **extra)
     d = to_dev(inp)
-    assert gdn2.sweeps_fused(B, T, H, dk, dv, d["q"].dtype) == one
+    assert one == sweeps_fuse(B, H, dk, dv, inp["q"].dtype == torch.bfloat16) or device_cus() != 256
+    assert gdn2.sweeps_fused(B, T, H, dk, dv, d["q"].dtype) == sweeps_fuse(B, H, dk, dv, inp["q"].dtype == torch.bfloat16)
     factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
     o, sf, st, dst, dS0 = gdn2.sweeps(factors, d["v"], d["w"], dk, d["S0"], d["dO"], d["dS_final"])
     o2, sf2, st2 = gdn2.fwd_factored(factors, d["v"], d["w"], dk, d["S0"])
@@ -202,7 +204,7 @@ def test_training_chain_through_fused_sweeps():
     against the oracle's forward and gradients."""
     inp = make_inputs(4, 333, 16, 128, 128, seed=4714, s0_std=0.05, grads=True)
     d = to_dev(inp)
-    assert gdn2.sweeps_fused(4, 333, 16, 128, 128)
+    assert gdn2.sweeps_fused(4, 333, 16, 128, 128) == sweeps_fuse(4, 16, 128, 128)
     factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])
     o, sf, states, dstates, dS0 = gdn2.sweeps(factors, d["v"], d["w"], 128, d["S0"], d["dO"], d["dS_final"])
     g = gdn2.bwd_grads(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["dO"], states, dstates, factors)
@@ -227,7 +229,7 @@ def test_sweeps_entry_optional_arguments(with_s0, with_dsf, want_state, want_dS0
     B, T, H, dk, dv = 2, 140, 8, 128, 128
     inp = make_inputs(B, T, H, dk, dv, seed=4715, s0_std=0.1, grads=True)
     d = to_dev(inp)
-    assert gdn2.sweeps_fused(B, T, H, dk, dv)
+    assert gdn2.sweeps_fused(B, T, H, dk, dv) == sweeps_fuse(B, H, dk, dv)
     S0 = d["S0"] if with_s0 else None
     dsf = d["dS_final"] if with_dsf else None
     factors = gdn2.bwd_factors(d["q"], d["k"], d["log_alpha"], d["b"])

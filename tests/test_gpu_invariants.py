@@ -37,16 +37,15 @@ def test_staged_forward_and_backward_match_one_call_forms():
     # the training forward from the factors (o and states)
     o3, s3, st3 = gdn2.fwd_factored(factors, d["v"], d["w"], 128, d["S0"])
     torch.cuda.synchronize()
-    # fwd_states and chunk_states run the same fused sweep; the inference forward takes the
-    # record path where it applies (checked against the fused one below, up to rounding)
-    assert torch.equal(states, st2)
+    # fwd_states sweeps o and the states, chunk_states the states alone (a narrower kernel where
+    # there are few heads): equal up to rounding
+    assert float((states - st2).abs().max()) <= 1e-3 * float(st2.abs().max())
     # the one-call backward is exactly this chain (same kernels, same inputs)
     for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"):
         assert torch.equal(g1[n], g2[n]), n
         assert torch.equal(g4[n], g2[n]), n
-    # the fused forward, the o + states sweep and the states-only sweep (which takes narrower
-    # tiles when there are few heads) form their products in different kernels: equal up to
-    # rounding
+    # the inference forward (forward-only records), the o + states sweep and the states-only
+    # sweep (which takes narrower tiles when there are few heads): equal up to rounding
     for x, y in ((o1, o2), (s1, s2), (o1, o3), (s1, s3), (states, st3), (st_s, st3)):
         assert float((x - y).abs().max()) <= 1e-3 * float(y.abs().max())
     # states[0] is the start state
@@ -129,7 +128,7 @@ def test_every_output_is_written_over_poisoned_memory(monkeypatch):
         return t
 
     monkeypatch.setattr(torch, "empty", poisoned_empty)
-    for qkv, dv in (("bf16", 128), ("f32", 64), ("bf16", 32)):   # record path, fused sweep, narrow tiles
+    for qkv, dv in (("bf16", 128), ("f32", 64), ("bf16", 32)):   # wide sweep, fp32 sweep, narrow tiles
         d = _dev(B=2, T=150, H=3, dk=128, dv=dv, seed=31, qkv=qkv)
         outs = list(gdn2.fwd(*_fargs(d)))
         outs += list(gdn2.fwd_states(*_fargs(d)))

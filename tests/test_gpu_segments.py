@@ -4,8 +4,8 @@ by side.  It sweeps every segment's state map from zero and identity starts, com
 in order (S_{s+1} = M_s S_s + N_s) and sweeps again from the true start states.  Checked against
 the fp64 oracle (3e-3, bf16) and against the unsegmented factored sweep (1e-3) on ragged T, with
 and without S0, both key widths and every gate format.  The one-call backward (gdn2_chunk_bwd)
-splits its state sweep the same way: its gradients are checked against the oracle's (5e-3) and
-against the unsegmented chain of entry points (1e-3)."""
+splits its state sweep the same way: its gradients are checked against the oracle's (5e-3), for
+every gate format, and against the unsegmented chain of entry points (1e-3)."""
 import ctypes
 
 import pytest
@@ -14,7 +14,7 @@ import torch
 import oracle
 import linear_attention_sequence_gdn2_amd as gdn2
 from linear_attention_sequence_gdn2_amd.inputs import make_inputs
-from _util import oracle_args, rel_err, to_dev
+from _util import device_cus, flags_bytes, oracle_args, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,9 +47,12 @@ def test_segmented_forward(B, T, H, dk, dv, extra):
     nc = (T + 63) // 64
     rec = 6 * 64 * dk * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * dk * 4 + dk * 4
     rec = (rec + 255) // 256 * 256
-    nseg = -(-nc // -(-nc // min(256 // (B * H * dv // 64), nc // 8)))
+    cus = device_cus()
+    assert B * H * (dv // 64) * 4 <= cus, "the shape is meant to take the segmented path"
+    nseg = -(-nc // -(-nc // min(cus // (B * H * dv // 64), nc // 8)))
     seg_bytes = B * H * nseg * dk * ((dv + dk) + dv) * 4
-    assert gdn2.load().gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == B * H * nc * rec + seg_bytes
+    assert gdn2.load().gdn2_chunk_fwd_workspace_size(ctypes.byref(s)) == \
+        B * H * nc * rec + flags_bytes(B * H * nc) + seg_bytes
     inp = make_inputs(B, T, H, dk, dv, seed=9300 + T + dk + dv, **extra)
     d = to_dev(inp)
     o, sf = gdn2.fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
@@ -88,9 +91,12 @@ def test_segmented_backward(B, T, H, dk, dv, extra):
     for n in NAMES:
         x, y = g[n], g2[n]
         assert float((x - y).abs().max()) <= 1e-3 * float(y.abs().max()), n
-    if extra.get("gate_logits") or extra.get("token_gates"):
-        return   # the gate formats' oracle gradients are checked on the unsegmented path
-    ref = oracle.bwd(*oracle_args(inp), inp["dO"], inp["dS_final"])
+    # the oracle's gradients, taken to the logits or summed over a per-token gate's channels
+    ref = oracle.bwd(*_oracle_inputs(inp), inp["dO"], inp["dS_final"])
+    if extra.get("gate_logits"):
+        ref = oracle.logit_grads(inp["log_alpha"], inp["b"], inp["w"], ref)
+    elif extra.get("token_gates"):
+        ref = oracle.per_token_grads(ref, inp["gate_scalar"])
     errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
     print(" ".join("%s=%.2e" % kv for kv in errs.items()))
     bad = {n: e for n, e in errs.items() if not e < 5e-3}
