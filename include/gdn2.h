@@ -69,7 +69,8 @@ typedef enum {
     GDN2_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, misaligned pointer */
     GDN2_ERR_UNSUPPORTED = 2,   /* valid request outside the supported sizes/dtypes */
     GDN2_ERR_WORKSPACE = 3,     /* workspace smaller than *_workspace_size() or NULL */
-    GDN2_ERR_HIP = 4            /* the HIP runtime reported an error at launch */
+    GDN2_ERR_HIP = 4,           /* the HIP runtime reported an error at launch */
+    GDN2_ERR_SCRATCH = 5        /* gdn2_chunk_fwd_noalloc: larger than its static scratch */
 } gdn2_status;
 
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
@@ -276,6 +277,33 @@ size_t gdn2_output_bwd_workspace_size(const gdn2_shape *shape);
 int gdn2_output_bwd(const gdn2_shape *shape, const float *o, const void *g, int g_dtype,
                     const float *weight, float eps, const float *dy, float *dO, float *dg,
                     float *dweight, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- forward without allocation ----
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  gdn2_chunk_fwd_noalloc computes exactly
+ * what gdn2_chunk_fwd computes (same arguments minus the workspace, same kernels), with the
+ * chunk records in a static device array inside the library instead of a caller-given
+ * workspace; it calls no hipMalloc, hipFree or allocating routine.
+ * - Limit: the array holds gdn2_chunk_fwd_noalloc_max_bytes() = 256 MiB on each GPU, from
+ *   the first call on that GPU until the process ends.  The batch is processed in groups of
+ *   batch elements whose records fit (gdn2_chunk_fwd_workspace_size of the group); a shape
+ *   whose single batch element needs more than the array (at dk = 128 about 181 KB per head
+ *   and 64 tokens, so H * T up to about 94,000) returns GDN2_ERR_SCRATCH before any launch.
+ * - The array is shared by every call on a GPU and keeps the last call's contents (nothing in
+ *   it needs clearing: every call writes all it reads).  Calls that overlap on one GPU, on
+ *   any streams, race on it and must be serialised by the caller.
+ * - The kernels run on the current device (the stream must belong to it); its copy of the
+ *   array is looked up once per device, on the first call there.
+ * Errors as gdn2_chunk_fwd, plus GDN2_ERR_SCRATCH; GDN2_ERR_HIP if the array's address
+ * cannot be obtained. */
+int gdn2_chunk_fwd_noalloc(const gdn2_shape *shape,
+                           const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *b, const void *w,
+                           const float *S0, float *o, float *S_final, void *stream);
+
+/* Bytes of the static scratch array of gdn2_chunk_fwd_noalloc on each GPU. */
+size_t gdn2_chunk_fwd_noalloc_max_bytes(void);
 
 /* Static, human-readable description of a gdn2_status value. */
 const char *gdn2_strerror(int status);

@@ -28,13 +28,14 @@ GDN2_GATES_F32 = 0
 GDN2_GATES_BF16_LOGITS = 1
 GDN2_SCALAR_DECAY, GDN2_SCALAR_ERASE, GDN2_SCALAR_WRITE = 1, 2, 4
 STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_INVALID_ARG", 2: "GDN2_ERR_UNSUPPORTED", 3: "GDN2_ERR_WORKSPACE",
-          4: "GDN2_ERR_HIP"}
+          4: "GDN2_ERR_HIP", 5: "GDN2_ERR_SCRATCH"}
 EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_workspace_size", "gdn2_strerror", "gdn2_chunk_states_bytes",
            "gdn2_chunk_factors_bytes", "gdn2_chunk_bwd_factors",
            "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step", "gdn2_output_fwd",
            "gdn2_output_bwd_workspace_size", "gdn2_output_bwd", "gdn2_chunk_fwd_factored",
-           "gdn2_chunk_sweeps", "gdn2_chunk_sweeps_fused"]
+           "gdn2_chunk_sweeps", "gdn2_chunk_sweeps_fused", "gdn2_chunk_fwd_noalloc",
+           "gdn2_chunk_fwd_noalloc_max_bytes"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -66,6 +67,10 @@ def load():
         lib.gdn2_chunk_fwd.restype = ctypes.c_int
         lib.gdn2_chunk_bwd.argtypes = [SP] + [P] * 16 + [P, ctypes.c_size_t, P]
         lib.gdn2_chunk_bwd.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_noalloc.argtypes = [SP] + [P] * 9 + [P]
+        lib.gdn2_chunk_fwd_noalloc.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_noalloc_max_bytes.argtypes = []
+        lib.gdn2_chunk_fwd_noalloc_max_bytes.restype = ctypes.c_size_t
         lib.gdn2_chunk_fwd_workspace_size.argtypes = [SP]
         lib.gdn2_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         lib.gdn2_chunk_bwd_workspace_size.argtypes = [SP]
@@ -197,6 +202,26 @@ def fwd(q, k, v, log_alpha, b, w, S0=None, want_state=True):
     _check(lib.gdn2_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
                               _ptr(w), _ptr(S0), _ptr(o), _ptr(sf), _ptr(ws), ws_bytes, _stream(q.device)))
     return o, sf
+
+
+def fwd_noalloc(q, k, v, log_alpha, b, w, S0=None, want_state=True, o=None, S_final=None):
+    """gdn2_chunk_fwd_noalloc: the forward with the chunk records in the library's static
+    scratch (no workspace).  o and S_final may be given (preallocated outputs)."""
+    B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (S0,))
+    if S0 is not None and (tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("gdn2: S0 must be float32 [B,H,dk,dv]")
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for t, shp in ((o, (B, T, H, dv)), (S_final, (B, H, dk, dv))):
+        if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("gdn2: outputs must be contiguous float32 of the output shapes")
+    _check(lib.gdn2_chunk_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                      _ptr(w), _ptr(S0), _ptr(o), _ptr(S_final), _stream(q.device)))
+    return o, S_final
 
 
 def bwd_workspace_bytes(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32, gate_scalar=0):

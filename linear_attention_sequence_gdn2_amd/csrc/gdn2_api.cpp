@@ -104,6 +104,7 @@ const char *gdn2_strerror(int status) {
         case GDN2_ERR_UNSUPPORTED: return "unsupported shape or dtype (chunk must be 64, dk/dv in {32,64,128})";
         case GDN2_ERR_WORKSPACE: return "workspace missing or smaller than the required size";
         case GDN2_ERR_HIP: return "HIP runtime error at kernel launch";
+        case GDN2_ERR_SCRATCH: return "request larger than the static scratch of gdn2_chunk_fwd_noalloc";
         default: return "unknown gdn2 status";
     }
 }

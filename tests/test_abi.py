@@ -171,8 +171,8 @@ def test_step_checks_arguments():
 
 def test_strerror_covers_every_status():
     lib = gdn2.load()
-    msgs = {lib.gdn2_strerror(c).decode() for c in range(5)}
-    assert len(msgs) == 5
+    msgs = {lib.gdn2_strerror(c).decode() for c in range(6)}
+    assert len(msgs) == 6
     assert "unknown" in lib.gdn2_strerror(99).decode()
 
 
