@@ -13,9 +13,13 @@ already resident in HBM when the timed region starts.
 
 Prints one JSON line (rank 0):
   value        tokens/s of whole steps (tokens = B*T per step)
-  roofline     for the dominant kernel: algorithmic bytes per launch / its
-               average launch time (HIP events on the stream it runs on),
-               against MI355X HBM3E 8 TB/s
+  roofline     for the dominant kernel (the chunk-gradient launch, which reads the backward's
+               inputs and writes all six token gradients): the backward pass's compulsory HBM
+               bytes (5,888 per token-head: q, k, v, the three gates, dO, six fp32 gradients) per
+               launch / its average launch time (HIP events on the stream it runs on), against
+               MI355X HBM3E 8 TB/s and against a device copy measured in the same run; `traffic`
+               is the launch's HBM bytes from the committed rocprofv3 counters, `design_bytes`
+               what the launch reads and writes by design (its records, states and dstates too)
   cpu_baseline the fp64 oracle (fwd + bwd) timed on the host's cores on a
                bounded sample of the same workload
 """
@@ -31,7 +35,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-WORKLOAD = "fwd_bf16_B8H16T2048d128"
+WORKLOAD = "train_bf16_B8H16T2048d128"
+METRIC = "GDN-2 chunk fwd(+bwd) tokens/s, H=16 dk=dv=128 B8\u00d7T2K; % of MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 # algorithmic HBM bytes per token-head (bf16 q/k/v, fp32 gates, o and gradients):
 #   forward : q,k,v 3*256 + log_alpha,b,w 3*512 + o 512              = 2816
@@ -98,6 +103,44 @@ def _traffic(kernel_key, launches_bytes):
     return k.get("hbm_bytes_per_launch")
 
 
+def copy_bench(dev, mib=1024, iters=10):
+    """A plain device copy of `mib` MiB (torch's copy kernel), HIP events: (read + write bytes)
+    per second, the rate a stream that is half reads and half writes reaches on this device."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def _host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    return {"host_nproc": os.cpu_count(), "affinity_cpus": aff, "cpu_model": model}
+
+
 def cpu_baseline(wl, sample_batches):
     import numpy as np  # noqa: F401
     import oracle
@@ -113,10 +156,13 @@ def cpu_baseline(wl, sample_batches):
     oracle.bwd(*args, dO, dsf, nthreads=nthreads)
     dt = time.perf_counter() - t0
     tokens = sample_batches * wl.T
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": min(nthreads, sample_batches * wl.H),
-            "kind": "oracle",
-            "sample": "fp64 token-by-token oracle, fwd + bwd, B=%d of %d batches (T=%d, H=%d, d=%d), %.1f s"
-                      % (sample_batches, wl.B, wl.T, wl.H, wl.dk, dt)}
+    out = {"value": tokens / dt, "unit": "tokens/s", "cores": min(nthreads, sample_batches * wl.H),
+           "kind": "oracle",
+           "sample": "fp64 token-by-token oracle, fwd + bwd, B=%d of %d batches (T=%d, H=%d, d=%d), %.1f s; "
+                     "threads over (batch, head) pairs: every CPU of the affinity mask, at most 16 (one "
+                     "GPU's share of the host's CPUs)" % (sample_batches, wl.B, wl.T, wl.H, wl.dk, dt)}
+    out.update(_host_cpu())
+    return out
 
 
 def decode_bench(dev, B=64, H=16, dk=128, dv=128, iters=100):
@@ -176,7 +222,7 @@ def _mfma_insts(kernel_key):
     return rec.get("kernels", {}).get(kernel_key, {}).get("mfma_insts_per_launch")
 
 
-def forward_bench(dev, wl, iters=20):
+def forward_bench(dev, wl, iters=20, copy_gbs=None):
     """The inference forward gdn2_chunk_fwd (o and S_final) on the training shape, timed
     with HIP events.  At this shape it launches the forward-only chunk-record kernel, then
     the eight-wave sweep, with the records in a workspace; `hbm` counts the operator's own
@@ -203,9 +249,11 @@ def forward_bench(dev, wl, iters=20):
     kbytes = (FWD_RECORDS_BYTES_PER_TOKHEAD + FWD_INFER_SWEEP_BYTES_PER_TOKHEAD) * tokheads + state
     gbs, kgbs = nbytes / (ms * 1e-3) / 1e9, kbytes / (ms * 1e-3) / 1e9
     tfl = FWD_USEFUL_FLOPS_PER_TOKHEAD * tokheads / (ms * 1e-3) / 1e12
-    out = {"entry": "gdn2_chunk_fwd", "kernels": ["bwd_factors_kernel (forward-only records)", "fwd_sweep64_kernel"],
+    out = {"entry": "gdn2_chunk_fwd", "kernels": ["bwd_factors_kernel (forward-only records; fast and exact pass)",
+                                                  "fwd_sweep64_kernel"],
            "ms": round(ms, 4), "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
-           "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
+           "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "frac_of_copy": round(gbs / copy_gbs, 4) if copy_gbs else None},
            "hbm_with_records": {"achieved_GBs": round(kgbs, 1), "frac": round(kgbs / HBM_PEAK_GBS, 4)},
            "mfma_useful": {"achieved_TFLOPs": round(tfl, 1), "peak": MFMA_PEAK_TFLOPS,
                            "frac": round(tfl / MFMA_PEAK_TFLOPS, 4)}}
@@ -214,6 +262,172 @@ def forward_bench(dev, wl, iters=20):
         ex = (i1 + i2) * 16384 / (ms * 1e-3) / 1e12
         out["mfma_executed"] = {"achieved_TFLOPs": round(ex, 1), "frac": round(ex / MFMA_PEAK_TFLOPS, 4)}
     return out
+
+
+def lean_bench(dev, names, iters=10):
+    """The memory-lean training pair: the one-call forward (gdn2_chunk_fwd: o, S_final) and the
+    one-call backward (gdn2_chunk_bwd, which rebuilds every chunk's state from the inputs), with
+    nothing held between them but the inputs and outputs.  HIP events over `iters` pairs, and
+    the workspace each call needs."""
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_workload
+    res = {}
+    for name in names:
+        wl = WORKLOADS[name]
+        x = make_workload(wl, grads=True)
+        d = {k: (x[k].to(dev) if x[k] is not None else None)
+             for k in ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final")}
+        args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"])
+        ws = torch.empty(gdn2.bwd_workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv, torch.bfloat16), dtype=torch.uint8,
+                         device=dev)
+
+        def pair():
+            gdn2.fwd(*args)
+            return gdn2.bwd(*args, d["dO"], d["dS_final"], workspace=ws)
+
+        for _ in range(2):
+            pair()
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            pair()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        import ctypes
+        shape = gdn2.make_shape(wl.B, wl.T, wl.H, wl.dk, wl.dv, torch.bfloat16)
+        fws = gdn2.load().gdn2_chunk_fwd_workspace_size(ctypes.byref(shape))
+        res[name] = {"entries": ["gdn2_chunk_fwd", "gdn2_chunk_bwd"], "ms_per_pair": round(ms, 4),
+                     "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
+                     "fwd_workspace_bytes": int(fws), "bwd_workspace_bytes": int(ws.numel())}
+        del ws
+    return res
+
+
+# MFMA instructions per wave in each stamped phase of the forward (dk = dv = 128, 64-column sweep
+# tiles), from the loop structure of the kernels: (16x16x32 executed, products, 16x16x16 executed).
+# Wave (hf, w) of the eight: half hf, token block w; a split-bf16 product is three MFMAs (two
+# for X = Z - Et S, which takes the hi part of Et).
+def _record_phase_mfma(hf, w):
+    n_a = sum(1 for mt in range(w + 1) if (mt & 1) == hf)      # A tiles of this wave
+    ap = 12 * (n_a + w + 1)                                     # (A and P tiles) x 4 steps x 3
+    solve16 = (24 + 3 * (w * (w + 1) // 2 + w)) if hf == 0 else 0
+    return {"a5 A,P": (ap, ap // 3, 0), "a6 solve": (0, 0, solve16)}
+
+
+def _sweep_phase_mfma(hf, w):
+    nkk = 2 if w >= 2 else 1
+    return {"a7 X,QtS": (40, 16, 0), "a7 U=TX": (6 * nkk, 2 * nkk, 0), "a7 O": (6 * nkk, 2 * nkk, 0),
+            "a7 S'": (24, 8, 0)}
+
+
+RECORD_PHASES = {"a5 A,P": (2, 3), "a6 solve": (3, 4)}
+SWEEP_PHASES = {"a7 X,QtS": (0, 1), "a7 U=TX": (2, 3), "a7 O": (4, 5), "a7 S'": (5, 6)}
+MFMA_FLOPS_PER_CU_CYCLE = 4096   # 2.5 PFLOP/s / (256 CUs x 2.4 GHz), bf16 dense
+
+
+def phase_stamps(dev, wl):
+    """Per-phase MFMA use of the forward (gdn2_chunk_fwd) on the training shape, from the
+    s_memtime stamps of the instrumented library (this process must have loaded it: GDN2_LIBRARY).
+    A phase's window on a CU runs from the first of its eight waves entering to the last leaving;
+    its use is the MFMA flops all eight issue in it over window x 4096 flops per CU-cycle
+    (executed: the split products' three MFMAs; useful: one per product).  Summed over every
+    window of the launch."""
+    import ctypes
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import make_workload
+    lib = gdn2.load()
+    x = make_workload(wl)
+    d = {k: x[k].to(dev) for k in ("q", "k", "v", "log_alpha", "b", "w")}
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    nc = (wl.T + 63) // 64
+    items = wl.B * wl.H * nc
+    wgs = wl.B * wl.H * (wl.dv // 64)
+    fst = torch.zeros(items * 8 * 8, dtype=torch.int64, device=dev)
+    sst = torch.zeros(wgs * 8 * nc * 8, dtype=torch.int64, device=dev)
+    for fn in (lib.gdn2_stamps_factors, lib.gdn2_stamps_sweep):
+        fn.argtypes = [ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    for _ in range(2):
+        gdn2.fwd(*args)
+    torch.cuda.synchronize()
+    assert lib.gdn2_stamps_factors(ctypes.c_void_p(fst.data_ptr())) == 0
+    assert lib.gdn2_stamps_sweep(ctypes.c_void_p(sst.data_ptr())) == 0
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    gdn2.fwd(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    lib.gdn2_stamps_factors(ctypes.c_void_p(0))
+    lib.gdn2_stamps_sweep(ctypes.c_void_p(0))
+    f = fst.cpu().numpy().reshape(items, 8, 8).astype(np.float64)
+    sw = sst.cpu().numpy().reshape(wgs, 8, nc, 8).astype(np.float64)
+    assert (f[:, :, :6] > 0).all() and (sw[..., :8] > 0).all(), "missing stamps"
+    # the stamp counter is per XCD (no common origin across them): only differences within one
+    # workgroup are used.  A sweep workgroup lives for the whole sweep launch, one per CU.
+    sweep_span = float(np.median(sw[:, :, -1, 7].max(axis=1) - sw[:, :, 0, 0].min(axis=1)))
+    out = {"workload": wl.name, "entry": "gdn2_chunk_fwd", "forward_ms_instrumented": round(ms, 4),
+           "sweep_workgroup_span_cycles": round(sweep_span, 1), "peak_flops_per_CU_cycle": MFMA_FLOPS_PER_CU_CYCLE,
+           "target": 0.40, "phases": {}}
+
+    def phase(st, counts, lo, hi, axis_waves):
+        # st: [..., 8 waves, stamps]; window per leading index from min over waves of st[lo] to max of st[hi]
+        win = st[..., hi].max(axis=axis_waves) - st[..., lo].min(axis=axis_waves)
+        e32 = sum(c[0] for c in counts)
+        u32 = sum(c[1] for c in counts)
+        e16 = sum(c[2] for c in counts)
+        cyc = float(win.sum())
+        nwin = win.size
+        executed = (e32 * 16384 + e16 * 8192) * nwin
+        useful = (u32 * 16384 + e16 * 8192 / 3) * nwin
+        return {"window_cycles_mean": round(cyc / nwin, 1), "windows": int(nwin),
+                "mfma_executed_per_window": int(e32 + e16),
+                "executed_frac": round(executed / (cyc * MFMA_FLOPS_PER_CU_CYCLE), 4),
+                "useful_frac": round(useful / (cyc * MFMA_FLOPS_PER_CU_CYCLE), 4),
+                "share_of_launch_cycles": None}
+
+    waves = [(wv >> 2, wv & 3) for wv in range(8)]
+    rec_total = float((f[:, :, 5].max(axis=1) - f[:, :, 0].min(axis=1)).sum())
+    for name, (lo, hi) in RECORD_PHASES.items():
+        counts = [_record_phase_mfma(hf, w)[name] for hf, w in waves]
+        r = phase(f, counts, lo, hi, 1)
+        r["kernel"] = "bwd_factors_kernel (forward-only records)"
+        r["share_of_launch_cycles"] = round(r["window_cycles_mean"] * r["windows"] / rec_total, 4)
+        out["phases"][name] = r
+    sw_total = float((sw[:, :, :, 7].max(axis=1) - sw[:, :, :, 0].min(axis=1)).sum())
+    for name, (lo, hi) in SWEEP_PHASES.items():
+        counts = [_sweep_phase_mfma(hf, w)[name] for hf, w in waves]
+        r = phase(sw, counts, lo, hi, 1)
+        r["kernel"] = "fwd_sweep64_kernel"
+        r["share_of_launch_cycles"] = round(r["window_cycles_mean"] * r["windows"] / sw_total, 4)
+        out["phases"][name] = r
+    # all GEMM phases together: executed flops over the summed windows
+    ex = sum(p["executed_frac"] * p["window_cycles_mean"] * p["windows"] for p in out["phases"].values())
+    us = sum(p["useful_frac"] * p["window_cycles_mean"] * p["windows"] for p in out["phases"].values())
+    cyc = sum(p["window_cycles_mean"] * p["windows"] for p in out["phases"].values())
+    out["gemm_phases"] = {"executed_frac": round(ex / cyc, 4), "useful_frac": round(us / cyc, 4),
+                          "gap_to_target_executed": round(0.40 - ex / cyc, 4)}
+    return out
+
+
+def _phase_stamps_child():
+    """Run phase_stamps in a child process on the instrumented library; None if it is not built."""
+    import subprocess
+    lib = os.path.join(ROOT, "linear_attention_sequence_gdn2_amd", "libgdn2_stamps.so")
+    if not os.path.exists(lib):
+        return {"error": "libgdn2_stamps.so not built"}
+    env = dict(os.environ, GDN2_LIBRARY=lib)
+    p = subprocess.run([sys.executable, os.path.abspath(__file__), "--phase-stamps"], env=env,
+                       capture_output=True, text=True, timeout=300)
+    if p.returncode != 0:
+        return {"error": "phase-stamps run failed", "stderr": p.stderr[-2000:]}
+    return json.loads(p.stdout.strip().splitlines()[-1])
 
 
 # the other configurations of the operator, measured beside the headline: forward of the long
@@ -336,9 +550,14 @@ def main():
     ap.add_argument("--no-token-gates", action="store_true", help="skip the step with per-token gates")
     ap.add_argument("--no-output", action="store_true", help="skip the output epilogue measurement")
     ap.add_argument("--no-forward", action="store_true", help="skip the inference-forward measurement")
+    ap.add_argument("--no-lean", action="store_true",
+                    help="skip the one-call forward + backward (recomputing every chunk state)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the long-sequence, per-token-gate and B4 T4096 training measurements")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="only the per-phase MFMA measurement (needs GDN2_LIBRARY=<libgdn2_stamps.so>)")
+    ap.add_argument("--no-phase-stamps", action="store_true", help="skip the per-phase MFMA measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times), to calibrate "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
@@ -368,6 +587,9 @@ def main():
                           "launches": 3}))
         return
     wl = WORKLOADS[WORKLOAD]
+    if args.phase_stamps:
+        print(json.dumps(phase_stamps(dev, WORKLOADS["fwd_bf16_B8H16T2048d128"])), flush=True)
+        return
     stream = torch.cuda.current_stream(dev)
     nk = 4
 
@@ -453,14 +675,27 @@ def main():
             per_kernel[name]["mfma_executed_TFLOPs"] = round(ex, 1)
             per_kernel[name]["mfma_frac"] = round(ex / MFMA_PEAK_TFLOPS, 4)
     dom = max(range(nk), key=lambda j: k_ms[j])
-    name, entry, nbytes = kernels[dom]
+    name, entry, design = kernels[dom]
+    copy_gbs = copy_bench(dev)
+    # the compulsory bytes (inputs read once, outputs written once, per token-head) of the pass the
+    # dominant launch completes: the backward for the chunk-gradient launch, the forward for the sweep
+    compulsory = {"bwd_chunk_kernel": BWD_BYTES_PER_TOKHEAD, "fwd_sweep_kernel": FWD_BYTES_PER_TOKHEAD}
+    nbytes = compulsory.get(name, 0) * tokheads
     achieved = nbytes / (k_ms[dom] * 1e-3) / 1e9
-    roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(name, nbytes),
-            "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(k_ms[dom], 4)}
-    step_alg = (FWD_BYTES_PER_TOKHEAD + BWD_BYTES_PER_TOKHEAD) * tokheads
+    traffic = _traffic(name, design)
+    roof = {"bound": "hbm", "kernel": name, "entry": entry, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(k_ms[dom], 4),
+            "copy_GBs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
+            "design_bytes": design, "design_frac": round(design / (k_ms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic_over_algorithmic": round(traffic / nbytes, 3) if traffic and nbytes else None}
+    # the whole step against the operator's compulsory bytes: forward + backward per token-head,
+    # plus dS_final read, S_final and dS0 written
+    step_alg = (FWD_BYTES_PER_TOKHEAD + BWD_BYTES_PER_TOKHEAD) * tokheads + 3 * state_bytes
+    step_gbs = step_alg / (step_ms * 1e-3) / 1e9
+    step_design = sum(k[2] for k in kernels)
     out = {
-        "metric": "GDN-2 chunk fwd+bwd tokens/s (H=16 dk=dv=128 B8xT2K)",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -477,7 +712,11 @@ def main():
                    "parallelism": "single-gpu"},
         "breakdown": {"kernels": per_kernel, "step_event_ms": round(step_ms, 4),
                       "fwd_tokens_per_s": round(tokens / ((k_ms[0] + k_ms[1]) * 1e-3), 1),
-                      "step_algorithmic_frac": round(step_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                      "step_roofline": {"algorithmic_bytes": step_alg, "achieved_GBs": round(step_gbs, 1),
+                                        "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                                        "frac_of_copy": round(step_gbs / copy_gbs, 4),
+                                        "design_bytes": step_design,
+                                        "design_over_algorithmic": round(step_design / step_alg, 3)}},
         "roofline": roof,
     }
     if not args.no_logit_gates:
@@ -503,13 +742,17 @@ def main():
             "step_event_ms": round(tstep_ms, 4),
             "step_algorithmic_frac": round(talg / (tstep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_forward:
-        out["breakdown"]["forward_only"] = forward_bench(dev, wl)
+        out["breakdown"]["forward_only"] = forward_bench(dev, wl, copy_gbs=copy_gbs)
+    if not args.no_lean:
+        out["breakdown"]["lean_fwd_bwd"] = lean_bench(dev, ("train_bf16_B8H16T2048d128", "fwdbwd_bf16_B4H16T4096d128"))
     if not args.no_configs:
         out["breakdown"]["other_configs"] = configs_bench(dev, timed_steps)
     if not args.no_output:
         out["breakdown"]["output_epilogue"] = output_bench(dev, wl)
     if not args.no_decode:
         out["breakdown"]["decode_step"] = decode_bench(dev)
+    if not args.no_phase_stamps:
+        out["breakdown"]["phase_mfma"] = _phase_stamps_child()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_batches)
     print(json.dumps(out), flush=True)

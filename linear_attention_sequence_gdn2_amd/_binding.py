@@ -20,7 +20,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+# GDN2_LIBRARY may name another build of the same library (the phase-stamped one, for
+# instrumented measurement runs)
+LIB_PATH = os.environ.get("GDN2_LIBRARY") or os.path.join(_HERE, "libgdn2.so")
 
 GDN2_F32 = 0
 GDN2_BF16 = 1

@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn2.so")
+STAMPS_LIB = os.path.join(HERE, "libgdn2_stamps.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gdn2_api.cpp", "gdn2_bwd.hip", "gdn2_reverse.hip", "gdn2_step.hip", "gdn2_output.hip",
            "gdn2_sweep.hip", "gdn2_noalloc.cpp"]
@@ -28,31 +29,35 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-I", INCLUDE, "-I", CSRC, "-Wno-unused-result"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, extra=(), tag="") -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + tag + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), p.stderr[-8000:]))
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    """Build libgdn2.so; with stamps=True the instrumented libgdn2_stamps.so instead (-DGDN2_STAMPS:
+    the forward's kernels record s_memtime at their phase boundaries, for per-phase MFMA use)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    extra, tag = (["-DGDN2_STAMPS"], ".stamps") if stamps else ((), "")
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, extra, tag), SOURCES))
+    lib = STAMPS_LIB if stamps else LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), p.stderr[-8000:]))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, stamps="--stamps" in sys.argv[1:])
     sys.exit(0)

@@ -49,6 +49,21 @@ constexpr int kChunkThreads = 2 * kThreads;   // workgroup of the chunk-parallel
 // above this point (bounds the live registers of a wave).
 #define GDN2_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Phase stamps of the instrumented build (-DGDN2_STAMPS, libgdn2_stamps.so): lane 0 of a wave
+// writes the shader-clock counter (s_memtime) to buf[idx] when buf is set.  In the normal
+// build the macro is empty.
+#ifdef GDN2_STAMPS
+#define GDN2_STAMP(buf, idx)                                                      \
+    do {                                                                         \
+        if ((buf) != nullptr && (threadIdx.x & 63) == 0)                         \
+            (buf)[idx] = __builtin_amdgcn_s_memtime();                           \
+    } while (0)
+#else
+#define GDN2_STAMP(buf, idx) \
+    do {                     \
+    } while (0)
+#endif
+
 struct Split8 {
     bf16x8 hi, lo;
 };

@@ -26,6 +26,11 @@
 
 namespace gdn2 {
 
+#ifdef GDN2_STAMPS
+// stamps of the fast pass of the factor kernel: 8 per (item, wave), see bwd_factors_kernel
+static __device__ unsigned long long *g_factor_stamps;
+#endif
+
 // 16x16 tile from its D-layout transpose: the lane holds X[16m + r][16kb + 4g + i] (i < 4)
 __device__ __forceinline__ void store_frag_tile(__bf16 *tile, int l, const f32x4 &v) {
     const Split4 s = split4(v);
@@ -121,6 +126,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     const int nkk = (w >= 2) ? 2 : 1;
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
+#ifdef GDN2_STAMPS
+    // element phase 0-1, record rows 1-2, A and P 2-3, the solve 3-4, T 4-5, W, Q2, R 5-6
+    unsigned long long *stp = !EX && g_factor_stamps ? g_factor_stamps + ((size_t)L * 8 + wv) * 8 : nullptr;
+#else
+    unsigned long long *stp = nullptr;
+#endif
+    (void)stp;
+    GDN2_STAMP(stp, 0);
     __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
     char *rec = recs + (size_t)L * Rec::BYTES;
 
@@ -175,6 +188,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         unsafe = __syncthreads_or(strong);
     }
     if (!EX && tid == 0) flags[L] = unsafe ? 1 : 0;
+    GDN2_STAMP(stp, 1);
 
     // ---- record: Kh rows (Kt diag(gamma) from the fast pass's Kt rows; the exact pass's LDS
     // rows are Kh already), one thread per 8 channels of a row (hi and lo) ----
@@ -208,6 +222,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     }
 
     Split4 Pf[4];
+    GDN2_STAMP(stp, 2);
     if constexpr (EX) {
         // ---- A and P with the exact pairwise decays; P fp32 over the slices ----
         float *sP = sEx;
@@ -302,7 +317,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         }
         __syncthreads();
     }
+    GDN2_STAMP(stp, 3);
     solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
+    GDN2_STAMP(stp, 4);
     {
         // record: T as split bf16 [row][col], one thread per 8 elements
         static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
@@ -312,6 +329,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         *reinterpret_cast<bf16x8 *>(rec + Rec::oT + (size_t)(row * kChunk + c8) * 2) = ts.hi;
         *reinterpret_cast<bf16x8 *>(rec + Rec::oT + (size_t)(kChunk * kChunk + row * kChunk + c8) * 2) = ts.lo;
     }
+    GDN2_STAMP(stp, 5);
     if (FWD) {
         __syncthreads();   // the next item overwrites the LDS this one still reads
         continue;
@@ -386,6 +404,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         }
         store_frag_tile(fac + (size_t)(am * NM + bm) * kFragTile, l, rt);
     }
+    GDN2_STAMP(stp, 6);
     __syncthreads();   // the next item overwrites the LDS this one still reads
     }
     }
@@ -405,6 +424,15 @@ __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+#ifdef GDN2_STAMPS
+// the instrumented build only: where the factor kernel's fast pass writes its phase stamps
+// (8 per item and wave; nullptr = none)
+extern "C" int gdn2_stamps_factors(void *buf) {
+    unsigned long long *p = static_cast<unsigned long long *>(buf);
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_factor_stamps), &p, sizeof(p)) == hipSuccess ? 0 : 4;
+}
+#endif
+
 size_t record_buffer_bytes(long items, int dk) {
     switch (dk) {
         case 32: return (size_t)items * ChunkRecord<32>::BYTES + record_flags_bytes(items);

@@ -37,6 +37,11 @@ namespace gdn2 {
 
 #define GDN2_SWEEP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+#ifdef GDN2_STAMPS
+// stamps of the unsegmented wide sweep: 8 per (workgroup, wave, chunk), see fwd_sweep64_body
+static __device__ unsigned long long *g_sweep_stamps;
+#endif
+
 template <int DK, int VT, bool BF16, bool OUT, bool STATES, bool GL, bool SG>
 __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
     using Rec = ChunkRecord<DK>;
@@ -471,6 +476,14 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         const int t0 = c * kChunk;
         const int cn = c + 1 < c_hi ? c + 1 : c;         // the next chunk (itself at the end)
         const int cn2 = c + 2 < c_hi ? c + 2 : cn;       // the one after
+#ifdef GDN2_STAMPS
+        // [A] from 0 to 1, [B] 2 to 3, O 4 to 5, S' 5 to 6; 1-2, 3-4 and 6-7 are barriers
+        unsigned long long *stp = SEG == 0 && g_sweep_stamps ? g_sweep_stamps + (((size_t)L * 8 + wv) * NC + c) * 8
+                                                             : nullptr;
+#else
+        unsigned long long *stp = nullptr;
+#endif
+        (void)stp;
 
         // ---- loads: Kh rows, v, w of the next chunk (T, P and gamma of this one are in flight) ----
         uint4 ktn[NKP];
@@ -492,6 +505,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         }
 
         // ---- [A] X = Z - Et S and Qt S: tiles (token block w, column blocks 2hf, 2hf + 1) ----
+        GDN2_STAMP(stp, 0);
         f32x4 QS[CBW];
 #pragma unroll
         for (int n = 0; n < CBW; ++n) {
@@ -513,9 +527,11 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
             *reinterpret_cast<bf16x4 *>(&sX[VT * PT + (16 * cb + r) * PT + 16 * w + 4 * g]) = xs.lo;
             QS[n] = accQ;
         }
+        GDN2_STAMP(stp, 1);
         __syncthreads();
 
         // ---- [B] U = T X; then the next chunk's Et/Qt rows into LDS ----
+        GDN2_STAMP(stp, 2);
         {
             f32x4 accU[CBW];
 #pragma unroll
@@ -541,11 +557,13 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
                 *reinterpret_cast<bf16x4 *>(&sU[VT * PT + (16 * cb + r) * PT + 16 * w + 4 * g]) = us.lo;
             }
         }
+        GDN2_STAMP(stp, 3);
         if (c + 1 < c_hi) {
 #pragma unroll
             for (int it = 0; it < NEP; ++it) eq_store(eqn[it], it, tid);
         }
         __syncthreads();
+        GDN2_STAMP(stp, 4);
 
         // ---- [C] O = Qt S + P U; S' = diag(gamma) S + Kh^T U ----
 #pragma unroll
@@ -580,6 +598,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
                 }
             load_P(recs + (size_t)cn * Rec::BYTES, pv);
         }
+        GDN2_STAMP(stp, 5);
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
             const int id = wv * NTS + s, m = id / NCB, n = id % NCB;
@@ -593,9 +612,11 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
             }
             S[s] = acc;
         }
+        GDN2_STAMP(stp, 6);
         gam = load_gam(recs + (size_t)cn * Rec::BYTES);
         store_state_lds(wv, r, g);     // sS is not read again in this chunk
         __syncthreads();
+        GDN2_STAMP(stp, 7);
         // the next chunk's Kh rows (sK is not read again in this chunk) and its z = w * v,
         // from loads issued at this chunk's start
         if (c + 1 < c_hi) {
@@ -725,6 +746,14 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(const float *E, const 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
+#ifdef GDN2_STAMPS
+// the instrumented build only: where the unsegmented wide sweep writes its phase stamps
+// (8 per workgroup, wave and chunk; nullptr = none)
+extern "C" int gdn2_stamps_sweep(void *buf) {
+    unsigned long long *p = static_cast<unsigned long long *>(buf);
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_sweep_stamps), &p, sizeof(p)) == hipSuccess ? 0 : 4;
+}
+#endif
 
 // Value-tile width of the four-wave sweep: 32 columns (two workgroups share a CU), 16 where that
 // gives too few workgroups (aiming at 512 or more).

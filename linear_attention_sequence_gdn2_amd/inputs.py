@@ -76,6 +76,8 @@ WORKLOADS = {
     "tiny_f32_B1H2T128d32": Workload("tiny_f32_B1H2T128d32", 1, 128, 2, 32, 32, 1001,
                                      qkv_dtype="f32", decay="softplus"),
     "fwd_bf16_B8H16T2048d128": Workload("fwd_bf16_B8H16T2048d128", 8, 2048, 16, 128, 128, 1002),
+    # the same batch with the upstream gradients drawn too: one training step (fwd + bwd)
+    "train_bf16_B8H16T2048d128": Workload("train_bf16_B8H16T2048d128", 8, 2048, 16, 128, 128, 1002, grads=True),
     "long_bf16_B1H16T16384d128": Workload("long_bf16_B1H16T16384d128", 1, 16384, 16, 128, 128, 1003,
                                           s0_std=0.02),
     "kda_bf16_B4H16T4096d128": Workload("kda_bf16_B4H16T4096d128", 4, 4096, 16, 128, 128, 1004,
