@@ -491,6 +491,51 @@ OUT_FWD_BYTES_PER_TOKHEAD = 1024
 OUT_BWD_BYTES_PER_TOKHEAD = 2304
 
 
+def fused_output_bench(dev, wl, iters=20, copy_gbs=None):
+    """The forward with the output epilogue fused (gdn2_chunk_fwd_output: o never written)
+    against the unfused pair (gdn2_chunk_fwd, then gdn2_output_fwd), bf16 output gate, y in
+    bf16 and in fp32, on the training shape, timed with HIP events.  Compulsory bytes of the
+    fused pass: the forward's 2,816 per token-head without o's 512, plus g (256) and y (256 in
+    bf16, 512 in fp32)."""
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import make_output_inputs, make_workload
+    x = make_workload(wl)
+    d = {k: x[k].to(dev) for k in ("q", "k", "v", "log_alpha", "b", "w")}
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    ex = make_output_inputs(wl.B, wl.T, wl.H, wl.dv, seed=4344, g_dtype="bf16")
+    g, wt = ex["g"].to(dev), ex["weight"].to(dev)
+    stream = torch.cuda.current_stream(dev)
+    tokheads = wl.B * wl.T * wl.H
+    res = {"entry": "gdn2_chunk_fwd_output",
+           "fused": gdn2.fwd_output_fused(wl.B, wl.T, wl.H, wl.dk, wl.dv, torch.bfloat16)}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for yname, ydt, ybytes in (("y_bf16", torch.bfloat16, 256), ("y_f32", torch.float32, 512)):
+        ws = gdn2.fwd_output(*args, g, wt, 1e-6, out_dtype=ydt)[2]
+        fused_ms = timed(lambda: gdn2.fwd_output(*args, g, wt, 1e-6, out_dtype=ydt, workspace=ws))
+        pair_ms = timed(lambda: gdn2.output_fwd(gdn2.fwd(*args)[0], g, wt, 1e-6, out_dtype=ydt))
+        nbytes = (FWD_BYTES_PER_TOKHEAD - 512 + 256 + ybytes) * tokheads + wl.B * wl.H * wl.dk * wl.dv * 4
+        gbs = nbytes / (fused_ms * 1e-3) / 1e9
+        res[yname] = {"fused_ms": round(fused_ms, 4), "pair_ms": round(pair_ms, 4),
+                      "saving_ms": round(pair_ms - fused_ms, 4),
+                      "tokens_per_s": round(wl.B * wl.T / (fused_ms * 1e-3), 1), "compulsory_bytes": nbytes,
+                      "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "frac_of_copy": round(gbs / copy_gbs, 4) if copy_gbs else None,
+                      "xerr": gdn2.fwd_output_xerr((wl.B, wl.T, wl.H, wl.dk, wl.dv, torch.bfloat16), ws)}
+    return res
+
+
 def output_bench(dev, wl, iters=20):
     """The output epilogue (gdn2_output_fwd / gdn2_output_bwd with dweight) on the
     operator's output shape of the training workload."""
@@ -749,6 +794,7 @@ def main():
         out["breakdown"]["other_configs"] = configs_bench(dev, timed_steps)
     if not args.no_output:
         out["breakdown"]["output_epilogue"] = output_bench(dev, wl)
+        out["breakdown"]["output_epilogue"]["fused_forward"] = fused_output_bench(dev, wl, copy_gbs=copy_gbs)
     if not args.no_decode:
         out["breakdown"]["decode_step"] = decode_bench(dev)
     if not args.no_phase_stamps:

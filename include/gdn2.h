@@ -278,6 +278,38 @@ int gdn2_output_bwd(const gdn2_shape *shape, const float *o, const void *g, int 
                     const float *weight, float eps, const float *dy, float *dO, float *dg,
                     float *dweight, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- forward with the output epilogue fused ----
+ *
+ * The inference forward followed by the output epilogue (blog on Gated DeltaNet-2, section
+ * "Token path and parallel training": the operator's output goes through an RMS
+ * normalisation and an output gate of its own before the projection), with o never written
+ * to device memory:
+ *     y = o / sqrt(mean_j o_j^2 + eps) * weight * g      per (b, t, h) row of dv channels,
+ * o being what gdn2_chunk_fwd computes.  Inputs and S0, S_final as gdn2_chunk_fwd; g, weight,
+ * eps, y, g_dtype, y_dtype as gdn2_output_fwd (g, weight, y 16-byte aligned).
+ * - Fused (gdn2_chunk_fwd_output_fused() == 1: bf16 q/k/v, dk 64 or 128, dv 64 or 128, a
+ *   shape the forward does not split into segments, and every workgroup of the sweep resident
+ *   at once): the launches of gdn2_chunk_fwd (chunk records, their exact pass, the sweep),
+ *   with the epilogue in the sweep's output stage; the sweep is a cooperative launch when a
+ *   head's value columns span several workgroups.  The workspace holds the records and flags, then the
+ *   exchange area (cleared by the records launch): 64-bit words {row sum of squares of one
+ *   wave's columns, chunk + 1} in a ring of two chunk slots per head, and in the last 256 bytes
+ *   an int that counts exchange waits that ran out (0 in a correct run; a wait runs out only if
+ *   a workgroup of the head never publishes, after about 2^16 reads).
+ * - Otherwise gdn2_chunk_fwd into o in the workspace, then gdn2_output_fwd: results equal to
+ *   those two calls.
+ * The norm's sum over a row is added in a different order from gdn2_output_fwd's, so the two
+ * paths agree to rounding, not bit for bit.  Errors as gdn2_chunk_fwd and gdn2_output_fwd. */
+size_t gdn2_chunk_fwd_output_workspace_size(const gdn2_shape *shape);
+int gdn2_chunk_fwd_output(const gdn2_shape *shape,
+                          const void *q, const void *k, const void *v,
+                          const void *log_alpha, const void *b, const void *w,
+                          const float *S0, const void *g, int g_dtype, const float *weight,
+                          float eps, void *y, int y_dtype, float *S_final,
+                          void *workspace, size_t workspace_bytes, void *stream);
+/* 1 if gdn2_chunk_fwd_output fuses the epilogue for this shape on the current device, else 0. */
+int gdn2_chunk_fwd_output_fused(const gdn2_shape *shape);
+
 /* ---- forward without allocation ----
  *
  * For callers that cannot allocate device memory: code under HIP graph capture, tight

@@ -37,7 +37,8 @@ EXPORTS = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "gdn2_chunk_bwd",
            "gdn2_chunk_bwd_reverse", "gdn2_chunk_bwd_grads", "gdn2_step", "gdn2_output_fwd",
            "gdn2_output_bwd_workspace_size", "gdn2_output_bwd", "gdn2_chunk_fwd_factored",
            "gdn2_chunk_sweeps", "gdn2_chunk_sweeps_fused", "gdn2_chunk_fwd_noalloc",
-           "gdn2_chunk_fwd_noalloc_max_bytes"]
+           "gdn2_chunk_fwd_noalloc_max_bytes", "gdn2_chunk_fwd_output", "gdn2_chunk_fwd_output_workspace_size",
+           "gdn2_chunk_fwd_output_fused"]
 
 
 class Gdn2Shape(ctypes.Structure):
@@ -98,6 +99,12 @@ def load():
         I, F = ctypes.c_int, ctypes.c_float
         lib.gdn2_output_fwd.argtypes = [SP, P, P, I, P, F, P, I, P]
         lib.gdn2_output_fwd.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_output.argtypes = [SP] + [P] * 8 + [I, P, F, P, I, P, P, ctypes.c_size_t, P]
+        lib.gdn2_chunk_fwd_output.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_output_workspace_size.argtypes = [SP]
+        lib.gdn2_chunk_fwd_output_workspace_size.restype = ctypes.c_size_t
+        lib.gdn2_chunk_fwd_output_fused.argtypes = [SP]
+        lib.gdn2_chunk_fwd_output_fused.restype = ctypes.c_int
         lib.gdn2_output_bwd_workspace_size.argtypes = [SP]
         lib.gdn2_output_bwd_workspace_size.restype = ctypes.c_size_t
         lib.gdn2_output_bwd.argtypes = [SP, P, P, I, P, F, P, P, P, P, P, ctypes.c_size_t, P]
@@ -502,6 +509,54 @@ def output_fwd(o, g, weight=None, eps=1e-6, out_dtype=torch.float32):
     _check(load().gdn2_output_fwd(ctypes.byref(shape), _ptr(o), _ptr(g), gdt, _ptr(weight), float(eps), _ptr(y),
                                   GDN2_BF16 if out_dtype == torch.bfloat16 else GDN2_F32, _stream(o.device)))
     return y
+
+
+def fwd_output(q, k, v, log_alpha, b, w, g, weight=None, eps=1e-6, S0=None, want_state=True,
+               out_dtype=torch.float32, workspace=None):
+    """gdn2_chunk_fwd_output: the forward with the output epilogue fused, o never written:
+    y = rmsnorm(o) * weight * g per (b, t, h) row (y of dtype out_dtype, fp32 or bf16) and
+    S_final.  g: output gate values fp32 or bf16 [B,T,H,dv]; weight fp32 [dv] or None.
+    Returns (y, S_final, workspace); the workspace's last 256 bytes hold the exchange
+    diagnostic counter (see fwd_output_xerr)."""
+    B, T, H, dk, dv, sc = _validate(q, k, v, log_alpha, b, w, (S0, g, weight))
+    if S0 is not None and (tuple(S0.shape) != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("gdn2: S0 must be float32 [B,H,dk,dv]")
+    if tuple(g.shape) != (B, T, H, dv) or g.dtype not in (torch.float32, torch.bfloat16) or g.device != q.device:
+        raise ValueError("gdn2: the output gate must be float32 or bfloat16 [B,T,H,dv]")
+    if weight is not None and (tuple(weight.shape) != (dv,) or weight.dtype != torch.float32
+                               or weight.device != q.device):
+        raise ValueError("gdn2: weight must be float32 [dv]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gdn2: the epilogue writes float32 or bfloat16")
+    lib = load()
+    shape = make_shape(B, T, H, dk, dv, q.dtype, log_alpha.dtype, sc)
+    y = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state else None
+    ws_bytes = lib.gdn2_chunk_fwd_output_workspace_size(ctypes.byref(shape))
+    if ws_bytes == ctypes.c_size_t(-1).value:
+        raise Gdn2Error(2, "unsupported shape")
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gdn2_chunk_fwd_output(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                     _ptr(w), _ptr(S0), _ptr(g), GDN2_BF16 if g.dtype == torch.bfloat16 else GDN2_F32,
+                                     _ptr(weight), float(eps), _ptr(y),
+                                     GDN2_BF16 if out_dtype == torch.bfloat16 else GDN2_F32, _ptr(sf),
+                                     _ptr(workspace), nbytes, _stream(q.device)))
+    return y, sf, workspace
+
+
+def fwd_output_fused(B, T, H, dk, dv, qkv_dtype, gate_dtype=torch.float32, gate_scalar=0):
+    """Whether gdn2_chunk_fwd_output fuses the epilogue into the sweep for this shape."""
+    return bool(load().gdn2_chunk_fwd_output_fused(ctypes.byref(make_shape(B, T, H, dk, dv, qkv_dtype, gate_dtype,
+                                                                             gate_scalar))))
+
+
+def fwd_output_xerr(shape_args, workspace):
+    """The fused path's count of exchange waits that ran out (int32 in the workspace's last
+    256 bytes, at the offset gdn2_chunk_fwd_output_workspace_size - 256); 0 in a correct run."""
+    n = load().gdn2_chunk_fwd_output_workspace_size(ctypes.byref(make_shape(*shape_args)))
+    return int(workspace[n - 256:n - 252].view(torch.int32).item())
 
 
 def output_bwd_workspace_bytes(B, T, H, dv):

@@ -83,6 +83,16 @@ size_t fwd_segment_bytes(const gdn2_shape *s, int nseg) {
     return blocks * (s->dv + s->dk) * sizeof(float) + blocks * s->dv * sizeof(float);
 }
 
+// The forward with the output epilogue fused into its sweep: the wide sweep without segments,
+// where every workgroup of the launch can be resident at once (gdn2::fwd_out_fused).
+bool out_fused(const gdn2_shape *s) {
+    int seg_len;
+    return wide_sweep_shape(s) && fwd_segments(s, &seg_len) == 1 &&
+           gdn2::fwd_out_fused(s->B, s->H, s->T, s->dk, s->dv, true);
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 // the alignment a gate tensor (or its gradient) needs: 4 bytes when it is per token
 bool gate_aligned(const gdn2_shape *s, int bit, const void *p) {
     return !p || ((s->gate_scalar & bit) ? aligned4(p) : aligned16(p));
@@ -158,6 +168,65 @@ int gdn2_chunk_fwd(const gdn2_shape *shape, const void *q, const void *k, const 
     const hipError_t e2 = gdn2::launch_fwd_sweep(f, shape->dk, vt, bf16, gate_logits(shape), gate_scalar(shape),
                                                  gdn2::kFwdOut, hs);
     return e2 == hipSuccess ? GDN2_OK : GDN2_ERR_HIP;
+}
+
+size_t gdn2_chunk_fwd_output_workspace_size(const gdn2_shape *shape) {
+    if (check_shape(shape) != GDN2_OK) return (size_t)-1;
+    if (out_fused(shape))
+        return gdn2::record_buffer_bytes((long)shape->B * shape->H * nchunks(shape), shape->dk) +
+               gdn2::fwd_out_exchange_bytes(shape->B, shape->H, shape->T, shape->dk, shape->dv);
+    // otherwise gdn2_chunk_fwd's workspace, then o
+    return round256(gdn2_chunk_fwd_workspace_size(shape)) + (size_t)shape->B * shape->T * shape->H * shape->dv * 4;
+}
+
+int gdn2_chunk_fwd_output(const gdn2_shape *shape, const void *q, const void *k, const void *v,
+                          const void *log_alpha, const void *b, const void *w, const float *S0, const void *g,
+                          int g_dtype, const float *weight, float eps, void *y, int y_dtype, float *S_final,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    const int st = check_shape(shape);
+    if (st != GDN2_OK) return st;
+    if (!q || !k || !v || !log_alpha || !b || !w || !g || !y || !(eps >= 0.f) || !isfinite(eps))
+        return GDN2_ERR_INVALID_ARG;
+    if ((g_dtype != GDN2_F32 && g_dtype != GDN2_BF16) || (y_dtype != GDN2_F32 && y_dtype != GDN2_BF16))
+        return GDN2_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, S0, g, weight, y, S_final, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARG;
+    if (!gates_aligned(shape, log_alpha, b, w)) return GDN2_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < gdn2_chunk_fwd_output_workspace_size(shape)) return GDN2_ERR_WORKSPACE;
+    if (!out_fused(shape)) {
+        // the forward into the workspace's o, then the epilogue
+        const size_t fw = round256(gdn2_chunk_fwd_workspace_size(shape));
+        float *o = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + fw);
+        const int rc = gdn2_chunk_fwd(shape, q, k, v, log_alpha, b, w, S0, o, S_final, workspace, fw, stream);
+        if (rc != GDN2_OK) return rc;
+        return gdn2_output_fwd(shape, o, g, g_dtype, weight, eps, y, y_dtype, stream);
+    }
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const long items = (long)shape->B * shape->H * nchunks(shape);
+    gdn2::BwdArgs r{};
+    r.B = shape->B; r.T = shape->T; r.H = shape->H; r.DV = shape->dv; r.scalar = shape->gate_scalar;
+    r.q = q; r.k = k; r.la = log_alpha; r.bg = b; r.factors = workspace;
+    // the records kernel also clears the sweep's row-sum exchange area
+    char *xr = reinterpret_cast<char *>(workspace) + gdn2::record_buffer_bytes(items, shape->dk);
+    const size_t xbytes = gdn2::fwd_out_exchange_bytes(shape->B, shape->H, shape->T, shape->dk, shape->dv);
+    r.zero = xr; r.zero16 = (long)(xbytes / 16);
+    if (gdn2::launch_fwd_records(r, shape->dk, true, gate_logits(shape), gate_scalar(shape), hs) != hipSuccess)
+        return GDN2_ERR_HIP;
+    gdn2::FwdArgs f{};
+    f.v = v; f.wg = w; f.S0 = S0; f.S_final = S_final; f.records = workspace;
+    f.B = shape->B; f.T = shape->T; f.H = shape->H; f.dv = shape->dv; f.scalar = shape->gate_scalar;
+    f.og = g; f.oweight = weight; f.y = y; f.eps = eps;
+    f.og_bf16 = g_dtype == GDN2_BF16; f.y_bf16 = y_dtype == GDN2_BF16;
+    f.xrow = reinterpret_cast<unsigned long long *>(xr);
+    f.xerr = reinterpret_cast<int *>(xr + xbytes - 256);
+    return gdn2::launch_fwd_sweep_out(f, shape->dk, gate_logits(shape), gate_scalar(shape), hs) == hipSuccess
+               ? GDN2_OK
+               : GDN2_ERR_HIP;
+}
+
+int gdn2_chunk_fwd_output_fused(const gdn2_shape *shape) {
+    return check_shape(shape) == GDN2_OK && out_fused(shape) ? 1 : 0;
 }
 
 size_t gdn2_chunk_states_bytes(const gdn2_shape *shape) {

@@ -24,6 +24,15 @@ struct FwdArgs {
     int nvt;                        // value tiles per (b, h) = dv / value-tile width
     int scalar;                     // kScalar* bits: gates given per token [B,T,H]
     int nseg, seg_len;              // segmented sweep: segments per (b, h), chunks per segment
+    // fused output epilogue (launch_fwd_sweep_out): y = o / sqrt(mean_j o_j^2 + eps) * weight * g
+    // per (b, t, h) row of dv channels; o itself is not written
+    const void *og;                 // output gate values [B,T,H,dv], fp32 or bf16 (og_bf16)
+    const float *oweight;           // [dv] or null (ones)
+    void *y;                        // [B,T,H,dv], fp32 or bf16 (y_bf16)
+    unsigned long long *xrow;       // row sums of squares exchanged between a head's value tiles
+    int *xerr;                      // exchange waits that ran out (0 in a correct run)
+    float eps;
+    int og_bf16, y_bf16;
 };
 
 // Arguments of the backward kernels.
@@ -35,6 +44,8 @@ struct BwdArgs {
     float *dstates;                 // [B,H,NC,dk,dv] gradient w.r.t. chunk-end states
     float *dq, *dk, *dv, *dla, *db, *dw, *dS0;
     void *factors;                  // per-chunk adjoint factors (bf16 tiles), then chunk operand records
+    void *zero;                     // forward-only records: zero16 16-byte words the fast pass also clears
+    long zero16;                    // (for a launch that follows), or null / 0
     int B, T, H, DV;
     int scalar;                     // kScalar* bits: gates (and their gradients) per token [B,T,H]
 };
@@ -79,6 +90,17 @@ enum FwdMode { kFwdOut = 0, kFwdStates = 1, kFwdOutStates = 2 };
 hipError_t launch_fwd_segments(const FwdArgs &a, int dk, bool gl, bool sg, float *E, float *Sin, hipStream_t st);
 hipError_t launch_fwd_sweep(const FwdArgs &a, int dk, int vt, bool bf16, bool gl, bool sg, FwdMode mode,
                             hipStream_t st);
+// The forward sweep with the output epilogue fused (a.og, a.oweight, a.eps, a.y, a.og_bf16,
+// a.y_bf16; a.o unused): the wide sweep without segments, where a head has at most four value
+// tiles (dv / tile width) and all of its workgroups can be resident at once.  Each wave
+// publishes the sums of squares of its rows over its columns as 64-bit words {value, chunk + 1}
+// in a.xrow (a ring of two chunks: B * H * 2 * 2 * tiles * 64 words, zero before the launch;
+// see fwd_out_exchange_bytes) and reads the other waves' words of its rows one chunk later.
+// fwd_out_fused tells whether a shape takes it; launch_fwd_sweep_out returns
+// hipErrorInvalidValue where it does not.
+bool fwd_out_fused(int B, int H, int T, int dk, int dv, bool bf16);
+size_t fwd_out_exchange_bytes(int B, int H, int T, int dk, int dv);
+hipError_t launch_fwd_sweep_out(const FwdArgs &a, int dk, bool gl, bool sg, hipStream_t st);
 // Whether the forward sweep (o, S_final, chunk states) and the reverse sweep from one factor
 // buffer run as one launch: bf16 q/k/v, dk 64 or 128, dv a multiple of 64, and 64-column tiles of
 // both sweeps together at most one workgroup per CU.

@@ -115,6 +115,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     // inputs at its start.
     const int nmine = blockIdx.x < (unsigned)nitems ? (nitems - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     if (!EX) issue(blockIdx.x < (unsigned)nitems ? blockIdx.x : 0);
+    if (!EX && a.zero) {
+        // the area a launch that follows needs cleared (vector stores, grid-stride)
+        uint4 *z = reinterpret_cast<uint4 *>(a.zero);
+        for (long i = (long)blockIdx.x * NTH + threadIdx.x; i < a.zero16; i += (long)gridDim.x * NTH)
+            z[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     for (long base = blockIdx.x; base < (EX ? nitems : (long)blockIdx.x + 1); base += (long)gridDim.x * NTH) {
     const int nwork = EX ? gather_flagged<NTH>(flags, nitems, base, gridDim.x, sList, sList + NTH) : nmine;
     for (int wi = 0; wi < nwork; ++wi) {

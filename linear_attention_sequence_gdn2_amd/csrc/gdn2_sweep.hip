@@ -37,6 +37,10 @@ namespace gdn2 {
 
 #define GDN2_SWEEP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Reads of a row-sum word of the fused epilogue before a wait counts as run out (each takes a
+// load and a short sleep; in a correct run the word is there at the first read or soon after).
+constexpr int kXrowSpins = 1 << 16;
+
 #ifdef GDN2_STAMPS
 // stamps of the unsegmented wide sweep: 8 per (workgroup, wave, chunk), see fwd_sweep64_body
 static __device__ unsigned long long *g_sweep_stamps;
@@ -303,11 +307,24 @@ struct Sweep64Lds {
 
 // One workgroup's sweep: L is its (batch, head[, segment], value tile) index in launch order.
 // VT = 64 value columns per tile, or 32 (no segments) where 64-column tiles would leave CUs idle.
-template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG, int VT = 64>
+// NV > 0: the output epilogue is fused, and a head has NV value tiles (dv = NV * VT).  Then
+// o is never stored: the O tile of chunk c stays in registers until chunk c + 1, when the
+// sums of squares of its rows over all dv columns are known, and y is stored instead.  Each
+// wave publishes the sums of its 16 rows over its VT / 2 columns as 64-bit words
+// {value, c + 1} (one store, so the tag and the value become visible together) with
+// device-scope atomic stores; during the next chunk the four lanes of a row read the row's
+// 2 NV words between them with device-scope atomic loads and add them with lane shuffles.  A
+// word whose tag is not there yet is read again (bounded; a.xerr counts waits that ran out).
+// Every wave adds the 2 NV sums in the same order, so the tiles of a row apply the same factor.
+template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG, int VT = 64, int NV = 0>
 __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, __bf16 *sK, __bf16 *sE,
-                                                 __bf16 *sQ, __bf16 *sS, __bf16 *sX, __bf16 *sU) {
+                                                 __bf16 *sQ, __bf16 *sS, __bf16 *sX, __bf16 *sU,
+                                                 float *sW = nullptr) {
     using Rec = ChunkRecord<DK>;
     static_assert(VT == 64 || (VT == 32 && SEG == 0), "64-column tiles, or 32 without segments");
+    constexpr bool EPI = NV > 0;
+    constexpr int NSRC = 2 * (EPI ? NV : 1);             // row sums per row: both halves of every tile
+    static_assert(!EPI || (OUT && !STATES && SEG == 0 && NV <= 4), "the epilogue rides on the plain o sweep");
     constexpr int NTH = kChunkThreads;
     constexpr int NCB = VT / 16, CBW = VT / 32;          // 16-column blocks: per tile, per wave half
     constexpr int NKS = DK / 32, NMT = DK / 16;
@@ -446,6 +463,9 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
 #pragma unroll
     for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(c_lo + 1 < c_hi ? c_lo + 1 : c_lo, it, tid);
     store_state_lds(wv, r, g);
+    if constexpr (EPI) {
+        if (tid < VT) sW[tid] = a.oweight ? a.oweight[j0 + tid] : 1.f;   // this tile's norm weights
+    }
     __syncthreads();
 
     const int nkk = (w >= 2) ? 2 : 1;
@@ -467,6 +487,103 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
     auto load_gam = [&](const char *rc) {
         return *reinterpret_cast<const f32x4 *>(rc + Rec::oGam + (size_t)(16 * ((wv * NTS) / NCB) + 4 * g) * 4);
     };
+    // ---- fused output epilogue (NV > 0) ----
+    // eo: the O tile of the pending chunk in the lane layout after the quad transpose (row erow =
+    // 16w + 4g + (r & 3), columns 16cb + 4(r >> 2) .. + 3); gr: its output-gate values as loaded
+    // (four bf16 in .x, .y, or four fp32).  The 2 NV row sums of a row are read by its four lanes
+    // (r >> 2 = 0 .. 3): lane k takes sources k, k + 4, .. (NSRC 2: source k & 1), and two xor
+    // shuffles add them, in an order that every wave of every tile repeats.  Words live in a
+    // ring of two chunk slots: slot c & 1 of chunk c is written again at chunk c + 2, after every
+    // reader of it has published chunk c + 1 (each reads its chunk-c words before that).
+    constexpr int XS = NSRC >= 4 ? NSRC / 4 : 1;          // words a lane reads per row and chunk
+    float eo[CBW][4];
+    unsigned long long xw[XS];
+    uint4 gr[CBW];
+    const int erow = 16 * w + 4 * g + (r & 3);
+    auto xrow_idx = [&](int cc, int src, int row) {
+        return ((size_t)(bh * 2 + (cc & 1)) * NSRC + src) * 64 + row;
+    };
+    auto xsrc = [&](int k) { return NSRC >= 4 ? (r >> 2) + 4 * k : (r >> 2) & 1; };
+    // loads for chunk cp: this lane's row-sum words (whatever is there yet) and the gate values
+    auto epi_issue = [&](int cp) {
+#pragma unroll
+        for (int k = 0; k < XS; ++k)
+            xw[k] = __hip_atomic_load(a.xrow + xrow_idx(cp, xsrc(k), erow), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        const int t = cp * kChunk + erow;
+        const size_t row = (size_t)(t < T ? t : T - 1);
+        const unsigned esz = a.og_bf16 ? 2u : 4u;
+#pragma unroll
+        for (int n = 0; n < CBW; ++n) {
+            // both halves loaded whatever the dtype (the bf16 case reads its 8 bytes twice), so that
+            // no load sits under a branch
+            const char *p = reinterpret_cast<const char *>(a.og) +
+                            (baseV + row * tokV + 16 * (CBW * hf + n) + 4 * (r >> 2)) * esz;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(p);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(p + (a.og_bf16 ? 0 : 8));
+            gr[n] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+    };
+    // a word whose tag has not arrived: read again, bounded
+    auto epi_wait = [&](int cp) {
+        const unsigned tag = (unsigned)(cp + 1);
+        for (int spin = 0; spin < kXrowSpins; ++spin) {
+            __builtin_amdgcn_s_sleep(2);
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < XS; ++k) {
+                if ((unsigned)(xw[k] >> 32) != tag)
+                    xw[k] = __hip_atomic_load(a.xrow + xrow_idx(cp, xsrc(k), erow), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (unsigned)(xw[k] >> 32) == tag;
+            }
+            if (__all(ok)) return;
+        }
+        if ((threadIdx.x & 63) == 0) atomicAdd(a.xerr, 1);
+    };
+    // y of chunk cp from eo: the row's sum of squares over all dv columns, then norm, weight and
+    // gate
+    auto epi_finish = [&](int cp) {
+        const unsigned tag = (unsigned)(cp + 1);
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < XS; ++k) ok = ok && (unsigned)(xw[k] >> 32) == tag;
+        if (!__all(ok)) epi_wait(cp);
+        float tot = __uint_as_float((unsigned)xw[0]);
+#pragma unroll
+        for (int k = 1; k < XS; ++k) tot += __uint_as_float((unsigned)xw[k]);
+        tot += __shfl_xor(tot, 4);
+        if (NSRC >= 4) tot += __shfl_xor(tot, 8);
+        const float rs = __builtin_amdgcn_rsqf(tot * (1.f / (float)(NSRC / 2 * VT)) + a.eps);
+        const int t = cp * kChunk + erow;
+#pragma unroll
+        for (int n = 0; n < CBW; ++n) {
+            const int col = 16 * (CBW * hf + n) + 4 * (r >> 2);
+            const float4 wt = *reinterpret_cast<const float4 *>(&sW[col]);
+            float gv[4];
+            if (a.og_bf16) {
+                gv[0] = __uint_as_float(gr[n].x << 16), gv[1] = __uint_as_float(gr[n].x & 0xffff0000u);
+                gv[2] = __uint_as_float(gr[n].y << 16), gv[3] = __uint_as_float(gr[n].y & 0xffff0000u);
+            } else {
+                gv[0] = __uint_as_float(gr[n].x), gv[1] = __uint_as_float(gr[n].y);
+                gv[2] = __uint_as_float(gr[n].z), gv[3] = __uint_as_float(gr[n].w);
+            }
+            const f32x4 yv = {eo[n][0] * rs * wt.x * gv[0], eo[n][1] * rs * wt.y * gv[1], eo[n][2] * rs * wt.z * gv[2],
+                              eo[n][3] * rs * wt.w * gv[3]};
+            if (t < T) {
+                const size_t off = baseV + (size_t)t * tokV + col;
+                if (a.y_bf16)
+                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(a.y) + off) =
+                        __builtin_convertvector(yv, bf16x4);
+                else
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + off) = yv;
+            }
+        }
+    };
+    (void)xrow_idx;
+    (void)epi_issue;
+    (void)epi_finish;
+
     Split8 Tf[2];
     uint4 pv[4];
     load_T(recs + (size_t)c_lo * Rec::BYTES, Tf);
@@ -478,18 +595,25 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         const int cn2 = c + 2 < c_hi ? c + 2 : cn;       // the one after
 #ifdef GDN2_STAMPS
         // [A] from 0 to 1, [B] 2 to 3, O 4 to 5, S' 5 to 6; 1-2, 3-4 and 6-7 are barriers
-        unsigned long long *stp = SEG == 0 && g_sweep_stamps ? g_sweep_stamps + (((size_t)L * 8 + wv) * NC + c) * 8
-                                                             : nullptr;
+        unsigned long long *stp = SEG == 0 && !EPI && g_sweep_stamps
+                                      ? g_sweep_stamps + (((size_t)L * 8 + wv) * NC + c) * 8
+                                      : nullptr;
 #else
         unsigned long long *stp = nullptr;
 #endif
         (void)stp;
 
-        // ---- loads: Kh rows, v, w of the next chunk (T, P and gamma of this one are in flight) ----
+        // ---- loads: Kh rows, v, w of the next chunk (T, P and gamma of this one are in flight);
+        // with the epilogue after stage A, where they leave room for its registers ----
         uint4 ktn[NKP];
+        if constexpr (!EPI) {
 #pragma unroll
-        for (int it = 0; it < NKP; ++it) ktn[it] = kt_piece(cn, it, tid);
-        load_vw(cn, vv, ww, w, hf, r, g);   // z of the next chunk is formed at this chunk's end
+            for (int it = 0; it < NKP; ++it) ktn[it] = kt_piece(cn, it, tid);
+            load_vw(cn, vv, ww, w, hf, r, g);   // z of the next chunk is formed at this chunk's end
+        } else {
+            // the row sums and gate values of the pending chunk, two stages ahead of their use
+            epi_issue(c > c_lo ? c - 1 : c_lo);   // unconditional: at c_lo its values go unused
+        }
         if (STATES) {
             // one 16-byte store per tile: the quad transpose gives the lane row 16m + 4g + (r & 3),
             // columns 16n + 4(r >> 2) ..
@@ -529,6 +653,11 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         }
         GDN2_STAMP(stp, 1);
         __syncthreads();
+        if constexpr (EPI) {
+#pragma unroll
+            for (int it = 0; it < NKP; ++it) ktn[it] = kt_piece(cn, it, tid);
+            load_vw(cn, vv, ww, w, hf, r, g);
+        }
 
         // ---- [B] U = T X; then the next chunk's Et/Qt rows into LDS ----
         GDN2_STAMP(stp, 2);
@@ -566,6 +695,9 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         GDN2_STAMP(stp, 4);
 
         // ---- [C] O = Qt S + P U; S' = diag(gamma) S + Kh^T U ----
+        if constexpr (EPI) {
+            if (c > c_lo) epi_finish(c - 1);   // y of the pending chunk; frees eo for this one
+        }
 #pragma unroll
         for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(cn2, it, tid);
         if (OUT) {
@@ -576,6 +708,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
                 Pf[mt].hi = __builtin_shufflevector(o, o, 0, 1, 2, 3);
                 Pf[mt].lo = __builtin_shufflevector(o, o, 4, 5, 6, 7);
             }
+            float ss = 0.f;                         // sum of squares of this lane's O elements
 #pragma unroll
             for (int n = 0; n < CBW; ++n) {
                 const int cb = CBW * hf + n;
@@ -591,11 +724,30 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
                 }
                 float x[4] = {acc[0], acc[1], acc[2], acc[3]};
                 quad_transpose4(x);   // row 16w + 4g + (r & 3), columns 16cb + 4(r >> 2) ..
-                const int to = t0 + 16 * w + 4 * g + (r & 3);
-                if (to < T)
-                    *reinterpret_cast<float4 *>(&a.o[baseV + (size_t)to * tokV + 16 * cb + 4 * (r >> 2)]) =
-                        make_float4(x[0], x[1], x[2], x[3]);
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        eo[n][i] = x[i];
+                        ss += x[i] * x[i];
+                    }
+                } else {
+                    const int to = t0 + 16 * w + 4 * g + (r & 3);
+                    if (to < T)
+                        *reinterpret_cast<float4 *>(&a.o[baseV + (size_t)to * tokV + 16 * cb + 4 * (r >> 2)]) =
+                            make_float4(x[0], x[1], x[2], x[3]);
                 }
+            }
+            if constexpr (EPI) {
+                // the row's sum over this wave's columns: the four lanes r >> 2 = 0 .. 3 of the row
+                ss += __shfl_xor(ss, 4);
+                ss += __shfl_xor(ss, 8);
+                if ((r >> 2) == 0) {
+                    const unsigned long long word =
+                        ((unsigned long long)(unsigned)(c + 1) << 32) | (unsigned long long)__float_as_uint(ss);
+                    __hip_atomic_store(a.xrow + xrow_idx(c, 2 * vt + hf, 16 * w + 4 * g + r), word, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
             load_P(recs + (size_t)cn * Rec::BYTES, pv);
         }
         GDN2_STAMP(stp, 5);
@@ -631,6 +783,13 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
                 z[n][i] = (c + 1) * kChunk + 16 * w + 4 * g + i < T ? zon * gate_act<GL>(ww[n][i]) * vv[n][i] : 0.f;
     }
 
+    if constexpr (EPI) {
+        if (c_hi > c_lo) {
+            epi_issue(c_hi - 1);
+            epi_finish(c_hi - 1);
+        }
+    }
+
     if (SEG == 1) {
         // the segment's end-state block [N | M], DK x (DV + DK), of this (b, h) and segment
         const int ldE = DV + DK;
@@ -652,12 +811,13 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
     }
 }
 
-template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG, int VT = 64>
+template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG, int VT = 64, int NV = 0>
 __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a) {
     using Lds = Sweep64Lds<DK, OUT, VT>;
     __shared__ __align__(16) __bf16 sK[Lds::K], sE[Lds::E], sQ[Lds::Q], sS[Lds::S], sX[Lds::X], sU[Lds::U];
-    fwd_sweep64_body<DK, OUT, STATES, GL, SG, SEG, VT>(a, xcd_swizzle(blockIdx.x, gridDim.x), sK, sE, sQ, sS, sX,
-                                                       sU);
+    __shared__ __align__(16) float sW[NV > 0 ? VT : 4];
+    fwd_sweep64_body<DK, OUT, STATES, GL, SG, SEG, VT, NV>(a, xcd_swizzle(blockIdx.x, gridDim.x), sK, sE, sQ, sS,
+                                                           sX, sU, sW);
 }
 
 // The training step's two sweeps in one launch: the forward sweep (the state before every chunk,
@@ -899,6 +1059,71 @@ hipError_t launch_fwd_sweep(const FwdArgs &a_in, int dk, int vt, bool bf16, bool
     if (gl) return bf16 ? sweep_mode<true, true, false>(a, dk, vt, mode, st) : hipErrorInvalidValue;
     if (sg) return bf16 ? sweep_mode<true, false, true>(a, dk, vt, mode, st) : hipErrorInvalidValue;
     return bf16 ? sweep_mode<true, false, false>(a, dk, vt, mode, st) : sweep_mode<false, false, false>(a, dk, vt, mode, st);
+}
+
+// ---- the forward sweep with the output epilogue fused ----
+// The tile width is the plain o sweep's (32 columns where they still give each workgroup a CU
+// of its own); NV = dv / width tiles share a row.  With NV > 1 the tiles of a head wait on each
+// other's row sums, so the launch is cooperative: every workgroup is resident at once.
+static int out_tile(int B, int H, int dv) { return 2L * B * H * (dv / 64) <= cu_count() ? 32 : 64; }
+
+template <int DK, bool GL, bool SG, int VT, int NV>
+static const void *out_kernel() {
+    return reinterpret_cast<const void *>(&fwd_sweep64_kernel<DK, true, false, GL, SG, 0, VT, NV>);
+}
+
+template <int DK, bool GL, bool SG>
+static const void *out_kernel_vt(int vt, int nv) {
+    if (vt == 64 && nv == 1) return out_kernel<DK, GL, SG, 64, 1>();
+    if (vt == 64 && nv == 2) return out_kernel<DK, GL, SG, 64, 2>();
+    if (vt == 32 && nv == 2) return out_kernel<DK, GL, SG, 32, 2>();
+    if (vt == 32 && nv == 4) return out_kernel<DK, GL, SG, 32, 4>();
+    return nullptr;
+}
+
+static const void *out_kernel_for(int dk, bool gl, bool sg, int vt, int nv) {
+    if (gl && sg) return nullptr;
+    if (dk == 128)
+        return gl ? out_kernel_vt<128, true, false>(vt, nv) : sg ? out_kernel_vt<128, false, true>(vt, nv)
+                                                                   : out_kernel_vt<128, false, false>(vt, nv);
+    if (dk == 64)
+        return gl ? out_kernel_vt<64, true, false>(vt, nv) : sg ? out_kernel_vt<64, false, true>(vt, nv)
+                                                                  : out_kernel_vt<64, false, false>(vt, nv);
+    return nullptr;
+}
+
+bool fwd_out_fused(int B, int H, int T, int dk, int dv, bool bf16) {
+    (void)T;
+    if (!bf16 || (dk != 64 && dk != 128) || dv % 64 != 0) return false;
+    const int vt = out_tile(B, H, dv), nv = dv / vt;
+    const void *k = out_kernel_for(dk, false, false, vt, nv);
+    if (!k) return false;
+    if (nv == 1) return true;
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kChunkThreads, 0) != hipSuccess || per < 1) return false;
+    return (long)B * H * nv <= (long)per * cu_count();
+}
+
+size_t fwd_out_exchange_bytes(int B, int H, int T, int dk, int dv) {
+    (void)dk;
+    const int nv = dv / out_tile(B, H, dv);
+    (void)T;
+    const size_t words = (size_t)B * H * 2 * (2 * nv) * 64;   // two chunk slots of 2 nv sources x 64 rows
+    return words * sizeof(unsigned long long) + 256;          // then the run-out counter (one int, 256-byte slot)
+}
+
+hipError_t launch_fwd_sweep_out(const FwdArgs &a_in, int dk, bool gl, bool sg, hipStream_t st) {
+    if (!fwd_out_fused(a_in.B, a_in.H, a_in.T, dk, a_in.dv, true)) return hipErrorInvalidValue;
+    FwdArgs a = a_in;
+    const int vt = out_tile(a.B, a.H, a.dv), nv = a.dv / vt;
+    a.nvt = nv;
+    a.o = nullptr, a.states = nullptr;
+    const void *k = out_kernel_for(dk, gl, sg, vt, nv);
+    if (!k) return hipErrorInvalidValue;
+    void *args[] = {&a};
+    const dim3 grid((unsigned)(a.B * a.H * nv)), block(kChunkThreads);
+    if (nv == 1) return hipLaunchKernel(k, grid, block, args, 0, st);
+    return hipLaunchCooperativeKernel(k, grid, block, args, 0, st);
 }
 
 template <int DK, bool GL, bool SG, int VT>

@@ -292,3 +292,42 @@ def test_forward_workspace():
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == \
         items * rec32 + _flags(items)
 
+
+
+def test_fused_forward_output_workspace_and_checks():
+    """gdn2_chunk_fwd_output: with no device answering, a shape whose heads span several
+    workgroups cannot be shown resident, so it takes the unfused route (gdn2_chunk_fwd's
+    workspace, then o); one value tile per head (dv 64 on 64-column tiles) fuses without a
+    cooperative launch: the records, then the row-sum words (a ring of two chunk slots of 2
+    words per row and head) and the 256-byte counter slot.  Argument checks come before any
+    launch."""
+    lib = gdn2.load()
+    f = P(0x10000)
+    F, Z = ctypes.c_float, ctypes.c_size_t
+    unf = _shape(B=8, T=2048, H=16, dk=128, dv=128, dt=0)          # fp32 q/k/v
+    fw = lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(unf))
+    assert lib.gdn2_chunk_fwd_output_fused(ctypes.byref(unf)) == 0
+    assert lib.gdn2_chunk_fwd_output_workspace_size(ctypes.byref(unf)) == \
+        (fw + 255) // 256 * 256 + 8 * 2048 * 16 * 128 * 4
+    one = _shape(B=3, T=70, H=50, dk=128, dv=64)                    # 150 heads: 64-column tiles, one a head
+    items = 3 * 50 * 2
+    assert lib.gdn2_chunk_fwd_output_fused(ctypes.byref(one)) == 1
+    assert lib.gdn2_chunk_fwd_output_workspace_size(ctypes.byref(one)) == \
+        items * RECORD + _flags(items) + 3 * 50 * 2 * 2 * 64 * 8 + 256
+    assert lib.gdn2_chunk_fwd_output_workspace_size(ctypes.byref(_shape(dv=96))) == ctypes.c_size_t(-1).value
+    s = one
+    need = lib.gdn2_chunk_fwd_output_workspace_size(ctypes.byref(s))
+
+    def call(g=f, gdt=0, wt=None, eps=1e-6, y=f, ydt=0, ws=f, nb=need, q=f):
+        return lib.gdn2_chunk_fwd_output(ctypes.byref(s), q, f, f, f, f, f, None, g, gdt, wt, F(eps), y, ydt, None,
+                                         ws, Z(nb), None)
+    assert call(g=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(gdt=2) == UNSUPPORTED
+    assert call(ydt=3) == UNSUPPORTED
+    assert call(wt=P(0x10008)) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(nb=need - 1) == WORKSPACE
