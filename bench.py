@@ -413,6 +413,50 @@ def phase_stamps(dev, wl):
     cyc = sum(p["window_cycles_mean"] * p["windows"] for p in out["phases"].values())
     out["gemm_phases"] = {"executed_frac": round(ex / cyc, 4), "useful_frac": round(us / cyc, 4),
                           "gap_to_target_executed": round(0.40 - ex / cyc, 4)}
+    out["chunk_gradient_phases"] = _chunk_phase_stamps(dev, wl, lib)
+    return out
+
+
+# phases of the chunk-gradient kernel's stamps (see bwd_chunk_kernel): name -> (from, to)
+CHUNK_PHASES = {"record into LDS": (0, 1), "value tile 0": (1, 2), "value tile 1": (2, 3),
+                "value tiles 2-3": (3, 4), "epilogue inputs": (4, 5), "dP/dA products and chain": (5, 6),
+                "dlog_alpha scans and stores": (6, 7)}
+
+
+def _chunk_phase_stamps(dev, wl, lib):
+    """Where a workgroup of the chunk-gradient kernel (the step's dominant launch) spends its
+    cycles: per item, each phase's window from the first of its eight waves entering to the last
+    leaving, from the instrumented library's stamps during one gdn2_chunk_bwd on the training
+    workload (the fast pass; one item per workgroup)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import linear_attention_sequence_gdn2_amd as gdn2
+    from linear_attention_sequence_gdn2_amd.inputs import WORKLOADS, make_workload
+    wl = WORKLOADS[WORKLOAD]                      # the training workload: it carries dO, dS_final
+    x = make_workload(wl)
+    names = ("q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_final")
+    d = {k: (x[k].to(dev) if x.get(k) is not None else None) for k in names}
+    args = tuple(d[k] for k in names)
+    items = wl.B * wl.H * ((wl.T + 63) // 64)
+    st = torch.zeros(items * 8 * 8, dtype=torch.int64, device=dev)
+    lib.gdn2_stamps_chunk.argtypes = [ctypes.c_void_p]
+    lib.gdn2_stamps_chunk.restype = ctypes.c_int
+    gdn2.bwd(*args)
+    torch.cuda.synchronize()
+    assert lib.gdn2_stamps_chunk(ctypes.c_void_p(st.data_ptr())) == 0
+    gdn2.bwd(*args)
+    torch.cuda.synchronize()
+    lib.gdn2_stamps_chunk(ctypes.c_void_p(0))
+    s = st.cpu().numpy().reshape(items, 8, 8).astype(np.float64)
+    assert (s > 0).all(), "missing stamps"
+    span = s[:, :, 7].max(axis=1) - s[:, :, 0].min(axis=1)
+    out = {"kernel": "bwd_chunk_kernel", "entry": "gdn2_chunk_bwd", "items": items,
+           "item_cycles_mean": round(float(span.mean()), 1), "phases": {}}
+    for name, (lo, hi) in CHUNK_PHASES.items():
+        win = s[:, :, hi].max(axis=1) - s[:, :, lo].min(axis=1)
+        out["phases"][name] = {"cycles_mean": round(float(win.mean()), 1),
+                               "share": round(float(win.sum() / span.sum()), 4)}
     return out
 
 

@@ -41,6 +41,11 @@
 
 namespace gdn2 {
 
+#ifdef GDN2_STAMPS
+// stamps of the fast pass of the chunk-gradient kernel: 8 per (item, wave), see bwd_chunk_kernel
+static __device__ unsigned long long *g_chunk_stamps;
+#endif
+
 // ---------------------------------------------------------------------------
 // chunk-parallel gradients of every token input
 // ---------------------------------------------------------------------------
@@ -134,6 +139,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const size_t srowK = baseK / DK + (size_t)(vk ? tk : T - 1) * H;   // per-token gate offset (SG)
     const int chh = hf * (DK / 2);               // first key channel of this half
     auto ch = [&](int e) { return chh + ch4(e, g); };
+#ifdef GDN2_STAMPS
+    // start 0, record in LDS 1, value tiles 0 and 1 done 2, 3, all tiles 4, epilogue inputs 5,
+    // element chain 6, end 7
+    unsigned long long *stp = !EX && g_chunk_stamps ? g_chunk_stamps + ((size_t)L * 8 + wv) * 8 : nullptr;
+#else
+    unsigned long long *stp = nullptr;
+#endif
+    (void)stp;
+    GDN2_STAMP(stp, 0);
 
     // ---- value-tile inputs, loaded one tile ahead into registers ----
     struct Tile {
@@ -243,6 +257,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     __syncthreads();
+    GDN2_STAMP(stp, 1);
 
     // ---- value tiles: X, U, dU, dX and the key-side accumulators ----
     f32x4 aQ[NMH], aE[NMH], aH[NMH], aPA[4];     // aPA: dP (half 0) or dA (half 1)
@@ -401,7 +416,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 }
         }
         __syncthreads();
+        if (j0 < 2 * VT) GDN2_STAMP(stp, 2 + j0 / VT);
     }
+    GDN2_STAMP(stp, 4);
 
     // ---- epilogue: dgamma, dP/dA products, element-wise chain ----
     // q, k and b are read again (their log-decay values are not used, so those loads are
@@ -504,6 +521,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         for (int q = 0; q < 8; ++q) sacc += sScr[8 * tid + q];
         sDG[tid] = sacc;
     }
+    GDN2_STAMP(stp, 5);
 
     // ---- element-wise chain (token 16w + r, channels ch(e)) ----
     // chain(mm, dq, dE, dK, h) for elements 4mm .. 4mm + 3, in the natural variables: dq, dE (the
@@ -624,6 +642,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             chain(mm, dq, dE, ck, h);
         }
     }
+    GDN2_STAMP(stp, 6);
     // dlog_alpha_t = sum_{s >= t} dG_s + dg_C, with dg_C = sum_s dKh_s Kh_s + dgamma gamma
     float xin[NEH], xtot[NEH], ytot[NEH];
 #pragma unroll
@@ -653,11 +672,21 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         __syncthreads();
         if (hf == 0 && g == 0 && vk) a.dla[srowK] = sl + sRed[kChunk + 16 * w + r];
     }
+    GDN2_STAMP(stp, 7);
   }
     if (EX) __syncthreads();   // the next chunk of the exact pass overwrites this one's LDS
     }
     }
 }
+
+#ifdef GDN2_STAMPS
+// the instrumented build only: where the chunk-gradient kernel's fast pass writes its phase
+// stamps (8 per item and wave; nullptr = none)
+extern "C" int gdn2_stamps_chunk(void *buf) {
+    unsigned long long *p = static_cast<unsigned long long *>(buf);
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_chunk_stamps), &p, sizeof(p)) == hipSuccess ? 0 : 4;
+}
+#endif
 
 // ---------------------------------------------------------------------------
 // host-side dispatch
