@@ -49,6 +49,112 @@ static __device__ unsigned long long *g_chunk_stamps;
 // ---------------------------------------------------------------------------
 // chunk-parallel gradients of every token input
 // ---------------------------------------------------------------------------
+
+// Value-tile inputs of the chunk-gradient kernel, loaded one tile ahead into registers.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DK>
+struct ChunkTile {
+    static constexpr int NSF = (DK * 8 + kChunkThreads - 1) / kChunkThreads;   // float4 of a state tile per thread
+    f32x4 s[NSF], d[NSF];    // S and dS' (channel idx/8, columns 4*(idx%8)..+3)
+    float o[4];              // dO; after the quad transpose: column tid%32, tokens 4*(tid/32)..+3
+    float v[4], wg[4];       // v and w of this wave's X tile; D layout after the quad transpose
+};
+
+// Value tile j0 (32 columns) of item L = (b * H + h) * NC + c.  Addresses: a base pointer common
+// to the workgroup (the item's chunk and the tile's first column) plus a 32-bit byte offset per
+// lane; the offsets stay inside one chunk of one (b, h), so they fit, and the loads take the
+// scalar-base + vector-offset form.
+template <int DK, bool BF16, bool GL, bool SG>
+__device__ __forceinline__ void chunk_load_tile(const BwdArgs &a, int NC, int L, int j0, ChunkTile<DK> &x, int tid) {
+    constexpr int NTH = kChunkThreads, NSF = ChunkTile<DK>::NSF;
+    constexpr unsigned ES = BF16 ? 2u : 4u, GS = GL ? 2u : 4u;
+    const int T = a.T, H = a.H, DV = a.DV;
+    const size_t tokV = (size_t)H * DV;
+    const int w = (tid >> 6) & 3, n = tid >> 8, r = tid & 15, g = (tid >> 4) & 3;
+    const int c = L % NC, bh = L / NC, h = bh % H, b = bh / H, t0 = c * kChunk;
+    const size_t stoff = ((size_t)bh * NC + c) * (size_t)DK * DV;
+    const size_t baseK = ((size_t)b * T * H + h) * DK;
+    const size_t tokBase = ((size_t)b * T * H + h) * DV + (size_t)t0 * tokV;
+    const unsigned last = (unsigned)(T - 1 - t0);   // last existing token of the chunk, from t0
+    const char *sb = reinterpret_cast<const char *>(a.states + stoff + j0);
+    const char *db = reinterpret_cast<const char *>(a.dstates + stoff + j0);
+#pragma unroll
+    for (int it = 0; it < NSF; ++it) {
+        int idx = tid + NTH * it;
+        idx = idx < DK * 8 ? idx : 0;
+        const unsigned o = (unsigned)((idx >> 3) * DV + 4 * (idx & 7)) * 4u;
+        x.s[it] = *reinterpret_cast<const f32x4 *>(sb + o);
+        x.d[it] = *reinterpret_cast<const f32x4 *>(db + o);
+    }
+    // Wide loads: a lane reads 4 consecutive columns of one token; the 4x4 transpose inside
+    // each quad of lanes, done at staging, turns that into one column of 4 tokens.
+    {
+        // dO: token 4 (tid / 32) + (tid % 4), columns 4 ((tid / 4) % 8) ..; after the
+        // transpose: column tid % 32, tokens 4 (tid / 32) ..
+        const char *ob = reinterpret_cast<const char *>(a.dO + tokBase + j0);
+        const unsigned tr = min((unsigned)(4 * (tid >> 5) + (tid & 3)), last);
+        const f32x4 o4 = *reinterpret_cast<const f32x4 *>(ob + (tr * (unsigned)tokV + 4u * ((tid >> 2) & 7)) * 4u);
+        x.o[0] = o4[0], x.o[1] = o4[1], x.o[2] = o4[2], x.o[3] = o4[3];
+    }
+    // v and w of the X tile: row 16w + 4g + (r % 4), columns 16n + 4 (r / 4) ..; after the
+    // transpose: rows 16w + 4g + i, column 16n + r (the D layout)
+    const unsigned vr = min((unsigned)(16 * w + 4 * g + (r & 3)), last);
+    const unsigned vo = vr * (unsigned)tokV + (unsigned)(16 * n + 4 * (r >> 2));
+    auto load4 = [](const char *p, bool b16, float (&y)[4]) {
+        if (b16) {
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+            y[0] = __uint_as_float(u[0] << 16), y[1] = __uint_as_float(u[0] & 0xffff0000u);
+            y[2] = __uint_as_float(u[1] << 16), y[3] = __uint_as_float(u[1] & 0xffff0000u);
+        } else {
+            const f32x4 f = *reinterpret_cast<const f32x4 *>(p);
+            y[0] = f[0], y[1] = f[1], y[2] = f[2], y[3] = f[3];
+        }
+    };
+    load4(reinterpret_cast<const char *>(a.v) + ((tokBase + j0) + vo) * ES, BF16, x.v);
+    if constexpr (SG) {
+        // gates per token or per channel (decided at run time): element loads, D layout as loaded
+        const bool wtok = a.scalar & kScalarWrite;
+        const char *wb = reinterpret_cast<const char *>(a.wg) + (wtok ? baseK / DK + (size_t)t0 * H : tokBase + j0) * GS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned tr = min((unsigned)(16 * w + 4 * g + i), last);
+            const unsigned ow = wtok ? tr * (unsigned)H : tr * (unsigned)tokV + (unsigned)(16 * n + r);
+            x.wg[i] = GL ? bf16_bits_to_float(*reinterpret_cast<const uint16_t *>(wb + ow * GS))
+                         : *reinterpret_cast<const float *>(wb + ow * GS);
+        }
+    } else {
+        load4(reinterpret_cast<const char *>(a.wg) + ((tokBase + j0) + vo) * GS, GL, x.wg);   // as stored
+    }
+}
+
+// The pieces of item L's chunk operand record the chunk-gradient kernel keeps (Kh and Et row
+// planes, T, P^T fragments, gamma), loaded into registers: the first half of its preparation.
+template <int DK>
+struct ChunkRecRegs {
+    u32x4 rv[DK / 16];   // 16-byte pieces of the four row planes, thread tid + 512 it
+    u32x4 th, tl;        // T hi and lo: row tid / 8, columns 8 (tid % 8) ..
+    u32x4 pv[4];         // the four P^T tiles of this lane (those with mt < w hold zeros)
+    float gm;            // gamma of channel tid (tid < DK)
+};
+
+template <int DK>
+__device__ __forceinline__ void chunk_load_record(const char *rc, int tid, ChunkRecRegs<DK> &x) {
+    using Rec = ChunkRecord<DK>;
+    constexpr int NTH = kChunkThreads;
+    static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
+    const int w = (tid >> 6) & 3, l = tid & 63, trow = tid >> 3, tc8 = 8 * (tid & 7);
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it)
+        x.rv[it] = *reinterpret_cast<const u32x4 *>(rc + Rec::oKh + (size_t)(tid + NTH * it) * 16);   // Kh, Et planes
+    x.th = *reinterpret_cast<const u32x4 *>(rc + Rec::oT + (size_t)(trow * kChunk + tc8) * 2);
+    x.tl = *reinterpret_cast<const u32x4 *>(rc + Rec::oT + (size_t)(kChunk * kChunk + trow * kChunk + tc8) * 2);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        x.pv[mt] = *reinterpret_cast<const u32x4 *>(rc + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16);
+    x.gm = reinterpret_cast<const float *>(rc + Rec::oGam)[tid < DK ? tid : 0];
+}
 // Eight waves in two halves of four.  Wave (hf, w) owns the 16 tokens 16w..16w+15 in
 // both halves; for the key-side element work and the key-side gradients it owns
 // channels of its half only (hf * DK/2 .. +DK/2), in the 4-group layout; on the value
@@ -118,10 +224,25 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const int *flags = reinterpret_cast<const int *>(reinterpret_cast<const char *>(a.factors) +
                                                      (size_t)nitems * factor_elems_per_chunk<DK>() * 2 +
                                                      record_flags_offset<DK>(nitems));
+    // Work list.  Fast pass: persistent (one workgroup per CU), items blockIdx.x, + gridDim.x, ...;
+    // each item loads the next one's record pieces and first value tile into registers during its
+    // scans and stores, where they are free and the loads' latency is hidden.  Exact pass: the
+    // flagged chunks of its share, gathered NTH candidates at a time.
+    const int nmine = EX ? 0 : (blockIdx.x < (unsigned)nitems ? (int)((nitems - 1 - blockIdx.x) / gridDim.x) + 1 : 0);
+    ChunkTile<DK> cur;               // value-tile inputs, one tile ahead (the next item's first in the fast pass)
+    ChunkRecRegs<DK> pr;
+    if (!EX && nmine > 0) {
+        const int L0 = blockIdx.x;
+        chunk_load_tile<DK, BF16, GL, SG>(a, NC, L0, 0, cur, threadIdx.x);
+        chunk_load_record<DK>(reinterpret_cast<const char *>(a.factors) +
+                                  (size_t)a.B * a.H * NC * factor_elems_per_chunk<DK>() * 2 +
+                                  (size_t)L0 * ChunkRecord<DK>::BYTES,
+                              threadIdx.x, pr);
+    }
     for (long base = blockIdx.x; base < (EX ? nitems : (long)blockIdx.x + 1); base += (long)gridDim.x * NTH) {
-    const int nwork = EX ? gather_flagged<NTH>(flags, nitems, base, gridDim.x, sList, sList + NTH) : 1;
+    const int nwork = EX ? gather_flagged<NTH>(flags, nitems, base, gridDim.x, sList, sList + NTH) : nmine;
     for (int wi = 0; wi < nwork; ++wi) {
-    const int L = EX ? sList[wi] : xcd_swizzle(blockIdx.x, gridDim.x);
+    const int L = EX ? sList[wi] : (int)blockIdx.x + wi * (int)gridDim.x;
     const int tid = threadIdx.x, wv = tid >> 6, hf = wv >> 2, w = wv & 3, l = tid & 63, r = l & 15, g = l >> 4;
     const int n = hf;                            // value column block of this wave's tiles
     const int c = L % NC, bh = L / NC, h = bh % a.H, b = bh / a.H;
@@ -130,7 +251,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
     const size_t baseK = ((size_t)b * T * H + h) * DK;
     const size_t baseV0 = ((size_t)b * T * H + h) * DV;
-    const size_t stoff = (((size_t)b * H + h) * NC + c) * (size_t)DK * DV;
+    const size_t tokBase = baseV0 + (size_t)t0 * tokV;
     const int kk_lo = (w >= 2) ? 1 : 0;
     const int nkk = (w >= 2) ? 2 : 1;
     const int tk = t0 + 16 * w + r;
@@ -149,109 +270,32 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     (void)stp;
     GDN2_STAMP(stp, 0);
 
-    // ---- value-tile inputs, loaded one tile ahead into registers ----
-    struct Tile {
-        float4 s[NSF], d[NSF];   // S and dS' (channel idx/8, columns 4*(idx%8)..+3)
-        float o[4];              // dO; after the quad transpose: column tid%32, tokens 4*(tid/32)..+3
-        float v[4], wg[4];       // v and w of this wave's X tile; D layout after the quad transpose
-    };
-    // Addresses: a base pointer common to the workgroup (this item's chunk and the tile's first
-    // column) plus a 32-bit byte offset per lane; the offsets stay inside one chunk of one (b, h),
-    // so they fit, and the loads take the scalar-base + vector-offset form.
-    const unsigned last = (unsigned)(T - 1 - t0);   // last existing token of the chunk, from t0
-    const size_t tokBase = baseV0 + (size_t)t0 * tokV;
-    constexpr unsigned ES = BF16 ? 2u : 4u, GS = GL ? 2u : 4u;
-    auto load_tile = [&](int j0, Tile &x, int tid) {
-        const int w = (tid >> 6) & 3, n = tid >> 8, r = tid & 15, g = (tid >> 4) & 3;
-        const char *sb = reinterpret_cast<const char *>(a.states + stoff + j0);
-        const char *db = reinterpret_cast<const char *>(a.dstates + stoff + j0);
-#pragma unroll
-        for (int it = 0; it < NSF; ++it) {
-            int idx = tid + NTH * it;
-            idx = idx < DK * 8 ? idx : 0;
-            const unsigned o = (unsigned)((idx >> 3) * DV + 4 * (idx & 7)) * 4u;
-            x.s[it] = *reinterpret_cast<const float4 *>(sb + o);
-            x.d[it] = *reinterpret_cast<const float4 *>(db + o);
-        }
-        // Wide loads: a lane reads 4 consecutive columns of one token; the 4x4 transpose inside
-        // each quad of lanes, done at staging, turns that into one column of 4 tokens.
-        {
-            // dO: token 4 (tid / 32) + (tid % 4), columns 4 ((tid / 4) % 8) ..; after the
-            // transpose: column tid % 32, tokens 4 (tid / 32) ..
-            const char *ob = reinterpret_cast<const char *>(a.dO + tokBase + j0);
-            const unsigned tr = min((unsigned)(4 * (tid >> 5) + (tid & 3)), last);
-            const float4 o4 =
-                *reinterpret_cast<const float4 *>(ob + (tr * (unsigned)tokV + 4u * ((tid >> 2) & 7)) * 4u);
-            x.o[0] = o4.x, x.o[1] = o4.y, x.o[2] = o4.z, x.o[3] = o4.w;
-        }
-        // v and w of the X tile: row 16w + 4g + (r % 4), columns 16n + 4 (r / 4) ..; after the
-        // transpose: rows 16w + 4g + i, column 16n + r (the D layout)
-        const unsigned vr = min((unsigned)(16 * w + 4 * g + (r & 3)), last);
-        const unsigned vo = vr * (unsigned)tokV + (unsigned)(16 * n + 4 * (r >> 2));
-        auto load4 = [](const char *p, bool b16, float (&y)[4]) {
-            if (b16) {
-                const uint2 u = *reinterpret_cast<const uint2 *>(p);
-                y[0] = __uint_as_float(u.x << 16), y[1] = __uint_as_float(u.x & 0xffff0000u);
-                y[2] = __uint_as_float(u.y << 16), y[3] = __uint_as_float(u.y & 0xffff0000u);
-            } else {
-                const float4 f = *reinterpret_cast<const float4 *>(p);
-                y[0] = f.x, y[1] = f.y, y[2] = f.z, y[3] = f.w;
-            }
-        };
-        load4(reinterpret_cast<const char *>(a.v) + ((tokBase + j0) + vo) * ES, BF16, x.v);
-        if constexpr (SG) {
-            // gates per token or per channel (decided at run time): element loads, D layout as loaded
-            const bool wtok = a.scalar & kScalarWrite;
-            const char *wb = reinterpret_cast<const char *>(a.wg) +
-                             (wtok ? baseK / DK + (size_t)t0 * H : tokBase + j0) * GS;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const unsigned tr = min((unsigned)(16 * w + 4 * g + i), last);
-                const unsigned ow = wtok ? tr * (unsigned)H : tr * (unsigned)tokV + (unsigned)(16 * n + r);
-                x.wg[i] = GL ? bf16_bits_to_float(*reinterpret_cast<const uint16_t *>(wb + ow * GS))
-                             : *reinterpret_cast<const float *>(wb + ow * GS);
-            }
-        } else {
-            load4(reinterpret_cast<const char *>(a.wg) + ((tokBase + j0) + vo) * GS, GL, x.wg);   // as stored
-        }
-    };
-
-    Tile cur;
-    load_tile(0, cur, tid);
-
-    // ---- preparation: the chunk operand record that the adjoint-factor kernel wrote
-    // (Kh and Et rows, T, P^T fragments and gamma), into LDS and registers
+    // ---- preparation: the chunk operand record that the adjoint-factor kernel wrote (Kh and
+    // Et rows, T, P^T fragments and gamma), into LDS and registers.  The fast pass loaded it (and
+    // the first value tile) during the previous item or before the first; the exact pass loads
+    // it here.
     using Rec = ChunkRecord<DK>;
     const char *rec = reinterpret_cast<const char *>(a.factors) +
                       (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)L * Rec::BYTES;
+    if (EX) {
+        chunk_load_tile<DK, BF16, GL, SG>(a, NC, L, 0, cur, tid);
+        chunk_load_record<DK>(rec, tid, pr);
+    }
     Split4 Pt[4];                  // lane holds P[16mt + 4g + i][16w + r] (zero for mt < w)
     {
-        constexpr int NROW = DK / 16;   // 16-byte pieces per thread of the four row planes
-        uint4 rv[NROW];
-#pragma unroll
-        for (int it = 0; it < NROW; ++it)
-            rv[it] = *reinterpret_cast<const uint4 *>(rec + Rec::oKh + (size_t)(tid + NTH * it) * 16);   // Kh, Et planes
-        static_assert(NTH == 8 * kChunk, "one thread per 8 elements of T");
         const int trow = tid >> 3, tc8 = 8 * (tid & 7);
-        const uint4 th = *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(trow * kChunk + tc8) * 2);
-        const uint4 tl =
-            *reinterpret_cast<const uint4 *>(rec + Rec::oT + (size_t)(kChunk * kChunk + trow * kChunk + tc8) * 2);
-        uint4 pv[4];   // all four tiles, those with mt < w hold zeros
+        if (tid < DK) sGam[tid] = pr.gm;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            pv[mt] = *reinterpret_cast<const uint4 *>(rec + Rec::oPt + (size_t)((4 * w + mt) * 64 + l) * 16);
-        if (tid < DK) sGam[tid] = reinterpret_cast<const float *>(rec + Rec::oGam)[tid];
-#pragma unroll
-        for (int it = 0; it < NROW; ++it) {
+        for (int it = 0; it < DK / 16; ++it) {
             const int idx = tid + NTH * it, plane = idx / (8 * DK), rem = idx % (8 * DK);
             const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
-            *reinterpret_cast<uint4 *>((plane < 2 ? sKt : sEt) + (plane & 1) * RK + row * PK + c8) = rv[it];
+            *reinterpret_cast<u32x4 *>((plane < 2 ? sKt : sEt) + (plane & 1) * RK + row * PK + c8) = pr.rv[it];
         }
-        *reinterpret_cast<uint4 *>(&sTs[trow * PT + tc8]) = th;
-        *reinterpret_cast<uint4 *>(&sTs[kChunk * PT + trow * PT + tc8]) = tl;
+        *reinterpret_cast<u32x4 *>(&sTs[trow * PT + tc8]) = pr.th;
+        *reinterpret_cast<u32x4 *>(&sTs[kChunk * PT + trow * PT + tc8]) = pr.tl;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const bf16x8 o = __builtin_bit_cast(bf16x8, pv[mt]);
+            const bf16x8 o = __builtin_bit_cast(bf16x8, pr.pv[mt]);
             Pt[mt].hi = __builtin_shufflevector(o, o, 0, 1, 2, 3);
             Pt[mt].lo = __builtin_shufflevector(o, o, 4, 5, 6, 7);
         }
@@ -285,10 +329,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
             const int idx = tid + NTH * it;
             if (idx < DK * 8) {
                 const int chn = idx >> 3, q = idx & 7;
-                const float4 sv = cur.s[it], dv = cur.d[it];
-                dgp[it] += (sv.x * dv.x + sv.y * dv.y) + (sv.z * dv.z + sv.w * dv.w);
-                const Split4 ss = split4(f32x4{sv.x, sv.y, sv.z, sv.w});
-                const Split4 ds = split4(f32x4{dv.x, dv.y, dv.z, dv.w});
+                const f32x4 sv = cur.s[it], dv = cur.d[it];
+                dgp[it] += (sv[0] * dv[0] + sv[1] * dv[1]) + (sv[2] * dv[2] + sv[3] * dv[3]);
+                const Split4 ss = split4(sv);
+                const Split4 ds = split4(dv);
                 *reinterpret_cast<bf16x4 *>(&S1[chn * PS + 4 * q]) = ss.hi;
                 *reinterpret_cast<bf16x4 *>(&S1[DK * PS + chn * PS + 4 * q]) = ss.lo;
                 *reinterpret_cast<bf16x4 *>(&D1[chn * PS + 4 * q]) = ds.hi;
@@ -316,7 +360,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
         __syncthreads();
         // next tile's loads are in flight during this tile's products
-        load_tile(j0 + VT < DV ? j0 + VT : j0, cur, tid);
+        chunk_load_tile<DK, BF16, GL, SG>(a, NC, L, j0 + VT < DV ? j0 + VT : j0, cur, tid);
 
         // X = Z - Et S and dU = P^T dO + Kh dS': tile (token block w, column block n)
         {
@@ -643,6 +687,16 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
     }
     GDN2_STAMP(stp, 6);
+    if (!EX) {
+        // the next item's preparation loads, in flight during the scans and stores below (the
+        // last item loads its own again: with a branch around the loads the compiler keeps two
+        // copies of these registers live and spills)
+        const int Ln = wi + 1 < nwork ? L + (int)gridDim.x : L;
+        chunk_load_tile<DK, BF16, GL, SG>(a, NC, Ln, 0, cur, tid);
+        chunk_load_record<DK>(reinterpret_cast<const char *>(a.factors) +
+                                  (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)Ln * Rec::BYTES,
+                              tid, pr);
+    }
     // dlog_alpha_t = sum_{s >= t} dG_s + dg_C, with dg_C = sum_s dKh_s Kh_s + dgamma gamma
     float xin[NEH], xtot[NEH], ytot[NEH];
 #pragma unroll
@@ -674,7 +728,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     }
     GDN2_STAMP(stp, 7);
   }
-    if (EX) __syncthreads();   // the next chunk of the exact pass overwrites this one's LDS
+    __syncthreads();   // the next item's preparation overwrites this one's LDS
     }
     }
 }
@@ -698,11 +752,12 @@ template <int DK, bool BF16, bool GL, bool SG>
 static hipError_t chunk_t(const BwdArgs &a, hipStream_t st) {
     const int NC = (a.T + kChunk - 1) / kChunk;
     const long items = (long)a.B * a.H * NC;
-    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG, false>), dim3((unsigned)items), dim3(kChunkThreads), 0, st,
+    // both passes persistent: one workgroup per CU (the kernel's LDS allows no second one)
+    const long grid = items < cu_count() ? items : cu_count();
+    hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG, false>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st,
                        a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long grid = items < cu_count() ? items : cu_count();
     hipLaunchKernelGGL((bwd_chunk_kernel<DK, BF16, GL, SG, true>), dim3((unsigned)grid), dim3(kChunkThreads), 0, st,
                        a);
     return hipGetLastError();
