@@ -51,8 +51,6 @@ static __device__ unsigned long long *g_chunk_stamps;
 // ---------------------------------------------------------------------------
 
 // Value-tile inputs of the chunk-gradient kernel, loaded one tile ahead into registers.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
 template <int DK>
 struct ChunkTile {
     static constexpr int NSF = (DK * 8 + kChunkThreads - 1) / kChunkThreads;   // float4 of a state tile per thread
@@ -360,7 +358,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         }
         __syncthreads();
         // next tile's loads are in flight during this tile's products
-        chunk_load_tile<DK, BF16, GL, SG>(a, NC, L, j0 + VT < DV ? j0 + VT : j0, cur, tid);
+        {
+            // the next tile of this item, or after the last one the first tile of the next item
+            // (fast pass; the exact pass reloads its last tile), chosen by address: no branch
+            const bool more = j0 + VT < DV;
+            const int Lt = more ? L : (EX ? L : (wi + 1 < nwork ? L + (int)gridDim.x : L));
+            chunk_load_tile<DK, BF16, GL, SG>(a, NC, Lt, more ? j0 + VT : (EX ? j0 : 0), cur, tid);
+        }
 
         // X = Z - Et S and dU = P^T dO + Kh dS': tile (token block w, column block n)
         {
@@ -688,11 +692,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     }
     GDN2_STAMP(stp, 6);
     if (!EX) {
-        // the next item's preparation loads, in flight during the scans and stores below (the
-        // last item loads its own again: with a branch around the loads the compiler keeps two
-        // copies of these registers live and spills)
+        // the next item's record pieces, in flight during the scans and stores below (its first
+        // value tile was loaded during the last tile; the last item loads its own again: with a
+        // branch around the loads the compiler keeps two copies of these registers live and spills)
         const int Ln = wi + 1 < nwork ? L + (int)gridDim.x : L;
-        chunk_load_tile<DK, BF16, GL, SG>(a, NC, Ln, 0, cur, tid);
         chunk_load_record<DK>(reinterpret_cast<const char *>(a.factors) +
                                   (size_t)a.B * H * NC * factor_elems_per_chunk<DK>() * 2 + (size_t)Ln * Rec::BYTES,
                               tid, pr);
