@@ -242,10 +242,12 @@ __device__ __forceinline__ int ch4(int e, int g) { return 16 * (e >> 2) + 4 * g 
 template <int DK, bool BF16, bool GL = false, bool SG = false>
 struct KeyRaw4 {
     static constexpr int NM = DK / 16;
-    uint2 q[NM], k[NM];
-    float4 qx[NM], kx[NM];
-    float4 la[NM], bg[NM];          // fp32 gate values
-    uint2 la16[NM], bg16[NM];       // bf16 gate logits
+    // native vector types: HIP's vector structs keep arrays of them that live across loops in
+    // scratch memory
+    u32x2 q[NM], k[NM];
+    f32x4 qx[NM], kx[NM];
+    f32x4 la[NM], bg[NM];           // fp32 gate values
+    u32x2 la16[NM], bg16[NM];       // bf16 gate logits
     bool valid;
 
     // q, k: qkv dtype; rowoff: element offset of channel 0 of the token row; srow: the
@@ -262,32 +264,32 @@ struct KeyRaw4 {
         for (int m = 0; m < NM; ++m) {
             const size_t off = rowoff + 16 * m + 4 * g;
             if (BF16) {
-                q[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(qp) + off);
-                k[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(kp) + off);
+                q[m] = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(qp) + off);
+                k[m] = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(kp) + off);
             } else {
-                qx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qp) + off);
-                kx[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(kp) + off);
+                qx[m] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(qp) + off);
+                kx[m] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(kp) + off);
             }
             if (GL) {
-                la16[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(lap) + off);
-                bg16[m] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(bgp) + off);
+                la16[m] = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(lap) + off);
+                bg16[m] = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(bgp) + off);
             } else if (SG) {
-                la[m] = (scalar & 1) ? make_float4(sla, sla, sla, sla)
-                                     : *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(lap) + off);
-                bg[m] = (scalar & 2) ? make_float4(sbg, sbg, sbg, sbg)
-                                     : *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(bgp) + off);
+                la[m] = (scalar & 1) ? f32x4{sla, sla, sla, sla}
+                                     : *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(lap) + off);
+                bg[m] = (scalar & 2) ? f32x4{sbg, sbg, sbg, sbg}
+                                     : *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(bgp) + off);
             } else {
-                la[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(lap) + off);
-                bg[m] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(bgp) + off);
+                la[m] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(lap) + off);
+                bg[m] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(bgp) + off);
             }
         }
     }
 
-    static __device__ __forceinline__ void bf16x4_to(const uint2 &u, float *o) {
-        o[0] = __builtin_bit_cast(float, u.x << 16);
-        o[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
-        o[2] = __builtin_bit_cast(float, u.y << 16);
-        o[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+    static __device__ __forceinline__ void bf16x4_to(const u32x2 &u, float *o) {
+        o[0] = __builtin_bit_cast(float, u[0] << 16);
+        o[1] = __builtin_bit_cast(float, u[0] & 0xffff0000u);
+        o[2] = __builtin_bit_cast(float, u[1] << 16);
+        o[3] = __builtin_bit_cast(float, u[1] & 0xffff0000u);
     }
 
     // q and k only (zero for a missing token)
@@ -298,8 +300,11 @@ struct KeyRaw4 {
                 bf16x4_to(q[m], &qf[4 * m]);
                 bf16x4_to(k[m], &kf[4 * m]);
             } else {
-                qf[4 * m + 0] = qx[m].x; qf[4 * m + 1] = qx[m].y; qf[4 * m + 2] = qx[m].z; qf[4 * m + 3] = qx[m].w;
-                kf[4 * m + 0] = kx[m].x; kf[4 * m + 1] = kx[m].y; kf[4 * m + 2] = kx[m].z; kf[4 * m + 3] = kx[m].w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qf[4 * m + i] = qx[m][i];
+                    kf[4 * m + i] = kx[m][i];
+                }
             }
         }
 #pragma unroll
@@ -325,8 +330,11 @@ struct KeyRaw4 {
                     bgf[4 * m + i] = gate_act<GL>(y[i]);
                 }
             } else {
-                laf[4 * m + 0] = la[m].x; laf[4 * m + 1] = la[m].y; laf[4 * m + 2] = la[m].z; laf[4 * m + 3] = la[m].w;
-                bgf[4 * m + 0] = bg[m].x; bgf[4 * m + 1] = bg[m].y; bgf[4 * m + 2] = bg[m].z; bgf[4 * m + 3] = bg[m].w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    laf[4 * m + i] = la[m][i];
+                    bgf[4 * m + i] = bg[m][i];
+                }
             }
         }
 #pragma unroll
