@@ -102,3 +102,16 @@ def test_one_call_backward_with_fused_sweeps(B, T, H, dk, dv, extra):
 def test_full_size_fwdbwd_workload():
     wl = WORKLOADS["fwdbwd_bf16_B4H16T4096d128"]
     _run(make_workload(wl))
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,qkv", [
+    (1, 64 * 257 - 30, 1, 64, 64, "bf16"),    # 257 chunks: one workgroup walks two items, the rest one
+    (2, 64 * 200 + 7, 1, 128, 64, "bf16"),    # 402 chunks: some workgroups two items, ragged tail
+    (1, 64 * 255, 1, 32, 64, "f32"),          # 255 chunks: fewer items than workgroups would be
+])
+def test_chunk_gradient_work_split(B, T, H, dk, dv, qkv):
+    """The chunk-gradient kernel is persistent (one workgroup per CU; a workgroup loads its next
+    item's record and first value tile during the current item, and its last item loads its own
+    again): item counts just above, well above and below the workgroup count, against the
+    oracle."""
+    _run(make_inputs(B, T, H, dk, dv, seed=9900 + T + dk, qkv_dtype=qkv, s0_std=0.1, grads=True))
