@@ -311,8 +311,10 @@ def lean_bench(dev, names, iters=10):
 # Wave (hf, w) of the eight: half hf, token block w; a split-bf16 product is three MFMAs (two
 # for X = Z - Et S, which takes the hi part of Et).
 def _record_phase_mfma(hf, w):
-    n_a = sum(1 for mt in range(w + 1) if (mt & 1) == hf)      # A tiles of this wave
-    ap = 12 * (n_a + w + 1)                                     # (A and P tiles) x 4 steps x 3
+    # A and P: the ten (query block, key block) pairs of a chunk come from a queue that all eight
+    # waves share; a pair is an A and a P tile of 4 steps x 3 MFMAs, 240 per item in all, counted
+    # here on wave 0 (only the sum over the waves is used)
+    ap = 240 if (hf, w) == (0, 0) else 0
     solve16 = (24 + 3 * (w * (w + 1) // 2 + w)) if hf == 0 else 0
     return {"a5 A,P": (ap, ap // 3, 0), "a6 solve": (0, 0, solve16)}
 

@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     unsigned long long *stp = nullptr;
 #endif
     (void)stp;
+    GDN2_STAMP_REGS;
     GDN2_STAMP(stp, 0);
 
     // ---- preparation: the chunk operand record that the adjoint-factor kernel wrote (Kh and
@@ -464,7 +465,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
                 }
         }
         __syncthreads();
-        if (j0 < 2 * VT) GDN2_STAMP(stp, 2 + j0 / VT);
+        if (j0 == 0) GDN2_STAMP(stp, 2);
+        if (j0 == VT) GDN2_STAMP(stp, 3);
     }
     GDN2_STAMP(stp, 4);
 
@@ -730,6 +732,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         if (hf == 0 && g == 0 && vk) a.dla[srowK] = sl + sRed[kChunk + 16 * w + r];
     }
     GDN2_STAMP(stp, 7);
+    GDN2_STAMP_FLUSH(stp);
   }
     __syncthreads();   // the next item's preparation overwrites this one's LDS
     }

@@ -115,9 +115,14 @@ __device__ __forceinline__ void solve_T(const float *sA, float *sT, int w, int r
 // row block I of A), then T is written over A.  The strictly upper 16x16
 // blocks of the buffer must be zero and stay zero.  4 workgroup barriers,
 // which every wave of the workgroup reaches; only waves with `active` set
-// (one per row block w) compute.
-template <int PA>
-__device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g, bool active = true) {
+// (one per row block w) compute.  The others call side(k) before barrier k
+// (k = 0 .. 3): work of their own that touches neither A nor T.
+struct NoSide {
+    __device__ void operator()(int) const {}
+};
+template <int PA, class Side = NoSide>
+__device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g, bool active = true,
+                                                const Side &side = Side()) {
     f32x4 arow[3];
 #pragma unroll
     for (int K = 0; K < 3; ++K)
@@ -135,10 +140,13 @@ __device__ __forceinline__ void solve_T_inplace(float *sAT, int w, int r, int g,
         const f32x4 tB = unit_lower_inverse16(nA, nB, r, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sAT[(16 * w + 4 * g + i) * PA + 16 * w + r] = tB[i];
+    } else {
+        side(0);
     }
     __syncthreads();
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
+        if (!active) side(d);
         if (active && w >= d) {
             const int I = w, J = w - d;
             f32x4 Y = {0.f, 0.f, 0.f, 0.f};

@@ -51,18 +51,34 @@ constexpr int kChunkThreads = 2 * kThreads;   // workgroup of the chunk-parallel
 // above this point (bounds the live registers of a wave).
 #define GDN2_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Phase stamps of the instrumented build (-DGDN2_STAMPS, libgdn2_stamps.so): lane 0 of a wave
-// writes the shader-clock counter (s_memtime) to buf[idx] when buf is set.  In the normal
-// build the macro is empty.
+// Phase stamps of the instrumented build (-DGDN2_STAMPS, libgdn2_stamps.so).  GDN2_STAMP_REGS
+// declares a wave's eight stamp registers (zero); GDN2_STAMP(buf, idx) reads the shader-clock
+// counter (s_memtime) into register idx (a constant); GDN2_STAMP_FLUSH(buf) has lane 0 write all
+// eight to buf[0..7] when buf is set.  The flush comes once, after a unit of work's last stamp:
+// a store per stamp would queue behind the kernel's own memory traffic and stretch the phases it
+// measures.  In the normal build the macros are empty.
 #ifdef GDN2_STAMPS
-#define GDN2_STAMP(buf, idx)                                                      \
-    do {                                                                         \
-        if ((buf) != nullptr && (threadIdx.x & 63) == 0)                         \
-            (buf)[idx] = __builtin_amdgcn_s_memtime();                           \
+#define GDN2_STAMP_REGS unsigned long long gdn2_stv[8] = {0, 0, 0, 0, 0, 0, 0, 0}
+#define GDN2_STAMP(buf, idx)                          \
+    do {                                             \
+        gdn2_stv[idx] = __builtin_amdgcn_s_memtime(); \
+    } while (0)
+#define GDN2_STAMP_FLUSH(buf)                                                              \
+    do {                                                                                  \
+        if ((buf) != nullptr && (threadIdx.x & 63) == 0) {                                \
+            _Pragma("unroll") for (int gdn2_i = 0; gdn2_i < 8; ++gdn2_i)(buf)[gdn2_i] =    \
+                gdn2_stv[gdn2_i];                                                         \
+        }                                                                                 \
     } while (0)
 #else
+#define GDN2_STAMP_REGS \
+    do {                \
+    } while (0)
 #define GDN2_STAMP(buf, idx) \
     do {                     \
+    } while (0)
+#define GDN2_STAMP_FLUSH(buf) \
+    do {                      \
     } while (0)
 #endif
 

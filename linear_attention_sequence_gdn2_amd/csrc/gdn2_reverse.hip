@@ -74,7 +74,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     constexpr int oAT = oQt + B_ROWS, oGam = oAT + kChunk * PA * 4;
     constexpr int oEx = oGam + DK * 4, B_EX = EX ? kSliceFloats * 4 : 0;
     constexpr int oList = oEx + B_EX, B_LIST = EX ? (NTH + 4) * 4 : 0;
-    constexpr int SMEM = oList + B_LIST;
+    constexpr int oCnt = oList + B_LIST;                // tile-pair queue of the forward records
+    constexpr int oPf = oCnt + 16;                      // their P fragment tiles, until stored
+    constexpr int SMEM = oPf + (FWD && !EX && BF16 ? Rec::B_FR : 0);
     static_assert(SMEM <= 160 * 1024, "LDS budget of a CU");
     static_assert(kChunk * PA <= kSliceFloats, "P fits over the slices");
 
@@ -85,6 +87,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     float *sGam = reinterpret_cast<float *>(smem + oGam);
     float *sEx = reinterpret_cast<float *>(smem + oEx);
     int *sList = reinterpret_cast<int *>(smem + oList);
+    int *sCnt = reinterpret_cast<int *>(smem + oCnt);
+    char *sPf = smem + oPf;
+    // Forward records (FWD, fast pass, bf16 inputs): A and P come from a queue of the ten (query
+    // block, key block) pairs that any wave takes, with no global access in that phase; the row
+    // planes and the P tiles are stored by the half that the solve leaves idle, during the solve.
+    // (With fp32 inputs the next item's inputs take too many registers across the solve for it.)
+    constexpr bool QUEUE = FWD && !EX && BF16;
 
     const int NC = (a.T + kChunk - 1) / kChunk;
     const int T = a.T, H = a.H;
@@ -133,17 +142,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     const int chh = hf * (DK / 2);
     auto ch = [&](int e) { return chh + ch4(e, g); };
 #ifdef GDN2_STAMPS
-    // element phase 0-1, record rows 1-2, A and P 2-3, the solve 3-4, T 4-5, W, Q2, R 5-6
+    // element phase 0-1, record rows 1-2, A and P 2-3, the solve 3-4, T 4-5, W, Q2, R 5-6; in
+    // the queued forward records, 2-6 issues the next item's loads and 6-3 is A and P
     unsigned long long *stp = !EX && g_factor_stamps ? g_factor_stamps + ((size_t)L * 8 + wv) * 8 : nullptr;
 #else
     unsigned long long *stp = nullptr;
 #endif
     (void)stp;
+    GDN2_STAMP_REGS;
     GDN2_STAMP(stp, 0);
     __bf16 *fac = reinterpret_cast<__bf16 *>(a.factors) + (size_t)L * factor_elems_per_chunk<DK>();
     char *rec = recs + (size_t)L * Rec::BYTES;
 
     for (int idx = tid; idx < kChunk * PA; idx += NTH) sAT[idx] = 0.f;
+    if (QUEUE && tid == 0) *sCnt = 0;
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH], ev[NEH];   // ev (e = b k) and G kept for the exact products
     int unsafe;
     {
@@ -198,10 +210,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 
     // ---- record: Kh rows (Kt diag(gamma) from the fast pass's Kt rows; the exact pass's LDS
     // rows are Kh already), one thread per 8 channels of a row (hi and lo) ----
-#pragma unroll
-    for (int it = 0; it < (8 * DK + NTH - 1) / NTH; ++it) {
-        const int idx = tid + NTH * it, row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
-        if (idx >= 8 * DK) break;
+    auto kh_group = [&](int idx) {
+        const int row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
         Split8 kh = frag_8(&sKt[row * PK + c8], &sKt[RK + row * PK + c8]);
         if (!EX) {
             const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&sGam[c8]);
@@ -214,18 +224,69 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         const size_t ro = (size_t)(row * DK + c8) * 2;
         *reinterpret_cast<bf16x8 *>(rec + Rec::oKh + ro) = kh.hi;
         *reinterpret_cast<bf16x8 *>(rec + Rec::oKh + Rec::PLANE + ro) = kh.lo;
-    }
-    // ---- record: Et and Qt rows (dense pitch) ----
-    static_assert((4 * 8 * DK) % NTH == 0, "row planes split evenly over the threads");
-#pragma unroll
-    for (int it = 0; it < 4 * 8 * DK / NTH; ++it) {
-        const int idx = tid + NTH * it, plane = 2 + idx / (8 * DK), rem = idx % (8 * DK);
+    };
+    // ---- record: Et and Qt rows (dense pitch); plane 2 + k: Et hi, Et lo, Qt hi, Qt lo ----
+    auto eq_piece = [&](int plane, int rem) {
         const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
         const __bf16 *src = (plane < 4 ? sEt : sQt) + (plane & 1) * RK + row * PK + c8;
-        if (!(FWD && BF16 && plane == 3))   // the bf16 forward sweep reads the hi plane of Et only
-            *reinterpret_cast<uint4 *>(rec + Rec::oKh + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
-                *reinterpret_cast<const uint4 *>(src);
+        *reinterpret_cast<uint4 *>(rec + Rec::oKh + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
+            *reinterpret_cast<const uint4 *>(src);
+    };
+    if constexpr (!QUEUE) {
+#pragma unroll
+        for (int it = 0; it < (8 * DK + NTH - 1) / NTH; ++it) {
+            const int idx = tid + NTH * it, row = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+            if (idx >= 8 * DK) break;
+            Split8 kh = frag_8(&sKt[row * PK + c8], &sKt[RK + row * PK + c8]);
+            if (!EX) {
+                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&sGam[c8]);
+                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&sGam[c8 + 4]);
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = ((float)kh.hi[i] + (float)kh.lo[i]) * (i < 4 ? g0[i] : g1[i - 4]);
+                kh = split8(x);
+            }
+            const size_t ro = (size_t)(row * DK + c8) * 2;
+            *reinterpret_cast<bf16x8 *>(rec + Rec::oKh + ro) = kh.hi;
+            *reinterpret_cast<bf16x8 *>(rec + Rec::oKh + Rec::PLANE + ro) = kh.lo;
+        }
+        static_assert((4 * 8 * DK) % NTH == 0, "row planes split evenly over the threads");
+#pragma unroll
+        for (int it = 0; it < 4 * 8 * DK / NTH; ++it) {
+            const int idx = tid + NTH * it, plane = 2 + idx / (8 * DK), rem = idx % (8 * DK);
+            const int row = rem / (DK / 8), c8 = 8 * (rem % (DK / 8));
+            const __bf16 *src = (plane < 4 ? sEt : sQt) + (plane & 1) * RK + row * PK + c8;
+            if (!(FWD && BF16 && plane == 3))   // the bf16 forward sweep reads the hi plane of Et only
+                *reinterpret_cast<uint4 *>(rec + Rec::oKh + (size_t)plane * Rec::PLANE + (size_t)(row * DK + c8) * 2) =
+                    *reinterpret_cast<const uint4 *>(src);
+        }
     }
+    // The same stores in the forward records, by the waves of half 1 during the solve: part k of
+    // four before its barrier k.  Items: the 8 DK Kh groups, the pieces of the Et and Qt planes
+    // the sweep reads (the bf16 sweep reads the hi plane of Et only), then the 16 P tiles' lane
+    // pieces (zero above the diagonal blocks, the others from LDS).
+    auto row_stores = [&](int k) {
+        constexpr int NG = 8 * DK, NPL = BF16 ? 3 : 4, NROW = NG * (1 + NPL), NITEM = NROW + 16 * 64;
+        constexpr int NH = NTH / 2, PER = (NITEM + 4 * NH - 1) / (4 * NH);
+        const int t1 = (int)threadIdx.x - NH;
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const int idx = (it * 4 + k) * NH + t1;
+            if (idx < NG) {
+                kh_group(idx);
+            } else if (idx < NROW) {
+                const int p = idx - NG, kq = p / NG;
+                eq_piece(2 + kq + (NPL == 3 && kq >= 1 ? 1 : 0), p % NG);
+            } else if (idx < NITEM) {
+                const int pc = idx - NROW, tile = pc >> 6;   // tile 4 qb + kb
+                const uint4 v = (tile & 3) > (tile >> 2) ? uint4{0u, 0u, 0u, 0u}
+                                                         : *reinterpret_cast<const uint4 *>(sPf + (size_t)pc * 16);
+                *reinterpret_cast<uint4 *>(rec + Rec::oP + (size_t)pc * 16) = v;
+            }
+            // one item's registers at a time (the next item's inputs are live across the solve)
+            asm volatile("" ::: "memory");
+        }
+    };
 
     Split4 Pf[4];
     GDN2_STAMP(stp, 2);
@@ -255,6 +316,47 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
                 for (int i = 0; i < 4; ++i) acc[i] = sP[(16 * mt + 4 * g + i) * PA + 16 * w + r];
                 store_frag_tile(reinterpret_cast<__bf16 *>(rec + Rec::oPt) + (size_t)((4 * w + mt) * 64) * 8, l, acc);
             }
+        }
+        __syncthreads();
+    } else if constexpr (QUEUE) {
+        // the next item's key-side inputs first.  Issuing them waits for room in the memory queue
+        // (the previous item's row stores are still draining); the waves that get through first
+        // take the pairs meanwhile, so the products run under that wait.  (Issued after the
+        // products instead, the item took 27.4K cycles against 23.7K.)
+        issue(Ln);
+        GDN2_STAMP(stp, 6);   // (slot 6 is free in the forward records)
+        // ---- A and P from the pair queue: pair p = (query block qb, key block kb <= qb); its
+        // A and P tiles share the Kt fragment and run as two interleaved MFMA chains ----
+        auto grab = [&]() {
+            int p = 0;
+            if (l == 0) p = atomicAdd(sCnt, 1);
+            return __builtin_amdgcn_readfirstlane(p);
+        };
+        for (int p = grab(); p < 10; p = grab()) {
+            const int qb = p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3)), kb = p - qb * (qb + 1) / 2;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKS; ++j) {
+                const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * kb + r, j, g);
+                accA = mfma32x3(kf, row_frag4<PK>(sEt, sEt + RK, 16 * qb + r, j, g), accA);
+                accP = mfma32x3(kf, row_frag4<PK>(sQt, sQt + RK, 16 * qb + r, j, g), accP);
+            }
+            // lane holds A[16qb + r][16kb + 4g + i] (strictly lower) and P[16qb + r][16kb + 4g + i]
+            // (key <= query: the query reads the updated state)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (!(16 * kb + 4 * g + i < 16 * qb + r)) accA[i] = 0.f;
+                if (!(16 * kb + 4 * g + i <= 16 * qb + r)) accP[i] = 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(&sAT[(16 * qb + r) * PA + 16 * kb + 4 * g]) = accA;
+            const Split4 pf = split4(accP);
+            bf16x8 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = pf.hi[i];
+                o[4 + i] = pf.lo[i];
+            }
+            *reinterpret_cast<bf16x8 *>(sPf + (size_t)((4 * qb + kb) * 64 + l) * 16) = o;
         }
         __syncthreads();
     } else {
@@ -324,7 +426,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         __syncthreads();
     }
     GDN2_STAMP(stp, 3);
-    solve_T_inplace<PA>(sAT, w, r, g, hf == 0);   // ends with a barrier
+    if constexpr (QUEUE)
+        solve_T_inplace<PA>(sAT, w, r, g, hf == 0, row_stores);   // ends with a barrier
+    else
+        solve_T_inplace<PA>(sAT, w, r, g, hf == 0);
     GDN2_STAMP(stp, 4);
     {
         // record: T as split bf16 [row][col], one thread per 8 elements
@@ -337,6 +442,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
     }
     GDN2_STAMP(stp, 5);
     if (FWD) {
+        GDN2_STAMP_FLUSH(stp);
         __syncthreads();   // the next item overwrites the LDS this one still reads
         continue;
     }
@@ -411,6 +517,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         store_frag_tile(fac + (size_t)(am * NM + bm) * kFragTile, l, rt);
     }
     GDN2_STAMP(stp, 6);
+    GDN2_STAMP_FLUSH(stp);
     __syncthreads();   // the next item overwrites the LDS this one still reads
     }
     }

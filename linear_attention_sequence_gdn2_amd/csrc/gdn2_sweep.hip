@@ -602,6 +602,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         unsigned long long *stp = nullptr;
 #endif
         (void)stp;
+        GDN2_STAMP_REGS;
 
         // ---- loads: Kh rows, v, w of the next chunk (T, P and gamma of this one are in flight);
         // with the epilogue after stage A, where they leave room for its registers ----
@@ -769,6 +770,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         store_state_lds(wv, r, g);     // sS is not read again in this chunk
         __syncthreads();
         GDN2_STAMP(stp, 7);
+        GDN2_STAMP_FLUSH(stp);
         // the next chunk's Kh rows (sK is not read again in this chunk) and its z = w * v,
         // from loads issued at this chunk's start
         if (c + 1 < c_hi) {
