@@ -416,6 +416,60 @@ def phase_stamps(dev, wl):
     out["gemm_phases"] = {"executed_frac": round(ex / cyc, 4), "useful_frac": round(us / cyc, 4),
                           "gap_to_target_executed": round(0.40 - ex / cyc, 4)}
     out["chunk_gradient_phases"] = _chunk_phase_stamps(dev, wl, lib)
+    out["resident_microkernel"] = _probe_phases(dev, lib)
+    return out
+
+
+# GEMM-phase microkernels of the instrumented library (gdn2_probe.hip): the same phases with their
+# operands resident in LDS and registers, no global memory inside the windows.  phase id -> windows
+PROBE_PHASES = {0: {"a5 A,P": (0, 1)}, 1: {"a6 solve": (0, 1)},
+                2: {"a7 X,QtS": (0, 1), "a7 U=TX": (2, 3), "a7 O": (4, 5), "a7 S'": (5, 6)}}
+
+
+def _probe_phases(dev, lib, reps=64, skip=4):
+    """Per-phase MFMA use of the forward's GEMM phases with resident operands: one workgroup of
+    eight waves per CU, `reps` repetitions each (the first `skip` not counted).  A window runs from
+    the first wave's start stamp to the last wave's end stamp of one repetition; the MFMA counts are
+    the product kernels' (the same loops).  Beside it, the launch's MFMA flops over its event time,
+    against the 2.5 PFLOP/s peak."""
+    import ctypes
+    import numpy as np
+    import torch
+    fn = lib.gdn2_probe_gemm_phases
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    waves = [(wv >> 2, wv & 3) for wv in range(8)]
+    out = {"workgroups": grid, "reps": reps, "reps_counted": reps - skip, "phases": {}}
+    for phase, windows in PROBE_PHASES.items():
+        st = torch.zeros(grid * 8 * reps * 8, dtype=torch.int64, device=dev)
+        sink = torch.zeros(grid, dtype=torch.float32, device=dev)
+        assert fn(phase, grid, reps, ctypes.c_void_p(st.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                  ctypes.c_void_p(stream.cuda_stream)) == 0   # warm-up launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert fn(phase, grid, reps, ctypes.c_void_p(st.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                  ctypes.c_void_p(stream.cuda_stream)) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        s = st.cpu().numpy().reshape(grid, 8, reps, 8).astype(np.float64)[:, :, skip:, :]
+        launch_flops = 0.0
+        for name, (lo, hi) in windows.items():
+            counts = [(_record_phase_mfma if phase < 2 else _sweep_phase_mfma)(hf, w)[name] for hf, w in waves]
+            e32 = sum(c[0] for c in counts)
+            u32 = sum(c[1] for c in counts)
+            e16 = sum(c[2] for c in counts)
+            win = s[:, :, :, hi].max(axis=1) - s[:, :, :, lo].min(axis=1)   # [workgroup, rep]
+            cyc = float(win.mean())
+            launch_flops += (e32 * 16384 + e16 * 8192) * grid * reps
+            out["phases"][name] = {
+                "window_cycles_mean": round(cyc, 1), "mfma_executed_per_window": int(e32 + e16),
+                "executed_frac": round((e32 * 16384 + e16 * 8192) / (cyc * MFMA_FLOPS_PER_CU_CYCLE), 4),
+                "useful_frac": round((u32 * 16384 + e16 * 8192 / 3) / (cyc * MFMA_FLOPS_PER_CU_CYCLE), 4)}
+        out["phases"][list(windows)[0]]["launch_ms"] = round(ms, 4)
+        out["phases"][list(windows)[0]]["launch_mfma_TFLOPs"] = round(launch_flops / (ms * 1e-3) / 1e12, 1)
     return out
 
 

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libgdn2.so")
 STAMPS_LIB = os.path.join(HERE, "libgdn2_stamps.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gdn2_api.cpp", "gdn2_bwd.hip", "gdn2_reverse.hip", "gdn2_step.hip", "gdn2_output.hip",
-           "gdn2_sweep.hip", "gdn2_noalloc.cpp"]
+           "gdn2_sweep.hip", "gdn2_noalloc.cpp", "gdn2_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -376,6 +376,50 @@ __device__ __forceinline__ Split8 row_frag4(const __bf16 *hi, const __bf16 *lo, 
                     &lo[row * PK + 32 * j + 4 * g], &lo[row * PK + 32 * j + 16 + 4 * g]);
 }
 
+// A = strictly-lower(Et Kt^T) and P = lower(Qt Kt^T) of one chunk, from [token][channel] split-bf16
+// rows in LDS (Kt, Et, Qt: hi plane, lo plane RK elements later, pitch PK).  The ten pairs (query
+// block qb, key block kb <= qb) come from a queue that every wave of the workgroup draws from
+// (*cnt: zero beforehand, and a barrier between); a pair's A and P tiles share the Kt fragment and
+// run as two interleaved MFMA chains.  A goes to sAT [64][PA] fp32 (tiles above the diagonal
+// blocks are left as they are); P goes to sPf as split-bf16 fragment tiles (tile 4 qb + kb, 16
+// bytes per lane: four hi then four lo values of P[16qb + r][16kb + 4g + i]).  No global access.
+template <int DK, int PK, int PA>
+__device__ __forceinline__ void ap_pair_queue(const __bf16 *sKt, const __bf16 *sEt, const __bf16 *sQt, float *sAT,
+                                              char *sPf, int *cnt, int l, int r, int g) {
+    constexpr int NKS = DK / 32, RK = kChunk * PK;
+    auto grab = [&]() {
+        int p = 0;
+        if (l == 0) p = atomicAdd(cnt, 1);
+        return __builtin_amdgcn_readfirstlane(p);
+    };
+    for (int p = grab(); p < 10; p = grab()) {
+        const int qb = p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3)), kb = p - qb * (qb + 1) / 2;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+            const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * kb + r, j, g);
+            accA = mfma32x3(kf, row_frag4<PK>(sEt, sEt + RK, 16 * qb + r, j, g), accA);
+            accP = mfma32x3(kf, row_frag4<PK>(sQt, sQt + RK, 16 * qb + r, j, g), accP);
+        }
+        // lane holds A[16qb + r][16kb + 4g + i] (strictly lower) and P[16qb + r][16kb + 4g + i]
+        // (key <= query: the query reads the updated state)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!(16 * kb + 4 * g + i < 16 * qb + r)) accA[i] = 0.f;
+            if (!(16 * kb + 4 * g + i <= 16 * qb + r)) accP[i] = 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(&sAT[(16 * qb + r) * PA + 16 * kb + 4 * g]) = accA;
+        const Split4 pf = split4(accP);
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[i] = pf.hi[i];
+            o[4 + i] = pf.lo[i];
+        }
+        *reinterpret_cast<bf16x8 *>(sPf + (size_t)((4 * qb + kb) * 64 + l) * 16) = o;
+    }
+}
+
 // ---- adjoint factor tiles (R and Q2^T of a chunk, MFMA fragment order) ----
 constexpr int kFragTile = 64 * 8;   // bf16 per stored 16x16 factor tile
 

@@ -327,37 +327,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
         GDN2_STAMP(stp, 6);   // (slot 6 is free in the forward records)
         // ---- A and P from the pair queue: pair p = (query block qb, key block kb <= qb); its
         // A and P tiles share the Kt fragment and run as two interleaved MFMA chains ----
-        auto grab = [&]() {
-            int p = 0;
-            if (l == 0) p = atomicAdd(sCnt, 1);
-            return __builtin_amdgcn_readfirstlane(p);
-        };
-        for (int p = grab(); p < 10; p = grab()) {
-            const int qb = p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3)), kb = p - qb * (qb + 1) / 2;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < NKS; ++j) {
-                const Split8 kf = row_frag4<PK>(sKt, sKt + RK, 16 * kb + r, j, g);
-                accA = mfma32x3(kf, row_frag4<PK>(sEt, sEt + RK, 16 * qb + r, j, g), accA);
-                accP = mfma32x3(kf, row_frag4<PK>(sQt, sQt + RK, 16 * qb + r, j, g), accP);
-            }
-            // lane holds A[16qb + r][16kb + 4g + i] (strictly lower) and P[16qb + r][16kb + 4g + i]
-            // (key <= query: the query reads the updated state)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (!(16 * kb + 4 * g + i < 16 * qb + r)) accA[i] = 0.f;
-                if (!(16 * kb + 4 * g + i <= 16 * qb + r)) accP[i] = 0.f;
-            }
-            *reinterpret_cast<f32x4 *>(&sAT[(16 * qb + r) * PA + 16 * kb + 4 * g]) = accA;
-            const Split4 pf = split4(accP);
-            bf16x8 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[i] = pf.hi[i];
-                o[4 + i] = pf.lo[i];
-            }
-            *reinterpret_cast<bf16x8 *>(sPf + (size_t)((4 * qb + kb) * 64 + l) * 16) = o;
-        }
+        ap_pair_queue<DK, PK, PA>(sKt, sEt, sQt, sAT, sPf, sCnt, l, r, g);
         __syncthreads();
     } else {
         // ---- record: P^T fragments ----
