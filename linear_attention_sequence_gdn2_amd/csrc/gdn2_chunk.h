@@ -5,6 +5,9 @@
 // NE = DK/4 channels of its token.
 #pragma once
 
+#ifndef GDN2_SPLIT_PAIRS
+#define GDN2_SPLIT_PAIRS 0
+#endif
 #include "gdn2_device.h"
 
 namespace gdn2 {
@@ -191,9 +194,21 @@ __device__ __forceinline__ Split8 frag_tr(const __bf16 *hi, const __bf16 *lo, in
 }
 
 // Split-bf16 MFMA fragment with the "4-group" contraction order: slots 0..3 are
-// taken from p0[0..3] and slots 4..7 from p1[0..3].
+// taken from p0[0..3] and slots 4..7 from p1[0..3].  SPLIT: the four 8-byte reads are kept apart.
+// Left to itself the compiler pairs them into ds_read2_b64, and the pieces of a pair then share
+// banks with another lane's (the hi pieces 32 bytes apart: lane r's second with lane r + 2's
+// first, at every row pitch); four ds_read_b64 are each conflict-free at rows of 8 mod 16 bf16.
+// Offsets the compiler cannot see through keep them apart.
+template <int SPLIT = GDN2_SPLIT_PAIRS>
 __device__ __forceinline__ Split8 frag_2x4(const __bf16 *hi0, const __bf16 *hi1, const __bf16 *lo0,
                                            const __bf16 *lo1) {
+    if constexpr (SPLIT != 0) {
+        int z0 = 0, z1 = 0, z2 = 0;
+        asm volatile("" : "+s"(z0), "+s"(z1), "+s"(z2));
+        hi1 += z0;
+        lo0 += z1;
+        lo1 += z2;
+    }
     Split8 f;
     const bf16x4 a = *reinterpret_cast<const bf16x4 *>(hi0);
     const bf16x4 b = *reinterpret_cast<const bf16x4 *>(hi1);
@@ -370,10 +385,10 @@ struct KeyRaw4 {
 };
 
 // Key-side fragment (4-group contraction order) of row `row` of a [row][channel] tile.
-template <int PK>
+template <int PK, int SPLIT = GDN2_SPLIT_PAIRS>
 __device__ __forceinline__ Split8 row_frag4(const __bf16 *hi, const __bf16 *lo, int row, int j, int g) {
-    return frag_2x4(&hi[row * PK + 32 * j + 4 * g], &hi[row * PK + 32 * j + 16 + 4 * g],
-                    &lo[row * PK + 32 * j + 4 * g], &lo[row * PK + 32 * j + 16 + 4 * g]);
+    return frag_2x4<SPLIT>(&hi[row * PK + 32 * j + 4 * g], &hi[row * PK + 32 * j + 16 + 4 * g],
+                           &lo[row * PK + 32 * j + 4 * g], &lo[row * PK + 32 * j + 16 + 4 * g]);
 }
 
 // A = strictly-lower(Et Kt^T) and P = lower(Qt Kt^T) of one chunk, from [token][channel] split-bf16

@@ -162,12 +162,12 @@ __device__ __forceinline__ void bwd_reverse_body(const BwdArgs &a, const int L, 
 #pragma unroll
             for (int j = 0; j < NKS; ++j)
                 acc = mfma32x3(frag_from_tiles(fr[2 * j], fr[2 * j + 1]),
-                               row_frag4<PK>(sDb, sDb + VT * PK, 16 * n + r, j, g), acc);
+                               row_frag4<PK, 1>(sDb, sDb + VT * PK, 16 * n + r, j, g), acc);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const __bf16 *oh = &sOb[(16 * n + r) * PT + 32 * kk], *ol = oh + VT * PT;
                 acc = mfma32x3(frag_from_tiles(fq[2 * kk], fq[2 * kk + 1]),
-                               frag_2x4(oh + 4 * g, oh + 16 + 4 * g, ol + 4 * g, ol + 16 + 4 * g), acc);
+                               frag_2x4<1>(oh + 4 * g, oh + 16 + 4 * g, ol + 4 * g, ol + 16 + 4 * g), acc);
             }
             DS[s] = acc;
         }
