@@ -710,9 +710,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
         sb = group_sum4(sb);
         if (hf == 1 && g == 0) sRed[16 * w + r] = sb;
     }
-    chunk_scan<NEH, DK>(xin, xtot, reinterpret_cast<float *>(smem + oTotA), w, r, ch);
-    if (SG && (a.scalar & kScalarErase) && hf == 0 && g == 0 && vk) a.db[srowK] = sb + sRed[16 * w + r];
-    chunk_scan<NEH, DK>(yh, ytot, reinterpret_cast<float *>(smem + oTotB), w, r, ch);
+    if constexpr (!SG) {
+        // both scans behind one barrier (with per-token gates their registers do not fit at once)
+        chunk_scan2<NEH, DK>(xin, xtot, reinterpret_cast<float *>(smem + oTotA), yh, ytot,
+                             reinterpret_cast<float *>(smem + oTotB), w, r, ch);
+    } else {
+        chunk_scan<NEH, DK>(xin, xtot, reinterpret_cast<float *>(smem + oTotA), w, r, ch);
+        if ((a.scalar & kScalarErase) && hf == 0 && g == 0 && vk) a.db[srowK] = sb + sRed[16 * w + r];
+        chunk_scan<NEH, DK>(yh, ytot, reinterpret_cast<float *>(smem + oTotB), w, r, ch);
+    }
     float sl = 0.f;                // per-token dlog_alpha partial (decay per token)
 #pragma unroll
     for (int mm = 0; mm < NMH; ++mm) {

@@ -39,6 +39,35 @@ __device__ __forceinline__ void chunk_scan(float (&x)[NE], float (&tot)[NE], flo
     }
 }
 
+// Two chunk_scan's at once (x with totals through sTotX, y through sTotY): one barrier.
+template <int NE, int DK, typename ChanFn>
+__device__ __forceinline__ void chunk_scan2(float (&x)[NE], float (&xt)[NE], float *sTotX, float (&y)[NE],
+                                            float (&yt)[NE], float *sTotY, int w, int r, ChanFn ch) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        x[e] = row_scan16(x[e]);
+        y[e] = row_scan16(y[e]);
+    }
+    if (r == 15) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            sTotX[w * DK + ch(e)] = x[e];
+            sTotY[w * DK + ch(e)] = y[e];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int c = ch(e);
+        const float a0 = sTotX[c], a1 = sTotX[DK + c], a2 = sTotX[2 * DK + c], a3 = sTotX[3 * DK + c];
+        const float b0 = sTotY[c], b1 = sTotY[DK + c], b2 = sTotY[2 * DK + c], b3 = sTotY[3 * DK + c];
+        x[e] += (w > 0 ? a0 : 0.f) + (w > 1 ? a1 : 0.f) + (w > 2 ? a2 : 0.f);
+        y[e] += (w > 0 ? b0 : 0.f) + (w > 1 ? b1 : 0.f) + (w > 2 ? b2 : 0.f);
+        xt[e] = (a0 + a1) + (a2 + a3);
+        yt[e] = (b0 + b1) + (b2 + b3);
+    }
+}
+
 // Inverse of one unit-lower 16x16 block, (I + N)^-1 with N strictly lower, so
 // N^16 = 0 and (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly.  The
 // powers are formed on MFMA in both the row layout (lane holds X[r][4g+i]) and
