@@ -46,14 +46,15 @@ BWD_BYTES_PER_TOKHEAD = 5888
 # per-kernel algorithmic bytes per token-head of the four launches of a step:
 #   adjoint factors     : q,k 512 + log_alpha,b 1024
 #                         + factors (128*128 + 64*128)*4 / 64 tokens = 1536
-#                         + chunk operand record 180736 / 64 tokens = 2824      -> 5896
+#                         + chunk operand record 150016 / 64 tokens = 2344      -> 5416
 #   forward sweep       : record operands it reads (Kt, Qt split, Et hi, T, P,
 #                         gamma: 115200 / 64 tokens) 1800 + v 256 + w 512
 #                         + o 512 + chunk states 1024                           -> 4104
 #   reverse sweep       : factors 1536 + dO 512 + dstates 1024                  -> 3072
-#   chunk gradients     : q,k,v 768 + b,w 1024 + dO 512 + states, dstates 2048
-#                         + record (Kt, Et split, T, P^T, G, gamma: 131584 / 64)
-#                         2056 + dq,dk,dv,dlog_alpha,db,dw 3072                 -> 9480
+#   chunk gradients     : q,k,v 768 + log_alpha,b,w 1536 + dO 512
+#                         + states, dstates 2048 + record (Kh, Et split, T, P^T,
+#                         decay offsets, gamma: 100864 / 64) 1576
+#                         + dq,dk,dv,dlog_alpha,db,dw 3072                      -> 9512
 # with the gates given as bf16 logits each pass reads 1536 -> 768 gate bytes per token-head
 GATE_BYTES_SAVED_PER_TOKHEAD = 768
 LOGIT_WORKLOAD = "logits_bf16_B8H16T2048d128"
@@ -68,9 +69,9 @@ FWD_SWEEP_BYTES_PER_TOKHEAD = 4104
 #   sweep (o, S_final)  : record operands 1800 + v 256 + w 512 + o 512           -> 3080
 FWD_RECORDS_BYTES_PER_TOKHEAD = 3336
 FWD_INFER_SWEEP_BYTES_PER_TOKHEAD = 3080
-BWD_FACTORS_BYTES_PER_TOKHEAD = 5896
+BWD_FACTORS_BYTES_PER_TOKHEAD = 5416
 BWD_REVERSE_BYTES_PER_TOKHEAD = 3072
-BWD_GRADS_BYTES_PER_TOKHEAD = 9480
+BWD_GRADS_BYTES_PER_TOKHEAD = 9512
 
 
 def _kernel_sources_digest():

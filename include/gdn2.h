@@ -110,7 +110,7 @@ typedef struct {
 
 /* Bytes of device workspace gdn2_chunk_fwd needs; (size_t)-1 if the shape is invalid.
  * The forward first writes forward-only chunk records (the key-side operands of every
- * chunk, about 2.8 KB per token-head at dk = 128, and one strong-decay flag per chunk)
+ * chunk, about 2.3 KB per token-head at dk = 128, and one strong-decay flag per chunk)
  * and then sweeps over them; the workspace holds those records.  With bf16 q/k/v,
  * dk in {64, 128}, dv a multiple of 64, so few heads that the sweep would keep at most
  * one CU in four busy and 64 chunks or more, the sequence is also split into segments
@@ -167,8 +167,8 @@ int gdn2_chunk_bwd(const gdn2_shape *shape,
 size_t gdn2_chunk_states_bytes(const gdn2_shape *shape);
 
 /* Bytes of the factor buffer of gdn2_chunk_bwd_factors: per (batch, head, chunk) the
- * adjoint factors, (dk*dk + 64*dk)*4 bytes, the chunk's key-side operands, about
- * 772*dk + 33000 bytes (rounded up to 256), and a strong-decay flag (4 bytes; the flags
+ * adjoint factors, (dk*dk + 64*dk)*4 bytes, the chunk's key-side operands,
+ * 788*dk + 49152 bytes (rounded up to 256), and a strong-decay flag (4 bytes; the flags
  * rounded up to 256); (size_t)-1 if the shape is invalid. */
 size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
 
@@ -181,8 +181,8 @@ size_t gdn2_chunk_factors_bytes(const gdn2_shape *shape);
  * (gdn2_chunk_factors_bytes() bytes, device memory owned by the caller, opaque
  * layout of split-bf16 MFMA tiles), followed by the key-side operands of every chunk
  * that the token gradients need as well (the decay-absorbed key and erase-key rows,
- * T = (I + A)^-1, P, the decay prefix) and each chunk's strong-decay flag, so that they
- * are formed once.  Two launches: every chunk, then the exact pass over flagged chunks.
+ * T = (I + A)^-1, P, the decay scan's per-block offsets) and each chunk's strong-decay
+ * flag, so that they are formed once.  Two launches: every chunk, then the exact pass over flagged chunks.
  * Read by gdn2_chunk_bwd_reverse and gdn2_chunk_bwd_grads. */
 int gdn2_chunk_bwd_factors(const gdn2_shape *shape, const void *q, const void *k,
                            const void *log_alpha, const void *b, void *factors, void *stream);
@@ -320,8 +320,8 @@ int gdn2_chunk_fwd_output_fused(const gdn2_shape *shape);
  * - Limit: the array holds gdn2_chunk_fwd_noalloc_max_bytes() = 256 MiB on each GPU, from
  *   the first call on that GPU until the process ends.  The batch is processed in groups of
  *   batch elements whose records fit (gdn2_chunk_fwd_workspace_size of the group); a shape
- *   whose single batch element needs more than the array (at dk = 128 about 181 KB per head
- *   and 64 tokens, so H * T up to about 94,000) returns GDN2_ERR_SCRATCH before any launch.
+ *   whose single batch element needs more than the array (at dk = 128 about 150 KB per head
+ *   and 64 tokens, so H * T up to about 114,000) returns GDN2_ERR_SCRATCH before any launch.
  * - The array is shared by every call on a GPU and keeps the last call's contents (nothing in
  *   it needs clearing: every call writes all it reads).  Calls that overlap on one GPU, on
  *   any streams, race on it and must be serialised by the caller.

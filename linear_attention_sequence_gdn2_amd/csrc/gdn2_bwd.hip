@@ -471,8 +471,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     GDN2_STAMP(stp, 4);
 
     // ---- epilogue: dgamma, dP/dA products, element-wise chain ----
-    // q, k and b are read again (their log-decay values are not used, so those loads are
-    // dropped), and the decay prefix G comes from the record here: only this chain uses it, and
+    // q, k, log alpha and b are read again, and the decay prefix G is formed from log alpha with
+    // the factor kernel's cross-block offsets from the record: only this chain uses it, and
     // leaving it out of the preparation shortens the loads the first value tile waits for.  The lane
     // indices are derived afresh from an opaque copy of the thread index, so that no
     // address arithmetic of the preparation is kept live across the value loop.
@@ -535,15 +535,17 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) 
     float qf[NEH], kf[NEH], G[NEH], bgf[NEH];
     KeyRaw4<DK / 2, BF16, GL, SG> raw;
     raw.issue(a.q, a.k, a.la, a.bg, rowK + chh, g, vk, srowK, a.scalar);
-    f32x4 gv[NEH / 4];             // the decay prefix of this thread's elements, from the record
+    f32x4 pre4[NEH / 4];           // decay offsets of this wave's token block, channels ch(4m) ..
 #pragma unroll
-    for (int e4 = 0; e4 < NEH / 4; ++e4)
-        gv[e4] = *reinterpret_cast<const f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + 4 * e4) * 4);
+    for (int m4 = 0; m4 < NEH / 4; ++m4)
+        pre4[m4] = *reinterpret_cast<const f32x4 *>(rec + Rec::oPre + (size_t)(w * DK + chh + 16 * m4 + 4 * g) * 4);
     raw.unpack(qf, kf, G, bgf);
     float dact[NEH];               // d log_alpha / d stored decay input
     raw.decay_dact_all(dact);
+    // G: the log2 decay prefix, as the factor kernel's chunk_scan forms it
 #pragma unroll
-    for (int e = 0; e < NEH; ++e) G[e] = gv[e / 4][e % 4];
+    for (int e = 0; e < NEH; ++e) G[e] *= kLog2e;
+    scan_with_offsets<NEH>(G, pre4);
     if constexpr (!EX) {
         // Qt rows of this half's channels again
 #pragma unroll

@@ -39,6 +39,29 @@ __device__ __forceinline__ void chunk_scan(float (&x)[NE], float (&tot)[NE], flo
     }
 }
 
+// The offsets chunk_scan adds to the in-wave prefixes, from the per-block totals it leaves in
+// sTot (the same sums in the same order): pre = sum of the totals of the token blocks before w.
+// Thread t < 4 DK writes the offset of block t / DK, channel t % DK, to pre[t].  Call after a
+// chunk_scan, before sTot is overwritten.
+template <int DK, int NTH>
+__device__ __forceinline__ void chunk_scan_offsets(const float *sTot, float *pre, int tid) {
+#pragma unroll
+    for (int t = tid; t < 4 * DK; t += NTH) {
+        const int w = t / DK, c = t % DK;
+        const float t0 = sTot[c], t1 = sTot[DK + c], t2 = sTot[2 * DK + c];
+        pre[t] = (w > 0 ? t0 : 0.f) + (w > 1 ? t1 : 0.f) + (w > 2 ? t2 : 0.f);
+    }
+}
+
+// chunk_scan's result without its barrier, given its offsets: x[e] (log2-decay of this lane's
+// elements) becomes the inclusive prefix G; pre4[m] holds the offsets of channels ch(4m) ..
+// ch(4m + 3) of this lane's token block.
+template <int NE>
+__device__ __forceinline__ void scan_with_offsets(float (&x)[NE], const f32x4 (&pre4)[NE / 4]) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) x[e] = row_scan16(x[e]) + pre4[e / 4][e % 4];
+}
+
 // Two chunk_scan's at once (x with totals through sTotX, y through sTotY): one barrier.
 template <int NE, int DK, typename ChanFn>
 __device__ __forceinline__ void chunk_scan2(float (&x)[NE], float (&xt)[NE], float *sTotX, float (&y)[NE],
@@ -485,8 +508,10 @@ constexpr size_t factor_elems_per_chunk() {
 //                      lane (r, g) holds P[16w + r][16mt + 4g + i], hi then lo (zero for mt > w)
 //   Every tile is written, so readers load all four of a block row unconditionally (a
 //   load under a branch would make the compiler wait for all loads in flight).
-//   G                  the log2 decay prefix, per thread of the 512-thread workgroup in
-//                      its element order (token 16w + r, channels DK/2 * hf + ch4(e, g))
+//   PRE                [4][DK] fp32: per token block w and key channel, the log2 decay of the
+//                      chunk's tokens before the block (the cross-wave part of chunk_scan), so
+//                      that a reader forms the decay prefix G from log alpha with one in-wave
+//                      scan (scan_with_offsets) and no barrier
 //   gamma              [DK] fp32, the chunk's total decay per key channel
 template <int DK>
 struct ChunkRecord {
@@ -496,8 +521,8 @@ struct ChunkRecord {
     static constexpr int oT = oQt + ROWS, B_T = kChunk * kChunk * 2 * 2;
     static constexpr int B_FR = 16 * 64 * 8 * 2;                // 16 fragment tiles of 64 lanes x 8 bf16
     static constexpr int oPt = oT + B_T, oP = oPt + B_FR;
-    static constexpr int oG = oP + B_FR, B_G = kChunkThreads * (DK / 8) * 4;
-    static constexpr int oGam = oG + B_G;
+    static constexpr int oPre = oP + B_FR, B_PRE = 4 * DK * 4;
+    static constexpr int oGam = oPre + B_PRE;
     static constexpr int BYTES = (oGam + DK * 4 + 255) / 256 * 256;
 };
 

@@ -49,13 +49,13 @@ __device__ __forceinline__ void store_frag_tile(__bf16 *tile, int l, const f32x4
 // Eight waves in two halves, as in bwd_chunk_kernel: wave (hf, w) owns tokens
 // 16w..16w+15 and, for the element work, the channels of half hf.
 // FWD: forward-only records (a.factors holds just the records): the rows, T, P and gamma
-// that the forward sweep reads, without the adjoint factors, P^T or G (and without the Et lo
-// plane for bf16 q/k/v, whose sweep reads the hi plane only).
+// that the forward sweep reads, without the adjoint factors, P^T or the decay offsets (and
+// without the Et lo plane for bf16 q/k/v, whose sweep reads the hi plane only).
 // EX: the exact pass.  The fast pass (EX false) forms A = Et Kt^T and P = Qt Kt^T from the
 // factorised rows Kt = k exp(-G), and flags every chunk in which some channel's decay gamma
 // is below kGamMin, where exp(-G) may leave fp32 range; the exact pass then redoes only the
 // flagged chunks, with A and P from the pairwise decays (gdn2_exact.h) and R = diag(gamma) -
-// W^T Kh.  The record's Kh, Et, Qt rows, gamma and G are the same in both passes.
+// W^T Kh.  The record's Kh, Et, Qt rows, gamma and decay offsets are the same in both passes.
 template <int DK, bool BF16, bool GL, bool SG, bool FWD, bool EX>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
     constexpr int NTH = kChunkThreads;
@@ -175,12 +175,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
                 reinterpret_cast<float *>(rec + Rec::oGam)[ch(e)] = gm;
             }
         }
-        if (!FWD) {
-#pragma unroll
-            for (int e = 0; e < NEH; e += 4)
-                *reinterpret_cast<f32x4 *>(rec + Rec::oG + (size_t)(tid * NEH + e) * 4) =
-                    f32x4{G[e], G[e + 1], G[e + 2], G[e + 3]};
-        }
+        // the scan's cross-block offsets, from which the chunk-gradient kernel forms G again
+        if (!FWD) chunk_scan_offsets<DK, NTH>(sTot, reinterpret_cast<float *>(rec + Rec::oPre), tid);
 #pragma unroll
         for (int mm = 0; mm < NMH; ++mm) {
             f32x4 et, qt, kt;

@@ -56,8 +56,8 @@ def _flags(items):
 
 
 # per chunk: the chunk operand record (Kh, Et, Qt rows and T split in bf16, 16 P^T and 16 P
-# fragment tiles, the decay prefix, gamma; rounded up to 256)
-RECORD = (6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 128 * 4 + 128 * 4 + 255) // 256 * 256
+# fragment tiles, the decay scan's offsets per token block and channel, gamma; rounded up to 256)
+RECORD = (6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 4 * 128 * 4 + 128 * 4 + 255) // 256 * 256
 
 
 def test_workspace_and_state_sizes():
@@ -288,7 +288,7 @@ def test_forward_workspace():
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=128, dv=32))) == \
         items * record + _flags(items)
     # dk = 32: the smaller record of that width
-    rec32 = (6 * 64 * 32 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * 32 * 4 + 32 * 4 + 255) // 256 * 256
+    rec32 = (6 * 64 * 32 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 4 * 32 * 4 + 32 * 4 + 255) // 256 * 256
     assert lib.gdn2_chunk_fwd_workspace_size(ctypes.byref(_shape(B=8, T=2048, H=16, dk=32, dv=128))) == \
         items * rec32 + _flags(items)
 

@@ -45,7 +45,7 @@ def test_segmented_forward(B, T, H, dk, dv, extra):
     s = gdn2.make_shape(B, T, H, dk, dv, torch.bfloat16, torch.bfloat16 if extra.get("gate_logits") else torch.float32,
                         7 if extra.get("token_gates") else 0)
     nc = (T + 63) // 64
-    rec = 6 * 64 * dk * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 64 * dk * 4 + dk * 4
+    rec = 6 * 64 * dk * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 4 * dk * 4 + dk * 4
     rec = (rec + 255) // 256 * 256
     cus = device_cus()
     assert B * H * (dv // 64) * 4 <= cus, "the shape is meant to take the segmented path"
