@@ -288,8 +288,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 // the previous chunk is in its products:
 //   chunk c start      issue Kh rows, v, w of chunk c + 1
 //   [A] X, Qt S        (Et, Qt rows and S from LDS)                 barrier
-//   [B] U = T X        issue T of chunk c + 1; Et, Qt rows of chunk c + 1 into LDS
-//                                                                    barrier
+//   [B] U = T X        issue T of chunk c + 1; with STATES store S (the chunk's start state);
+//                      Et, Qt rows of chunk c + 1 into LDS           barrier
 //   [C] O; S'          issue Et, Qt rows of chunk c + 2; after O, P of chunk c + 1;
 //                      after S', gamma of chunk c + 1; S' into LDS   barrier
 //   Kh rows of chunk c + 1 into LDS
@@ -615,19 +615,6 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
             // the row sums and gate values of the pending chunk, two stages ahead of their use
             epi_issue(c > c_lo ? c - 1 : c_lo);   // unconditional: at c_lo its values go unused
         }
-        if (STATES) {
-            // one 16-byte store per tile: the quad transpose gives the lane row 16m + 4g + (r & 3),
-            // columns 16n + 4(r >> 2) ..
-            float *dst = a.states + (((size_t)b * H + h) * NC + c) * (size_t)DK * DV + j0;
-#pragma unroll
-            for (int s = 0; s < NTS; ++s) {
-                const int id = wv * NTS + s, m = id / NCB, n = id % NCB;
-                float x[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
-                quad_transpose4(x);
-                *reinterpret_cast<float4 *>(&dst[(size_t)(16 * m + 4 * g + (r & 3)) * DV + 16 * n + 4 * (r >> 2)]) =
-                    make_float4(x[0], x[1], x[2], x[3]);
-            }
-        }
 
         // ---- [A] X = Z - Et S and Qt S: tiles (token block w, column blocks 2hf, 2hf + 1) ----
         GDN2_STAMP(stp, 0);
@@ -679,6 +666,21 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
                 }
             }
             load_T(recs + (size_t)cn * Rec::BYTES, Tf);
+        if (STATES) {
+            // the chunk-start state (S is updated only in S'), here rather than at the chunk's
+            // start, where the stores held up the issue of the next chunk's loads.  One 16-byte
+            // store per tile: the quad transpose gives the lane row 16m + 4g + (r & 3), columns
+            // 16n + 4(r >> 2) ..
+            float *dst = a.states + (((size_t)b * H + h) * NC + c) * (size_t)DK * DV + j0;
+#pragma unroll
+            for (int s = 0; s < NTS; ++s) {
+                const int id = wv * NTS + s, m = id / NCB, n = id % NCB;
+                float x[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
+                quad_transpose4(x);
+                *reinterpret_cast<float4 *>(&dst[(size_t)(16 * m + 4 * g + (r & 3)) * DV + 16 * n + 4 * (r >> 2)]) =
+                    make_float4(x[0], x[1], x[2], x[3]);
+            }
+        }
 #pragma unroll
             for (int n = 0; n < CBW; ++n) {
                 const int cb = CBW * hf + n;
