@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
 //   [A] X, Qt S        (Et, Qt rows and S from LDS)                 barrier
 //   [B] U = T X        issue T of chunk c + 1; with STATES store S (the chunk's start state);
 //                      Et, Qt rows of chunk c + 1 into LDS           barrier
-//   [C] O; S'          issue Et, Qt rows of chunk c + 2; after O, P of chunk c + 1;
+//   [C] O; S'          after O, P of chunk c + 1 and the Et, Qt rows of chunk c + 2;
 //                      after S', gamma of chunk c + 1; S' into LDS   barrier
 //   Kh rows of chunk c + 1 into LDS
 // Wave (hf, w) owns tokens 16w..16w+15 and columns 32hf..32hf+31 of X, U and O, and
@@ -701,8 +701,6 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
         if constexpr (EPI) {
             if (c > c_lo) epi_finish(c - 1);   // y of the pending chunk; frees eo for this one
         }
-#pragma unroll
-        for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(cn2, it, tid);
         if (OUT) {
             Split4 Pf[4];
 #pragma unroll
@@ -753,6 +751,10 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
             }
             load_P(recs + (size_t)cn * Rec::BYTES, pv);
         }
+        // the Et/Qt rows of chunk c + 2, after O's products (issued before them, they held the
+        // products up behind a full memory queue)
+#pragma unroll
+        for (int it = 0; it < NEP; ++it) eqn[it] = eq_piece(cn2, it, tid);
         GDN2_STAMP(stp, 5);
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
