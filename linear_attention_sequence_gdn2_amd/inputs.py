@@ -229,3 +229,45 @@ def make_output_inputs(B, T, H, dv, seed, *, g_dtype="f32"):
     weight = torch.rand(dv, generator=gen) + 0.5
     dy = torch.randn(B, T, H, dv, generator=gen)
     return {"o": o, "g": g, "weight": weight, "dy": dy}
+
+
+def make_inputs_device(B, T, H, dk, dv, seed, device, *, s0_std=0.0, grads=False, read_after_write=False):
+    """The bf16 workload recipe above (channel gates, log(sigmoid(N(3,1))) decay), drawn on
+    ``device`` with a seeded device generator: for shapes whose host-side generation would
+    take minutes (tensors of several GiB).  The same seed gives the same tensors on the same
+    device type; they are not the values make_inputs draws on the host.  Draw order: q, k, v,
+    log_alpha, b, w, S0, dO, dS_final.
+
+    ``read_after_write=True`` replaces q and k by one hot key (a uniformly drawn channel per
+    (b, t, h), drawn after dS_final) and b by ones: the erase-then-write case of the rule in
+    which every output equals w * v of its own token."""
+    g = torch.Generator(device=device).manual_seed(int(seed))
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32, device=device)
+
+    def unit_bf16(shape):
+        x = randn(*shape)
+        x /= x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+        return x.to(torch.bfloat16)
+
+    out = {"q": unit_bf16((B, T, H, dk)), "k": unit_bf16((B, T, H, dk)),
+           "v": randn(B, T, H, dv).to(torch.bfloat16)}
+    la = randn(B, T, H, dk)
+    la += 3.0
+    out["log_alpha"] = F.logsigmoid(la)
+    del la
+    out["b"] = torch.sigmoid(randn(B, T, H, dk))
+    out["w"] = torch.sigmoid(randn(B, T, H, dv))
+    out["S0"] = randn(B, H, dk, dv) * s0_std if s0_std > 0 else None
+    if grads:
+        out["dO"] = randn(B, T, H, dv)
+        out["dS_final"] = randn(B, H, dk, dv) * 0.01
+    if read_after_write:
+        ch = torch.randint(0, dk, (B, T, H), generator=g, device=device)
+        onehot = torch.zeros(B, T, H, dk, dtype=torch.bfloat16, device=device)
+        onehot.scatter_(-1, ch.unsqueeze(-1), 1.0)
+        del ch
+        out["q"], out["k"] = onehot, onehot.clone()
+        out["b"].fill_(1.0)
+    return out

@@ -1,0 +1,122 @@
+"""GPU parity on tensors larger than 4 GiB: B=4, T=140037 (a ragged last chunk), H=16,
+dk=dv=128, bf16 q/k/v.  Every fp32 tensor of per-token values ([B,T,H,128]: log_alpha, b, w,
+o, dO and the gradients) spans 4.59 GB, so the last tokens of the last batch sit more than
+2^32 bytes from their tensor's start, and the chunk records, factors, states and dstates of
+the backward run to tens of GB.  The header's size limit (B*T*H*max(dk,dv) < 2^31 elements)
+is met: 1.15e9.
+
+Inputs are the bf16 workload recipe drawn on the device (make_inputs_device).  Two checks:
+
+* random inputs: o, S_final and every gradient of two heads, the first (b=0, h=0) and the last
+  (b=3, h=15, whose last tokens lie past 4 GiB), against the fp64 oracle run on those heads'
+  inputs alone (heads are independent in the rule: blog on Gated DeltaNet-2, the per-token
+  state update of section "Independent control on two axes" acts per head), within 3e-3
+  (forward) and 5e-3 (gradients); every output is finite;
+* the read-after-write identity (b = 1, q = k one-hot): o = w * v for every token of every
+  head, and dv = dO * w, dw = dO * v for every element, on the one-call backward and on the
+  staged training chain.  This checks every address of o, dv and dw without the oracle."""
+import pytest
+import torch
+
+import oracle
+import linear_attention_sequence_gdn2_amd as gdn2
+from linear_attention_sequence_gdn2_amd.inputs import make_inputs_device
+from _util import rel_err
+
+pytestmark = pytest.mark.gpu
+
+B, T, H, D = 4, 140037, 16, 128
+SAMPLES = ((0, 0), (3, 15))
+NAMES = ["dq", "dk", "dv", "dlog_alpha", "db", "dw"]
+
+
+def _need_memory(gb):
+    total = torch.cuda.get_device_properties(0).total_memory
+    if total < gb * 1e9:
+        pytest.skip("needs %d GB of device memory, the device has %.0f" % (gb, total / 1e9))
+
+
+def _heads(t):
+    """The sampled heads of a [B, T, H, d] tensor as a [len(SAMPLES), T, 1, d] fp32 CPU tensor."""
+    return torch.stack([t[b, :, h, :].float().cpu() for b, h in SAMPLES]).unsqueeze(2).contiguous()
+
+
+def _head_states(t):
+    """The sampled heads of a [B, H, dk, dv] tensor as [len(SAMPLES), 1, dk, dv] on the CPU."""
+    return torch.stack([t[b, h].float().cpu() for b, h in SAMPLES]).unsqueeze(1).contiguous()
+
+
+def _max_rel(x, ref, chunk=1 << 26):
+    """max |x - ref| / max |ref| over two device tensors, in pieces (no full-size temporaries)."""
+    xf, rf = x.reshape(-1), ref.reshape(-1)
+    num = den = 0.0
+    for i in range(0, xf.numel(), chunk):
+        a, r = xf[i:i + chunk].float(), rf[i:i + chunk].float()
+        num = max(num, float((a - r).abs().max()))
+        den = max(den, float(r.abs().max()))
+    return num / den
+
+
+def test_large_tensors_sampled_heads():
+    _need_memory(130)
+    print("case large B%d T%d H%d d%d: random inputs, heads %s" % (B, T, H, D, SAMPLES), flush=True)
+    x = make_inputs_device(B, T, H, D, D, 9900, "cuda", s0_std=0.02, grads=True)
+    args = (x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["S0"])
+    o, sf = gdn2.fwd(*args)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(sf).all())
+    got = {"o": _heads(o), "S_final": _head_states(sf)}
+    del o, sf
+    g = gdn2.bwd(*args, x["dO"], x["dS_final"])
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert bool(torch.isfinite(g[n]).all()), n
+        got[n] = _heads(g[n])
+    got["dS0"] = _head_states(g["dS0"])
+    del g
+    inp = {n: _heads(x[n]) for n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
+    inp["S0"], inp["dS_final"] = _head_states(x["S0"]), _head_states(x["dS_final"])
+    del x, args
+    torch.cuda.empty_cache()
+    oargs = [inp[n] for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")]
+    o_ref, sf_ref = oracle.fwd(*oargs)
+    ref = oracle.bwd(*oargs, inp["dO"], inp["dS_final"])
+    errs = {"o": rel_err(got["o"], o_ref), "S_final": rel_err(got["S_final"], sf_ref)}
+    errs.update({n: rel_err(got[n], ref[n]) for n in NAMES + ["dS0"]})
+    print(" ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    assert errs["o"] < 3e-3 and errs["S_final"] < 3e-3, errs
+    bad = {n: e for n, e in errs.items() if n not in ("o", "S_final") and not e < 5e-3}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("staged", [False, True])
+def test_large_tensors_read_after_write(staged):
+    _need_memory(130)
+    print("case large B%d T%d H%d d%d: read-after-write, %s backward" %
+          (B, T, H, D, "staged" if staged else "one-call"), flush=True)
+    x = make_inputs_device(B, T, H, D, D, 9910, "cuda", grads=True, read_after_write=True)
+    args = (x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], None)
+    if not staged:
+        o, _ = gdn2.fwd(*args, want_state=False)
+        torch.cuda.synchronize()
+        eo = _max_rel(o, x["w"] * x["v"].float())
+        del o
+        print("max |o - w v| / max |w v| = %.2e" % eo, flush=True)
+        assert eo < 3e-3, eo
+        g = gdn2.bwd(*args, x["dO"], None)
+    else:
+        factors = gdn2.bwd_factors(x["q"], x["k"], x["log_alpha"], x["b"])
+        o, _, states, dstates, _ = gdn2.sweeps(factors, x["v"], x["w"], D, None, x["dO"], None)
+        torch.cuda.synchronize()
+        eo = _max_rel(o, x["w"] * x["v"].float())
+        del o
+        print("training forward: max |o - w v| / max |w v| = %.2e" % eo, flush=True)
+        assert eo < 3e-3, eo
+        g = gdn2.bwd_grads(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], x["dO"], states, dstates,
+                           factors)
+        del factors, states, dstates
+    torch.cuda.synchronize()
+    ev = _max_rel(g["dv"], x["dO"] * x["w"])
+    ew = _max_rel(g["dw"], x["dO"] * x["v"].float())
+    print("dv %.2e dw %.2e" % (ev, ew), flush=True)
+    assert ev < 5e-3 and ew < 5e-3, (ev, ew)
