@@ -165,6 +165,7 @@ __device__ __forceinline__ void chunk_load_record(const char *rc, int tid, Chunk
 
 template <int DK, bool BF16, bool GL, bool SG, bool EX>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_chunk_kernel(BwdArgs a) {
+    GDN2_POISON_LDS();
     constexpr int NTH = kChunkThreads;
     constexpr int VT = 32;                       // value columns per tile
     constexpr int NKS = DK / 32;                 // 32-channel contraction steps

@@ -82,6 +82,31 @@ constexpr int kChunkThreads = 2 * kThreads;   // workgroup of the chunk-parallel
     } while (0)
 #endif
 
+// LDS poison fill of the debug build (-DGDN2_LDS_POISON, libgdn2_poison.so).  At the top of
+// every kernel the workgroup fills its whole static LDS allocation, bytes [0,
+// __builtin_amdgcn_groupstaticsize()), with all-ones words (a NaN in fp32 and in bf16) and
+// waits at a barrier.  A kernel that reads a word of LDS before writing it then sees NaN
+// instead of a previous workgroup's leftovers, and its results differ from the normal build's.
+// In the normal build the macro is empty.
+#ifdef GDN2_LDS_POISON
+__device__ __forceinline__ void lds_poison_fill() {
+    typedef __attribute__((address_space(3))) unsigned lds_u32;
+    // LDS address 0 from a value the compiler cannot fold: a literal null would become the
+    // local address space's null value, which is not address 0
+    unsigned base = 0;
+    asm volatile("" : "+v"(base));
+    lds_u32 *p = reinterpret_cast<lds_u32 *>(static_cast<uintptr_t>(base));
+    const unsigned n = __builtin_amdgcn_groupstaticsize() / 4u;
+    for (unsigned i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0xffffffffu;
+    __syncthreads();
+}
+#define GDN2_POISON_LDS() lds_poison_fill()
+#else
+#define GDN2_POISON_LDS() \
+    do {                  \
+    } while (0)
+#endif
+
 struct Split8 {
     bf16x8 hi, lo;
 };

@@ -63,6 +63,7 @@ __device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
 
 template <int DV, bool GB, bool YB>
 __global__ __launch_bounds__(kOutThreads) void out_fwd_kernel(OutArgs a) {
+    GDN2_POISON_LDS();
     using C = OutCfg<DV>;
     const int lane = threadIdx.x % C::LPR, rg = threadIdx.x / C::LPR;
     const float4 wt = a.weight ? reinterpret_cast<const float4 *>(a.weight)[lane] : make_float4(1.f, 1.f, 1.f, 1.f);
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(kOutThreads) void out_fwd_kernel(OutArgs a) {
 
 template <int DV, bool GB>
 __global__ __launch_bounds__(kOutThreads) void out_bwd_kernel(OutArgs a) {
+    GDN2_POISON_LDS();
     using C = OutCfg<DV>;
     const int lane = threadIdx.x % C::LPR, rg = threadIdx.x / C::LPR;
     const float4 wt = a.weight ? reinterpret_cast<const float4 *>(a.weight)[lane] : make_float4(1.f, 1.f, 1.f, 1.f);
@@ -170,6 +172,7 @@ __global__ __launch_bounds__(kOutThreads) void out_bwd_kernel(OutArgs a) {
 constexpr int kRedThreads = 1024, kRedCols = 16, kRedGroups = kRedThreads / kRedCols, kRedBatch = 8;
 __global__ __launch_bounds__(kRedThreads) void out_dweight_kernel(const float *partial, int nblk, int dv,
                                                                    float *dweight) {
+    GDN2_POISON_LDS();
     __shared__ float sPart[kRedThreads];
     const int col = blockIdx.x * kRedCols + threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols;
     float s = 0.f;

@@ -58,6 +58,7 @@ __device__ __forceinline__ void store_frag_tile(__bf16 *tile, int l, const f32x4
 // W^T Kh.  The record's Kh, Et, Qt rows, gamma and decay offsets are the same in both passes.
 template <int DK, bool BF16, bool GL, bool SG, bool FWD, bool EX>
 __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a) {
+    GDN2_POISON_LDS();
     constexpr int NTH = kChunkThreads;
     constexpr int NM = DK / 16, NKS = DK / 32, NMH = DK / 32, NEH = 4 * NMH;
     constexpr int PK = DK + 8, PT = kChunk + 8, PA = kChunk + 4;
@@ -495,6 +496,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void bwd_factors_kernel(BwdArgs a
 template <int DK, int VT>
 __global__ __launch_bounds__((ReverseCfg<DK, VT>::NTH), (ReverseCfg<DK, VT>::WG_PER_CU)) void bwd_reverse_kernel(
     BwdArgs a) {
+    GDN2_POISON_LDS();
     using Lds = RevLds<DK, VT>;
     __shared__ __align__(16) __bf16 sD0[Lds::D], sD1[Lds::D], sO0[Lds::O], sO1[Lds::O];
     bwd_reverse_body<DK, VT>(a, xcd_swizzle(blockIdx.x, gridDim.x), sD0, sD1, sO0, sO1);

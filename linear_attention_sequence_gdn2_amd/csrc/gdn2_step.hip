@@ -20,6 +20,7 @@ namespace gdn2 {
 
 template <int DK, bool BF16, bool GL, bool SG>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
+    GDN2_POISON_LDS();
     constexpr int VT = 32, NS = kThreads / VT, RPS = DK / NS;   // slices, rows per slice
     __shared__ float sAlpha[DK], sE[DK], sK[DK], sQ[DK];
     __shared__ float sRed[NS][VT];

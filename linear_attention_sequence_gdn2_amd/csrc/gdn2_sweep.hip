@@ -48,6 +48,7 @@ static __device__ unsigned long long *g_sweep_stamps;
 
 template <int DK, int VT, bool BF16, bool OUT, bool STATES, bool GL, bool SG>
 __global__ __launch_bounds__(kThreads, 2) void fwd_sweep_kernel(FwdArgs a) {
+    GDN2_POISON_LDS();
     using Rec = ChunkRecord<DK>;
     constexpr int NKS = DK / 32;           // 32-channel contraction steps
     constexpr int NVT = VT / 16;           // 16-column value tiles
@@ -819,6 +820,7 @@ __device__ __forceinline__ void fwd_sweep64_body(const FwdArgs &a, const int L, 
 
 template <int DK, bool OUT, bool STATES, bool GL, bool SG, int SEG, int VT = 64, int NV = 0>
 __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a) {
+    GDN2_POISON_LDS();
     using Lds = Sweep64Lds<DK, OUT, VT>;
     __shared__ __align__(16) __bf16 sK[Lds::K], sE[Lds::E], sQ[Lds::Q], sS[Lds::S], sX[Lds::X], sU[Lds::U];
     __shared__ __align__(16) float sW[NV > 0 ? VT : 4];
@@ -834,6 +836,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_sweep64_kernel(FwdArgs a
 // role keeps its dS' and dO buffers in the forward role's arrays.
 template <int DK, bool OUT, bool GL, bool SG, int VT>
 __global__ __launch_bounds__(kChunkThreads, 1) void fwd_rev_sweep_kernel(FwdArgs fa, BwdArgs ba, int nfwd) {
+    GDN2_POISON_LDS();
     using Lds = Sweep64Lds<DK, OUT, VT>;
     using RL = RevLds<DK, VT>;
     static_assert(RL::D <= Lds::K && RL::D <= Lds::S && RL::O <= Lds::X && RL::O <= Lds::U,
@@ -856,6 +859,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void fwd_rev_sweep_kernel(FwdArgs
 template <int DK>
 __global__ __launch_bounds__(256) void seg_combine_kernel(const float *E, const float *S0, float *Sin, int DV,
                                                           int nseg) {
+    GDN2_POISON_LDS();
     constexpr int NCB = 16;                       // state columns per workgroup
     constexpr int PM = DK + 4;                    // row pitch of M in LDS
     constexpr int RPT = DK / 64;                  // rows per thread: 64 row blocks x 4 column blocks
