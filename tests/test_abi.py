@@ -17,6 +17,20 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 P = ctypes.c_void_p
 
 
+def _library_cus():
+    """The compute-unit count the library sizes its launches from: the device's, or 256 when
+    no device answers (a host without a GPU)."""
+    import torch
+    if not torch.cuda.is_available():
+        return 256
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# launch-shape and workspace expectations computed for 256 compute units (an MI355X, or a host
+# with no device); on a device partitioned into fewer CUs the library picks other launches
+cus_256 = pytest.mark.skipif(_library_cus() != 256, reason="expectations assume 256 compute units")
+
+
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -60,6 +74,7 @@ def _flags(items):
 RECORD = (6 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2 * 16 * 64 * 16 + 4 * 128 * 4 + 128 * 4 + 255) // 256 * 256
 
 
+@cus_256
 def test_workspace_and_state_sizes():
     lib = gdn2.load()
     s = _shape()
@@ -208,6 +223,7 @@ def test_output_epilogue_checks_arguments():
     assert lib.gdn2_output_bwd(ctypes.byref(s), f, f, 1, None, F(-0.5), f, f, f, None, None, 0, None) == INVALID
 
 
+@cus_256
 def test_sweeps_entry_checks_arguments_and_fusion_rule():
     lib = gdn2.load()
     f = P(0x10000)
@@ -250,6 +266,7 @@ def test_factored_forward_checks_arguments():
     assert lib.gdn2_chunk_fwd_factored(ctypes.byref(s), f, f, P(0x10004), None, f, None, None, None) == INVALID
 
 
+@cus_256
 def test_forward_workspace():
     """The forward writes forward-only chunk records first: it needs a workspace of one record
     per (batch, head, chunk) and their flags.  The segment expectations assume 256 CUs, the
@@ -294,6 +311,7 @@ def test_forward_workspace():
 
 
 
+@cus_256
 def test_fused_forward_output_workspace_and_checks():
     """gdn2_chunk_fwd_output: with no device answering, a shape whose heads span several
     workgroups cannot be shown resident, so it takes the unfused route (gdn2_chunk_fwd's
