@@ -5,7 +5,7 @@ o, dO and the gradients) spans 4.59 GB, so the last tokens of the last batch sit
 the backward run to tens of GB.  The header's size limit (B*T*H*max(dk,dv) < 2^31 elements)
 is met: 1.15e9.
 
-Inputs are the bf16 workload recipe drawn on the device (make_inputs_device).  Two checks:
+Inputs are the bf16 workload recipe drawn on the device (make_inputs_device).  Three checks:
 
 * random inputs: o, S_final and every gradient of two heads, the first (b=0, h=0) and the last
   (b=3, h=15, whose last tokens lie past 4 GiB), against the fp64 oracle run on those heads'
@@ -14,7 +14,10 @@ Inputs are the bf16 workload recipe drawn on the device (make_inputs_device).  T
   (forward) and 5e-3 (gradients); every output is finite;
 * the read-after-write identity (b = 1, q = k one-hot): o = w * v for every token of every
   head, and dv = dO * w, dw = dO * v for every element, on the one-call backward and on the
-  staged training chain.  This checks every address of o, dv and dw without the oracle."""
+  staged training chain.  This checks every address of o, dv and dw without the oracle;
+* the forward with the fused output epilogue under the same identity: y = rmsnorm(w * v) *
+  weight * g on every element (the blog's output path: RMS normalisation and an output gate
+  after the operator, section "Token path and parallel training")."""
 import pytest
 import torch
 
@@ -120,3 +123,32 @@ def test_large_tensors_read_after_write(staged):
     ew = _max_rel(g["dw"], x["dO"] * x["v"].float())
     print("dv %.2e dw %.2e" % (ev, ew), flush=True)
     assert ev < 5e-3 and ew < 5e-3, (ev, ew)
+
+
+def test_large_tensors_fused_output_epilogue():
+    """gdn2_chunk_fwd_output at the same size under the read-after-write identity: o = w * v, so
+    y = rmsnorm(w * v) * weight * g for every row, a closed form of the inputs alone (the output
+    gate g and the norm weight drawn on the device), checked on every element of the bf16 y."""
+    _need_memory(130)
+    print("case large B%d T%d H%d d%d: fused output epilogue, read-after-write" % (B, T, H, D), flush=True)
+    x = make_inputs_device(B, T, H, D, D, 9920, "cuda", read_after_write=True)
+    gen = torch.Generator(device="cuda").manual_seed(9921)
+    g = torch.sigmoid(torch.randn(B, T, H, D, generator=gen, device="cuda")).to(torch.bfloat16)
+    wt = torch.rand(D, generator=gen, device="cuda") + 0.5
+    eps = 1e-6
+    args = (x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"])
+    y, _, ws = gdn2.fwd_output(*args, g, wt, eps, None, want_state=False, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert gdn2.fwd_output_xerr((B, T, H, D, D, torch.bfloat16), ws) == 0
+    num = den = 0.0
+    step = 1 << 14                                 # tokens per piece
+    for t0 in range(0, T, step):
+        z = x["w"][:, t0:t0 + step] * x["v"][:, t0:t0 + step].float()
+        ref = z * torch.rsqrt((z * z).mean(-1, keepdim=True) + eps) * wt * g[:, t0:t0 + step].float()
+        num = max(num, float((y[:, t0:t0 + step].float() - ref).abs().max()))
+        den = max(den, float(ref.abs().max()))
+    print("max |y - rmsnorm(w v) weight g| / max = %.2e" % (num / den), flush=True)
+    # the bar: the bf16 forward's 3e-3 on o (here o = w v up to the path's arithmetic; the rms norm
+    # is scale-free per row, and a row's rms over 128 columns is stable) plus one rounding of y to
+    # bf16, 2^-9 of a value
+    assert num / den < 3e-3 + 2.0 ** -9, num / den
