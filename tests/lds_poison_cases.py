@@ -49,11 +49,15 @@ def main(path):
         keep(name + ".staged", o=o2, S_final=sf2, states=states, dstates=dstates, dS0=dS0, **g2)
         torch.cuda.synchronize()
 
+    # the fused epilogue on a shape with one workgroup per head (dv = 64 on 64-column tiles): the
+    # shapes whose heads span several workgroups are cooperative launches, which ROCm grants to one
+    # process per device at a time, and the test process that starts this one may hold that grant
     print("case output epilogue", flush=True)
-    x = make_inputs(2, 100, 40, 64, 128, seed=9650, s0_std=0.05)
-    ex = make_output_inputs(2, 100, 40, 128, seed=9651, g_dtype="bf16")
+    x = make_inputs(3, 70, 50, 128, 64, seed=9650, s0_std=0.05)
+    ex = make_output_inputs(3, 70, 50, 64, seed=9651, g_dtype="bf16")
     d = {n: (x[n].to(dev) if x.get(n) is not None else None) for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")}
     g, wt, dy = ex["g"].to(dev), ex["weight"].to(dev), ex["dy"].to(dev)
+    assert gdn2.fwd_output_fused(3, 70, 50, 128, 64, torch.bfloat16), "the shape should take the fused sweep"
     y, sf, _ = gdn2.fwd_output(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], g, wt, 1e-6, d["S0"],
                                out_dtype=torch.bfloat16)
     keep("fused_output", y=y, S_final=sf)

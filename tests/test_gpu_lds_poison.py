@@ -4,7 +4,9 @@ before writing it would then compute from NaN instead of whatever the CU's previ
 left there, and its results would change.  Every kernel of the library runs on small seeded
 cases (tests/lds_poison_cases.py: every launch path, gate format and pass) in a child process
 with each build, and the two sets of results must be identical bit for bit.  The library is
-chosen per process (GDN2_LIBRARY), hence the child processes."""
+chosen per process (GDN2_LIBRARY), hence the child processes.  The fused epilogue runs there on a
+shape with one workgroup per head: cooperative launches, which the shapes with several take, are
+granted to one process per device at a time, and this test's own process may hold the grant."""
 import os
 import subprocess
 import sys
