@@ -291,10 +291,11 @@ int gdn2_output_bwd(const gdn2_shape *shape, const float *o, const void *g, int 
  *   shape the forward does not split into segments, and every workgroup of the sweep resident
  *   at once): the launches of gdn2_chunk_fwd (chunk records, their exact pass, the sweep),
  *   with the epilogue in the sweep's output stage; the sweep is a cooperative launch when a
- *   head's value columns span several workgroups.  ROCm grants cooperative launches on a device
- *   to one process at a time: while another process on the same GPU holds that grant (it keeps
- *   it once it has made a cooperative launch), such a call fails with GDN2_ERR_HIP and writes
- *   nothing.  Shapes with one workgroup per head launch normally.  The workspace holds the records and flags, then the
+ *   head's value columns span several workgroups.  The runtime can refuse a cooperative launch
+ *   while another process on the same GPU holds the device's cooperative-launch resources (seen
+ *   once that process had made a cooperative launch of its own); the call then returns
+ *   GDN2_ERR_HIP after the records launch, with y and S_final not written.  Shapes with one
+ *   workgroup per head launch normally.  The workspace holds the records and flags, then the
  *   exchange area (cleared by the records launch): 64-bit words {row sum of squares of one
  *   wave's columns, chunk + 1} in a ring of two chunk slots per head, and in the last 256 bytes
  *   an int that counts exchange waits that ran out (0 in a correct run; a wait runs out only if
