@@ -50,8 +50,8 @@ def main(path):
         torch.cuda.synchronize()
 
     # the fused epilogue on a shape with one workgroup per head (dv = 64 on 64-column tiles): the
-    # shapes whose heads span several workgroups are cooperative launches, which ROCm grants to one
-    # process per device at a time, and the test process that starts this one may hold that grant
+    # shapes whose heads span several workgroups take a cooperative launch, which the runtime can
+    # refuse while the test process that starts this one holds the device's cooperative resources
     print("case output epilogue", flush=True)
     x = make_inputs(3, 70, 50, 128, 64, seed=9650, s0_std=0.05)
     ex = make_output_inputs(3, 70, 50, 64, seed=9651, g_dtype="bf16")

@@ -5,8 +5,9 @@ left there, and its results would change.  Every kernel of the library runs on s
 cases (tests/lds_poison_cases.py: every launch path, gate format and pass) in a child process
 with each build, and the two sets of results must be identical bit for bit.  The library is
 chosen per process (GDN2_LIBRARY), hence the child processes.  The fused epilogue runs there on a
-shape with one workgroup per head: cooperative launches, which the shapes with several take, are
-granted to one process per device at a time, and this test's own process may hold the grant."""
+shape with one workgroup per head: the shapes with several take a cooperative launch, which the
+runtime can refuse while another process on the GPU (this test's own) holds the device's
+cooperative-launch resources."""
 import os
 import subprocess
 import sys
